@@ -1,0 +1,160 @@
+/*
+ * mmvq.h - C ABI of the MI355X (gfx950) decode-time quantized mat-vec.
+ *
+ * The library computes, on the GPU, the quantized matrix-vector product used
+ * at decode time: an fp32 activation is first quantized to q8_1 blocks, then
+ * every row of a block-quantized weight matrix (Q4_0, Q4_K or Q6_K) is
+ * reduced against it with integer block dot products, the block scales
+ * applied afterwards. Variants: n = 1..8 activation columns against one
+ * weight read, a fused gate/up GLU epilogue, and an expert-indexed product.
+ *
+ * Citations (sources of each operation's definition):
+ *   [MMVQ §X]   page "llama.cpp 源码完全拆解(十四):mul_mat_vec_q——解码时一条量化权重
+ *               如何被 dp4a 逐块点积" (pinghaoyang.com.cn), section X.
+ *   [GGUF16 §X] page "GGUF 量化内幕：第16章 llama.cpp 量化代码架构"
+ *               (cnblogs apachecn), section X.
+ *
+ * Conventions for every entry point:
+ *   - Pointers to data (x, W, y_q, ids, out, dots) are DEVICE pointers. The
+ *     caller allocates, owns and frees them; the library keeps no
+ *     allocation, no pointer and no mutable global state, and may be called
+ *     from several host threads at once.
+ *   - `stream` is a hipStream_t (NULL = the null stream). All work is
+ *     enqueued asynchronously on it; the library never synchronizes. Inputs
+ *     must stay valid and outputs untouched until the stream reaches the
+ *     enqueued work.
+ *   - Shapes: M output rows, K the reduction length (row length), n
+ *     activation columns (1..8).
+ *   - Weights W: M rows stored back to back, each K/qk blocks of the type's
+ *     block size (qk = 32 for Q4_0, 256 for Q4_K and Q6_K); row stride
+ *     (K/qk)*block_bytes. Byte layouts:
+ *       Q4_0 (18 B / 32): fp16 d @0, 16 B of 4-bit codes @2; qs[j] low
+ *            nibble = element j, high nibble = element j+16; w = d*(q-8).
+ *       Q4_K (144 B / 256): fp16 d @0, fp16 dmin @2, 12 B of packed 6-bit
+ *            sub-block scales and mins @4, 128 B of 4-bit codes @16;
+ *            w = d*sc*q - dmin*m.
+ *       Q6_K (210 B / 256): 128 B low code bits @0, 64 B high code bits
+ *            @128, 16 int8 sub-block scales @192, fp16 d @208;
+ *            w = d*sc*(q-32).
+ *   - Activations y_q: n columns, column j at y_q + j*(K/32)*36 bytes, each
+ *     K/32 q8_1 blocks of 36 bytes: fp16 d @0, fp16 s = d*sum(q) @2, 32 int8
+ *     codes @4 [MMVQ §激活的量化].
+ *   - Output out: fp32, column-major by activation column:
+ *     out[j*M + r] is row r against column j [MMVQ §归约与写出].
+ *   - Alignment: W and y_q 16-byte aligned, x, out, ids and dots 4-byte
+ *     aligned; expert_stride_bytes a multiple of 16.
+ *   - Return value: MMVQ_OK (0) or a negative MMVQ_ERR_* code. Arguments are
+ *     validated on the host before anything is enqueued; an invalid call
+ *     enqueues nothing. No entry point aborts the process.
+ *   - Expert ids are not checked on the GPU: an id outside 0..n_experts-1
+ *     reads outside the weights and is undefined behaviour.
+ */
+#ifndef MMVQ_H
+#define MMVQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Type ids follow the ggml numbering, whose ids are never reused
+ * [GGUF16 §16.1.1]. */
+enum {
+    MMVQ_Q4_0 = 2,
+    MMVQ_Q8_1 = 9,
+    MMVQ_Q4_K = 12,
+    MMVQ_Q6_K = 14
+};
+
+/* Epilogue of the fused gate/up variants [MMVQ §融合]. */
+enum {
+    MMVQ_GLU_PLAIN = 0,   /* out = gate * up                  */
+    MMVQ_GLU_SWIGLU = 1   /* out = silu(gate) * up, silu(z) = z/(1+e^-z) */
+};
+
+enum {
+    MMVQ_OK = 0,
+    MMVQ_ERR_NULL = -1,      /* a required pointer is NULL                         */
+    MMVQ_ERR_TYPE = -2,      /* unknown weight type or glu_op                       */
+    MMVQ_ERR_SHAPE = -3,     /* K not a multiple of the block, n outside 1..8,
+                                M < 1, ldx < K, top_k outside 1..n_experts, ...   */
+    MMVQ_ERR_ALIGN = -4,     /* a pointer or stride is not aligned as required      */
+    MMVQ_ERR_LAUNCH = -5     /* the HIP runtime reported an error at launch         */
+};
+
+/* Largest number of activation columns (tokens) per call [MMVQ §分派]. */
+#define MMVQ_MAX_COLS 8
+
+/* Block geometry of a type: elements per block and bytes per block
+ * (Q4_0 32/18, Q4_K 256/144, Q6_K 256/210, Q8_1 32/36)
+ * [MMVQ §一次 vec_dot 的解剖 (format table); GGUF16 §16.1.2, §16.1.3].
+ * Either output pointer may be NULL. Host-only; touches no device. */
+int mmvq_type_info(int type, int *block_elems, int *block_bytes);
+
+/* Quantize n fp32 columns to q8_1 [MMVQ §激活的量化]. Column j of x starts at
+ * x + j*ldx (ldx >= K floats); the first K values of each column are used.
+ * Per block of 32: d = amax/127 in fp32, q = roundf(x/d) (0 when d == 0),
+ * stored fp16(d), fp16(fp32(d*sum(q))), q. y_q receives n*(K/32)*36 bytes.
+ * Requires K % 32 == 0, 1 <= n <= MMVQ_MAX_COLS. Inputs must be finite; for
+ * blocks whose amax is below 127*2^-126 the fp32 d is subnormal and the
+ * codes are not meaningful (the computation is still defined). */
+int mmvq_quantize_q8_1(const float *x, int64_t K, int64_t n, int64_t ldx,
+                       void *y_q, void *stream);
+
+/* out[j*M + r] = sum over the K/qk blocks of row r of W of (block scales)
+ * x (integer block dot against column j of y_q), for r < M, j < n
+ * [MMVQ §一次 vec_dot 的解剖, §kernel 的形状, §归约与写出, §多个 token 时].
+ * Q4_0: d_w*(d8*sum(q*qy) - 8*s) per 32-block. Q4_K: per 32-element
+ * sub-block t, d*sc_t*d8*sum(q*qy) - dmin*m_t*d8*sum(qy). Q6_K: per
+ * 16-element sub-block, d*sc*d8*sum((q-32)*qy). Accumulated in fp32.
+ * Requires K % qk == 0, M >= 1, 1 <= n <= MMVQ_MAX_COLS. */
+int mmvq(const void *W, int type, int64_t M, int64_t K,
+         const void *y_q, int64_t n, float *out, void *stream);
+
+/* Fused gate/up: out[j*M + r] = act(g) * u with g the mmvq of W_gate and u
+ * the mmvq of W_up (same type and shape), act per glu_op; both weight
+ * streams are read in one kernel and the epilogue applies the GLU
+ * [MMVQ §融合]. Same requirements as mmvq. */
+int mmvq_glu(const void *W_gate, const void *W_up, int type, int64_t M,
+             int64_t K, const void *y_q, int64_t n, int glu_op, float *out,
+             void *stream);
+
+/* Expert-indexed product (mul_mat_id) [MMVQ §MoE, §正确性上的几个坑].
+ * Expert e's M x K matrix starts at W + e*expert_stride_bytes. ids holds
+ * n_tokens*top_k int32 expert ids, token-major (device memory). For token
+ * t and slot k: out[(t*top_k + k)*M + r] = row r of expert ids[t*top_k+k]
+ * against column t of y_q (each token's one q8_1 column serves all its
+ * slots). Each expert's weights are read once per call, for all tokens
+ * routed to it. Requires 1 <= n_tokens <= MMVQ_MAX_COLS,
+ * 1 <= top_k <= n_experts, expert_stride_bytes >= M*row_bytes. */
+int mmvq_id(const void *W, int64_t expert_stride_bytes, int n_experts,
+            int type, int64_t M, int64_t K, const void *y_q,
+            int64_t n_tokens, const int32_t *ids, int top_k, float *out,
+            void *stream);
+
+/* Expert-indexed fused gate/up: as mmvq_id with the epilogue of mmvq_glu;
+ * W_gate and W_up share expert_stride_bytes. */
+int mmvq_id_glu(const void *W_gate, const void *W_up,
+                int64_t expert_stride_bytes, int n_experts, int type,
+                int64_t M, int64_t K, const void *y_q, int64_t n_tokens,
+                const int32_t *ids, int top_k, int glu_op, float *out,
+                void *stream);
+
+/* TEST SUPPORT: the integer block dots that mmvq forms, through the same
+ * device decode routines, written instead of being scaled and summed.
+ * dots[((j*M + r)*(K/qk) + b)*D + i] with D = 16 for Q4_K (sum(q*qy) of
+ * sub-blocks 0..7, then sum(qy) of sub-blocks 0..7), 16 for Q6_K
+ * (sum((q-32)*qy) of sub-blocks 0..15), 1 for Q4_0 (sum(q*qy)).
+ * [MMVQ §dp4a, §一次 vec_dot 的解剖]. Same requirements as mmvq. */
+int mmvq_block_dots(const void *W, int type, int64_t M, int64_t K,
+                    const void *y_q, int64_t n, int32_t *dots, void *stream);
+
+/* Static, human-readable text for a return code. Never NULL. */
+const char *mmvq_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MMVQ_H */

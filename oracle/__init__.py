@@ -1,0 +1,199 @@
+"""CPU oracle for the decode-time quantized mat-vec (MMVQ).
+
+TEST INFRASTRUCTURE ONLY. This package wraps ``libmmvq_oracle.so`` (plain C,
+fp64 accumulation, built from ``mmvq_oracle.c`` with gcc). Only ``tests/``,
+``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may
+import it. The product library and its Python binding never import it, and
+the two share no code: only the seeded input generator
+(``quantized_decode_gemv_quantize_amd.synth``) feeds both.
+
+What each function computes is stated in ``mmvq_oracle.h``; the page
+citations are there and in ``mmvq_oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "mmvq_oracle.c")
+LIB = os.path.join(HERE, "libmmvq_oracle.so")
+
+Q4_0, Q8_1, Q4_K, Q6_K = 2, 9, 12, 14
+GLU_PLAIN, GLU_SWIGLU = 0, 1
+BLOCK = {Q4_0: (32, 18), Q4_K: (256, 144), Q6_K: (256, 210), Q8_1: (32, 36)}
+DOTS_PER_BLOCK = {Q4_0: 1, Q4_K: 16, Q6_K: 16}
+
+_c_i64 = ctypes.c_int64
+_p = ctypes.c_void_p
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (plain C11, no fp contraction)."""
+    if force or not os.path.exists(LIB):
+        tmp = LIB + ".tmp"
+        subprocess.check_call([
+            "gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-ffp-contract=off",
+            "-fno-fast-math", "-fPIC", "-shared", "-o", tmp, SRC, "-lm"])
+        os.replace(tmp, LIB)
+    return LIB
+
+
+class OracleError(RuntimeError):
+    def __init__(self, code: int):
+        super().__init__(f"oracle returned {code}")
+        self.code = code
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise OracleError(rc)
+
+
+def _ptr(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _u8(a) -> np.ndarray:
+    return np.ascontiguousarray(np.frombuffer(a, dtype=np.uint8) if isinstance(a, (bytes, bytearray))
+                                else a).view(np.uint8).reshape(-1)
+
+
+def _load(path: str):
+    L = ctypes.CDLL(path)
+    L.orc_f32_to_f16.restype = ctypes.c_uint16
+    L.orc_f32_to_f16.argtypes = [ctypes.c_float]
+    L.orc_f16_to_f64.restype = ctypes.c_double
+    L.orc_f16_to_f64.argtypes = [ctypes.c_uint16]
+    L.orc_quantize_q8_1.argtypes = [_p, _c_i64, _c_i64, _c_i64, _p]
+    L.orc_mmvq_rows.argtypes = [_p, ctypes.c_int, _c_i64, _c_i64, _p, _c_i64,
+                                _c_i64, _c_i64, _p, _p, _p]
+    L.orc_mmvq.argtypes = [_p, ctypes.c_int, _c_i64, _c_i64, _p, _c_i64, _p, _p, _p]
+    L.orc_mmvq_glu.argtypes = [_p, _p, ctypes.c_int, _c_i64, _c_i64, _p, _c_i64,
+                               ctypes.c_int, _p]
+    L.orc_mmvq_id.argtypes = [_p, _c_i64, ctypes.c_int, ctypes.c_int, _c_i64, _c_i64,
+                              _p, _c_i64, _p, ctypes.c_int, _p, _p]
+    L.orc_mmvq_id_glu.argtypes = [_p, _p, _c_i64, ctypes.c_int, ctypes.c_int, _c_i64,
+                                  _c_i64, _p, _c_i64, _p, ctypes.c_int, ctypes.c_int, _p]
+    L.orc_dequantize_row.argtypes = [ctypes.c_int, _p, _c_i64, _p]
+    L.orc_dequantize_q8_1.argtypes = [_p, _c_i64, _p]
+    L.orc_q4_k_scale_min.argtypes = [_p, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
+                                     ctypes.POINTER(ctypes.c_int)]
+    L.orc_q4_k_scale_min.restype = None
+    L.orc_type_info.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_int),
+                                ctypes.POINTER(ctypes.c_int)]
+    L.orc_dots_per_block.argtypes = [ctypes.c_int]
+    return L
+
+
+class Oracle:
+    """ctypes wrapper over one build of the oracle library."""
+
+    def __init__(self, path: str = LIB):
+        self.path = path
+        self.L = _load(path)
+
+    def f32_to_f16(self, v: float) -> int:
+        return int(self.L.orc_f32_to_f16(float(np.float32(v))))
+
+    def f16_to_f64(self, h: int) -> float:
+        return float(self.L.orc_f16_to_f64(int(h)))
+
+    def type_info(self, t: int):
+        e, b = ctypes.c_int(), ctypes.c_int()
+        _check(self.L.orc_type_info(t, ctypes.byref(e), ctypes.byref(b)))
+        return e.value, b.value
+
+    def dots_per_block(self, t: int) -> int:
+        return int(self.L.orc_dots_per_block(t))
+
+    def q4_k_scale_min(self, scales12, t: int):
+        s = _u8(bytes(scales12))
+        sc, m = ctypes.c_int(), ctypes.c_int()
+        self.L.orc_q4_k_scale_min(_ptr(s), t, ctypes.byref(sc), ctypes.byref(m))
+        return sc.value, m.value
+
+    def quantize_q8_1(self, x: np.ndarray, K: int | None = None) -> np.ndarray:
+        """x: float32 [n, ldx]; quantizes the first K of each row. Returns uint8
+        [n, (K/32)*36]."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        if x.ndim == 1:
+            x = x.reshape(1, -1)
+        n, ldx = x.shape
+        K = ldx if K is None else K
+        y = np.zeros((n, (K // 32) * 36), dtype=np.uint8)
+        _check(self.L.orc_quantize_q8_1(_ptr(x), K, n, ldx, _ptr(y)))
+        return y
+
+    def mmvq(self, W, wtype: int, M: int, K: int, y_q: np.ndarray, n: int,
+             rows: tuple[int, int] | None = None, want_dots: bool = False):
+        """Returns (out [n, M] f64, mag [n, M] f64, dots or None). With rows=(r0, r1)
+        only those rows are filled (others are NaN)."""
+        Wb = _u8(W)
+        y = _u8(y_q)
+        out = np.full((n, M), np.nan)
+        mag = np.full((n, M), np.nan)
+        dots = None
+        dptr = None
+        if want_dots:
+            qk, _ = BLOCK[wtype]
+            dots = np.zeros((n, M, K // qk, DOTS_PER_BLOCK[wtype]), dtype=np.int32)
+            dptr = _ptr(dots)
+        r0, r1 = rows if rows is not None else (0, M)
+        _check(self.L.orc_mmvq_rows(_ptr(Wb), wtype, M, K, _ptr(y), n, r0, r1,
+                                   _ptr(out), _ptr(mag), dptr))
+        return out, mag, dots
+
+    def mmvq_glu(self, Wg, Wu, wtype: int, M: int, K: int, y_q: np.ndarray, n: int,
+                 glu_op: int = GLU_SWIGLU) -> np.ndarray:
+        out = np.zeros((n, M))
+        _check(self.L.orc_mmvq_glu(_ptr(_u8(Wg)), _ptr(_u8(Wu)), wtype, M, K, _ptr(_u8(y_q)), n,
+                                  glu_op, _ptr(out)))
+        return out
+
+    def mmvq_id(self, W, expert_stride: int, n_experts: int, wtype: int, M: int, K: int,
+                y_q: np.ndarray, n_tokens: int, ids: np.ndarray, top_k: int):
+        """Returns (out [n_tokens*top_k, M], mag [n_tokens*top_k, M])."""
+        ids = np.ascontiguousarray(ids, dtype=np.int32).reshape(-1)
+        out = np.zeros((n_tokens * top_k, M))
+        mag = np.zeros((n_tokens * top_k, M))
+        _check(self.L.orc_mmvq_id(_ptr(_u8(W)), expert_stride, n_experts, wtype, M, K,
+                                 _ptr(_u8(y_q)), n_tokens, _ptr(ids), top_k, _ptr(out), _ptr(mag)))
+        return out, mag
+
+    def mmvq_id_glu(self, Wg, Wu, expert_stride: int, n_experts: int, wtype: int, M: int, K: int,
+                    y_q: np.ndarray, n_tokens: int, ids: np.ndarray, top_k: int,
+                    glu_op: int = GLU_SWIGLU) -> np.ndarray:
+        ids = np.ascontiguousarray(ids, dtype=np.int32).reshape(-1)
+        out = np.zeros((n_tokens * top_k, M))
+        _check(self.L.orc_mmvq_id_glu(_ptr(_u8(Wg)), _ptr(_u8(Wu)), expert_stride, n_experts,
+                                     wtype, M, K, _ptr(_u8(y_q)), n_tokens, _ptr(ids), top_k,
+                                     glu_op, _ptr(out)))
+        return out
+
+    def dequantize_row(self, wtype: int, row, K: int) -> np.ndarray:
+        w = np.zeros(K)
+        _check(self.L.orc_dequantize_row(wtype, _ptr(_u8(row)), K, _ptr(w)))
+        return w
+
+    def dequantize_q8_1(self, y_col, K: int) -> np.ndarray:
+        y = np.zeros(K)
+        _check(self.L.orc_dequantize_q8_1(_ptr(_u8(y_col)), K, _ptr(y)))
+        return y
+
+
+_default = None
+
+
+def default() -> Oracle:
+    """The oracle built from oracle/mmvq_oracle.c (built on first use)."""
+    global _default
+    if _default is None:
+        if not os.path.exists(LIB):
+            build(force=False)
+        _default = Oracle(LIB)
+    return _default

@@ -1,0 +1,121 @@
+/*
+ * mmvq_oracle.h - plain CPU oracle for the decode-time quantized mat-vec (MMVQ).
+ *
+ * TEST INFRASTRUCTURE ONLY. This library exists to check the GPU library
+ * against a slow, obviously correct definition. Only the test suite, the
+ * smoke check and the benchmark's CPU-baseline leg may load it. The product
+ * path (include/mmvq.h and the HIP library) never links, loads or calls it,
+ * and it shares no code, header, table or helper with the product.
+ *
+ * Citations (the reader has the pages, not this repository's notes):
+ *   [MMVQ §X]   page "llama.cpp 源码完全拆解(十四):mul_mat_vec_q——解码时一条量化权重
+ *               如何被 dp4a 逐块点积" (pinghaoyang.com.cn), section X.
+ *   [GGUF16 §X] page "GGUF 量化内幕：第16章 llama.cpp 量化代码架构"
+ *               (cnblogs apachecn), section X.
+ *
+ * What the oracle computes:
+ *   1. q8_1 quantization of fp32 activations [MMVQ §激活的量化]: per 32
+ *      values, d = amax/127 (fp32), q = roundf(x/d), stored as
+ *      {fp16 d, fp16 s = d*sum(q), int8 q[32]}.
+ *   2. The quantized mat-vec as the sum over weight blocks of
+ *      (scale products) x (integer block dot), accumulated in fp64
+ *      [MMVQ §一次 vec_dot 的解剖, §dp4a].
+ *   3. The fused gate/up GLU epilogue [MMVQ §融合] and the expert-indexed
+ *      mul_mat_id [MMVQ §MoE, §正确性上的几个坑].
+ *
+ * Every function returns 0 on success or a negative ORC_ERR_* code, and
+ * never aborts.
+ */
+#ifndef MMVQ_ORACLE_H
+#define MMVQ_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Type ids follow the ggml numbering [GGUF16 §16.1.1]. */
+#define ORC_Q4_0 2
+#define ORC_Q8_1 9
+#define ORC_Q4_K 12
+#define ORC_Q6_K 14
+
+#define ORC_GLU_PLAIN  0 /* out = gate * up (the epilogue's default branch) */
+#define ORC_GLU_SWIGLU 1 /* out = silu(gate) * up                          */
+
+#define ORC_OK          0
+#define ORC_ERR_NULL   -1
+#define ORC_ERR_TYPE   -2
+#define ORC_ERR_SHAPE  -3
+#define ORC_ERR_ID     -6
+
+/* IEEE 754 binary16 conversions, written from the format definition. */
+uint16_t orc_f32_to_f16(float f);   /* round to nearest, ties to even */
+double   orc_f16_to_f64(uint16_t h);
+
+/* Elements and bytes per block: Q4_0 32/18, Q4_K 256/144, Q6_K 256/210,
+ * Q8_1 32/36. */
+int orc_type_info(int type, int *block_elems, int *block_bytes);
+
+/* Number of int32 dots the oracle reports per weight block:
+ * Q4_0 1 (the block dot), Q4_K 16 (dot1 of sub-blocks 0..7, then the
+ * activation sums dot2 of sub-blocks 0..7), Q6_K 16 (one per sub-block). */
+int orc_dots_per_block(int type);
+
+/* x: n columns of K floats, column j at x + j*ldx. y_q: n*(K/32) blocks of
+ * 36 bytes, column j at y_q + j*(K/32)*36. */
+int orc_quantize_q8_1(const float *x, int64_t K, int64_t n, int64_t ldx,
+                      uint8_t *y_q);
+
+/* out[j*M + r] = sum over the blocks of row r of W against column j of y_q,
+ * for rows r0 <= r < r1 only (other entries are left untouched).
+ * mag (optional) receives, in the same layout, the sum of the absolute
+ * values of every per-block term added into out.
+ * dots (optional) receives the integer dots, at
+ * dots[((j*M + r)*nblocks + b)*orc_dots_per_block(type) + i]. */
+int orc_mmvq_rows(const uint8_t *W, int type, int64_t M, int64_t K,
+                  const uint8_t *y_q, int64_t n, int64_t r0, int64_t r1,
+                  double *out, double *mag, int32_t *dots);
+
+/* All rows. */
+int orc_mmvq(const uint8_t *W, int type, int64_t M, int64_t K,
+             const uint8_t *y_q, int64_t n, double *out, double *mag,
+             int32_t *dots);
+
+/* out[j*M + r] = act(g) * u with g = W_gate row r . y_j, u = W_up row r . y_j,
+ * act = silu (ORC_GLU_SWIGLU) or identity (ORC_GLU_PLAIN). */
+int orc_mmvq_glu(const uint8_t *W_gate, const uint8_t *W_up, int type,
+                 int64_t M, int64_t K, const uint8_t *y_q, int64_t n,
+                 int glu_op, double *out);
+
+/* Expert-indexed product: expert e's matrix starts at W + e*expert_stride.
+ * ids holds n_tokens*top_k expert ids, token-major. For token t and slot k,
+ * out[(t*top_k + k)*M + r] = row r of expert ids[t*top_k+k] . column t of
+ * y_q. mag as for orc_mmvq. Returns ORC_ERR_ID for an id outside
+ * 0..n_experts-1. */
+int orc_mmvq_id(const uint8_t *W, int64_t expert_stride, int n_experts,
+                int type, int64_t M, int64_t K, const uint8_t *y_q,
+                int64_t n_tokens, const int32_t *ids, int top_k,
+                double *out, double *mag);
+
+int orc_mmvq_id_glu(const uint8_t *W_gate, const uint8_t *W_up,
+                    int64_t expert_stride, int n_experts, int type,
+                    int64_t M, int64_t K, const uint8_t *y_q,
+                    int64_t n_tokens, const int32_t *ids, int top_k,
+                    int glu_op, double *out);
+
+/* Dequantize one row of K weights to fp64 (w[e] = the weight value of
+ * element e), and one column of q8_1 to fp64 (y[e] = d * q[e]). */
+int orc_dequantize_row(int type, const uint8_t *row, int64_t K, double *w);
+int orc_dequantize_q8_1(const uint8_t *y_q, int64_t K, double *y);
+
+/* The 6-bit scale and min of Q4_K sub-block t (0..7) from the 12 packed
+ * scale bytes. */
+void orc_q4_k_scale_min(const uint8_t *scales, int t, int *sc, int *m);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

@@ -1,0 +1,83 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each case copies ``oracle/mmvq_oracle.c`` to a temporary directory, applies
+one textual change that models a plausible mistake (a dropped term, a wrong
+sign, index or shift, a swapped operand, another rounding rule), builds it
+with gcc and runs the pin suite on it. At least one pin must fail. The
+oracle in the repository is never modified.
+"""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import oracle_pins
+
+MUTATIONS = {
+    "q8_1_ties_to_even": ("(int)roundf(xb[i] / d)", "(int)rintf(xb[i] / d)"),
+    "q8_1_s_without_d": ("const float s = d * (float)sumq;", "const float s = (float)sumq;"),
+    "q8_1_divides_by_fp16_d": ("(int)roundf(xb[i] / d)",
+                               "(int)roundf(xb[i] / (float)orc_f16_to_f64(orc_f32_to_f16(d)))"),
+    "q8_1_scale_128": ("const float d = amax / 127.0f;", "const float d = amax / 128.0f;"),
+    "f16_ties_up": ("return fmod(fl, 2.0) == 0.0 ? fl : fl + 1.0;", "return fl + 1.0;"),
+    "q4_0_nibbles_swapped": ("return e < 16 ? (qs[e] & 0x0F) : (qs[e - 16] >> 4);",
+                             "return e < 16 ? (qs[e] >> 4) : (qs[e - 16] & 0x0F);"),
+    "q4_0_zero_point_7": ("const double t2 = 8.0 * dw * q8_s(ycol, qb);",
+                          "const double t2 = 7.0 * dw * q8_s(ycol, qb);"),
+    "q4_0_no_zero_point": ("const double t2 = 8.0 * dw * q8_s(ycol, qb);",
+                           "const double t2 = 0.0 * dw * q8_s(ycol, qb);"),
+    "q4_k_min_sign": ("const double t2 = dmin * m * d8 * dot2;\n        *acc += t1 - t2;",
+                      "const double t2 = dmin * m * d8 * dot2;\n        *acc += t1 + t2;"),
+    "q4_k_d_dmin_swapped": ("const double dmin = orc_f16_to_f64(rd16(blk + 2));",
+                            "const double dmin = orc_f16_to_f64(rd16(blk));"),
+    "q4_k_scale_high_bits_from_t": ("*sc = (B[t + 4] & 15) | ((B[t - 4] >> 6) << 4);",
+                                    "*sc = (B[t + 4] & 15) | ((B[t] >> 6) << 4);"),
+    "q4_k_min_low_bits_from_scale_byte": ("*m = B[t + 4] & 63;", "*m = B[t] & 63;"),
+    "q4_k_nibble_parity_swapped": ("return (t % 2 == 0) ? (byte & 0x0F) : (byte >> 4);",
+                                   "return (t % 2 == 1) ? (byte & 0x0F) : (byte >> 4);"),
+    "q4_k_chunk_index": ("const uint8_t byte = qs[32 * c + l];",
+                         "const uint8_t byte = qs[32 * (t % 4) + l];"),
+    "q4_k_wrong_q8_block": ("const int qy = q8_q(ycol, qb + t, l);",
+                            "const int qy = q8_q(ycol, qb + (t ^ 1), l);"),
+    "q4_k_field_order": ("const uint8_t *qs = blk + 16;\n    const int t = e / 32",
+                         "const uint8_t *qs = blk + 0;\n    const int t = e / 32"),
+    "q6_k_high_shift": ("const int high = (qh[32 * h + l] >> (2 * g)) & 3;",
+                        "const int high = (qh[32 * h + l] >> g) & 3;"),
+    "q6_k_low_half_select": ("ql[64 * h + 32 * (g % 2) + l]", "ql[64 * h + 32 * (g / 2) + l]"),
+    "q6_k_offset_31": ("isum += (q6_k_code(blk, e) - 32)", "isum += (q6_k_code(blk, e) - 31)"),
+    "q6_k_q8_block_map": ("const int64_t yb = qb + s / 2;", "const int64_t yb = qb + s % 8;"),
+    "q6_k_scale_unsigned": ("return (int8_t)blk[192 + s];", "return blk[192 + s];"),
+    "glu_sigmoid_only": ("return g / (1.0 + exp(-g)) * u;", "return 1.0 / (1.0 + exp(-g)) * u;"),
+    "id_slot_as_token": ("rc = orc_mmvq(We, type, M, K, y_q + t * (K / 32) * 36, 1,",
+                         "rc = orc_mmvq(We, type, M, K, y_q + k * (K / 32) * 36, 1,"),
+    "columns_share_first": ("row_dot(W + r * nb * bb, type, nb, bb, qk, y_q + j * ycol_bytes, &acc, &mg,",
+                            "row_dot(W + r * nb * bb, type, nb, bb, qk, y_q, &acc, &mg,"),
+}
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(oracle.SRC) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(tmp_path, source, name):
+    old, new = MUTATIONS[name]
+    assert source.count(old) == 1, f"mutation anchor for {name} not unique"
+    src = tmp_path / "mmvq_oracle.c"
+    src.write_text(source.replace(old, new))
+    hdr = os.path.join(oracle.HERE, "mmvq_oracle.h")
+    (tmp_path / "mmvq_oracle.h").write_text(open(hdr).read())
+    lib = tmp_path / "libmut.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared",
+                           "-o", str(lib), str(src), "-lm"])
+    mutant = oracle.Oracle(str(lib))
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(mutant)
+        except Exception as e:  # noqa: BLE001 - any failure counts as caught
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"planted mistake {name} passed every pin"
