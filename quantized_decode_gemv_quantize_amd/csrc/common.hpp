@@ -1,0 +1,185 @@
+// common.hpp - device helpers shared by the MMVQ kernels (gfx950, wave64).
+//
+// Cross-lane reduction, raw loads and small integer helpers. Everything here
+// is CDNA4 code: 64-lane wavefronts, DPP row/quad permutes, and the gfx950
+// v_permlane16_swap / v_permlane32_swap instructions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmv {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kMaxCols = 8;
+constexpr int kMaxThreads = 1024;
+
+__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
+// ---------------------------------------------------------------------------
+// Loads. Weights are streamed once, so they are read with the non-temporal
+// hint; activations and headers use ordinary loads.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ u32x4 ld_nt_x4(const uint8_t* p) {   // p 16-byte aligned
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ u32x4 ld_x4(const uint8_t* p) {      // p 4-byte aligned
+  const uint32_t* q = reinterpret_cast<const uint32_t*>(__builtin_assume_aligned(p, 4));
+  u32x4 v;
+  __builtin_memcpy(&v, q, 16);
+  return v;
+}
+__device__ __forceinline__ u32x2 ld_x2(const uint8_t* p) {      // p 4-byte aligned
+  const uint32_t* q = reinterpret_cast<const uint32_t*>(__builtin_assume_aligned(p, 4));
+  u32x2 v;
+  __builtin_memcpy(&v, q, 8);
+  return v;
+}
+__device__ __forceinline__ uint32_t ld_u16(const uint8_t* p) {   // p 2-byte aligned
+  return *reinterpret_cast<const uint16_t*>(__builtin_assume_aligned(p, 2));
+}
+__device__ __forceinline__ uint32_t ld_u32(const uint8_t* p) {   // p 4-byte aligned
+  return *reinterpret_cast<const uint32_t*>(__builtin_assume_aligned(p, 4));
+}
+
+// ({hi, lo} >> 16) as 32 bits: re-aligns a 16-byte run that starts two bytes
+// into a dword.
+__device__ __forceinline__ uint32_t shr16_pair(uint32_t hi, uint32_t lo) {
+  return __builtin_amdgcn_alignbyte(hi, lo, 2);
+}
+
+// fp16 bit pattern (low 16 bits) -> float.
+__device__ __forceinline__ float h2f(uint32_t bits) {
+  _Float16 h = __builtin_bit_cast(_Float16, static_cast<uint16_t>(bits & 0xFFFFu));
+  return static_cast<float>(h);
+}
+
+// 4-way signed int8 dot product with accumulate (v_dot4_i32_i8).
+__device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
+  return __builtin_amdgcn_sdot4(static_cast<int>(a), static_cast<int>(b), c, false);
+}
+
+// 24-bit signed multiply (v_mul_i32_i24); both factors fit in 24 bits here.
+__device__ __forceinline__ int mul24(int a, int b) { return __mul24(a, b); }
+
+// ---------------------------------------------------------------------------
+// Cross-lane exchange
+// ---------------------------------------------------------------------------
+// DPP controls (row = 16 lanes): row_mirror l <-> 15-l, row_half_mirror
+// l <-> 7-l, quad_perm [2,3,0,1] l <-> l^2, quad_perm [1,0,3,2] l <-> l^1.
+constexpr int kDppMirror16 = 0x140;
+constexpr int kDppMirror8 = 0x141;
+constexpr int kDppXor2 = 0x4E;
+constexpr int kDppXor1 = 0xB1;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Partner of a lane across lane bit MASK (8, 4, 2, 1) uses the mirror/perm
+// that flips that bit and keeps all higher bits.
+template <int MASK>
+__device__ __forceinline__ float dpp_partner(float v) {
+  if constexpr (MASK == 8) return dpp_f<kDppMirror16>(v);
+  else if constexpr (MASK == 4) return dpp_f<kDppMirror8>(v);
+  else if constexpr (MASK == 2) return dpp_f<kDppXor2>(v);
+  else return dpp_f<kDppXor1>(v);
+}
+
+// Swap step across lane bit 5 (MASK 32) or 4 (MASK 16) on a pair (a, b):
+// afterwards a lane with the bit clear holds a + partner's a, a lane with the
+// bit set holds b + partner's b.
+template <int MASK>
+__device__ __forceinline__ float swap_pair_sum(float a, float b) {
+  if constexpr (MASK == 32) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Transposed team reduction
+// ---------------------------------------------------------------------------
+// A team of LANES lanes (8, 16, 32 or 64, aligned inside the wave) holds P
+// planes of V partial sums per lane. Summing every value over the team would
+// cost log2(LANES) exchanges per value; instead each exchange step halves the
+// number of values a lane carries: across lane bit b, a lane with b clear
+// keeps the even value of each pair and one with b set the odd value, each
+// adding its partner's copy of the kept value. After S = min(log2 V,
+// log2 LANES) such steps, the remaining steps are plain pairwise sums. Value
+// position i of lane l then holds the team total of value index
+//   i * 2^S + sum_{k<S} bit_{L-1-k}(l) * 2^k      (L = log2 LANES),
+// identical in every lane whose top S bits (within the team) agree. V must be
+// a power of two. Every plane is reduced with the same lane mapping.
+template <int LANES>
+constexpr int log2i() { return LANES <= 1 ? 0 : 1 + log2i<LANES / 2>(); }
+
+// One step across lane bit MASK on the first C values of every plane.
+template <int MASK, int P, int V, int C>
+__device__ __forceinline__ void reduce_step(float (&v)[P][V], int lane) {
+  if constexpr (C > 1) {
+    const bool bit = (lane & MASK) != 0;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+#pragma unroll
+      for (int i = 0; i < C / 2; ++i) {
+        const float a = v[p][2 * i], b = v[p][2 * i + 1];
+        if constexpr (MASK >= 16) {
+          v[p][i] = swap_pair_sum<MASK>(a, b);
+        } else {
+          const float keep = bit ? b : a;
+          const float send = bit ? a : b;
+          v[p][i] = keep + dpp_partner<MASK>(send);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      if constexpr (MASK >= 16) v[p][0] = swap_pair_sum<MASK>(v[p][0], v[p][0]);
+      else v[p][0] = v[p][0] + dpp_partner<MASK>(v[p][0]);
+    }
+  }
+}
+
+template <int MASK, int P, int V, int C>
+__device__ __forceinline__ void reduce_from(float (&v)[P][V], int lane) {
+  if constexpr (MASK >= 1) {
+    reduce_step<MASK, P, V, C>(v, lane);
+    reduce_from<MASK / 2, P, V, (C > 1 ? C / 2 : 1)>(v, lane);
+  }
+}
+
+// Reduces in place; afterwards v[p][0 .. V/2^S) are valid.
+template <int LANES, int P, int V>
+__device__ __forceinline__ void team_reduce(float (&v)[P][V], int lane) {
+  static_assert((V & (V - 1)) == 0, "V must be a power of two");
+  reduce_from<LANES / 2, P, V, V>(v, lane);
+}
+
+template <int LANES, int V>
+struct ReduceMap {
+  static constexpr int L = log2i<LANES>();
+  static constexpr int S = log2i<V>() < L ? log2i<V>() : L;
+  static constexpr int kPerLane = V >> S;       // positions a lane holds
+  // index of the value at position i in the lane with in-team id l
+  __device__ static int index(int l, int i) {
+    int b = 0;
+#pragma unroll
+    for (int k = 0; k < S; ++k) b |= ((l >> (L - 1 - k)) & 1) << k;
+    return (i << S) | b;
+  }
+  // one representative lane per distinct result
+  __device__ static bool representative(int l) { return (l & ((1 << (L - S)) - 1)) == 0; }
+};
+
+constexpr int pow2ceil(int v) { int p = 1; while (p < v) p <<= 1; return p; }
+
+}  // namespace qmv

@@ -1,0 +1,373 @@
+// formats.hpp - GGUF-style weight blocks and the q8_1 activation block, as
+// seen by one lane of the MMVQ kernels.
+//
+// Citations: [MMVQ §X] = page "llama.cpp 源码完全拆解(十四):mul_mat_vec_q——解码时
+// 一条量化权重如何被 dp4a 逐块点积", section X; [GGUF16 §X] = page "GGUF 量化内幕：
+// 第16章 llama.cpp 量化代码架构", section X.
+//
+// Work unit. A row of K weights is cut into units, one per lane of the team
+// that owns the row; a lane keeps the same unit for every row it processes,
+// so it loads the matching activation codes once and keeps them in
+// registers. Units are chosen so that a wave's weight loads for one row are
+// contiguous 16-byte pieces:
+//   Q4_K: unit = 16 bytes of codes of one super-block (32 weights; 8 units
+//         per super-block), plus that super-block's 16-byte header.
+//   Q4_0: unit = one 18-byte block (32 weights).
+//   Q6_K: unit = one quarter of a super-block (64 weights): 2 x 16 bytes of
+//         low bits, 16 bytes of high bits, 4 int8 scales, the fp16 d.
+//
+// Each format provides:
+//   Act           activation registers of one column for the lane's unit
+//   load_act      fill Act from a q8_1 column
+//   Wt            raw weight words of the lane's unit in one row
+//   load_wt       issue the loads of Wt
+//   Dec / decode  per-row decode shared by all columns (codes, scales)
+//   col_dot       the unit's fp32 contribution for one column
+//   int_dots      the unit's integer dots, added into the block's dot array
+//                 (test support: the same decode, no scaling)
+#pragma once
+
+#include "common.hpp"
+
+namespace qmv {
+
+constexpr int kQ8Bytes = 36;     // fp16 d, fp16 s, 32 x int8   [MMVQ §激活的量化]
+
+// q8_1 block fields
+__device__ __forceinline__ float q8_d(const uint8_t* blk) { return h2f(ld_u16(blk)); }
+
+// Sum of the 4 signed bytes of a word, via a dot with 0x01010101 (the pages'
+// trick for the activation sum of a sub-block [MMVQ §一次 vec_dot 的解剖]).
+__device__ __forceinline__ int bsum4(uint32_t w, int c) { return dot4(w, 0x01010101u, c); }
+
+// ===========================================================================
+// Q4_K  [GGUF16 §16.1.2, §16.2.1; MMVQ §权重的排法, §一次 vec_dot 的解剖]
+// 144 bytes: fp16 d @0, fp16 dmin @2, 12 bytes of packed 6-bit scales and
+// mins @4, 128 bytes of nibbles @16. Sub-block t (32 weights) of 64-element
+// chunk c = t/2 reads the low (t even) or high (t odd) nibbles of
+// qs[32c .. 32c+31]. Weight = d*sc_t*q - dmin*m_t.
+// Unit u: super-block sb = u/8, p = u%8, chunk c = p/2, half = p%2; its 16
+// code bytes qs[32c + 16*half ..] hold elements 16*half.. of sub-blocks
+// t0 = 2c (low nibbles) and t1 = 2c+1 (high nibbles).
+// ===========================================================================
+struct Q4K {
+  static constexpr int kType = 12, kQK = 256, kBlockBytes = 144;
+  static constexpr int kUnitsPerBlock = 8, kDotsPerBlock = 16;
+
+  struct Act {
+    uint32_t y0[4], y1[4];   // activation codes paired with the t0 / t1 nibbles
+    float d0, d1;            // q8_1 scales of the two sub-blocks
+    float s0, s1;            // d8 * (sum of the 16 codes): exact in fp32
+  };
+
+  // int sums of the 16 codes of each half sub-block (also used by int_dots)
+  __device__ static void act_codes(const uint8_t* ycol, int u, u32x4& q0, u32x4& q1,
+                                   const uint8_t*& b0, const uint8_t*& b1) {
+    const int sb = u >> 3, p = u & 7, c = p >> 1, half = p & 1;
+    b0 = ycol + static_cast<int64_t>(8 * sb + 2 * c) * kQ8Bytes;
+    b1 = b0 + kQ8Bytes;
+    q0 = ld_x4(b0 + 4 + 16 * half);
+    q1 = ld_x4(b1 + 4 + 16 * half);
+  }
+
+  __device__ static void load_act(Act& a, const uint8_t* ycol, int u) {
+    u32x4 q0, q1;
+    const uint8_t *b0, *b1;
+    act_codes(ycol, u, q0, q1, b0, b1);
+    a.y0[0] = q0.x; a.y0[1] = q0.y; a.y0[2] = q0.z; a.y0[3] = q0.w;
+    a.y1[0] = q1.x; a.y1[1] = q1.y; a.y1[2] = q1.z; a.y1[3] = q1.w;
+    a.d0 = q8_d(b0);
+    a.d1 = q8_d(b1);
+    const int s0 = bsum4(q0.w, bsum4(q0.z, bsum4(q0.y, bsum4(q0.x, 0))));
+    const int s1 = bsum4(q1.w, bsum4(q1.z, bsum4(q1.y, bsum4(q1.x, 0))));
+    a.s0 = a.d0 * static_cast<float>(s0);
+    a.s1 = a.d1 * static_cast<float>(s1);
+  }
+
+  struct Wt {
+    u32x4 qs;    // 16 code bytes
+    u32x4 hdr;   // d | dmin, scales[0..3], scales[4..7], scales[8..11]
+  };
+
+  // row: start of the row (16-byte aligned: 144-byte blocks, 16-byte base)
+  __device__ static void load_wt(Wt& w, const uint8_t* row, int u) {
+    const uint8_t* blk = row + static_cast<int64_t>(u >> 3) * kBlockBytes;
+    w.qs = ld_nt_x4(blk + 16 + 16 * (u & 7));
+    w.hdr = ld_x4(blk);
+  }
+
+  struct Dec {
+    uint32_t lo[4], hi[4];   // nibbles of t0 and t1 as unsigned bytes
+    int sc0, sc1;
+    float m0, m1, d, dmin;
+  };
+
+  // 6-bit scales/mins of sub-blocks t0 = 2c and t1 = 2c+1 as 16-bit pairs
+  // (one per byte), following the pages' branch-free unpack with the scale
+  // words read as little-endian 16-bit words.
+  __device__ static void decode(const Wt& w, Dec& o, int u) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      o.lo[k] = w.qs[k] & 0x0F0F0F0Fu;
+      o.hi[k] = (w.qs[k] >> 4) & 0x0F0F0F0Fu;
+    }
+    o.d = h2f(w.hdr.x);
+    o.dmin = h2f(w.hdr.x >> 16);
+    const int c = (u & 7) >> 1;
+    const uint32_t sh = 16u * (c & 1);
+    const uint32_t H1 = w.hdr.y, H2 = w.hdr.z, H3 = w.hdr.w;
+    uint32_t scp, mp;
+    if (c < 2) {                  // lane-constant: no divergence across rows
+      scp = (H1 >> sh) & 0x3F3Fu;
+      mp = (H2 >> sh) & 0x3F3Fu;
+    } else {
+      scp = ((H3 >> sh) & 0x0F0Fu) | (((H1 >> sh) & 0xC0C0u) >> 2);
+      mp = ((H3 >> (sh + 4)) & 0x0F0Fu) | (((H2 >> sh) & 0xC0C0u) >> 2);
+    }
+    o.sc0 = scp & 0xFF;
+    o.sc1 = (scp >> 8) & 0xFF;
+    o.m0 = static_cast<float>(mp & 0xFF);
+    o.m1 = static_cast<float>((mp >> 8) & 0xFF);
+  }
+
+  __device__ static void nibble_dots(const Dec& o, const Act& a, int& dot0, int& dot1) {
+    dot0 = dot4(o.lo[3], a.y0[3], dot4(o.lo[2], a.y0[2], dot4(o.lo[1], a.y0[1], dot4(o.lo[0], a.y0[0], 0))));
+    dot1 = dot4(o.hi[3], a.y1[3], dot4(o.hi[2], a.y1[2], dot4(o.hi[1], a.y1[1], dot4(o.hi[0], a.y1[0], 0))));
+  }
+
+  // d * (sc0*d8_0*dot0 + sc1*d8_1*dot1) - dmin * (m0*d8_0*S0 + m1*d8_1*S1)
+  __device__ static float col_dot(const Dec& o, const Act& a) {
+    int dot0, dot1;
+    nibble_dots(o, a, dot0, dot1);
+    const float sd = static_cast<float>(mul24(dot0, o.sc0)) * a.d0 +
+                     static_cast<float>(mul24(dot1, o.sc1)) * a.d1;
+    const float sm = o.m0 * a.s0 + o.m1 * a.s1;
+    return o.d * sd - o.dmin * sm;
+  }
+
+  // dots of one super-block: [dot1 of t = 0..7, sum(qy) of t = 0..7]
+  __device__ static void int_dots(const Dec& o, const uint8_t* ycol, int u, int* dots) {
+    Act a;
+    load_act(a, ycol, u);
+    int dot0, dot1;
+    nibble_dots(o, a, dot0, dot1);
+    u32x4 q0, q1;
+    const uint8_t *b0, *b1;
+    act_codes(ycol, u, q0, q1, b0, b1);
+    const int c = (u & 7) >> 1;
+    dots[2 * c] += dot0;
+    dots[2 * c + 1] += dot1;
+    dots[8 + 2 * c] += bsum4(q0.w, bsum4(q0.z, bsum4(q0.y, bsum4(q0.x, 0))));
+    dots[8 + 2 * c + 1] += bsum4(q1.w, bsum4(q1.z, bsum4(q1.y, bsum4(q1.x, 0))));
+  }
+};
+
+// ===========================================================================
+// Q4_0  [MMVQ §权重的排法, §一次 vec_dot 的解剖]
+// 18 bytes: fp16 d @0, qs[16] @2; qs[j] low nibble = element j, high nibble
+// = element j+16. Weight = d*(q-8); per block the product is
+// d*(d8*sum(q*qy) - 8*s). Unit = one block.
+// Blocks are 2-byte aligned: a block at an offset = 2 (mod 4) has its 16
+// code bytes dword aligned; one at 0 (mod 4) has them two bytes into a
+// dword. Both cases read one dword-aligned 16-byte run plus one 16-bit word,
+// all inside the block.
+// ===========================================================================
+struct Q40 {
+  static constexpr int kType = 2, kQK = 32, kBlockBytes = 18;
+  static constexpr int kUnitsPerBlock = 1, kDotsPerBlock = 1;
+
+  struct Act {
+    uint32_t y[8];
+    float d8;
+    float s8;      // 8 * s
+  };
+
+  __device__ static void load_act(Act& a, const uint8_t* ycol, int u) {
+    const uint8_t* b = ycol + static_cast<int64_t>(u) * kQ8Bytes;
+    const u32x4 lo = ld_x4(b + 4), hi = ld_x4(b + 20);
+    a.y[0] = lo.x; a.y[1] = lo.y; a.y[2] = lo.z; a.y[3] = lo.w;
+    a.y[4] = hi.x; a.y[5] = hi.y; a.y[6] = hi.z; a.y[7] = hi.w;
+    const uint32_t ds = ld_u32(b);
+    a.d8 = h2f(ds);
+    a.s8 = 8.0f * h2f(ds >> 16);
+  }
+
+  struct Wt {
+    u32x4 run;       // dword-aligned 16 bytes
+    uint32_t extra;  // 16-bit word: d (odd placement) or qs[14..15]
+    bool odd;        // block offset = 2 (mod 4)
+  };
+
+  __device__ static void load_wt(Wt& w, const uint8_t* row, int u) {
+    const uint8_t* blk = row + static_cast<int64_t>(u) * kBlockBytes;
+    w.odd = (reinterpret_cast<uintptr_t>(blk) & 2u) != 0;
+    w.run = ld_x4(w.odd ? blk + 2 : blk);
+    w.extra = ld_u16(w.odd ? blk : blk + 16);
+  }
+
+  struct Dec {
+    uint32_t lo[4], hi[4];
+    float d;
+  };
+
+  __device__ static void decode(const Wt& w, Dec& o, int) {
+    uint32_t qs[4];
+    qs[0] = w.odd ? w.run.x : shr16_pair(w.run.y, w.run.x);
+    qs[1] = w.odd ? w.run.y : shr16_pair(w.run.z, w.run.y);
+    qs[2] = w.odd ? w.run.z : shr16_pair(w.run.w, w.run.z);
+    qs[3] = w.odd ? w.run.w : shr16_pair(w.extra, w.run.w);
+    o.d = h2f(w.odd ? w.extra : w.run.x);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      o.lo[k] = qs[k] & 0x0F0F0F0Fu;
+      o.hi[k] = (qs[k] >> 4) & 0x0F0F0F0Fu;
+    }
+  }
+
+  __device__ static int isum(const Dec& o, const Act& a) {
+    int s = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) s = dot4(o.lo[k], a.y[k], s);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) s = dot4(o.hi[k], a.y[4 + k], s);
+    return s;
+  }
+
+  __device__ static float col_dot(const Dec& o, const Act& a) {
+    return o.d * (a.d8 * static_cast<float>(isum(o, a)) - a.s8);
+  }
+
+  __device__ static void int_dots(const Dec& o, const uint8_t* ycol, int u, int* dots) {
+    Act a;
+    load_act(a, ycol, u);
+    dots[0] += isum(o, a);
+  }
+};
+
+// ===========================================================================
+// Q6_K  [MMVQ §dp4a, §一次 vec_dot 的解剖]
+// 210 bytes: ql[128] @0 (low 4 bits), qh[64] @128 (high 2 bits), int8
+// sc[16] @192, fp16 d @208. Element 128h + 32g + l (h 0..1, g 0..3, l 0..31):
+// low bits from ql[64h + 32(g%2) + l] (low nibble for g < 2, high nibble
+// otherwise), high bits (qh[32h + l] >> 2g) & 3; sub-block 8h + 2g + l/16;
+// weight = d*sc*(q-32).
+// Unit u: super-block sb = u/4, h = (u/2)%2, lq = u%2 (l in 16lq..16lq+15):
+// pieces A = ql[64h+16lq ..+16], B = ql[64h+32+16lq ..+16],
+// C = qh[32h+16lq ..+16]; sub-blocks 8h + 2g + lq for g = 0..3, each paired
+// with q8_1 block 8sb + 4h + g, codes 16lq..16lq+15.
+// Blocks are 2-byte aligned: as for Q4_0, a piece at an offset = 2 (mod 4)
+// is read as the dword-aligned run starting two bytes earlier plus the
+// piece's last 16-bit word, then re-aligned.
+// ===========================================================================
+struct Q6K {
+  static constexpr int kType = 14, kQK = 256, kBlockBytes = 210;
+  static constexpr int kUnitsPerBlock = 4, kDotsPerBlock = 16;
+
+  struct Act {
+    uint32_t y[4][4];
+    float d8[4];
+    int c32[4];      // 32 * (sum of the 16 codes): the -32 offset term
+  };
+
+  __device__ static const uint8_t* act_block(const uint8_t* ycol, int u, int g) {
+    const int sb = u >> 2, h = (u >> 1) & 1;
+    return ycol + static_cast<int64_t>(8 * sb + 4 * h + g) * kQ8Bytes;
+  }
+
+  __device__ static void load_act(Act& a, const uint8_t* ycol, int u) {
+    const int lq = u & 1;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint8_t* b = act_block(ycol, u, g);
+      const u32x4 q = ld_x4(b + 4 + 16 * lq);
+      a.y[g][0] = q.x; a.y[g][1] = q.y; a.y[g][2] = q.z; a.y[g][3] = q.w;
+      a.d8[g] = q8_d(b);
+      a.c32[g] = 32 * bsum4(q.w, bsum4(q.z, bsum4(q.y, bsum4(q.x, 0))));
+    }
+  }
+
+  struct Wt {
+    u32x4 A, B, C;              // dword-aligned runs
+    uint32_t a2, b2, c2;        // last 16-bit word of each piece
+    u32x2 S;                    // dword-aligned run over the 8 scales
+    uint32_t s2;                // last 16-bit word of the scales
+    uint32_t dbits;
+    bool odd;
+  };
+
+  __device__ static void load_wt(Wt& w, const uint8_t* row, int u) {
+    const int sb = u >> 2, h = (u >> 1) & 1, lq = u & 1;
+    const uint8_t* blk = row + static_cast<int64_t>(sb) * kBlockBytes;
+    w.odd = (reinterpret_cast<uintptr_t>(blk) & 2u) != 0;
+    const uint8_t* b4 = w.odd ? blk - 2 : blk;          // dword aligned
+    const int oA = 64 * h + 16 * lq, oB = oA + 32, oC = 128 + 32 * h + 16 * lq, oS = 192 + 8 * h;
+    w.A = ld_x4(b4 + oA);
+    w.B = ld_x4(b4 + oB);
+    w.C = ld_x4(b4 + oC);
+    w.S = ld_x2(b4 + oS);
+    w.a2 = ld_u16(blk + oA + 14);
+    w.b2 = ld_u16(blk + oB + 14);
+    w.c2 = ld_u16(blk + oC + 14);
+    w.s2 = ld_u16(blk + oS + 6);
+    w.dbits = ld_u16(blk + 208);
+  }
+
+  struct Dec {
+    uint32_t code[4][4];        // 6-bit codes, 4 per word, sub-block g
+    int sc[4];
+    float d;
+  };
+
+  __device__ static void realign(const u32x4& r, uint32_t tail, bool odd, uint32_t (&o)[4]) {
+    o[0] = odd ? shr16_pair(r.y, r.x) : r.x;
+    o[1] = odd ? shr16_pair(r.z, r.y) : r.y;
+    o[2] = odd ? shr16_pair(r.w, r.z) : r.z;
+    o[3] = odd ? shr16_pair(tail, r.w) : r.w;
+  }
+
+  __device__ static void decode(const Wt& w, Dec& o, int u) {
+    uint32_t A[4], B[4], C[4];
+    realign(w.A, w.a2, w.odd, A);
+    realign(w.B, w.b2, w.odd, B);
+    realign(w.C, w.c2, w.odd, C);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      o.code[0][k] = (A[k] & 0x0F0F0F0Fu) | ((C[k] << 4) & 0x30303030u);
+      o.code[1][k] = (B[k] & 0x0F0F0F0Fu) | ((C[k] << 2) & 0x30303030u);
+      o.code[2][k] = ((A[k] >> 4) & 0x0F0F0F0Fu) | (C[k] & 0x30303030u);
+      o.code[3][k] = ((B[k] >> 4) & 0x0F0F0F0Fu) | ((C[k] >> 2) & 0x30303030u);
+    }
+    const uint32_t s0 = w.odd ? shr16_pair(w.S.y, w.S.x) : w.S.x;   // scales 8h+0..3
+    const uint32_t s1 = w.odd ? shr16_pair(w.s2, w.S.y) : w.S.y;    // scales 8h+4..7
+    const int lq = u & 1;
+    o.sc[0] = __builtin_amdgcn_sbfe(s0, 8 * lq, 8);
+    o.sc[1] = __builtin_amdgcn_sbfe(s0, 8 * lq + 16, 8);
+    o.sc[2] = __builtin_amdgcn_sbfe(s1, 8 * lq, 8);
+    o.sc[3] = __builtin_amdgcn_sbfe(s1, 8 * lq + 16, 8);
+    o.d = h2f(w.dbits);
+  }
+
+  __device__ static int isum(const Dec& o, const Act& a, int g) {
+    int s = -a.c32[g];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) s = dot4(o.code[g][k], a.y[g][k], s);
+    return s;
+  }
+
+  __device__ static float col_dot(const Dec& o, const Act& a) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) acc += static_cast<float>(mul24(isum(o, a, g), o.sc[g])) * a.d8[g];
+    return o.d * acc;
+  }
+
+  __device__ static void int_dots(const Dec& o, const uint8_t* ycol, int u, int* dots) {
+    Act a;
+    load_act(a, ycol, u);
+    const int h = (u >> 1) & 1, lq = u & 1;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) dots[8 * h + 2 * g + lq] += isum(o, a, g);
+  }
+};
+
+}  // namespace qmv

@@ -1,0 +1,11 @@
+// kernels_q4_k.hip - instantiates the MMVQ kernels for the Q4_K format.
+#include "launch.hpp"
+
+namespace qmv {
+
+const Dispatch& dispatch_q4_k() {
+  static const Dispatch d = make_dispatch<Q4K>();
+  return d;
+}
+
+}  // namespace qmv

@@ -1,0 +1,171 @@
+// launch.hpp - host-side launch shapes for the MMVQ kernels.
+//
+// Shapes are derived from the problem, not from per-architecture tables:
+//   * team lanes TL = units per row rounded up to whole waves (<= 512);
+//   * rows per team: enough teams for about 16 resident waves per compute
+//     unit, capped by the register budget R of the instantiation;
+//   * teams per workgroup: enough for at least 256 threads when TL < 256.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <atomic>
+
+#include "../../include/mmvq.h"
+#include "mmvq_kernel.hpp"
+
+namespace qmv {
+
+struct Shape {
+  int units, team_lanes, teams_per_block, rows_per_team;
+  int64_t teams, blocks;
+};
+
+// Compute units of the current device (cached per device id).
+inline int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+template <class F>
+inline int units_per_row(int64_t K) {
+  return static_cast<int>(K / F::kQK) * F::kUnitsPerBlock;
+}
+
+// Largest K whose row fits one workgroup's team.
+template <class F>
+inline bool row_fits(int64_t K) {
+  return units_per_row<F>(K) <= kLaunchBound;
+}
+
+template <class F>
+inline Shape make_shape(int64_t M, int64_t K, int rmax) {
+  Shape s;
+  s.units = units_per_row<F>(K);
+  s.team_lanes = (s.units + kWave - 1) / kWave * kWave;
+  const int tw = s.team_lanes / kWave;
+  s.teams_per_block = s.team_lanes >= 256 ? 1 : 256 / s.team_lanes;
+  const int64_t cus = device_cus();
+  const int64_t target_teams = cus * (tw >= 16 ? 1 : 16 / tw);
+  int64_t rpt = (M + target_teams - 1) / target_teams;
+  if (rpt < 1) rpt = 1;
+  if (rpt > rmax) rpt = rmax;
+  s.rows_per_team = static_cast<int>(rpt);
+  s.teams = (M + rpt - 1) / rpt;
+  s.blocks = (s.teams + s.teams_per_block - 1) / s.teams_per_block;
+  return s;
+}
+
+// Rows per pass (register budget) of an instantiation.
+template <class F>
+constexpr int rows_per_pass(int nc, int g) {
+  int r;
+  if (F::kType == 14) r = nc == 1 ? 8 : (nc <= 4 ? 4 : 2);          // Q6_K: 19 words/row
+  else r = nc == 1 ? 16 : (nc <= 4 ? 8 : 4);                         // Q4_K, Q4_0
+  return g == 2 ? (r > 1 ? r / 2 : 1) : r;
+}
+
+template <class F>
+constexpr int id_rows_per_pass(int g) {
+  return F::kType == 14 ? (g == 2 ? 1 : 2) : (g == 2 ? 2 : 4);
+}
+
+inline int check_launch() {
+  return hipGetLastError() == hipSuccess ? MMVQ_OK : MMVQ_ERR_LAUNCH;
+}
+
+template <class F, int NC, int G>
+inline int launch_rows_nc(RowArgs a, int64_t K, hipStream_t st) {
+  constexpr int R = rows_per_pass<F>(NC, G);
+  const Shape s = make_shape<F>(a.M, K, R);
+  a.units = s.units;
+  a.team_lanes = s.team_lanes;
+  a.rows_per_team = s.rows_per_team;
+  hipLaunchKernelGGL((mmvq_rows_kernel<F, NC, R, G>), dim3(static_cast<unsigned>(s.blocks)),
+                     dim3(s.teams_per_block * s.team_lanes), 0, st, a);
+  return check_launch();
+}
+
+template <class F, int G>
+inline int launch_rows(const RowArgs& a, int64_t K, int64_t n, hipStream_t st) {
+  switch (n) {
+    case 1: return launch_rows_nc<F, 1, G>(a, K, st);
+    case 2: return launch_rows_nc<F, 2, G>(a, K, st);
+    case 3: return launch_rows_nc<F, 3, G>(a, K, st);
+    case 4: return launch_rows_nc<F, 4, G>(a, K, st);
+    case 5: return launch_rows_nc<F, 5, G>(a, K, st);
+    case 6: return launch_rows_nc<F, 6, G>(a, K, st);
+    case 7: return launch_rows_nc<F, 7, G>(a, K, st);
+    case 8: return launch_rows_nc<F, 8, G>(a, K, st);
+    default: return MMVQ_ERR_SHAPE;
+  }
+}
+
+template <class F, int G>
+inline int launch_id(RowArgs a, int64_t K, int n_experts, hipStream_t st) {
+  constexpr int R = id_rows_per_pass<F>(G);
+  const Shape s = make_shape<F>(a.M, K, R);
+  a.units = s.units;
+  a.team_lanes = s.team_lanes;
+  a.rows_per_team = s.rows_per_team;
+  hipLaunchKernelGGL((mmvq_id_kernel<F, R, G>),
+                     dim3(static_cast<unsigned>(s.blocks), static_cast<unsigned>(n_experts)),
+                     dim3(s.teams_per_block * s.team_lanes), 0, st, a);
+  return check_launch();
+}
+
+template <class F>
+inline int launch_block_dots(const uint8_t* W, const uint8_t* y, int32_t* dots, int64_t M, int64_t K,
+                             int64_t n, hipStream_t st) {
+  const int64_t nblocks = K / F::kQK;
+  const int64_t total = n * M * nblocks;
+  const int64_t row_bytes = nblocks * F::kBlockBytes;
+  const int64_t ycol_bytes = K / 32 * kQ8Bytes;
+  const int64_t grid = (total + 255) / 256;
+  hipLaunchKernelGGL(mmvq_block_dots_kernel<F>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st,
+                     W, y, dots, M, nblocks, row_bytes, ycol_bytes, n);
+  return check_launch();
+}
+
+// Per-format entry points (one translation unit per format).
+struct Dispatch {
+  int (*rows)(const RowArgs&, int64_t K, int64_t n, hipStream_t);
+  int (*rows_glu)(const RowArgs&, int64_t K, int64_t n, hipStream_t);
+  int (*id)(const RowArgs&, int64_t K, int n_experts, hipStream_t);
+  int (*id_glu)(const RowArgs&, int64_t K, int n_experts, hipStream_t);
+  int (*block_dots)(const uint8_t*, const uint8_t*, int32_t*, int64_t, int64_t, int64_t, hipStream_t);
+  int qk, block_bytes, units_per_block;
+};
+
+template <class F>
+Dispatch make_dispatch() {
+  Dispatch d;
+  d.rows = [](const RowArgs& a, int64_t K, int64_t n, hipStream_t s) { return launch_rows<F, 1>(a, K, n, s); };
+  d.rows_glu = [](const RowArgs& a, int64_t K, int64_t n, hipStream_t s) { return launch_rows<F, 2>(a, K, n, s); };
+  d.id = [](const RowArgs& a, int64_t K, int e, hipStream_t s) { return launch_id<F, 1>(a, K, e, s); };
+  d.id_glu = [](const RowArgs& a, int64_t K, int e, hipStream_t s) { return launch_id<F, 2>(a, K, e, s); };
+  d.block_dots = launch_block_dots<F>;
+  d.qk = F::kQK;
+  d.block_bytes = F::kBlockBytes;
+  d.units_per_block = F::kUnitsPerBlock;
+  return d;
+}
+
+const Dispatch& dispatch_q4_0();
+const Dispatch& dispatch_q4_k();
+const Dispatch& dispatch_q6_k();
+
+int launch_quantize_q8_1(const float* x, uint8_t* y, int64_t K, int64_t n, int64_t ldx, hipStream_t st);
+
+}  // namespace qmv

@@ -1,0 +1,281 @@
+// mmvq_kernel.hpp - the quantized mat-vec kernels for gfx950.
+//
+// Citations: [MMVQ §X] = page "llama.cpp 源码完全拆解(十四):mul_mat_vec_q——解码时
+// 一条量化权重如何被 dp4a 逐块点积", section X.
+//
+// Decomposition (CDNA4-first, not the pages' warp-per-K-slice tiling):
+//   * A team of TL lanes (a whole number of waves) owns a row: lane i of the
+//     team always handles unit i of the row (see formats.hpp), so it loads
+//     its slice of the activation once and keeps it in registers for every
+//     row and column. Weight reuse is 1, so weights never touch LDS.
+//   * A team owns up to R consecutive rows. It issues the weight loads of
+//     all its rows before any arithmetic (branch-free: rows past the end are
+//     clamped and their results dropped), so each wave has R x 32 bytes per
+//     lane in flight and the whole matrix is requested early.
+//   * Per row the lane decodes its unit once and forms one fp32 partial per
+//     activation column with v_dot4_i32_i8 integer dots; scales are applied
+//     per block after the integer dot [MMVQ §一次 vec_dot 的解剖].
+//   * The R x n partials of every lane are summed over the team with a
+//     transposed reduction (common.hpp): each exchange halves the values a
+//     lane carries, then waves combine through LDS and one lane per output
+//     applies the epilogue and stores [MMVQ §归约与写出, §融合].
+//   * G = 1 plain product; G = 2 fused gate/up: both weight streams are
+//     read in the same pass and the GLU is applied in the epilogue.
+//   * Expert-indexed mode: blockIdx.y is the expert; the block gathers the
+//     tokens routed to it (at most 8) and reads that expert's rows once for
+//     all of them [MMVQ §MoE].
+#pragma once
+
+#include "common.hpp"
+#include "formats.hpp"
+
+namespace qmv {
+
+constexpr int kLaunchBound = 512;       // 8 waves per workgroup at most
+constexpr int kMaxWavesPerBlock = kLaunchBound / kWave;
+
+struct RowArgs {
+  const uint8_t* W;          // up / plain weights (expert 0 in id mode)
+  const uint8_t* Wg;         // gate weights (G = 2)
+  const uint8_t* y;          // q8_1 columns
+  float* out;
+  const int32_t* ids;        // id mode: n_tokens x top_k
+  int64_t M;
+  int64_t row_bytes;
+  int64_t ycol_bytes;
+  int64_t expert_stride;
+  int units;                 // units per row
+  int team_lanes;            // TL: multiple of 64
+  int rows_per_team;         // <= R
+  int glu_op;                // 0 plain product, 1 silu(gate) * up
+  int n_tokens;              // id mode
+  int top_k;                 // id mode
+};
+
+__device__ __forceinline__ float glu(int op, float gate, float up) {
+  if (op == 1) return gate / (1.0f + __expf(-gate)) * up;
+  return gate * up;
+}
+
+// Column descriptor: which q8_1 column feeds activation slot j, and where
+// its results go (one output slot per column in plain mode; in id mode a
+// token may feed several slots of the same expert, bitmask over k).
+struct Cols {
+  int n;                       // active columns
+  int tok[kMaxCols];
+  uint64_t slots[kMaxCols];    // id mode: bit k set -> out slot tok*top_k + k
+};
+
+// LDS for the cross-wave step: G planes x waves x (values per lane group).
+template <int G, int V>
+struct RedLds {
+  float v[G][kMaxWavesPerBlock * V];
+};
+
+template <class F, int NC, int R, int G, bool ID, int VMAX>
+__device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
+                                          const uint8_t* Wbase, const uint8_t* Wgbase,
+                                          RedLds<G, VMAX>& red) {
+  constexpr int V = pow2ceil(NC * R);
+  static_assert(V <= VMAX, "LDS sized for fewer values");
+  const int tid = threadIdx.x;
+  const int TL = a.team_lanes;
+  const int team_local = tid / TL;
+  const int lt = tid - team_local * TL;                 // unit index
+  const int teams_per_block = blockDim.x / TL;
+  const int64_t team = static_cast<int64_t>(blockIdx.x) * teams_per_block + team_local;
+  const int64_t row0 = team * a.rows_per_team;
+  const bool active = lt < a.units;
+  const int u = active ? lt : a.units - 1;              // idle lanes re-read a valid unit
+  const int lane = lane_id();
+
+  // ---- issue all weight loads of this team's rows -----------------------
+  typename F::Wt w[R];
+  typename F::Wt wg[G == 2 ? R : 1];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    int64_t r = row0 + (i < a.rows_per_team ? i : 0);
+    r = r < a.M ? r : a.M - 1;
+    F::load_wt(w[i], Wbase + r * a.row_bytes, u);
+    if constexpr (G == 2) F::load_wt(wg[i], Wgbase + r * a.row_bytes, u);
+  }
+  // ---- activation slice of every column ----------------------------------
+  typename F::Act act[NC];
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    const int t = (!ID || j < cols.n) ? cols.tok[j] : cols.tok[0];
+    F::load_act(act[j], a.y + t * a.ycol_bytes, u);
+  }
+
+  // ---- per row: decode once, one partial per column ----------------------
+  float part[G][V];
+#pragma unroll
+  for (int p = 0; p < G; ++p)
+#pragma unroll
+    for (int k = 0; k < V; ++k) part[p][k] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    typename F::Dec dec;
+    F::decode(w[i], dec, u);
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      const float v = F::col_dot(dec, act[j]);
+      part[0][j * R + i] = active ? v : 0.0f;
+    }
+    if constexpr (G == 2) {
+      F::decode(wg[i], dec, u);
+#pragma unroll
+      for (int j = 0; j < NC; ++j) {
+        const float v = F::col_dot(dec, act[j]);
+        part[1][j * R + i] = active ? v : 0.0f;
+      }
+    }
+  }
+
+  // ---- reduce over the team ----------------------------------------------
+  team_reduce<kWave, G, V>(part, lane);
+  using RM = ReduceMap<kWave, V>;
+
+  auto store = [&](int idx, float up, float gate) {
+    const int j = idx / R, i = idx - j * R;
+    if (j >= NC || i >= a.rows_per_team) return;
+    if (ID && j >= cols.n) return;
+    const int64_t r = row0 + i;
+    if (r >= a.M) return;
+    const float v = (G == 2) ? glu(a.glu_op, gate, up) : up;
+    if constexpr (ID) {
+      // select column j's token and slots with compile-time indices
+      uint64_t m = 0;
+      int t = 0;
+#pragma unroll
+      for (int jj = 0; jj < NC; ++jj)
+        if (jj == j) { m = cols.slots[jj]; t = cols.tok[jj]; }
+      while (m) {
+        const int k = __builtin_ctzll(m);
+        m &= m - 1;
+        a.out[(static_cast<int64_t>(t) * a.top_k + k) * a.M + r] = v;
+      }
+    } else {
+      a.out[static_cast<int64_t>(j) * a.M + r] = v;
+    }
+  };
+
+  if (TL == kWave) {
+    if (RM::representative(lane)) {
+#pragma unroll
+      for (int pos = 0; pos < RM::kPerLane; ++pos) {
+        const int idx = RM::index(lane, pos);
+        store(idx, part[0][pos], G == 2 ? part[G - 1][pos] : 0.0f);
+      }
+    }
+  } else {
+    const int wave = tid / kWave;
+    if (RM::representative(lane)) {
+#pragma unroll
+      for (int pos = 0; pos < RM::kPerLane; ++pos) {
+        const int idx = RM::index(lane, pos);
+#pragma unroll
+        for (int p = 0; p < G; ++p) red.v[p][wave * V + idx] = part[p][pos];
+      }
+    }
+    __syncthreads();
+    const int tw = TL / kWave;
+    const int wave0 = team_local * tw;
+    for (int idx = lt; idx < NC * R; idx += TL) {
+      float s[G];
+#pragma unroll
+      for (int p = 0; p < G; ++p) {
+        s[p] = 0.0f;
+        for (int k = 0; k < tw; ++k) s[p] += red.v[p][(wave0 + k) * V + idx];
+      }
+      store(idx, s[0], s[G - 1]);
+    }
+  }
+}
+
+// Plain / fused kernel: columns 0..NC-1 of y.
+template <class F, int NC, int R, int G>
+__global__ void __launch_bounds__(kLaunchBound) mmvq_rows_kernel(RowArgs a) {
+  Cols cols;
+  cols.n = NC;
+#pragma unroll
+  for (int j = 0; j < kMaxCols; ++j) { cols.tok[j] = j; cols.slots[j] = 0; }
+  constexpr int V = pow2ceil(NC * R);
+  __shared__ RedLds<G, V> red;
+  rows_body<F, NC, R, G, false, V>(a, cols, a.W, a.Wg, red);
+}
+
+// Expert-indexed kernel: blockIdx.y = expert. The token list is the same for
+// every thread of the block (ids are read with uniform addresses).
+template <class F, int R, int G>
+__global__ void __launch_bounds__(kLaunchBound) mmvq_id_kernel(RowArgs a) {
+  const int e = blockIdx.y;
+  // Tokens routed to expert e, compacted with compile-time indices only (a
+  // runtime index into a register array would go through scratch memory).
+  uint64_t m[kMaxCols];
+#pragma unroll
+  for (int t = 0; t < kMaxCols; ++t) {
+    m[t] = 0;
+    if (t < a.n_tokens)
+      for (int k = 0; k < a.top_k; ++k)
+        if (a.ids[t * a.top_k + k] == e) m[t] |= 1ull << k;
+  }
+  Cols cols;
+  cols.n = 0;
+#pragma unroll
+  for (int j = 0; j < kMaxCols; ++j) { cols.tok[j] = 0; cols.slots[j] = 0; }
+#pragma unroll
+  for (int t = 0; t < kMaxCols; ++t) {
+    if (m[t]) {
+#pragma unroll
+      for (int j = 0; j < kMaxCols; ++j)
+        if (j == cols.n) { cols.tok[j] = t; cols.slots[j] = m[t]; }
+      ++cols.n;
+    }
+  }
+  if (cols.n == 0) return;     // uniform: the whole block leaves together
+  const uint8_t* We = a.W + static_cast<int64_t>(e) * a.expert_stride;
+  const uint8_t* Wge = G == 2 ? a.Wg + static_cast<int64_t>(e) * a.expert_stride : nullptr;
+  constexpr int VMAX = pow2ceil(kMaxCols * R);
+  __shared__ RedLds<G, VMAX> red;
+  switch (cols.n) {
+    case 1: rows_body<F, 1, R, G, true, VMAX>(a, cols, We, Wge, red); break;
+    case 2: rows_body<F, 2, R, G, true, VMAX>(a, cols, We, Wge, red); break;
+    case 3: rows_body<F, 3, R, G, true, VMAX>(a, cols, We, Wge, red); break;
+    case 4: rows_body<F, 4, R, G, true, VMAX>(a, cols, We, Wge, red); break;
+    case 5: rows_body<F, 5, R, G, true, VMAX>(a, cols, We, Wge, red); break;
+    case 6: rows_body<F, 6, R, G, true, VMAX>(a, cols, We, Wge, red); break;
+    case 7: rows_body<F, 7, R, G, true, VMAX>(a, cols, We, Wge, red); break;
+    default: rows_body<F, 8, R, G, true, VMAX>(a, cols, We, Wge, red); break;
+  }
+}
+
+// Test support: integer dots of every (column, row, block), one thread per
+// (column, row, block), through the same load/decode routines.
+template <class F>
+__global__ void __launch_bounds__(256) mmvq_block_dots_kernel(const uint8_t* W, const uint8_t* y,
+                                                              int32_t* dots, int64_t M, int64_t nblocks,
+                                                              int64_t row_bytes, int64_t ycol_bytes,
+                                                              int64_t n) {
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= n * M * nblocks) return;
+  const int64_t b = gid % nblocks;
+  const int64_t r = (gid / nblocks) % M;
+  const int64_t j = gid / (nblocks * M);
+  int acc[F::kDotsPerBlock];
+#pragma unroll
+  for (int k = 0; k < F::kDotsPerBlock; ++k) acc[k] = 0;
+  for (int q = 0; q < F::kUnitsPerBlock; ++q) {
+    const int u = static_cast<int>(b) * F::kUnitsPerBlock + q;
+    typename F::Wt w;
+    F::load_wt(w, W + r * row_bytes, u);
+    typename F::Dec dec;
+    F::decode(w, dec, u);
+    F::int_dots(dec, y + j * ycol_bytes, u, acc);
+  }
+  int32_t* o = dots + gid * F::kDotsPerBlock;
+#pragma unroll
+  for (int k = 0; k < F::kDotsPerBlock; ++k) o[k] = acc[k];
+}
+
+}  // namespace qmv

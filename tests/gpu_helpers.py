@@ -1,0 +1,97 @@
+"""Shared helpers of the GPU parity tests: device transfer, the oracle
+comparison with the stated tolerances, and case announcements (printed and
+flushed before each GPU step so a failing run names its case)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle
+from quantized_decode_gemv_quantize_amd import binding as B
+
+# |gpu - oracle| <= REL * A + ABS, with A the sum of |block contributions|.
+REL, ABS = 1e-5, 1e-6
+
+
+def announce(msg: str) -> None:
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def dev(a: np.ndarray):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+
+
+def host(t) -> np.ndarray:
+    import torch
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def gpu_quantize(x: np.ndarray, K: int | None = None):
+    """x float32 [n, ldx] -> device q8_1 [n, K/32*36] (uint8)."""
+    import torch
+    xd = dev(x.astype(np.float32))
+    n, ldx = x.shape
+    K = ldx if K is None else K
+    y = torch.zeros((n, K // 32 * 36), dtype=torch.uint8, device="cuda:0")
+    B.mmvq_quantize_q8_1(xd, K, n, ldx, y)
+    return y
+
+
+def gpu_gemv(Wd, wtype, M, K, yd, n):
+    import torch
+    out = torch.full((n, M), float("nan"), dtype=torch.float32, device="cuda:0")
+    B.mmvq(Wd, wtype, M, K, yd, n, out)
+    return host(out)
+
+
+def assert_close(got: np.ndarray, ref: np.ndarray, mag: np.ndarray, what: str) -> None:
+    got = np.asarray(got, dtype=np.float64)
+    tol = REL * mag + ABS
+    err = np.abs(got - ref)
+    bad = ~(err <= tol)           # also catches NaN
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        raise AssertionError(
+            f"{what}: {int(bad.sum())} of {bad.size} outside |d| <= {REL}*A + {ABS}; first at "
+            f"{tuple(int(v) for v in i)}: gpu {got[tuple(i)]!r} oracle {ref[tuple(i)]!r} "
+            f"A {mag[tuple(i)]!r} (max err/tol {float(np.max(err / tol)):.3g})")
+
+
+def glu_tolerance(g, u, mg, mu, out, op):
+    """Bound for act(g)*u given per-dot bounds tg, tu of g and u:
+    |d(act(g)*u)| <= |act'(g)|*|u|*tg + |act(g)|*tu + (GPU exp) 1e-6*|out| + ABS,
+    with |silu'| <= 1.1 and act' = 1 for the plain product."""
+    tg = REL * mg + ABS
+    tu = REL * mu + ABS
+    if op == B.GLU_SWIGLU:
+        act = g / (1.0 + np.exp(-g))
+        dact = 1.1
+    else:
+        act = g
+        dact = 1.0
+    return dact * np.abs(u) * tg + np.abs(act) * tu + 1e-6 * np.abs(out) + ABS
+
+
+def sample_rows(M: int, count: int, seed: int) -> list[tuple[int, int]]:
+    """Contiguous row ranges covering the first and last rows and random
+    interior spans (several teams each)."""
+    rng = np.random.default_rng(seed)
+    span = max(1, min(M, count // 4))
+    starts = {0, max(0, M - span)}
+    while len(starts) < 4 and len(starts) < M:
+        starts.add(int(rng.integers(0, max(1, M - span))))
+    return sorted((s, min(M, s + span)) for s in starts)
+
+
+def oracle_rows(O: oracle.Oracle, W, wtype, M, K, y, n, ranges):
+    out = np.full((n, M), np.nan)
+    mag = np.full((n, M), np.nan)
+    for r0, r1 in ranges:
+        o, m, _ = O.mmvq(W, wtype, M, K, y, n, rows=(r0, r1))
+        out[:, r0:r1] = o[:, r0:r1]
+        mag[:, r0:r1] = m[:, r0:r1]
+    return out, mag

@@ -1,0 +1,98 @@
+"""The C-ABI library without a GPU: it loads, exports every function that
+include/mmvq.h declares, reports the block geometry, and rejects invalid
+arguments with the documented codes before touching any device (argument
+checks run on the host and enqueue nothing)."""
+import ctypes
+
+import pytest
+
+from quantized_decode_gemv_quantize_amd import binding as B
+
+
+@pytest.fixture(scope="module")
+def L():
+    return B.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = B.declared_symbols()
+    assert set(names) == {"mmvq_type_info", "mmvq_quantize_q8_1", "mmvq", "mmvq_glu", "mmvq_id",
+                          "mmvq_id_glu", "mmvq_block_dots", "mmvq_strerror"}
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_type_info():
+    assert B.mmvq_type_info(B.Q4_0) == (32, 18)
+    assert B.mmvq_type_info(B.Q4_K) == (256, 144)
+    assert B.mmvq_type_info(B.Q6_K) == (256, 210)
+    assert B.mmvq_type_info(B.Q8_1) == (32, 36)
+    with pytest.raises(B.MMVQError) as e:
+        B.mmvq_type_info(3)
+    assert e.value.code == B.ERR_TYPE
+    assert B.lib().mmvq_type_info(B.Q4_K, None, None) == 0
+
+
+def test_strerror(L):
+    for code in (0, -1, -2, -3, -4, -5, -99):
+        assert isinstance(B.mmvq_strerror(code), str) and B.mmvq_strerror(code)
+
+
+# Fake, never dereferenced addresses: validation fails before any device work.
+P16, P4 = 1 << 20, (1 << 20) + 4
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, B.Q4_K, 1, 256, P16, 1, P16), B.ERR_NULL),
+    ((P16, B.Q4_K, 1, 256, None, 1, P16), B.ERR_NULL),
+    ((P16, B.Q4_K, 1, 256, P16, 1, None), B.ERR_NULL),
+    ((P16, 7, 1, 256, P16, 1, P16), B.ERR_TYPE),
+    ((P16, B.Q8_1, 1, 256, P16, 1, P16), B.ERR_TYPE),
+    ((P16, B.Q4_K, 1, 200, P16, 1, P16), B.ERR_SHAPE),
+    ((P16, B.Q4_0, 1, 48, P16, 1, P16), B.ERR_SHAPE),
+    ((P16, B.Q4_K, 0, 256, P16, 1, P16), B.ERR_SHAPE),
+    ((P16, B.Q4_K, 1, 256, P16, 0, P16), B.ERR_SHAPE),
+    ((P16, B.Q4_K, 1, 256, P16, 9, P16), B.ERR_SHAPE),
+    ((P16, B.Q4_K, 1, 256 * 65, P16, 1, P16), B.ERR_SHAPE),
+    ((P16, B.Q6_K, 1, 256 * 129, P16, 1, P16), B.ERR_SHAPE),
+    ((P4, B.Q4_K, 1, 256, P16, 1, P16), B.ERR_ALIGN),
+    ((P16, B.Q4_K, 1, 256, P4, 1, P16), B.ERR_ALIGN),
+    ((P16, B.Q4_K, 1, 256, P16, 1, P16 + 2), B.ERR_ALIGN),
+])
+def test_mmvq_argument_checks(L, args, code):
+    assert L.mmvq(*args, None) == code
+
+
+def test_other_entry_points_argument_checks(L):
+    assert L.mmvq_glu(None, P16, B.Q4_K, 1, 256, P16, 1, 1, P16, None) == B.ERR_NULL
+    assert L.mmvq_glu(P16, P16, B.Q4_K, 1, 256, P16, 1, 2, P16, None) == B.ERR_TYPE
+    assert L.mmvq_glu(P4, P16, B.Q4_K, 1, 256, P16, 1, 1, P16, None) == B.ERR_ALIGN
+    assert L.mmvq_id(P16, 288, 4, B.Q4_K, 2, 256, P16, 1, None, 1, P16, None) == B.ERR_NULL
+    assert L.mmvq_id(P16, 144, 4, B.Q4_K, 2, 256, P16, 1, P16, 1, P16, None) == B.ERR_SHAPE
+    assert L.mmvq_id(P16, 288, 4, B.Q4_K, 2, 256, P16, 1, P16, 5, P16, None) == B.ERR_SHAPE
+    assert L.mmvq_id(P16, 288, 4, B.Q4_K, 2, 256, P16, 9, P16, 1, P16, None) == B.ERR_SHAPE
+    assert L.mmvq_id(P16, 296, 4, B.Q4_K, 2, 256, P16, 1, P16, 1, P16, None) == B.ERR_ALIGN
+    assert L.mmvq_id(P16, 288, 0, B.Q4_K, 2, 256, P16, 1, P16, 1, P16, None) == B.ERR_SHAPE
+    assert L.mmvq_id_glu(None, P16, 288, 4, B.Q4_K, 2, 256, P16, 1, P16, 1, 1, P16, None) == B.ERR_NULL
+    assert L.mmvq_id_glu(P16, P16, 288, 4, B.Q4_K, 2, 256, P16, 1, P16, 1, 3, P16, None) == B.ERR_TYPE
+    assert L.mmvq_block_dots(P16, B.Q4_K, 1, 100, P16, 1, P16, None) == B.ERR_SHAPE
+    assert L.mmvq_quantize_q8_1(None, 32, 1, 32, P16, None) == B.ERR_NULL
+    assert L.mmvq_quantize_q8_1(P16, 33, 1, 33, P16, None) == B.ERR_SHAPE
+    assert L.mmvq_quantize_q8_1(P16, 32, 1, 16, P16, None) == B.ERR_SHAPE
+    assert L.mmvq_quantize_q8_1(P16, 32, 9, 32, P16, None) == B.ERR_SHAPE
+    assert L.mmvq_quantize_q8_1(P16 + 2, 32, 1, 32, P16, None) == B.ERR_ALIGN
+    assert L.mmvq_quantize_q8_1(P16, 32, 1, 32, P4, None) == B.ERR_ALIGN
+
+
+def test_binding_raises_with_code():
+    with pytest.raises(B.MMVQError) as e:
+        B.mmvq(P16, B.Q4_K, 1, 200, P16, 1, P16, stream=0)
+    assert e.value.code == B.ERR_SHAPE and "invalid shape" in str(e.value)
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "LIB", str(tmp_path / "absent.so"))
+    monkeypatch.setattr(B, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        B.lib()
+    assert ctypes  # keep import used

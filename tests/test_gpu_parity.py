@@ -1,0 +1,332 @@
+"""GPU parity: the HIP library through its C ABI against the CPU oracle.
+
+Bit-exact: q8_1 bytes (codes, fp16 d and s) and every per-block integer dot.
+fp32 outputs: |gpu - oracle| <= 1e-5 * A + 1e-6 per output, A = sum of the
+absolute values of the per-block terms (the oracle reports it); the GLU
+bound propagates the two dot bounds through act(g) * u.
+
+Inputs come from the seeded generator shared with the benchmark
+(quantized_decode_gemv_quantize_amd.synth); nothing here is computed by the
+GPU path and then trusted.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import (announce, assert_close, dev, glu_tolerance, gpu_gemv, gpu_quantize, host,
+                         oracle_rows, sample_rows)
+from quantized_decode_gemv_quantize_amd import binding as B
+from quantized_decode_gemv_quantize_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+Q4_0, Q4_K, Q6_K = B.Q4_0, B.Q4_K, B.Q6_K
+TNAME = {Q4_0: "q4_0", Q4_K: "q4_k", Q6_K: "q6_k"}
+
+
+@pytest.fixture(scope="module")
+def O():
+    return oracle.default()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+
+
+def special_x(K: int, n: int, seed: int, ldx: int | None = None) -> np.ndarray:
+    """N(0,1) activations with some blocks replaced by edge cases: all zero,
+    exact .5 ties at d = 1, fp32 subnormals, large values (s overflows fp16),
+    a single nonzero element, constant blocks."""
+    rng = np.random.default_rng(seed)
+    x = synth.activations(K, n, rng, ldx)
+    nb = K // 32
+    for j in range(n):
+        for b in range(nb):
+            kind = (b + 3 * j) % 9
+            blk = x[j, 32 * b:32 * b + 32]
+            if kind == 1:
+                blk[:] = 0
+            elif kind == 2:
+                blk[:] = (rng.integers(-100, 100, 32) + 0.5).astype(np.float32)
+                blk[0] = 127.0
+            elif kind == 3:
+                blk[:] = rng.standard_normal(32).astype(np.float32) * np.float32(1e-40)
+            elif kind == 4:
+                blk[:] = rng.standard_normal(32).astype(np.float32) * np.float32(3e4)
+            elif kind == 5:
+                blk[:] = 0
+                blk[int(rng.integers(0, 32))] = -7.25
+            elif kind == 6:
+                blk[:] = 2.0
+    return x
+
+
+# ---------------------------------------------------------------------------
+# q8_1 quantization: bit-exact
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("K,n,ldx", [(32, 1, 32), (1024, 1, 1024), (4096, 3, 4160), (256, 2, 301),
+                                     (14336, 8, 14336), (4096, 1, 4096)])
+def test_quantize_bitexact(O, K, n, ldx):
+    announce(f"quantize K={K} n={n} ldx={ldx}")
+    x = special_x(K, n, seed=K + n, ldx=ldx)
+    y = host(gpu_quantize(x, K))
+    ref = O.quantize_q8_1(x, K)
+    if not np.array_equal(y, ref):
+        bad = np.argwhere(y != ref)[0]
+        j, byte = int(bad[0]), int(bad[1])
+        raise AssertionError(f"column {j} block {byte // 36} byte {byte % 36}: "
+                             f"gpu {y[j, byte]} oracle {ref[j, byte]}")
+
+
+# ---------------------------------------------------------------------------
+# Integer block dots: bit-exact
+# ---------------------------------------------------------------------------
+DOT_CASES = [(Q4_0, 37, 96, 2), (Q4_0, 5, 1024, 1), (Q4_0, 7, 32, 3), (Q4_K, 37, 512, 3),
+             (Q4_K, 3, 4096, 1), (Q6_K, 37, 768, 2), (Q6_K, 9, 256, 1), (Q6_K, 3, 4096, 1)]
+
+
+@pytest.mark.parametrize("wtype,M,K,n", DOT_CASES,
+                         ids=[f"{TNAME[c[0]]}-{c[1]}x{c[2]}-n{c[3]}" for c in DOT_CASES])
+def test_block_dots_bitexact(O, wtype, M, K, n):
+    import torch
+    announce(f"block_dots {TNAME[wtype]} M={M} K={K} n={n}")
+    rng = np.random.default_rng(7 * M + K)
+    W = synth.weights(wtype, M, K, rng)
+    x = synth.activations(K, n, rng)
+    y = O.quantize_q8_1(x)
+    _, _, ref = O.mmvq(W, wtype, M, K, y, n, want_dots=True)
+    dots = torch.zeros(ref.shape, dtype=torch.int32, device="cuda:0")
+    B.mmvq_block_dots(dev(W), wtype, M, K, dev(y), n, dots)
+    got = host(dots)
+    if not np.array_equal(got, ref):
+        i = tuple(int(v) for v in np.argwhere(got != ref)[0])
+        raise AssertionError(f"dot {i}: gpu {got[i]} oracle {ref[i]}")
+
+
+# ---------------------------------------------------------------------------
+# GEMV: all rows, shapes spanning several teams and ragged tails
+# ---------------------------------------------------------------------------
+SHAPES = {
+    Q4_0: [(1, 32), (37, 96), (300, 1024), (1000, 4096), (129, 16384)],
+    Q4_K: [(1, 256), (37, 512), (300, 2304), (1000, 4096), (129, 16384)],
+    Q6_K: [(1, 256), (37, 768), (300, 4096), (129, 32768)],
+}
+GEMV_CASES = [(t, M, K, n) for t, shapes in SHAPES.items() for (M, K) in shapes
+              for n in (1, 2, 3, 5, 8)]
+GEMV_CASES += [(Q4_K, 1000, 4096, 4), (Q4_K, 1000, 4096, 6), (Q4_K, 1000, 4096, 7),
+               (Q4_0, 300, 1024, 4), (Q6_K, 300, 4096, 4), (Q6_K, 300, 4096, 7)]
+
+
+@pytest.mark.parametrize("wtype,M,K,n", GEMV_CASES,
+                         ids=[f"{TNAME[c[0]]}-{c[1]}x{c[2]}-n{c[3]}" for c in GEMV_CASES])
+def test_gemv_parity(O, wtype, M, K, n):
+    announce(f"mmvq {TNAME[wtype]} M={M} K={K} n={n}")
+    rng = np.random.default_rng(1000 * n + M + K + wtype)
+    W = synth.weights(wtype, M, K, rng)
+    x = synth.activations(K, n, rng)
+    yd = gpu_quantize(x)
+    y = O.quantize_q8_1(x)
+    assert np.array_equal(host(yd), y)
+    got = gpu_gemv(dev(W), wtype, M, K, yd, n)
+    ref, mag, _ = O.mmvq(W, wtype, M, K, y, n)
+    assert_close(got, ref, mag, f"mmvq {TNAME[wtype]} {M}x{K} n={n}")
+
+
+# ---------------------------------------------------------------------------
+# GEMV at the workload sizes, in the launch configuration the benchmark
+# times; the oracle checks sampled row ranges.
+# ---------------------------------------------------------------------------
+FULL = [("q4_0_256x1024", 1), ("q4_k_4096x4096", 1), ("q4_k_4096x14336", 1),
+        ("q4_k_4096x14336", 2), ("q4_k_4096x14336", 4), ("q4_k_4096x14336", 8),
+        ("q4_k_14336x4096", 1), ("q4_k_14336x4096", 2), ("q4_k_14336x4096", 4),
+        ("q4_k_14336x4096", 8), ("q6_k_128256x4096", 1)]
+
+
+@pytest.mark.parametrize("name,n", FULL, ids=[f"{a}-n{b}" for a, b in FULL])
+def test_gemv_workload_sampled(O, name, n):
+    wl = synth.BY_NAME[name]
+    announce(f"mmvq workload {name} n={n}")
+    data = synth.make(wl, n)
+    W, x = data["W"], data["x"]
+    yd = gpu_quantize(x)
+    y = O.quantize_q8_1(x)
+    assert np.array_equal(host(yd), y)
+    got = gpu_gemv(dev(W), wl.wtype, wl.M, wl.K, yd, n)
+    ranges = sample_rows(wl.M, 256, seed=n) if wl.M > 512 else [(0, wl.M)]
+    ref, mag = oracle_rows(O, W, wl.wtype, wl.M, wl.K, y, n, ranges)
+    rows = np.concatenate([np.arange(a, b) for a, b in ranges])
+    assert_close(got[:, rows], ref[:, rows], mag[:, rows], f"{name} n={n}")
+    assert np.isfinite(got).all()
+
+
+# ---------------------------------------------------------------------------
+# Fused gate/up GLU
+# ---------------------------------------------------------------------------
+GLU_CASES = [(t, M, K, n, op) for t, M, K in [(Q4_K, 300, 4096), (Q4_K, 37, 512), (Q4_0, 300, 1024),
+                                               (Q6_K, 100, 4096), (Q4_K, 129, 16384)]
+             for n in (1, 2, 8) for op in (B.GLU_SWIGLU, B.GLU_PLAIN)]
+
+
+@pytest.mark.parametrize("wtype,M,K,n,op", GLU_CASES,
+                         ids=[f"{TNAME[c[0]]}-{c[1]}x{c[2]}-n{c[3]}-op{c[4]}" for c in GLU_CASES])
+def test_glu_parity(O, wtype, M, K, n, op):
+    import torch
+    announce(f"mmvq_glu {TNAME[wtype]} M={M} K={K} n={n} op={op}")
+    rng = np.random.default_rng(31 * M + K + n + op)
+    Wg = synth.weights(wtype, M, K, rng)
+    Wu = synth.weights(wtype, M, K, rng)
+    x = synth.activations(K, n, rng)
+    y = O.quantize_q8_1(x)
+    out = torch.full((n, M), float("nan"), dtype=torch.float32, device="cuda:0")
+    B.mmvq_glu(dev(Wg), dev(Wu), wtype, M, K, dev(y), n, op, out)
+    got = host(out).astype(np.float64)
+    ref = O.mmvq_glu(Wg, Wu, wtype, M, K, y, n, op)
+    g, mg, _ = O.mmvq(Wg, wtype, M, K, y, n)
+    u, mu, _ = O.mmvq(Wu, wtype, M, K, y, n)
+    tol = glu_tolerance(g, u, mg, mu, ref, op)
+    bad = ~(np.abs(got - ref) <= tol)
+    assert not bad.any(), f"{int(bad.sum())} outside; first {np.argwhere(bad)[0]}"
+
+
+# ---------------------------------------------------------------------------
+# Expert-indexed product (plain and fused)
+# ---------------------------------------------------------------------------
+def id_case(O, wtype, E, M, K, ids, fused, op=B.GLU_SWIGLU, rows=None, seed=0, data=None):
+    import torch
+    T, top_k = ids.shape
+    rng = np.random.default_rng(seed)
+    if data is None:
+        Wu = np.stack([synth.weights(wtype, M, K, rng) for _ in range(E)])
+        Wg = np.stack([synth.weights(wtype, M, K, rng) for _ in range(E)])
+        x = synth.activations(K, T, rng)
+    else:
+        Wu, Wg, x = data
+    # experts sit at a 16-byte-aligned stride (the ABI requires it), so
+    # matrices whose size is not a multiple of 16 are padded
+    stride = (Wu[0].size + 15) // 16 * 16
+    pad = lambda A: np.concatenate(  # noqa: E731
+        [np.pad(A[e].reshape(-1), (0, stride - A[e].size)) for e in range(E)])
+    Wu_buf, Wg_buf = pad(Wu), pad(Wg)
+    y = O.quantize_q8_1(x)
+    out = torch.full((T * top_k, M), float("nan"), dtype=torch.float32, device="cuda:0")
+    idsd = dev(ids.astype(np.int32))
+    yd = dev(y)
+    if fused:
+        B.mmvq_id_glu(dev(Wg_buf), dev(Wu_buf), stride, E, wtype, M, K, yd, T, idsd, top_k, op, out)
+    else:
+        B.mmvq_id(dev(Wu_buf), stride, E, wtype, M, K, yd, T, idsd, top_k, out)
+    got = host(out).astype(np.float64)
+    ranges = rows or [(0, M)]
+    sel = np.concatenate([np.arange(a, b) for a, b in ranges])
+    for t in range(T):
+        for k in range(top_k):
+            e = int(ids[t, k])
+            s = t * top_k + k
+            g, mg = oracle_rows(O, Wg[e], wtype, M, K, y[t:t + 1], 1, ranges)
+            u, mu = oracle_rows(O, Wu[e], wtype, M, K, y[t:t + 1], 1, ranges)
+            if fused:
+                act = g / (1.0 + np.exp(-g)) if op == B.GLU_SWIGLU else g
+                ref = act * u
+                tol = glu_tolerance(g, u, mg, mu, ref, op)
+                bad = ~(np.abs(got[s:s + 1, sel] - ref[:, sel]) <= tol[:, sel])
+                assert not bad.any(), f"token {t} slot {k} expert {e}: {np.argwhere(bad)[0]}"
+            else:
+                assert_close(got[s:s + 1, sel], u[:, sel], mu[:, sel], f"id token {t} slot {k}")
+
+
+ID_CASES = [
+    ("q4_k-E4-T3-k2", Q4_K, 4, 200, 512, [[2, 0], [1, 2], [2, 3]]),
+    ("q4_k-E8-T8-k2", Q4_K, 8, 300, 2048, "random"),
+    ("q4_k-E3-T5-k3", Q4_K, 3, 64, 256, [[0, 1, 2], [2, 1, 0], [1, 0, 2], [0, 2, 1], [2, 0, 1]]),
+    ("q4_k-E6-T1-k1", Q4_K, 6, 129, 4096, [[5]]),
+    ("q4_k-dup-in-token", Q4_K, 4, 100, 512, [[1, 1], [3, 1]]),
+    ("q4_0-E5-T4-k2", Q4_0, 5, 77, 1024, [[4, 0], [0, 4], [2, 2], [1, 3]]),
+    ("q6_k-E4-T2-k2", Q6_K, 4, 50, 768, [[3, 1], [1, 0]]),
+]
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("name,wtype,E,M,K,ids", ID_CASES, ids=[c[0] for c in ID_CASES])
+def test_id_parity(O, name, wtype, E, M, K, ids, fused):
+    announce(f"mmvq_id{'_glu' if fused else ''} {name}")
+    if isinstance(ids, str):
+        ids = synth.expert_ids(8, 2, E, np.random.default_rng(5))
+    id_case(O, wtype, E, M, K, np.asarray(ids), fused, seed=len(name))
+
+
+def test_id_glu_moe_workload_sampled(O):
+    """The MoE workload (8 experts, 8 tokens, top-2, 14336x4096 gate and up)
+    in the launch configuration the benchmark times; sampled rows."""
+    wl = synth.BY_NAME["moe_q4_k_8x14336x4096"]
+    announce("mmvq_id_glu moe workload")
+    d = synth.make(wl, 8)
+    id_case(O, wl.wtype, wl.n_experts, wl.M, wl.K, d["ids"], True,
+            rows=sample_rows(wl.M, 128, seed=3), data=(d["W_up"], d["W_gate"], d["x"]))
+
+
+# ---------------------------------------------------------------------------
+# Argument checks through the ABI, streams, graph capture
+# ---------------------------------------------------------------------------
+def test_abi_errors_on_device():
+    import torch
+    announce("abi errors")
+    W = torch.zeros(1 << 20, dtype=torch.uint8, device="cuda:0")
+    y = torch.zeros(1 << 16, dtype=torch.uint8, device="cuda:0")
+    out = torch.zeros(1 << 16, dtype=torch.float32, device="cuda:0")
+    L = B.lib()
+    s = torch.cuda.current_stream().cuda_stream
+    p, q, o = W.data_ptr(), y.data_ptr(), out.data_ptr()
+    assert L.mmvq(p, Q4_K, 1, 256 * 65, q, 1, o, s) == B.ERR_SHAPE      # row too long for a team
+    assert L.mmvq(p + 4, Q4_K, 1, 256, q, 1, o, s) == B.ERR_ALIGN
+    assert L.mmvq(p, Q4_K, 1, 256, q + 4, 1, o, s) == B.ERR_ALIGN
+    assert L.mmvq(p, Q4_K, 1, 256, q, 0, o, s) == B.ERR_SHAPE
+    assert L.mmvq(p, Q4_K, 1, 256, q, 9, o, s) == B.ERR_SHAPE
+    assert L.mmvq(p, Q4_K, 0, 256, q, 1, o, s) == B.ERR_SHAPE
+    assert L.mmvq(p, 3, 1, 256, q, 1, o, s) == B.ERR_TYPE
+    assert L.mmvq_glu(p, p, Q4_K, 1, 256, q, 1, 7, o, s) == B.ERR_TYPE
+    ids = torch.zeros(16, dtype=torch.int32, device="cuda:0")
+    assert L.mmvq_id(p, 144, 4, Q4_K, 2, 256, q, 1, ids.data_ptr(), 1, o, s) == B.ERR_SHAPE  # stride < M*row
+    assert L.mmvq_id(p, 288, 4, Q4_K, 2, 256, q, 1, ids.data_ptr(), 5, o, s) == B.ERR_SHAPE  # top_k > E
+    assert L.mmvq_id(p, 296, 4, Q4_K, 2, 256, q, 1, ids.data_ptr(), 1, o, s) == B.ERR_ALIGN
+    assert L.mmvq_quantize_q8_1(o, 33, 1, 33, q, s) == B.ERR_SHAPE
+    assert L.mmvq_quantize_q8_1(o + 2, 32, 1, 32, q, s) == B.ERR_ALIGN
+    torch.cuda.synchronize()
+
+
+def test_side_stream_and_graph_replay(O):
+    """Work enqueued on a non-default stream, and quantize + mmvq captured in
+    a HIP graph and replayed several times (eager work and synchronization
+    between replays) must match the eager result bit for bit."""
+    import torch
+    announce("side stream + graph replay")
+    rng = np.random.default_rng(77)
+    M, K = 1000, 4096
+    W = dev(synth.weights(Q4_K, M, K, rng))
+    xs = [dev(synth.activations(K, 1, rng)) for _ in range(3)]
+    y = torch.zeros((1, K // 32 * 36), dtype=torch.uint8, device="cuda:0")
+    out = torch.zeros((1, M), dtype=torch.float32, device="cuda:0")
+    x_in = xs[0].clone()
+    side = torch.cuda.Stream()
+    eager = []
+    for xv in xs:
+        with torch.cuda.stream(side):
+            B.mmvq_quantize_q8_1(xv, K, 1, K, y, side)
+            B.mmvq(W, Q4_K, M, K, y, 1, out, side)
+        side.synchronize()
+        eager.append(out.clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        B.mmvq_quantize_q8_1(x_in, K, 1, K, y, side)
+        B.mmvq(W, Q4_K, M, K, y, 1, out, side)
+    for rep in range(6):
+        x_in.copy_(xs[rep % 3])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager[rep % 3]), f"replay {rep} differs from eager"
+        _ = (W[:1024].float().sum())       # unrelated eager work between replays
+    torch.cuda.synchronize()
