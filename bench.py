@@ -1,0 +1,272 @@
+"""Benchmark of the decode-time quantized mat-vec on one MI355X.
+
+Default workload: Q4_K weights, M = 4096 rows x K = 14336, n = 1 activation
+column (the FFN down-projection shape of a 7B/8B-class model), fp32 output.
+One step is one pass of the hot path over one activation: quantize the fp32
+activation to q8_1, then the quantized mat-vec against a weight matrix.
+
+Measurement:
+  * inputs (weights, activation) are resident in HBM before timing starts;
+  * weights rotate over enough copies (>= 3 x the 256 MB last-level cache)
+    that every step streams its matrix from HBM, not from cache;
+  * steps are captured in a HIP graph (one graph = one pass over all weight
+    copies) and replayed, so host launch cost does not pace microsecond
+    kernels;
+  * HIP events on the launch stream time the steps and, separately, a graph
+    of back-to-back mat-vec launches alone (the roofline figure);
+  * the CPU oracle (plain C, fp64) runs the same workload on a bounded
+    number of repetitions, rows split over the host's threads, as a
+    reported baseline.
+
+Prints one JSON line (rank 0). ``--all`` also prints one line per workload
+and column count to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+LLC_BYTES = 256 * 2 ** 20    # MI355X Infinity Cache
+TOKENS_DENOM_GB = 3.9        # weight bytes of one decode step of a 7B Q4_K model
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=4000)
+    p.add_argument("--warmup", type=int, default=400)
+    p.add_argument("--workload", default="q4_k_4096x14336")
+    p.add_argument("--n", type=int, default=1, help="activation columns")
+    p.add_argument("--all", action="store_true", help="also time every workload (stderr)")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="wall-clock budget of the oracle baseline (0 disables it)")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="also run a plain device copy of known size (counter calibration)")
+    return p.parse_args()
+
+
+def algorithmic_bytes(wl, n: int) -> int:
+    """Bytes one mat-vec launch must move: weights once, the q8_1 columns,
+    the fp32 outputs (plus the gate matrix and expert gather in fused/id
+    modes, counted by the callers)."""
+    return wl.weight_bytes + n * (wl.K // 32) * 36 + n * wl.M * 4
+
+
+class Timer:
+    """HIP events on the given stream."""
+
+    def __init__(self, torch, stream):
+        self.torch = torch
+        self.stream = stream
+
+    def __enter__(self):
+        self.a = self.torch.cuda.Event(enable_timing=True)
+        self.b = self.torch.cuda.Event(enable_timing=True)
+        self.a.record(self.stream)
+        return self
+
+    def __exit__(self, *exc):
+        self.b.record(self.stream)
+        self.b.synchronize()
+        self.ms = self.a.elapsed_time(self.b)
+
+
+def gpu_setup(torch, wl, n: int, seed_offset: int = 0):
+    from quantized_decode_gemv_quantize_amd import synth
+    data = synth.make(wl, n)
+    copies = max(2, math.ceil(3 * LLC_BYTES / wl.weight_bytes))
+    W0 = torch.from_numpy(data["W"]).to("cuda:0")
+    Ws = [W0] + [W0.clone() for _ in range(copies - 1)]
+    x = torch.from_numpy(data["x"]).to("cuda:0")
+    y = torch.empty((n, wl.K // 32 * 36), dtype=torch.uint8, device="cuda:0")
+    out = torch.empty((n, wl.M), dtype=torch.float32, device="cuda:0")
+    return data, Ws, x, y, out
+
+
+def capture(torch, stream, fn):
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=stream):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_workload(torch, B, wl, n: int, steps: int, warmup: int):
+    """Returns a dict of GPU timings for one workload."""
+    data, Ws, x, y, out = gpu_setup(torch, wl, n)
+    C = len(Ws)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+
+    def step_pass():
+        for W in Ws:
+            B.mmvq_quantize_q8_1(x, wl.K, n, wl.K, y, s)
+            B.mmvq(W, wl.wtype, wl.M, wl.K, y, n, out, s)
+
+    def gemv_pass():
+        for W in Ws:
+            B.mmvq(W, wl.wtype, wl.M, wl.K, y, n, out, s)
+
+    def quant_pass():
+        for _ in Ws:
+            B.mmvq_quantize_q8_1(x, wl.K, n, wl.K, y, s)
+
+    g_step = capture(torch, s, step_pass)
+    g_gemv = capture(torch, s, gemv_pass)
+    g_quant = capture(torch, s, quant_pass)
+    reps = max(1, math.ceil(steps / C))
+    wreps = max(1, math.ceil(warmup / C))
+    res = {"copies": C, "steps": reps * C, "warmup": wreps * C}
+    with torch.cuda.stream(s):
+        for g, key in ((g_step, "step"), (g_gemv, "gemv"), (g_quant, "quant")):
+            for _ in range(wreps):
+                g.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            with Timer(torch, s) as t:
+                for _ in range(reps):
+                    g.replay()
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+            res[f"{key}_ms_total"] = t.ms
+            res[f"{key}_us"] = t.ms * 1e3 / (reps * C)
+            res[f"{key}_wall_s"] = wall
+    return res, data, Ws, y, out
+
+
+def cpu_baseline(wl, data, n: int, budget_s: float):
+    """The oracle on the host: full mat-vecs (quantize + all rows), rows split
+    over the host threads, repeated until the wall-clock budget is spent."""
+    import concurrent.futures as cf
+
+    import oracle
+    O = oracle.default()
+    L = O.L
+    W = np.ascontiguousarray(data["W"]).reshape(-1)
+    x = np.ascontiguousarray(data["x"])
+    cores = min(16, os.cpu_count() or 1)
+    out = np.zeros((n, wl.M))
+    chunks = np.linspace(0, wl.M, cores + 1).astype(np.int64)
+
+    def rows(i, y):
+        rc = L.orc_mmvq_rows(W.ctypes.data, wl.wtype, wl.M, wl.K, y.ctypes.data, n,
+                             int(chunks[i]), int(chunks[i + 1]), out.ctypes.data, None, None)
+        assert rc == 0
+
+    reps = 0
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(max_workers=cores) as ex:
+        while True:
+            y = O.quantize_q8_1(x)
+            list(ex.map(lambda i: rows(i, y), range(cores)))
+            reps += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    dt = time.perf_counter() - t0
+    return {"value": round(wl.weight_bytes * reps / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{reps} full {wl.name} n={n} passes (q8_1 quantize + all {wl.M} rows), "
+                      f"rows split over {cores} threads, {dt:.1f} s wall",
+            "us_per_gemv": round(dt / reps * 1e6, 1)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              f"(the mat-vec shards by rows across GPUs, see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from quantized_decode_gemv_quantize_amd import binding as B
+    from quantized_decode_gemv_quantize_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    B.lib()
+    wl = synth.BY_NAME[args.workload]
+    n = args.n
+
+    if args.copy_probe:
+        a = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device="cuda:0")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    res, data, Ws, y, out = time_workload(torch, B, wl, n, args.steps, args.warmup)
+    step_ms = res["step_us"] / 1e3
+    value = wl.weight_bytes / (res["step_us"] * 1e-6) / 1e9
+    gemv_bytes = algorithmic_bytes(wl, n)
+    achieved = gemv_bytes / (res["gemv_us"] * 1e-6) / 1e9
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(wl, data, n, args.cpu_seconds)
+
+    line = {
+        "metric": "Q4_K GEMV effective weight GB/s (% of HBM peak) at 4096x14336, n=1",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": res["steps"],
+        "warmup": res["warmup"],
+        "ms_per_step": round(step_ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8xu4 dot, f32 scale",
+        "data": "synthetic (seeded; random codes and scales, x ~ N(0,1))",
+        "config": {"workload": wl.name, "type": synth.TYPE_NAME[wl.wtype], "M": wl.M, "K": wl.K,
+                   "n": n, "weight_bytes": wl.weight_bytes, "weight_copies": res["copies"],
+                   "parallelism": "single GPU"},
+        "detail": {
+            "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+            "gemv_us": round(res["gemv_us"], 3),
+            "quantize_us": round(res["quant_us"], 3),
+            "step_us": round(res["step_us"], 3),
+            "gemv_weight_gbs": round(wl.weight_bytes / (res["gemv_us"] * 1e-6) / 1e9, 1),
+            "gemv_per_s": round(1e6 / res["gemv_us"], 1),
+            "decode_tokens_per_s_equiv": round(value / TOKENS_DENOM_GB, 1),
+            "step_wall_s": round(res["step_wall_s"], 4),
+        },
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "mmvq_rows_kernel (Q4_K, n=1)",
+                     "bytes_per_launch": gemv_bytes,
+                     "avg_launch_us": round(res["gemv_us"], 3)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+    if args.all:
+        for name in ["q4_0_256x1024", "q4_k_4096x4096", "q4_k_4096x14336", "q4_k_14336x4096",
+                     "q6_k_128256x4096"]:
+            w = synth.BY_NAME[name]
+            for nn in (w.n if name != "q4_k_4096x14336" else (1, 2, 4, 8)):
+                r, *_ = time_workload(torch, B, w, nn, 1000, 100)
+                gb = algorithmic_bytes(w, nn) / (r["gemv_us"] * 1e-6) / 1e9
+                print(json.dumps({"workload": name, "n": nn, "gemv_us": round(r["gemv_us"], 3),
+                                  "quantize_us": round(r["quant_us"], 3),
+                                  "step_us": round(r["step_us"], 3),
+                                  "gemv_gbs": round(gb, 1), "frac": round(gb / HBM_PEAK_GBS, 4)}),
+                      file=sys.stderr, flush=True)
+
+
+if __name__ == "__main__":
+    main()

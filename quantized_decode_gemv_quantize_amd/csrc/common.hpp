@@ -3,10 +3,25 @@
 // Cross-lane reduction, raw loads and small integer helpers. Everything here
 // is CDNA4 code: 64-lane wavefronts, DPP row/quad permutes, and the gfx950
 // v_permlane16_swap / v_permlane32_swap instructions.
+//
+// With QMV_HOST_MODEL defined (a host-only clang build used by the test
+// suite), the loads become bounds-checked host reads that record every
+// access outside the registered buffers, and the few integer builtins the
+// block decoders use get portable equivalents; the cross-lane part is left
+// out. This lets the host run the exact addressing code of the kernels.
 #pragma once
 
-#include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#ifndef QMV_HOST_MODEL
+#include <hip/hip_runtime.h>
+#else
+#include <string.h>
+#include <vector>
+#define __device__
+#define __host__
+#define __forceinline__ inline
+#endif
 
 namespace qmv {
 
@@ -16,6 +31,77 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kWave = 64;
 constexpr int kMaxCols = 8;
 constexpr int kMaxThreads = 1024;
+constexpr int kLaunchBound = 512;       // 8 waves per workgroup at most
+constexpr int kMaxWavesPerBlock = kLaunchBound / kWave;
+
+#ifdef QMV_HOST_MODEL
+namespace hostmodel {
+struct Range {
+  const uint8_t* lo;
+  const uint8_t* hi;
+};
+inline std::vector<Range>& ranges() {
+  static std::vector<Range> r;
+  return r;
+}
+inline long& violations() {
+  static long v = 0;
+  return v;
+}
+inline long& accesses() {
+  static long v = 0;
+  return v;
+}
+// True if [p, p+n) lies inside one registered buffer and p is aligned as the
+// device load requires; otherwise counts a violation (and nothing is read).
+inline bool ok(const uint8_t* p, size_t n, uintptr_t align) {
+  ++accesses();
+  if (reinterpret_cast<uintptr_t>(p) % align != 0) { ++violations(); return false; }
+  for (const Range& r : ranges())
+    if (p >= r.lo && p + n <= r.hi) return true;
+  ++violations();
+  return false;
+}
+}  // namespace hostmodel
+
+inline u32x4 ld_nt_x4(const uint8_t* p) {
+  u32x4 v = {0, 0, 0, 0};
+  if (hostmodel::ok(p, 16, 16)) memcpy(&v, p, 16);
+  return v;
+}
+inline u32x4 ld_x4(const uint8_t* p) {
+  u32x4 v = {0, 0, 0, 0};
+  if (hostmodel::ok(p, 16, 4)) memcpy(&v, p, 16);
+  return v;
+}
+inline u32x2 ld_x2(const uint8_t* p) {
+  u32x2 v = {0, 0};
+  if (hostmodel::ok(p, 8, 4)) memcpy(&v, p, 8);
+  return v;
+}
+inline uint32_t ld_u16(const uint8_t* p) {
+  uint16_t v = 0;
+  if (hostmodel::ok(p, 2, 2)) memcpy(&v, p, 2);
+  return v;
+}
+inline uint32_t ld_u32(const uint8_t* p) {
+  uint32_t v = 0;
+  if (hostmodel::ok(p, 4, 4)) memcpy(&v, p, 4);
+  return v;
+}
+inline uint32_t shr16_pair(uint32_t hi, uint32_t lo) {
+  return static_cast<uint32_t>(((static_cast<uint64_t>(hi) << 32) | lo) >> 16);
+}
+inline int dot4(uint32_t a, uint32_t b, int c) {
+  for (int k = 0; k < 4; ++k)
+    c += static_cast<int8_t>(a >> (8 * k)) * static_cast<int8_t>(b >> (8 * k));
+  return c;
+}
+inline int mul24(int a, int b) { return a * b; }
+inline int sbfe(uint32_t v, uint32_t off, uint32_t width) {
+  return static_cast<int>(v << (32 - off - width)) >> (32 - width);
+}
+#else
 
 __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
 
@@ -51,12 +137,6 @@ __device__ __forceinline__ uint32_t shr16_pair(uint32_t hi, uint32_t lo) {
   return __builtin_amdgcn_alignbyte(hi, lo, 2);
 }
 
-// fp16 bit pattern (low 16 bits) -> float.
-__device__ __forceinline__ float h2f(uint32_t bits) {
-  _Float16 h = __builtin_bit_cast(_Float16, static_cast<uint16_t>(bits & 0xFFFFu));
-  return static_cast<float>(h);
-}
-
 // 4-way signed int8 dot product with accumulate (v_dot4_i32_i8).
 __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
   return __builtin_amdgcn_sdot4(static_cast<int>(a), static_cast<int>(b), c, false);
@@ -65,6 +145,21 @@ __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
 // 24-bit signed multiply (v_mul_i32_i24); both factors fit in 24 bits here.
 __device__ __forceinline__ int mul24(int a, int b) { return __mul24(a, b); }
 
+// Signed bit-field extract (v_bfe_i32).
+__device__ __forceinline__ int sbfe(uint32_t v, uint32_t off, uint32_t width) {
+  return __builtin_amdgcn_sbfe(v, off, width);
+}
+#endif
+
+// fp16 bit pattern (low 16 bits) -> float.
+__device__ __forceinline__ float h2f(uint32_t bits) {
+  _Float16 h = __builtin_bit_cast(_Float16, static_cast<uint16_t>(bits & 0xFFFFu));
+  return static_cast<float>(h);
+}
+
+constexpr int pow2ceil(int v) { int p = 1; while (p < v) p <<= 1; return p; }
+
+#ifndef QMV_HOST_MODEL
 // ---------------------------------------------------------------------------
 // Cross-lane exchange
 // ---------------------------------------------------------------------------
@@ -180,6 +275,6 @@ struct ReduceMap {
   __device__ static bool representative(int l) { return (l & ((1 << (L - S)) - 1)) == 0; }
 };
 
-constexpr int pow2ceil(int v) { int p = 1; while (p < v) p <<= 1; return p; }
+#endif  // !QMV_HOST_MODEL
 
 }  // namespace qmv

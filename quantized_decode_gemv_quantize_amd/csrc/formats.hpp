@@ -10,8 +10,8 @@
 // so it loads the matching activation codes once and keeps them in
 // registers. Units are chosen so that a wave's weight loads for one row are
 // contiguous 16-byte pieces:
-//   Q4_K: unit = 16 bytes of codes of one super-block (32 weights; 8 units
-//         per super-block), plus that super-block's 16-byte header.
+//   Q4_K: unit = 32 bytes of codes of one super-block (64 weights, two
+//         sub-blocks; 4 units per super-block), plus its 16-byte header.
 //   Q4_0: unit = one 18-byte block (32 weights).
 //   Q6_K: unit = one quarter of a super-block (64 weights): 2 x 16 bytes of
 //         low bits, 16 bytes of high bits, 4 int8 scales, the fp16 d.
@@ -46,101 +46,134 @@ __device__ __forceinline__ int bsum4(uint32_t w, int c) { return dot4(w, 0x01010
 // mins @4, 128 bytes of nibbles @16. Sub-block t (32 weights) of 64-element
 // chunk c = t/2 reads the low (t even) or high (t odd) nibbles of
 // qs[32c .. 32c+31]. Weight = d*sc_t*q - dmin*m_t.
-// Unit u: super-block sb = u/8, p = u%8, chunk c = p/2, half = p%2; its 16
-// code bytes qs[32c + 16*half ..] hold elements 16*half.. of sub-blocks
-// t0 = 2c (low nibbles) and t1 = 2c+1 (high nibbles).
+// Unit u: super-block sb = u/4, chunk c = u%4: the 32 code bytes
+// qs[32c ..] (64 weights) = sub-blocks t0 = 2c (low nibbles) and t1 = 2c+1
+// (high nibbles), with their q8_1 blocks 8sb+2c and 8sb+2c+1.
 // ===========================================================================
 struct Q4K {
   static constexpr int kType = 12, kQK = 256, kBlockBytes = 144;
-  static constexpr int kUnitsPerBlock = 8, kDotsPerBlock = 16;
+  static constexpr int kUnitsPerBlock = 4, kDotsPerBlock = 16;
 
   struct Act {
-    uint32_t y0[4], y1[4];   // activation codes paired with the t0 / t1 nibbles
+    uint32_t y0[8], y1[8];   // activation codes paired with the t0 / t1 nibbles
     float d0, d1;            // q8_1 scales of the two sub-blocks
-    float s0, s1;            // d8 * (sum of the 16 codes): exact in fp32
+    float s0, s1;            // d8 * (sum of the 32 codes): exact in fp32
   };
 
-  // int sums of the 16 codes of each half sub-block (also used by int_dots)
-  __device__ static void act_codes(const uint8_t* ycol, int u, u32x4& q0, u32x4& q1,
+  __device__ static void act_codes(const uint8_t* ycol, int u, uint32_t (&q0)[8], uint32_t (&q1)[8],
                                    const uint8_t*& b0, const uint8_t*& b1) {
-    const int sb = u >> 3, p = u & 7, c = p >> 1, half = p & 1;
+    const int sb = u >> 2, c = u & 3;
     b0 = ycol + static_cast<int64_t>(8 * sb + 2 * c) * kQ8Bytes;
     b1 = b0 + kQ8Bytes;
-    q0 = ld_x4(b0 + 4 + 16 * half);
-    q1 = ld_x4(b1 + 4 + 16 * half);
+    const u32x4 a0 = ld_x4(b0 + 4), a1 = ld_x4(b0 + 20), c0 = ld_x4(b1 + 4), c1 = ld_x4(b1 + 20);
+    q0[0] = a0.x; q0[1] = a0.y; q0[2] = a0.z; q0[3] = a0.w;
+    q0[4] = a1.x; q0[5] = a1.y; q0[6] = a1.z; q0[7] = a1.w;
+    q1[0] = c0.x; q1[1] = c0.y; q1[2] = c0.z; q1[3] = c0.w;
+    q1[4] = c1.x; q1[5] = c1.y; q1[6] = c1.z; q1[7] = c1.w;
+  }
+
+  __device__ static int sum8(const uint32_t (&q)[8]) {
+    int s = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s = bsum4(q[k], s);
+    return s;
   }
 
   __device__ static void load_act(Act& a, const uint8_t* ycol, int u) {
-    u32x4 q0, q1;
     const uint8_t *b0, *b1;
-    act_codes(ycol, u, q0, q1, b0, b1);
-    a.y0[0] = q0.x; a.y0[1] = q0.y; a.y0[2] = q0.z; a.y0[3] = q0.w;
-    a.y1[0] = q1.x; a.y1[1] = q1.y; a.y1[2] = q1.z; a.y1[3] = q1.w;
+    act_codes(ycol, u, a.y0, a.y1, b0, b1);
     a.d0 = q8_d(b0);
     a.d1 = q8_d(b1);
-    const int s0 = bsum4(q0.w, bsum4(q0.z, bsum4(q0.y, bsum4(q0.x, 0))));
-    const int s1 = bsum4(q1.w, bsum4(q1.z, bsum4(q1.y, bsum4(q1.x, 0))));
-    a.s0 = a.d0 * static_cast<float>(s0);
-    a.s1 = a.d1 * static_cast<float>(s1);
+    a.s0 = a.d0 * static_cast<float>(sum8(a.y0));
+    a.s1 = a.d1 * static_cast<float>(sum8(a.y1));
+  }
+
+  __device__ static void zero_act(Act& a) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) { a.y0[k] = 0; a.y1[k] = 0; }
+    a.d0 = a.d1 = a.s0 = a.s1 = 0.0f;
+  }
+
+  // Per-lane constants, computed once: byte offsets inside a row, and the
+  // shifts and masks that pick this lane's two 6-bit scales and mins out of
+  // the 12 packed bytes. With scale words H1 = bytes 0..3, H2 = 4..7,
+  // H3 = 8..11 and sh = 16*(c%2), sub-blocks 2c, 2c+1 take
+  //   c < 2 : sc = (H1 >> sh) & 0x3F3F,   m = (H2 >> sh) & 0x3F3F
+  //   c >= 2: sc = ((H3 >> sh) & 0x0F0F)     | ((H1 >> (sh+2)) & 0x3030),
+  //           m  = ((H3 >> (sh+4)) & 0x0F0F) | ((H2 >> (sh+2)) & 0x3030)
+  // (one byte per sub-block): the pages' branch-free unpack with the scale
+  // words read as little-endian 16-bit words.
+  struct Lane {
+    uint32_t qoff, hoff;       // code bytes and header, from the row start
+    uint32_t sh, shm, maskA, maskB;
+    bool lo;                   // c < 2
+  };
+  __device__ static Lane lane(int u) {
+    Lane l;
+    const int sb = u >> 2, c = u & 3;
+    l.hoff = static_cast<uint32_t>(sb * kBlockBytes);
+    l.qoff = l.hoff + 16 + 32 * c;
+    l.lo = c < 2;
+    l.sh = 16u * (c & 1);
+    l.shm = l.lo ? l.sh : l.sh + 4;
+    l.maskA = l.lo ? 0x3F3Fu : 0x0F0Fu;
+    l.maskB = l.lo ? 0u : 0x3030u;
+    return l;
   }
 
   struct Wt {
-    u32x4 qs;    // 16 code bytes
-    u32x4 hdr;   // d | dmin, scales[0..3], scales[4..7], scales[8..11]
+    u32x4 q0, q1;  // 32 code bytes
+    u32x4 hdr;     // d | dmin, scales[0..3], scales[4..7], scales[8..11]
   };
 
-  // row: start of the row (16-byte aligned: 144-byte blocks, 16-byte base)
-  __device__ static void load_wt(Wt& w, const uint8_t* row, int u) {
-    const uint8_t* blk = row + static_cast<int64_t>(u >> 3) * kBlockBytes;
-    w.qs = ld_nt_x4(blk + 16 + 16 * (u & 7));
-    w.hdr = ld_x4(blk);
+  // row: wave-uniform row start; extra: per-lane byte offset added to it
+  __device__ static void load_wt(Wt& w, const uint8_t* row, uint32_t extra, const Lane& l) {
+    w.q0 = ld_nt_x4(row + (extra + l.qoff));
+    w.q1 = ld_nt_x4(row + (extra + l.qoff + 16));
+    w.hdr = ld_x4(row + (extra + l.hoff));
   }
 
   struct Dec {
-    uint32_t lo[4], hi[4];   // nibbles of t0 and t1 as unsigned bytes
-    int sc0, sc1;
+    uint32_t lo[8], hi[8];   // nibbles of t0 and t1 as unsigned bytes
+    uint32_t scp;            // sc of t0 (byte 0) and t1 (byte 1)
     float m0, m1, d, dmin;
   };
 
-  // 6-bit scales/mins of sub-blocks t0 = 2c and t1 = 2c+1 as 16-bit pairs
-  // (one per byte), following the pages' branch-free unpack with the scale
-  // words read as little-endian 16-bit words.
-  __device__ static void decode(const Wt& w, Dec& o, int u) {
+  __device__ static void decode(const Wt& w, Dec& o, const Lane& l) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      o.lo[k] = w.qs[k] & 0x0F0F0F0Fu;
-      o.hi[k] = (w.qs[k] >> 4) & 0x0F0F0F0Fu;
+      o.lo[k] = w.q0[k] & 0x0F0F0F0Fu;
+      o.hi[k] = (w.q0[k] >> 4) & 0x0F0F0F0Fu;
+      o.lo[4 + k] = w.q1[k] & 0x0F0F0F0Fu;
+      o.hi[4 + k] = (w.q1[k] >> 4) & 0x0F0F0F0Fu;
     }
     o.d = h2f(w.hdr.x);
     o.dmin = h2f(w.hdr.x >> 16);
-    const int c = (u & 7) >> 1;
-    const uint32_t sh = 16u * (c & 1);
     const uint32_t H1 = w.hdr.y, H2 = w.hdr.z, H3 = w.hdr.w;
-    uint32_t scp, mp;
-    if (c < 2) {                  // lane-constant: no divergence across rows
-      scp = (H1 >> sh) & 0x3F3Fu;
-      mp = (H2 >> sh) & 0x3F3Fu;
-    } else {
-      scp = ((H3 >> sh) & 0x0F0Fu) | (((H1 >> sh) & 0xC0C0u) >> 2);
-      mp = ((H3 >> (sh + 4)) & 0x0F0Fu) | (((H2 >> sh) & 0xC0C0u) >> 2);
-    }
-    o.sc0 = scp & 0xFF;
-    o.sc1 = (scp >> 8) & 0xFF;
-    o.m0 = static_cast<float>(mp & 0xFF);
-    o.m1 = static_cast<float>((mp >> 8) & 0xFF);
+    const uint32_t Xs = l.lo ? H1 : H3, Xm = l.lo ? H2 : H3;
+    o.scp = ((Xs >> l.sh) & l.maskA) | ((H1 >> (l.sh + 2)) & l.maskB);
+    const uint32_t mp = ((Xm >> l.shm) & l.maskA) | ((H2 >> (l.sh + 2)) & l.maskB);
+    o.m0 = static_cast<float>(mp & 0xFFu);
+    o.m1 = static_cast<float>((mp >> 8) & 0xFFu);
   }
 
   __device__ static void nibble_dots(const Dec& o, const Act& a, int& dot0, int& dot1) {
-    dot0 = dot4(o.lo[3], a.y0[3], dot4(o.lo[2], a.y0[2], dot4(o.lo[1], a.y0[1], dot4(o.lo[0], a.y0[0], 0))));
-    dot1 = dot4(o.hi[3], a.y1[3], dot4(o.hi[2], a.y1[2], dot4(o.hi[1], a.y1[1], dot4(o.hi[0], a.y1[0], 0))));
+    dot0 = 0;
+    dot1 = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      dot0 = dot4(o.lo[k], a.y0[k], dot0);
+      dot1 = dot4(o.hi[k], a.y1[k], dot1);
+    }
   }
 
   // d * (sc0*d8_0*dot0 + sc1*d8_1*dot1) - dmin * (m0*d8_0*S0 + m1*d8_1*S1)
   __device__ static float col_dot(const Dec& o, const Act& a) {
     int dot0, dot1;
     nibble_dots(o, a, dot0, dot1);
-    const float sd = static_cast<float>(mul24(dot0, o.sc0)) * a.d0 +
-                     static_cast<float>(mul24(dot1, o.sc1)) * a.d1;
+    const int sc0 = static_cast<int>(o.scp & 0xFFu), sc1 = static_cast<int>((o.scp >> 8) & 0xFFu);
+    const float sd = static_cast<float>(mul24(dot0, sc0)) * a.d0 +
+                     static_cast<float>(mul24(dot1, sc1)) * a.d1;
     const float sm = o.m0 * a.s0 + o.m1 * a.s1;
     return o.d * sd - o.dmin * sm;
   }
@@ -151,14 +184,11 @@ struct Q4K {
     load_act(a, ycol, u);
     int dot0, dot1;
     nibble_dots(o, a, dot0, dot1);
-    u32x4 q0, q1;
-    const uint8_t *b0, *b1;
-    act_codes(ycol, u, q0, q1, b0, b1);
-    const int c = (u & 7) >> 1;
+    const int c = u & 3;
     dots[2 * c] += dot0;
     dots[2 * c + 1] += dot1;
-    dots[8 + 2 * c] += bsum4(q0.w, bsum4(q0.z, bsum4(q0.y, bsum4(q0.x, 0))));
-    dots[8 + 2 * c + 1] += bsum4(q1.w, bsum4(q1.z, bsum4(q1.y, bsum4(q1.x, 0))));
+    dots[8 + 2 * c] += sum8(a.y0);
+    dots[8 + 2 * c + 1] += sum8(a.y1);
   }
 };
 
@@ -192,17 +222,28 @@ struct Q40 {
     a.s8 = 8.0f * h2f(ds >> 16);
   }
 
+  __device__ static void zero_act(Act& a) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) a.y[k] = 0;
+    a.d8 = a.s8 = 0.0f;
+  }
+
+  struct Lane {
+    uint32_t off;    // block offset from the row start
+  };
+  __device__ static Lane lane(int u) { return Lane{static_cast<uint32_t>(u * kBlockBytes)}; }
+
   struct Wt {
     u32x4 run;       // dword-aligned 16 bytes
     uint32_t extra;  // 16-bit word: d (odd placement) or qs[14..15]
-    bool odd;        // block offset = 2 (mod 4)
+    bool odd;        // block address = 2 (mod 4)
   };
 
-  __device__ static void load_wt(Wt& w, const uint8_t* row, int u) {
-    const uint8_t* blk = row + static_cast<int64_t>(u) * kBlockBytes;
-    w.odd = (reinterpret_cast<uintptr_t>(blk) & 2u) != 0;
-    w.run = ld_x4(w.odd ? blk + 2 : blk);
-    w.extra = ld_u16(w.odd ? blk : blk + 16);
+  __device__ static void load_wt(Wt& w, const uint8_t* row, uint32_t extra, const Lane& l) {
+    const uint32_t off = extra + l.off;
+    w.odd = ((static_cast<uint32_t>(reinterpret_cast<uintptr_t>(row)) + off) & 2u) != 0;
+    w.run = ld_x4(row + (off + (w.odd ? 2u : 0u)));
+    w.extra = ld_u16(row + (off + (w.odd ? 0u : 16u)));
   }
 
   struct Dec {
@@ -210,7 +251,7 @@ struct Q40 {
     float d;
   };
 
-  __device__ static void decode(const Wt& w, Dec& o, int) {
+  __device__ static void decode(const Wt& w, Dec& o, const Lane&) {
     uint32_t qs[4];
     qs[0] = w.odd ? w.run.x : shr16_pair(w.run.y, w.run.x);
     qs[1] = w.odd ? w.run.y : shr16_pair(w.run.z, w.run.y);
@@ -255,9 +296,9 @@ struct Q40 {
 // pieces A = ql[64h+16lq ..+16], B = ql[64h+32+16lq ..+16],
 // C = qh[32h+16lq ..+16]; sub-blocks 8h + 2g + lq for g = 0..3, each paired
 // with q8_1 block 8sb + 4h + g, codes 16lq..16lq+15.
-// Blocks are 2-byte aligned: as for Q4_0, a piece at an offset = 2 (mod 4)
-// is read as the dword-aligned run starting two bytes earlier plus the
-// piece's last 16-bit word, then re-aligned.
+// Blocks are 2-byte aligned: a piece at an address = 2 (mod 4) is read as
+// the dword-aligned run starting two bytes into it plus its first 16-bit
+// word, then re-aligned (all reads stay inside the super-block).
 // ===========================================================================
 struct Q6K {
   static constexpr int kType = 14, kQK = 256, kBlockBytes = 210;
@@ -286,30 +327,59 @@ struct Q6K {
     }
   }
 
+  __device__ static void zero_act(Act& a) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) a.y[g][k] = 0;
+      a.d8[g] = 0.0f;
+      a.c32[g] = 0;
+    }
+  }
+
+  struct Lane {
+    uint32_t blk;                 // super-block offset from the row start
+    uint32_t oA, oB, oC, oS;      // piece offsets inside the super-block
+    uint32_t lq;
+  };
+  __device__ static Lane lane(int u) {
+    Lane l;
+    const int sb = u >> 2, h = (u >> 1) & 1, lq = u & 1;
+    l.blk = static_cast<uint32_t>(sb * kBlockBytes);
+    l.oA = 64 * h + 16 * lq;
+    l.oB = l.oA + 32;
+    l.oC = 128 + 32 * h + 16 * lq;
+    l.oS = 192 + 8 * h;
+    l.lq = lq;
+    return l;
+  }
+
+  // Pieces start at even offsets. When a piece's address is 2 (mod 4) the
+  // lane reads the dword-aligned run starting two bytes INTO the piece plus
+  // the piece's first 16-bit word, so every offset is at or above the
+  // piece start and every byte read lies inside the super-block.
   struct Wt {
     u32x4 A, B, C;              // dword-aligned runs
-    uint32_t a2, b2, c2;        // last 16-bit word of each piece
+    uint32_t a0, b0, c0;        // first 16-bit word of each piece
     u32x2 S;                    // dword-aligned run over the 8 scales
-    uint32_t s2;                // last 16-bit word of the scales
+    uint32_t s0;                // first 16-bit word of the scales
     uint32_t dbits;
     bool odd;
   };
 
-  __device__ static void load_wt(Wt& w, const uint8_t* row, int u) {
-    const int sb = u >> 2, h = (u >> 1) & 1, lq = u & 1;
-    const uint8_t* blk = row + static_cast<int64_t>(sb) * kBlockBytes;
-    w.odd = (reinterpret_cast<uintptr_t>(blk) & 2u) != 0;
-    const uint8_t* b4 = w.odd ? blk - 2 : blk;          // dword aligned
-    const int oA = 64 * h + 16 * lq, oB = oA + 32, oC = 128 + 32 * h + 16 * lq, oS = 192 + 8 * h;
-    w.A = ld_x4(b4 + oA);
-    w.B = ld_x4(b4 + oB);
-    w.C = ld_x4(b4 + oC);
-    w.S = ld_x2(b4 + oS);
-    w.a2 = ld_u16(blk + oA + 14);
-    w.b2 = ld_u16(blk + oB + 14);
-    w.c2 = ld_u16(blk + oC + 14);
-    w.s2 = ld_u16(blk + oS + 6);
-    w.dbits = ld_u16(blk + 208);
+  __device__ static void load_wt(Wt& w, const uint8_t* row, uint32_t extra, const Lane& l) {
+    const uint32_t blk = extra + l.blk;
+    w.odd = ((static_cast<uint32_t>(reinterpret_cast<uintptr_t>(row)) + blk) & 2u) != 0;
+    const uint32_t sh = w.odd ? 2u : 0u;
+    w.A = ld_x4(row + (blk + l.oA + sh));
+    w.B = ld_x4(row + (blk + l.oB + sh));
+    w.C = ld_x4(row + (blk + l.oC + sh));
+    w.S = ld_x2(row + (blk + l.oS + sh));
+    w.a0 = ld_u16(row + (blk + l.oA));
+    w.b0 = ld_u16(row + (blk + l.oB));
+    w.c0 = ld_u16(row + (blk + l.oC));
+    w.s0 = ld_u16(row + (blk + l.oS));
+    w.dbits = ld_u16(row + (blk + 208));
   }
 
   struct Dec {
@@ -318,18 +388,19 @@ struct Q6K {
     float d;
   };
 
-  __device__ static void realign(const u32x4& r, uint32_t tail, bool odd, uint32_t (&o)[4]) {
-    o[0] = odd ? shr16_pair(r.y, r.x) : r.x;
-    o[1] = odd ? shr16_pair(r.z, r.y) : r.y;
-    o[2] = odd ? shr16_pair(r.w, r.z) : r.z;
-    o[3] = odd ? shr16_pair(tail, r.w) : r.w;
+  // 16 piece bytes from a run read two bytes into the piece (odd) or at it
+  __device__ static void realign(const u32x4& r, uint32_t head, bool odd, uint32_t (&o)[4]) {
+    o[0] = odd ? ((r.x << 16) | (head & 0xFFFFu)) : r.x;
+    o[1] = odd ? shr16_pair(r.y, r.x) : r.y;
+    o[2] = odd ? shr16_pair(r.z, r.y) : r.z;
+    o[3] = odd ? shr16_pair(r.w, r.z) : r.w;
   }
 
-  __device__ static void decode(const Wt& w, Dec& o, int u) {
+  __device__ static void decode(const Wt& w, Dec& o, const Lane& l) {
     uint32_t A[4], B[4], C[4];
-    realign(w.A, w.a2, w.odd, A);
-    realign(w.B, w.b2, w.odd, B);
-    realign(w.C, w.c2, w.odd, C);
+    realign(w.A, w.a0, w.odd, A);
+    realign(w.B, w.b0, w.odd, B);
+    realign(w.C, w.c0, w.odd, C);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       o.code[0][k] = (A[k] & 0x0F0F0F0Fu) | ((C[k] << 4) & 0x30303030u);
@@ -337,13 +408,12 @@ struct Q6K {
       o.code[2][k] = ((A[k] >> 4) & 0x0F0F0F0Fu) | (C[k] & 0x30303030u);
       o.code[3][k] = ((B[k] >> 4) & 0x0F0F0F0Fu) | ((C[k] >> 2) & 0x30303030u);
     }
-    const uint32_t s0 = w.odd ? shr16_pair(w.S.y, w.S.x) : w.S.x;   // scales 8h+0..3
-    const uint32_t s1 = w.odd ? shr16_pair(w.s2, w.S.y) : w.S.y;    // scales 8h+4..7
-    const int lq = u & 1;
-    o.sc[0] = __builtin_amdgcn_sbfe(s0, 8 * lq, 8);
-    o.sc[1] = __builtin_amdgcn_sbfe(s0, 8 * lq + 16, 8);
-    o.sc[2] = __builtin_amdgcn_sbfe(s1, 8 * lq, 8);
-    o.sc[3] = __builtin_amdgcn_sbfe(s1, 8 * lq + 16, 8);
+    const uint32_t s0 = w.odd ? ((w.S.x << 16) | (w.s0 & 0xFFFFu)) : w.S.x;   // scales 8h+0..3
+    const uint32_t s1 = w.odd ? shr16_pair(w.S.y, w.S.x) : w.S.y;              // scales 8h+4..7
+    o.sc[0] = sbfe(s0, 8 * l.lq, 8);
+    o.sc[1] = sbfe(s0, 8 * l.lq + 16, 8);
+    o.sc[2] = sbfe(s1, 8 * l.lq, 8);
+    o.sc[3] = sbfe(s1, 8 * l.lq + 16, 8);
     o.d = h2f(w.dbits);
   }
 

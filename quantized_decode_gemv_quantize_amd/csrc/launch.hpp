@@ -11,16 +11,13 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <cstdlib>
 
 #include "../../include/mmvq.h"
 #include "mmvq_kernel.hpp"
+#include "plan.hpp"
 
 namespace qmv {
-
-struct Shape {
-  int units, team_lanes, teams_per_block, rows_per_team;
-  int64_t teams, blocks;
-};
 
 // Compute units of the current device (cached per device id).
 inline int device_cus() {
@@ -43,58 +40,46 @@ inline int units_per_row(int64_t K) {
   return static_cast<int>(K / F::kQK) * F::kUnitsPerBlock;
 }
 
-// Largest K whose row fits one workgroup's team.
-template <class F>
-inline bool row_fits(int64_t K) {
-  return units_per_row<F>(K) <= kLaunchBound;
-}
-
 template <class F>
 inline Shape make_shape(int64_t M, int64_t K, int rmax) {
-  Shape s;
-  s.units = units_per_row<F>(K);
-  s.team_lanes = (s.units + kWave - 1) / kWave * kWave;
-  const int tw = s.team_lanes / kWave;
-  s.teams_per_block = s.team_lanes >= 256 ? 1 : 256 / s.team_lanes;
-  const int64_t cus = device_cus();
-  const int64_t target_teams = cus * (tw >= 16 ? 1 : 16 / tw);
-  int64_t rpt = (M + target_teams - 1) / target_teams;
-  if (rpt < 1) rpt = 1;
-  if (rpt > rmax) rpt = rmax;
-  s.rows_per_team = static_cast<int>(rpt);
-  s.teams = (M + rpt - 1) / rpt;
-  s.blocks = (s.teams + s.teams_per_block - 1) / s.teams_per_block;
-  return s;
-}
-
-// Rows per pass (register budget) of an instantiation.
-template <class F>
-constexpr int rows_per_pass(int nc, int g) {
-  int r;
-  if (F::kType == 14) r = nc == 1 ? 8 : (nc <= 4 ? 4 : 2);          // Q6_K: 19 words/row
-  else r = nc == 1 ? 16 : (nc <= 4 ? 8 : 4);                         // Q4_K, Q4_0
-  return g == 2 ? (r > 1 ? r / 2 : 1) : r;
-}
-
-template <class F>
-constexpr int id_rows_per_pass(int g) {
-  return F::kType == 14 ? (g == 2 ? 1 : 2) : (g == 2 ? 2 : 4);
+  int64_t force = 0;
+#ifdef QMV_TUNING
+  if (const char* e = getenv("MMVQ_FORCE_ROWS")) force = atoi(e);
+#endif
+  return plan_rows(M, units_per_row<F>(K), rmax, device_cus(), QMV_TARGET_WAVES_PER_CU, force);
 }
 
 inline int check_launch() {
   return hipGetLastError() == hipSuccess ? MMVQ_OK : MMVQ_ERR_LAUNCH;
 }
 
-template <class F, int NC, int G>
-inline int launch_rows_nc(RowArgs a, int64_t K, hipStream_t st) {
-  constexpr int R = rows_per_pass<F>(NC, G);
-  const Shape s = make_shape<F>(a.M, K, R);
-  a.units = s.units;
-  a.team_lanes = s.team_lanes;
-  a.rows_per_team = s.rows_per_team;
-  hipLaunchKernelGGL((mmvq_rows_kernel<F, NC, R, G>), dim3(static_cast<unsigned>(s.blocks)),
+template <class F, int NC, int G, int R, int P>
+inline int launch_rows_r(const RowArgs& a, const Shape& s, hipStream_t st) {
+  hipLaunchKernelGGL((mmvq_rows_kernel<F, NC, R, P, G>), dim3(static_cast<unsigned>(s.blocks)),
                      dim3(s.teams_per_block * s.team_lanes), 0, st, a);
   return check_launch();
+}
+
+template <class F, int NC, int G, int R>
+inline int launch_rows_p(const RowArgs& a, const Shape& s, hipStream_t st) {
+  return s.slots == 2 ? launch_rows_r<F, NC, G, R, 2>(a, s, st) : launch_rows_r<F, NC, G, R, 1>(a, s, st);
+}
+
+template <class F, int NC, int G>
+inline int launch_rows_nc(RowArgs a, int64_t K, hipStream_t st) {
+  constexpr int RMAX = rows_per_pass<F>(NC, G);
+  const Shape s = make_shape<F>(a.M, K, RMAX);
+  a.units = s.units;
+  a.team_lanes = s.team_lanes;
+  switch (s.rows) {
+    case 1: return launch_rows_p<F, NC, G, 1>(a, s, st);
+    case 2: if constexpr (RMAX >= 2) return launch_rows_p<F, NC, G, 2>(a, s, st); break;
+    case 4: if constexpr (RMAX >= 4) return launch_rows_p<F, NC, G, 4>(a, s, st); break;
+    case 8: if constexpr (RMAX >= 8) return launch_rows_p<F, NC, G, 8>(a, s, st); break;
+    case 16: if constexpr (RMAX >= 16) return launch_rows_p<F, NC, G, 16>(a, s, st); break;
+    default: break;
+  }
+  return MMVQ_ERR_SHAPE;
 }
 
 template <class F, int G>
@@ -112,17 +97,29 @@ inline int launch_rows(const RowArgs& a, int64_t K, int64_t n, hipStream_t st) {
   }
 }
 
-template <class F, int G>
-inline int launch_id(RowArgs a, int64_t K, int n_experts, hipStream_t st) {
-  constexpr int R = id_rows_per_pass<F>(G);
-  const Shape s = make_shape<F>(a.M, K, R);
-  a.units = s.units;
-  a.team_lanes = s.team_lanes;
-  a.rows_per_team = s.rows_per_team;
-  hipLaunchKernelGGL((mmvq_id_kernel<F, R, G>),
+template <class F, int G, int R, int P>
+inline int launch_id_r(const RowArgs& a, const Shape& s, int n_experts, hipStream_t st) {
+  hipLaunchKernelGGL((mmvq_id_kernel<F, R, P, G>),
                      dim3(static_cast<unsigned>(s.blocks), static_cast<unsigned>(n_experts)),
                      dim3(s.teams_per_block * s.team_lanes), 0, st, a);
   return check_launch();
+}
+
+template <class F, int G>
+inline int launch_id(RowArgs a, int64_t K, int n_experts, hipStream_t st) {
+  constexpr int R = id_rows_per_pass<F>(G);
+  Shape s = make_shape<F>(a.M, K, R);
+  a.units = s.units;
+  a.team_lanes = s.team_lanes;
+  if (s.rows != R) {            // fewer rows than the instantiation holds: one per slot
+    s.rows = 1;
+    s.teams = (a.M + s.slots - 1) / s.slots;
+    s.blocks = (s.teams + s.teams_per_block - 1) / s.teams_per_block;
+    return s.slots == 2 ? launch_id_r<F, G, 1, 2>(a, s, n_experts, st)
+                        : launch_id_r<F, G, 1, 1>(a, s, n_experts, st);
+  }
+  return s.slots == 2 ? launch_id_r<F, G, R, 2>(a, s, n_experts, st)
+                      : launch_id_r<F, G, R, 1>(a, s, n_experts, st);
 }
 
 template <class F>

@@ -28,11 +28,10 @@
 
 #include "common.hpp"
 #include "formats.hpp"
+#include "plan.hpp"
 
 namespace qmv {
 
-constexpr int kLaunchBound = 512;       // 8 waves per workgroup at most
-constexpr int kMaxWavesPerBlock = kLaunchBound / kWave;
 
 struct RowArgs {
   const uint8_t* W;          // up / plain weights (expert 0 in id mode)
@@ -46,7 +45,6 @@ struct RowArgs {
   int64_t expert_stride;
   int units;                 // units per row
   int team_lanes;            // TL: multiple of 64
-  int rows_per_team;         // <= R
   int glu_op;                // 0 plain product, 1 silu(gate) * up
   int n_tokens;              // id mode
   int top_k;                 // id mode
@@ -72,39 +70,59 @@ struct RedLds {
   float v[G][kMaxWavesPerBlock * V];
 };
 
-template <class F, int NC, int R, int G, bool ID, int VMAX>
+// P row slots: when the units of a row fill only part of the last wave,
+// the team covers P rows at once (slot s = lane / units), so a 224-unit row
+// pair fills 7 waves exactly. Lane values are indexed
+// (column j, row i*P + slot); a lane holds zeros for the other slots, and
+// the team reduction sums each value over the lanes of its own slot.
+template <class F, int NC, int R, int P, int G, bool ID, int VMAX>
 __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
                                           const uint8_t* Wbase, const uint8_t* Wgbase,
                                           RedLds<G, VMAX>& red) {
-  constexpr int V = pow2ceil(NC * R);
+  constexpr int RP = R * P;                 // rows per team
+  constexpr int V = pow2ceil(NC * RP);
   static_assert(V <= VMAX, "LDS sized for fewer values");
   const int tid = threadIdx.x;
   const int TL = a.team_lanes;
-  const int team_local = tid / TL;
-  const int lt = tid - team_local * TL;                 // unit index
+  // team index and row window are wave-uniform (teams are whole waves):
+  // keep them scalar so row addresses are SGPR base + per-lane offset
+  const int team_local = __builtin_amdgcn_readfirstlane(tid / TL);
+  const int lt = tid - team_local * TL;
   const int teams_per_block = blockDim.x / TL;
   const int64_t team = static_cast<int64_t>(blockIdx.x) * teams_per_block + team_local;
-  const int64_t row0 = team * a.rows_per_team;
-  const bool active = lt < a.units;
-  const int u = active ? lt : a.units - 1;              // idle lanes re-read a valid unit
+  const Window win = team_window(team, lt, R, P, a.units, a.M);
+  const int64_t row0 = win.row0, skip = win.skip;
+  const int slot = win.slot;
+  const bool active = win.active;
+  const int u = win.unit;
   const int lane = lane_id();
+  const typename F::Lane L = F::lane(u);
+  const int64_t step = static_cast<int64_t>(P) * a.row_bytes;
 
   // ---- issue all weight loads of this team's rows -----------------------
   typename F::Wt w[R];
   typename F::Wt wg[G == 2 ? R : 1];
+  {
+    // uniform row pointers; the slot's row is a per-lane 32-bit offset
+    const uint32_t slot_off = static_cast<uint32_t>(slot * a.row_bytes);
+    const uint8_t* rp = Wbase + row0 * a.row_bytes;
+    const uint8_t* gp = (G == 2) ? Wgbase + row0 * a.row_bytes : nullptr;
 #pragma unroll
-  for (int i = 0; i < R; ++i) {
-    int64_t r = row0 + (i < a.rows_per_team ? i : 0);
-    r = r < a.M ? r : a.M - 1;
-    F::load_wt(w[i], Wbase + r * a.row_bytes, u);
-    if constexpr (G == 2) F::load_wt(wg[i], Wgbase + r * a.row_bytes, u);
+    for (int i = 0; i < R; ++i) {
+      F::load_wt(w[i], rp, slot_off, L);
+      rp += step;
+      if constexpr (G == 2) {
+        F::load_wt(wg[i], gp, slot_off, L);
+        gp += step;
+      }
+    }
   }
-  // ---- activation slice of every column ----------------------------------
+  // ---- activation slice of every column (zero for idle lanes) -----------
   typename F::Act act[NC];
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
-    const int t = (!ID || j < cols.n) ? cols.tok[j] : cols.tok[0];
-    F::load_act(act[j], a.y + t * a.ycol_bytes, u);
+    F::load_act(act[j], a.y + cols.tok[j] * a.ycol_bytes, u);
+    if (!active) F::zero_act(act[j]);
   }
 
   // ---- per row: decode once, one partial per column ----------------------
@@ -113,22 +131,24 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
   for (int p = 0; p < G; ++p)
 #pragma unroll
     for (int k = 0; k < V; ++k) part[p][k] = 0.0f;
+  auto put = [&](int p, int j, int i, float v) {
+    if constexpr (P == 1) {
+      part[p][j * RP + i] = v;
+    } else {
+#pragma unroll
+      for (int s = 0; s < P; ++s) part[p][j * RP + i * P + s] = slot == s ? v : 0.0f;
+    }
+  };
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     typename F::Dec dec;
-    F::decode(w[i], dec, u);
+    F::decode(w[i], dec, L);
 #pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      const float v = F::col_dot(dec, act[j]);
-      part[0][j * R + i] = active ? v : 0.0f;
-    }
+    for (int j = 0; j < NC; ++j) put(0, j, i, F::col_dot(dec, act[j]));
     if constexpr (G == 2) {
-      F::decode(wg[i], dec, u);
+      F::decode(wg[i], dec, L);
 #pragma unroll
-      for (int j = 0; j < NC; ++j) {
-        const float v = F::col_dot(dec, act[j]);
-        part[1][j * R + i] = active ? v : 0.0f;
-      }
+      for (int j = 0; j < NC; ++j) put(1, j, i, F::col_dot(dec, act[j]));
     }
   }
 
@@ -137,11 +157,9 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
   using RM = ReduceMap<kWave, V>;
 
   auto store = [&](int idx, float up, float gate) {
-    const int j = idx / R, i = idx - j * R;
-    if (j >= NC || i >= a.rows_per_team) return;
-    if (ID && j >= cols.n) return;
+    const int j = idx / RP, i = idx - j * RP;
+    if (j >= NC || i < skip) return;
     const int64_t r = row0 + i;
-    if (r >= a.M) return;
     const float v = (G == 2) ? glu(a.glu_op, gate, up) : up;
     if constexpr (ID) {
       // select column j's token and slots with compile-time indices
@@ -181,7 +199,7 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
     __syncthreads();
     const int tw = TL / kWave;
     const int wave0 = team_local * tw;
-    for (int idx = lt; idx < NC * R; idx += TL) {
+    for (int idx = lt; idx < NC * RP; idx += TL) {
       float s[G];
 #pragma unroll
       for (int p = 0; p < G; ++p) {
@@ -194,20 +212,20 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
 }
 
 // Plain / fused kernel: columns 0..NC-1 of y.
-template <class F, int NC, int R, int G>
+template <class F, int NC, int R, int P, int G>
 __global__ void __launch_bounds__(kLaunchBound) mmvq_rows_kernel(RowArgs a) {
   Cols cols;
   cols.n = NC;
 #pragma unroll
   for (int j = 0; j < kMaxCols; ++j) { cols.tok[j] = j; cols.slots[j] = 0; }
-  constexpr int V = pow2ceil(NC * R);
+  constexpr int V = pow2ceil(NC * R * P);
   __shared__ RedLds<G, V> red;
-  rows_body<F, NC, R, G, false, V>(a, cols, a.W, a.Wg, red);
+  rows_body<F, NC, R, P, G, false, V>(a, cols, a.W, a.Wg, red);
 }
 
 // Expert-indexed kernel: blockIdx.y = expert. The token list is the same for
 // every thread of the block (ids are read with uniform addresses).
-template <class F, int R, int G>
+template <class F, int R, int P, int G>
 __global__ void __launch_bounds__(kLaunchBound) mmvq_id_kernel(RowArgs a) {
   const int e = blockIdx.y;
   // Tokens routed to expert e, compacted with compile-time indices only (a
@@ -236,17 +254,17 @@ __global__ void __launch_bounds__(kLaunchBound) mmvq_id_kernel(RowArgs a) {
   if (cols.n == 0) return;     // uniform: the whole block leaves together
   const uint8_t* We = a.W + static_cast<int64_t>(e) * a.expert_stride;
   const uint8_t* Wge = G == 2 ? a.Wg + static_cast<int64_t>(e) * a.expert_stride : nullptr;
-  constexpr int VMAX = pow2ceil(kMaxCols * R);
+  constexpr int VMAX = pow2ceil(kMaxCols * R * P);
   __shared__ RedLds<G, VMAX> red;
   switch (cols.n) {
-    case 1: rows_body<F, 1, R, G, true, VMAX>(a, cols, We, Wge, red); break;
-    case 2: rows_body<F, 2, R, G, true, VMAX>(a, cols, We, Wge, red); break;
-    case 3: rows_body<F, 3, R, G, true, VMAX>(a, cols, We, Wge, red); break;
-    case 4: rows_body<F, 4, R, G, true, VMAX>(a, cols, We, Wge, red); break;
-    case 5: rows_body<F, 5, R, G, true, VMAX>(a, cols, We, Wge, red); break;
-    case 6: rows_body<F, 6, R, G, true, VMAX>(a, cols, We, Wge, red); break;
-    case 7: rows_body<F, 7, R, G, true, VMAX>(a, cols, We, Wge, red); break;
-    default: rows_body<F, 8, R, G, true, VMAX>(a, cols, We, Wge, red); break;
+    case 1: rows_body<F, 1, R, P, G, true, VMAX>(a, cols, We, Wge, red); break;
+    case 2: rows_body<F, 2, R, P, G, true, VMAX>(a, cols, We, Wge, red); break;
+    case 3: rows_body<F, 3, R, P, G, true, VMAX>(a, cols, We, Wge, red); break;
+    case 4: rows_body<F, 4, R, P, G, true, VMAX>(a, cols, We, Wge, red); break;
+    case 5: rows_body<F, 5, R, P, G, true, VMAX>(a, cols, We, Wge, red); break;
+    case 6: rows_body<F, 6, R, P, G, true, VMAX>(a, cols, We, Wge, red); break;
+    case 7: rows_body<F, 7, R, P, G, true, VMAX>(a, cols, We, Wge, red); break;
+    default: rows_body<F, 8, R, P, G, true, VMAX>(a, cols, We, Wge, red); break;
   }
 }
 
@@ -267,10 +285,11 @@ __global__ void __launch_bounds__(256) mmvq_block_dots_kernel(const uint8_t* W, 
   for (int k = 0; k < F::kDotsPerBlock; ++k) acc[k] = 0;
   for (int q = 0; q < F::kUnitsPerBlock; ++q) {
     const int u = static_cast<int>(b) * F::kUnitsPerBlock + q;
+    const typename F::Lane L = F::lane(u);
     typename F::Wt w;
-    F::load_wt(w, W + r * row_bytes, u);
+    F::load_wt(w, W + r * row_bytes, 0u, L);
     typename F::Dec dec;
-    F::decode(w, dec, u);
+    F::decode(w, dec, L);
     F::int_dots(dec, y + j * ycol_bytes, u, acc);
   }
   int32_t* o = dots + gid * F::kDotsPerBlock;

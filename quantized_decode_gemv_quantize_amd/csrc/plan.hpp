@@ -1,0 +1,100 @@
+// plan.hpp - launch shape and per-lane row window of the MMVQ kernels.
+//
+// Pure integer arithmetic shared by the host launcher, the kernels and the
+// host model of the kernels' addressing (which checks every load of every
+// lane against the buffers on the CPU).
+#pragma once
+
+#include "common.hpp"
+
+namespace qmv {
+
+// Waves per compute unit the row split aims for: enough to keep every
+// CU's share of the matrix in flight in one round of resident waves.
+#ifndef QMV_TARGET_WAVES_PER_CU
+#define QMV_TARGET_WAVES_PER_CU 8
+#endif
+
+struct Shape {
+  int units;            // units per row
+  int slots;            // rows a team covers per step (P)
+  int team_lanes;       // lanes per team (whole waves)
+  int teams_per_block;
+  int rows;             // rows per slot (R)
+  int64_t teams, blocks;
+};
+
+inline int pow2floor(int64_t v) {
+  int p = 1;
+  while (static_cast<int64_t>(p) * 2 <= v) p *= 2;
+  return p;
+}
+
+// Team layout and rows per team for an M-row matrix whose rows hold `units`
+// units:
+//  * slots P = 2 when a row's units fill whole waves only in pairs (e.g.
+//    224 units), else 1 (idle lanes pad the last wave);
+//  * rows per slot R: a power of two, at most rmax (register budget), with
+//    R*P <= M, sized for about `target_waves` waves per CU (force_rows > 0
+//    overrides the size, for tuning).
+inline Shape plan_rows(int64_t M, int units, int rmax, int64_t cus, int target_waves, int64_t force_rows) {
+  Shape s;
+  s.units = units;
+  s.slots = (units % kWave != 0 && (2 * units) % kWave == 0 && 2 * units <= kLaunchBound && M >= 2) ? 2 : 1;
+  s.team_lanes = (s.slots * units + kWave - 1) / kWave * kWave;
+  const int tw = s.team_lanes / kWave;
+  s.teams_per_block = s.team_lanes >= 256 ? 1 : 256 / s.team_lanes;
+  int64_t want = force_rows > 0 ? force_rows : M * tw / (cus * target_waves * s.slots);
+  int r = pow2floor(want < 1 ? 1 : want);
+  if (r > rmax) r = rmax;
+  if (static_cast<int64_t>(r) * s.slots > M) r = pow2floor(M / s.slots);
+  s.rows = r;
+  const int64_t rp = static_cast<int64_t>(r) * s.slots;
+  s.teams = (M + rp - 1) / rp;
+  s.blocks = (s.teams + s.teams_per_block - 1) / s.teams_per_block;
+  return s;
+}
+
+// Largest rows per slot (register budget) of an instantiation.
+template <class F>
+constexpr int rows_per_pass(int nc, int g) {
+  int r = 1;
+  if (F::kType == 14) r = nc == 1 ? 8 : (nc == 2 ? 4 : (nc <= 4 ? 2 : 1));   // Q6_K: 19 + 24n words
+  else if (F::kType == 12) r = nc <= 2 ? 8 : (nc <= 4 ? 4 : 2);              // Q4_K: 12 + 20n words
+  else r = nc == 1 ? 16 : (nc <= 4 ? 8 : 4);                                 // Q4_0: 5 + 10n words
+  return g == 2 ? (r > 1 ? r / 2 : 1) : r;
+}
+
+template <class F>
+constexpr int id_rows_per_pass(int g) {
+  return F::kType == 14 ? 1 : (F::kType == 12 ? (g == 2 ? 1 : 2) : (g == 2 ? 2 : 4));
+}
+
+// Row window of one team and the unit / slot of one of its lanes.
+// The team owns rows [first, first + RP); the last team's window is moved
+// back to end at row M-1 (M >= RP), and rows of the window below `first`
+// (owned by the previous team) are skipped at the store. Lanes past the
+// units of their slot are idle: they re-read the last unit and contribute 0.
+struct Window {
+  int64_t row0;     // first row of the window
+  int64_t skip;     // leading window rows not stored by this team
+  int slot;         // row slot of the lane (0 .. P-1)
+  int unit;         // unit the lane loads (valid even when idle)
+  bool active;
+};
+
+__host__ __device__ __forceinline__ Window team_window(int64_t team, int lt, int R, int P, int units,
+                                                       int64_t M) {
+  Window w;
+  const int64_t rp = static_cast<int64_t>(R) * P;
+  const int64_t first = team * rp;
+  w.row0 = first + rp <= M ? first : M - rp;
+  w.skip = first - w.row0;
+  w.slot = (P == 1 || lt < units) ? 0 : 1;       // P <= 2
+  const int lu = lt - w.slot * units;
+  w.active = lu < units;
+  w.unit = w.active ? lu : units - 1;
+  return w;
+}
+
+}  // namespace qmv

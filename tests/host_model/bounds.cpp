@@ -1,0 +1,241 @@
+// Host model of the MMVQ kernels' memory accesses.
+//
+// Compiled for the host with QMV_HOST_MODEL, the kernels' own format and
+// planning code (formats.hpp, plan.hpp) runs for every workgroup, team, lane
+// and row of the launch the library would make, with loads replaced by
+// bounds-checked host reads. Checks, for every case:
+//   * every weight, header, scale and activation load lies inside its
+//     buffer and is aligned as the device load requires;
+//   * every output row of every column is stored exactly once;
+//   * the quantizer's and the block-dot kernel's loads stay in bounds.
+// Prints one line per failing case and exits non-zero if any case fails.
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <vector>
+
+#include "formats.hpp"
+#include "plan.hpp"
+
+using namespace qmv;
+
+static uint8_t* alloc16(size_t n) {
+  // exactly n usable bytes at a 16-byte aligned address
+  void* p = aligned_alloc(16, (n + 15) / 16 * 16 + 16);
+  memset(p, 0x5A, (n + 15) / 16 * 16 + 16);
+  return static_cast<uint8_t*>(p);
+}
+
+static int failures = 0;
+
+static void begin(std::initializer_list<hostmodel::Range> rs) {
+  hostmodel::ranges().assign(rs.begin(), rs.end());
+  hostmodel::violations() = 0;
+  hostmodel::accesses() = 0;
+}
+
+static void report(const char* what, bool ok_extra, const char* name, int64_t M, int64_t K, int nc, int g) {
+  if (hostmodel::violations() != 0 || !ok_extra) {
+    ++failures;
+    printf("FAIL %s %s M=%lld K=%lld n=%d g=%d: %ld bad of %ld accesses%s\n", what, name, (long long)M,
+           (long long)K, nc, g, hostmodel::violations(), hostmodel::accesses(), ok_extra ? "" : ", store coverage");
+  }
+}
+
+// One launch of the rows kernel (plain G=1 or fused G=2), or of the id
+// kernel for one expert (base = expert's matrix, tok = its token columns).
+template <class F>
+static bool model_rows(const Shape& s, int R, int P, int G, int64_t M, const uint8_t* W, const uint8_t* Wg,
+                       int64_t row_bytes, const uint8_t* y, int64_t ycol_bytes, const int* tok, int nc,
+                       std::vector<int>& stores) {
+  typename F::Wt wt;
+  typename F::Act act;
+  typename F::Dec dec;
+  for (int64_t b = 0; b < s.blocks; ++b) {
+    for (int tl = 0; tl < s.teams_per_block; ++tl) {
+      const int64_t team = b * s.teams_per_block + tl;
+      for (int lt = 0; lt < s.team_lanes; ++lt) {
+        const Window w = team_window(team, lt, R, P, s.units, M);
+        const typename F::Lane L = F::lane(w.unit);
+        const uint32_t slot_off = static_cast<uint32_t>(w.slot * row_bytes);
+        const uint8_t* rp = W + w.row0 * row_bytes;
+        const uint8_t* gp = Wg ? Wg + w.row0 * row_bytes : nullptr;
+        for (int i = 0; i < R; ++i) {
+          F::load_wt(wt, rp, slot_off, L);
+          F::decode(wt, dec, L);
+          rp += P * row_bytes;
+          if (G == 2) {
+            F::load_wt(wt, gp, slot_off, L);
+            gp += P * row_bytes;
+          }
+        }
+        for (int j = 0; j < nc; ++j) F::load_act(act, y + tok[j] * ycol_bytes, w.unit);
+        if (lt == 0) {   // the store pattern of the team (one lane's view suffices)
+          for (int64_t i = w.skip; i < static_cast<int64_t>(R) * P; ++i) {
+            const int64_t r = w.row0 + i;
+            if (r < 0 || r >= M) return false;
+            stores[r] += 1;
+          }
+        }
+      }
+    }
+  }
+  return true;
+}
+
+template <class F>
+static void case_rows(const char* name, int64_t M, int64_t K, int nc, int g) {
+  const int64_t row_bytes = K / F::kQK * F::kBlockBytes;
+  const int64_t ycol = K / 32 * kQ8Bytes;
+  uint8_t* W = alloc16(M * row_bytes);
+  uint8_t* Wg = g == 2 ? alloc16(M * row_bytes) : nullptr;
+  uint8_t* y = alloc16(nc * ycol);
+  const int units = static_cast<int>(K / F::kQK) * F::kUnitsPerBlock;
+  const Shape s = plan_rows(M, units, rows_per_pass<F>(nc, g), 256, QMV_TARGET_WAVES_PER_CU, 0);
+  bool ok = s.team_lanes <= kLaunchBound && s.rows * s.slots <= M;
+  int tok[kMaxCols];
+  for (int j = 0; j < kMaxCols; ++j) tok[j] = j;
+  std::vector<int> stores(M, 0);
+  if (Wg) begin({{W, W + M * row_bytes}, {Wg, Wg + M * row_bytes}, {y, y + nc * ycol}});
+  else begin({{W, W + M * row_bytes}, {y, y + nc * ycol}});
+  ok = ok && model_rows<F>(s, s.rows, s.slots, g, M, W, Wg, row_bytes, y, ycol, tok, nc, stores);
+  for (int64_t r = 0; r < M && ok; ++r) ok = stores[r] == 1;
+  report("rows", ok, name, M, K, nc, g);
+  free(W);
+  free(Wg);
+  free(y);
+}
+
+// id kernel: every expert with tokens reads its own matrix at e * stride.
+template <class F>
+static void case_id(const char* name, int64_t M, int64_t K, int E, int T, int g) {
+  const int64_t row_bytes = K / F::kQK * F::kBlockBytes;
+  const int64_t stride = (M * row_bytes + 15) / 16 * 16;
+  const int64_t ycol = K / 32 * kQ8Bytes;
+  uint8_t* W = alloc16(E * stride);
+  uint8_t* Wg = alloc16(E * stride);
+  uint8_t* y = alloc16(T * ycol);
+  const int units = static_cast<int>(K / F::kQK) * F::kUnitsPerBlock;
+  const int R = id_rows_per_pass<F>(g);
+  Shape s = plan_rows(M, units, R, 256, QMV_TARGET_WAVES_PER_CU, 0);
+  int r = R;
+  if (s.rows != R) {       // same fallback as the launcher
+    r = 1;
+    s.rows = 1;
+    s.teams = (M + s.slots - 1) / s.slots;
+    s.blocks = (s.teams + s.teams_per_block - 1) / s.teams_per_block;
+  }
+  begin({{W, W + E * stride}, {Wg, Wg + E * stride}, {y, y + T * ycol}});
+  bool ok = true;
+  for (int e = 0; e < E && ok; ++e) {
+    int tok[kMaxCols];
+    const int nt = T < kMaxCols ? T : kMaxCols;
+    for (int j = 0; j < nt; ++j) tok[j] = (j + e) % T;
+    std::vector<int> stores(M, 0);
+    ok = model_rows<F>(s, r, s.slots, g, M, W + e * stride, g == 2 ? Wg + e * stride : nullptr, row_bytes, y,
+                       ycol, tok, nt, stores);
+    for (int64_t q = 0; q < M && ok; ++q) ok = stores[q] == 1;
+  }
+  report("id", ok, name, M, K, T, g);
+  free(W);
+  free(Wg);
+  free(y);
+}
+
+template <class F>
+static void case_block_dots(const char* name, int64_t M, int64_t K, int nc) {
+  const int64_t row_bytes = K / F::kQK * F::kBlockBytes;
+  const int64_t nb = K / F::kQK;
+  const int64_t ycol = K / 32 * kQ8Bytes;
+  uint8_t* W = alloc16(M * row_bytes);
+  uint8_t* y = alloc16(nc * ycol);
+  begin({{W, W + M * row_bytes}, {y, y + nc * ycol}});
+  typename F::Wt wt;
+  typename F::Dec dec;
+  int dots[F::kDotsPerBlock];
+  for (int j = 0; j < nc; ++j)
+    for (int64_t r = 0; r < M; ++r)
+      for (int64_t b = 0; b < nb; ++b)
+        for (int q = 0; q < F::kUnitsPerBlock; ++q) {
+          const int u = static_cast<int>(b) * F::kUnitsPerBlock + q;
+          const typename F::Lane L = F::lane(u);
+          F::load_wt(wt, W + r * row_bytes, 0u, L);
+          F::decode(wt, dec, L);
+          F::int_dots(dec, y + j * ycol, u, dots);
+        }
+  report("block_dots", true, name, M, K, nc, 1);
+  free(W);
+  free(y);
+}
+
+// quantizer: 8 lanes per q8_1 block, 4 floats each (clamped to block 0 when
+// past the end), column j at x + j*ldx
+static void case_quantize(int64_t K, int64_t n, int64_t ldx) {
+  const int64_t nb = K / 32;
+  uint8_t* x = alloc16(((n - 1) * ldx + K) * 4);
+  begin({{x, x + ((n - 1) * ldx + K) * 4}});
+  const int64_t threads = (n * nb * 8 + 255) / 256 * 256;
+  for (int64_t gid = 0; gid < threads; ++gid) {
+    const int64_t blk = gid >> 3;
+    const int sub = static_cast<int>(gid & 7);
+    const int64_t bc = blk < n * nb ? blk : 0;
+    const int64_t j = bc / nb, b = bc - j * nb;
+    (void)ld_x4(x + 4 * (j * ldx + 32 * b + 4 * sub));
+  }
+  report("quantize", true, "q8_1", n, K, static_cast<int>(n), 1);
+  free(x);
+}
+
+int main(int argc, char** argv) {
+  const bool full = argc > 1 && strcmp(argv[1], "full") == 0;
+  const int64_t Ms[] = {1, 2, 3, 5, 7, 8, 9, 15, 16, 17, 31, 33, 64, 100, 129, 300, 1000};
+  for (int64_t M : Ms) {
+    for (int nb : {1, 2, 3, 5, 7, 8, 9, 16, 56}) {
+      for (int nc = 1; nc <= 8; ++nc) {
+        for (int g = 1; g <= 2; ++g) {
+          if (nb <= 16 || nc <= 2) {
+            case_rows<Q4K>("q4_k", M, 256LL * nb, nc, g);
+            case_rows<Q6K>("q6_k", M, 256LL * nb, nc, g);
+          }
+          if (nb * 8 * 32 <= 16384 && (nb <= 16 || nc <= 2)) case_rows<Q40>("q4_0", M, 32LL * nb * 8, nc, g);
+          case_rows<Q40>("q4_0", M, 32LL * nb, nc, g);
+        }
+      }
+      if (M <= 64) {
+        case_block_dots<Q4K>("q4_k", M, 256LL * nb, 2);
+        case_block_dots<Q6K>("q6_k", M, 256LL * nb, 2);
+        case_block_dots<Q40>("q4_0", M, 32LL * nb, 2);
+      }
+    }
+  }
+  // longest rows a team can hold
+  case_rows<Q4K>("q4_k", 129, 16384, 1, 1);
+  case_rows<Q4K>("q4_k", 65, 32768, 8, 1);
+  case_rows<Q4K>("q4_k", 65, 32768, 1, 2);
+  case_rows<Q40>("q4_0", 129, 16384, 8, 2);
+  case_rows<Q6K>("q6_k", 129, 32768, 1, 1);
+  for (int g = 1; g <= 2; ++g) {
+    case_id<Q4K>("q4_k", 200, 512, 4, 3, g);
+    case_id<Q4K>("q4_k", 300, 2048, 8, 8, g);
+    case_id<Q40>("q4_0", 77, 1024, 5, 4, g);
+    case_id<Q6K>("q6_k", 50, 768, 4, 2, g);
+    case_id<Q4K>("q4_k", 1, 256, 3, 1, g);
+  }
+  for (int64_t K : {32, 64, 96, 1024, 14336})
+    for (int64_t n : {1, 3, 8})
+      for (int64_t pad : {0, 1, 3, 64}) case_quantize(K, n, K + pad);
+  if (full) {   // the benchmark workloads
+    for (int nc : {1, 2, 4, 8}) {
+      case_rows<Q4K>("q4_k", 4096, 14336, nc, 1);
+      case_rows<Q4K>("q4_k", 14336, 4096, nc, 1);
+    }
+    case_rows<Q4K>("q4_k", 4096, 4096, 1, 1);
+    case_rows<Q40>("q4_0", 256, 1024, 1, 1);
+    case_rows<Q6K>("q6_k", 128256, 4096, 1, 1);
+    case_id<Q4K>("q4_k", 14336, 4096, 8, 8, 2);
+    case_id<Q4K>("q4_k", 14336, 4096, 8, 8, 1);
+  }
+  printf("host model: %d failing case(s)\n", failures);
+  return failures ? 1 : 0;
+}
