@@ -10,8 +10,8 @@
 // so it loads the matching activation codes once and keeps them in
 // registers. Units are chosen so that a wave's weight loads for one row are
 // contiguous 16-byte pieces:
-//   Q4_K: unit = 32 bytes of codes of one super-block (64 weights, two
-//         sub-blocks; 4 units per super-block), plus its 16-byte header.
+//   Q4_K: unit = 16 bytes of codes of one super-block (32 weights; 8 units
+//         per super-block), plus that super-block's 16-byte header.
 //   Q4_0: unit = one 18-byte block (32 weights).
 //   Q6_K: unit = one quarter of a super-block (64 weights): 2 x 16 bytes of
 //         low bits, 16 bytes of high bits, 4 int8 scales, the fp16 d.
@@ -46,36 +46,35 @@ __device__ __forceinline__ int bsum4(uint32_t w, int c) { return dot4(w, 0x01010
 // mins @4, 128 bytes of nibbles @16. Sub-block t (32 weights) of 64-element
 // chunk c = t/2 reads the low (t even) or high (t odd) nibbles of
 // qs[32c .. 32c+31]. Weight = d*sc_t*q - dmin*m_t.
-// Unit u: super-block sb = u/4, chunk c = u%4: the 32 code bytes
-// qs[32c ..] (64 weights) = sub-blocks t0 = 2c (low nibbles) and t1 = 2c+1
-// (high nibbles), with their q8_1 blocks 8sb+2c and 8sb+2c+1.
+// Unit u: super-block sb = u/8, p = u%8, chunk c = p/2, half = p%2: the 16
+// code bytes qs[32c + 16*half ..] hold elements 16*half .. 16*half+15 of
+// sub-blocks t0 = 2c (low nibbles) and t1 = 2c+1 (high nibbles). A wave's 64
+// lanes read 8 super-blocks' codes as 8 contiguous 128-byte runs.
 // ===========================================================================
 struct Q4K {
   static constexpr int kType = 12, kQK = 256, kBlockBytes = 144;
-  static constexpr int kUnitsPerBlock = 4, kDotsPerBlock = 16;
+  static constexpr int kUnitsPerBlock = 8, kDotsPerBlock = 16;
 
   struct Act {
-    uint32_t y0[8], y1[8];   // activation codes paired with the t0 / t1 nibbles
+    uint32_t y0[4], y1[4];   // activation codes paired with the t0 / t1 nibbles
     float d0, d1;            // q8_1 scales of the two sub-blocks
-    float s0, s1;            // d8 * (sum of the 32 codes): exact in fp32
+    float s0, s1;            // d8 * (sum of the 16 codes): exact in fp32
   };
 
-  __device__ static void act_codes(const uint8_t* ycol, int u, uint32_t (&q0)[8], uint32_t (&q1)[8],
+  __device__ static void act_codes(const uint8_t* ycol, int u, uint32_t (&q0)[4], uint32_t (&q1)[4],
                                    const uint8_t*& b0, const uint8_t*& b1) {
-    const int sb = u >> 2, c = u & 3;
+    const int sb = u >> 3, p = u & 7, c = p >> 1, half = p & 1;
     b0 = ycol + static_cast<int64_t>(8 * sb + 2 * c) * kQ8Bytes;
     b1 = b0 + kQ8Bytes;
-    const u32x4 a0 = ld_x4(b0 + 4), a1 = ld_x4(b0 + 20), c0 = ld_x4(b1 + 4), c1 = ld_x4(b1 + 20);
+    const u32x4 a0 = ld_x4(b0 + 4 + 16 * half), a1 = ld_x4(b1 + 4 + 16 * half);
     q0[0] = a0.x; q0[1] = a0.y; q0[2] = a0.z; q0[3] = a0.w;
-    q0[4] = a1.x; q0[5] = a1.y; q0[6] = a1.z; q0[7] = a1.w;
-    q1[0] = c0.x; q1[1] = c0.y; q1[2] = c0.z; q1[3] = c0.w;
-    q1[4] = c1.x; q1[5] = c1.y; q1[6] = c1.z; q1[7] = c1.w;
+    q1[0] = a1.x; q1[1] = a1.y; q1[2] = a1.z; q1[3] = a1.w;
   }
 
-  __device__ static int sum8(const uint32_t (&q)[8]) {
+  __device__ static int sum4(const uint32_t (&q)[4]) {
     int s = 0;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) s = bsum4(q[k], s);
+    for (int k = 0; k < 4; ++k) s = bsum4(q[k], s);
     return s;
   }
 
@@ -84,13 +83,13 @@ struct Q4K {
     act_codes(ycol, u, a.y0, a.y1, b0, b1);
     a.d0 = q8_d(b0);
     a.d1 = q8_d(b1);
-    a.s0 = a.d0 * static_cast<float>(sum8(a.y0));
-    a.s1 = a.d1 * static_cast<float>(sum8(a.y1));
+    a.s0 = a.d0 * static_cast<float>(sum4(a.y0));
+    a.s1 = a.d1 * static_cast<float>(sum4(a.y1));
   }
 
   __device__ static void zero_act(Act& a) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) { a.y0[k] = 0; a.y1[k] = 0; }
+    for (int k = 0; k < 4; ++k) { a.y0[k] = 0; a.y1[k] = 0; }
     a.d0 = a.d1 = a.s0 = a.s1 = 0.0f;
   }
 
@@ -110,9 +109,9 @@ struct Q4K {
   };
   __device__ static Lane lane(int u) {
     Lane l;
-    const int sb = u >> 2, c = u & 3;
+    const int sb = u >> 3, p = u & 7, c = p >> 1;
     l.hoff = static_cast<uint32_t>(sb * kBlockBytes);
-    l.qoff = l.hoff + 16 + 32 * c;
+    l.qoff = l.hoff + 16 + 16 * p;
     l.lo = c < 2;
     l.sh = 16u * (c & 1);
     l.shm = l.lo ? l.sh : l.sh + 4;
@@ -122,19 +121,19 @@ struct Q4K {
   }
 
   struct Wt {
-    u32x4 q0, q1;  // 32 code bytes
-    u32x4 hdr;     // d | dmin, scales[0..3], scales[4..7], scales[8..11]
+    u32x4 qs;    // 16 code bytes
+    u32x4 hdr;   // d | dmin, scales[0..3], scales[4..7], scales[8..11]
   };
 
-  // row: wave-uniform row start; extra: per-lane byte offset added to it
+  // row: wave-uniform row start (16-byte aligned: 144-byte blocks, 16-byte
+  // base); extra: per-lane byte offset added to it
   __device__ static void load_wt(Wt& w, const uint8_t* row, uint32_t extra, const Lane& l) {
-    w.q0 = ld_nt_x4(row + (extra + l.qoff));
-    w.q1 = ld_nt_x4(row + (extra + l.qoff + 16));
     w.hdr = ld_x4(row + (extra + l.hoff));
+    w.qs = ld_nt_x4(row + (extra + l.qoff));
   }
 
   struct Dec {
-    uint32_t lo[8], hi[8];   // nibbles of t0 and t1 as unsigned bytes
+    uint32_t lo[4], hi[4];   // nibbles of t0 and t1 as unsigned bytes
     uint32_t scp;            // sc of t0 (byte 0) and t1 (byte 1)
     float m0, m1, d, dmin;
   };
@@ -142,10 +141,8 @@ struct Q4K {
   __device__ static void decode(const Wt& w, Dec& o, const Lane& l) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      o.lo[k] = w.q0[k] & 0x0F0F0F0Fu;
-      o.hi[k] = (w.q0[k] >> 4) & 0x0F0F0F0Fu;
-      o.lo[4 + k] = w.q1[k] & 0x0F0F0F0Fu;
-      o.hi[4 + k] = (w.q1[k] >> 4) & 0x0F0F0F0Fu;
+      o.lo[k] = w.qs[k] & 0x0F0F0F0Fu;
+      o.hi[k] = (w.qs[k] >> 4) & 0x0F0F0F0Fu;
     }
     o.d = h2f(w.hdr.x);
     o.dmin = h2f(w.hdr.x >> 16);
@@ -161,7 +158,7 @@ struct Q4K {
     dot0 = 0;
     dot1 = 0;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < 4; ++k) {
       dot0 = dot4(o.lo[k], a.y0[k], dot0);
       dot1 = dot4(o.hi[k], a.y1[k], dot1);
     }
@@ -184,11 +181,11 @@ struct Q4K {
     load_act(a, ycol, u);
     int dot0, dot1;
     nibble_dots(o, a, dot0, dot1);
-    const int c = u & 3;
+    const int c = (u & 7) >> 1;
     dots[2 * c] += dot0;
     dots[2 * c + 1] += dot1;
-    dots[8 + 2 * c] += sum8(a.y0);
-    dots[8 + 2 * c + 1] += sum8(a.y1);
+    dots[8 + 2 * c] += sum4(a.y0);
+    dots[8 + 2 * c + 1] += sum4(a.y1);
   }
 };
 

@@ -99,6 +99,15 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
   const typename F::Lane L = F::lane(u);
   const int64_t step = static_cast<int64_t>(P) * a.row_bytes;
 
+  // ---- activation slice of every column (zero for idle lanes) -----------
+  typename F::Act act[NC];
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    F::load_act(act[j], a.y + cols.tok[j] * a.ycol_bytes, u);
+    if (!active) F::zero_act(act[j]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
   // ---- issue all weight loads of this team's rows -----------------------
   typename F::Wt w[R];
   typename F::Wt wg[G == 2 ? R : 1];
@@ -115,16 +124,11 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
         F::load_wt(wg[i], gp, slot_off, L);
         gp += step;
       }
+      // keep the loads in row order: row i's arithmetic then waits only for
+      // rows 0..i (the vector memory counter retires loads in issue order)
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
-  // ---- activation slice of every column (zero for idle lanes) -----------
-  typename F::Act act[NC];
-#pragma unroll
-  for (int j = 0; j < NC; ++j) {
-    F::load_act(act[j], a.y + cols.tok[j] * a.ycol_bytes, u);
-    if (!active) F::zero_act(act[j]);
-  }
-
   // ---- per row: decode once, one partial per column ----------------------
   float part[G][V];
 #pragma unroll

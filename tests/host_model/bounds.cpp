@@ -211,8 +211,8 @@ int main(int argc, char** argv) {
   }
   // longest rows a team can hold
   case_rows<Q4K>("q4_k", 129, 16384, 1, 1);
-  case_rows<Q4K>("q4_k", 65, 32768, 8, 1);
-  case_rows<Q4K>("q4_k", 65, 32768, 1, 2);
+  case_rows<Q4K>("q4_k", 65, 16384, 8, 1);
+  case_rows<Q4K>("q4_k", 65, 16384, 1, 2);
   case_rows<Q40>("q4_0", 129, 16384, 8, 2);
   case_rows<Q6K>("q6_k", 129, 32768, 1, 1);
   for (int g = 1; g <= 2; ++g) {

@@ -53,7 +53,7 @@ P16, P4 = 1 << 20, (1 << 20) + 4
     ((P16, B.Q4_K, 0, 256, P16, 1, P16), B.ERR_SHAPE),
     ((P16, B.Q4_K, 1, 256, P16, 0, P16), B.ERR_SHAPE),
     ((P16, B.Q4_K, 1, 256, P16, 9, P16), B.ERR_SHAPE),
-    ((P16, B.Q4_K, 1, 256 * 129, P16, 1, P16), B.ERR_SHAPE),
+    ((P16, B.Q4_K, 1, 256 * 65, P16, 1, P16), B.ERR_SHAPE),
     ((P16, B.Q6_K, 1, 256 * 129, P16, 1, P16), B.ERR_SHAPE),
     ((P4, B.Q4_K, 1, 256, P16, 1, P16), B.ERR_ALIGN),
     ((P16, B.Q4_K, 1, 256, P4, 1, P16), B.ERR_ALIGN),
