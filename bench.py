@@ -37,6 +37,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "quantized_decode_gemv_quantize_amd", "csrc")
 LLC_BYTES = 256 * 2 ** 20    # MI355X Infinity Cache
 TOKENS_DENOM_GB = 3.9        # weight bytes of one decode step of a 7B Q4_K model
 
@@ -53,7 +55,119 @@ def parse():
                    help="wall-clock budget of the oracle baseline (0 disables it)")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a plain device copy of known size (counter calibration)")
+    p.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                   help="write profiles/ summaries from rocprofv3 csv output and exit")
     return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the HIP sources and build flags: counters taken on one
+    kernel build are reported only while the sources are unchanged."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    with open(os.path.join(ROOT, "quantized_decode_gemv_quantize_amd", "build.py"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_PREFIX = "void qmv::mmvq_rows_kernel<qmv::Q4K, 1,"
+COPY_BYTES = 256 * 2 ** 20     # the --copy-probe copy: reads and writes this many bytes
+
+
+def summarize(trace_dir: str, fetch_dir: str, write_dir: str) -> None:
+    """Write the kernel-trace and HBM-traffic summaries of the default
+    workload under profiles/ (text with one JSON block of the figures)."""
+    import csv
+    import glob
+    import statistics
+
+    def rows(d, pat):
+        f = glob.glob(os.path.join(d, "**", pat), recursive=True)
+        return list(csv.DictReader(open(f[0])))
+
+    stats = rows(trace_dir, "*kernel_stats.csv")
+    trace = rows(trace_dir, "*kernel_trace.csv")
+    gemv = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in trace
+            if r["Kernel_Name"].startswith(KERNEL_PREFIX)]
+    quant = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in trace
+             if r["Kernel_Name"].startswith("qmv::quantize_q8_1_kernel")]
+
+    def counter(d, kernel_pred):
+        vals = [float(r["Counter_Value"]) for r in rows(d, "*counter_collection.csv")
+                if kernel_pred(r["Kernel_Name"])]
+        return statistics.median(vals), len(vals)
+
+    # calibration: the 256 MiB device copy (reads and writes COPY_BYTES)
+    def is_big_copy(r):
+        return r["Kernel_Name"].startswith("__amd_rocclr_copyBuffer")
+    fr = [float(r["Counter_Value"]) for r in rows(fetch_dir, "*counter_collection.csv") if is_big_copy(r)]
+    wr = [float(r["Counter_Value"]) for r in rows(write_dir, "*counter_collection.csv") if is_big_copy(r)]
+    fetch_copy, write_copy = max(fr), max(wr)            # the 256 MiB copies (weight clones are smaller)
+    fetch_scale = COPY_BYTES / 1024 / fetch_copy
+    write_scale = COPY_BYTES / 1024 / write_copy
+    fk, nf = counter(fetch_dir, lambda k: k.startswith(KERNEL_PREFIX))
+    wk, nw = counter(write_dir, lambda k: k.startswith(KERNEL_PREFIX))
+    traffic = fk * 1024 * fetch_scale + wk * 1024 * write_scale
+    from quantized_decode_gemv_quantize_amd import synth
+    wl = synth.BY_NAME["q4_k_4096x14336"]
+    alg = algorithmic_bytes(wl, 1)
+    figures = {
+        "kernel": KERNEL_PREFIX + " ...>", "workload": wl.name, "n": 1,
+        "source_sha256_16": kernel_source_hash(),
+        "gemv_launches": len(gemv), "gemv_avg_us": round(statistics.mean(gemv) / 1e3, 3),
+        "gemv_median_us": round(statistics.median(gemv) / 1e3, 3),
+        "quantize_avg_us": round(statistics.mean(quant) / 1e3, 3) if quant else None,
+        "fetch_kib_per_launch": fk, "write_kib_per_launch": wk,
+        "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4),
+        "traffic_bytes_per_launch": int(traffic), "algorithmic_bytes_per_launch": alg,
+        "traffic_over_algorithmic": round(traffic / alg, 4),
+    }
+    os.makedirs(PROFILES, exist_ok=True)
+    cmd_trace = ("cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <out>/trace -o bench "
+                 "-- python3 <repo>/bench.py --cpu-seconds 0")
+    cmd_fetch = ("cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/pmc_fetch -o bench "
+                 "-- python3 <repo>/bench.py --cpu-seconds 0 --steps 50 --warmup 10 --copy-probe")
+    cmd_write = cmd_fetch.replace("FETCH_SIZE", "WRITE_SIZE").replace("pmc_fetch", "pmc_write")
+    with open(os.path.join(PROFILES, "mmvq_q4_k_4096x14336_n1_kernel_trace.md"), "w") as f:
+        f.write("# Kernel trace: Q4_K mat-vec 4096x14336, n=1 (default bench workload)\n\n")
+        f.write(f"Command (MI355X, one GPU):\n\n    {cmd_trace}\n\n")
+        f.write("rocprofv3 --stats summary (durations in ns):\n\n")
+        f.write("| kernel | calls | avg ns | min ns | max ns |\n|---|---|---|---|---|\n")
+        for r in stats:
+            f.write(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                    f"{r['MinNs']} | {r['MaxNs']} |\n")
+        f.write(f"\nmat-vec launches: {len(gemv)}, average {figures['gemv_avg_us']} us, "
+                f"median {figures['gemv_median_us']} us.\n")
+    with open(os.path.join(PROFILES, "mmvq_q4_k_4096x14336_n1_hbm_traffic.md"), "w") as f:
+        f.write("# HBM traffic: Q4_K mat-vec 4096x14336, n=1\n\n")
+        f.write(f"Commands:\n\n    {cmd_fetch}\n    {cmd_write}\n\n")
+        f.write("Calibration: the same process copies a 256 MiB device buffer (reads and writes 256 MiB);\n"
+                f"FETCH_SIZE reads {fetch_copy:.0f} KiB for it (scale {fetch_scale:.4f}), WRITE_SIZE "
+                f"{write_copy:.0f} KiB (scale {write_scale:.4f}).\n\n")
+        f.write(f"Per mat-vec launch (median of {nf} / {nw} dispatches): FETCH_SIZE {fk:.1f} KiB, "
+                f"WRITE_SIZE {wk:.1f} KiB -> {traffic / 1e6:.3f} MB of HBM traffic against "
+                f"{alg / 1e6:.3f} MB algorithmic ({figures['traffic_over_algorithmic']}x).\n\n")
+        f.write("```json\n" + json.dumps(figures, indent=1) + "\n```\n")
+    print(json.dumps(figures))
+
+
+def measured_traffic():
+    """Traffic per launch from the committed counter summary, or None when
+    the kernel sources changed since the counters were taken."""
+    path = os.path.join(PROFILES, "mmvq_q4_k_4096x14336_n1_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    try:
+        fig = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    except (IndexError, ValueError):
+        return None
+    if fig.get("source_sha256_16") != kernel_source_hash():
+        return None
+    return fig["traffic_bytes_per_launch"]
 
 
 def algorithmic_bytes(wl, n: int) -> int:
@@ -184,6 +298,9 @@ def cpu_baseline(wl, data, n: int, budget_s: float):
 
 def main():
     args = parse()
+    if args.summarize:
+        summarize(*args.summarize)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               f"(the mat-vec shards by rows across GPUs, see DESIGN.md)", file=sys.stderr)
@@ -246,7 +363,7 @@ def main():
             "step_wall_s": round(res["step_wall_s"], 4),
         },
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": "mmvq_rows_kernel (Q4_K, n=1)",
                      "bytes_per_launch": gemv_bytes,
                      "avg_launch_us": round(res["gemv_us"], 3)},

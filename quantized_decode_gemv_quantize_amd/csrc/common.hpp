@@ -64,7 +64,7 @@ inline bool ok(const uint8_t* p, size_t n, uintptr_t align) {
 }
 }  // namespace hostmodel
 
-inline u32x4 ld_nt_x4(const uint8_t* p) {
+inline u32x4 ld_a16_x4(const uint8_t* p) {
   u32x4 v = {0, 0, 0, 0};
   if (hostmodel::ok(p, 16, 16)) memcpy(&v, p, 16);
   return v;
@@ -106,11 +106,12 @@ inline int sbfe(uint32_t v, uint32_t off, uint32_t width) {
 __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
 
 // ---------------------------------------------------------------------------
-// Loads. Weights are streamed once, so they are read with the non-temporal
-// hint; activations and headers use ordinary loads.
+// Loads. Ordinary cached loads throughout: the streaming (non-temporal) hint
+// measured slower for the weight stream, whose header and code bytes share
+// cache lines.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ u32x4 ld_nt_x4(const uint8_t* p) {   // p 16-byte aligned
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+__device__ __forceinline__ u32x4 ld_a16_x4(const uint8_t* p) {  // p 16-byte aligned
+  return *reinterpret_cast<const u32x4*>(__builtin_assume_aligned(p, 16));
 }
 __device__ __forceinline__ u32x4 ld_x4(const uint8_t* p) {      // p 4-byte aligned
   const uint32_t* q = reinterpret_cast<const uint32_t*>(__builtin_assume_aligned(p, 4));

@@ -129,7 +129,7 @@ struct Q4K {
   // base); extra: per-lane byte offset added to it
   __device__ static void load_wt(Wt& w, const uint8_t* row, uint32_t extra, const Lane& l) {
     w.hdr = ld_x4(row + (extra + l.hoff));
-    w.qs = ld_nt_x4(row + (extra + l.qoff));
+    w.qs = ld_a16_x4(row + (extra + l.qoff));
   }
 
   struct Dec {

@@ -12,7 +12,7 @@ namespace qmv {
 // Waves per compute unit the row split aims for: enough to keep every
 // CU's share of the matrix in flight in one round of resident waves.
 #ifndef QMV_TARGET_WAVES_PER_CU
-#define QMV_TARGET_WAVES_PER_CU 8
+#define QMV_TARGET_WAVES_PER_CU 6
 #endif
 
 struct Shape {
