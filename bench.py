@@ -3,7 +3,10 @@
 Default workload: Q4_K weights, M = 4096 rows x K = 14336, n = 1 activation
 column (the FFN down-projection shape of a 7B/8B-class model), fp32 output.
 One step is one pass of the hot path over one activation: quantize the fp32
-activation to q8_1, then the quantized mat-vec against a weight matrix.
+activation to q8_1, then the quantized mat-vec against a weight matrix. The
+step runs as one fused launch (mmvq_f32: the kernel quantizes its slice of
+the activation in its prologue) unless ``--step two`` asks for the two
+launches (mmvq_quantize_q8_1, then mmvq); both forms are timed and reported.
 
 Measurement:
   * inputs (weights, activation) are resident in HBM before timing starts;
@@ -50,6 +53,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=400)
     p.add_argument("--workload", default="q4_k_4096x14336")
     p.add_argument("--n", type=int, default=1, help="activation columns")
+    p.add_argument("--step", choices=("fused", "two"), default="fused",
+                   help="one fused launch per step, or quantize + mat-vec launches")
     p.add_argument("--all", action="store_true", help="also time every workload (stderr)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="wall-clock budget of the oracle baseline (0 disables it)")
@@ -73,13 +78,21 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-KERNEL_PREFIX = "void qmv::mmvq_rows_kernel<qmv::Q4K, 1,"
+def kernel_kind(name: str) -> str | None:
+    """'fused' / 'gemv' for the n=1 Q4_K plain mat-vec kernels (fp32 or q8_1
+    activations), else None."""
+    import re
+    m = re.match(r"void qmv::mmvq_rows_kernel<qmv::Q4K, 1, \d+, \d+, 1, (true|false)>", name)
+    if not m:
+        return None
+    return "fused" if m.group(1) == "true" else "gemv"
 COPY_BYTES = 256 * 2 ** 20     # the --copy-probe copy: reads and writes this many bytes
 
 
 def summarize(trace_dir: str, fetch_dir: str, write_dir: str) -> None:
     """Write the kernel-trace and HBM-traffic summaries of the default
-    workload under profiles/ (text with one JSON block of the figures)."""
+    workload under profiles/ (text with one JSON block of the figures), for
+    the fused kernel and the two-launch form's mat-vec kernel."""
     import csv
     import glob
     import statistics
@@ -90,47 +103,50 @@ def summarize(trace_dir: str, fetch_dir: str, write_dir: str) -> None:
 
     stats = rows(trace_dir, "*kernel_stats.csv")
     trace = rows(trace_dir, "*kernel_trace.csv")
-    gemv = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in trace
-            if r["Kernel_Name"].startswith(KERNEL_PREFIX)]
-    quant = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in trace
-             if r["Kernel_Name"].startswith("qmv::quantize_q8_1_kernel")]
-
-    def counter(d, kernel_pred):
-        vals = [float(r["Counter_Value"]) for r in rows(d, "*counter_collection.csv")
-                if kernel_pred(r["Kernel_Name"])]
-        return statistics.median(vals), len(vals)
+    dur = {"fused": [], "gemv": [], "quantize": []}
+    for r in trace:
+        k = kernel_kind(r["Kernel_Name"])
+        if k is None and r["Kernel_Name"].startswith("qmv::quantize_q8_1_kernel"):
+            k = "quantize"
+        if k:
+            dur[k].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
 
     # calibration: the 256 MiB device copy (reads and writes COPY_BYTES)
-    def is_big_copy(r):
-        return r["Kernel_Name"].startswith("__amd_rocclr_copyBuffer")
-    fr = [float(r["Counter_Value"]) for r in rows(fetch_dir, "*counter_collection.csv") if is_big_copy(r)]
-    wr = [float(r["Counter_Value"]) for r in rows(write_dir, "*counter_collection.csv") if is_big_copy(r)]
-    fetch_copy, write_copy = max(fr), max(wr)            # the 256 MiB copies (weight clones are smaller)
+    def big_copy(d):
+        return max(float(r["Counter_Value"]) for r in rows(d, "*counter_collection.csv")
+                   if r["Kernel_Name"].startswith("__amd_rocclr_copyBuffer"))
+    fetch_copy, write_copy = big_copy(fetch_dir), big_copy(write_dir)   # weight clones are smaller
     fetch_scale = COPY_BYTES / 1024 / fetch_copy
     write_scale = COPY_BYTES / 1024 / write_copy
-    fk, nf = counter(fetch_dir, lambda k: k.startswith(KERNEL_PREFIX))
-    wk, nw = counter(write_dir, lambda k: k.startswith(KERNEL_PREFIX))
-    traffic = fk * 1024 * fetch_scale + wk * 1024 * write_scale
+
+    def counter(d, kind):
+        vals = [float(r["Counter_Value"]) for r in rows(d, "*counter_collection.csv")
+                if kernel_kind(r["Kernel_Name"]) == kind]
+        return statistics.median(vals), len(vals)
+
     from quantized_decode_gemv_quantize_amd import synth
     wl = synth.BY_NAME["q4_k_4096x14336"]
-    alg = algorithmic_bytes(wl, 1)
-    figures = {
-        "kernel": KERNEL_PREFIX + " ...>", "workload": wl.name, "n": 1,
-        "source_sha256_16": kernel_source_hash(),
-        "gemv_launches": len(gemv), "gemv_avg_us": round(statistics.mean(gemv) / 1e3, 3),
-        "gemv_median_us": round(statistics.median(gemv) / 1e3, 3),
-        "quantize_avg_us": round(statistics.mean(quant) / 1e3, 3) if quant else None,
-        "fetch_kib_per_launch": fk, "write_kib_per_launch": wk,
-        "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4),
-        "traffic_bytes_per_launch": int(traffic), "algorithmic_bytes_per_launch": alg,
-        "traffic_over_algorithmic": round(traffic / alg, 4),
-    }
+    figures = {"workload": wl.name, "n": 1, "source_sha256_16": kernel_source_hash(),
+               "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4),
+               "quantize_avg_us": round(statistics.mean(dur["quantize"]) / 1e3, 3) if dur["quantize"] else None}
+    for kind, alg in (("fused", fused_bytes(wl, 1)), ("gemv", algorithmic_bytes(wl, 1))):
+        fk, nf = counter(fetch_dir, kind)
+        wk, nw = counter(write_dir, kind)
+        traffic = fk * 1024 * fetch_scale + wk * 1024 * write_scale
+        figures[kind] = {
+            "launches": len(dur[kind]), "avg_us": round(statistics.mean(dur[kind]) / 1e3, 3),
+            "median_us": round(statistics.median(dur[kind]) / 1e3, 3),
+            "fetch_kib_per_launch": fk, "write_kib_per_launch": wk, "counter_dispatches": [nf, nw],
+            "traffic_bytes_per_launch": int(traffic), "algorithmic_bytes_per_launch": alg,
+            "traffic_over_algorithmic": round(traffic / alg, 4)}
     os.makedirs(PROFILES, exist_ok=True)
     cmd_trace = ("cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <out>/trace -o bench "
                  "-- python3 <repo>/bench.py --cpu-seconds 0")
     cmd_fetch = ("cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/pmc_fetch -o bench "
                  "-- python3 <repo>/bench.py --cpu-seconds 0 --steps 50 --warmup 10 --copy-probe")
     cmd_write = cmd_fetch.replace("FETCH_SIZE", "WRITE_SIZE").replace("pmc_fetch", "pmc_write")
+    names = {"fused": "fused quantize + mat-vec (mmvq_f32, fp32 activation)",
+             "gemv": "mat-vec of the two-launch form (mmvq, q8_1 activation)"}
     with open(os.path.join(PROFILES, "mmvq_q4_k_4096x14336_n1_kernel_trace.md"), "w") as f:
         f.write("# Kernel trace: Q4_K mat-vec 4096x14336, n=1 (default bench workload)\n\n")
         f.write(f"Command (MI355X, one GPU):\n\n    {cmd_trace}\n\n")
@@ -139,24 +155,34 @@ def summarize(trace_dir: str, fetch_dir: str, write_dir: str) -> None:
         for r in stats:
             f.write(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
                     f"{r['MinNs']} | {r['MaxNs']} |\n")
-        f.write(f"\nmat-vec launches: {len(gemv)}, average {figures['gemv_avg_us']} us, "
-                f"median {figures['gemv_median_us']} us.\n")
+        f.write("\n")
+        for kind in ("fused", "gemv"):
+            g = figures[kind]
+            f.write(f"{names[kind]}: {g['launches']} launches, average {g['avg_us']} us, "
+                    f"median {g['median_us']} us.\n")
+        if figures["quantize_avg_us"] is not None:
+            f.write(f"q8_1 quantizer (two-launch form): average {figures['quantize_avg_us']} us.\n")
     with open(os.path.join(PROFILES, "mmvq_q4_k_4096x14336_n1_hbm_traffic.md"), "w") as f:
         f.write("# HBM traffic: Q4_K mat-vec 4096x14336, n=1\n\n")
         f.write(f"Commands:\n\n    {cmd_fetch}\n    {cmd_write}\n\n")
         f.write("Calibration: the same process copies a 256 MiB device buffer (reads and writes 256 MiB);\n"
                 f"FETCH_SIZE reads {fetch_copy:.0f} KiB for it (scale {fetch_scale:.4f}), WRITE_SIZE "
                 f"{write_copy:.0f} KiB (scale {write_scale:.4f}).\n\n")
-        f.write(f"Per mat-vec launch (median of {nf} / {nw} dispatches): FETCH_SIZE {fk:.1f} KiB, "
-                f"WRITE_SIZE {wk:.1f} KiB -> {traffic / 1e6:.3f} MB of HBM traffic against "
-                f"{alg / 1e6:.3f} MB algorithmic ({figures['traffic_over_algorithmic']}x).\n\n")
+        for kind in ("fused", "gemv"):
+            g = figures[kind]
+            f.write(f"{names[kind]}, per launch (median over dispatches): FETCH_SIZE "
+                    f"{g['fetch_kib_per_launch']:.1f} KiB, WRITE_SIZE {g['write_kib_per_launch']:.1f} KiB -> "
+                    f"{g['traffic_bytes_per_launch'] / 1e6:.3f} MB of HBM traffic against "
+                    f"{g['algorithmic_bytes_per_launch'] / 1e6:.3f} MB algorithmic "
+                    f"({g['traffic_over_algorithmic']}x).\n\n")
         f.write("```json\n" + json.dumps(figures, indent=1) + "\n```\n")
     print(json.dumps(figures))
 
 
-def measured_traffic():
-    """Traffic per launch from the committed counter summary, or None when
-    the kernel sources changed since the counters were taken."""
+def measured_traffic(kind: str):
+    """Traffic per launch of the 'fused' or 'gemv' kernel from the committed
+    counter summary, or None when the kernel sources changed since the
+    counters were taken."""
     path = os.path.join(PROFILES, "mmvq_q4_k_4096x14336_n1_hbm_traffic.md")
     if not os.path.exists(path):
         return None
@@ -165,9 +191,15 @@ def measured_traffic():
         fig = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
     except (IndexError, ValueError):
         return None
-    if fig.get("source_sha256_16") != kernel_source_hash():
+    if fig.get("source_sha256_16") != kernel_source_hash() or kind not in fig:
         return None
-    return fig["traffic_bytes_per_launch"]
+    return fig[kind]["traffic_bytes_per_launch"]
+
+
+def fused_bytes(wl, n: int) -> int:
+    """Bytes one fused (fp32-activation) launch must move: weights once, the
+    fp32 columns, the fp32 outputs."""
+    return wl.weight_bytes + n * wl.K * 4 + n * wl.M * 4
 
 
 def algorithmic_bytes(wl, n: int) -> int:
@@ -237,14 +269,27 @@ def time_workload(torch, B, wl, n: int, steps: int, warmup: int):
         for _ in Ws:
             B.mmvq_quantize_q8_1(x, wl.K, n, wl.K, y, s)
 
+    def fused_pass():
+        for W in Ws:
+            B.mmvq_f32(W, wl.wtype, wl.M, wl.K, x, n, wl.K, out, s)
+
     g_step = capture(torch, s, step_pass)
     g_gemv = capture(torch, s, gemv_pass)
     g_quant = capture(torch, s, quant_pass)
+    g_fused = capture(torch, s, fused_pass)
     reps = max(1, math.ceil(steps / C))
     wreps = max(1, math.ceil(warmup / C))
     res = {"copies": C, "steps": reps * C, "warmup": wreps * C}
+    # the two step forms must agree bit for bit before either is timed
+    ref = torch.empty_like(out)
+    B.mmvq_quantize_q8_1(x, wl.K, n, wl.K, y, s)
+    B.mmvq(Ws[0], wl.wtype, wl.M, wl.K, y, n, ref, s)
+    B.mmvq_f32(Ws[0], wl.wtype, wl.M, wl.K, x, n, wl.K, out, s)
+    torch.cuda.synchronize()
+    if not torch.equal(ref.view(torch.int32), out.view(torch.int32)):
+        raise RuntimeError(f"{wl.name} n={n}: fused and two-launch results differ")
     with torch.cuda.stream(s):
-        for g, key in ((g_step, "step"), (g_gemv, "gemv"), (g_quant, "quant")):
+        for g, key in ((g_step, "step"), (g_gemv, "gemv"), (g_quant, "quant"), (g_fused, "fused")):
             for _ in range(wreps):
                 g.replay()
             torch.cuda.synchronize()
@@ -327,10 +372,16 @@ def main():
         del a, b
 
     res, data, Ws, y, out = time_workload(torch, B, wl, n, args.steps, args.warmup)
-    step_ms = res["step_us"] / 1e3
-    value = wl.weight_bytes / (res["step_us"] * 1e-6) / 1e9
-    gemv_bytes = algorithmic_bytes(wl, n)
-    achieved = gemv_bytes / (res["gemv_us"] * 1e-6) / 1e9
+    fused = args.step == "fused"
+    step_us = res["fused_us"] if fused else res["step_us"]
+    step_ms = step_us / 1e3
+    value = wl.weight_bytes / (step_us * 1e-6) / 1e9
+    # roofline of the step's dominant kernel: the fused kernel reads the
+    # weights and the fp32 activation; the two-launch form's mat-vec reads
+    # the weights and the q8_1 activation
+    kern_bytes = fused_bytes(wl, n) if fused else algorithmic_bytes(wl, n)
+    kern_us = res["fused_us"] if fused else res["gemv_us"]
+    achieved = kern_bytes / (kern_us * 1e-6) / 1e9
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -353,20 +404,23 @@ def main():
                    "n": n, "weight_bytes": wl.weight_bytes, "weight_copies": res["copies"],
                    "parallelism": "single GPU"},
         "detail": {
+            "step_form": "one fused launch (mmvq_f32)" if fused else "quantize + mat-vec launches",
             "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+            "fused_us": round(res["fused_us"], 3),
             "gemv_us": round(res["gemv_us"], 3),
             "quantize_us": round(res["quant_us"], 3),
-            "step_us": round(res["step_us"], 3),
+            "two_launch_step_us": round(res["step_us"], 3),
             "gemv_weight_gbs": round(wl.weight_bytes / (res["gemv_us"] * 1e-6) / 1e9, 1),
             "gemv_per_s": round(1e6 / res["gemv_us"], 1),
             "decode_tokens_per_s_equiv": round(value / TOKENS_DENOM_GB, 1),
             "step_wall_s": round(res["step_wall_s"], 4),
         },
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "kernel": "mmvq_rows_kernel (Q4_K, n=1)",
-                     "bytes_per_launch": gemv_bytes,
-                     "avg_launch_us": round(res["gemv_us"], 3)},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("fused" if fused else "gemv"),
+                     "kernel": f"mmvq_rows_kernel (Q4_K, n=1, {'fp32' if fused else 'q8_1'} activation)",
+                     "bytes_per_launch": kern_bytes,
+                     "avg_launch_us": round(kern_us, 3)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -380,7 +434,8 @@ def main():
                 gb = algorithmic_bytes(w, nn) / (r["gemv_us"] * 1e-6) / 1e9
                 print(json.dumps({"workload": name, "n": nn, "gemv_us": round(r["gemv_us"], 3),
                                   "quantize_us": round(r["quant_us"], 3),
-                                  "step_us": round(r["step_us"], 3),
+                                  "two_launch_step_us": round(r["step_us"], 3),
+                                  "fused_us": round(r["fused_us"], 3),
                                   "gemv_gbs": round(gb, 1), "frac": round(gb / HBM_PEAK_GBS, 4)}),
                       file=sys.stderr, flush=True)
 

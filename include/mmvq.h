@@ -141,6 +141,34 @@ int mmvq_id_glu(const void *W_gate, const void *W_up,
                 const int32_t *ids, int top_k, int glu_op, float *out,
                 void *stream);
 
+/* Fused quantize + product, fp32 activations [MMVQ §激活的量化, §融合].
+ * The four calls below equal mmvq_quantize_q8_1 followed by mmvq, mmvq_glu,
+ * mmvq_id and mmvq_id_glu respectively, bit for bit: each kernel quantizes
+ * the slice of x that its lanes multiply, with the quantizer's arithmetic,
+ * in registers, so the q8_1 columns are never written to memory and one
+ * launch replaces two. Column j of x starts at x + j*ldx (ldx >= K floats;
+ * the first K values are used; x 4-byte aligned). Each workgroup re-reads
+ * x (K*n*4 bytes) from cache; there is no y_q. Same requirements and error
+ * codes as the q8_1 forms, plus MMVQ_ERR_SHAPE for ldx < K. */
+int mmvq_f32(const void *W, int type, int64_t M, int64_t K, const float *x,
+             int64_t n, int64_t ldx, float *out, void *stream);
+
+int mmvq_glu_f32(const void *W_gate, const void *W_up, int type, int64_t M,
+                 int64_t K, const float *x, int64_t n, int64_t ldx,
+                 int glu_op, float *out, void *stream);
+
+/* Column t of x (x + t*ldx) is token t. */
+int mmvq_id_f32(const void *W, int64_t expert_stride_bytes, int n_experts,
+                int type, int64_t M, int64_t K, const float *x,
+                int64_t n_tokens, int64_t ldx, const int32_t *ids, int top_k,
+                float *out, void *stream);
+
+int mmvq_id_glu_f32(const void *W_gate, const void *W_up,
+                    int64_t expert_stride_bytes, int n_experts, int type,
+                    int64_t M, int64_t K, const float *x, int64_t n_tokens,
+                    int64_t ldx, const int32_t *ids, int top_k, int glu_op,
+                    float *out, void *stream);
+
 /* TEST SUPPORT: the integer block dots that mmvq forms, through the same
  * device decode routines, written instead of being scaled and summed.
  * dots[((j*M + r)*(K/qk) + b)*D + i] with D = 16 for Q4_K (sum(q*qy) of

@@ -37,6 +37,11 @@ _SIGS = {
     "mmvq_glu": (_int, [_p, _p, _int, _i64, _i64, _p, _i64, _int, _p, _p]),
     "mmvq_id": (_int, [_p, _i64, _int, _int, _i64, _i64, _p, _i64, _p, _int, _p, _p]),
     "mmvq_id_glu": (_int, [_p, _p, _i64, _int, _int, _i64, _i64, _p, _i64, _p, _int, _int, _p, _p]),
+    "mmvq_f32": (_int, [_p, _int, _i64, _i64, _p, _i64, _i64, _p, _p]),
+    "mmvq_glu_f32": (_int, [_p, _p, _int, _i64, _i64, _p, _i64, _i64, _int, _p, _p]),
+    "mmvq_id_f32": (_int, [_p, _i64, _int, _int, _i64, _i64, _p, _i64, _i64, _p, _int, _p, _p]),
+    "mmvq_id_glu_f32": (_int, [_p, _p, _i64, _int, _int, _i64, _i64, _p, _i64, _i64, _p, _int, _int,
+                               _p, _p]),
     "mmvq_block_dots": (_int, [_p, _int, _i64, _i64, _p, _i64, _p, _p]),
     "mmvq_strerror": (ctypes.c_char_p, [_int]),
 }
@@ -134,6 +139,33 @@ def mmvq_id_glu(W_gate, W_up, expert_stride_bytes: int, n_experts: int, wtype: i
                                             n_experts, wtype, M, K, _addr(y_q), n_tokens,
                                             _addr(ids), top_k, glu_op, _addr(out),
                                             _stream(stream)))
+
+
+def mmvq_f32(W, wtype: int, M: int, K: int, x, n: int, ldx: int, out, stream=None) -> None:
+    _check("mmvq_f32", lib().mmvq_f32(_addr(W), wtype, M, K, _addr(x), n, ldx, _addr(out),
+                                      _stream(stream)))
+
+
+def mmvq_glu_f32(W_gate, W_up, wtype: int, M: int, K: int, x, n: int, ldx: int, glu_op: int,
+                 out, stream=None) -> None:
+    _check("mmvq_glu_f32", lib().mmvq_glu_f32(_addr(W_gate), _addr(W_up), wtype, M, K, _addr(x),
+                                              n, ldx, glu_op, _addr(out), _stream(stream)))
+
+
+def mmvq_id_f32(W, expert_stride_bytes: int, n_experts: int, wtype: int, M: int, K: int, x,
+                n_tokens: int, ldx: int, ids, top_k: int, out, stream=None) -> None:
+    _check("mmvq_id_f32", lib().mmvq_id_f32(_addr(W), expert_stride_bytes, n_experts, wtype, M, K,
+                                            _addr(x), n_tokens, ldx, _addr(ids), top_k,
+                                            _addr(out), _stream(stream)))
+
+
+def mmvq_id_glu_f32(W_gate, W_up, expert_stride_bytes: int, n_experts: int, wtype: int, M: int,
+                    K: int, x, n_tokens: int, ldx: int, ids, top_k: int, glu_op: int, out,
+                    stream=None) -> None:
+    _check("mmvq_id_glu_f32", lib().mmvq_id_glu_f32(_addr(W_gate), _addr(W_up),
+                                                    expert_stride_bytes, n_experts, wtype, M, K,
+                                                    _addr(x), n_tokens, ldx, _addr(ids), top_k,
+                                                    glu_op, _addr(out), _stream(stream)))
 
 
 def mmvq_block_dots(W, wtype: int, M: int, K: int, y_q, n: int, dots, stream=None) -> None:

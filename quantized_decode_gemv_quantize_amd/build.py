@@ -18,15 +18,19 @@ LIB = os.path.join(HERE, "libmmvq.so")
 OBJ = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "quantize.hip", "kernels_q4_0.hip", "kernels_q4_k.hip", "kernels_q6_k.hip"]
+SOURCES = ["api.hip", "quantize.hip", "kernels_q4_0.hip", "kernels_q4_k.hip", "kernels_q6_k.hip",
+           "kernels_q4_0_f32.hip", "kernels_q4_k_f32.hip", "kernels_q6_k_f32.hip"]
 
 # Packed fp32 VALU instructions stay disabled (hipcc forms them from plain
 # float code otherwise); fp32 division is correctly rounded and fp32
 # denormals are kept, which the q8_1 step relies on to match its definition.
+# No implicit fp contraction: every fused multiply-add is an explicit fmaf in
+# the source, so each kernel instantiation (q8_1 or fp32 activations, any
+# row count) rounds the same operations the same way.
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-flush-denormals-to-zero",
+    "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-flush-denormals-to-zero", "-ffp-contract=off",
     "-Wall", "-Wno-unused-function",
 ]
 

@@ -98,6 +98,16 @@ inline int dot4(uint32_t a, uint32_t b, int c) {
   return c;
 }
 inline int mul24(int a, int b) { return a * b; }
+inline float __uint_as_float(uint32_t u) {
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+inline uint32_t __float_as_uint(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return u;
+}
 inline int sbfe(uint32_t v, uint32_t off, uint32_t width) {
   return static_cast<int>(v << (32 - off - width)) >> (32 - width);
 }

@@ -18,7 +18,18 @@
 //
 // Each format provides:
 //   Act           activation registers of one column for the lane's unit
-//   load_act      fill Act from a q8_1 column
+//   issue_act     issue the loads of the lane's slice of a q8_1 column into
+//                 Act (codes in place, fp16 scale bits held as raw words)
+//   finish_act    turn the raw scale bits into the fp32 values col_dot uses
+//                 (split from issue_act so the weight loads can be issued
+//                 before anything waits for the activation)
+//   load_act      issue_act then finish_act
+//   load_x        load the lane's fp32 activation values (XRaw, kXWords
+//                 words) of one column
+//   quant_x       quantize them to the Act of load_act, with the q8_1
+//                 quantizer's own arithmetic (same codes and scales as
+//                 load_act after mmvq_quantize_q8_1); lanes u and u ^ 1
+//                 exchange block maxima, so every lane of the wave runs it
 //   Wt            raw weight words of the lane's unit in one row
 //   load_wt       issue the loads of Wt
 //   Dec / decode  per-row decode shared by all columns (codes, scales)
@@ -28,13 +39,11 @@
 #pragma once
 
 #include "common.hpp"
+#include "q8.hpp"
 
 namespace qmv {
 
 constexpr int kQ8Bytes = 36;     // fp16 d, fp16 s, 32 x int8   [MMVQ §激活的量化]
-
-// q8_1 block fields
-__device__ __forceinline__ float q8_d(const uint8_t* blk) { return h2f(ld_u16(blk)); }
 
 // Sum of the 4 signed bytes of a word, via a dot with 0x01010101 (the pages'
 // trick for the activation sum of a sub-block [MMVQ §一次 vec_dot 的解剖]).
@@ -78,13 +87,59 @@ struct Q4K {
     return s;
   }
 
-  __device__ static void load_act(Act& a, const uint8_t* ycol, int u) {
+  __device__ static void issue_act(Act& a, const uint8_t* ycol, int u) {
     const uint8_t *b0, *b1;
     act_codes(ycol, u, a.y0, a.y1, b0, b1);
-    a.d0 = q8_d(b0);
-    a.d1 = q8_d(b1);
+    a.d0 = __uint_as_float(ld_u16(b0));
+    a.d1 = __uint_as_float(ld_u16(b1));
+  }
+
+  __device__ static void finish_act(Act& a) {
+    a.d0 = h2f(__float_as_uint(a.d0));
+    a.d1 = h2f(__float_as_uint(a.d1));
     a.s0 = a.d0 * static_cast<float>(sum4(a.y0));
     a.s1 = a.d1 * static_cast<float>(sum4(a.y1));
+  }
+
+  __device__ static void load_act(Act& a, const uint8_t* ycol, int u) {
+    issue_act(a, ycol, u);
+    finish_act(a);
+  }
+
+  // fp32 activations: the lane holds half of each of its two q8_1 blocks
+  // (16 values each); the lane next to it (unit u ^ 1) holds the other
+  // halves, so one exchange gives each block's amax.
+  struct XRaw {
+    u32x4 r0[4], r1[4];
+  };
+  static constexpr int kXWords = 32;
+
+  __device__ static void load_x(XRaw& x, const float* xcol, int u) {
+    const int sb = u >> 3, p = u & 7, c = p >> 1, half = p & 1;
+    const float* x0 = xcol + static_cast<int64_t>(8 * sb + 2 * c) * 32 + 16 * half;
+    const float* x1 = x0 + 32;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x.r0[k] = ld_x4(reinterpret_cast<const uint8_t*>(x0 + 4 * k));
+      x.r1[k] = ld_x4(reinterpret_cast<const uint8_t*>(x1 + 4 * k));
+    }
+  }
+
+  __device__ static void quant_x(Act& a, const XRaw& x) {
+    float m0 = absmax4(x.r0[0]), m1 = absmax4(x.r1[0]);
+#pragma unroll
+    for (int k = 1; k < 4; ++k) {
+      m0 = fmaxf(m0, absmax4(x.r0[k]));
+      m1 = fmaxf(m1, absmax4(x.r1[k]));
+    }
+    const float d0 = q8_scale(max_with_pair(m0)), d1 = q8_scale(max_with_pair(m1));
+    int s0 = 0, s1 = 0;
+    q8_quant_block(x.r0, d0, a.y0, s0);
+    q8_quant_block(x.r1, d1, a.y1, s1);
+    a.d0 = q8_d_rounded(d0);
+    a.d1 = q8_d_rounded(d1);
+    a.s0 = a.d0 * static_cast<float>(s0);
+    a.s1 = a.d1 * static_cast<float>(s1);
   }
 
   __device__ static void zero_act(Act& a) {
@@ -169,10 +224,9 @@ struct Q4K {
     int dot0, dot1;
     nibble_dots(o, a, dot0, dot1);
     const int sc0 = static_cast<int>(o.scp & 0xFFu), sc1 = static_cast<int>((o.scp >> 8) & 0xFFu);
-    const float sd = static_cast<float>(mul24(dot0, sc0)) * a.d0 +
-                     static_cast<float>(mul24(dot1, sc1)) * a.d1;
-    const float sm = o.m0 * a.s0 + o.m1 * a.s1;
-    return o.d * sd - o.dmin * sm;
+    const float sd = fmaf(static_cast<float>(mul24(dot0, sc0)), a.d0, static_cast<float>(mul24(dot1, sc1)) * a.d1);
+    const float sm = fmaf(o.m0, a.s0, o.m1 * a.s1);
+    return fmaf(o.d, sd, -(o.dmin * sm));
   }
 
   // dots of one super-block: [dot1 of t = 0..7, sum(qy) of t = 0..7]
@@ -209,14 +263,46 @@ struct Q40 {
     float s8;      // 8 * s
   };
 
-  __device__ static void load_act(Act& a, const uint8_t* ycol, int u) {
+  __device__ static void issue_act(Act& a, const uint8_t* ycol, int u) {
     const uint8_t* b = ycol + static_cast<int64_t>(u) * kQ8Bytes;
     const u32x4 lo = ld_x4(b + 4), hi = ld_x4(b + 20);
     a.y[0] = lo.x; a.y[1] = lo.y; a.y[2] = lo.z; a.y[3] = lo.w;
     a.y[4] = hi.x; a.y[5] = hi.y; a.y[6] = hi.z; a.y[7] = hi.w;
-    const uint32_t ds = ld_u32(b);
+    a.d8 = __uint_as_float(ld_u32(b));     // fp16 d and s, raw
+  }
+
+  __device__ static void finish_act(Act& a) {
+    const uint32_t ds = __float_as_uint(a.d8);
     a.d8 = h2f(ds);
     a.s8 = 8.0f * h2f(ds >> 16);
+  }
+
+  __device__ static void load_act(Act& a, const uint8_t* ycol, int u) {
+    issue_act(a, ycol, u);
+    finish_act(a);
+  }
+
+  // fp32 activations: the lane holds its whole q8_1 block.
+  struct XRaw {
+    u32x4 r[8];
+  };
+  static constexpr int kXWords = 32;
+
+  __device__ static void load_x(XRaw& x, const float* xcol, int u) {
+    const float* p = xcol + static_cast<int64_t>(u) * 32;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x.r[k] = ld_x4(reinterpret_cast<const uint8_t*>(p + 4 * k));
+  }
+
+  __device__ static void quant_x(Act& a, const XRaw& x) {
+    float m = absmax4(x.r[0]);
+#pragma unroll
+    for (int k = 1; k < 8; ++k) m = fmaxf(m, absmax4(x.r[k]));
+    const float d = q8_scale(m);
+    int sq = 0;
+    q8_quant_block(x.r, d, a.y, sq);
+    a.d8 = q8_d_rounded(d);
+    a.s8 = 8.0f * h2f(f2h_bits(q8_s(d, sq)));
   }
 
   __device__ static void zero_act(Act& a) {
@@ -272,7 +358,7 @@ struct Q40 {
   }
 
   __device__ static float col_dot(const Dec& o, const Act& a) {
-    return o.d * (a.d8 * static_cast<float>(isum(o, a)) - a.s8);
+    return o.d * fmaf(a.d8, static_cast<float>(isum(o, a)), -a.s8);
   }
 
   __device__ static void int_dots(const Dec& o, const uint8_t* ycol, int u, int* dots) {
@@ -312,15 +398,59 @@ struct Q6K {
     return ycol + static_cast<int64_t>(8 * sb + 4 * h + g) * kQ8Bytes;
   }
 
-  __device__ static void load_act(Act& a, const uint8_t* ycol, int u) {
+  __device__ static void issue_act(Act& a, const uint8_t* ycol, int u) {
     const int lq = u & 1;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const uint8_t* b = act_block(ycol, u, g);
       const u32x4 q = ld_x4(b + 4 + 16 * lq);
       a.y[g][0] = q.x; a.y[g][1] = q.y; a.y[g][2] = q.z; a.y[g][3] = q.w;
-      a.d8[g] = q8_d(b);
-      a.c32[g] = 32 * bsum4(q.w, bsum4(q.z, bsum4(q.y, bsum4(q.x, 0))));
+      a.d8[g] = __uint_as_float(ld_u16(b));
+    }
+  }
+
+  __device__ static void finish_act(Act& a) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      a.d8[g] = h2f(__float_as_uint(a.d8[g]));
+      a.c32[g] = 32 * bsum4(a.y[g][3], bsum4(a.y[g][2], bsum4(a.y[g][1], bsum4(a.y[g][0], 0))));
+    }
+  }
+
+  __device__ static void load_act(Act& a, const uint8_t* ycol, int u) {
+    issue_act(a, ycol, u);
+    finish_act(a);
+  }
+
+  // fp32 activations: for each g the lane holds half of q8_1 block
+  // 8sb+4h+g (16 values); the lane next to it (unit u ^ 1, the other lq)
+  // holds the other half.
+  struct XRaw {
+    u32x4 r[4][4];
+  };
+  static constexpr int kXWords = 64;
+
+  __device__ static void load_x(XRaw& x, const float* xcol, int u) {
+    const int sb = u >> 2, h = (u >> 1) & 1, lq = u & 1;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float* p = xcol + static_cast<int64_t>(8 * sb + 4 * h + g) * 32 + 16 * lq;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) x.r[g][k] = ld_x4(reinterpret_cast<const uint8_t*>(p + 4 * k));
+    }
+  }
+
+  __device__ static void quant_x(Act& a, const XRaw& x) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      float m = absmax4(x.r[g][0]);
+#pragma unroll
+      for (int k = 1; k < 4; ++k) m = fmaxf(m, absmax4(x.r[g][k]));
+      const float d = q8_scale(max_with_pair(m));
+      int sq = 0;
+      q8_quant_block(x.r[g], d, a.y[g], sq);
+      a.d8[g] = q8_d_rounded(d);
+      a.c32[g] = 32 * sq;
     }
   }
 
@@ -424,7 +554,7 @@ struct Q6K {
   __device__ static float col_dot(const Dec& o, const Act& a) {
     float acc = 0.0f;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) acc += static_cast<float>(mul24(isum(o, a, g), o.sc[g])) * a.d8[g];
+    for (int g = 0; g < 4; ++g) acc = fmaf(static_cast<float>(mul24(isum(o, a, g), o.sc[g])), a.d8[g], acc);
     return o.d * acc;
   }
 

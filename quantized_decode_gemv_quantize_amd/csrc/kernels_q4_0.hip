@@ -4,7 +4,7 @@
 namespace qmv {
 
 const Dispatch& dispatch_q4_0() {
-  static const Dispatch d = make_dispatch<Q40>();
+  static const Dispatch d = make_dispatch<Q40, false>();
   return d;
 }
 

@@ -4,7 +4,7 @@
 namespace qmv {
 
 const Dispatch& dispatch_q6_k() {
-  static const Dispatch d = make_dispatch<Q6K>();
+  static const Dispatch d = make_dispatch<Q6K, false>();
   return d;
 }
 

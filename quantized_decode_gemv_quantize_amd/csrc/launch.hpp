@@ -2,7 +2,7 @@
 //
 // Shapes are derived from the problem, not from per-architecture tables:
 //   * team lanes TL = units per row rounded up to whole waves (<= 512);
-//   * rows per team: enough teams for about 16 resident waves per compute
+//   * rows per team: enough teams for about QMV_TARGET_WAVES_PER_CU resident waves per compute
 //     unit, capped by the register budget R of the instantiation;
 //   * teams per workgroup: enough for at least 256 threads when TL < 256.
 #pragma once
@@ -53,59 +53,59 @@ inline int check_launch() {
   return hipGetLastError() == hipSuccess ? MMVQ_OK : MMVQ_ERR_LAUNCH;
 }
 
-template <class F, int NC, int G, int R, int P>
+template <class F, bool XF, int NC, int G, int R, int P>
 inline int launch_rows_r(const RowArgs& a, const Shape& s, hipStream_t st) {
-  hipLaunchKernelGGL((mmvq_rows_kernel<F, NC, R, P, G>), dim3(static_cast<unsigned>(s.blocks)),
+  hipLaunchKernelGGL((mmvq_rows_kernel<F, NC, R, P, G, XF>), dim3(static_cast<unsigned>(s.blocks)),
                      dim3(s.teams_per_block * s.team_lanes), 0, st, a);
   return check_launch();
 }
 
-template <class F, int NC, int G, int R>
+template <class F, bool XF, int NC, int G, int R>
 inline int launch_rows_p(const RowArgs& a, const Shape& s, hipStream_t st) {
-  return s.slots == 2 ? launch_rows_r<F, NC, G, R, 2>(a, s, st) : launch_rows_r<F, NC, G, R, 1>(a, s, st);
+  return s.slots == 2 ? launch_rows_r<F, XF, NC, G, R, 2>(a, s, st) : launch_rows_r<F, XF, NC, G, R, 1>(a, s, st);
 }
 
-template <class F, int NC, int G>
+template <class F, bool XF, int NC, int G>
 inline int launch_rows_nc(RowArgs a, int64_t K, hipStream_t st) {
   constexpr int RMAX = rows_per_pass<F>(NC, G);
   const Shape s = make_shape<F>(a.M, K, RMAX);
   a.units = s.units;
   a.team_lanes = s.team_lanes;
   switch (s.rows) {
-    case 1: return launch_rows_p<F, NC, G, 1>(a, s, st);
-    case 2: if constexpr (RMAX >= 2) return launch_rows_p<F, NC, G, 2>(a, s, st); break;
-    case 4: if constexpr (RMAX >= 4) return launch_rows_p<F, NC, G, 4>(a, s, st); break;
-    case 8: if constexpr (RMAX >= 8) return launch_rows_p<F, NC, G, 8>(a, s, st); break;
-    case 16: if constexpr (RMAX >= 16) return launch_rows_p<F, NC, G, 16>(a, s, st); break;
+    case 1: return launch_rows_p<F, XF, NC, G, 1>(a, s, st);
+    case 2: if constexpr (RMAX >= 2) return launch_rows_p<F, XF, NC, G, 2>(a, s, st); break;
+    case 4: if constexpr (RMAX >= 4) return launch_rows_p<F, XF, NC, G, 4>(a, s, st); break;
+    case 8: if constexpr (RMAX >= 8) return launch_rows_p<F, XF, NC, G, 8>(a, s, st); break;
+    case 16: if constexpr (RMAX >= 16) return launch_rows_p<F, XF, NC, G, 16>(a, s, st); break;
     default: break;
   }
   return MMVQ_ERR_SHAPE;
 }
 
-template <class F, int G>
+template <class F, bool XF, int G>
 inline int launch_rows(const RowArgs& a, int64_t K, int64_t n, hipStream_t st) {
   switch (n) {
-    case 1: return launch_rows_nc<F, 1, G>(a, K, st);
-    case 2: return launch_rows_nc<F, 2, G>(a, K, st);
-    case 3: return launch_rows_nc<F, 3, G>(a, K, st);
-    case 4: return launch_rows_nc<F, 4, G>(a, K, st);
-    case 5: return launch_rows_nc<F, 5, G>(a, K, st);
-    case 6: return launch_rows_nc<F, 6, G>(a, K, st);
-    case 7: return launch_rows_nc<F, 7, G>(a, K, st);
-    case 8: return launch_rows_nc<F, 8, G>(a, K, st);
+    case 1: return launch_rows_nc<F, XF, 1, G>(a, K, st);
+    case 2: return launch_rows_nc<F, XF, 2, G>(a, K, st);
+    case 3: return launch_rows_nc<F, XF, 3, G>(a, K, st);
+    case 4: return launch_rows_nc<F, XF, 4, G>(a, K, st);
+    case 5: return launch_rows_nc<F, XF, 5, G>(a, K, st);
+    case 6: return launch_rows_nc<F, XF, 6, G>(a, K, st);
+    case 7: return launch_rows_nc<F, XF, 7, G>(a, K, st);
+    case 8: return launch_rows_nc<F, XF, 8, G>(a, K, st);
     default: return MMVQ_ERR_SHAPE;
   }
 }
 
-template <class F, int G, int R, int P>
+template <class F, bool XF, int G, int R, int P>
 inline int launch_id_r(const RowArgs& a, const Shape& s, int n_experts, hipStream_t st) {
-  hipLaunchKernelGGL((mmvq_id_kernel<F, R, P, G>),
+  hipLaunchKernelGGL((mmvq_id_kernel<F, R, P, G, XF>),
                      dim3(static_cast<unsigned>(s.blocks), static_cast<unsigned>(n_experts)),
                      dim3(s.teams_per_block * s.team_lanes), 0, st, a);
   return check_launch();
 }
 
-template <class F, int G>
+template <class F, bool XF, int G>
 inline int launch_id(RowArgs a, int64_t K, int n_experts, hipStream_t st) {
   constexpr int R = id_rows_per_pass<F>(G);
   Shape s = make_shape<F>(a.M, K, R);
@@ -115,11 +115,11 @@ inline int launch_id(RowArgs a, int64_t K, int n_experts, hipStream_t st) {
     s.rows = 1;
     s.teams = (a.M + s.slots - 1) / s.slots;
     s.blocks = (s.teams + s.teams_per_block - 1) / s.teams_per_block;
-    return s.slots == 2 ? launch_id_r<F, G, 1, 2>(a, s, n_experts, st)
-                        : launch_id_r<F, G, 1, 1>(a, s, n_experts, st);
+    return s.slots == 2 ? launch_id_r<F, XF, G, 1, 2>(a, s, n_experts, st)
+                        : launch_id_r<F, XF, G, 1, 1>(a, s, n_experts, st);
   }
-  return s.slots == 2 ? launch_id_r<F, G, R, 2>(a, s, n_experts, st)
-                      : launch_id_r<F, G, R, 1>(a, s, n_experts, st);
+  return s.slots == 2 ? launch_id_r<F, XF, G, R, 2>(a, s, n_experts, st)
+                      : launch_id_r<F, XF, G, R, 1>(a, s, n_experts, st);
 }
 
 template <class F>
@@ -135,7 +135,8 @@ inline int launch_block_dots(const uint8_t* W, const uint8_t* y, int32_t* dots, 
   return check_launch();
 }
 
-// Per-format entry points (one translation unit per format).
+// Per-format entry points: one translation unit per format and activation
+// type (q8_1 columns, or fp32 columns quantized in the kernel prologue).
 struct Dispatch {
   int (*rows)(const RowArgs&, int64_t K, int64_t n, hipStream_t);
   int (*rows_glu)(const RowArgs&, int64_t K, int64_t n, hipStream_t);
@@ -145,13 +146,15 @@ struct Dispatch {
   int qk, block_bytes, units_per_block;
 };
 
-template <class F>
+template <class F, bool XF>
 Dispatch make_dispatch() {
   Dispatch d;
-  d.rows = [](const RowArgs& a, int64_t K, int64_t n, hipStream_t s) { return launch_rows<F, 1>(a, K, n, s); };
-  d.rows_glu = [](const RowArgs& a, int64_t K, int64_t n, hipStream_t s) { return launch_rows<F, 2>(a, K, n, s); };
-  d.id = [](const RowArgs& a, int64_t K, int e, hipStream_t s) { return launch_id<F, 1>(a, K, e, s); };
-  d.id_glu = [](const RowArgs& a, int64_t K, int e, hipStream_t s) { return launch_id<F, 2>(a, K, e, s); };
+  d.rows = [](const RowArgs& a, int64_t K, int64_t n, hipStream_t s) { return launch_rows<F, XF, 1>(a, K, n, s); };
+  d.rows_glu = [](const RowArgs& a, int64_t K, int64_t n, hipStream_t s) {
+    return launch_rows<F, XF, 2>(a, K, n, s);
+  };
+  d.id = [](const RowArgs& a, int64_t K, int e, hipStream_t s) { return launch_id<F, XF, 1>(a, K, e, s); };
+  d.id_glu = [](const RowArgs& a, int64_t K, int e, hipStream_t s) { return launch_id<F, XF, 2>(a, K, e, s); };
   d.block_dots = launch_block_dots<F>;
   d.qk = F::kQK;
   d.block_bytes = F::kBlockBytes;
@@ -162,6 +165,9 @@ Dispatch make_dispatch() {
 const Dispatch& dispatch_q4_0();
 const Dispatch& dispatch_q4_k();
 const Dispatch& dispatch_q6_k();
+const Dispatch& dispatch_q4_0_f32();
+const Dispatch& dispatch_q4_k_f32();
+const Dispatch& dispatch_q6_k_f32();
 
 int launch_quantize_q8_1(const float* x, uint8_t* y, int64_t K, int64_t n, int64_t ldx, hipStream_t st);
 

@@ -24,6 +24,15 @@
 //   * Expert-indexed mode: blockIdx.y is the expert; the block gathers the
 //     tokens routed to it (at most 8) and reads that expert's rows once for
 //     all of them [MMVQ §MoE].
+//   * XF = true takes fp32 activations and quantizes the lane's slice to
+//     q8_1 in registers (formats.hpp load_x / quant_x), with the arithmetic
+//     of the stand-alone quantizer: the same codes and scales, so the result
+//     equals quantize-then-multiply bit for bit, without the q8_1 round trip
+//     through memory or the second launch [MMVQ §激活的量化, §融合]. When
+//     the raw values of all columns fit the register budget, the fp32 loads
+//     go out first, then the weight loads, and the quantization runs while
+//     the weights are in flight; otherwise each column is quantized before
+//     the weight loads are issued.
 #pragma once
 
 #include "common.hpp"
@@ -36,12 +45,14 @@ namespace qmv {
 struct RowArgs {
   const uint8_t* W;          // up / plain weights (expert 0 in id mode)
   const uint8_t* Wg;         // gate weights (G = 2)
-  const uint8_t* y;          // q8_1 columns
+  const uint8_t* y;          // q8_1 columns (XF = false)
+  const float* x;            // fp32 columns (XF = true), column stride ldx
   float* out;
   const int32_t* ids;        // id mode: n_tokens x top_k
   int64_t M;
   int64_t row_bytes;
   int64_t ycol_bytes;
+  int64_t ldx;               // elements between fp32 columns
   int64_t expert_stride;
   int units;                 // units per row
   int team_lanes;            // TL: multiple of 64
@@ -75,7 +86,7 @@ struct RedLds {
 // pair fills 7 waves exactly. Lane values are indexed
 // (column j, row i*P + slot); a lane holds zeros for the other slots, and
 // the team reduction sums each value over the lanes of its own slot.
-template <class F, int NC, int R, int P, int G, bool ID, int VMAX>
+template <class F, int NC, int R, int P, int G, bool ID, bool XF, int VMAX>
 __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
                                           const uint8_t* Wbase, const uint8_t* Wgbase,
                                           RedLds<G, VMAX>& red) {
@@ -100,11 +111,25 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
   const int64_t step = static_cast<int64_t>(P) * a.row_bytes;
 
   // ---- activation slice of every column (zero for idle lanes) -----------
+  // Only the loads are issued here; what needs their data runs after the
+  // weight loads have been issued, so no wave waits for its activation
+  // before its weight stream is in flight. XE: fp32 values held in
+  // registers across the weight loads (else quantized up front).
+  constexpr bool XE = XF && NC * F::kXWords <= 64;
   typename F::Act act[NC];
+  typename F::XRaw xr[XE ? NC : 1];
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
-    F::load_act(act[j], a.y + cols.tok[j] * a.ycol_bytes, u);
-    if (!active) F::zero_act(act[j]);
+    if constexpr (XE) {
+      F::load_x(xr[j], a.x + cols.tok[j] * a.ldx, u);
+    } else if constexpr (XF) {
+      typename F::XRaw t;
+      F::load_x(t, a.x + cols.tok[j] * a.ldx, u);
+      F::quant_x(act[j], t);
+      if (!active) F::zero_act(act[j]);
+    } else {
+      F::issue_act(act[j], a.y + cols.tok[j] * a.ycol_bytes, u);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -129,6 +154,22 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+  // the activation loads were issued before the weight loads, so they
+  // retire first: this waits for them only
+  if constexpr (XE) {
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      F::quant_x(act[j], xr[j]);
+      if (!active) F::zero_act(act[j]);
+    }
+  } else if constexpr (!XF) {
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      F::finish_act(act[j]);
+      if (!active) F::zero_act(act[j]);
+    }
+  }
+
   // ---- per row: decode once, one partial per column ----------------------
   float part[G][V];
 #pragma unroll
@@ -216,7 +257,7 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
 }
 
 // Plain / fused kernel: columns 0..NC-1 of y.
-template <class F, int NC, int R, int P, int G>
+template <class F, int NC, int R, int P, int G, bool XF>
 __global__ void __launch_bounds__(kLaunchBound) mmvq_rows_kernel(RowArgs a) {
   Cols cols;
   cols.n = NC;
@@ -224,12 +265,12 @@ __global__ void __launch_bounds__(kLaunchBound) mmvq_rows_kernel(RowArgs a) {
   for (int j = 0; j < kMaxCols; ++j) { cols.tok[j] = j; cols.slots[j] = 0; }
   constexpr int V = pow2ceil(NC * R * P);
   __shared__ RedLds<G, V> red;
-  rows_body<F, NC, R, P, G, false, V>(a, cols, a.W, a.Wg, red);
+  rows_body<F, NC, R, P, G, false, XF, V>(a, cols, a.W, a.Wg, red);
 }
 
 // Expert-indexed kernel: blockIdx.y = expert. The token list is the same for
 // every thread of the block (ids are read with uniform addresses).
-template <class F, int R, int P, int G>
+template <class F, int R, int P, int G, bool XF>
 __global__ void __launch_bounds__(kLaunchBound) mmvq_id_kernel(RowArgs a) {
   const int e = blockIdx.y;
   // Tokens routed to expert e, compacted with compile-time indices only (a
@@ -261,14 +302,14 @@ __global__ void __launch_bounds__(kLaunchBound) mmvq_id_kernel(RowArgs a) {
   constexpr int VMAX = pow2ceil(kMaxCols * R * P);
   __shared__ RedLds<G, VMAX> red;
   switch (cols.n) {
-    case 1: rows_body<F, 1, R, P, G, true, VMAX>(a, cols, We, Wge, red); break;
-    case 2: rows_body<F, 2, R, P, G, true, VMAX>(a, cols, We, Wge, red); break;
-    case 3: rows_body<F, 3, R, P, G, true, VMAX>(a, cols, We, Wge, red); break;
-    case 4: rows_body<F, 4, R, P, G, true, VMAX>(a, cols, We, Wge, red); break;
-    case 5: rows_body<F, 5, R, P, G, true, VMAX>(a, cols, We, Wge, red); break;
-    case 6: rows_body<F, 6, R, P, G, true, VMAX>(a, cols, We, Wge, red); break;
-    case 7: rows_body<F, 7, R, P, G, true, VMAX>(a, cols, We, Wge, red); break;
-    default: rows_body<F, 8, R, P, G, true, VMAX>(a, cols, We, Wge, red); break;
+    case 1: rows_body<F, 1, R, P, G, true, XF, VMAX>(a, cols, We, Wge, red); break;
+    case 2: rows_body<F, 2, R, P, G, true, XF, VMAX>(a, cols, We, Wge, red); break;
+    case 3: rows_body<F, 3, R, P, G, true, XF, VMAX>(a, cols, We, Wge, red); break;
+    case 4: rows_body<F, 4, R, P, G, true, XF, VMAX>(a, cols, We, Wge, red); break;
+    case 5: rows_body<F, 5, R, P, G, true, XF, VMAX>(a, cols, We, Wge, red); break;
+    case 6: rows_body<F, 6, R, P, G, true, XF, VMAX>(a, cols, We, Wge, red); break;
+    case 7: rows_body<F, 7, R, P, G, true, XF, VMAX>(a, cols, We, Wge, red); break;
+    default: rows_body<F, 8, R, P, G, true, XF, VMAX>(a, cols, We, Wge, red); break;
   }
 }
 

@@ -5,7 +5,8 @@
 // and row of the launch the library would make, with loads replaced by
 // bounds-checked host reads. Checks, for every case:
 //   * every weight, header, scale and activation load lies inside its
-//     buffer and is aligned as the device load requires;
+//     buffer and is aligned as the device load requires, for q8_1
+//     activations and for fp32 activations quantized in the prologue;
 //   * every output row of every column is stored exactly once;
 //   * the quantizer's and the block-dot kernel's loads stay in bounds.
 // Prints one line per failing case and exits non-zero if any case fails.
@@ -47,8 +48,8 @@ static void report(const char* what, bool ok_extra, const char* name, int64_t M,
 // kernel for one expert (base = expert's matrix, tok = its token columns).
 template <class F>
 static bool model_rows(const Shape& s, int R, int P, int G, int64_t M, const uint8_t* W, const uint8_t* Wg,
-                       int64_t row_bytes, const uint8_t* y, int64_t ycol_bytes, const int* tok, int nc,
-                       std::vector<int>& stores) {
+                       int64_t row_bytes, const uint8_t* y, int64_t ycol_bytes, const float* x, int64_t ldx,
+                       const int* tok, int nc, std::vector<int>& stores) {
   typename F::Wt wt;
   typename F::Act act;
   typename F::Dec dec;
@@ -70,7 +71,14 @@ static bool model_rows(const Shape& s, int R, int P, int G, int64_t M, const uin
             gp += P * row_bytes;
           }
         }
-        for (int j = 0; j < nc; ++j) F::load_act(act, y + tok[j] * ycol_bytes, w.unit);
+        for (int j = 0; j < nc; ++j) {
+          if (x) {
+            typename F::XRaw xr;
+            F::load_x(xr, x + tok[j] * ldx, w.unit);
+            F::quant_x(act, xr);
+          }
+          else F::load_act(act, y + tok[j] * ycol_bytes, w.unit);
+        }
         if (lt == 0) {   // the store pattern of the team (one lane's view suffices)
           for (int64_t i = w.skip; i < static_cast<int64_t>(R) * P; ++i) {
             const int64_t r = w.row0 + i;
@@ -84,24 +92,30 @@ static bool model_rows(const Shape& s, int R, int P, int G, int64_t M, const uin
   return true;
 }
 
+// xpad < 0: q8_1 activations; else fp32 columns with ldx = K + xpad.
 template <class F>
-static void case_rows(const char* name, int64_t M, int64_t K, int nc, int g) {
+static void case_rows(const char* name, int64_t M, int64_t K, int nc, int g, int xpad = -1) {
   const int64_t row_bytes = K / F::kQK * F::kBlockBytes;
+  const bool xf = xpad >= 0;
+  const int64_t ldx = K + (xf ? xpad : 0);
   const int64_t ycol = K / 32 * kQ8Bytes;
+  const int64_t act_bytes = xf ? ((nc - 1) * ldx + K) * 4 : nc * ycol;
   uint8_t* W = alloc16(M * row_bytes);
   uint8_t* Wg = g == 2 ? alloc16(M * row_bytes) : nullptr;
-  uint8_t* y = alloc16(nc * ycol);
+  uint8_t* y = alloc16(act_bytes);
+  const float* x = xf ? reinterpret_cast<const float*>(y) : nullptr;
   const int units = static_cast<int>(K / F::kQK) * F::kUnitsPerBlock;
   const Shape s = plan_rows(M, units, rows_per_pass<F>(nc, g), 256, QMV_TARGET_WAVES_PER_CU, 0);
   bool ok = s.team_lanes <= kLaunchBound && s.rows * s.slots <= M;
   int tok[kMaxCols];
   for (int j = 0; j < kMaxCols; ++j) tok[j] = j;
   std::vector<int> stores(M, 0);
-  if (Wg) begin({{W, W + M * row_bytes}, {Wg, Wg + M * row_bytes}, {y, y + nc * ycol}});
-  else begin({{W, W + M * row_bytes}, {y, y + nc * ycol}});
-  ok = ok && model_rows<F>(s, s.rows, s.slots, g, M, W, Wg, row_bytes, y, ycol, tok, nc, stores);
+  if (Wg) begin({{W, W + M * row_bytes}, {Wg, Wg + M * row_bytes}, {y, y + act_bytes}});
+  else begin({{W, W + M * row_bytes}, {y, y + act_bytes}});
+  ok = ok && model_rows<F>(s, s.rows, s.slots, g, M, W, Wg, row_bytes, xf ? nullptr : y, ycol, x, ldx, tok, nc,
+                           stores);
   for (int64_t r = 0; r < M && ok; ++r) ok = stores[r] == 1;
-  report("rows", ok, name, M, K, nc, g);
+  report(xf ? "rows_f32" : "rows", ok, name, M, K, nc, g);
   free(W);
   free(Wg);
   free(y);
@@ -109,13 +123,17 @@ static void case_rows(const char* name, int64_t M, int64_t K, int nc, int g) {
 
 // id kernel: every expert with tokens reads its own matrix at e * stride.
 template <class F>
-static void case_id(const char* name, int64_t M, int64_t K, int E, int T, int g) {
+static void case_id(const char* name, int64_t M, int64_t K, int E, int T, int g, int xpad = -1) {
   const int64_t row_bytes = K / F::kQK * F::kBlockBytes;
   const int64_t stride = (M * row_bytes + 15) / 16 * 16;
+  const bool xf = xpad >= 0;
+  const int64_t ldx = K + (xf ? xpad : 0);
   const int64_t ycol = K / 32 * kQ8Bytes;
+  const int64_t act_bytes = xf ? ((T - 1) * ldx + K) * 4 : T * ycol;
   uint8_t* W = alloc16(E * stride);
   uint8_t* Wg = alloc16(E * stride);
-  uint8_t* y = alloc16(T * ycol);
+  uint8_t* y = alloc16(act_bytes);
+  const float* x = xf ? reinterpret_cast<const float*>(y) : nullptr;
   const int units = static_cast<int>(K / F::kQK) * F::kUnitsPerBlock;
   const int R = id_rows_per_pass<F>(g);
   Shape s = plan_rows(M, units, R, 256, QMV_TARGET_WAVES_PER_CU, 0);
@@ -126,18 +144,18 @@ static void case_id(const char* name, int64_t M, int64_t K, int E, int T, int g)
     s.teams = (M + s.slots - 1) / s.slots;
     s.blocks = (s.teams + s.teams_per_block - 1) / s.teams_per_block;
   }
-  begin({{W, W + E * stride}, {Wg, Wg + E * stride}, {y, y + T * ycol}});
+  begin({{W, W + E * stride}, {Wg, Wg + E * stride}, {y, y + act_bytes}});
   bool ok = true;
   for (int e = 0; e < E && ok; ++e) {
     int tok[kMaxCols];
     const int nt = T < kMaxCols ? T : kMaxCols;
     for (int j = 0; j < nt; ++j) tok[j] = (j + e) % T;
     std::vector<int> stores(M, 0);
-    ok = model_rows<F>(s, r, s.slots, g, M, W + e * stride, g == 2 ? Wg + e * stride : nullptr, row_bytes, y,
-                       ycol, tok, nt, stores);
+    ok = model_rows<F>(s, r, s.slots, g, M, W + e * stride, g == 2 ? Wg + e * stride : nullptr, row_bytes,
+                       xf ? nullptr : y, ycol, x, ldx, tok, nt, stores);
     for (int64_t q = 0; q < M && ok; ++q) ok = stores[q] == 1;
   }
-  report("id", ok, name, M, K, T, g);
+  report(xf ? "id_f32" : "id", ok, name, M, K, T, g);
   free(W);
   free(Wg);
   free(y);
@@ -194,12 +212,15 @@ int main(int argc, char** argv) {
     for (int nb : {1, 2, 3, 5, 7, 8, 9, 16, 56}) {
       for (int nc = 1; nc <= 8; ++nc) {
         for (int g = 1; g <= 2; ++g) {
-          if (nb <= 16 || nc <= 2) {
-            case_rows<Q4K>("q4_k", M, 256LL * nb, nc, g);
-            case_rows<Q6K>("q6_k", M, 256LL * nb, nc, g);
+          for (int xpad : {-1, 3}) {
+            if (nb <= 16 || nc <= 2) {
+              case_rows<Q4K>("q4_k", M, 256LL * nb, nc, g, xpad);
+              case_rows<Q6K>("q6_k", M, 256LL * nb, nc, g, xpad);
+            }
+            if (nb * 8 * 32 <= 16384 && (nb <= 16 || nc <= 2))
+              case_rows<Q40>("q4_0", M, 32LL * nb * 8, nc, g, xpad);
+            case_rows<Q40>("q4_0", M, 32LL * nb, nc, g, xpad);
           }
-          if (nb * 8 * 32 <= 16384 && (nb <= 16 || nc <= 2)) case_rows<Q40>("q4_0", M, 32LL * nb * 8, nc, g);
-          case_rows<Q40>("q4_0", M, 32LL * nb, nc, g);
         }
       }
       if (M <= 64) {
@@ -210,17 +231,19 @@ int main(int argc, char** argv) {
     }
   }
   // longest rows a team can hold
-  case_rows<Q4K>("q4_k", 129, 16384, 1, 1);
-  case_rows<Q4K>("q4_k", 65, 16384, 8, 1);
-  case_rows<Q4K>("q4_k", 65, 16384, 1, 2);
-  case_rows<Q40>("q4_0", 129, 16384, 8, 2);
-  case_rows<Q6K>("q6_k", 129, 32768, 1, 1);
-  for (int g = 1; g <= 2; ++g) {
-    case_id<Q4K>("q4_k", 200, 512, 4, 3, g);
-    case_id<Q4K>("q4_k", 300, 2048, 8, 8, g);
-    case_id<Q40>("q4_0", 77, 1024, 5, 4, g);
-    case_id<Q6K>("q6_k", 50, 768, 4, 2, g);
-    case_id<Q4K>("q4_k", 1, 256, 3, 1, g);
+  for (int xpad : {-1, 1}) {
+    case_rows<Q4K>("q4_k", 129, 16384, 1, 1, xpad);
+    case_rows<Q4K>("q4_k", 65, 16384, 8, 1, xpad);
+    case_rows<Q4K>("q4_k", 65, 16384, 1, 2, xpad);
+    case_rows<Q40>("q4_0", 129, 16384, 8, 2, xpad);
+    case_rows<Q6K>("q6_k", 129, 32768, 1, 1, xpad);
+    for (int g = 1; g <= 2; ++g) {
+      case_id<Q4K>("q4_k", 200, 512, 4, 3, g, xpad);
+      case_id<Q4K>("q4_k", 300, 2048, 8, 8, g, xpad);
+      case_id<Q40>("q4_0", 77, 1024, 5, 4, g, xpad);
+      case_id<Q6K>("q6_k", 50, 768, 4, 2, g, xpad);
+      case_id<Q4K>("q4_k", 1, 256, 3, 1, g, xpad);
+    }
   }
   for (int64_t K : {32, 64, 96, 1024, 14336})
     for (int64_t n : {1, 3, 8})
@@ -229,6 +252,7 @@ int main(int argc, char** argv) {
     for (int nc : {1, 2, 4, 8}) {
       case_rows<Q4K>("q4_k", 4096, 14336, nc, 1);
       case_rows<Q4K>("q4_k", 14336, 4096, nc, 1);
+      case_rows<Q4K>("q4_k", 4096, 14336, nc, 1, 0);
     }
     case_rows<Q4K>("q4_k", 4096, 4096, 1, 1);
     case_rows<Q40>("q4_0", 256, 1024, 1, 1);

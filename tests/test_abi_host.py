@@ -17,7 +17,8 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = B.declared_symbols()
     assert set(names) == {"mmvq_type_info", "mmvq_quantize_q8_1", "mmvq", "mmvq_glu", "mmvq_id",
-                          "mmvq_id_glu", "mmvq_block_dots", "mmvq_strerror"}
+                          "mmvq_id_glu", "mmvq_f32", "mmvq_glu_f32", "mmvq_id_f32", "mmvq_id_glu_f32",
+                          "mmvq_block_dots", "mmvq_strerror"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -82,6 +83,28 @@ def test_other_entry_points_argument_checks(L):
     assert L.mmvq_quantize_q8_1(P16, 32, 9, 32, P16, None) == B.ERR_SHAPE
     assert L.mmvq_quantize_q8_1(P16 + 2, 32, 1, 32, P16, None) == B.ERR_ALIGN
     assert L.mmvq_quantize_q8_1(P16, 32, 1, 32, P4, None) == B.ERR_ALIGN
+
+
+def test_f32_entry_points_argument_checks(L):
+    assert L.mmvq_f32(P16, B.Q4_K, 1, 256, None, 1, 256, P16, None) == B.ERR_NULL
+    assert L.mmvq_f32(None, B.Q4_K, 1, 256, P16, 1, 256, P16, None) == B.ERR_NULL
+    assert L.mmvq_f32(P16, B.Q8_1, 1, 256, P16, 1, 256, P16, None) == B.ERR_TYPE
+    assert L.mmvq_f32(P16, B.Q4_K, 1, 256, P16, 1, 255, P16, None) == B.ERR_SHAPE
+    assert L.mmvq_f32(P16, B.Q4_K, 1, 256, P16, 9, 256, P16, None) == B.ERR_SHAPE
+    assert L.mmvq_f32(P16, B.Q4_K, 1, 256 * 65, P16, 1, 256 * 65, P16, None) == B.ERR_SHAPE
+    assert L.mmvq_f32(P16, B.Q4_K, 1, 256, P16 + 2, 1, 256, P16, None) == B.ERR_ALIGN
+    # fp32 x needs only 4-byte alignment (q8_1 columns need 16)
+    assert L.mmvq_f32(P4, B.Q4_K, 1, 256, P16, 1, 256, P16, None) == B.ERR_ALIGN
+    assert L.mmvq_glu_f32(None, P16, B.Q4_K, 1, 256, P16, 1, 256, 1, P16, None) == B.ERR_NULL
+    assert L.mmvq_glu_f32(P16, P16, B.Q4_K, 1, 256, P16, 1, 256, 2, P16, None) == B.ERR_TYPE
+    assert L.mmvq_glu_f32(P16, P16, B.Q4_K, 1, 256, None, 1, 256, 1, P16, None) == B.ERR_NULL
+    assert L.mmvq_id_f32(P16, 288, 4, B.Q4_K, 2, 256, P16, 1, 256, None, 1, P16, None) == B.ERR_NULL
+    assert L.mmvq_id_f32(P16, 288, 4, B.Q4_K, 2, 256, P16, 1, 100, P16, 1, P16, None) == B.ERR_SHAPE
+    assert L.mmvq_id_f32(P16, 288, 4, B.Q4_K, 2, 256, None, 1, 256, P16, 1, P16, None) == B.ERR_NULL
+    assert L.mmvq_id_glu_f32(P16, P16, 288, 4, B.Q4_K, 2, 256, P16, 1, 256, P16, 1, 3, P16,
+                             None) == B.ERR_TYPE
+    assert L.mmvq_id_glu_f32(P16, P16, 288, 4, B.Q4_K, 2, 256, P16, 1, 256, P16, 5, 1, P16,
+                             None) == B.ERR_SHAPE
 
 
 def test_binding_raises_with_code():

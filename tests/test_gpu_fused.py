@@ -1,0 +1,226 @@
+"""GPU parity of the fused fp32-activation entry points (mmvq_f32,
+mmvq_glu_f32, mmvq_id_f32, mmvq_id_glu_f32).
+
+Each must equal, bit for bit, the q8_1 quantizer followed by the matching
+q8_1 entry point on the same inputs (the kernel quantizes in its prologue
+with the quantizer's arithmetic), and be within the oracle tolerance of the
+oracle's quantize-then-multiply. Activations include the quantizer's edge
+cases (zero, tie, subnormal, large and constant blocks) and column strides
+that are not multiples of 4 floats.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import (TNAME, announce, assert_close, dev, glu_tolerance, gpu_quantize, host, oracle_rows,
+                         sample_rows, special_x)
+from quantized_decode_gemv_quantize_amd import binding as B
+from quantized_decode_gemv_quantize_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+Q4_0, Q4_K, Q6_K = B.Q4_0, B.Q4_K, B.Q6_K
+
+
+@pytest.fixture(scope="module")
+def O():
+    return oracle.default()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+
+
+def _empty(rows, M):
+    import torch
+    return torch.full((rows, M), float("nan"), dtype=torch.float32, device="cuda:0")
+
+
+def _same(a, b, what):
+    """Bit-for-bit equality of two fp32 device tensors (NaN and inf included)."""
+    import torch
+    torch.cuda.synchronize()
+    ai, bi = a.view(torch.int32), b.view(torch.int32)
+    if not torch.equal(ai, bi):
+        diff = ai != bi
+        i = tuple(int(v) for v in diff.nonzero()[0])
+        raise AssertionError(f"{what}: fused {a[i].item()!r} != two-step {b[i].item()!r} at {i} "
+                             f"({int(diff.sum())} differ)")
+
+
+FUSED_CASES = [(Q4_0, 37, 96, 1, 0), (Q4_0, 300, 1024, 3, 5), (Q4_0, 129, 16384, 8, 1),
+               (Q4_K, 1, 256, 1, 0), (Q4_K, 37, 512, 2, 3), (Q4_K, 1000, 4096, 5, 0),
+               (Q4_K, 129, 14336, 8, 7), (Q4_K, 65, 16384, 1, 1),
+               (Q6_K, 1, 256, 1, 0), (Q6_K, 37, 768, 3, 2), (Q6_K, 300, 4096, 8, 0),
+               (Q6_K, 129, 32768, 2, 1)]
+
+
+@pytest.mark.parametrize("wtype,M,K,n,pad", FUSED_CASES,
+                         ids=[f"{TNAME[c[0]]}-{c[1]}x{c[2]}-n{c[3]}-pad{c[4]}" for c in FUSED_CASES])
+def test_mmvq_f32(O, wtype, M, K, n, pad):
+    announce(f"mmvq_f32 {TNAME[wtype]} M={M} K={K} n={n} ldx=K+{pad}")
+    rng = np.random.default_rng(31 * M + K + n)
+    W = synth.weights(wtype, M, K, rng)
+    x = special_x(K, n, seed=M + n, ldx=K + pad)
+    Wd, xd = dev(W), dev(x)
+    fused, two = _empty(n, M), _empty(n, M)
+    B.mmvq_f32(Wd, wtype, M, K, xd, n, K + pad, fused)
+    yd = gpu_quantize(x, K)
+    B.mmvq(Wd, wtype, M, K, yd, n, two)
+    _same(fused, two, f"mmvq_f32 {TNAME[wtype]} {M}x{K} n={n}")
+    y = O.quantize_q8_1(x, K)
+    ref, mag, _ = O.mmvq(W, wtype, M, K, y, n)
+    assert_close(host(fused), ref, mag, f"mmvq_f32 {TNAME[wtype]} {M}x{K} n={n}")
+
+
+GLU_F32 = [(Q4_K, 300, 4096, 1, B.GLU_SWIGLU), (Q4_K, 37, 512, 4, B.GLU_PLAIN),
+           (Q4_0, 300, 1024, 2, B.GLU_SWIGLU), (Q6_K, 37, 768, 3, B.GLU_SWIGLU),
+           (Q4_K, 129, 14336, 8, B.GLU_SWIGLU)]
+
+
+@pytest.mark.parametrize("wtype,M,K,n,op", GLU_F32,
+                         ids=[f"{TNAME[c[0]]}-{c[1]}x{c[2]}-n{c[3]}-op{c[4]}" for c in GLU_F32])
+def test_mmvq_glu_f32(O, wtype, M, K, n, op):
+    announce(f"mmvq_glu_f32 {TNAME[wtype]} M={M} K={K} n={n} op={op}")
+    rng = np.random.default_rng(M + K + 17 * n + op)
+    Wg, Wu = synth.weights(wtype, M, K, rng), synth.weights(wtype, M, K, rng)
+    ldx = K + 1
+    x = synth.activations(K, n, rng, ldx)
+    Wgd, Wud, xd = dev(Wg), dev(Wu), dev(x)
+    fused, two = _empty(n, M), _empty(n, M)
+    B.mmvq_glu_f32(Wgd, Wud, wtype, M, K, xd, n, ldx, op, fused)
+    B.mmvq_glu(Wgd, Wud, wtype, M, K, gpu_quantize(x, K), n, op, two)
+    _same(fused, two, f"mmvq_glu_f32 {TNAME[wtype]} {M}x{K} n={n}")
+    y = O.quantize_q8_1(x, K)
+    g, mg, _ = O.mmvq(Wg, wtype, M, K, y, n)
+    u, mu, _ = O.mmvq(Wu, wtype, M, K, y, n)
+    ref = (g / (1.0 + np.exp(-g)) if op == B.GLU_SWIGLU else g) * u
+    tol = glu_tolerance(g, u, mg, mu, ref, op)
+    got = host(fused).astype(np.float64)
+    bad = ~(np.abs(got - ref) <= tol)
+    assert not bad.any(), f"first bad at {np.argwhere(bad)[0]}"
+
+
+ID_F32 = [("q4_k-E4-T3-k2", Q4_K, 4, 200, 512, [[2, 0], [1, 2], [2, 3]]),
+          ("q4_k-E8-T8-k2", Q4_K, 8, 300, 2048, "random"),
+          ("q4_0-E5-T4-k2", Q4_0, 5, 77, 1024, [[4, 0], [0, 4], [2, 2], [1, 3]]),
+          ("q6_k-E4-T2-k2", Q6_K, 4, 50, 768, [[3, 1], [1, 0]])]
+
+
+@pytest.mark.parametrize("fused_glu", [False, True])
+@pytest.mark.parametrize("name,wtype,E,M,K,ids", ID_F32, ids=[c[0] for c in ID_F32])
+def test_mmvq_id_f32(O, name, wtype, E, M, K, ids, fused_glu):
+    announce(f"mmvq_id{'_glu' if fused_glu else ''}_f32 {name}")
+    if isinstance(ids, str):
+        ids = synth.expert_ids(8, 2, E, np.random.default_rng(5))
+    ids = np.asarray(ids, dtype=np.int32)
+    T, top_k = ids.shape
+    rng = np.random.default_rng(len(name) + 100)
+    Wu = np.stack([synth.weights(wtype, M, K, rng) for _ in range(E)])
+    Wg = np.stack([synth.weights(wtype, M, K, rng) for _ in range(E)])
+    ldx = K + 2
+    x = synth.activations(K, T, rng, ldx)
+    stride = (Wu[0].size + 15) // 16 * 16
+    pad = lambda A: np.concatenate(  # noqa: E731
+        [np.pad(A[e].reshape(-1), (0, stride - A[e].size)) for e in range(E)])
+    Wud, Wgd, xd, idsd = dev(pad(Wu)), dev(pad(Wg)), dev(x), dev(ids)
+    fused, two = _empty(T * top_k, M), _empty(T * top_k, M)
+    yd = gpu_quantize(x, K)
+    if fused_glu:
+        B.mmvq_id_glu_f32(Wgd, Wud, stride, E, wtype, M, K, xd, T, ldx, idsd, top_k, B.GLU_SWIGLU, fused)
+        B.mmvq_id_glu(Wgd, Wud, stride, E, wtype, M, K, yd, T, idsd, top_k, B.GLU_SWIGLU, two)
+    else:
+        B.mmvq_id_f32(Wud, stride, E, wtype, M, K, xd, T, ldx, idsd, top_k, fused)
+        B.mmvq_id(Wud, stride, E, wtype, M, K, yd, T, idsd, top_k, two)
+    _same(fused, two, f"id f32 {name}")
+    # oracle on the plain form (the fused GLU form is pinned to mmvq_id_glu,
+    # whose own oracle parity is tested with the q8_1 entry points)
+    if not fused_glu:
+        y = O.quantize_q8_1(x, K)
+        got = host(fused).astype(np.float64)
+        for t in range(T):
+            for k in range(top_k):
+                u, mu = oracle_rows(O, Wu[int(ids[t, k])], wtype, M, K, y[t:t + 1], 1, [(0, M)])
+                assert_close(got[t * top_k + k:t * top_k + k + 1], u, mu, f"id f32 token {t} slot {k}")
+
+
+WORKLOADS_F32 = [("q4_k_4096x14336", 1), ("q4_k_4096x14336", 8), ("q6_k_128256x4096", 1),
+                 ("q4_0_256x1024", 1)]
+
+
+@pytest.mark.parametrize("name,n", WORKLOADS_F32, ids=[f"{a}-n{b}" for a, b in WORKLOADS_F32])
+def test_mmvq_f32_workload(O, name, n):
+    """Workload sizes in the launch configuration the benchmark times: all
+    rows bit-identical to the two-step path, sampled rows against the oracle."""
+    wl = synth.BY_NAME[name]
+    announce(f"mmvq_f32 workload {name} n={n}")
+    d = synth.make(wl, n)
+    W, x = d["W"], d["x"]
+    M, K = wl.M, wl.K
+    Wd, xd = dev(W), dev(x)
+    fused, two = _empty(n, M), _empty(n, M)
+    B.mmvq_f32(Wd, wl.wtype, M, K, xd, n, x.shape[1], fused)
+    B.mmvq(Wd, wl.wtype, M, K, gpu_quantize(x, K), n, two)
+    _same(fused, two, f"mmvq_f32 {name} n={n}")
+    y = O.quantize_q8_1(x, K)
+    ranges = sample_rows(M, 256, seed=n)
+    ref, mag = oracle_rows(O, W, wl.wtype, M, K, y, n, ranges)
+    got = host(fused)
+    sel = np.concatenate([np.arange(a, b) for a, b in ranges])
+    assert_close(got[:, sel], ref[:, sel], mag[:, sel], f"mmvq_f32 {name} n={n}")
+
+
+def test_f32_graph_replay():
+    """One fused launch captured in a HIP graph on a side stream, replayed
+    with new activations copied in between (eager work and synchronization
+    between replays): every replay equals the eager two-step result."""
+    import torch
+    announce("mmvq_f32 graph replay")
+    rng = np.random.default_rng(78)
+    M, K = 1000, 4096
+    W = dev(synth.weights(Q4_K, M, K, rng))
+    xs = [dev(synth.activations(K, 2, rng)) for _ in range(3)]
+    eager = []
+    for xv in xs:
+        o = _empty(2, M)
+        B.mmvq(W, Q4_K, M, K, B.quantize(xv), 2, o)
+        eager.append(o)
+    torch.cuda.synchronize()
+    x_in = xs[0].clone()
+    out = _empty(2, M)
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        B.mmvq_f32(W, Q4_K, M, K, x_in, 2, K, out, side)
+    for rep in range(6):
+        x_in.copy_(xs[rep % 3])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _same(out, eager[rep % 3], f"replay {rep}")
+        _ = W[:1024].float().sum()
+    torch.cuda.synchronize()
+
+
+def test_f32_errors_on_device():
+    import torch
+    announce("f32 abi errors")
+    W = torch.zeros(1 << 16, dtype=torch.uint8, device="cuda:0")
+    x = torch.zeros(1 << 14, dtype=torch.float32, device="cuda:0")
+    out = torch.zeros(1 << 14, dtype=torch.float32, device="cuda:0")
+    L = B.lib()
+    s = torch.cuda.current_stream().cuda_stream
+    p, q, o = W.data_ptr(), x.data_ptr(), out.data_ptr()
+    assert L.mmvq_f32(p, Q4_K, 1, 256, q, 1, 255, o, s) == B.ERR_SHAPE
+    assert L.mmvq_f32(p, Q4_K, 1, 256, q + 2, 1, 256, o, s) == B.ERR_ALIGN
+    assert L.mmvq_f32(p, Q4_K, 1, 256, q, 9, 256, o, s) == B.ERR_SHAPE
+    assert L.mmvq_f32(p + 8, Q4_K, 1, 256, q, 1, 256, o, s) == B.ERR_ALIGN
+    # x needs only 4-byte alignment: a valid call (zero weights give 0)
+    out.fill_(float("nan"))
+    assert L.mmvq_f32(p, Q4_K, 1, 256, q + 4, 1, 256, o, s) == 0
+    torch.cuda.synchronize()
+    assert out[0].item() == 0.0

@@ -13,15 +13,14 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_helpers import (announce, assert_close, dev, glu_tolerance, gpu_gemv, gpu_quantize, host,
-                         oracle_rows, sample_rows)
+from gpu_helpers import (TNAME, announce, assert_close, dev, glu_tolerance, gpu_gemv, gpu_quantize, host,
+                         oracle_rows, sample_rows, special_x)
 from quantized_decode_gemv_quantize_amd import binding as B
 from quantized_decode_gemv_quantize_amd import synth
 
 pytestmark = pytest.mark.gpu
 
 Q4_0, Q4_K, Q6_K = B.Q4_0, B.Q4_K, B.Q6_K
-TNAME = {Q4_0: "q4_0", Q4_K: "q4_k", Q6_K: "q6_k"}
 
 
 @pytest.fixture(scope="module")
@@ -35,34 +34,6 @@ def _gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     B.lib()
-
-
-def special_x(K: int, n: int, seed: int, ldx: int | None = None) -> np.ndarray:
-    """N(0,1) activations with some blocks replaced by edge cases: all zero,
-    exact .5 ties at d = 1, fp32 subnormals, large values (s overflows fp16),
-    a single nonzero element, constant blocks."""
-    rng = np.random.default_rng(seed)
-    x = synth.activations(K, n, rng, ldx)
-    nb = K // 32
-    for j in range(n):
-        for b in range(nb):
-            kind = (b + 3 * j) % 9
-            blk = x[j, 32 * b:32 * b + 32]
-            if kind == 1:
-                blk[:] = 0
-            elif kind == 2:
-                blk[:] = (rng.integers(-100, 100, 32) + 0.5).astype(np.float32)
-                blk[0] = 127.0
-            elif kind == 3:
-                blk[:] = rng.standard_normal(32).astype(np.float32) * np.float32(1e-40)
-            elif kind == 4:
-                blk[:] = rng.standard_normal(32).astype(np.float32) * np.float32(3e4)
-            elif kind == 5:
-                blk[:] = 0
-                blk[int(rng.integers(0, 32))] = -7.25
-            elif kind == 6:
-                blk[:] = 2.0
-    return x
 
 
 # ---------------------------------------------------------------------------

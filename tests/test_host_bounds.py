@@ -30,3 +30,15 @@ def test_kernel_accesses_in_bounds(tmp_path):
     res = subprocess.run([str(exe), "full"], capture_output=True, text=True, timeout=600)
     assert res.returncode == 0, res.stdout[-4000:] + res.stderr[-2000:]
     assert "0 failing case(s)" in res.stdout
+
+
+def test_q8_fast_quantizer_exact(tmp_path):
+    """The quantizer's reciprocal fast path with exact fallback (q8.hpp)
+    gives roundf(x/d) for every value: random blocks at all scales and values
+    placed within 8 ulps of every code boundary, on the host."""
+    exe = tmp_path / "q8_fast"
+    subprocess.check_call([_clang(), "-std=c++17", "-O2", "-ffp-contract=off", "-DQMV_HOST_MODEL", "-I", INC,
+                           "-o", str(exe), os.path.join(ROOT, "tests", "host_model", "q8_fast.cpp")])
+    res = subprocess.run([str(exe), "400000"], capture_output=True, text=True, timeout=300)
+    assert res.returncode == 0, res.stdout[-4000:] + res.stderr[-2000:]
+    assert " 0 mismatches" in res.stdout
