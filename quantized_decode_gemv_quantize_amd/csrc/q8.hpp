@@ -44,37 +44,51 @@ __device__ __forceinline__ uint32_t q8_quant4(const u32x4& r, float d, int& sum)
          ((static_cast<uint32_t>(q2) & 0xFFu) << 16) | (static_cast<uint32_t>(q3) << 24);
 }
 
+// Low bytes of four words packed into one word (byte k = low byte of w_k).
+__device__ __forceinline__ uint32_t pack_low_bytes(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
+#ifndef QMV_HOST_MODEL
+  // v_perm_b32 selects bytes of {hi, lo}: 0x0c yields 0
+  const uint32_t lo = __builtin_amdgcn_perm(w1, w0, 0x0c0c0400u);
+  const uint32_t hi = __builtin_amdgcn_perm(w3, w2, 0x04000c0cu);
+  return lo | hi;
+#else
+  return (w0 & 0xFFu) | ((w1 & 0xFFu) << 8) | ((w2 & 0xFFu) << 16) | ((w3 & 0xFFu) << 24);
+#endif
+}
+
 // Codes of the 4*W values of one q8_1 block that the lane holds (word k of
 // `out` packs the codes of v[k]), their sum added to `sum`; equal to
-// q8_quant4 on every word, at about half the arithmetic:
+// q8_quant4 on every word, at about a third of the arithmetic:
 //   r = 1/d correctly rounded, once per block; q1 = x*r. With u = 2^-24,
 //   |q1 - RN(x/d)| <= 3.001*u*|q1| (one rounding in r, one in the product,
 //   one in RN(x/d)), and |q1| <= 127.0001 since |x| <= amax and
 //   d = RN(amax/127). So when q1 is farther than 2^-15 (> 3.001*u*128) from
 //   every half-integer, no half-integer lies between q1 and RN(x/d) or on
-//   either, and roundf(q1) == roundf(RN(x/d)). Otherwise (rare), or when d
-//   is 0 or subnormal (r out of range), the block is redone with exact
-//   quotients.
+//   either, and both round to the same integer: then rounding q1 to nearest
+//   (adding and removing 1.5*2^23, whose ulp is 1) gives the code, whose
+//   two's complement low byte is the low byte of the biased sum. Otherwise
+//   (rare), or when d is 0 or subnormal (r out of range), the block is redone
+//   with exact quotients.
 template <int W>
 __device__ __forceinline__ void q8_quant_block(const u32x4 (&v)[W], float d, uint32_t (&out)[W], int& sum) {
+  constexpr float kBias = 0x1.8p23f;
   const bool normal = d >= 0x1p-126f;
   const float r = 1.0f / (normal ? d : 1.0f);
   bool near = !normal;
   int s = 0;
 #pragma unroll
   for (int k = 0; k < W; ++k) {
-    uint32_t w = 0;
+    uint32_t m[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float q = __uint_as_float(v[k][e]) * r;
-      const float t = truncf(q);
-      const float f = fabsf(q - t);                 // exact
-      near = near || fabsf(f - 0.5f) <= 0x1p-15f;
-      const int c = static_cast<int>(t) + (f >= 0.5f ? (q < 0.0f ? -1 : 1) : 0);
-      s += c;
-      w |= (static_cast<uint32_t>(c) & 0xFFu) << (8 * e);
+      const float biased = q + kBias;
+      const float rq = biased - kBias;                 // q rounded to nearest, exact
+      near = near || fabsf(q - rq) >= 0.5f - 0x1p-15f;
+      m[e] = __float_as_uint(biased);
     }
-    out[k] = w;
+    out[k] = pack_low_bytes(m[0], m[1], m[2], m[3]);
+    s = dot4(out[k], 0x01010101u, s);
   }
   if (near) {
     s = 0;
