@@ -23,7 +23,7 @@ SRC = os.path.join(HERE, "mmvq_oracle.c")
 LIB = os.path.join(HERE, "libmmvq_oracle.so")
 
 Q4_0, Q8_1, Q4_K, Q6_K = 2, 9, 12, 14
-GLU_PLAIN, GLU_SWIGLU = 0, 1
+GLU_PLAIN, GLU_SWIGLU, GLU_GEGLU, GLU_SWIGLU_OAI, GLU_SWIGLU_CLAMP = 0, 1, 2, 3, 4
 BLOCK = {Q4_0: (32, 18), Q4_K: (256, 144), Q6_K: (256, 210), Q8_1: (32, 36)}
 DOTS_PER_BLOCK = {Q4_0: 1, Q4_K: 16, Q6_K: 16}
 
@@ -63,6 +63,29 @@ def _u8(a) -> np.ndarray:
                                 else a).view(np.uint8).reshape(-1)
 
 
+class _Epilogue(ctypes.Structure):
+    _fields_ = [("up_bias", _p), ("gate_bias", _p), ("up_scale", _p), ("gate_scale", _p),
+                ("glu_op", ctypes.c_int), ("limit", ctypes.c_double), ("alpha", ctypes.c_double)]
+
+
+def _epilogue(epi: dict | None, keep: list):
+    """dict(up_bias=, gate_bias=, up_scale=, gate_scale= (arrays or None),
+    glu_op=, limit=, alpha=) -> ctypes struct (arrays kept alive in keep)."""
+    if epi is None:
+        return None
+    e = _Epilogue()
+    for name in ("up_bias", "gate_bias", "up_scale", "gate_scale"):
+        v = epi.get(name)
+        if v is not None:
+            a = np.ascontiguousarray(np.asarray(v, dtype=np.float64).reshape(-1))
+            keep.append(a)
+            setattr(e, name, a.ctypes.data)
+    e.glu_op = int(epi.get("glu_op", GLU_PLAIN))
+    e.limit = float(epi.get("limit", 0.0))
+    e.alpha = float(epi.get("alpha", 0.0))
+    return ctypes.byref(e), e
+
+
 def _load(path: str):
     L = ctypes.CDLL(path)
     L.orc_f32_to_f16.restype = ctypes.c_uint16
@@ -79,6 +102,13 @@ def _load(path: str):
                               _p, _c_i64, _p, ctypes.c_int, _p, _p]
     L.orc_mmvq_id_glu.argtypes = [_p, _p, _c_i64, ctypes.c_int, ctypes.c_int, _c_i64,
                                   _c_i64, _p, _c_i64, _p, ctypes.c_int, ctypes.c_int, _p]
+    L.orc_glu.argtypes = [ctypes.c_int, ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                          ctypes.c_double, ctypes.POINTER(ctypes.c_double)]
+    L.orc_mmvq_ex.argtypes = [_p, _p, ctypes.c_int, _c_i64, _c_i64, _p, _c_i64,
+                              ctypes.POINTER(_Epilogue), _p]
+    L.orc_mmvq_id_ex.argtypes = [_p, _p, _c_i64, ctypes.c_int, ctypes.c_int, _c_i64, _c_i64,
+                                 _p, _c_i64, _p, ctypes.c_int, ctypes.POINTER(_Epilogue),
+                                 _p, _p, _p, _p]
     L.orc_dequantize_row.argtypes = [ctypes.c_int, _p, _c_i64, _p]
     L.orc_dequantize_q8_1.argtypes = [_p, _c_i64, _p]
     L.orc_q4_k_scale_min.argtypes = [_p, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
@@ -174,6 +204,38 @@ class Oracle:
                                      wtype, M, K, _ptr(_u8(y_q)), n_tokens, _ptr(ids), top_k,
                                      glu_op, _ptr(out)))
         return out
+
+    def glu(self, glu_op: int, g: float, u: float, limit: float = 0.0, alpha: float = 0.0) -> float:
+        out = ctypes.c_double()
+        _check(self.L.orc_glu(glu_op, g, u, limit, alpha, ctypes.byref(out)))
+        return out.value
+
+    def mmvq_ex(self, Wu, Wg, wtype: int, M: int, K: int, y_q: np.ndarray, n: int,
+                epi: dict | None = None) -> np.ndarray:
+        """Full fused epilogue (Wg None: no gate). Returns out [n, M]."""
+        keep: list = []
+        ep = _epilogue(epi, keep)
+        out = np.zeros((n, M))
+        _check(self.L.orc_mmvq_ex(_ptr(_u8(Wu)), None if Wg is None else _ptr(_u8(Wg)), wtype, M, K,
+                                 _ptr(_u8(y_q)), n, None if ep is None else ep[0], _ptr(out)))
+        return out
+
+    def mmvq_id_ex(self, Wu, Wg, expert_stride: int, n_experts: int, wtype: int, M: int, K: int,
+                   y_q: np.ndarray, n_tokens: int, ids: np.ndarray, top_k: int,
+                   epi: dict | None = None, shared_up=None, shared_gate=None):
+        """Returns (out [n_tokens*top_k, M], shared_out [n_tokens, M] or None)."""
+        keep: list = []
+        ep = _epilogue(epi, keep)
+        ids = np.ascontiguousarray(ids, dtype=np.int32).reshape(-1)
+        out = np.zeros((n_tokens * top_k, M))
+        sh = np.zeros((n_tokens, M)) if shared_up is not None else None
+        _check(self.L.orc_mmvq_id_ex(
+            _ptr(_u8(Wu)), None if Wg is None else _ptr(_u8(Wg)), expert_stride, n_experts, wtype, M, K,
+            _ptr(_u8(y_q)), n_tokens, _ptr(ids), top_k, None if ep is None else ep[0],
+            None if shared_up is None else _ptr(_u8(shared_up)),
+            None if shared_gate is None else _ptr(_u8(shared_gate)),
+            None if sh is None else _ptr(sh), _ptr(out)))
+        return out, sh
 
     def dequantize_row(self, wtype: int, row, K: int) -> np.ndarray:
         w = np.zeros(K)

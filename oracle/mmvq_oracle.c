@@ -401,6 +401,72 @@ int orc_mmvq_glu(const uint8_t *W_gate, const uint8_t *W_up, int type,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Full fused epilogue [MMVQ §融合]                                           */
+/* ------------------------------------------------------------------------ */
+/* The pages name the GLU variants but print only the silu one. Readings:
+ * gelu is the exact z*Phi(z) = z/2*(1 + erf(z/sqrt 2)); the OAI variant is
+ * the published clamped form g'*sigmoid(alpha*g')*(u'+1); the clamp variant
+ * is silu(g')*u'; g' = min(g, limit), u' = clamp(u, -limit, limit). */
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+int orc_glu(int glu_op, double g, double u, double limit, double alpha, double *out) {
+    if (!out) return ORC_ERR_NULL;
+    const double gc = g < limit ? g : limit;
+    const double uc = u < -limit ? -limit : (u > limit ? limit : u);
+    switch (glu_op) {
+    case ORC_GLU_PLAIN: *out = g * u; break;
+    case ORC_GLU_SWIGLU: *out = silu(g) * u; break;
+    case ORC_GLU_GEGLU: *out = 0.5 * g * (1.0 + erf(g / sqrt(2.0))) * u; break;
+    case ORC_GLU_SWIGLU_OAI: *out = gc / (1.0 + exp(-alpha * gc)) * (uc + 1.0); break;
+    case ORC_GLU_SWIGLU_CLAMP: *out = silu(gc) * uc; break;
+    default: return ORC_ERR_TYPE;
+    }
+    return ORC_OK;
+}
+
+/* One output: raw dots of the up (and gate) row, then the epilogue, with
+ * the scales and biases of expert e (0 outside the expert-indexed form). */
+static int epilogue_one(const orc_epilogue *epi, int has_gate, int e, int64_t M, int64_t r,
+                        double up, double gate, double *out) {
+    if (!epi) {
+        *out = has_gate ? gate * up : up;
+        return ORC_OK;
+    }
+    double u = up;
+    if (epi->up_scale) u *= epi->up_scale[e];
+    if (epi->up_bias) u += epi->up_bias[(int64_t)e * M + r];
+    if (!has_gate) {
+        *out = u;
+        return ORC_OK;
+    }
+    double g = gate;
+    if (epi->gate_scale) g *= epi->gate_scale[e];
+    if (epi->gate_bias) g += epi->gate_bias[(int64_t)e * M + r];
+    return orc_glu(epi->glu_op, g, u, epi->limit, epi->alpha, out);
+}
+
+int orc_mmvq_ex(const uint8_t *W_up, const uint8_t *W_gate, int type,
+                int64_t M, int64_t K, const uint8_t *y_q, int64_t n,
+                const orc_epilogue *epi, double *out) {
+    int qk, bb;
+    int rc = gemv_args_ok(W_up, type, M, K, y_q, n, &qk, &bb);
+    if (rc) return rc;
+    if (!out) return ORC_ERR_NULL;
+    const int64_t nb = K / qk;
+    const int64_t ycol_bytes = (K / 32) * 36;
+    for (int64_t j = 0; j < n; ++j) {
+        for (int64_t r = 0; r < M; ++r) {
+            double u, g = 0.0, mag;
+            row_dot(W_up + r * nb * bb, type, nb, bb, qk, y_q + j * ycol_bytes, &u, &mag, NULL);
+            if (W_gate) row_dot(W_gate + r * nb * bb, type, nb, bb, qk, y_q + j * ycol_bytes, &g, &mag, NULL);
+            rc = epilogue_one(epi, W_gate != NULL, 0, M, r, u, g, &out[j * M + r]);
+            if (rc) return rc;
+        }
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Expert-indexed product [MMVQ §MoE, §正确性上的几个坑]                      */
 /* ------------------------------------------------------------------------ */
 /* Reading: token t's one q8_1 column is shared by its top_k slots, and the
@@ -454,6 +520,55 @@ int orc_mmvq_id_glu(const uint8_t *W_gate, const uint8_t *W_up,
             rc = orc_mmvq_glu(W_gate + off, W_up + off, type, M, K,
                               y_q + t * (K / 32) * 36, 1, glu_op, out + slot * M);
             if (rc) return rc;
+        }
+    }
+    return ORC_OK;
+}
+
+/* Expert-indexed epilogue form; the shared expert (an extra grid slice on
+ * the pages) applies to every token with the GLU only [MMVQ §融合]. */
+int orc_mmvq_id_ex(const uint8_t *W_up, const uint8_t *W_gate,
+                   int64_t expert_stride, int n_experts, int type,
+                   int64_t M, int64_t K, const uint8_t *y_q,
+                   int64_t n_tokens, const int32_t *ids, int top_k,
+                   const orc_epilogue *epi, const uint8_t *shared_up,
+                   const uint8_t *shared_gate, double *shared_out,
+                   double *out) {
+    if (!y_q || !out) return ORC_ERR_NULL;
+    if (shared_up && !shared_out) return ORC_ERR_NULL;
+    int rc = id_args_ok(W_up, expert_stride, n_experts, type, M, K, n_tokens, ids, top_k);
+    if (rc) return rc;
+    int qk, bb;
+    orc_type_info(type, &qk, &bb);
+    const int64_t nb = K / qk;
+    const int64_t ycol_bytes = (K / 32) * 36;
+    for (int64_t t = 0; t < n_tokens; ++t) {
+        const uint8_t *yt = y_q + t * ycol_bytes;
+        for (int k = 0; k < top_k; ++k) {
+            const int64_t slot = t * top_k + k;
+            const int e = ids[slot];
+            const int64_t off = (int64_t)e * expert_stride;
+            for (int64_t r = 0; r < M; ++r) {
+                double u, g = 0.0, mag;
+                row_dot(W_up + off + r * nb * bb, type, nb, bb, qk, yt, &u, &mag, NULL);
+                if (W_gate) row_dot(W_gate + off + r * nb * bb, type, nb, bb, qk, yt, &g, &mag, NULL);
+                rc = epilogue_one(epi, W_gate != NULL, e, M, r, u, g, &out[slot * M + r]);
+                if (rc) return rc;
+            }
+        }
+        if (shared_up) {
+            for (int64_t r = 0; r < M; ++r) {
+                double u, g = 0.0, mag;
+                row_dot(shared_up + r * nb * bb, type, nb, bb, qk, yt, &u, &mag, NULL);
+                if (shared_gate) {
+                    row_dot(shared_gate + r * nb * bb, type, nb, bb, qk, yt, &g, &mag, NULL);
+                    rc = orc_glu(epi ? epi->glu_op : ORC_GLU_PLAIN, g, u, epi ? epi->limit : 0.0,
+                                 epi ? epi->alpha : 0.0, &shared_out[t * M + r]);
+                    if (rc) return rc;
+                } else {
+                    shared_out[t * M + r] = u;
+                }
+            }
         }
     }
     return ORC_OK;

@@ -22,6 +22,8 @@
  *      [MMVQ §一次 vec_dot 的解剖, §dp4a].
  *   3. The fused gate/up GLU epilogue [MMVQ §融合] and the expert-indexed
  *      mul_mat_id [MMVQ §MoE, §正确性上的几个坑].
+ *   4. The full fused epilogue [MMVQ §融合]: per-matrix scales, biases, the
+ *      GLU variants, and the shared expert of a MoE layer.
  *
  * Every function returns 0 on success or a negative ORC_ERR_* code, and
  * never aborts.
@@ -41,8 +43,12 @@ extern "C" {
 #define ORC_Q4_K 12
 #define ORC_Q6_K 14
 
-#define ORC_GLU_PLAIN  0 /* out = gate * up (the epilogue's default branch) */
-#define ORC_GLU_SWIGLU 1 /* out = silu(gate) * up                          */
+#define ORC_GLU_PLAIN        0 /* out = gate * up (the epilogue's default branch) */
+#define ORC_GLU_SWIGLU       1 /* out = silu(gate) * up                          */
+#define ORC_GLU_GEGLU        2 /* out = gelu(gate) * up, gelu exact (erf form)    */
+#define ORC_GLU_SWIGLU_OAI   3 /* out = g' * sigmoid(alpha*g') * (u' + 1)         */
+#define ORC_GLU_SWIGLU_CLAMP 4 /* out = silu(g') * u'                             */
+/* with g' = min(gate, limit), u' = min(max(up, -limit), limit). */
 
 #define ORC_OK          0
 #define ORC_ERR_NULL   -1
@@ -104,6 +110,45 @@ int orc_mmvq_id_glu(const uint8_t *W_gate, const uint8_t *W_up,
                     int64_t M, int64_t K, const uint8_t *y_q,
                     int64_t n_tokens, const int32_t *ids, int top_k,
                     int glu_op, double *out);
+
+/* The GLU of one gate value g and one up value u [MMVQ §融合]; limit and
+ * alpha are used by the clamped variants only. ORC_ERR_TYPE for an unknown
+ * op. */
+int orc_glu(int glu_op, double g, double u, double limit, double alpha,
+            double *out);
+
+/* Fused epilogue [MMVQ §融合], applied in the order the pages list it:
+ * u = up_dot * up_scale + up_bias[r]; with a gate matrix,
+ * g = gate_dot * gate_scale + gate_bias[r] and out = glu(g, u); without
+ * one, out = u. Any pointer may be NULL (scale 1, bias 0). In the
+ * expert-indexed form the scales hold one value per expert and the biases
+ * n_experts*M values, expert-major (expert e's row r at e*M + r). */
+typedef struct {
+    const double *up_bias;
+    const double *gate_bias;
+    const double *up_scale;
+    const double *gate_scale;
+    int glu_op;
+    double limit;
+    double alpha;
+} orc_epilogue;
+
+/* out[j*M + r] for r < M, j < n. W_gate may be NULL (no gate). */
+int orc_mmvq_ex(const uint8_t *W_up, const uint8_t *W_gate, int type,
+                int64_t M, int64_t K, const uint8_t *y_q, int64_t n,
+                const orc_epilogue *epi, double *out);
+
+/* Expert-indexed form of orc_mmvq_ex, out[(t*top_k + k)*M + r]. With
+ * shared_up non-NULL, a shared expert (matrices shared_up / shared_gate,
+ * same shape and type) is applied to every token as well:
+ * shared_out[t*M + r], with the GLU of epi and no scale or bias. */
+int orc_mmvq_id_ex(const uint8_t *W_up, const uint8_t *W_gate,
+                   int64_t expert_stride, int n_experts, int type,
+                   int64_t M, int64_t K, const uint8_t *y_q,
+                   int64_t n_tokens, const int32_t *ids, int top_k,
+                   const orc_epilogue *epi, const uint8_t *shared_up,
+                   const uint8_t *shared_gate, double *shared_out,
+                   double *out);
 
 /* Dequantize one row of K weights to fp64 (w[e] = the weight value of
  * element e), and one column of q8_1 to fp64 (y[e] = d * q[e]). */

@@ -14,7 +14,9 @@ when the oracle disagrees with what the pages or the mathematics fix:
   the pages' row decoders, against the oracle's integer block dots;
 * special cases that reduce to a plain integer dot, and invariants (column
   independence, the GLU composition, identity expert ids, zero padding,
-  linearity in the block scale).
+  linearity in the block scale);
+* the GLU variants at values the mathematics fixes (tabulated normal-CDF
+  values for gelu, the swish identity, clamping) and the epilogue's order.
 
 ``test_oracle_pins.py`` runs them on the oracle as built;
 ``test_oracle_mutations.py`` runs them on copies of the oracle with planted
@@ -603,6 +605,103 @@ def pin_linearity(O, seed: int = 71):
         assert np.allclose(o2, 2 * o1, rtol=1e-15, atol=0)
 
 
+# Standard normal CDF Phi(z), printed-table constants (not computed here).
+NORMAL_CDF = {0.5: 0.6914624612740131, 1.0: 0.8413447460685429, 2.0: 0.9772498680518208,
+              3.0: 0.9986501019683699}
+GEGLU, SWIGLU_OAI, SWIGLU_CLAMP = 2, 3, 4
+
+
+def pin_glu_variants(O):
+    """GLU ops of the fused epilogue [MMVQ §融合] at values fixed by the
+    mathematics: gelu(z) = z*Phi(z) at tabulated normal-CDF values and
+    gelu(-z) = -z*(1 - Phi(z)); the swish identity s(z) - s(-z) = z for silu
+    and for z*sigmoid(alpha*z); clamping at +-limit (the gate from above, the
+    up value on both sides); a very large alpha turns the OAI form into
+    relu(g)*(u + 1); plain is g*u; an unknown op is rejected."""
+    from oracle import OracleError
+    for z, phi in NORMAL_CDF.items():
+        assert abs(O.glu(GEGLU, z, 1.0) - z * phi) <= 1e-14 * z
+        assert abs(O.glu(GEGLU, -z, 1.0) + z * (1.0 - phi)) <= 1e-14 * z
+        assert abs(O.glu(GEGLU, z, -3.0) + 3.0 * z * phi) <= 3e-14 * z
+    assert O.glu(GEGLU, 0.0, 5.0) == 0.0
+    L, a = 7.0, 1.702
+    for g in (0.25, 1.0, 3.5, 6.9):
+        for u in (-9.0, -2.0, 0.5, 3.0, 20.0):
+            uc = min(max(u, -L), L)
+            assert abs(O.glu(1, g, u) - O.glu(1, -g, u) - g * u) <= 1e-13 * (1 + abs(g * u))
+            d = O.glu(SWIGLU_OAI, g, u, L, a) - O.glu(SWIGLU_OAI, -g, u, L, a)
+            assert abs(d - g * (uc + 1.0)) <= 1e-13 * (1 + abs(g * (uc + 1)))
+            assert O.glu(SWIGLU_OAI, g, u, L, a) == O.glu(SWIGLU_OAI, g, uc, L, a)
+            assert O.glu(SWIGLU_CLAMP, g, u, L) == O.glu(SWIGLU_CLAMP, g, uc, L)
+            if -L <= u <= L:
+                assert O.glu(SWIGLU_CLAMP, g, u, L) == O.glu(1, g, u)
+            assert O.glu(0, g, u) == g * u
+    for u in (-3.0, 0.0, 2.0):
+        assert O.glu(SWIGLU_OAI, 50.0, u, L, a) == O.glu(SWIGLU_OAI, L, u, L, a)
+        assert O.glu(SWIGLU_CLAMP, 50.0, u, L) == O.glu(SWIGLU_CLAMP, L, u, L)
+        assert O.glu(SWIGLU_OAI, 0.0, u, L, a) == 0.0
+        assert abs(O.glu(SWIGLU_OAI, 2.0, u, L, 1e4) - 2.0 * (u + 1.0)) <= 1e-12
+        assert abs(O.glu(SWIGLU_OAI, -2.0, u, L, 1e4)) <= 1e-12
+    # the gate is clamped from above only: a very negative gate is not lifted to -limit
+    assert O.glu(SWIGLU_CLAMP, -20.0, 1.0, L) != O.glu(SWIGLU_CLAMP, -L, 1.0, L)
+    try:
+        O.glu(9, 1.0, 1.0)
+    except OracleError as e:
+        assert e.code == -2
+    else:
+        raise AssertionError("unknown glu op accepted")
+
+
+def pin_epilogue(O, seed: int = 81):
+    """The full epilogue in the pages' order [MMVQ §融合]: up result times its
+    scale, plus its bias row; the same for the gate; then the GLU. With no
+    epilogue and no gate it is the plain product; the expert-indexed form
+    uses each slot's expert scale and bias row; the shared expert is the
+    plain GLU product of the shared matrices for every token."""
+    from quantized_decode_gemv_quantize_amd import synth
+    rng = np.random.default_rng(seed)
+    for wtype, K in [(Q4_K, 512), (Q4_0, 128), (Q6_K, 256)]:
+        M = 5
+        Wu, x = _tiny(wtype, M, K, seed + wtype)
+        Wg, _ = _tiny(wtype, M, K, seed + wtype + 1)
+        y = O.quantize_q8_1(x)
+        u, _, _ = O.mmvq(Wu, wtype, M, K, y, 2)
+        g, _, _ = O.mmvq(Wg, wtype, M, K, y, 2)
+        assert np.array_equal(O.mmvq_ex(Wu, None, wtype, M, K, y, 2), u)
+        ub, gb = rng.standard_normal(M), rng.standard_normal(M)
+        out = O.mmvq_ex(Wu, None, wtype, M, K, y, 2, dict(up_bias=ub, up_scale=[0.75]))
+        assert np.allclose(out, u * 0.75 + ub, rtol=1e-15, atol=1e-15)
+        for op in range(5):
+            epi = dict(up_bias=ub, gate_bias=gb, up_scale=[1.25], gate_scale=[-0.5], glu_op=op,
+                       limit=2.0, alpha=1.702)
+            out = O.mmvq_ex(Wu, Wg, wtype, M, K, y, 2, epi)
+            for j in range(2):
+                for r in range(M):
+                    ref = O.glu(op, g[j, r] * -0.5 + gb[r], u[j, r] * 1.25 + ub[r], 2.0, 1.702)
+                    assert abs(out[j, r] - ref) <= 1e-14 * (1 + abs(ref))
+        # expert-indexed form with per-expert scales and bias rows, and a shared expert
+        E, T, top_k = 3, 2, 2
+        Ws = [synth.weights(wtype, M, K, rng) for _ in range(2 * E)]
+        stride = Ws[0].size
+        Wu_all = np.concatenate([w.reshape(-1) for w in Ws[:E]])
+        Wg_all = np.concatenate([w.reshape(-1) for w in Ws[E:]])
+        Su, Sg = synth.weights(wtype, M, K, rng), synth.weights(wtype, M, K, rng)
+        ids = np.array([[2, 0], [1, 2]], dtype=np.int32)
+        sc_u, sc_g = rng.uniform(0.5, 2.0, E), rng.uniform(0.5, 2.0, E)
+        b_u, b_g = rng.standard_normal(E * M), rng.standard_normal(E * M)
+        epi = dict(up_bias=b_u, gate_bias=b_g, up_scale=sc_u, gate_scale=sc_g, glu_op=1)
+        out, sh = O.mmvq_id_ex(Wu_all, Wg_all, stride, E, wtype, M, K, y, T, ids, top_k, epi, Su, Sg)
+        for t in range(T):
+            for k in range(top_k):
+                e = int(ids[t, k])
+                one = dict(up_bias=b_u[e * M:(e + 1) * M], gate_bias=b_g[e * M:(e + 1) * M],
+                           up_scale=[sc_u[e]], gate_scale=[sc_g[e]], glu_op=1)
+                ref = O.mmvq_ex(Ws[e], Ws[E + e], wtype, M, K, y[t:t + 1], 1, one)
+                assert np.array_equal(out[t * top_k + k], ref[0])
+            ref = O.mmvq_ex(Su, Sg, wtype, M, K, y[t:t + 1], 1, dict(glu_op=1))
+            assert np.array_equal(sh[t], ref[0])
+
+
 def pin_error_codes(O):
     """Bad arguments return codes instead of aborting."""
     L = O.L
@@ -620,4 +719,4 @@ ALL_PINS = [pin_type_info, pin_f16_decode, pin_f16_encode, pin_q8_1_e1, pin_q8_1
             pin_q8_1_properties, pin_q4_0_e3, pin_q4_k_e4, pin_q6_k_e5, pin_q4_k_fragment,
             pin_q4_k_bijection, pin_q6_k_fragment, pin_brute_force, pin_int_dot_special,
             pin_columns_independent, pin_glu, pin_id, pin_zero_padding, pin_linearity,
-            pin_error_codes]
+            pin_glu_variants, pin_epilogue, pin_error_codes]

@@ -51,6 +51,20 @@ MUTATIONS = {
     "glu_sigmoid_only": ("return g / (1.0 + exp(-g)) * u;", "return 1.0 / (1.0 + exp(-g)) * u;"),
     "id_slot_as_token": ("rc = orc_mmvq(We, type, M, K, y_q + t * (K / 32) * 36, 1,",
                          "rc = orc_mmvq(We, type, M, K, y_q + k * (K / 32) * 36, 1,"),
+    "gelu_erf_unscaled": ("erf(g / sqrt(2.0))", "erf(g)"),
+    "oai_no_plus_one": ("* (uc + 1.0); break;", "* uc; break;"),
+    "oai_alpha_dropped": ("exp(-alpha * gc)", "exp(-gc)"),
+    "clamp_up_one_sided": ("const double uc = u < -limit ? -limit : (u > limit ? limit : u);",
+                           "const double uc = u > limit ? limit : u;"),
+    "clamp_gate_both_sides": ("const double gc = g < limit ? g : limit;",
+                              "const double gc = g < -limit ? -limit : (g < limit ? g : limit);"),
+    "epilogue_bias_before_scale": ("if (epi->up_scale) u *= epi->up_scale[e];\n    if (epi->up_bias) u += epi->up_bias[(int64_t)e * M + r];",
+                                   "if (epi->up_bias) u += epi->up_bias[(int64_t)e * M + r];\n    if (epi->up_scale) u *= epi->up_scale[e];"),
+    "epilogue_gate_bias_from_up": ("g += epi->gate_bias[", "g += epi->up_bias["),
+    "id_ex_bias_of_expert_0": ("if (epi->up_bias) u += epi->up_bias[(int64_t)e * M + r];",
+                               "if (epi->up_bias) u += epi->up_bias[r];"),
+    "shared_expert_gate_up_swapped": ("rc = orc_glu(epi ? epi->glu_op : ORC_GLU_PLAIN, g, u,",
+                                      "rc = orc_glu(epi ? epi->glu_op : ORC_GLU_PLAIN, u, g,"),
     "columns_share_first": ("row_dot(W + r * nb * bb, type, nb, bb, qk, y_q + j * ycol_bytes, &acc, &mg,",
                             "row_dot(W + r * nb * bb, type, nb, bb, qk, y_q, &acc, &mg,"),
 }
