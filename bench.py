@@ -305,6 +305,83 @@ def time_workload(torch, B, wl, n: int, steps: int, warmup: int):
     return res, data, Ws, y, out
 
 
+def time_moe(torch, B, wl, reps: int = 200):
+    """The expert-indexed fused gate/up workload: quantize + mmvq_id_glu (two
+    launches), mmvq_id_glu alone, and the fused mmvq_id_glu_f32, on two
+    copies of the expert weights used alternately (each copy exceeds the
+    last-level cache). Returns a dict of µs per call and the algorithmic
+    bytes (distinct experts hit x gate and up matrices + activation + out)."""
+    from quantized_decode_gemv_quantize_amd import synth
+    n = wl.n[0]
+    d = synth.make(wl, n)
+    E, M, K, top_k = wl.n_experts, wl.M, wl.K, wl.top_k
+    per = d["W_up"][0].size
+    stride = (per + 15) // 16 * 16
+    def stack(A):
+        buf = np.zeros(E * stride, dtype=np.uint8)
+        for e in range(E):
+            buf[e * stride:e * stride + per] = A[e].reshape(-1)
+        return torch.from_numpy(buf).to("cuda:0")
+    copies = [(stack(d["W_gate"]), stack(d["W_up"]))]
+    copies.append((copies[0][0].clone(), copies[0][1].clone()))
+    x = torch.from_numpy(d["x"]).to("cuda:0")
+    ids = torch.from_numpy(d["ids"]).to("cuda:0")
+    y = torch.empty((n, K // 32 * 36), dtype=torch.uint8, device="cuda:0")
+    out = torch.empty((n * top_k, M), dtype=torch.float32, device="cuda:0")
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+
+    def two():
+        for g, u in copies:
+            B.mmvq_quantize_q8_1(x, K, n, K, y, s)
+            B.mmvq_id_glu(g, u, stride, E, wl.wtype, M, K, y, n, ids, top_k, B.GLU_SWIGLU, out, s)
+
+    def gemv():
+        for g, u in copies:
+            B.mmvq_id_glu(g, u, stride, E, wl.wtype, M, K, y, n, ids, top_k, B.GLU_SWIGLU, out, s)
+
+    def fused():
+        for g, u in copies:
+            B.mmvq_id_glu_f32(g, u, stride, E, wl.wtype, M, K, x, n, K, ids, top_k, B.GLU_SWIGLU, out, s)
+
+    # full epilogue (per-expert scales and bias rows) plus a shared expert,
+    # one launch: 2 more matrices per call, every token
+    rng = np.random.default_rng(0)
+    Sg = torch.from_numpy(synth.weights(wl.wtype, M, K, rng)).to("cuda:0")
+    Su = torch.from_numpy(synth.weights(wl.wtype, M, K, rng)).to("cuda:0")
+    biases = [torch.from_numpy(rng.standard_normal(E * M).astype(np.float32)).to("cuda:0") for _ in range(2)]
+    scales = [torch.ones(E, dtype=torch.float32, device="cuda:0") for _ in range(2)]
+    epi = B.epilogue(up_bias=biases[0], gate_bias=biases[1], up_scale=scales[0], gate_scale=scales[1],
+                     glu_op=B.GLU_SWIGLU)
+    shared_out = torch.empty((n, M), dtype=torch.float32, device="cuda:0")
+
+    def ex_shared():
+        for g, u in copies:
+            B.mmvq_id_ex(u, g, stride, E, wl.wtype, M, K, y, None, 0, n, ids, top_k, epi, Su, Sg, shared_out,
+                         out, s)
+
+    res = {}
+    with torch.cuda.stream(s):
+        for key, fn in (("two_launch_step_us", two), ("id_glu_us", gemv), ("fused_us", fused),
+                        ("ex_shared_us", ex_shared)):
+            g = capture(torch, s, fn)
+            for _ in range(5):
+                g.replay()
+            torch.cuda.synchronize()
+            with Timer(torch, s) as t:
+                for _ in range(reps):
+                    g.replay()
+            res[key] = round(t.ms * 1e3 / (reps * len(copies)), 3)
+    distinct = len(set(int(v) for v in d["ids"].reshape(-1)))
+    alg = distinct * 2 * M * (K // 256) * 144 + n * (K // 32) * 36 + n * top_k * M * 4
+    res.update(workload=wl.name, n=n, distinct_experts=distinct, bytes_per_call=alg,
+               id_glu_gbs=round(alg / (res["id_glu_us"] * 1e-6) / 1e9, 1))
+    res["frac"] = round(res["id_glu_gbs"] / HBM_PEAK_GBS, 4)
+    ex_bytes = alg + 2 * M * (K // 256) * 144 + n * M * 4
+    res["ex_shared_gbs"] = round(ex_bytes / (res["ex_shared_us"] * 1e-6) / 1e9, 1)
+    return res
+
+
 def cpu_baseline(wl, data, n: int, budget_s: float):
     """The oracle on the host: full mat-vecs (quantize + all rows), rows split
     over the host threads, repeated until the wall-clock budget is spent."""
@@ -438,6 +515,8 @@ def main():
                                   "fused_us": round(r["fused_us"], 3),
                                   "gemv_gbs": round(gb, 1), "frac": round(gb / HBM_PEAK_GBS, 4)}),
                       file=sys.stderr, flush=True)
+        print(json.dumps(time_moe(torch, B, synth.BY_NAME["moe_q4_k_8x14336x4096"])), file=sys.stderr,
+              flush=True)
 
 
 if __name__ == "__main__":

@@ -67,11 +67,34 @@ enum {
     MMVQ_Q6_K = 14
 };
 
-/* Epilogue of the fused gate/up variants [MMVQ §融合]. */
+/* GLU of the fused gate/up variants [MMVQ §融合]. The pages name GEGLU,
+ * SWIGLU_OAI and SWIGLU_CLAMP without defining them; the definitions below
+ * are this library's (gelu exact; the OAI form as published with the
+ * gpt-oss models), with g' = min(gate, limit), u' = clamp(up, -limit, limit). */
 enum {
-    MMVQ_GLU_PLAIN = 0,   /* out = gate * up                  */
-    MMVQ_GLU_SWIGLU = 1   /* out = silu(gate) * up, silu(z) = z/(1+e^-z) */
+    MMVQ_GLU_PLAIN = 0,        /* out = gate * up                                  */
+    MMVQ_GLU_SWIGLU = 1,       /* out = silu(gate) * up, silu(z) = z/(1+e^-z)      */
+    MMVQ_GLU_GEGLU = 2,        /* out = gelu(gate) * up, gelu(z) = z/2*(1+erf(z/sqrt 2)) */
+    MMVQ_GLU_SWIGLU_OAI = 3,   /* out = g' * sigmoid(alpha*g') * (u' + 1)          */
+    MMVQ_GLU_SWIGLU_CLAMP = 4  /* out = silu(g') * u'                              */
 };
+
+/* Fused epilogue [MMVQ §融合], applied to each output in the order the
+ * pages give: up = up*up_scale + up_bias[r]; with a gate matrix also
+ * gate = gate*gate_scale + gate_bias[r], then out = GLU(gate, up); without
+ * one, out = up. All pointers are DEVICE pointers (4-byte aligned) or NULL
+ * (scale 1, bias 0). In the expert-indexed calls the scales hold one float
+ * per expert and the biases n_experts*M floats, expert e's row r at
+ * e*M + r. The struct itself is read on the host during the call. */
+typedef struct mmvq_epilogue {
+    const float *up_bias;
+    const float *gate_bias;
+    const float *up_scale;
+    const float *gate_scale;
+    int glu_op;        /* MMVQ_GLU_*, used when a gate matrix is given */
+    float glu_limit;   /* SWIGLU_OAI, SWIGLU_CLAMP                      */
+    float glu_alpha;   /* SWIGLU_OAI (the published value is 1.702)     */
+} mmvq_epilogue;
 
 enum {
     MMVQ_OK = 0,
@@ -112,8 +135,9 @@ int mmvq_quantize_q8_1(const float *x, int64_t K, int64_t n, int64_t ldx,
 int mmvq(const void *W, int type, int64_t M, int64_t K,
          const void *y_q, int64_t n, float *out, void *stream);
 
-/* Fused gate/up: out[j*M + r] = act(g) * u with g the mmvq of W_gate and u
- * the mmvq of W_up (same type and shape), act per glu_op; both weight
+/* Fused gate/up: out[j*M + r] = GLU(g, u) with g the mmvq of W_gate and u
+ * the mmvq of W_up (same type and shape), per glu_op (limit and alpha 0;
+ * mmvq_ex sets them); both weight
  * streams are read in one kernel and the epilogue applies the GLU
  * [MMVQ §融合]. Same requirements as mmvq. */
 int mmvq_glu(const void *W_gate, const void *W_up, int type, int64_t M,
@@ -168,6 +192,32 @@ int mmvq_id_glu_f32(const void *W_gate, const void *W_up,
                     int64_t M, int64_t K, const float *x, int64_t n_tokens,
                     int64_t ldx, const int32_t *ids, int top_k, int glu_op,
                     float *out, void *stream);
+
+/* General form of mmvq / mmvq_glu / mmvq_f32 / mmvq_glu_f32 with the full
+ * epilogue [MMVQ §融合]. W_gate NULL: no gate (out = up after its scale and
+ * bias). Activations: exactly one of y_q (q8_1 columns) and x (fp32 columns
+ * at stride ldx, quantized in the kernel); neither -> MMVQ_ERR_NULL, both ->
+ * MMVQ_ERR_SHAPE. epi NULL: no scale, no bias, and GLU gate*up. Otherwise
+ * the requirements and codes of the forms it generalizes. */
+int mmvq_ex(const void *W_up, const void *W_gate, int type, int64_t M,
+            int64_t K, const void *y_q, const float *x, int64_t ldx,
+            int64_t n, const mmvq_epilogue *epi, float *out, void *stream);
+
+/* General form of the expert-indexed calls [MMVQ §MoE, §融合]: routed
+ * experts as in mmvq_id / mmvq_id_glu with the epilogue of epi (per-expert
+ * scales and bias rows), plus an optional shared expert: with shared_up
+ * non-NULL, shared_up (and shared_gate, required when W_gate is given) are
+ * M x K matrices of the same type applied to every token, out
+ * shared_out[t*M + r] (n_tokens*M floats), with the GLU of epi and no scale
+ * or bias; on the GPU it is one more grid slice of the same launch.
+ * Requires n_experts + 1 <= 65535 with a shared expert. */
+int mmvq_id_ex(const void *W_up, const void *W_gate,
+               int64_t expert_stride_bytes, int n_experts, int type,
+               int64_t M, int64_t K, const void *y_q, const float *x,
+               int64_t ldx, int64_t n_tokens, const int32_t *ids, int top_k,
+               const mmvq_epilogue *epi, const void *shared_up,
+               const void *shared_gate, float *shared_out, float *out,
+               void *stream);
 
 /* TEST SUPPORT: the integer block dots that mmvq forms, through the same
  * device decode routines, written instead of being scaled and summed.

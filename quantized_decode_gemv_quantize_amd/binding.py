@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "libmmvq.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "mmvq.h")
 
 Q4_0, Q8_1, Q4_K, Q6_K = 2, 9, 12, 14
-GLU_PLAIN, GLU_SWIGLU = 0, 1
+GLU_PLAIN, GLU_SWIGLU, GLU_GEGLU, GLU_SWIGLU_OAI, GLU_SWIGLU_CLAMP = 0, 1, 2, 3, 4
 MAX_COLS = 8
 BLOCK = {Q4_0: (32, 18), Q4_K: (256, 144), Q6_K: (256, 210), Q8_1: (32, 36)}
 DOTS_PER_BLOCK = {Q4_0: 1, Q4_K: 16, Q6_K: 16}
@@ -29,6 +29,23 @@ ERR_NULL, ERR_TYPE, ERR_SHAPE, ERR_ALIGN, ERR_LAUNCH = -1, -2, -3, -4, -5
 _i64 = ctypes.c_int64
 _int = ctypes.c_int
 _p = ctypes.c_void_p
+
+class Epilogue(ctypes.Structure):
+    """``mmvq_epilogue``: device pointers (ints, tensors via ``epilogue()``)."""
+    _fields_ = [("up_bias", _p), ("gate_bias", _p), ("up_scale", _p), ("gate_scale", _p),
+                ("glu_op", _int), ("glu_limit", ctypes.c_float), ("glu_alpha", ctypes.c_float)]
+
+
+def epilogue(up_bias=None, gate_bias=None, up_scale=None, gate_scale=None, glu_op: int = 0,
+             glu_limit: float = 0.0, glu_alpha: float = 0.0) -> Epilogue:
+    e = Epilogue()
+    e.up_bias, e.gate_bias = _addr(up_bias), _addr(gate_bias)
+    e.up_scale, e.gate_scale = _addr(up_scale), _addr(gate_scale)
+    e.glu_op, e.glu_limit, e.glu_alpha = glu_op, glu_limit, glu_alpha
+    return e
+
+
+_EP = ctypes.POINTER(Epilogue)
 
 _SIGS = {
     "mmvq_type_info": (_int, [_int, ctypes.POINTER(_int), ctypes.POINTER(_int)]),
@@ -42,6 +59,9 @@ _SIGS = {
     "mmvq_id_f32": (_int, [_p, _i64, _int, _int, _i64, _i64, _p, _i64, _i64, _p, _int, _p, _p]),
     "mmvq_id_glu_f32": (_int, [_p, _p, _i64, _int, _int, _i64, _i64, _p, _i64, _i64, _p, _int, _int,
                                _p, _p]),
+    "mmvq_ex": (_int, [_p, _p, _int, _i64, _i64, _p, _p, _i64, _i64, _EP, _p, _p]),
+    "mmvq_id_ex": (_int, [_p, _p, _i64, _int, _int, _i64, _i64, _p, _p, _i64, _i64, _p, _int, _EP,
+                          _p, _p, _p, _p, _p]),
     "mmvq_block_dots": (_int, [_p, _int, _i64, _i64, _p, _i64, _p, _p]),
     "mmvq_strerror": (ctypes.c_char_p, [_int]),
 }
@@ -166,6 +186,25 @@ def mmvq_id_glu_f32(W_gate, W_up, expert_stride_bytes: int, n_experts: int, wtyp
                                                     expert_stride_bytes, n_experts, wtype, M, K,
                                                     _addr(x), n_tokens, ldx, _addr(ids), top_k,
                                                     glu_op, _addr(out), _stream(stream)))
+
+
+def _ep(epi):
+    return None if epi is None else ctypes.byref(epi)
+
+
+def mmvq_ex(W_up, W_gate, wtype: int, M: int, K: int, y_q, x, ldx: int, n: int,
+            epi: Epilogue | None, out, stream=None) -> None:
+    _check("mmvq_ex", lib().mmvq_ex(_addr(W_up), _addr(W_gate), wtype, M, K, _addr(y_q), _addr(x), ldx,
+                                    n, _ep(epi), _addr(out), _stream(stream)))
+
+
+def mmvq_id_ex(W_up, W_gate, expert_stride_bytes: int, n_experts: int, wtype: int, M: int, K: int,
+               y_q, x, ldx: int, n_tokens: int, ids, top_k: int, epi: Epilogue | None,
+               shared_up, shared_gate, shared_out, out, stream=None) -> None:
+    _check("mmvq_id_ex", lib().mmvq_id_ex(_addr(W_up), _addr(W_gate), expert_stride_bytes, n_experts,
+                                          wtype, M, K, _addr(y_q), _addr(x), ldx, n_tokens, _addr(ids),
+                                          top_k, _ep(epi), _addr(shared_up), _addr(shared_gate),
+                                          _addr(shared_out), _addr(out), _stream(stream)))
 
 
 def mmvq_block_dots(W, wtype: int, M: int, K: int, y_q, n: int, dots, stream=None) -> None:

@@ -55,53 +55,88 @@ int check_gemv(const void* W, int type, int64_t M, int64_t K, const ActIn& in, i
   return MMVQ_OK;
 }
 
-int gemv_common(const void* W, int type, int64_t M, int64_t K, const ActIn& in, int64_t n, float* out,
-                void* stream) {
-  const Dispatch* d;
-  RowArgs a;
-  const int rc = check_gemv(W, type, M, K, in, n, out, &d, &a);
-  if (rc) return rc;
-  return d->rows(a, K, n, static_cast<hipStream_t>(stream));
+bool valid_glu(int op) { return op >= MMVQ_GLU_PLAIN && op <= MMVQ_GLU_SWIGLU_CLAMP; }
+
+// Epilogue fields of RowArgs from a caller's (host) mmvq_epilogue.
+int set_epilogue(const mmvq_epilogue* epi, bool gate, RowArgs* a) {
+  if (!epi) return MMVQ_OK;
+  const float* ptrs[4] = {epi->up_bias, epi->gate_bias, epi->up_scale, epi->gate_scale};
+  for (const float* q : ptrs)
+    if (q && !aligned(q, 4)) return MMVQ_ERR_ALIGN;
+  if (gate && !valid_glu(epi->glu_op)) return MMVQ_ERR_TYPE;
+  a->up_bias = epi->up_bias;
+  a->up_scale = epi->up_scale;
+  a->gate_bias = gate ? epi->gate_bias : nullptr;
+  a->gate_scale = gate ? epi->gate_scale : nullptr;
+  a->glu_op = epi->glu_op;
+  a->glu_limit = epi->glu_limit;
+  a->glu_alpha = epi->glu_alpha;
+  return MMVQ_OK;
 }
 
-int glu_common(const void* W_gate, const void* W_up, int type, int64_t M, int64_t K, const ActIn& in, int64_t n,
-               int glu_op, float* out, void* stream) {
-  if (!W_gate) return MMVQ_ERR_NULL;
+// The activation operand of the _ex calls: exactly one of y_q and x.
+int act_in(const void* y_q, const float* x, int64_t ldx, ActIn* in) {
+  if (!y_q && !x) return MMVQ_ERR_NULL;
+  if (y_q && x) return MMVQ_ERR_SHAPE;
+  *in = ActIn{y_q, x, ldx};
+  return MMVQ_OK;
+}
+
+ActIn q8(const void* y_q) { return ActIn{y_q, nullptr, 0}; }
+ActIn f32(const float* x, int64_t ldx) { return ActIn{nullptr, x, ldx}; }   // x checked non-NULL first
+
+mmvq_epilogue glu_only(int glu_op) {
+  mmvq_epilogue e{};
+  e.glu_op = glu_op;
+  return e;
+}
+
+// Plain or gate/up product with an optional epilogue (W_gate NULL: no gate).
+int rows_common(const void* W_up, const void* W_gate, int type, int64_t M, int64_t K, const ActIn& in, int64_t n,
+                const mmvq_epilogue* epi, float* out, void* stream) {
   const Dispatch* d;
   RowArgs a;
-  const int rc = check_gemv(W_up, type, M, K, in, n, out, &d, &a);
+  int rc = check_gemv(W_up, type, M, K, in, n, out, &d, &a);
   if (rc) return rc;
-  if (glu_op != MMVQ_GLU_PLAIN && glu_op != MMVQ_GLU_SWIGLU) return MMVQ_ERR_TYPE;
-  if (!aligned(W_gate, 16)) return MMVQ_ERR_ALIGN;
+  if (W_gate && !aligned(W_gate, 16)) return MMVQ_ERR_ALIGN;
+  rc = set_epilogue(epi, W_gate != nullptr, &a);
+  if (rc) return rc;
   a.Wg = static_cast<const uint8_t*>(W_gate);
-  a.glu_op = glu_op;
-  return d->rows_glu(a, K, n, static_cast<hipStream_t>(stream));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  return W_gate ? d->rows_glu(a, K, n, st) : d->rows(a, K, n, st);
 }
 
+// Expert-indexed product with an optional epilogue and shared expert.
 int id_common(const void* W_gate, const void* W_up, int64_t expert_stride_bytes, int n_experts, int type,
-              int64_t M, int64_t K, const ActIn& in, int64_t n_tokens, const int32_t* ids, int top_k, int glu_op,
-              bool fused, float* out, void* stream) {
-  if (!ids || (fused && !W_gate)) return MMVQ_ERR_NULL;
+              int64_t M, int64_t K, const ActIn& in, int64_t n_tokens, const int32_t* ids, int top_k,
+              const mmvq_epilogue* epi, const void* shared_up, const void* shared_gate, float* shared_out,
+              float* out, void* stream) {
+  if (!ids) return MMVQ_ERR_NULL;
+  if (shared_up && (!shared_out || (W_gate && !shared_gate))) return MMVQ_ERR_NULL;
   const Dispatch* d;
   RowArgs a;
-  const int rc = check_gemv(W_up, type, M, K, in, n_tokens, out, &d, &a);
+  int rc = check_gemv(W_up, type, M, K, in, n_tokens, out, &d, &a);
   if (rc) return rc;
-  if (fused && glu_op != MMVQ_GLU_PLAIN && glu_op != MMVQ_GLU_SWIGLU) return MMVQ_ERR_TYPE;
-  if (n_experts < 1 || n_experts > 65535 || top_k < 1 || top_k > n_experts || top_k > 64) return MMVQ_ERR_SHAPE;
+  const int slices = n_experts + (shared_up ? 1 : 0);
+  if (n_experts < 1 || slices > 65535 || top_k < 1 || top_k > n_experts || top_k > 64) return MMVQ_ERR_SHAPE;
   if (expert_stride_bytes < M * a.row_bytes) return MMVQ_ERR_SHAPE;
-  if (expert_stride_bytes % 16 != 0 || !aligned(ids, 4) || (fused && !aligned(W_gate, 16))) return MMVQ_ERR_ALIGN;
+  if (expert_stride_bytes % 16 != 0 || !aligned(ids, 4) || (W_gate && !aligned(W_gate, 16))) return MMVQ_ERR_ALIGN;
+  if (shared_up && (!aligned(shared_up, 16) || (W_gate && !aligned(shared_gate, 16)) || !aligned(shared_out, 4)))
+    return MMVQ_ERR_ALIGN;
+  rc = set_epilogue(epi, W_gate != nullptr, &a);
+  if (rc) return rc;
   a.Wg = static_cast<const uint8_t*>(W_gate);
   a.ids = ids;
   a.expert_stride = expert_stride_bytes;
   a.n_tokens = static_cast<int>(n_tokens);
   a.top_k = top_k;
-  a.glu_op = glu_op;
+  a.n_experts = n_experts;
+  a.Ws_up = static_cast<const uint8_t*>(shared_up);
+  a.Ws_gate = W_gate ? static_cast<const uint8_t*>(shared_gate) : nullptr;
+  a.shared_out = shared_up ? shared_out : nullptr;
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  return fused ? d->id_glu(a, K, n_experts, st) : d->id(a, K, n_experts, st);
+  return W_gate ? d->id_glu(a, K, n_experts, st) : d->id(a, K, n_experts, st);
 }
-
-ActIn q8(const void* y_q) { return ActIn{y_q, nullptr, 0}; }
-ActIn f32(const float* x, int64_t ldx) { return ActIn{nullptr, x, ldx}; }   // x checked non-NULL first
 
 }  // namespace
 
@@ -130,53 +165,78 @@ int mmvq_quantize_q8_1(const float* x, int64_t K, int64_t n, int64_t ldx, void* 
 }
 
 int mmvq(const void* W, int type, int64_t M, int64_t K, const void* y_q, int64_t n, float* out, void* stream) {
-  return gemv_common(W, type, M, K, q8(y_q), n, out, stream);
+  return rows_common(W, nullptr, type, M, K, q8(y_q), n, nullptr, out, stream);
 }
 
 int mmvq_glu(const void* W_gate, const void* W_up, int type, int64_t M, int64_t K, const void* y_q, int64_t n,
              int glu_op, float* out, void* stream) {
-  return glu_common(W_gate, W_up, type, M, K, q8(y_q), n, glu_op, out, stream);
+  if (!W_gate) return MMVQ_ERR_NULL;
+  const mmvq_epilogue e = glu_only(glu_op);
+  return rows_common(W_up, W_gate, type, M, K, q8(y_q), n, &e, out, stream);
 }
 
 int mmvq_id(const void* W, int64_t expert_stride_bytes, int n_experts, int type, int64_t M, int64_t K,
             const void* y_q, int64_t n_tokens, const int32_t* ids, int top_k, float* out, void* stream) {
-  return id_common(nullptr, W, expert_stride_bytes, n_experts, type, M, K, q8(y_q), n_tokens, ids, top_k, 0,
-                   false, out, stream);
+  return id_common(nullptr, W, expert_stride_bytes, n_experts, type, M, K, q8(y_q), n_tokens, ids, top_k, nullptr,
+                   nullptr, nullptr, nullptr, out, stream);
 }
 
 int mmvq_id_glu(const void* W_gate, const void* W_up, int64_t expert_stride_bytes, int n_experts, int type,
                 int64_t M, int64_t K, const void* y_q, int64_t n_tokens, const int32_t* ids, int top_k,
                 int glu_op, float* out, void* stream) {
-  return id_common(W_gate, W_up, expert_stride_bytes, n_experts, type, M, K, q8(y_q), n_tokens, ids, top_k,
-                   glu_op, true, out, stream);
+  if (!W_gate) return MMVQ_ERR_NULL;
+  const mmvq_epilogue e = glu_only(glu_op);
+  return id_common(W_gate, W_up, expert_stride_bytes, n_experts, type, M, K, q8(y_q), n_tokens, ids, top_k, &e,
+                   nullptr, nullptr, nullptr, out, stream);
 }
 
 int mmvq_f32(const void* W, int type, int64_t M, int64_t K, const float* x, int64_t n, int64_t ldx, float* out,
              void* stream) {
   if (!x) return MMVQ_ERR_NULL;
-  return gemv_common(W, type, M, K, f32(x, ldx), n, out, stream);
+  return rows_common(W, nullptr, type, M, K, f32(x, ldx), n, nullptr, out, stream);
 }
 
 int mmvq_glu_f32(const void* W_gate, const void* W_up, int type, int64_t M, int64_t K, const float* x, int64_t n,
                  int64_t ldx, int glu_op, float* out, void* stream) {
-  if (!x) return MMVQ_ERR_NULL;
-  return glu_common(W_gate, W_up, type, M, K, f32(x, ldx), n, glu_op, out, stream);
+  if (!x || !W_gate) return MMVQ_ERR_NULL;
+  const mmvq_epilogue e = glu_only(glu_op);
+  return rows_common(W_up, W_gate, type, M, K, f32(x, ldx), n, &e, out, stream);
 }
 
 int mmvq_id_f32(const void* W, int64_t expert_stride_bytes, int n_experts, int type, int64_t M, int64_t K,
                 const float* x, int64_t n_tokens, int64_t ldx, const int32_t* ids, int top_k, float* out,
                 void* stream) {
   if (!x) return MMVQ_ERR_NULL;
-  return id_common(nullptr, W, expert_stride_bytes, n_experts, type, M, K, f32(x, ldx), n_tokens, ids, top_k, 0,
-                   false, out, stream);
+  return id_common(nullptr, W, expert_stride_bytes, n_experts, type, M, K, f32(x, ldx), n_tokens, ids, top_k,
+                   nullptr, nullptr, nullptr, nullptr, out, stream);
 }
 
 int mmvq_id_glu_f32(const void* W_gate, const void* W_up, int64_t expert_stride_bytes, int n_experts, int type,
                     int64_t M, int64_t K, const float* x, int64_t n_tokens, int64_t ldx, const int32_t* ids,
                     int top_k, int glu_op, float* out, void* stream) {
-  if (!x) return MMVQ_ERR_NULL;
+  if (!x || !W_gate) return MMVQ_ERR_NULL;
+  const mmvq_epilogue e = glu_only(glu_op);
   return id_common(W_gate, W_up, expert_stride_bytes, n_experts, type, M, K, f32(x, ldx), n_tokens, ids, top_k,
-                   glu_op, true, out, stream);
+                   &e, nullptr, nullptr, nullptr, out, stream);
+}
+
+int mmvq_ex(const void* W_up, const void* W_gate, int type, int64_t M, int64_t K, const void* y_q, const float* x,
+            int64_t ldx, int64_t n, const mmvq_epilogue* epi, float* out, void* stream) {
+  ActIn in;
+  const int rc = act_in(y_q, x, ldx, &in);
+  if (rc) return rc;
+  return rows_common(W_up, W_gate, type, M, K, in, n, epi, out, stream);
+}
+
+int mmvq_id_ex(const void* W_up, const void* W_gate, int64_t expert_stride_bytes, int n_experts, int type,
+               int64_t M, int64_t K, const void* y_q, const float* x, int64_t ldx, int64_t n_tokens,
+               const int32_t* ids, int top_k, const mmvq_epilogue* epi, const void* shared_up,
+               const void* shared_gate, float* shared_out, float* out, void* stream) {
+  ActIn in;
+  const int rc = act_in(y_q, x, ldx, &in);
+  if (rc) return rc;
+  return id_common(W_gate, W_up, expert_stride_bytes, n_experts, type, M, K, in, n_tokens, ids, top_k, epi,
+                   shared_up, shared_gate, shared_out, out, stream);
 }
 
 int mmvq_block_dots(const void* W, int type, int64_t M, int64_t K, const void* y_q, int64_t n, int32_t* dots,

@@ -71,6 +71,7 @@ inline int launch_rows_nc(RowArgs a, int64_t K, hipStream_t st) {
   const Shape s = make_shape<F>(a.M, K, RMAX);
   a.units = s.units;
   a.team_lanes = s.team_lanes;
+  a.teams_per_block = s.teams_per_block;
   switch (s.rows) {
     case 1: return launch_rows_p<F, XF, NC, G, 1>(a, s, st);
     case 2: if constexpr (RMAX >= 2) return launch_rows_p<F, XF, NC, G, 2>(a, s, st); break;
@@ -97,29 +98,33 @@ inline int launch_rows(const RowArgs& a, int64_t K, int64_t n, hipStream_t st) {
   }
 }
 
-template <class F, bool XF, int G, int R, int P>
+template <class F, bool XF, int G, int RB, int P>
 inline int launch_id_r(const RowArgs& a, const Shape& s, int n_experts, hipStream_t st) {
-  hipLaunchKernelGGL((mmvq_id_kernel<F, R, P, G, XF>),
-                     dim3(static_cast<unsigned>(s.blocks), static_cast<unsigned>(n_experts)),
+  const unsigned slices = static_cast<unsigned>(n_experts) + (a.Ws_up ? 1u : 0u);   // + shared expert
+  hipLaunchKernelGGL((mmvq_id_kernel<F, RB, P, G, XF>), dim3(static_cast<unsigned>(s.blocks), slices),
                      dim3(s.teams_per_block * s.team_lanes), 0, st, a);
   return check_launch();
 }
 
+// Expert blocks own RB rows per slot (RB = the register budget at one token);
+// matrices with fewer rows fall back to one row per slot.
 template <class F, bool XF, int G>
 inline int launch_id(RowArgs a, int64_t K, int n_experts, hipStream_t st) {
-  constexpr int R = id_rows_per_pass<F>(G);
-  Shape s = make_shape<F>(a.M, K, R);
+  constexpr int RB = rows_per_pass<F>(1, G);
+  Shape s = make_shape<F>(a.M, K, RB);
   a.units = s.units;
   a.team_lanes = s.team_lanes;
-  if (s.rows != R) {            // fewer rows than the instantiation holds: one per slot
-    s.rows = 1;
-    s.teams = (a.M + s.slots - 1) / s.slots;
-    s.blocks = (s.teams + s.teams_per_block - 1) / s.teams_per_block;
-    return s.slots == 2 ? launch_id_r<F, XF, G, 1, 2>(a, s, n_experts, st)
-                        : launch_id_r<F, XF, G, 1, 1>(a, s, n_experts, st);
-  }
-  return s.slots == 2 ? launch_id_r<F, XF, G, R, 2>(a, s, n_experts, st)
-                      : launch_id_r<F, XF, G, R, 1>(a, s, n_experts, st);
+  a.teams_per_block = s.teams_per_block;
+  const bool full = static_cast<int64_t>(RB) * s.slots <= a.M;
+  const int rb = full ? RB : 1;
+  s.rows = rb;
+  s.teams = (a.M + static_cast<int64_t>(rb) * s.slots - 1) / (static_cast<int64_t>(rb) * s.slots);
+  s.blocks = (s.teams + s.teams_per_block - 1) / s.teams_per_block;
+  if (full)
+    return s.slots == 2 ? launch_id_r<F, XF, G, RB, 2>(a, s, n_experts, st)
+                        : launch_id_r<F, XF, G, RB, 1>(a, s, n_experts, st);
+  return s.slots == 2 ? launch_id_r<F, XF, G, 1, 2>(a, s, n_experts, st)
+                      : launch_id_r<F, XF, G, 1, 1>(a, s, n_experts, st);
 }
 
 template <class F>

@@ -23,7 +23,8 @@
 //     read in the same pass and the GLU is applied in the epilogue.
 //   * Expert-indexed mode: blockIdx.y is the expert; the block gathers the
 //     tokens routed to it (at most 8) and reads that expert's rows once for
-//     all of them [MMVQ §MoE].
+//     all of them [MMVQ §MoE]. A team owns RB rows and takes them in passes
+//     of as many rows as the registers hold for the block's token count.
 //   * XF = true takes fp32 activations and quantizes the lane's slice to
 //     q8_1 in registers (formats.hpp load_x / quant_x), with the arithmetic
 //     of the stand-alone quantizer: the same codes and scales, so the result
@@ -56,14 +57,43 @@ struct RowArgs {
   int64_t expert_stride;
   int units;                 // units per row
   int team_lanes;            // TL: multiple of 64
-  int glu_op;                // 0 plain product, 1 silu(gate) * up
+  int teams_per_block;       // the workgroup is teams_per_block * TL lanes
+  int glu_op;                // GLU of the gate forms (see glu())
   int n_tokens;              // id mode
   int top_k;                 // id mode
+  // epilogue [MMVQ §融合]: up = up*up_scale[e] + up_bias[e*M + r], the same
+  // for the gate, then the GLU; NULL pointers are skipped (e = expert in id
+  // mode, else 0)
+  const float* up_bias;
+  const float* gate_bias;
+  const float* up_scale;
+  const float* gate_scale;
+  float glu_limit;
+  float glu_alpha;
+  // id mode: shared expert in the extra grid slice blockIdx.y == n_experts
+  int n_experts;
+  const uint8_t* Ws_up;
+  const uint8_t* Ws_gate;
+  float* shared_out;
 };
 
-__device__ __forceinline__ float glu(int op, float gate, float up) {
-  if (op == 1) return gate / (1.0f + __expf(-gate)) * up;
-  return gate * up;
+// GLU ops of the fused epilogue [MMVQ §融合]: 0 gate*up, 1 silu(gate)*up,
+// 2 gelu(gate)*up (exact erf form), 3 g'*sigmoid(alpha*g')*(u'+1),
+// 4 silu(g')*u', with g' = min(gate, limit), u' = clamp(up, -limit, limit).
+__device__ __forceinline__ float glu(int op, float gate, float up, float limit, float alpha) {
+  switch (op) {
+    case 1: return gate / (1.0f + __expf(-gate)) * up;
+    case 2: return 0.5f * gate * (1.0f + erff(gate * 0.70710678118654752f)) * up;
+    case 3: {
+      const float g = fminf(gate, limit), u = fminf(fmaxf(up, -limit), limit);
+      return g / (1.0f + __expf(-alpha * g)) * (u + 1.0f);
+    }
+    case 4: {
+      const float g = fminf(gate, limit), u = fminf(fmaxf(up, -limit), limit);
+      return g / (1.0f + __expf(-g)) * u;
+    }
+    default: return gate * up;
+  }
 }
 
 // Column descriptor: which q8_1 column feeds activation slot j, and where
@@ -86,23 +116,35 @@ struct RedLds {
 // pair fills 7 waves exactly. Lane values are indexed
 // (column j, row i*P + slot); a lane holds zeros for the other slots, and
 // the team reduction sums each value over the lanes of its own slot.
-template <class F, int NC, int R, int P, int G, bool ID, bool XF, int VMAX>
+// PASSES: the team owns PASSES * R * P consecutive rows and takes them R * P
+// at a time, loading its activation slice once (the expert-indexed kernel
+// uses this to keep R*P rows of loads in flight whatever the column count).
+template <class F, int NC, int R, int P, int G, bool ID, bool XF, int VMAX, int PASSES = 1>
 __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
                                           const uint8_t* Wbase, const uint8_t* Wgbase,
                                           RedLds<G, VMAX>& red) {
-  constexpr int RP = R * P;                 // rows per team
+  constexpr int RP = R * P;                 // rows per pass
   constexpr int V = pow2ceil(NC * RP);
   static_assert(V <= VMAX, "LDS sized for fewer values");
+  // Every scalar argument the weight loads and the epilogue need, read in
+  // the kernel's first batch of argument loads: left to the compiler, some
+  // were loaded after the activation loads (one more scalar round trip before
+  // the weight stream) or at the store (one at the end of every wave).
+  // (Input-only operands: the pointers keep their global address space.)
+  const uint8_t* Wb = Wbase;
+  const uint8_t* Wgb = Wgbase;
+  const float *up_scale = a.up_scale, *up_bias = a.up_bias, *gate_scale = a.gate_scale, *gate_bias = a.gate_bias;
+  asm volatile("" ::"s"(Wb), "s"(Wgb), "s"(up_scale), "s"(up_bias), "s"(gate_scale), "s"(gate_bias));
   const int tid = threadIdx.x;
   const int TL = a.team_lanes;
   // team index and row window are wave-uniform (teams are whole waves):
   // keep them scalar so row addresses are SGPR base + per-lane offset
   const int team_local = __builtin_amdgcn_readfirstlane(tid / TL);
   const int lt = tid - team_local * TL;
-  const int teams_per_block = blockDim.x / TL;
+  const int teams_per_block = a.teams_per_block;
   const int64_t team = static_cast<int64_t>(blockIdx.x) * teams_per_block + team_local;
-  const Window win = team_window(team, lt, R, P, a.units, a.M);
-  const int64_t row0 = win.row0, skip = win.skip;
+  const Window win = team_window(team, lt, R * PASSES, P, a.units, a.M);
+  int64_t row0 = win.row0, skip = win.skip;   // of the current pass
   const int slot = win.slot;
   const bool active = win.active;
   const int u = win.unit;
@@ -133,14 +175,14 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- issue all weight loads of this team's rows -----------------------
+  // ---- issue all weight loads of this pass's rows -----------------------
   typename F::Wt w[R];
   typename F::Wt wg[G == 2 ? R : 1];
-  {
-    // uniform row pointers; the slot's row is a per-lane 32-bit offset
-    const uint32_t slot_off = static_cast<uint32_t>(slot * a.row_bytes);
-    const uint8_t* rp = Wbase + row0 * a.row_bytes;
-    const uint8_t* gp = (G == 2) ? Wgbase + row0 * a.row_bytes : nullptr;
+  // uniform row pointers; the slot's row is a per-lane 32-bit offset
+  const uint32_t slot_off = static_cast<uint32_t>(slot * a.row_bytes);
+  auto issue = [&]() {
+    const uint8_t* rp = Wb + row0 * a.row_bytes;
+    const uint8_t* gp = (G == 2) ? Wgb + row0 * a.row_bytes : nullptr;
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       F::load_wt(w[i], rp, slot_off, L);
@@ -153,7 +195,8 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
       // rows 0..i (the vector memory counter retires loads in issue order)
       __builtin_amdgcn_sched_barrier(0);
     }
-  }
+  };
+  issue();
   // the activation loads were issued before the weight loads, so they
   // retire first: this waits for them only
   if constexpr (XE) {
@@ -170,6 +213,12 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
     }
   }
 
+  for (int pass = 0; pass < PASSES; ++pass) {
+  if (pass > 0) {
+    row0 += RP;
+    skip -= RP;
+    issue();
+  }
   // ---- per row: decode once, one partial per column ----------------------
   float part[G][V];
 #pragma unroll
@@ -205,7 +254,14 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
     const int j = idx / RP, i = idx - j * RP;
     if (j >= NC || i < skip) return;
     const int64_t r = row0 + i;
-    const float v = (G == 2) ? glu(a.glu_op, gate, up) : up;
+    const int64_t e = ID ? static_cast<int64_t>(blockIdx.y) : 0;
+    if (up_scale) up *= up_scale[e];
+    if (up_bias) up += up_bias[e * a.M + r];
+    if constexpr (G == 2) {
+      if (gate_scale) gate *= gate_scale[e];
+      if (gate_bias) gate += gate_bias[e * a.M + r];
+    }
+    const float v = (G == 2) ? glu(a.glu_op, gate, up, a.glu_limit, a.glu_alpha) : up;
     if constexpr (ID) {
       // select column j's token and slots with compile-time indices
       uint64_t m = 0;
@@ -233,6 +289,9 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
     }
   } else {
     const int wave = tid / kWave;
+    // the previous pass's readers must be done with the LDS (uniform: every
+    // team of the block runs the same passes)
+    if (PASSES > 1 && pass > 0) __syncthreads();
     if (RM::representative(lane)) {
 #pragma unroll
       for (int pos = 0; pos < RM::kPerLane; ++pos) {
@@ -254,6 +313,7 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
       store(idx, s[0], s[G - 1]);
     }
   }
+  }   // passes
 }
 
 // Plain / fused kernel: columns 0..NC-1 of y.
@@ -269,19 +329,54 @@ __global__ void __launch_bounds__(kLaunchBound) mmvq_rows_kernel(RowArgs a) {
 }
 
 // Expert-indexed kernel: blockIdx.y = expert. The token list is the same for
-// every thread of the block (ids are read with uniform addresses).
-template <class F, int R, int P, int G, bool XF>
+// every thread of the block (ids are read with uniform addresses). The slice
+// blockIdx.y == n_experts, when launched, is the shared expert: every token,
+// its own matrices and output, the GLU without scales or biases.
+// Rows per pass of an expert block with NC tokens: what the register budget
+// allows for NC columns, at most RB; the team owns RB * P rows and takes them
+// in RB / id_rows passes.
+template <class F, int NC, int RB, int G>
+constexpr int id_rows() {
+  return rows_per_pass<F>(NC, G) < RB ? rows_per_pass<F>(NC, G) : RB;
+}
+
+template <class F, int RB, int P, int G>
+constexpr int id_lds_values() {
+  int v = 1;
+  for (int nc = 1; nc <= kMaxCols; ++nc) {
+    const int r = rows_per_pass<F>(nc, G) < RB ? rows_per_pass<F>(nc, G) : RB;
+    const int w = pow2ceil(nc * r * P);
+    if (w > v) v = w;
+  }
+  return v;
+}
+
+template <class F, int RB, int P, int G, bool XF>
 __global__ void __launch_bounds__(kLaunchBound) mmvq_id_kernel(RowArgs a) {
   const int e = blockIdx.y;
+  const bool shared = e == a.n_experts;
+  if (shared) {
+    a.W = a.Ws_up;
+    a.Wg = a.Ws_gate;
+    a.out = a.shared_out;
+    a.top_k = 1;
+    a.expert_stride = 0;
+    a.up_bias = a.gate_bias = a.up_scale = a.gate_scale = nullptr;
+  }
   // Tokens routed to expert e, compacted with compile-time indices only (a
   // runtime index into a register array would go through scratch memory).
   uint64_t m[kMaxCols];
 #pragma unroll
   for (int t = 0; t < kMaxCols; ++t) {
     m[t] = 0;
-    if (t < a.n_tokens)
-      for (int k = 0; k < a.top_k; ++k)
-        if (a.ids[t * a.top_k + k] == e) m[t] |= 1ull << k;
+    if (t < a.n_tokens) {
+      if (shared) {
+        m[t] = 1;
+      } else {
+        for (int k = 0; k < a.top_k; ++k)
+          if (a.ids[t * a.top_k + k] == e) m[t] |= 1ull << k;
+      }
+    }
   }
   Cols cols;
   cols.n = 0;
@@ -297,19 +392,24 @@ __global__ void __launch_bounds__(kLaunchBound) mmvq_id_kernel(RowArgs a) {
     }
   }
   if (cols.n == 0) return;     // uniform: the whole block leaves together
-  const uint8_t* We = a.W + static_cast<int64_t>(e) * a.expert_stride;
-  const uint8_t* Wge = G == 2 ? a.Wg + static_cast<int64_t>(e) * a.expert_stride : nullptr;
-  constexpr int VMAX = pow2ceil(kMaxCols * R * P);
+  const int64_t eo = shared ? 0 : static_cast<int64_t>(e) * a.expert_stride;
+  const uint8_t* We = a.W + eo;
+  const uint8_t* Wge = G == 2 ? a.Wg + eo : nullptr;
+  constexpr int VMAX = id_lds_values<F, RB, P, G>();
   __shared__ RedLds<G, VMAX> red;
   switch (cols.n) {
-    case 1: rows_body<F, 1, R, P, G, true, XF, VMAX>(a, cols, We, Wge, red); break;
-    case 2: rows_body<F, 2, R, P, G, true, XF, VMAX>(a, cols, We, Wge, red); break;
-    case 3: rows_body<F, 3, R, P, G, true, XF, VMAX>(a, cols, We, Wge, red); break;
-    case 4: rows_body<F, 4, R, P, G, true, XF, VMAX>(a, cols, We, Wge, red); break;
-    case 5: rows_body<F, 5, R, P, G, true, XF, VMAX>(a, cols, We, Wge, red); break;
-    case 6: rows_body<F, 6, R, P, G, true, XF, VMAX>(a, cols, We, Wge, red); break;
-    case 7: rows_body<F, 7, R, P, G, true, XF, VMAX>(a, cols, We, Wge, red); break;
-    default: rows_body<F, 8, R, P, G, true, XF, VMAX>(a, cols, We, Wge, red); break;
+#define QMV_ID_CASE(NC)                                                                          \
+  rows_body<F, NC, id_rows<F, NC, RB, G>(), P, G, true, XF, VMAX, RB / id_rows<F, NC, RB, G>()>( \
+      a, cols, We, Wge, red)
+    case 1: QMV_ID_CASE(1); break;
+    case 2: QMV_ID_CASE(2); break;
+    case 3: QMV_ID_CASE(3); break;
+    case 4: QMV_ID_CASE(4); break;
+    case 5: QMV_ID_CASE(5); break;
+    case 6: QMV_ID_CASE(6); break;
+    case 7: QMV_ID_CASE(7); break;
+    default: QMV_ID_CASE(8); break;
+#undef QMV_ID_CASE
   }
 }
 
@@ -320,7 +420,7 @@ __global__ void __launch_bounds__(256) mmvq_block_dots_kernel(const uint8_t* W, 
                                                               int32_t* dots, int64_t M, int64_t nblocks,
                                                               int64_t row_bytes, int64_t ycol_bytes,
                                                               int64_t n) {
-  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;   // 256-lane blocks
   if (gid >= n * M * nblocks) return;
   const int64_t b = gid % nblocks;
   const int64_t r = (gid / nblocks) % M;

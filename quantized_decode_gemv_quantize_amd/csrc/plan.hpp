@@ -65,11 +65,6 @@ constexpr int rows_per_pass(int nc, int g) {
   return g == 2 ? (r > 1 ? r / 2 : 1) : r;
 }
 
-template <class F>
-constexpr int id_rows_per_pass(int g) {
-  return F::kType == 14 ? 1 : (F::kType == 12 ? (g == 2 ? 1 : 2) : (g == 2 ? 2 : 4));
-}
-
 // Row window of one team and the unit / slot of one of its lanes.
 // The team owns rows [first, first + RP); the last team's window is moved
 // back to end at row M-1 (M >= RP), and rows of the window below `first`

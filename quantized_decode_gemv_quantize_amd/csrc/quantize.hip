@@ -17,7 +17,7 @@ namespace qmv {
 __global__ void __launch_bounds__(256) quantize_q8_1_kernel(const float* __restrict__ x,
                                                             uint8_t* __restrict__ y, int64_t nb,
                                                             int64_t n, int64_t ldx) {
-  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;   // 256-lane blocks
   const int64_t blk = gid >> 3;          // global q8_1 block (column-major over n)
   const int sub = static_cast<int>(gid & 7);
   const bool valid = blk < n * nb;

@@ -144,3 +144,49 @@ def special_x(K: int, n: int, seed: int, ldx: int | None = None) -> np.ndarray:
                 t[0] = amax
                 blk[:] = t
     return x
+
+
+def epilogue_tolerance(g, u, mg, mu, epi: dict, e_idx=None):
+    """Bound on |gpu - oracle| for the full epilogue out = GLU(g*sg + bg,
+    u*su + bu) (or u*su + bu without a gate: g None), from the per-dot bounds
+    of the raw up and gate products (REL*mag + ABS), the fp32 rounding of the
+    scale and bias steps, and the derivatives of each GLU: |d/dg| and |d/du|
+    bounded by 1.1*|u'| and |silu| (SWIGLU), 1.13*|u'| and |gelu| (GEGLU,
+    |gelu'| <= 1.13), (1 + alpha*|g'|/4)*|u'+1| and |g' sigmoid(alpha g')|
+    (OAI), as SWIGLU on the clamped values (CLAMP); the device exp/erf add
+    1e-6*(|out| + |g*u|). e_idx: per-row expert index for the scales and
+    bias rows (id form), else expert 0."""
+    M = u.shape[-1]
+    rows = np.arange(M)
+    e = np.zeros(u.shape, dtype=np.int64) if e_idx is None else e_idx
+
+    def apply(v, mag, scale, bias):
+        tol = REL * mag + ABS
+        sc = np.ones_like(v) if scale is None else np.asarray(scale, dtype=np.float64)[e]
+        b = np.zeros_like(v) if bias is None else np.asarray(bias, dtype=np.float64).reshape(-1)[e * M + rows]
+        w = v * sc + b
+        return w, np.abs(sc) * tol + 2.0 ** -23 * (np.abs(v * sc) + np.abs(b)) * 2
+
+    uu, tu = apply(u, mu, epi.get("up_scale"), epi.get("up_bias"))
+    if g is None:
+        return uu, tu
+    gg, tg = apply(g, mg, epi.get("gate_scale"), epi.get("gate_bias"))
+    op, L, a = epi.get("glu_op", 0), epi.get("limit", 0.0), epi.get("alpha", 0.0)
+    gc = np.minimum(gg, L)
+    uc = np.clip(uu, -L, L)
+    silu = lambda z: z / (1.0 + np.exp(-z))  # noqa: E731
+    if op == 0:
+        out, dg, du = gg * uu, np.abs(uu), np.abs(gg)
+    elif op == 1:
+        out, dg, du = silu(gg) * uu, 1.1 * np.abs(uu), np.abs(silu(gg))
+    elif op == 2:
+        from math import erf, sqrt
+        gel = np.array([0.5 * z * (1.0 + erf(z / sqrt(2.0))) for z in gg.reshape(-1)]).reshape(gg.shape)
+        out, dg, du = gel * uu, 1.13 * np.abs(uu), np.abs(gel)
+    elif op == 3:
+        h = gc / (1.0 + np.exp(-a * gc))
+        out, dg, du = h * (uc + 1.0), (1.0 + a * np.abs(gc) / 4.0) * np.abs(uc + 1.0), np.abs(h)
+    else:
+        out, dg, du = silu(gc) * uc, 1.1 * np.abs(uc), np.abs(silu(gc))
+    tol = dg * tg + du * tu + 1e-6 * (np.abs(out) + np.abs(gg * uu)) + ABS
+    return out, tol

@@ -46,10 +46,11 @@ static void report(const char* what, bool ok_extra, const char* name, int64_t M,
 
 // One launch of the rows kernel (plain G=1 or fused G=2), or of the id
 // kernel for one expert (base = expert's matrix, tok = its token columns).
+// passes: the team owns passes * R * P rows, taken R * P at a time.
 template <class F>
 static bool model_rows(const Shape& s, int R, int P, int G, int64_t M, const uint8_t* W, const uint8_t* Wg,
                        int64_t row_bytes, const uint8_t* y, int64_t ycol_bytes, const float* x, int64_t ldx,
-                       const int* tok, int nc, std::vector<int>& stores) {
+                       const int* tok, int nc, std::vector<int>& stores, int passes = 1) {
   typename F::Wt wt;
   typename F::Act act;
   typename F::Dec dec;
@@ -57,18 +58,21 @@ static bool model_rows(const Shape& s, int R, int P, int G, int64_t M, const uin
     for (int tl = 0; tl < s.teams_per_block; ++tl) {
       const int64_t team = b * s.teams_per_block + tl;
       for (int lt = 0; lt < s.team_lanes; ++lt) {
-        const Window w = team_window(team, lt, R, P, s.units, M);
+        const Window w = team_window(team, lt, R * passes, P, s.units, M);
         const typename F::Lane L = F::lane(w.unit);
         const uint32_t slot_off = static_cast<uint32_t>(w.slot * row_bytes);
-        const uint8_t* rp = W + w.row0 * row_bytes;
-        const uint8_t* gp = Wg ? Wg + w.row0 * row_bytes : nullptr;
-        for (int i = 0; i < R; ++i) {
-          F::load_wt(wt, rp, slot_off, L);
-          F::decode(wt, dec, L);
-          rp += P * row_bytes;
-          if (G == 2) {
-            F::load_wt(wt, gp, slot_off, L);
-            gp += P * row_bytes;
+        for (int pass = 0; pass < passes; ++pass) {
+          const int64_t row0 = w.row0 + static_cast<int64_t>(pass) * R * P;
+          const uint8_t* rp = W + row0 * row_bytes;
+          const uint8_t* gp = Wg ? Wg + row0 * row_bytes : nullptr;
+          for (int i = 0; i < R; ++i) {
+            F::load_wt(wt, rp, slot_off, L);
+            F::decode(wt, dec, L);
+            rp += P * row_bytes;
+            if (G == 2) {
+              F::load_wt(wt, gp, slot_off, L);
+              gp += P * row_bytes;
+            }
           }
         }
         for (int j = 0; j < nc; ++j) {
@@ -80,10 +84,15 @@ static bool model_rows(const Shape& s, int R, int P, int G, int64_t M, const uin
           else F::load_act(act, y + tok[j] * ycol_bytes, w.unit);
         }
         if (lt == 0) {   // the store pattern of the team (one lane's view suffices)
-          for (int64_t i = w.skip; i < static_cast<int64_t>(R) * P; ++i) {
-            const int64_t r = w.row0 + i;
-            if (r < 0 || r >= M) return false;
-            stores[r] += 1;
+          for (int pass = 0; pass < passes; ++pass) {
+            const int64_t row0 = w.row0 + static_cast<int64_t>(pass) * R * P;
+            const int64_t skip = w.skip - static_cast<int64_t>(pass) * R * P;
+            for (int64_t i = 0; i < static_cast<int64_t>(R) * P; ++i) {
+              if (i < skip) continue;
+              const int64_t r = row0 + i;
+              if (r < 0 || r >= M) return false;
+              stores[r] += 1;
+            }
           }
         }
       }
@@ -135,15 +144,12 @@ static void case_id(const char* name, int64_t M, int64_t K, int E, int T, int g,
   uint8_t* y = alloc16(act_bytes);
   const float* x = xf ? reinterpret_cast<const float*>(y) : nullptr;
   const int units = static_cast<int>(K / F::kQK) * F::kUnitsPerBlock;
-  const int R = id_rows_per_pass<F>(g);
-  Shape s = plan_rows(M, units, R, 256, QMV_TARGET_WAVES_PER_CU, 0);
-  int r = R;
-  if (s.rows != R) {       // same fallback as the launcher
-    r = 1;
-    s.rows = 1;
-    s.teams = (M + s.slots - 1) / s.slots;
-    s.blocks = (s.teams + s.teams_per_block - 1) / s.teams_per_block;
-  }
+  const int RB = rows_per_pass<F>(1, g);
+  Shape s = plan_rows(M, units, RB, 256, QMV_TARGET_WAVES_PER_CU, 0);
+  const int rb = static_cast<int64_t>(RB) * s.slots <= M ? RB : 1;   // as the launcher
+  s.rows = rb;
+  s.teams = (M + static_cast<int64_t>(rb) * s.slots - 1) / (static_cast<int64_t>(rb) * s.slots);
+  s.blocks = (s.teams + s.teams_per_block - 1) / s.teams_per_block;
   begin({{W, W + E * stride}, {Wg, Wg + E * stride}, {y, y + act_bytes}});
   bool ok = true;
   for (int e = 0; e < E && ok; ++e) {
@@ -151,8 +157,10 @@ static void case_id(const char* name, int64_t M, int64_t K, int E, int T, int g,
     const int nt = T < kMaxCols ? T : kMaxCols;
     for (int j = 0; j < nt; ++j) tok[j] = (j + e) % T;
     std::vector<int> stores(M, 0);
-    ok = model_rows<F>(s, r, s.slots, g, M, W + e * stride, g == 2 ? Wg + e * stride : nullptr, row_bytes,
-                       xf ? nullptr : y, ycol, x, ldx, tok, nt, stores);
+    // rows per pass for nt tokens, as the kernel picks them
+    const int rn = rows_per_pass<F>(nt, g) < rb ? rows_per_pass<F>(nt, g) : rb;
+    ok = model_rows<F>(s, rn, s.slots, g, M, W + e * stride, g == 2 ? Wg + e * stride : nullptr, row_bytes,
+                       xf ? nullptr : y, ycol, x, ldx, tok, nt, stores, rb / rn);
     for (int64_t q = 0; q < M && ok; ++q) ok = stores[q] == 1;
   }
   report(xf ? "id_f32" : "id", ok, name, M, K, T, g);
@@ -243,6 +251,11 @@ int main(int argc, char** argv) {
       case_id<Q40>("q4_0", 77, 1024, 5, 4, g, xpad);
       case_id<Q6K>("q6_k", 50, 768, 4, 2, g, xpad);
       case_id<Q4K>("q4_k", 1, 256, 3, 1, g, xpad);
+      for (int T : {1, 2, 3, 5, 8}) {
+        case_id<Q4K>("q4_k", 77, 1024, 2, T, g, xpad);
+        case_id<Q6K>("q6_k", 33, 512, 2, T, g, xpad);
+        case_id<Q40>("q4_0", 300, 512, 2, T, g, xpad);
+      }
     }
   }
   for (int64_t K : {32, 64, 96, 1024, 14336})

@@ -18,7 +18,7 @@ def test_exports_every_declared_symbol(L):
     names = B.declared_symbols()
     assert set(names) == {"mmvq_type_info", "mmvq_quantize_q8_1", "mmvq", "mmvq_glu", "mmvq_id",
                           "mmvq_id_glu", "mmvq_f32", "mmvq_glu_f32", "mmvq_id_f32", "mmvq_id_glu_f32",
-                          "mmvq_block_dots", "mmvq_strerror"}
+                          "mmvq_ex", "mmvq_id_ex", "mmvq_block_dots", "mmvq_strerror"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -66,7 +66,7 @@ def test_mmvq_argument_checks(L, args, code):
 
 def test_other_entry_points_argument_checks(L):
     assert L.mmvq_glu(None, P16, B.Q4_K, 1, 256, P16, 1, 1, P16, None) == B.ERR_NULL
-    assert L.mmvq_glu(P16, P16, B.Q4_K, 1, 256, P16, 1, 2, P16, None) == B.ERR_TYPE
+    assert L.mmvq_glu(P16, P16, B.Q4_K, 1, 256, P16, 1, 7, P16, None) == B.ERR_TYPE
     assert L.mmvq_glu(P4, P16, B.Q4_K, 1, 256, P16, 1, 1, P16, None) == B.ERR_ALIGN
     assert L.mmvq_id(P16, 288, 4, B.Q4_K, 2, 256, P16, 1, None, 1, P16, None) == B.ERR_NULL
     assert L.mmvq_id(P16, 144, 4, B.Q4_K, 2, 256, P16, 1, P16, 1, P16, None) == B.ERR_SHAPE
@@ -75,7 +75,7 @@ def test_other_entry_points_argument_checks(L):
     assert L.mmvq_id(P16, 296, 4, B.Q4_K, 2, 256, P16, 1, P16, 1, P16, None) == B.ERR_ALIGN
     assert L.mmvq_id(P16, 288, 0, B.Q4_K, 2, 256, P16, 1, P16, 1, P16, None) == B.ERR_SHAPE
     assert L.mmvq_id_glu(None, P16, 288, 4, B.Q4_K, 2, 256, P16, 1, P16, 1, 1, P16, None) == B.ERR_NULL
-    assert L.mmvq_id_glu(P16, P16, 288, 4, B.Q4_K, 2, 256, P16, 1, P16, 1, 3, P16, None) == B.ERR_TYPE
+    assert L.mmvq_id_glu(P16, P16, 288, 4, B.Q4_K, 2, 256, P16, 1, P16, 1, 9, P16, None) == B.ERR_TYPE
     assert L.mmvq_block_dots(P16, B.Q4_K, 1, 100, P16, 1, P16, None) == B.ERR_SHAPE
     assert L.mmvq_quantize_q8_1(None, 32, 1, 32, P16, None) == B.ERR_NULL
     assert L.mmvq_quantize_q8_1(P16, 33, 1, 33, P16, None) == B.ERR_SHAPE
@@ -96,15 +96,36 @@ def test_f32_entry_points_argument_checks(L):
     # fp32 x needs only 4-byte alignment (q8_1 columns need 16)
     assert L.mmvq_f32(P4, B.Q4_K, 1, 256, P16, 1, 256, P16, None) == B.ERR_ALIGN
     assert L.mmvq_glu_f32(None, P16, B.Q4_K, 1, 256, P16, 1, 256, 1, P16, None) == B.ERR_NULL
-    assert L.mmvq_glu_f32(P16, P16, B.Q4_K, 1, 256, P16, 1, 256, 2, P16, None) == B.ERR_TYPE
+    assert L.mmvq_glu_f32(P16, P16, B.Q4_K, 1, 256, P16, 1, 256, 5, P16, None) == B.ERR_TYPE
     assert L.mmvq_glu_f32(P16, P16, B.Q4_K, 1, 256, None, 1, 256, 1, P16, None) == B.ERR_NULL
     assert L.mmvq_id_f32(P16, 288, 4, B.Q4_K, 2, 256, P16, 1, 256, None, 1, P16, None) == B.ERR_NULL
     assert L.mmvq_id_f32(P16, 288, 4, B.Q4_K, 2, 256, P16, 1, 100, P16, 1, P16, None) == B.ERR_SHAPE
     assert L.mmvq_id_f32(P16, 288, 4, B.Q4_K, 2, 256, None, 1, 256, P16, 1, P16, None) == B.ERR_NULL
-    assert L.mmvq_id_glu_f32(P16, P16, 288, 4, B.Q4_K, 2, 256, P16, 1, 256, P16, 1, 3, P16,
+    assert L.mmvq_id_glu_f32(P16, P16, 288, 4, B.Q4_K, 2, 256, P16, 1, 256, P16, 1, 9, P16,
                              None) == B.ERR_TYPE
     assert L.mmvq_id_glu_f32(P16, P16, 288, 4, B.Q4_K, 2, 256, P16, 1, 256, P16, 5, 1, P16,
                              None) == B.ERR_SHAPE
+
+
+def test_ex_entry_points_argument_checks(L):
+    e = B.epilogue(glu_op=B.GLU_SWIGLU)
+    bad_op = B.epilogue(glu_op=5)
+    bad_bias = B.epilogue(up_bias=P16 + 2)
+    ref = ctypes.byref
+    # activation operand: neither -> NULL, both -> SHAPE
+    assert L.mmvq_ex(P16, None, B.Q4_K, 1, 256, None, None, 0, 1, ref(e), P16, None) == B.ERR_NULL
+    assert L.mmvq_ex(P16, None, B.Q4_K, 1, 256, P16, P16, 256, 1, ref(e), P16, None) == B.ERR_SHAPE
+    assert L.mmvq_ex(P16, P16, B.Q4_K, 1, 256, P16, None, 0, 1, ref(bad_op), P16, None) == B.ERR_TYPE
+    assert L.mmvq_ex(P16, None, B.Q4_K, 1, 256, P16, None, 0, 1, ref(bad_bias), P16, None) == B.ERR_ALIGN
+    assert L.mmvq_ex(P16, P4, B.Q4_K, 1, 256, P16, None, 0, 1, ref(e), P16, None) == B.ERR_ALIGN
+    assert L.mmvq_ex(P16, None, B.Q4_K, 1, 256, None, P16, 255, 1, None, P16, None) == B.ERR_SHAPE
+    args = (P16, 288, 4, B.Q4_K, 2, 256, P16, None, 0, 1, P16, 1, ref(e))
+    # shared expert: output required; a gate form needs the shared gate too
+    assert L.mmvq_id_ex(P16, None, *args[1:], P16, None, None, P16, None) == B.ERR_NULL
+    assert L.mmvq_id_ex(P16, P16, *args[1:], P16, None, P16, P16, None) == B.ERR_NULL
+    assert L.mmvq_id_ex(P16, P16, *args[1:], P4, P16, P16, P16, None) == B.ERR_ALIGN
+    assert L.mmvq_id_ex(P16, None, 288, 65535, B.Q4_K, 2, 256, P16, None, 0, 1, P16, 1, ref(e),
+                        P16, None, P16, P16, None) == B.ERR_SHAPE
 
 
 def test_binding_raises_with_code():
