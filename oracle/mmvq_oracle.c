@@ -78,6 +78,7 @@ int orc_type_info(int type, int *block_elems, int *block_bytes) {
     int e, b;
     switch (type) {
     case ORC_Q4_0: e = 32;  b = 18;  break;   /* half d + 16 bytes of nibbles      */
+    case ORC_Q8_0: e = 32;  b = 34;  break;   /* half d + 32 int8                   */
     case ORC_Q4_K: e = 256; b = 144; break;   /* half d, half dmin, 12 + 128 bytes  */
     case ORC_Q6_K: e = 256; b = 210; break;   /* 128 + 64 + 16 + half d             */
     case ORC_Q8_1: e = 32;  b = 36;  break;   /* half d, half s, 32 int8            */
@@ -91,6 +92,7 @@ int orc_type_info(int type, int *block_elems, int *block_bytes) {
 int orc_dots_per_block(int type) {
     switch (type) {
     case ORC_Q4_0: return 1;
+    case ORC_Q8_0: return 1;
     case ORC_Q4_K: return 16;
     case ORC_Q6_K: return 16;
     default: return ORC_ERR_TYPE;
@@ -168,6 +170,13 @@ static int q4_0_code(const uint8_t *blk, int e) {
     return e < 16 ? (qs[e] & 0x0F) : (qs[e - 16] >> 4);
 }
 
+/* Q8_0 [LLM §量化格式 (format table: 8-bit, 34 bytes per 32 weights);
+ * MMVQ §权重的排法 (old-style blocks: one fp16 scale for 32 codes)]. The
+ * pages give the size and the block shape, not the struct. Reading: fp16 d
+ * at bytes 0-1, 32 signed 8-bit codes at bytes 2..33 (element e = byte 2+e),
+ * symmetric, no zero point. Weight value d*q. */
+static int q8_0_code(const uint8_t *blk, int e) { return (int8_t)blk[2 + e]; }
+
 /* Q4_K [GGUF16 §16.1.2, §16.2.1]: bytes 0-1 fp16 d, 2-3 fp16 dmin,
  * 4..15 the packed scales, 16..143 qs (the field order of the struct on the
  * GGUF16 page; the MMVQ page lists the fields in another order, read as a
@@ -234,6 +243,8 @@ int orc_dequantize_row(int type, const uint8_t *row, int64_t K, double *w) {
         const int i = (int)(e % qk);
         if (type == ORC_Q4_0) {
             w[e] = orc_f16_to_f64(rd16(blk)) * (q4_0_code(blk, i) - 8);
+        } else if (type == ORC_Q8_0) {
+            w[e] = orc_f16_to_f64(rd16(blk)) * q8_0_code(blk, i);
         } else if (type == ORC_Q4_K) {
             int sc, m;
             orc_q4_k_scale_min(blk + 4, i / 32, &sc, &m);
@@ -267,6 +278,18 @@ static void block_q4_0(const uint8_t *blk, const uint8_t *ycol, int64_t qb,
     const double t2 = 8.0 * dw * q8_s(ycol, qb);
     *acc += t1 - t2;
     *mag += fabs(t1) + fabs(t2);
+    if (dots) dots[0] = isum;
+}
+
+/* Q8_0: isum = sum q*qy; contribution d_w*d8*isum (symmetric codes: no
+ * zero-point or min term). */
+static void block_q8_0(const uint8_t *blk, const uint8_t *ycol, int64_t qb,
+                       double *acc, double *mag, int32_t *dots) {
+    int isum = 0;
+    for (int e = 0; e < 32; ++e) isum += q8_0_code(blk, e) * q8_q(ycol, qb, e);
+    const double t = orc_f16_to_f64(rd16(blk)) * q8_d(ycol, qb) * isum;
+    *acc += t;
+    *mag += fabs(t);
     if (dots) dots[0] = isum;
 }
 
@@ -326,6 +349,7 @@ static void row_dot(const uint8_t *Wrow, int type, int64_t nb, int bb, int qk,
         const int64_t qb = b * (qk / 32);
         int32_t *dp = dots ? dots + b * nd : NULL;
         if (type == ORC_Q4_0) block_q4_0(blk, ycol, qb, acc, mag, dp);
+        else if (type == ORC_Q8_0) block_q8_0(blk, ycol, qb, acc, mag, dp);
         else if (type == ORC_Q4_K) block_q4_k(blk, ycol, qb, acc, mag, dp);
         else block_q6_k(blk, ycol, qb, acc, mag, dp);
     }

@@ -12,6 +12,8 @@
  *               如何被 dp4a 逐块点积" (pinghaoyang.com.cn), section X.
  *   [GGUF16 §X] page "GGUF 量化内幕：第16章 llama.cpp 量化代码架构"
  *               (cnblogs apachecn), section X.
+ *   [LLM §X]    page "解构LLM：以llama.cpp分析模型推理过程" (laumy.tech),
+ *               section X.
  *
  * What the oracle computes:
  *   1. q8_1 quantization of fp32 activations [MMVQ §激活的量化]: per 32
@@ -38,7 +40,9 @@ extern "C" {
 #endif
 
 /* Type ids follow the ggml numbering [GGUF16 §16.1.1]. */
+/* (Q8_0 is in the same enumeration, id 8.) */
 #define ORC_Q4_0 2
+#define ORC_Q8_0 8
 #define ORC_Q8_1 9
 #define ORC_Q4_K 12
 #define ORC_Q6_K 14
@@ -60,12 +64,12 @@ extern "C" {
 uint16_t orc_f32_to_f16(float f);   /* round to nearest, ties to even */
 double   orc_f16_to_f64(uint16_t h);
 
-/* Elements and bytes per block: Q4_0 32/18, Q4_K 256/144, Q6_K 256/210,
- * Q8_1 32/36. */
+/* Elements and bytes per block: Q4_0 32/18, Q8_0 32/34, Q4_K 256/144,
+ * Q6_K 256/210, Q8_1 32/36. */
 int orc_type_info(int type, int *block_elems, int *block_bytes);
 
 /* Number of int32 dots the oracle reports per weight block:
- * Q4_0 1 (the block dot), Q4_K 16 (dot1 of sub-blocks 0..7, then the
+ * Q4_0 and Q8_0 1 (the block dot), Q4_K 16 (dot1 of sub-blocks 0..7, then the
  * activation sums dot2 of sub-blocks 0..7), Q6_K 16 (one per sub-block). */
 int orc_dots_per_block(int type);
 

@@ -9,6 +9,8 @@ HIP library and (independently) in the oracle.
 Block layouts (byte offsets inside one block):
 
 * Q4_0, 18 bytes / 32 weights: fp16 ``d`` at 0, 16 bytes of 4-bit codes at 2.
+* Q8_0, 34 bytes / 32 weights: fp16 ``d`` at 0, 32 int8 codes at 2 (drawn
+  uniform in -127..127).
 * Q4_K, 144 bytes / 256 weights: fp16 ``d`` at 0, fp16 ``dmin`` at 2,
   12 bytes of packed 6-bit scales and mins at 4, 128 bytes of 4-bit codes at 16.
 * Q6_K, 210 bytes / 256 weights: 128 bytes of low code bits at 0, 64 bytes of
@@ -42,12 +44,12 @@ from dataclasses import dataclass
 
 import numpy as np
 
-Q4_0, Q8_1, Q4_K, Q6_K = 2, 9, 12, 14
-BLOCK = {Q4_0: (32, 18), Q4_K: (256, 144), Q6_K: (256, 210), Q8_1: (32, 36)}
-TYPE_NAME = {Q4_0: "q4_0", Q4_K: "q4_k", Q6_K: "q6_k", Q8_1: "q8_1"}
+Q4_0, Q8_0, Q8_1, Q4_K, Q6_K = 2, 8, 9, 12, 14
+BLOCK = {Q4_0: (32, 18), Q8_0: (32, 34), Q4_K: (256, 144), Q6_K: (256, 210), Q8_1: (32, 36)}
+TYPE_NAME = {Q4_0: "q4_0", Q8_0: "q8_0", Q4_K: "q4_k", Q6_K: "q6_k", Q8_1: "q8_1"}
 
 # fp16 scale ranges per format
-D_RANGE = {Q4_0: (0.001, 0.02), Q4_K: (1e-4, 5e-3), Q6_K: (1e-4, 2e-3)}
+D_RANGE = {Q4_0: (0.001, 0.02), Q8_0: (1e-4, 2e-3), Q4_K: (1e-4, 5e-3), Q6_K: (1e-4, 2e-3)}
 DMIN_RANGE = (1e-4, 5e-3)
 
 
@@ -113,6 +115,9 @@ def weights(wtype: int, M: int, K: int, rng: np.random.Generator,
     if wtype == Q4_0:
         blk[:, 0:2] = _fp16_bytes(rng, (nb,), lo, hi)
         blk[:, 2:18] = rng.integers(0, 256, size=(nb, 16), dtype=np.uint8)
+    elif wtype == Q8_0:
+        blk[:, 0:2] = _fp16_bytes(rng, (nb,), lo, hi)
+        blk[:, 2:34] = rng.integers(-127, 128, size=(nb, 32), dtype=np.int8).view(np.uint8)
     elif wtype == Q4_K:
         mlo, mhi = dmin_range or DMIN_RANGE
         blk[:, 0:2] = _fp16_bytes(rng, (nb,), lo, hi)

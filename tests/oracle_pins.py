@@ -34,7 +34,7 @@ import os
 
 import numpy as np
 
-Q4_0, Q8_1, Q4_K, Q6_K = 2, 9, 12, 14
+Q4_0, Q8_0, Q8_1, Q4_K, Q6_K = 2, 8, 9, 12, 14
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
@@ -73,6 +73,13 @@ def deq_q4_0(row: np.ndarray, K: int) -> np.ndarray:
     qs = blk[:, 2:18].astype(np.int64)
     codes = np.concatenate([qs & 15, qs >> 4], axis=1)
     return (d[:, None] * (codes - 8)).reshape(-1)
+
+
+def deq_q8_0(row: np.ndarray, K: int) -> np.ndarray:
+    """[LLM §量化格式]: 34 bytes per 32 weights, one fp16 scale and signed
+    8-bit codes: weight = d*q."""
+    blk = row.reshape(K // 32, 34)
+    return (_f16v(blk[:, 0:2])[:, None] * blk[:, 2:34].view(np.int8).astype(np.float64)).reshape(-1)
 
 
 def q4_k_scales_from_fragment(scales: np.ndarray):
@@ -149,8 +156,8 @@ def deq_q6_k(row: np.ndarray, K: int) -> np.ndarray:
     return np.concatenate(out)
 
 
-DEQ = {Q4_0: deq_q4_0, Q4_K: deq_q4_k, Q6_K: deq_q6_k}
-BLOCK = {Q4_0: (32, 18), Q4_K: (256, 144), Q6_K: (256, 210)}
+DEQ = {Q4_0: deq_q4_0, Q8_0: deq_q8_0, Q4_K: deq_q4_k, Q6_K: deq_q6_k}
+BLOCK = {Q4_0: (32, 18), Q8_0: (32, 34), Q4_K: (256, 144), Q6_K: (256, 210)}
 
 
 def deq_y(col: np.ndarray, K: int) -> np.ndarray:
@@ -205,8 +212,10 @@ def q8_1_exact(qy: np.ndarray, d: float) -> np.ndarray:
 
 def pin_type_info(O):
     """Block footprints [MMVQ §一次 vec_dot 的解剖 table; §激活的量化;
-    GGUF16 §16.1.2]: Q4_0 18 B/32, Q4_K 144 B/256, Q6_K 210 B/256, q8_1 36 B/32."""
+    GGUF16 §16.1.2; LLM §量化格式 (Q8_0 34 B/32)]: Q4_0 18 B/32, Q8_0 34 B/32,
+    Q4_K 144 B/256, Q6_K 210 B/256, q8_1 36 B/32."""
     assert O.type_info(Q4_0) == (32, 18)
+    assert O.type_info(Q8_0) == (32, 34)
     assert O.type_info(Q4_K) == (256, 144)
     assert O.type_info(Q6_K) == (256, 210)
     assert O.type_info(Q8_1) == (32, 36)
@@ -341,6 +350,16 @@ def pin_q4_0_e3(O):
     assert dots[0][0] == e["isum"] and out == e["out"] and mag == e["mag"], (dots, out, mag)
 
 
+def pin_q8_0_e6(O):
+    fx = golden("q8_0_e6.json")
+    blk = bytes.fromhex(fx["weight_block_hex"])
+    yb = fx["q8_1_block"]
+    y = np.frombuffer(q8_1_block(yb["d_bits"], yb["s_bits"], yb["q"]), dtype=np.uint8)
+    out, mag, dots = _run_block(O, Q8_0, blk, y, 32)
+    e = fx["expected"]
+    assert dots[0][0] == e["isum"] and out == e["out"] and mag == e["mag"], (dots, out, mag)
+
+
 def pin_q4_k_e4(O):
     fx = golden("q4_k_e4.json")
     hdr = bytes.fromhex(fx["weight_block_header_hex"])
@@ -435,7 +454,7 @@ def pin_brute_force(O, seeds=(0, 1, 2)):
     dequantize-then-dot [MMVQ §一次 vec_dot 的解剖; GGUF16 §16.2.2]. K-quants
     agree to fp64 roundoff; Q4_0 uses the fp16 s, so it agrees to within
     8*|d_w|*|s - d8*sum(q)| per block."""
-    for wtype, Ks in [(Q4_0, (32, 64, 256)), (Q4_K, (256, 512)), (Q6_K, (256, 512))]:
+    for wtype, Ks in [(Q4_0, (32, 64, 256)), (Q8_0, (32, 96)), (Q4_K, (256, 512)), (Q6_K, (256, 512))]:
         qk, bb = BLOCK[wtype]
         for K in Ks:
             for seed in seeds:
@@ -490,6 +509,12 @@ def pin_int_dot_special(O, seed: int = 21):
         W = b"".join(pack_q6_k(1.0, [1] * 16, c6[256 * b:256 * b + 256]) for b in range(K // 256))
         out, _, _ = O.mmvq(W, Q6_K, 1, K, y, 1)
         assert out[0, 0] == 0.5 * float(np.dot(c6 - 32, qy))
+        # Q8_0: d = 1, weight q (signed, no zero point)
+        c8 = rng.integers(-127, 128, size=K)
+        W = b"".join(f16(1.0).tobytes() + c8[32 * b:32 * b + 32].astype(np.int8).tobytes()
+                     for b in range(K // 32))
+        out, _, _ = O.mmvq(W, Q8_0, 1, K, y, 1)
+        assert out[0, 0] == 0.5 * float(np.dot(c8, qy))
 
 
 def pin_columns_independent(O, seed: int = 31):
@@ -576,7 +601,7 @@ def pin_zero_padding(O, seed: int = 61):
     the weights there [MMVQ §激活的量化 (padding quantizes to 0)]."""
     from quantized_decode_gemv_quantize_amd import synth
     rng = np.random.default_rng(seed)
-    for wtype, K, P in [(Q4_0, 64, 64), (Q4_K, 256, 256), (Q6_K, 256, 256)]:
+    for wtype, K, P in [(Q4_0, 64, 64), (Q8_0, 64, 32), (Q4_K, 256, 256), (Q6_K, 256, 256)]:
         W = synth.weights(wtype, 3, K + P, rng)
         x = np.zeros((1, K + P), dtype=np.float32)
         x[0, :K] = rng.standard_normal(K)
@@ -592,7 +617,7 @@ def pin_linearity(O, seed: int = 71):
     """Doubling every weight block scale (exact in fp16) doubles the output."""
     from quantized_decode_gemv_quantize_amd import synth
     rng = np.random.default_rng(seed)
-    for wtype, K, fields in [(Q4_0, 128, [(0, 2)]), (Q4_K, 256, [(0, 2), (2, 4)]),
+    for wtype, K, fields in [(Q4_0, 128, [(0, 2)]), (Q8_0, 64, [(0, 2)]), (Q4_K, 256, [(0, 2), (2, 4)]),
                              (Q6_K, 256, [(208, 210)])]:
         W = synth.weights(wtype, 2, K, rng)
         y = O.quantize_q8_1(rng.standard_normal((1, K)).astype(np.float32))
@@ -716,7 +741,7 @@ def pin_error_codes(O):
 
 
 ALL_PINS = [pin_type_info, pin_f16_decode, pin_f16_encode, pin_q8_1_e1, pin_q8_1_e2,
-            pin_q8_1_properties, pin_q4_0_e3, pin_q4_k_e4, pin_q6_k_e5, pin_q4_k_fragment,
+            pin_q8_1_properties, pin_q4_0_e3, pin_q4_k_e4, pin_q6_k_e5, pin_q8_0_e6, pin_q4_k_fragment,
             pin_q4_k_bijection, pin_q6_k_fragment, pin_brute_force, pin_int_dot_special,
             pin_columns_independent, pin_glu, pin_id, pin_zero_padding, pin_linearity,
             pin_glu_variants, pin_epilogue, pin_error_codes]

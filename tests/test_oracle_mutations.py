@@ -65,6 +65,11 @@ MUTATIONS = {
                                "if (epi->up_bias) u += epi->up_bias[r];"),
     "shared_expert_gate_up_swapped": ("rc = orc_glu(epi ? epi->glu_op : ORC_GLU_PLAIN, g, u,",
                                       "rc = orc_glu(epi ? epi->glu_op : ORC_GLU_PLAIN, u, g,"),
+    "q8_0_unsigned_codes": ("static int q8_0_code(const uint8_t *blk, int e) { return (int8_t)blk[2 + e]; }",
+                            "static int q8_0_code(const uint8_t *blk, int e) { return blk[2 + e]; }"),
+    "q8_0_codes_at_0": ("return (int8_t)blk[2 + e]; }", "return (int8_t)blk[e]; }"),
+    "q8_0_zero_point": ("isum += q8_0_code(blk, e) * q8_q(ycol, qb, e);",
+                        "isum += (q8_0_code(blk, e) - 1) * q8_q(ycol, qb, e);"),
     "columns_share_first": ("row_dot(W + r * nb * bb, type, nb, bb, qk, y_q + j * ycol_bytes, &acc, &mg,",
                             "row_dot(W + r * nb * bb, type, nb, bb, qk, y_q, &acc, &mg,"),
 }
