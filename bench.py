@@ -504,7 +504,7 @@ def main():
 
     if args.all:
         for name in ["q4_0_256x1024", "q4_k_4096x4096", "q4_k_4096x14336", "q4_k_14336x4096",
-                     "q6_k_128256x4096"]:
+                     "q6_k_128256x4096", "q8_0_4096x14336"]:
             w = synth.BY_NAME[name]
             for nn in (w.n if name != "q4_k_4096x14336" else (1, 2, 4, 8)):
                 r, *_ = time_workload(torch, B, w, nn, 1000, 100)

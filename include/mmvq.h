@@ -13,6 +13,8 @@
  *               如何被 dp4a 逐块点积" (pinghaoyang.com.cn), section X.
  *   [GGUF16 §X] page "GGUF 量化内幕：第16章 llama.cpp 量化代码架构"
  *               (cnblogs apachecn), section X.
+ *   [LLM §X]    page "解构LLM：以llama.cpp分析模型推理过程" (laumy.tech),
+ *               section X.
  *
  * Conventions for every entry point:
  *   - Pointers to data (x, W, y_q, ids, out, dots) are DEVICE pointers. The
@@ -30,6 +32,7 @@
  *     (K/qk)*block_bytes. Byte layouts:
  *       Q4_0 (18 B / 32): fp16 d @0, 16 B of 4-bit codes @2; qs[j] low
  *            nibble = element j, high nibble = element j+16; w = d*(q-8).
+ *       Q8_0 (34 B / 32): fp16 d @0, 32 int8 codes @2; w = d*q.
  *       Q4_K (144 B / 256): fp16 d @0, fp16 dmin @2, 12 B of packed 6-bit
  *            sub-block scales and mins @4, 128 B of 4-bit codes @16;
  *            w = d*sc*q - dmin*m.
@@ -62,6 +65,7 @@ extern "C" {
  * [GGUF16 §16.1.1]. */
 enum {
     MMVQ_Q4_0 = 2,
+    MMVQ_Q8_0 = 8,
     MMVQ_Q8_1 = 9,
     MMVQ_Q4_K = 12,
     MMVQ_Q6_K = 14
@@ -110,8 +114,9 @@ enum {
 #define MMVQ_MAX_COLS 8
 
 /* Block geometry of a type: elements per block and bytes per block
- * (Q4_0 32/18, Q4_K 256/144, Q6_K 256/210, Q8_1 32/36)
- * [MMVQ §一次 vec_dot 的解剖 (format table); GGUF16 §16.1.2, §16.1.3].
+ * (Q4_0 32/18, Q8_0 32/34, Q4_K 256/144, Q6_K 256/210, Q8_1 32/36)
+ * [MMVQ §一次 vec_dot 的解剖 (format table); GGUF16 §16.1.2, §16.1.3;
+ * LLM §量化格式 (Q8_0)].
  * Either output pointer may be NULL. Host-only; touches no device. */
 int mmvq_type_info(int type, int *block_elems, int *block_bytes);
 
@@ -128,7 +133,8 @@ int mmvq_quantize_q8_1(const float *x, int64_t K, int64_t n, int64_t ldx,
 /* out[j*M + r] = sum over the K/qk blocks of row r of W of (block scales)
  * x (integer block dot against column j of y_q), for r < M, j < n
  * [MMVQ §一次 vec_dot 的解剖, §kernel 的形状, §归约与写出, §多个 token 时].
- * Q4_0: d_w*(d8*sum(q*qy) - 8*s) per 32-block. Q4_K: per 32-element
+ * Q4_0: d_w*(d8*sum(q*qy) - 8*s) per 32-block. Q8_0: d_w*d8*sum(q*qy)
+ * per 32-block. Q4_K: per 32-element
  * sub-block t, d*sc_t*d8*sum(q*qy) - dmin*m_t*d8*sum(qy). Q6_K: per
  * 16-element sub-block, d*sc*d8*sum((q-32)*qy). Accumulated in fp32.
  * Requires K % qk == 0, M >= 1, 1 <= n <= MMVQ_MAX_COLS. */
@@ -223,7 +229,7 @@ int mmvq_id_ex(const void *W_up, const void *W_gate,
  * device decode routines, written instead of being scaled and summed.
  * dots[((j*M + r)*(K/qk) + b)*D + i] with D = 16 for Q4_K (sum(q*qy) of
  * sub-blocks 0..7, then sum(qy) of sub-blocks 0..7), 16 for Q6_K
- * (sum((q-32)*qy) of sub-blocks 0..15), 1 for Q4_0 (sum(q*qy)).
+ * (sum((q-32)*qy) of sub-blocks 0..15), 1 for Q4_0 and Q8_0 (sum(q*qy)).
  * [MMVQ §dp4a, §一次 vec_dot 的解剖]. Same requirements as mmvq. */
 int mmvq_block_dots(const void *W, int type, int64_t M, int64_t K,
                     const void *y_q, int64_t n, int32_t *dots, void *stream);

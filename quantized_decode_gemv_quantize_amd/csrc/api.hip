@@ -14,6 +14,7 @@ namespace {
 const Dispatch* dispatch_for(int type, bool f32) {
   switch (type) {
     case MMVQ_Q4_0: return f32 ? &dispatch_q4_0_f32() : &dispatch_q4_0();
+    case MMVQ_Q8_0: return f32 ? &dispatch_q8_0_f32() : &dispatch_q8_0();
     case MMVQ_Q4_K: return f32 ? &dispatch_q4_k_f32() : &dispatch_q4_k();
     case MMVQ_Q6_K: return f32 ? &dispatch_q6_k_f32() : &dispatch_q6_k();
     default: return nullptr;
@@ -146,6 +147,7 @@ int mmvq_type_info(int type, int* block_elems, int* block_bytes) {
   int e, b;
   switch (type) {
     case MMVQ_Q4_0: e = 32; b = 18; break;
+    case MMVQ_Q8_0: e = 32; b = 34; break;
     case MMVQ_Q4_K: e = 256; b = 144; break;
     case MMVQ_Q6_K: e = 256; b = 210; break;
     case MMVQ_Q8_1: e = 32; b = 36; break;

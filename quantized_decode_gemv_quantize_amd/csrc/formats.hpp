@@ -369,6 +369,117 @@ struct Q40 {
 };
 
 // ===========================================================================
+// Q8_0  [LLM §量化格式 (34 bytes per 32 weights); MMVQ §权重的排法]
+// 34 bytes: fp16 d @0, int8 qs[32] @2 (element e = byte 2+e). Weight = d*q;
+// per block the product is d*d8*sum(q*qy) (symmetric: no s term). Unit =
+// one block. Blocks are 2-byte aligned: at an offset = 2 (mod 4) the 32 code
+// bytes are dword aligned (two 16-byte runs) and d is the 16-bit word before
+// them; at 0 (mod 4) the block is read as two 16-byte runs from its start
+// plus its last 16-bit word, and the codes are re-aligned by two bytes.
+// ===========================================================================
+struct Q80 {
+  static constexpr int kType = 8, kQK = 32, kBlockBytes = 34;
+  static constexpr int kUnitsPerBlock = 1, kDotsPerBlock = 1;
+
+  struct Act {
+    uint32_t y[8];
+    float d8;
+  };
+
+  __device__ static void issue_act(Act& a, const uint8_t* ycol, int u) {
+    const uint8_t* b = ycol + static_cast<int64_t>(u) * kQ8Bytes;
+    const u32x4 lo = ld_x4(b + 4), hi = ld_x4(b + 20);
+    a.y[0] = lo.x; a.y[1] = lo.y; a.y[2] = lo.z; a.y[3] = lo.w;
+    a.y[4] = hi.x; a.y[5] = hi.y; a.y[6] = hi.z; a.y[7] = hi.w;
+    a.d8 = __uint_as_float(ld_u16(b));      // fp16 d, raw
+  }
+
+  __device__ static void finish_act(Act& a) { a.d8 = h2f(__float_as_uint(a.d8)); }
+
+  __device__ static void load_act(Act& a, const uint8_t* ycol, int u) {
+    issue_act(a, ycol, u);
+    finish_act(a);
+  }
+
+  // fp32 activations: the lane holds its whole q8_1 block.
+  struct XRaw {
+    u32x4 r[8];
+  };
+  static constexpr int kXWords = 32;
+
+  __device__ static void load_x(XRaw& x, const float* xcol, int u) {
+    const float* p = xcol + static_cast<int64_t>(u) * 32;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x.r[k] = ld_x4(reinterpret_cast<const uint8_t*>(p + 4 * k));
+  }
+
+  __device__ static void quant_x(Act& a, const XRaw& x) {
+    float m = absmax4(x.r[0]);
+#pragma unroll
+    for (int k = 1; k < 8; ++k) m = fmaxf(m, absmax4(x.r[k]));
+    const float d = q8_scale(m);
+    int sq = 0;
+    q8_quant_block(x.r, d, a.y, sq);
+    a.d8 = q8_d_rounded(d);
+  }
+
+  __device__ static void zero_act(Act& a) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) a.y[k] = 0;
+    a.d8 = 0.0f;
+  }
+
+  struct Lane {
+    uint32_t off;    // block offset from the row start
+  };
+  __device__ static Lane lane(int u) { return Lane{static_cast<uint32_t>(u * kBlockBytes)}; }
+
+  struct Wt {
+    u32x4 lo, hi;    // two dword-aligned 16-byte runs
+    uint32_t extra;  // 16-bit word: d (offset 2 mod 4) or code bytes 30..31
+    bool odd;        // block address = 2 (mod 4)
+  };
+
+  __device__ static void load_wt(Wt& w, const uint8_t* row, uint32_t extra, const Lane& l) {
+    const uint32_t off = extra + l.off;
+    w.odd = ((static_cast<uint32_t>(reinterpret_cast<uintptr_t>(row)) + off) & 2u) != 0;
+    const uint32_t run = off + (w.odd ? 2u : 0u);
+    w.lo = ld_x4(row + run);
+    w.hi = ld_x4(row + (run + 16u));
+    w.extra = ld_u16(row + (off + (w.odd ? 0u : 32u)));
+  }
+
+  struct Dec {
+    uint32_t q[8];
+    float d;
+  };
+
+  __device__ static void decode(const Wt& w, Dec& o, const Lane&) {
+    const uint32_t dw[9] = {w.lo.x, w.lo.y, w.lo.z, w.lo.w, w.hi.x, w.hi.y, w.hi.z, w.hi.w, w.extra};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o.q[k] = w.odd ? dw[k] : shr16_pair(dw[k + 1], dw[k]);
+    o.d = h2f(w.odd ? w.extra : w.lo.x);
+  }
+
+  __device__ static int isum(const Dec& o, const Act& a) {
+    int s = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s = dot4(o.q[k], a.y[k], s);
+    return s;
+  }
+
+  __device__ static float col_dot(const Dec& o, const Act& a) {
+    return o.d * (a.d8 * static_cast<float>(isum(o, a)));
+  }
+
+  __device__ static void int_dots(const Dec& o, const uint8_t* ycol, int u, int* dots) {
+    Act a;
+    load_act(a, ycol, u);
+    dots[0] += isum(o, a);
+  }
+};
+
+// ===========================================================================
 // Q6_K  [MMVQ §dp4a, §一次 vec_dot 的解剖]
 // 210 bytes: ql[128] @0 (low 4 bits), qh[64] @128 (high 2 bits), int8
 // sc[16] @192, fp16 d @208. Element 128h + 32g + l (h 0..1, g 0..3, l 0..31):

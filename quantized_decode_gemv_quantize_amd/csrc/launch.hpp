@@ -168,9 +168,11 @@ Dispatch make_dispatch() {
 }
 
 const Dispatch& dispatch_q4_0();
+const Dispatch& dispatch_q8_0();
 const Dispatch& dispatch_q4_k();
 const Dispatch& dispatch_q6_k();
 const Dispatch& dispatch_q4_0_f32();
+const Dispatch& dispatch_q8_0_f32();
 const Dispatch& dispatch_q4_k_f32();
 const Dispatch& dispatch_q6_k_f32();
 

@@ -11,7 +11,7 @@ import oracle
 from quantized_decode_gemv_quantize_amd import binding as B
 from quantized_decode_gemv_quantize_amd import synth
 
-TNAME = {B.Q4_0: "q4_0", B.Q4_K: "q4_k", B.Q6_K: "q6_k"}
+TNAME = {B.Q4_0: "q4_0", B.Q8_0: "q8_0", B.Q4_K: "q4_k", B.Q6_K: "q6_k"}
 
 # |gpu - oracle| <= REL * A + ABS, with A the sum of |block contributions|.
 REL, ABS = 1e-5, 1e-6

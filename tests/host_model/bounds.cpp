@@ -228,6 +228,9 @@ int main(int argc, char** argv) {
             if (nb * 8 * 32 <= 16384 && (nb <= 16 || nc <= 2))
               case_rows<Q40>("q4_0", M, 32LL * nb * 8, nc, g, xpad);
             case_rows<Q40>("q4_0", M, 32LL * nb, nc, g, xpad);
+            case_rows<Q80>("q8_0", M, 32LL * nb, nc, g, xpad);
+            if (nb * 8 * 32 <= 16384 && (nb <= 16 || nc <= 2))
+              case_rows<Q80>("q8_0", M, 32LL * nb * 8, nc, g, xpad);
           }
         }
       }
@@ -235,6 +238,7 @@ int main(int argc, char** argv) {
         case_block_dots<Q4K>("q4_k", M, 256LL * nb, 2);
         case_block_dots<Q6K>("q6_k", M, 256LL * nb, 2);
         case_block_dots<Q40>("q4_0", M, 32LL * nb, 2);
+        case_block_dots<Q80>("q8_0", M, 32LL * nb, 2);
       }
     }
   }
@@ -244,6 +248,8 @@ int main(int argc, char** argv) {
     case_rows<Q4K>("q4_k", 65, 16384, 8, 1, xpad);
     case_rows<Q4K>("q4_k", 65, 16384, 1, 2, xpad);
     case_rows<Q40>("q4_0", 129, 16384, 8, 2, xpad);
+    case_rows<Q80>("q8_0", 129, 16384, 8, 2, xpad);
+    case_rows<Q80>("q8_0", 33, 16384, 1, 1, xpad);
     case_rows<Q6K>("q6_k", 129, 32768, 1, 1, xpad);
     for (int g = 1; g <= 2; ++g) {
       case_id<Q4K>("q4_k", 200, 512, 4, 3, g, xpad);
@@ -255,6 +261,7 @@ int main(int argc, char** argv) {
         case_id<Q4K>("q4_k", 77, 1024, 2, T, g, xpad);
         case_id<Q6K>("q6_k", 33, 512, 2, T, g, xpad);
         case_id<Q40>("q4_0", 300, 512, 2, T, g, xpad);
+        case_id<Q80>("q8_0", 45, 96, 3, T, g, xpad);
       }
     }
   }
@@ -269,6 +276,8 @@ int main(int argc, char** argv) {
     }
     case_rows<Q4K>("q4_k", 4096, 4096, 1, 1);
     case_rows<Q40>("q4_0", 256, 1024, 1, 1);
+    case_rows<Q80>("q8_0", 4096, 14336, 1, 1);
+    case_rows<Q80>("q8_0", 4096, 14336, 1, 1, 0);
     case_rows<Q6K>("q6_k", 128256, 4096, 1, 1);
     case_id<Q4K>("q4_k", 14336, 4096, 8, 8, 2);
     case_id<Q4K>("q4_k", 14336, 4096, 8, 8, 1);

@@ -25,6 +25,7 @@ def test_exports_every_declared_symbol(L):
 
 def test_type_info():
     assert B.mmvq_type_info(B.Q4_0) == (32, 18)
+    assert B.mmvq_type_info(B.Q8_0) == (32, 34)
     assert B.mmvq_type_info(B.Q4_K) == (256, 144)
     assert B.mmvq_type_info(B.Q6_K) == (256, 210)
     assert B.mmvq_type_info(B.Q8_1) == (32, 36)
@@ -51,6 +52,8 @@ P16, P4 = 1 << 20, (1 << 20) + 4
     ((P16, B.Q8_1, 1, 256, P16, 1, P16), B.ERR_TYPE),
     ((P16, B.Q4_K, 1, 200, P16, 1, P16), B.ERR_SHAPE),
     ((P16, B.Q4_0, 1, 48, P16, 1, P16), B.ERR_SHAPE),
+    ((P16, B.Q8_0, 1, 48, P16, 1, P16), B.ERR_SHAPE),
+    ((P16, B.Q8_0, 1, 32 * 513, P16, 1, P16), B.ERR_SHAPE),
     ((P16, B.Q4_K, 0, 256, P16, 1, P16), B.ERR_SHAPE),
     ((P16, B.Q4_K, 1, 256, P16, 0, P16), B.ERR_SHAPE),
     ((P16, B.Q4_K, 1, 256, P16, 9, P16), B.ERR_SHAPE),

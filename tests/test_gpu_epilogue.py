@@ -13,7 +13,7 @@ from quantized_decode_gemv_quantize_amd import synth
 
 pytestmark = pytest.mark.gpu
 
-Q4_0, Q4_K, Q6_K = B.Q4_0, B.Q4_K, B.Q6_K
+Q4_0, Q8_0, Q4_K, Q6_K = B.Q4_0, B.Q8_0, B.Q4_K, B.Q6_K
 OPS = [B.GLU_PLAIN, B.GLU_SWIGLU, B.GLU_GEGLU, B.GLU_SWIGLU_OAI, B.GLU_SWIGLU_CLAMP]
 
 
@@ -45,7 +45,7 @@ def _check(got, ref, tol, what):
 
 
 CASES = [(t, M, K, n, op, gate, f32)
-         for (t, M, K) in [(Q4_K, 300, 2048), (Q4_0, 77, 1024), (Q6_K, 65, 768)]
+         for (t, M, K) in [(Q4_K, 300, 2048), (Q4_0, 77, 1024), (Q6_K, 65, 768), (Q8_0, 45, 512)]
          for n in (1, 3)
          for op in OPS
          for gate in (True,)

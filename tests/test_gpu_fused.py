@@ -19,7 +19,7 @@ from quantized_decode_gemv_quantize_amd import synth
 
 pytestmark = pytest.mark.gpu
 
-Q4_0, Q4_K, Q6_K = B.Q4_0, B.Q4_K, B.Q6_K
+Q4_0, Q8_0, Q4_K, Q6_K = B.Q4_0, B.Q8_0, B.Q4_K, B.Q6_K
 
 
 @pytest.fixture(scope="module")
@@ -56,7 +56,8 @@ FUSED_CASES = [(Q4_0, 37, 96, 1, 0), (Q4_0, 300, 1024, 3, 5), (Q4_0, 129, 16384,
                (Q4_K, 1, 256, 1, 0), (Q4_K, 37, 512, 2, 3), (Q4_K, 1000, 4096, 5, 0),
                (Q4_K, 129, 14336, 8, 7), (Q4_K, 65, 16384, 1, 1),
                (Q6_K, 1, 256, 1, 0), (Q6_K, 37, 768, 3, 2), (Q6_K, 300, 4096, 8, 0),
-               (Q6_K, 129, 32768, 2, 1)]
+               (Q6_K, 129, 32768, 2, 1), (Q8_0, 37, 96, 1, 0), (Q8_0, 300, 1024, 3, 5),
+               (Q8_0, 129, 16384, 8, 1)]
 
 
 @pytest.mark.parametrize("wtype,M,K,n,pad", FUSED_CASES,
@@ -149,7 +150,7 @@ def test_mmvq_id_f32(O, name, wtype, E, M, K, ids, fused_glu):
 
 
 WORKLOADS_F32 = [("q4_k_4096x14336", 1), ("q4_k_4096x14336", 8), ("q6_k_128256x4096", 1),
-                 ("q4_0_256x1024", 1)]
+                 ("q4_0_256x1024", 1), ("q8_0_4096x14336", 1)]
 
 
 @pytest.mark.parametrize("name,n", WORKLOADS_F32, ids=[f"{a}-n{b}" for a, b in WORKLOADS_F32])

@@ -20,7 +20,7 @@ from quantized_decode_gemv_quantize_amd import synth
 
 pytestmark = pytest.mark.gpu
 
-Q4_0, Q4_K, Q6_K = B.Q4_0, B.Q4_K, B.Q6_K
+Q4_0, Q8_0, Q4_K, Q6_K = B.Q4_0, B.Q8_0, B.Q4_K, B.Q6_K
 
 
 @pytest.fixture(scope="module")
@@ -57,7 +57,8 @@ def test_quantize_bitexact(O, K, n, ldx):
 # Integer block dots: bit-exact
 # ---------------------------------------------------------------------------
 DOT_CASES = [(Q4_0, 37, 96, 2), (Q4_0, 5, 1024, 1), (Q4_0, 7, 32, 3), (Q4_K, 37, 512, 3),
-             (Q4_K, 3, 4096, 1), (Q6_K, 37, 768, 2), (Q6_K, 9, 256, 1), (Q6_K, 3, 4096, 1)]
+             (Q4_K, 3, 4096, 1), (Q6_K, 37, 768, 2), (Q6_K, 9, 256, 1), (Q6_K, 3, 4096, 1),
+             (Q8_0, 37, 96, 2), (Q8_0, 5, 1024, 1), (Q8_0, 7, 32, 3)]
 
 
 @pytest.mark.parametrize("wtype,M,K,n", DOT_CASES,
@@ -83,6 +84,7 @@ def test_block_dots_bitexact(O, wtype, M, K, n):
 # ---------------------------------------------------------------------------
 SHAPES = {
     Q4_0: [(1, 32), (37, 96), (300, 1024), (1000, 4096), (129, 16384)],
+    Q8_0: [(1, 32), (37, 96), (300, 1024), (1000, 4096), (129, 16384)],
     Q4_K: [(1, 256), (37, 512), (300, 2304), (1000, 4096), (129, 14336), (65, 16384)],
     Q6_K: [(1, 256), (37, 768), (300, 4096), (129, 32768)],
 }
@@ -114,7 +116,7 @@ def test_gemv_parity(O, wtype, M, K, n):
 FULL = [("q4_0_256x1024", 1), ("q4_k_4096x4096", 1), ("q4_k_4096x14336", 1),
         ("q4_k_4096x14336", 2), ("q4_k_4096x14336", 4), ("q4_k_4096x14336", 8),
         ("q4_k_14336x4096", 1), ("q4_k_14336x4096", 2), ("q4_k_14336x4096", 4),
-        ("q4_k_14336x4096", 8), ("q6_k_128256x4096", 1)]
+        ("q4_k_14336x4096", 8), ("q6_k_128256x4096", 1), ("q8_0_4096x14336", 1)]
 
 
 @pytest.mark.parametrize("name,n", FULL, ids=[f"{a}-n{b}" for a, b in FULL])
@@ -138,7 +140,7 @@ def test_gemv_workload_sampled(O, name, n):
 # Fused gate/up GLU
 # ---------------------------------------------------------------------------
 GLU_CASES = [(t, M, K, n, op) for t, M, K in [(Q4_K, 300, 4096), (Q4_K, 37, 512), (Q4_0, 300, 1024),
-                                               (Q6_K, 100, 4096), (Q4_K, 129, 16384)]
+                                               (Q6_K, 100, 4096), (Q4_K, 129, 16384), (Q8_0, 77, 2048)]
              for n in (1, 2, 8) for op in (B.GLU_SWIGLU, B.GLU_PLAIN)]
 
 
@@ -212,6 +214,7 @@ def id_case(O, wtype, E, M, K, ids, fused, op=B.GLU_SWIGLU, rows=None, seed=0, d
 ID_CASES = [
     ("q4_k-E4-T3-k2", Q4_K, 4, 200, 512, [[2, 0], [1, 2], [2, 3]]),
     ("q4_k-E8-T8-k2", Q4_K, 8, 300, 2048, "random"),
+    ("q8_0-E3-T4-k2", Q8_0, 3, 45, 96, [[2, 0], [1, 2], [0, 1], [2, 1]]),
     ("q4_k-E3-T5-k3", Q4_K, 3, 64, 256, [[0, 1, 2], [2, 1, 0], [1, 0, 2], [0, 2, 1], [2, 0, 1]]),
     ("q4_k-E6-T1-k1", Q4_K, 6, 129, 4096, [[5]]),
     ("q4_k-dup-in-token", Q4_K, 4, 100, 512, [[1, 1], [3, 1]]),
