@@ -110,8 +110,15 @@ enum {
     MMVQ_ERR_LAUNCH = -5     /* the HIP runtime reported an error at launch         */
 };
 
-/* Largest number of activation columns (tokens) per call [MMVQ §分派]. */
+/* Largest number of activation columns (tokens) per call of the mat-vec
+ * forms [MMVQ §分派]. */
 #define MMVQ_MAX_COLS 8
+
+/* Largest number of columns of the many-column path: mmvq and mmvq_ex
+ * (q8_1 activations, no gate, Q4_K weights) with MMVQ_MAX_COLS < n <=
+ * MMVQ_MAX_COLS_BATCH run on the matrix cores [MMVQ §多个 token 时]; so does
+ * the quantizer. Other forms and types return MMVQ_ERR_SHAPE for n > 8. */
+#define MMVQ_MAX_COLS_BATCH 256
 
 /* Block geometry of a type: elements per block and bytes per block
  * (Q4_0 32/18, Q8_0 32/34, Q4_K 256/144, Q6_K 256/210, Q8_1 32/36)
@@ -124,7 +131,7 @@ int mmvq_type_info(int type, int *block_elems, int *block_bytes);
  * x + j*ldx (ldx >= K floats); the first K values of each column are used.
  * Per block of 32: d = amax/127 in fp32, q = roundf(x/d) (0 when d == 0),
  * stored fp16(d), fp16(fp32(d*sum(q))), q. y_q receives n*(K/32)*36 bytes.
- * Requires K % 32 == 0, 1 <= n <= MMVQ_MAX_COLS. Inputs must be finite; for
+ * Requires K % 32 == 0, 1 <= n <= MMVQ_MAX_COLS_BATCH. Inputs must be finite; for
  * blocks whose amax is below 127*2^-126 the fp32 d is subnormal and the
  * codes are not meaningful (the computation is still defined). */
 int mmvq_quantize_q8_1(const float *x, int64_t K, int64_t n, int64_t ldx,
@@ -137,7 +144,11 @@ int mmvq_quantize_q8_1(const float *x, int64_t K, int64_t n, int64_t ldx,
  * per 32-block. Q4_K: per 32-element
  * sub-block t, d*sc_t*d8*sum(q*qy) - dmin*m_t*d8*sum(qy). Q6_K: per
  * 16-element sub-block, d*sc*d8*sum((q-32)*qy). Accumulated in fp32.
- * Requires K % qk == 0, M >= 1, 1 <= n <= MMVQ_MAX_COLS. */
+ * Requires K % qk == 0, M >= 1 and 1 <= n <= MMVQ_MAX_COLS, or for Q4_K
+ * 1 <= n <= MMVQ_MAX_COLS_BATCH: n > 8 takes the many-column path, where
+ * the integer dots of 16 rows x 16 columns x 32 elements come from one int8
+ * matrix-core instruction and the same scales are applied per sub-block
+ * (no upper bound on K there). */
 int mmvq(const void *W, int type, int64_t M, int64_t K,
          const void *y_q, int64_t n, float *out, void *stream);
 

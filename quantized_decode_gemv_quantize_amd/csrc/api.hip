@@ -6,6 +6,7 @@
 
 #include "../../include/mmvq.h"
 #include "launch.hpp"
+#include "mmq_plan.hpp"
 
 using namespace qmv;
 
@@ -92,9 +93,36 @@ mmvq_epilogue glu_only(int glu_op) {
   return e;
 }
 
+// Many columns (n > MMVQ_MAX_COLS): the MFMA kernel, Q4_K weights, q8_1
+// activations, no gate; the epilogue's up scale and bias apply.
+int mmq_common(const void* W, int type, int64_t M, int64_t K, const void* y_q, int64_t n,
+               const mmvq_epilogue* epi, float* out, void* stream) {
+  if (!W || !y_q || !out) return MMVQ_ERR_NULL;
+  if (type != MMVQ_Q4_K) return dispatch_for(type, false) ? MMVQ_ERR_SHAPE : MMVQ_ERR_TYPE;
+  if (M < 1 || K < 1 || K % 256 != 0 || n > MMVQ_MAX_COLS_BATCH) return MMVQ_ERR_SHAPE;
+  if (M > (int64_t(1) << 40) / K || K / 256 > (int64_t(1) << 24)) return MMVQ_ERR_SHAPE;
+  if (!aligned(W, 16) || !aligned(y_q, 16) || !aligned(out, 4)) return MMVQ_ERR_ALIGN;
+  RowArgs ra{};
+  int rc = set_epilogue(epi, false, &ra);
+  if (rc) return rc;
+  MmqArgs a{};
+  a.W = static_cast<const uint8_t*>(W);
+  a.y = static_cast<const uint8_t*>(y_q);
+  a.out = out;
+  a.up_bias = ra.up_bias;
+  a.up_scale = ra.up_scale;
+  a.M = M;
+  a.row_bytes = K / 256 * 144;
+  a.ycol_bytes = K / 32 * kQ8Bytes;
+  a.n = static_cast<int>(n);
+  a.nsb = static_cast<int>(K / 256);
+  return launch_mmq_q4k(a, static_cast<hipStream_t>(stream));
+}
+
 // Plain or gate/up product with an optional epilogue (W_gate NULL: no gate).
 int rows_common(const void* W_up, const void* W_gate, int type, int64_t M, int64_t K, const ActIn& in, int64_t n,
                 const mmvq_epilogue* epi, float* out, void* stream) {
+  if (n > MMVQ_MAX_COLS && !W_gate && !in.x) return mmq_common(W_up, type, M, K, in.y_q, n, epi, out, stream);
   const Dispatch* d;
   RowArgs a;
   int rc = check_gemv(W_up, type, M, K, in, n, out, &d, &a);
@@ -160,7 +188,7 @@ int mmvq_type_info(int type, int* block_elems, int* block_bytes) {
 
 int mmvq_quantize_q8_1(const float* x, int64_t K, int64_t n, int64_t ldx, void* y_q, void* stream) {
   if (!x || !y_q) return MMVQ_ERR_NULL;
-  if (K < 32 || K % 32 != 0 || n < 1 || n > MMVQ_MAX_COLS || ldx < K) return MMVQ_ERR_SHAPE;
+  if (K < 32 || K % 32 != 0 || n < 1 || n > MMVQ_MAX_COLS_BATCH || ldx < K) return MMVQ_ERR_SHAPE;
   if (K > (int64_t(1) << 30)) return MMVQ_ERR_SHAPE;
   if (!aligned(x, 4) || !aligned(y_q, 16)) return MMVQ_ERR_ALIGN;
   return launch_quantize_q8_1(x, static_cast<uint8_t*>(y_q), K, n, ldx, static_cast<hipStream_t>(stream));

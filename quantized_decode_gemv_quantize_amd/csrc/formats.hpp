@@ -201,12 +201,19 @@ struct Q4K {
     }
     o.d = h2f(w.hdr.x);
     o.dmin = h2f(w.hdr.x >> 16);
-    const uint32_t H1 = w.hdr.y, H2 = w.hdr.z, H3 = w.hdr.w;
-    const uint32_t Xs = l.lo ? H1 : H3, Xm = l.lo ? H2 : H3;
-    o.scp = ((Xs >> l.sh) & l.maskA) | ((H1 >> (l.sh + 2)) & l.maskB);
-    const uint32_t mp = ((Xm >> l.shm) & l.maskA) | ((H2 >> (l.sh + 2)) & l.maskB);
+    uint32_t mp;
+    chunk_scales(w.hdr, l, o.scp, mp);
     o.m0 = static_cast<float>(mp & 0xFFu);
     o.m1 = static_cast<float>((mp >> 8) & 0xFFu);
+  }
+
+  // The 6-bit scales (scp) and mins (mp) of the lane's chunk c: byte 0 for
+  // sub-block 2c, byte 1 for 2c+1 (the unpack rule above).
+  __device__ static void chunk_scales(const u32x4& hdr, const Lane& l, uint32_t& scp, uint32_t& mp) {
+    const uint32_t H1 = hdr.y, H2 = hdr.z, H3 = hdr.w;
+    const uint32_t Xs = l.lo ? H1 : H3, Xm = l.lo ? H2 : H3;
+    scp = ((Xs >> l.sh) & l.maskA) | ((H1 >> (l.sh + 2)) & l.maskB);
+    mp = ((Xm >> l.shm) & l.maskA) | ((H2 >> (l.sh + 2)) & l.maskB);
   }
 
   __device__ static void nibble_dots(const Dec& o, const Act& a, int& dot0, int& dot1) {

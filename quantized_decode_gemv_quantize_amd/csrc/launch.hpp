@@ -178,4 +178,7 @@ const Dispatch& dispatch_q6_k_f32();
 
 int launch_quantize_q8_1(const float* x, uint8_t* y, int64_t K, int64_t n, int64_t ldx, hipStream_t st);
 
+struct MmqArgs;
+int launch_mmq_q4k(const MmqArgs& a, hipStream_t st);
+
 }  // namespace qmv

@@ -56,7 +56,9 @@ P16, P4 = 1 << 20, (1 << 20) + 4
     ((P16, B.Q8_0, 1, 32 * 513, P16, 1, P16), B.ERR_SHAPE),
     ((P16, B.Q4_K, 0, 256, P16, 1, P16), B.ERR_SHAPE),
     ((P16, B.Q4_K, 1, 256, P16, 0, P16), B.ERR_SHAPE),
-    ((P16, B.Q4_K, 1, 256, P16, 9, P16), B.ERR_SHAPE),
+    ((P16, B.Q4_K, 1, 256, P16, 257, P16), B.ERR_SHAPE),
+    ((P16, B.Q4_0, 1, 256, P16, 9, P16), B.ERR_SHAPE),
+    ((P16, B.Q6_K, 1, 256, P16, 9, P16), B.ERR_SHAPE),
     ((P16, B.Q4_K, 1, 256 * 65, P16, 1, P16), B.ERR_SHAPE),
     ((P16, B.Q6_K, 1, 256 * 129, P16, 1, P16), B.ERR_SHAPE),
     ((P4, B.Q4_K, 1, 256, P16, 1, P16), B.ERR_ALIGN),
@@ -83,7 +85,7 @@ def test_other_entry_points_argument_checks(L):
     assert L.mmvq_quantize_q8_1(None, 32, 1, 32, P16, None) == B.ERR_NULL
     assert L.mmvq_quantize_q8_1(P16, 33, 1, 33, P16, None) == B.ERR_SHAPE
     assert L.mmvq_quantize_q8_1(P16, 32, 1, 16, P16, None) == B.ERR_SHAPE
-    assert L.mmvq_quantize_q8_1(P16, 32, 9, 32, P16, None) == B.ERR_SHAPE
+    assert L.mmvq_quantize_q8_1(P16, 32, 257, 32, P16, None) == B.ERR_SHAPE
     assert L.mmvq_quantize_q8_1(P16 + 2, 32, 1, 32, P16, None) == B.ERR_ALIGN
     assert L.mmvq_quantize_q8_1(P16, 32, 1, 32, P4, None) == B.ERR_ALIGN
 

@@ -258,7 +258,7 @@ def test_abi_errors_on_device():
     assert L.mmvq(p + 4, Q4_K, 1, 256, q, 1, o, s) == B.ERR_ALIGN
     assert L.mmvq(p, Q4_K, 1, 256, q + 4, 1, o, s) == B.ERR_ALIGN
     assert L.mmvq(p, Q4_K, 1, 256, q, 0, o, s) == B.ERR_SHAPE
-    assert L.mmvq(p, Q4_K, 1, 256, q, 9, o, s) == B.ERR_SHAPE
+    assert L.mmvq(p, Q4_K, 1, 256, q, 257, o, s) == B.ERR_SHAPE
     assert L.mmvq(p, Q4_K, 0, 256, q, 1, o, s) == B.ERR_SHAPE
     assert L.mmvq(p, 3, 1, 256, q, 1, o, s) == B.ERR_TYPE
     assert L.mmvq_glu(p, p, Q4_K, 1, 256, q, 1, 7, o, s) == B.ERR_TYPE
