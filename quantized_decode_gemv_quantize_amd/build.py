@@ -36,6 +36,14 @@ HIPCC_FLAGS = [
 ]
 
 
+# Per-source flags. The many-column kernel keeps its matrix-core results in
+# ordinary vector registers (the scale arithmetic reads every result; in
+# accumulation registers each value would first be copied out).
+SOURCE_FLAGS = {
+    "kernels_mmq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -45,7 +53,7 @@ def hipcc() -> str:
 
 def _compile(src: str, extra: list[str]) -> str:
     obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stderr}")

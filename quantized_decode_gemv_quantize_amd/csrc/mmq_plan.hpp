@@ -22,61 +22,55 @@ struct MmqArgs {
   int nsb;                   // super-blocks per row
 };
 
-constexpr int kMmqWaves = 4;
+// First super-block of wave w's share of the K range when nw waves split it
+// (w = 0..nw).
+__host__ __device__ __forceinline__ int mmq_sb_begin(int nsb, int w, int nw) { return (nsb * w) / nw; }
 
-// First super-block of wave w's share of the K range (w = 0..kMmqWaves).
-__host__ __device__ __forceinline__ int mmq_sb_begin(int nsb, int w) { return (nsb * w) / kMmqWaves; }
+// Staging loads of super-block sb: every load is a 16-byte piece of a
+// contiguous run, so a wave's loads cover whole cache lines. A: the 16 rows'
+// 144-byte super-blocks of each row tile (144 pieces, row = k / 9); B: the
+// 16 columns' 8 q8_1 blocks of each column tile (a 288-byte run per column,
+// 288 pieces, column = k / 18). Lane L takes pieces L, L + 64, ...; pieces
+// past the end are not loaded. The kernel stores them to LDS and reads the
+// MFMA operands from there.
+constexpr int kMmqAPieces = 144, kMmqBPieces = 288;
+constexpr int kMmqAPerLane = (kMmqAPieces + kWave - 1) / kWave;   // 3
+constexpr int kMmqBPerLane = (kMmqBPieces + kWave - 1) / kWave;   // 5
 
-// Operand pointers of one lane: A rows row_base + 16*rt + r16 (clamped to the
-// matrix: rows past M are loaded but never stored) and B columns
-// col_base + 16*ct + r16 (clamped: columns past n contribute zero).
 template <int RT, int CT>
-__device__ __forceinline__ void mmq_pointers(const MmqArgs& a, int64_t row_base, int col_base, int r16,
-                                             const uint8_t* (&arow)[RT], const uint8_t* (&bcol)[CT],
-                                             bool (&bvalid)[CT]) {
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    int64_t r = row_base + 16 * rt + r16;
-    r = r < a.M ? r : a.M - 1;
-    arow[rt] = a.W + r * a.row_bytes;
-  }
-#pragma unroll
-  for (int ct = 0; ct < CT; ++ct) {
-    const int c = col_base + 16 * ct + r16;
-    bvalid[ct] = c < a.n;
-    bcol[ct] = a.y + static_cast<int64_t>(bvalid[ct] ? c : a.n - 1) * a.ycol_bytes;
-  }
-}
-
-// Loads of super-block sb for a lane of k-slice q: the row headers, the
-// 8 code bytes of each 64-element chunk at offset 8q (low nibbles feed
-// sub-block 2c, high nibbles 2c+1), and the q8_1 codes 8q..8q+7 and fp16 d
-// of the 8 blocks of each column.
-template <int RT, int CT>
-struct MmqQ4KLoads {
-  u32x4 hdr[RT];
-  u32x2 qs[RT][4];
-  u32x2 yq[CT][8];
-  uint32_t yd[CT][8];
+struct MmqStage {
+  u32x4 a[RT][kMmqAPerLane];
+  u32x4 b[CT][kMmqBPerLane];
 };
 
+// Piece pointers of a lane: rows of the row tiles and columns of the column
+// tiles, clamped to the matrix and to n (clamped rows and columns are read
+// and computed, never stored; each output column depends only on its own).
 template <int RT, int CT>
-__device__ __forceinline__ void mmq_q4k_load(const uint8_t* const (&arow)[RT], const uint8_t* const (&bcol)[CT],
-                                             int sb, int q, MmqQ4KLoads<RT, CT>& ld) {
-  const int64_t boff = static_cast<int64_t>(sb) * Q4K::kBlockBytes;
+__device__ __forceinline__ void mmq_stage_load(const MmqArgs& a, int64_t row_base, int col_base, int lane, int sb,
+                                               MmqStage<RT, CT>& st) {
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    ld.hdr[rt] = ld_x4(arow[rt] + boff);
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) ld.qs[rt][c] = ld_x2(arow[rt] + (boff + 16 + 32 * c + 8 * q));
-  }
+    for (int j = 0; j < kMmqAPerLane; ++j) {
+      const int k = lane + kWave * j;
+      if (k < kMmqAPieces) {
+        int64_t r = row_base + 16 * rt + k / 9;
+        r = r < a.M ? r : a.M - 1;
+        st.a[rt][j] = ld_a16_x4(a.W + (r * a.row_bytes + static_cast<int64_t>(sb) * 144 + 16 * (k % 9)));
+      }
+    }
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const uint8_t* b = bcol[ct] + static_cast<int64_t>(8 * sb + t) * kQ8Bytes;
-      ld.yq[ct][t] = ld_x2(b + 4 + 8 * q);
-      ld.yd[ct][t] = ld_u16(b);
+    for (int j = 0; j < kMmqBPerLane; ++j) {
+      const int k = lane + kWave * j;
+      if (k < kMmqBPieces) {
+        int c = col_base + 16 * ct + k / 18;
+        c = c < a.n ? c : a.n - 1;
+        st.b[ct][j] = ld_a16_x4(a.y + (static_cast<int64_t>(c) * a.ycol_bytes + static_cast<int64_t>(sb) * 288 +
+                                       16 * (k % 18)));
+      }
     }
 }
 

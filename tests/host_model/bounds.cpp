@@ -198,7 +198,7 @@ static void case_block_dots(const char* name, int64_t M, int64_t K, int nc) {
 
 // many-column (MFMA) kernel, Q4_K: every load of every lane, wave and
 // super-block; every output stored exactly once.
-template <int RT, int CT>
+template <int RT, int CT, int NW>
 static void case_mmq(int64_t M, int64_t K, int n) {
   const int64_t row_bytes = K / 256 * 144, ycol = K / 32 * kQ8Bytes;
   uint8_t* W = alloc16(M * row_bytes);
@@ -213,19 +213,17 @@ static void case_mmq(int64_t M, int64_t K, int n) {
   bool ok = true;
   for (int64_t bx = 0; bx < gx; ++bx)
     for (int by = 0; by < gy; ++by)
-      for (int wave = 0; wave < kMmqWaves; ++wave)
+      for (int wave = 0; wave < NW; ++wave)
         for (int lane = 0; lane < 64; ++lane) {
           const int r16 = lane & 15, q = lane >> 4;
           const int64_t row_base = bx * 16 * RT;
           const int col_base = by * 16 * CT;
-          const uint8_t* arow[RT];
-          const uint8_t* bcol[CT];
-          bool bvalid[CT];
-          mmq_pointers<RT, CT>(a, row_base, col_base, r16, arow, bcol, bvalid);
-          MmqQ4KLoads<RT, CT> ld;
-          for (int sb = mmq_sb_begin(a.nsb, wave); sb < mmq_sb_begin(a.nsb, wave + 1); ++sb)
-            mmq_q4k_load<RT, CT>(arow, bcol, sb, q, ld);
-          for (int v = wave; v < RT * CT * 4; v += kMmqWaves) {
+          MmqStage<RT, CT> st;
+          const int sb0 = mmq_sb_begin(a.nsb, wave, NW), sb1 = mmq_sb_begin(a.nsb, wave + 1, NW);
+          if (sb0 < sb1) mmq_stage_load<RT, CT>(a, row_base, col_base, lane, sb0, st);
+          for (int sb = sb0; sb < sb1; ++sb)
+            mmq_stage_load<RT, CT>(a, row_base, col_base, lane, sb + 1 < sb1 ? sb + 1 : sb, st);
+          for (int v = wave; v < RT * CT * 4; v += NW) {
             int64_t r;
             int c;
             mmq_store_pos<RT, CT>(v, q, r16, row_base, col_base, r, c);
@@ -310,8 +308,16 @@ int main(int argc, char** argv) {
   }
   for (int64_t M : {1, 15, 16, 17, 33, 100})
     for (int64_t K : {256, 512, 768, 1024, 1280})
-      for (int n : {9, 16, 17, 31, 32, 33, 64, 100}) case_mmq<2, 2>(M, K, n);
-  case_mmq<2, 2>(300, 4096, 256);
+      for (int n : {9, 16, 17, 31, 32, 33, 64, 100}) {
+        case_mmq<2, 2, 4>(M, K, n);
+        case_mmq<2, 2, 8>(M, K, n);
+        case_mmq<2, 1, 4>(M, K, n);
+        case_mmq<2, 1, 8>(M, K, n);
+        case_mmq<1, 1, 4>(M, K, n);
+        case_mmq<1, 1, 8>(M, K, n);
+      }
+  case_mmq<2, 2, 4>(300, 4096, 256);
+  case_mmq<1, 1, 8>(300, 4096, 256);
   for (int64_t K : {32, 64, 96, 1024, 14336})
     for (int64_t n : {1, 3, 8})
       for (int64_t pad : {0, 1, 3, 64}) case_quantize(K, n, K + pad);
@@ -327,8 +333,10 @@ int main(int argc, char** argv) {
     case_rows<Q80>("q8_0", 4096, 14336, 1, 1, 0);
     case_rows<Q6K>("q6_k", 128256, 4096, 1, 1);
     case_id<Q4K>("q4_k", 14336, 4096, 8, 8, 2);
-    case_mmq<2, 2>(4096, 14336, 64);
-    case_mmq<2, 2>(14336, 4096, 32);
+    case_mmq<2, 2, 4>(4096, 14336, 64);
+    case_mmq<2, 1, 8>(4096, 14336, 16);
+    case_mmq<1, 1, 8>(4096, 14336, 16);
+    case_mmq<2, 2, 8>(14336, 4096, 32);
     case_id<Q4K>("q4_k", 14336, 4096, 8, 8, 1);
   }
   printf("host model: %d failing case(s)\n", failures);

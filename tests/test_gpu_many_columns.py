@@ -34,8 +34,12 @@ def _nan(rows, M):
     return torch.full((rows, M), float("nan"), dtype=torch.float32, device="cuda:0")
 
 
+# The launch picks its tile and wave count from the grid size; on a 256-CU
+# part the last four shapes take 2x2 tiles with 4 waves, 2x1 with 4, 2x1
+# with 8 and 1x1 with 4 (the others 1x1 with 8; the workload test 2x2 with 8).
 SHAPES = [(1, 256, 9), (37, 512, 16), (300, 2304, 17), (1000, 4096, 33), (129, 14336, 64),
-          (65, 16384, 100), (33, 768, 256), (17, 1280, 31)]
+          (65, 16384, 100), (33, 768, 256), (17, 1280, 31),
+          (9000, 256, 32), (9000, 512, 16), (8192, 256, 9), (5000, 256, 16)]
 
 
 @pytest.mark.parametrize("M,K,n", SHAPES, ids=[f"{m}x{k}-n{n}" for m, k, n in SHAPES])
