@@ -218,11 +218,13 @@ static void case_mmq(int64_t M, int64_t K, int n) {
           const int r16 = lane & 15, q = lane >> 4;
           const int64_t row_base = bx * 16 * RT;
           const int col_base = by * 16 * CT;
+          MmqOffsets<RT, CT> off;
+          mmq_offsets<RT, CT>(a, row_base, col_base, lane, off);
           MmqStage<RT, CT> st;
           const int sb0 = mmq_sb_begin(a.nsb, wave, NW), sb1 = mmq_sb_begin(a.nsb, wave + 1, NW);
-          if (sb0 < sb1) mmq_stage_load<RT, CT>(a, row_base, col_base, lane, sb0, st);
+          if (sb0 < sb1) mmq_stage_load<RT, CT>(a, row_base, col_base, lane, sb0, off, st);
           for (int sb = sb0; sb < sb1; ++sb)
-            mmq_stage_load<RT, CT>(a, row_base, col_base, lane, sb + 1 < sb1 ? sb + 1 : sb, st);
+            mmq_stage_load<RT, CT>(a, row_base, col_base, lane, sb + 1 < sb1 ? sb + 1 : sb, off, st);
           for (int v = wave; v < RT * CT * 4; v += NW) {
             int64_t r;
             int c;
