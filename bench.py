@@ -65,16 +65,23 @@ def parse():
     return p.parse_args()
 
 
+# What the measured Q4_K mat-vec kernels (q8_1 and fp32 activations) are
+# built from: their translation units, the headers they include and the
+# compile flags.
+HEADLINE_SOURCES = ["common.hpp", "q8.hpp", "formats.hpp", "plan.hpp", "mmvq_kernel.hpp", "launch.hpp",
+                    "kernels_q4_k.hip", "kernels_q4_k_f32.hip", os.path.join("..", "..", "include", "mmvq.h")]
+
+
 def kernel_source_hash() -> str:
-    """sha256 over the HIP sources and build flags: counters taken on one
-    kernel build are reported only while the sources are unchanged."""
+    """sha256 over the sources and compile flags of the measured kernels:
+    counters taken on one build are reported only while these are unchanged."""
     import hashlib
+    from quantized_decode_gemv_quantize_amd import build as qbuild
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in HEADLINE_SOURCES:
         with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
-    with open(os.path.join(ROOT, "quantized_decode_gemv_quantize_amd", "build.py"), "rb") as f:
-        h.update(f.read())
+            h.update(os.path.basename(name).encode() + b"\0" + f.read())
+    h.update(" ".join(qbuild.HIPCC_FLAGS).encode())
     return h.hexdigest()[:16]
 
 
@@ -454,7 +461,8 @@ def main():
         del a, b
 
     res, data, Ws, y, out = time_workload(torch, B, wl, n, args.steps, args.warmup)
-    fused = args.step == "fused"
+    # the fused forms take at most 8 columns; beyond that a step is the two launches
+    fused = args.step == "fused" and res["fused_us"] is not None
     step_us = res["fused_us"] if fused else res["step_us"]
     step_ms = step_us / 1e3
     value = wl.weight_bytes / (step_us * 1e-6) / 1e9
@@ -470,7 +478,8 @@ def main():
         cpu = cpu_baseline(wl, data, n, args.cpu_seconds)
 
     line = {
-        "metric": "Q4_K GEMV effective weight GB/s (% of HBM peak) at 4096x14336, n=1",
+        "metric": f"{synth.TYPE_NAME[wl.wtype].upper()} GEMV effective weight GB/s (% of HBM peak) "
+                  f"at {wl.M}\u00d7{wl.K}, n={n}",
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -488,7 +497,7 @@ def main():
         "detail": {
             "step_form": "one fused launch (mmvq_f32)" if fused else "quantize + mat-vec launches",
             "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-            "fused_us": round(res["fused_us"], 3),
+            "fused_us": None if res["fused_us"] is None else round(res["fused_us"], 3),
             "gemv_us": round(res["gemv_us"], 3),
             "quantize_us": round(res["quant_us"], 3),
             "two_launch_step_us": round(res["step_us"], 3),
@@ -499,8 +508,12 @@ def main():
         },
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("fused" if fused else "gemv"),
-                     "kernel": f"mmvq_rows_kernel (Q4_K, n=1, {'fp32' if fused else 'q8_1'} activation)",
+                     "traffic": (measured_traffic("fused" if fused else "gemv")
+                                 if wl.name == "q4_k_4096x14336" and n == 1 else None),
+                     "kernel": (f"mmq_q4k_kernel ({synth.TYPE_NAME[wl.wtype].upper()}, n={n}, int8 matrix cores)"
+                                if n > 8 else
+                                f"mmvq_rows_kernel ({synth.TYPE_NAME[wl.wtype].upper()}, n={n}, "
+                                f"{'fp32' if fused else 'q8_1'} activation)"),
                      "bytes_per_launch": kern_bytes,
                      "avg_launch_us": round(kern_us, 3)},
         "cpu_baseline": cpu,
