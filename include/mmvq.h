@@ -145,7 +145,12 @@ int mmvq_quantize_q8_1(const float *x, int64_t K, int64_t n, int64_t ldx,
  * sub-block t, d*sc_t*d8*sum(q*qy) - dmin*m_t*d8*sum(qy). Q6_K: per
  * 16-element sub-block, d*sc*d8*sum((q-32)*qy). Accumulated in fp32.
  * Requires K % qk == 0, M >= 1 and 1 <= n <= MMVQ_MAX_COLS, or for Q4_K
- * 1 <= n <= MMVQ_MAX_COLS_BATCH: n > 8 takes the many-column path, where
+ * 1 <= n <= MMVQ_MAX_COLS_BATCH. For n <= MMVQ_MAX_COLS one row must fit
+ * a team of at most 512 lanes: K <= 16384 for Q4_0 and Q8_0 (a block per
+ * lane), K <= 32768 for Q4_K (64 weights per lane) and Q6_K (a quarter
+ * super-block per lane); longer rows return MMVQ_ERR_SHAPE (the same limits
+ * hold for every entry point below except the many-column path).
+ * n > 8 takes the many-column path, where
  * the integer dots of 16 rows x 16 columns x 32 elements come from one int8
  * matrix-core instruction and the same scales are applied per sub-block
  * (no upper bound on K there). */

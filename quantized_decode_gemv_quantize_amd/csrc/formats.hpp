@@ -251,6 +251,176 @@ struct Q4K {
 };
 
 // ===========================================================================
+// Q4_K with one whole 64-weight chunk per lane (the mat-vec and expert
+// kernels; the half-chunk layout above serves the many-column kernel's scale
+// unpack and the block-dot test kernel's reference layout).
+// Unit u: super-block sb = u/4, chunk c = u%4: the 32 code bytes
+// qs[32c .. 32c+31] hold sub-blocks t0 = 2c (low nibbles) and t1 = 2c+1
+// (high nibbles) whole. A lane loads its super-block's 16-byte header beside
+// its two 16-byte code loads, so one header load serves 64 weights, and the
+// scale arithmetic of a column dot is shared by 64 weights (32 in the
+// half-chunk layout). A wave's 64 lanes read 16 super-blocks' codes.
+// ===========================================================================
+struct Q4K2 {
+  static constexpr int kType = 12, kQK = 256, kBlockBytes = 144;
+  static constexpr int kUnitsPerBlock = 4, kDotsPerBlock = 16;
+
+  struct Act {
+    uint32_t y0[8], y1[8];   // codes of q8_1 blocks t0 and t1
+    float d0, d1;            // their scales
+    float s0, s1;            // d8 * (sum of the 32 codes): exact in fp32
+  };
+
+  __device__ static void act_blocks(const uint8_t* ycol, int u, const uint8_t*& b0, const uint8_t*& b1) {
+    b0 = ycol + static_cast<int64_t>(8 * (u >> 2) + 2 * (u & 3)) * kQ8Bytes;
+    b1 = b0 + kQ8Bytes;
+  }
+
+  __device__ static int sum8(const uint32_t (&q)[8]) {
+    int s = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s = bsum4(q[k], s);
+    return s;
+  }
+
+  __device__ static void issue_act(Act& a, const uint8_t* ycol, int u) {
+    const uint8_t *b0, *b1;
+    act_blocks(ycol, u, b0, b1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const u32x4 p0 = ld_x4(b0 + 4 + 16 * h), p1 = ld_x4(b1 + 4 + 16 * h);
+      a.y0[4 * h] = p0.x; a.y0[4 * h + 1] = p0.y; a.y0[4 * h + 2] = p0.z; a.y0[4 * h + 3] = p0.w;
+      a.y1[4 * h] = p1.x; a.y1[4 * h + 1] = p1.y; a.y1[4 * h + 2] = p1.z; a.y1[4 * h + 3] = p1.w;
+    }
+    a.d0 = __uint_as_float(ld_u16(b0));
+    a.d1 = __uint_as_float(ld_u16(b1));
+  }
+
+  __device__ static void finish_act(Act& a) {
+    a.d0 = h2f(__float_as_uint(a.d0));
+    a.d1 = h2f(__float_as_uint(a.d1));
+    a.s0 = a.d0 * static_cast<float>(sum8(a.y0));
+    a.s1 = a.d1 * static_cast<float>(sum8(a.y1));
+  }
+
+  __device__ static void load_act(Act& a, const uint8_t* ycol, int u) {
+    issue_act(a, ycol, u);
+    finish_act(a);
+  }
+
+  // fp32 activations: the lane holds both of its q8_1 blocks whole (32
+  // values each), so each block's amax needs no exchange with other lanes.
+  struct XRaw {
+    u32x4 r0[8], r1[8];
+  };
+  static constexpr int kXWords = 64;
+
+  __device__ static void load_x(XRaw& x, const float* xcol, int u) {
+    const float* x0 = xcol + static_cast<int64_t>(8 * (u >> 2) + 2 * (u & 3)) * 32;
+    const float* x1 = x0 + 32;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      x.r0[k] = ld_x4(reinterpret_cast<const uint8_t*>(x0 + 4 * k));
+      x.r1[k] = ld_x4(reinterpret_cast<const uint8_t*>(x1 + 4 * k));
+    }
+  }
+
+  __device__ static void quant_x(Act& a, const XRaw& x) {
+    float m0 = absmax4(x.r0[0]), m1 = absmax4(x.r1[0]);
+#pragma unroll
+    for (int k = 1; k < 8; ++k) {
+      m0 = fmaxf(m0, absmax4(x.r0[k]));
+      m1 = fmaxf(m1, absmax4(x.r1[k]));
+    }
+    const float d0 = q8_scale(m0), d1 = q8_scale(m1);
+    int s0 = 0, s1 = 0;
+    q8_quant_block(x.r0, d0, a.y0, s0);
+    q8_quant_block(x.r1, d1, a.y1, s1);
+    a.d0 = q8_d_rounded(d0);
+    a.d1 = q8_d_rounded(d1);
+    a.s0 = a.d0 * static_cast<float>(s0);
+    a.s1 = a.d1 * static_cast<float>(s1);
+  }
+
+  __device__ static void zero_act(Act& a) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) { a.y0[k] = 0; a.y1[k] = 0; }
+    a.d0 = a.d1 = a.s0 = a.s1 = 0.0f;
+  }
+
+  // the half-chunk lane of the chunk's first half: same header offset, the
+  // chunk's first code byte, the same scale unpack
+  using Lane = Q4K::Lane;
+  __device__ static Lane lane(int u) { return Q4K::lane(8 * (u >> 2) + 2 * (u & 3)); }
+
+  struct Wt {
+    u32x4 hdr;   // d | dmin, scales[0..3], scales[4..7], scales[8..11]
+    u32x4 qs0, qs1;
+  };
+
+  __device__ static void load_wt(Wt& w, const uint8_t* row, uint32_t extra, const Lane& l) {
+    w.hdr = ld_x4(row + (extra + l.hoff));
+    w.qs0 = ld_a16_x4(row + (extra + l.qoff));
+    w.qs1 = ld_a16_x4(row + (extra + l.qoff + 16));
+  }
+
+  struct Dec {
+    uint32_t lo[8], hi[8];   // nibbles of t0 and t1 as unsigned bytes
+    uint32_t scp;            // sc of t0 (byte 0) and t1 (byte 1)
+    float m0, m1, d, dmin;
+  };
+
+  __device__ static void decode(const Wt& w, Dec& o, const Lane& l) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      o.lo[k] = w.qs0[k] & 0x0F0F0F0Fu;
+      o.hi[k] = (w.qs0[k] >> 4) & 0x0F0F0F0Fu;
+      o.lo[4 + k] = w.qs1[k] & 0x0F0F0F0Fu;
+      o.hi[4 + k] = (w.qs1[k] >> 4) & 0x0F0F0F0Fu;
+    }
+    o.d = h2f(w.hdr.x);
+    o.dmin = h2f(w.hdr.x >> 16);
+    uint32_t mp;
+    Q4K::chunk_scales(w.hdr, l, o.scp, mp);
+    o.m0 = static_cast<float>(mp & 0xFFu);
+    o.m1 = static_cast<float>((mp >> 8) & 0xFFu);
+  }
+
+  __device__ static void nibble_dots(const Dec& o, const Act& a, int& dot0, int& dot1) {
+    dot0 = 0;
+    dot1 = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      dot0 = dot4(o.lo[k], a.y0[k], dot0);
+      dot1 = dot4(o.hi[k], a.y1[k], dot1);
+    }
+  }
+
+  // d * (sc0*d8_0*dot0 + sc1*d8_1*dot1) - dmin * (m0*d8_0*S0 + m1*d8_1*S1)
+  __device__ static float col_dot(const Dec& o, const Act& a) {
+    int dot0, dot1;
+    nibble_dots(o, a, dot0, dot1);
+    const int sc0 = static_cast<int>(o.scp & 0xFFu), sc1 = static_cast<int>((o.scp >> 8) & 0xFFu);
+    const float sd = fmaf(static_cast<float>(mul24(dot0, sc0)), a.d0, static_cast<float>(mul24(dot1, sc1)) * a.d1);
+    const float sm = fmaf(o.m0, a.s0, o.m1 * a.s1);
+    return fmaf(o.d, sd, -(o.dmin * sm));
+  }
+
+  // dots of one super-block: [dot1 of t = 0..7, sum(qy) of t = 0..7]
+  __device__ static void int_dots(const Dec& o, const uint8_t* ycol, int u, int* dots) {
+    Act a;
+    load_act(a, ycol, u);
+    int dot0, dot1;
+    nibble_dots(o, a, dot0, dot1);
+    const int c = u & 3;
+    dots[2 * c] += dot0;
+    dots[2 * c + 1] += dot1;
+    dots[8 + 2 * c] += sum8(a.y0);
+    dots[8 + 2 * c + 1] += sum8(a.y1);
+  }
+};
+
+// ===========================================================================
 // Q4_0  [MMVQ §权重的排法, §一次 vec_dot 的解剖]
 // 18 bytes: fp16 d @0, qs[16] @2; qs[j] low nibble = element j, high nibble
 // = element j+16. Weight = d*(q-8); per block the product is

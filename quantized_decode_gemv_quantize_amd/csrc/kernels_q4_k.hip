@@ -4,7 +4,7 @@
 namespace qmv {
 
 const Dispatch& dispatch_q4_k() {
-  static const Dispatch d = make_dispatch<Q4K, false>();
+  static const Dispatch d = make_dispatch_q4k<false>();
   return d;
 }
 

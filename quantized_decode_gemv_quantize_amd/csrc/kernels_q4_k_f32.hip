@@ -5,7 +5,7 @@
 namespace qmv {
 
 const Dispatch& dispatch_q4_k_f32() {
-  static const Dispatch d = make_dispatch<Q4K, true>();
+  static const Dispatch d = make_dispatch_q4k<true>();
   return d;
 }
 

@@ -167,6 +167,36 @@ Dispatch make_dispatch() {
   return d;
 }
 
+// Q4_K has two lane layouts: half chunks (Q4K: 32 weights per lane) and
+// whole chunks (Q4K2: 64). The fp32-activation forms must equal quantize +
+// q8_1 form bit for bit, so both forms of a call take the same layout:
+//  * mat-vec (rows kernels): half chunks, whole chunks only for rows longer
+//    than a team of half-chunk lanes holds. Whole chunks make the q8_1 form
+//    faster at one column (14336x4096: 8.6 -> 7.9 us) but the fused form
+//    slower (9.5 -> 11.2 us: twice the teams or row slots, each quantizing
+//    the whole activation), and the fused form is the faster step;
+//  * expert kernels: whole chunks (8-expert gate/up, q8_1 activations:
+//    122 -> 107 us; the fused form 162 -> 198 us, where the two-launch form
+//    is the faster step either way: every expert block re-quantizes its
+//    tokens).
+// The row limit is the whole-chunk one.
+constexpr int64_t kQ4KHalfMaxK = static_cast<int64_t>(kLaunchBound) / Q4K::kUnitsPerBlock * Q4K::kQK;
+
+template <bool XF>
+Dispatch make_dispatch_q4k() {
+  Dispatch d = make_dispatch<Q4K, XF>();
+  d.rows = [](const RowArgs& a, int64_t K, int64_t n, hipStream_t s) {
+    return K > kQ4KHalfMaxK ? launch_rows<Q4K2, XF, 1>(a, K, n, s) : launch_rows<Q4K, XF, 1>(a, K, n, s);
+  };
+  d.rows_glu = [](const RowArgs& a, int64_t K, int64_t n, hipStream_t s) {
+    return K > kQ4KHalfMaxK ? launch_rows<Q4K2, XF, 2>(a, K, n, s) : launch_rows<Q4K, XF, 2>(a, K, n, s);
+  };
+  d.id = [](const RowArgs& a, int64_t K, int e, hipStream_t s) { return launch_id<Q4K2, XF, 1>(a, K, e, s); };
+  d.id_glu = [](const RowArgs& a, int64_t K, int e, hipStream_t s) { return launch_id<Q4K2, XF, 2>(a, K, e, s); };
+  d.units_per_block = Q4K2::kUnitsPerBlock;
+  return d;
+}
+
 const Dispatch& dispatch_q4_0();
 const Dispatch& dispatch_q8_0();
 const Dispatch& dispatch_q4_k();

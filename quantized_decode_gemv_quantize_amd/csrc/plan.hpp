@@ -60,6 +60,8 @@ template <class F>
 constexpr int rows_per_pass(int nc, int g) {
   int r = 1;
   if (F::kType == 14) r = nc == 1 ? 8 : (nc == 2 ? 4 : (nc <= 4 ? 2 : 1));   // Q6_K: 19 + 24n words
+  else if (F::kType == 12 && F::kUnitsPerBlock == 4)
+    r = nc == 1 ? 8 : (nc <= 4 ? 4 : 2);                                      // Q4_K whole chunks: 12 + 20n words
   else if (F::kType == 12) r = nc == 1 ? 16 : (nc <= 4 ? 8 : 4);              // Q4_K: 8 + 12n words
   else r = nc == 1 ? 16 : (nc <= 4 ? 8 : 4);                                 // Q4_0: 5 + 10n words
   return g == 2 ? (r > 1 ? r / 2 : 1) : r;

@@ -266,6 +266,7 @@ int main(int argc, char** argv) {
           for (int xpad : {-1, 3}) {
             if (nb <= 16 || nc <= 2) {
               case_rows<Q4K>("q4_k", M, 256LL * nb, nc, g, xpad);
+              case_rows<Q4K2>("q4_k2", M, 256LL * nb, nc, g, xpad);
               case_rows<Q6K>("q6_k", M, 256LL * nb, nc, g, xpad);
             }
             if (nb * 8 * 32 <= 16384 && (nb <= 16 || nc <= 2))
@@ -279,6 +280,7 @@ int main(int argc, char** argv) {
       }
       if (M <= 64) {
         case_block_dots<Q4K>("q4_k", M, 256LL * nb, 2);
+        case_block_dots<Q4K2>("q4_k2", M, 256LL * nb, 2);
         case_block_dots<Q6K>("q6_k", M, 256LL * nb, 2);
         case_block_dots<Q40>("q4_0", M, 32LL * nb, 2);
         case_block_dots<Q80>("q8_0", M, 32LL * nb, 2);
@@ -288,20 +290,29 @@ int main(int argc, char** argv) {
   // longest rows a team can hold
   for (int xpad : {-1, 1}) {
     case_rows<Q4K>("q4_k", 129, 16384, 1, 1, xpad);
+    case_rows<Q4K2>("q4_k2", 129, 16384, 1, 1, xpad);
+    case_rows<Q4K2>("q4_k2", 33, 32768, 1, 1, xpad);
+    case_rows<Q4K2>("q4_k2", 33, 32768, 8, 2, xpad);
     case_rows<Q4K>("q4_k", 65, 16384, 8, 1, xpad);
+    case_rows<Q4K2>("q4_k2", 65, 16384, 8, 1, xpad);
     case_rows<Q4K>("q4_k", 65, 16384, 1, 2, xpad);
+    case_rows<Q4K2>("q4_k2", 65, 16384, 1, 2, xpad);
     case_rows<Q40>("q4_0", 129, 16384, 8, 2, xpad);
     case_rows<Q80>("q8_0", 129, 16384, 8, 2, xpad);
     case_rows<Q80>("q8_0", 33, 16384, 1, 1, xpad);
     case_rows<Q6K>("q6_k", 129, 32768, 1, 1, xpad);
     for (int g = 1; g <= 2; ++g) {
       case_id<Q4K>("q4_k", 200, 512, 4, 3, g, xpad);
+      case_id<Q4K2>("q4_k2", 200, 512, 4, 3, g, xpad);
       case_id<Q4K>("q4_k", 300, 2048, 8, 8, g, xpad);
+      case_id<Q4K2>("q4_k2", 300, 2048, 8, 8, g, xpad);
       case_id<Q40>("q4_0", 77, 1024, 5, 4, g, xpad);
       case_id<Q6K>("q6_k", 50, 768, 4, 2, g, xpad);
       case_id<Q4K>("q4_k", 1, 256, 3, 1, g, xpad);
+      case_id<Q4K2>("q4_k2", 1, 256, 3, 1, g, xpad);
       for (int T : {1, 2, 3, 5, 8}) {
         case_id<Q4K>("q4_k", 77, 1024, 2, T, g, xpad);
+        case_id<Q4K2>("q4_k2", 77, 1024, 2, T, g, xpad);
         case_id<Q6K>("q6_k", 33, 512, 2, T, g, xpad);
         case_id<Q40>("q4_0", 300, 512, 2, T, g, xpad);
         case_id<Q80>("q8_0", 45, 96, 3, T, g, xpad);
@@ -326,20 +337,26 @@ int main(int argc, char** argv) {
   if (full) {   // the benchmark workloads
     for (int nc : {1, 2, 4, 8}) {
       case_rows<Q4K>("q4_k", 4096, 14336, nc, 1);
+      case_rows<Q4K2>("q4_k2", 4096, 14336, nc, 1);
       case_rows<Q4K>("q4_k", 14336, 4096, nc, 1);
+      case_rows<Q4K2>("q4_k2", 14336, 4096, nc, 1);
       case_rows<Q4K>("q4_k", 4096, 14336, nc, 1, 0);
+      case_rows<Q4K2>("q4_k2", 4096, 14336, nc, 1, 0);
     }
     case_rows<Q4K>("q4_k", 4096, 4096, 1, 1);
+    case_rows<Q4K2>("q4_k2", 4096, 4096, 1, 1);
     case_rows<Q40>("q4_0", 256, 1024, 1, 1);
     case_rows<Q80>("q8_0", 4096, 14336, 1, 1);
     case_rows<Q80>("q8_0", 4096, 14336, 1, 1, 0);
     case_rows<Q6K>("q6_k", 128256, 4096, 1, 1);
     case_id<Q4K>("q4_k", 14336, 4096, 8, 8, 2);
+    case_id<Q4K2>("q4_k2", 14336, 4096, 8, 8, 2);
     case_mmq<2, 2, 4>(4096, 14336, 64);
     case_mmq<2, 1, 8>(4096, 14336, 16);
     case_mmq<1, 1, 8>(4096, 14336, 16);
     case_mmq<2, 2, 8>(14336, 4096, 32);
     case_id<Q4K>("q4_k", 14336, 4096, 8, 8, 1);
+    case_id<Q4K2>("q4_k2", 14336, 4096, 8, 8, 1);
   }
   printf("host model: %d failing case(s)\n", failures);
   return failures ? 1 : 0;

@@ -54,7 +54,8 @@ def _same(a, b, what):
 
 FUSED_CASES = [(Q4_0, 37, 96, 1, 0), (Q4_0, 300, 1024, 3, 5), (Q4_0, 129, 16384, 8, 1),
                (Q4_K, 1, 256, 1, 0), (Q4_K, 37, 512, 2, 3), (Q4_K, 1000, 4096, 5, 0),
-               (Q4_K, 129, 14336, 8, 7), (Q4_K, 65, 16384, 1, 1),
+               (Q4_K, 129, 14336, 8, 7), (Q4_K, 65, 16384, 1, 1), (Q4_K, 33, 32768, 1, 2),
+               (Q4_K, 20, 32768, 8, 3),
                (Q6_K, 1, 256, 1, 0), (Q6_K, 37, 768, 3, 2), (Q6_K, 300, 4096, 8, 0),
                (Q6_K, 129, 32768, 2, 1), (Q8_0, 37, 96, 1, 0), (Q8_0, 300, 1024, 3, 5),
                (Q8_0, 129, 16384, 8, 1)]

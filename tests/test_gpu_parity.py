@@ -85,7 +85,7 @@ def test_block_dots_bitexact(O, wtype, M, K, n):
 SHAPES = {
     Q4_0: [(1, 32), (37, 96), (300, 1024), (1000, 4096), (129, 16384)],
     Q8_0: [(1, 32), (37, 96), (300, 1024), (1000, 4096), (129, 16384)],
-    Q4_K: [(1, 256), (37, 512), (300, 2304), (1000, 4096), (129, 14336), (65, 16384)],
+    Q4_K: [(1, 256), (37, 512), (300, 2304), (1000, 4096), (129, 14336), (65, 16384), (33, 32768)],
     Q6_K: [(1, 256), (37, 768), (300, 4096), (129, 32768)],
 }
 GEMV_CASES = [(t, M, K, n) for t, shapes in SHAPES.items() for (M, K) in shapes
@@ -254,7 +254,7 @@ def test_abi_errors_on_device():
     L = B.lib()
     s = torch.cuda.current_stream().cuda_stream
     p, q, o = W.data_ptr(), y.data_ptr(), out.data_ptr()
-    assert L.mmvq(p, Q4_K, 1, 256 * 65, q, 1, o, s) == B.ERR_SHAPE      # row too long for a team
+    assert L.mmvq(p, Q4_K, 1, 256 * 129, q, 1, o, s) == B.ERR_SHAPE      # row too long for a team
     assert L.mmvq(p + 4, Q4_K, 1, 256, q, 1, o, s) == B.ERR_ALIGN
     assert L.mmvq(p, Q4_K, 1, 256, q + 4, 1, o, s) == B.ERR_ALIGN
     assert L.mmvq(p, Q4_K, 1, 256, q, 0, o, s) == B.ERR_SHAPE
