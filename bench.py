@@ -288,14 +288,20 @@ def time_workload(torch, B, wl, n: int, steps: int, warmup: int):
     reps = max(1, math.ceil(steps / C))
     wreps = max(1, math.ceil(warmup / C))
     res = {"copies": C, "steps": reps * C, "warmup": wreps * C}
-    # the two step forms must agree bit for bit before either is timed
+    # the two step forms must agree before either is timed: bit for bit,
+    # except Q4_K at 6..8 columns, where the q8_1 form runs the many-column
+    # kernel (another summation order; a loose relative check)
     if n <= B.MAX_COLS:
         ref = torch.empty_like(out)
         B.mmvq_quantize_q8_1(x, wl.K, n, wl.K, y, s)
         B.mmvq(Ws[0], wl.wtype, wl.M, wl.K, y, n, ref, s)
         B.mmvq_f32(Ws[0], wl.wtype, wl.M, wl.K, x, n, wl.K, out, s)
         torch.cuda.synchronize()
-        if not torch.equal(ref.view(torch.int32), out.view(torch.int32)):
+        if wl.wtype == B.Q4_K and n >= 6:
+            same = bool(((ref - out).abs() <= 1e-4 * ref.abs().max() + 1e-6).all())
+        else:
+            same = torch.equal(ref.view(torch.int32), out.view(torch.int32))
+        if not same:
             raise RuntimeError(f"{wl.name} n={n}: fused and two-launch results differ")
     with torch.cuda.stream(s):
         for g, key in ((g_step, "step"), (g_gemv, "gemv"), (g_quant, "quant"), (g_fused, "fused")):

@@ -150,7 +150,8 @@ int mmvq_quantize_q8_1(const float *x, int64_t K, int64_t n, int64_t ldx,
  * lane), K <= 32768 for Q4_K (64 weights per lane) and Q6_K (a quarter
  * super-block per lane); longer rows return MMVQ_ERR_SHAPE (the same limits
  * hold for every entry point below except the many-column path).
- * n > 8 takes the many-column path, where
+ * For Q4_K, n >= 6 (without a gate, q8_1 columns) takes the many-column
+ * path, where
  * the integer dots of 16 rows x 16 columns x 32 elements come from one int8
  * matrix-core instruction and the same scales are applied per sub-block
  * (no upper bound on K there). */
@@ -189,7 +190,10 @@ int mmvq_id_glu(const void *W_gate, const void *W_up,
 
 /* Fused quantize + product, fp32 activations [MMVQ §激活的量化, §融合].
  * The four calls below equal mmvq_quantize_q8_1 followed by mmvq, mmvq_glu,
- * mmvq_id and mmvq_id_glu respectively, bit for bit: each kernel quantizes
+ * mmvq_id and mmvq_id_glu respectively, bit for bit (one exception: Q4_K
+ * mmvq with 6 <= n <= 8 runs the many-column kernel on q8_1 columns, whose
+ * sums are ordered differently; mmvq_f32 then agrees with it within the
+ * tolerance, its q8_1 codes and scales still identical): each kernel quantizes
  * the slice of x that its lanes multiply, with the quantizer's arithmetic,
  * in registers, so the q8_1 columns are never written to memory and one
  * launch replaces two. Column j of x starts at x + j*ldx (ldx >= K floats;

@@ -2,6 +2,7 @@
 //
 // Every entry point validates its arguments on the host and enqueues
 // nothing when they are invalid; it never synchronizes and never aborts.
+#include <cstdlib>
 #include <stdint.h>
 
 #include "../../include/mmvq.h"
@@ -120,9 +121,21 @@ int mmq_common(const void* W, int type, int64_t M, int64_t K, const void* y_q, i
 }
 
 // Plain or gate/up product with an optional epilogue (W_gate NULL: no gate).
+constexpr int64_t kMmqMinColsQ4K = 6;
+
 int rows_common(const void* W_up, const void* W_gate, int type, int64_t M, int64_t K, const ActIn& in, int64_t n,
                 const mmvq_epilogue* epi, float* out, void* stream) {
   if (n > MMVQ_MAX_COLS && !W_gate && !in.x) return mmq_common(W_up, type, M, K, in.y_q, n, epi, out, stream);
+  // From 6 columns the matrix-core kernel is faster than the row kernels
+  // for Q4_K with q8_1 columns (one 16-column tile: ~14.5 us at 4096x14336
+  // and 14336x4096 for any n <= 16, the row kernels 16.5 / 14.5 us at n = 6
+  // and 24.8 / 17.8 us at n = 8).
+  if (type == MMVQ_Q4_K && n >= kMmqMinColsQ4K && !W_gate && !in.x)
+    return mmq_common(W_up, type, M, K, in.y_q, n, epi, out, stream);
+#ifdef QMV_TUNING
+  if (getenv("MMVQ_FORCE_MMQ") && !W_gate && !in.x && type == MMVQ_Q4_K)
+    return mmq_common(W_up, type, M, K, in.y_q, n, epi, out, stream);
+#endif
   const Dispatch* d;
   RowArgs a;
   int rc = check_gemv(W_up, type, M, K, in, n, out, &d, &a);

@@ -321,7 +321,7 @@ int main(int argc, char** argv) {
   }
   for (int64_t M : {1, 15, 16, 17, 33, 100})
     for (int64_t K : {256, 512, 768, 1024, 1280})
-      for (int n : {9, 16, 17, 31, 32, 33, 64, 100}) {
+      for (int n : {6, 7, 8, 9, 16, 17, 31, 32, 33, 64, 100}) {
         case_mmq<2, 2, 4>(M, K, n);
         case_mmq<2, 2, 8>(M, K, n);
         case_mmq<2, 1, 4>(M, K, n);
