@@ -60,6 +60,8 @@ def parse():
                    help="wall-clock budget of the oracle baseline (0 disables it)")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a plain device copy of known size (counter calibration)")
+    p.add_argument("--moe", action="store_true",
+                   help="time only the expert-indexed gate/up workload (one JSON line) and exit")
     p.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                    help="write profiles/ summaries from rocprofv3 csv output and exit")
     return p.parse_args()
@@ -465,6 +467,10 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         del a, b
+
+    if args.moe:
+        print(json.dumps(time_moe(torch, B, synth.BY_NAME["moe_q4_k_8x14336x4096"])), flush=True)
+        return
 
     res, data, Ws, y, out = time_workload(torch, B, wl, n, args.steps, args.warmup)
     # the fused forms take at most 8 columns; beyond that a step is the two launches
