@@ -175,14 +175,18 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- issue all weight loads of this pass's rows -----------------------
-  typename F::Wt w[R];
-  typename F::Wt wg[G == 2 ? R : 1];
+  // ---- issue all weight loads of a pass's rows ---------------------------
+  // With several passes the weights are double-buffered: the loads of pass
+  // p+1 are issued before pass p is computed, so a wave never waits for a
+  // whole round trip between passes.
+  constexpr int NB = PASSES > 1 ? 2 : 1;
+  typename F::Wt wb[NB][R];
+  typename F::Wt wgb[NB][G == 2 ? R : 1];
   // uniform row pointers; the slot's row is a per-lane 32-bit offset
   const uint32_t slot_off = static_cast<uint32_t>(slot * a.row_bytes);
-  auto issue = [&]() {
-    const uint8_t* rp = Wb + row0 * a.row_bytes;
-    const uint8_t* gp = (G == 2) ? Wgb + row0 * a.row_bytes : nullptr;
+  auto issue = [&](typename F::Wt (&w)[R], typename F::Wt (&wg)[G == 2 ? R : 1], int64_t r0) {
+    const uint8_t* rp = Wb + r0 * a.row_bytes;
+    const uint8_t* gp = (G == 2) ? Wgb + r0 * a.row_bytes : nullptr;
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       F::load_wt(w[i], rp, slot_off, L);
@@ -196,7 +200,7 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  issue();
+  issue(wb[0], wgb[0], row0);
   // the activation loads were issued before the weight loads, so they
   // retire first: this waits for them only
   if constexpr (XE) {
@@ -213,12 +217,15 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
     }
   }
 
+#pragma unroll
   for (int pass = 0; pass < PASSES; ++pass) {
   if (pass > 0) {
     row0 += RP;
     skip -= RP;
-    issue();
   }
+  if (pass + 1 < PASSES) issue(wb[(pass + 1) % NB], wgb[(pass + 1) % NB], row0 + RP);
+  typename F::Wt (&w)[R] = wb[pass % NB];
+  typename F::Wt (&wg)[G == 2 ? R : 1] = wgb[pass % NB];
   // ---- per row: decode once, one partial per column ----------------------
   float part[G][V];
 #pragma unroll
