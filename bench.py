@@ -523,7 +523,7 @@ def main():
                      "traffic": (measured_traffic("fused" if fused else "gemv")
                                  if wl.name == "q4_k_4096x14336" and n == 1 else None),
                      "kernel": (f"mmq_q4k_kernel ({synth.TYPE_NAME[wl.wtype].upper()}, n={n}, int8 matrix cores)"
-                                if n > 8 else
+                                if wl.wtype == B.Q4_K and n >= 6 and not fused else
                                 f"mmvq_rows_kernel ({synth.TYPE_NAME[wl.wtype].upper()}, n={n}, "
                                 f"{'fp32' if fused else 'q8_1'} activation)"),
                      "bytes_per_launch": kern_bytes,

@@ -104,8 +104,9 @@ enum {
     MMVQ_OK = 0,
     MMVQ_ERR_NULL = -1,      /* a required pointer is NULL                         */
     MMVQ_ERR_TYPE = -2,      /* unknown weight type or glu_op                       */
-    MMVQ_ERR_SHAPE = -3,     /* K not a multiple of the block, n outside 1..8,
-                                M < 1, ldx < K, top_k outside 1..n_experts, ...   */
+    MMVQ_ERR_SHAPE = -3,     /* K not a multiple of the block, n out of range, row
+                                too long, M < 1, ldx < K, top_k outside
+                                1..n_experts, ...                                 */
     MMVQ_ERR_ALIGN = -4,     /* a pointer or stride is not aligned as required      */
     MMVQ_ERR_LAUNCH = -5     /* the HIP runtime reported an error at launch         */
 };
@@ -115,9 +116,10 @@ enum {
 #define MMVQ_MAX_COLS 8
 
 /* Largest number of columns of the many-column path: mmvq and mmvq_ex
- * (q8_1 activations, no gate, Q4_K weights) with MMVQ_MAX_COLS < n <=
- * MMVQ_MAX_COLS_BATCH run on the matrix cores [MMVQ §多个 token 时]; so does
- * the quantizer. Other forms and types return MMVQ_ERR_SHAPE for n > 8. */
+ * (q8_1 activations, no gate, Q4_K weights) with 6 <= n <=
+ * MMVQ_MAX_COLS_BATCH run on the matrix cores [MMVQ §多个 token 时]; the
+ * quantizer takes up to MMVQ_MAX_COLS_BATCH columns too. Other forms and
+ * types return MMVQ_ERR_SHAPE for n > MMVQ_MAX_COLS. */
 #define MMVQ_MAX_COLS_BATCH 256
 
 /* Block geometry of a type: elements per block and bytes per block

@@ -94,8 +94,8 @@ mmvq_epilogue glu_only(int glu_op) {
   return e;
 }
 
-// Many columns (n > MMVQ_MAX_COLS): the MFMA kernel, Q4_K weights, q8_1
-// activations, no gate; the epilogue's up scale and bias apply.
+// Many columns (Q4_K from 6 columns, up to MMVQ_MAX_COLS_BATCH): the MFMA
+// kernel, q8_1 activations, no gate; the epilogue's up scale and bias apply.
 int mmq_common(const void* W, int type, int64_t M, int64_t K, const void* y_q, int64_t n,
                const mmvq_epilogue* epi, float* out, void* stream) {
   if (!W || !y_q || !out) return MMVQ_ERR_NULL;

@@ -1,4 +1,4 @@
-// mmq_kernel.hpp - the many-column path (n > 8 activation columns) for
+// mmq_kernel.hpp - the many-column path (6 or more activation columns) for
 // Q4_K weights: int8 matrix-core (MFMA) products of 16x16 tiles.
 //
 // Citations: [MMVQ §X] = page "llama.cpp 源码完全拆解(十四):mul_mat_vec_q——解码时
