@@ -68,7 +68,7 @@ inline int launch_rows_p(const RowArgs& a, const Shape& s, hipStream_t st) {
 template <class F, bool XF, int NC, int G>
 inline int launch_rows_nc(RowArgs a, int64_t K, hipStream_t st) {
   constexpr int RMAX = rows_per_pass<F>(NC, G);
-  const Shape s = make_shape<F>(a.M, K, RMAX);
+  const Shape s = make_shape<F>(a.M, K, launch_max_rows<F>(XF, NC, G));
   a.units = s.units;
   a.team_lanes = s.team_lanes;
   a.teams_per_block = s.teams_per_block;

@@ -67,6 +67,18 @@ constexpr int rows_per_pass(int nc, int g) {
   return g == 2 ? (r > 1 ? r / 2 : 1) : r;
 }
 
+// Most rows per slot a mat-vec launch uses: the register budget, except the
+// plain half-chunk Q4_K mat-vec at one q8_1 column, where teams of at most 4
+// rows measured faster (more, shorter teams: 4096x14336 8.65 -> 8.05 us,
+// 14336x4096 8.58 -> 7.75 us); its fused fp32 form keeps larger teams, which
+// re-read the fp32 activation fewer times. The result does not depend on the
+// rows per team: every output's team sum runs the same reduction tree.
+template <class F>
+constexpr int launch_max_rows(bool xf, int nc, int g) {
+  const int rmax = rows_per_pass<F>(nc, g);
+  return (F::kType == 12 && F::kUnitsPerBlock == 8 && !xf && nc == 1 && g == 1 && rmax > 4) ? 4 : rmax;
+}
+
 // Row window of one team and the unit / slot of one of its lanes.
 // The team owns rows [first, first + RP); the last team's window is moved
 // back to end at row M-1 (M >= RP), and rows of the window below `first`

@@ -115,7 +115,7 @@ static void case_rows(const char* name, int64_t M, int64_t K, int nc, int g, int
   uint8_t* y = alloc16(act_bytes);
   const float* x = xf ? reinterpret_cast<const float*>(y) : nullptr;
   const int units = static_cast<int>(K / F::kQK) * F::kUnitsPerBlock;
-  const Shape s = plan_rows(M, units, rows_per_pass<F>(nc, g), 256, QMV_TARGET_WAVES_PER_CU, 0);
+  const Shape s = plan_rows(M, units, launch_max_rows<F>(xf, nc, g), 256, QMV_TARGET_WAVES_PER_CU, 0);
   bool ok = s.team_lanes <= kLaunchBound && s.rows * s.slots <= M;
   int tok[kMaxCols];
   for (int j = 0; j < kMaxCols; ++j) tok[j] = j;
