@@ -68,15 +68,17 @@ constexpr int rows_per_pass(int nc, int g) {
 }
 
 // Most rows per slot a mat-vec launch uses: the register budget, except the
-// plain half-chunk Q4_K mat-vec at one q8_1 column, where teams of at most 4
-// rows measured faster (more, shorter teams: 4096x14336 8.65 -> 8.05 us,
-// 14336x4096 8.58 -> 7.75 us); its fused fp32 form keeps larger teams, which
-// re-read the fp32 activation fewer times. The result does not depend on the
-// rows per team: every output's team sum runs the same reduction tree.
+// plain half-chunk Q4_K and the Q8_0 mat-vec at one q8_1 column, where teams
+// of at most 4 rows measured faster (more, shorter teams: Q4_K 4096x14336
+// 8.65 -> 8.05 us, 14336x4096 8.58 -> 7.75 us; Q8_0 4096x14336 13.25 ->
+// 12.83 us); their fused fp32 forms keep larger teams, which re-read the
+// fp32 activation fewer times. The result does not depend on the rows per
+// team: every output's team sum runs the same reduction tree.
 template <class F>
 constexpr int launch_max_rows(bool xf, int nc, int g) {
   const int rmax = rows_per_pass<F>(nc, g);
-  return (F::kType == 12 && F::kUnitsPerBlock == 8 && !xf && nc == 1 && g == 1 && rmax > 4) ? 4 : rmax;
+  const bool short_teams = (F::kType == 12 && F::kUnitsPerBlock == 8) || F::kType == 8;
+  return (short_teams && !xf && nc == 1 && g == 1 && rmax > 4) ? 4 : rmax;
 }
 
 // Row window of one team and the unit / slot of one of its lanes.
