@@ -106,11 +106,11 @@ inline int launch_id_r(const RowArgs& a, const Shape& s, int n_experts, hipStrea
   return check_launch();
 }
 
-// Expert blocks own RB rows per slot (RB = the register budget at one token);
+// Expert blocks own RB = id_block_rows rows per slot;
 // matrices with fewer rows fall back to one row per slot.
 template <class F, bool XF, int G>
 inline int launch_id(RowArgs a, int64_t K, int n_experts, hipStream_t st) {
-  constexpr int RB = rows_per_pass<F>(1, G);
+  constexpr int RB = id_block_rows<F>(G);
   Shape s = make_shape<F>(a.M, K, RB);
   a.units = s.units;
   a.team_lanes = s.team_lanes;

@@ -81,6 +81,15 @@ constexpr int launch_max_rows(bool xf, int nc, int g) {
   return (short_teams && !xf && nc == 1 && g == 1 && rmax > 4) ? 4 : rmax;
 }
 
+// Rows per slot an expert block owns (taken in passes when its token count
+// leaves registers for fewer): the register budget at one token, except the
+// whole-chunk Q4_K gate/up kernel, where 8-row blocks measured faster than 4
+// (8-expert gate/up MoE: ~100 -> ~92 us; 2 rows: ~138, 16: ~100).
+template <class F>
+constexpr int id_block_rows(int g) {
+  return (F::kType == 12 && F::kUnitsPerBlock == 4 && g == 2) ? 8 : rows_per_pass<F>(1, g);
+}
+
 // Row window of one team and the unit / slot of one of its lanes.
 // The team owns rows [first, first + RP); the last team's window is moved
 // back to end at row M-1 (M >= RP), and rows of the window below `first`

@@ -145,7 +145,7 @@ static void case_id(const char* name, int64_t M, int64_t K, int E, int T, int g,
   uint8_t* y = alloc16(act_bytes);
   const float* x = xf ? reinterpret_cast<const float*>(y) : nullptr;
   const int units = static_cast<int>(K / F::kQK) * F::kUnitsPerBlock;
-  const int RB = rows_per_pass<F>(1, g);
+  const int RB = id_block_rows<F>(g);
   Shape s = plan_rows(M, units, RB, 256, QMV_TARGET_WAVES_PER_CU, 0);
   const int rb = static_cast<int64_t>(RB) * s.slots <= M ? RB : 1;   // as the launcher
   s.rows = rb;
