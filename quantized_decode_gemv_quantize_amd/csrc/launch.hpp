@@ -41,34 +41,45 @@ inline int units_per_row(int64_t K) {
 }
 
 template <class F>
-inline Shape make_shape(int64_t M, int64_t K, int rmax) {
+inline Shape make_shape(int64_t M, int64_t K, int rmax, int max_passes = 1) {
   int64_t force = 0;
 #ifdef QMV_TUNING
   if (const char* e = getenv("MMVQ_FORCE_ROWS")) force = atoi(e);
+  if (const char* e = getenv("MMVQ_MAX_PASSES")) max_passes = max_passes > 1 ? atoi(e) : 1;
 #endif
-  return plan_rows(M, units_per_row<F>(K), rmax, device_cus(), QMV_TARGET_WAVES_PER_CU, force);
+  return plan_rows(M, units_per_row<F>(K), rmax, device_cus(), QMV_TARGET_WAVES_PER_CU, force, max_passes);
 }
 
 inline int check_launch() {
   return hipGetLastError() == hipSuccess ? MMVQ_OK : MMVQ_ERR_LAUNCH;
 }
 
-template <class F, bool XF, int NC, int G, int R, int P>
+template <class F, bool XF, int NC, int G, int R, int P, int PASSES>
 inline int launch_rows_r(const RowArgs& a, const Shape& s, hipStream_t st) {
-  hipLaunchKernelGGL((mmvq_rows_kernel<F, NC, R, P, G, XF>), dim3(static_cast<unsigned>(s.blocks)),
+  hipLaunchKernelGGL((mmvq_rows_kernel<F, NC, R, P, G, XF, PASSES>), dim3(static_cast<unsigned>(s.blocks)),
                      dim3(s.teams_per_block * s.team_lanes), 0, st, a);
   return check_launch();
 }
 
+// Passes > 1 come only with R = the register budget (plan_rows).
 template <class F, bool XF, int NC, int G, int R>
 inline int launch_rows_p(const RowArgs& a, const Shape& s, hipStream_t st) {
-  return s.slots == 2 ? launch_rows_r<F, XF, NC, G, R, 2>(a, s, st) : launch_rows_r<F, XF, NC, G, R, 1>(a, s, st);
+  if constexpr (R == rows_per_pass<F>(NC, G) && launch_max_passes<F>(XF, NC, G) > 1) {
+    static_assert(launch_max_passes<F>(XF, NC, G) == 4, "rows kernels instantiated for 2 and 4 passes");
+    if (s.passes == 2)
+      return s.slots == 2 ? launch_rows_r<F, XF, NC, G, R, 2, 2>(a, s, st) : launch_rows_r<F, XF, NC, G, R, 1, 2>(a, s, st);
+    if (s.passes == 4)
+      return s.slots == 2 ? launch_rows_r<F, XF, NC, G, R, 2, 4>(a, s, st) : launch_rows_r<F, XF, NC, G, R, 1, 4>(a, s, st);
+  }
+  if (s.passes != 1) return MMVQ_ERR_SHAPE;
+  return s.slots == 2 ? launch_rows_r<F, XF, NC, G, R, 2, 1>(a, s, st)
+                      : launch_rows_r<F, XF, NC, G, R, 1, 1>(a, s, st);
 }
 
 template <class F, bool XF, int NC, int G>
 inline int launch_rows_nc(RowArgs a, int64_t K, hipStream_t st) {
   constexpr int RMAX = rows_per_pass<F>(NC, G);
-  const Shape s = make_shape<F>(a.M, K, launch_max_rows<F>(XF, NC, G));
+  const Shape s = make_shape<F>(a.M, K, launch_max_rows<F>(XF, NC, G), launch_max_passes<F>(XF, NC, G));
   a.units = s.units;
   a.team_lanes = s.team_lanes;
   a.teams_per_block = s.teams_per_block;

@@ -323,8 +323,9 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
   }   // passes
 }
 
-// Plain / fused kernel: columns 0..NC-1 of y.
-template <class F, int NC, int R, int P, int G, bool XF>
+// Plain / fused kernel: columns 0..NC-1 of y; a team owns PASSES * R * P
+// rows, taken R * P at a time.
+template <class F, int NC, int R, int P, int G, bool XF, int PASSES>
 __global__ void __launch_bounds__(kLaunchBound) mmvq_rows_kernel(RowArgs a) {
   Cols cols;
   cols.n = NC;
@@ -332,7 +333,7 @@ __global__ void __launch_bounds__(kLaunchBound) mmvq_rows_kernel(RowArgs a) {
   for (int j = 0; j < kMaxCols; ++j) { cols.tok[j] = j; cols.slots[j] = 0; }
   constexpr int V = pow2ceil(NC * R * P);
   __shared__ RedLds<G, V> red;
-  rows_body<F, NC, R, P, G, false, XF, V>(a, cols, a.W, a.Wg, red);
+  rows_body<F, NC, R, P, G, false, XF, V, PASSES>(a, cols, a.W, a.Wg, red);
 }
 
 // Expert-indexed kernel: blockIdx.y = expert. The token list is the same for

@@ -20,7 +20,8 @@ struct Shape {
   int slots;            // rows a team covers per step (P)
   int team_lanes;       // lanes per team (whole waves)
   int teams_per_block;
-  int rows;             // rows per slot (R)
+  int rows;             // rows per slot and pass (R)
+  int passes;           // passes per team: the team owns passes * R * P rows
   int64_t teams, blocks;
 };
 
@@ -34,10 +35,14 @@ inline int pow2floor(int64_t v) {
 // units:
 //  * slots P = 2 when a row's units fill whole waves only in pairs (e.g.
 //    224 units), else 1 (idle lanes pad the last wave);
-//  * rows per slot R: a power of two, at most rmax (register budget), with
-//    R*P <= M, sized for about `target_waves` waves per CU (force_rows > 0
-//    overrides the size, for tuning).
-inline Shape plan_rows(int64_t M, int units, int rmax, int64_t cus, int target_waves, int64_t force_rows) {
+//  * rows per slot and team: a power of two with rows * P <= M, sized for
+//    about `target_waves` waves per CU (force_rows > 0 overrides the size,
+//    for tuning), at most rmax * max_passes;
+//  * rows per pass R: at most rmax (register budget); a team that owns more
+//    rows takes them in passes of R (so the grid stays one round of resident
+//    waves when the registers cap the rows of a pass).
+inline Shape plan_rows(int64_t M, int units, int rmax, int64_t cus, int target_waves, int64_t force_rows,
+                       int max_passes = 1) {
   Shape s;
   s.units = units;
   s.slots = (units % kWave != 0 && (2 * units) % kWave == 0 && 2 * units <= kLaunchBound && M >= 2) ? 2 : 1;
@@ -46,9 +51,10 @@ inline Shape plan_rows(int64_t M, int units, int rmax, int64_t cus, int target_w
   s.teams_per_block = s.team_lanes >= 256 ? 1 : 256 / s.team_lanes;
   int64_t want = force_rows > 0 ? force_rows : M * tw / (cus * target_waves * s.slots);
   int r = pow2floor(want < 1 ? 1 : want);
-  if (r > rmax) r = rmax;
+  if (r > rmax * max_passes) r = rmax * max_passes;
   if (static_cast<int64_t>(r) * s.slots > M) r = pow2floor(M / s.slots);
-  s.rows = r;
+  s.passes = r > rmax ? r / rmax : 1;
+  s.rows = r / s.passes;
   const int64_t rp = static_cast<int64_t>(r) * s.slots;
   s.teams = (M + rp - 1) / rp;
   s.blocks = (s.teams + s.teams_per_block - 1) / s.teams_per_block;
@@ -75,10 +81,35 @@ constexpr int rows_per_pass(int nc, int g) {
 // fp32 activation fewer times. The result does not depend on the rows per
 // team: every output's team sum runs the same reduction tree.
 template <class F>
-constexpr int launch_max_rows(bool xf, int nc, int g) {
-  const int rmax = rows_per_pass<F>(nc, g);
+constexpr bool launch_short_teams(bool xf, int nc, int g) {
   const bool short_teams = (F::kType == 12 && F::kUnitsPerBlock == 8) || F::kType == 8;
-  return (short_teams && !xf && nc == 1 && g == 1 && rmax > 4) ? 4 : rmax;
+  return short_teams && !xf && nc == 1 && g == 1 && rows_per_pass<F>(nc, g) > 4;
+}
+
+template <class F>
+constexpr int launch_max_rows(bool xf, int nc, int g) {
+  return launch_short_teams<F>(xf, nc, g) ? 4 : rows_per_pass<F>(nc, g);
+}
+
+// Passes per team a mat-vec launch may use (rows kernels take a pass count of
+// 1, 2 or 4): where the register budget caps the rows of a pass below
+// what the row split wants, the team can take its rows in double-buffered
+// passes instead of the grid growing into more teams. Fewer, longer teams
+// pay off where each team has a large fixed cost: the fp32-activation
+// forms, where every team reads and quantizes the whole activation
+// (Q4_K 4096x14336 n = 2 / 4 / 8: 15.3 / 22.4 / 59 -> 12.0 / 17.0 / 38.6 us),
+// and Q6_K, whose one-wave teams at K = 4096 make a grid of many rounds
+// (128256x4096 n = 2: 94.6 -> 85.6 us). The q8_1 forms of the other formats
+// and the gate/up forms measured slower with passes (Q4_K n = 2: 9.6 ->
+// 10.6 us). Two passes hold two passes' weights in registers, which fits
+// without spilling from two columns on (Q6_K: two to six).
+constexpr int kMaxRowPasses = 4;
+
+template <class F>
+constexpr int launch_max_passes(bool xf, int nc, int g) {
+  const bool fits = nc >= 2 && !(F::kType == 14 && nc >= 7);
+  const bool pays = F::kType == 14 || (xf && g == 1);
+  return fits && pays ? kMaxRowPasses : 1;
 }
 
 // Rows per slot an expert block owns (taken in passes when its token count

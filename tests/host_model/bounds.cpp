@@ -115,15 +115,18 @@ static void case_rows(const char* name, int64_t M, int64_t K, int nc, int g, int
   uint8_t* y = alloc16(act_bytes);
   const float* x = xf ? reinterpret_cast<const float*>(y) : nullptr;
   const int units = static_cast<int>(K / F::kQK) * F::kUnitsPerBlock;
-  const Shape s = plan_rows(M, units, launch_max_rows<F>(xf, nc, g), 256, QMV_TARGET_WAVES_PER_CU, 0);
-  bool ok = s.team_lanes <= kLaunchBound && s.rows * s.slots <= M;
+  const Shape s = plan_rows(M, units, launch_max_rows<F>(xf, nc, g), 256, QMV_TARGET_WAVES_PER_CU, 0,
+                            launch_max_passes<F>(xf, nc, g));
+  // the launcher instantiates passes > 1 only at R = the register budget
+  bool ok = s.team_lanes <= kLaunchBound && static_cast<int64_t>(s.rows) * s.slots * s.passes <= M &&
+            (s.passes == 1 || ((s.passes == 2 || s.passes == 4) && s.rows == rows_per_pass<F>(nc, g)));
   int tok[kMaxCols];
   for (int j = 0; j < kMaxCols; ++j) tok[j] = j;
   std::vector<int> stores(M, 0);
   if (Wg) begin({{W, W + M * row_bytes}, {Wg, Wg + M * row_bytes}, {y, y + act_bytes}});
   else begin({{W, W + M * row_bytes}, {y, y + act_bytes}});
   ok = ok && model_rows<F>(s, s.rows, s.slots, g, M, W, Wg, row_bytes, xf ? nullptr : y, ycol, x, ldx, tok, nc,
-                           stores);
+                           stores, s.passes);
   for (int64_t r = 0; r < M && ok; ++r) ok = stores[r] == 1;
   report(xf ? "rows_f32" : "rows", ok, name, M, K, nc, g);
   free(W);
@@ -319,6 +322,21 @@ int main(int argc, char** argv) {
       }
     }
   }
+  // teams that take their rows in passes (more rows wanted than a pass's
+  // register budget), with a ragged last team
+  for (int nc : {1, 2, 4, 5, 8})
+    for (int g = 1; g <= 2; ++g)
+      for (int xpad : {-1, 3}) {
+        case_rows<Q4K>("q4_k", 3605, 14336, nc, g, xpad);
+        case_rows<Q4K2>("q4_k2", 3605, 14336, nc, g, xpad);
+        case_rows<Q6K>("q6_k", 3605, 14336, nc, g, xpad);
+        case_rows<Q40>("q4_0", 3605, 14336, nc, g, xpad);
+        case_rows<Q80>("q8_0", 3605, 14336, nc, g, xpad);
+        case_rows<Q4K>("q4_k", 12301, 4096, nc, g, xpad);
+        case_rows<Q40>("q4_0", 12301, 4096, nc, g, xpad);
+        case_rows<Q80>("q8_0", 12301, 4096, nc, g, xpad);
+        case_rows<Q6K>("q6_k", 12301, 4096, nc, g, xpad);
+      }
   for (int64_t M : {1, 15, 16, 17, 33, 100})
     for (int64_t K : {256, 512, 768, 1024, 1280})
       for (int n : {6, 7, 8, 9, 16, 17, 31, 32, 33, 64, 100}) {
@@ -342,6 +360,14 @@ int main(int argc, char** argv) {
       case_rows<Q4K2>("q4_k2", 14336, 4096, nc, 1);
       case_rows<Q4K>("q4_k", 4096, 14336, nc, 1, 0);
       case_rows<Q4K2>("q4_k2", 4096, 14336, nc, 1, 0);
+    }
+    for (int nc : {2, 3, 4, 5}) {
+      case_rows<Q4K>("q4_k", 14336, 4096, nc, 2);
+      case_rows<Q4K>("q4_k", 14336, 4096, nc, 2, 0);
+      case_rows<Q4K>("q4_k", 14336, 4096, nc, 1, 0);
+      case_rows<Q80>("q8_0", 4096, 14336, nc, 1);
+      case_rows<Q6K>("q6_k", 128256, 4096, nc, 1);
+      case_rows<Q6K>("q6_k", 128256, 4096, nc, 1, 0);
     }
     case_rows<Q4K>("q4_k", 4096, 4096, 1, 1);
     case_rows<Q4K2>("q4_k2", 4096, 4096, 1, 1);

@@ -73,7 +73,10 @@ FUSED_CASES = [(Q4_0, 37, 96, 1, 0), (Q4_0, 300, 1024, 3, 5), (Q4_0, 129, 16384,
                (Q4_K, 20, 32768, 8, 3),
                (Q6_K, 1, 256, 1, 0), (Q6_K, 37, 768, 3, 2), (Q6_K, 300, 4096, 8, 0),
                (Q6_K, 129, 32768, 2, 1), (Q8_0, 37, 96, 1, 0), (Q8_0, 300, 1024, 3, 5),
-               (Q8_0, 129, 16384, 8, 1)]
+               (Q8_0, 129, 16384, 8, 1),
+               # enough rows that teams take them in 2 or 4 passes (ragged last team)
+               (Q4_K, 12301, 4096, 2, 1), (Q4_K, 12301, 4096, 5, 0), (Q4_0, 12301, 4096, 3, 0),
+               (Q8_0, 12301, 4096, 8, 2), (Q6_K, 12301, 4096, 4, 1)]
 
 
 @pytest.mark.parametrize("wtype,M,K,n,pad", FUSED_CASES,
@@ -168,7 +171,8 @@ def test_mmvq_id_f32(O, name, wtype, E, M, K, ids, fused_glu):
                 assert_close(got[t * top_k + k:t * top_k + k + 1], u, mu, f"id f32 token {t} slot {k}")
 
 
-WORKLOADS_F32 = [("q4_k_4096x14336", 1), ("q4_k_4096x14336", 8), ("q6_k_128256x4096", 1),
+WORKLOADS_F32 = [("q4_k_4096x14336", 1), ("q4_k_4096x14336", 2), ("q4_k_4096x14336", 8),
+                 ("q4_k_14336x4096", 4), ("q6_k_128256x4096", 1), ("q6_k_128256x4096", 2),
                  ("q4_0_256x1024", 1), ("q8_0_4096x14336", 1)]
 
 

@@ -91,7 +91,9 @@ SHAPES = {
 GEMV_CASES = [(t, M, K, n) for t, shapes in SHAPES.items() for (M, K) in shapes
               for n in (1, 2, 3, 5, 8)]
 GEMV_CASES += [(Q4_K, 1000, 4096, 4), (Q4_K, 1000, 4096, 6), (Q4_K, 1000, 4096, 7),
-               (Q4_0, 300, 1024, 4), (Q6_K, 300, 4096, 4), (Q6_K, 300, 4096, 7)]
+               (Q4_0, 300, 1024, 4), (Q6_K, 300, 4096, 4), (Q6_K, 300, 4096, 7),
+               # enough rows that Q6_K teams take them in 2 or 4 passes
+               (Q6_K, 12301, 4096, 2), (Q6_K, 12301, 4096, 5)]
 
 
 @pytest.mark.parametrize("wtype,M,K,n", GEMV_CASES,
@@ -116,7 +118,8 @@ def test_gemv_parity(O, wtype, M, K, n):
 FULL = [("q4_0_256x1024", 1), ("q4_k_4096x4096", 1), ("q4_k_4096x14336", 1),
         ("q4_k_4096x14336", 2), ("q4_k_4096x14336", 4), ("q4_k_4096x14336", 8),
         ("q4_k_14336x4096", 1), ("q4_k_14336x4096", 2), ("q4_k_14336x4096", 4),
-        ("q4_k_14336x4096", 8), ("q6_k_128256x4096", 1), ("q8_0_4096x14336", 1)]
+        ("q4_k_14336x4096", 8), ("q6_k_128256x4096", 1), ("q6_k_128256x4096", 2),
+        ("q8_0_4096x14336", 1)]
 
 
 @pytest.mark.parametrize("name,n", FULL, ids=[f"{a}-n{b}" for a, b in FULL])
