@@ -121,7 +121,7 @@ inline int launch_id_r(const RowArgs& a, const Shape& s, int n_experts, hipStrea
 // matrices with fewer rows fall back to one row per slot.
 template <class F, bool XF, int G>
 inline int launch_id(RowArgs a, int64_t K, int n_experts, hipStream_t st) {
-  constexpr int RB = id_block_rows<F>(G);
+  constexpr int RB = id_block_rows<F>(G, XF);
   Shape s = make_shape<F>(a.M, K, RB);
   a.units = s.units;
   a.team_lanes = s.team_lanes;

@@ -115,10 +115,12 @@ constexpr int launch_max_passes(bool xf, int nc, int g) {
 // Rows per slot an expert block owns (taken in passes when its token count
 // leaves registers for fewer): the register budget at one token, except the
 // whole-chunk Q4_K gate/up kernel, where 8-row blocks measured faster than 4
-// (8-expert gate/up MoE: ~100 -> ~92 us; 2 rows: ~138, 16: ~100).
+// with q8_1 activations (8-expert gate/up MoE: ~100 -> ~92 us; 2 rows: ~138,
+// 16: ~100), and 32-row blocks with fp32 activations, where every block
+// re-quantizes its tokens (131 -> 112 us; 16 rows: 126, 64: 127).
 template <class F>
-constexpr int id_block_rows(int g) {
-  return (F::kType == 12 && F::kUnitsPerBlock == 4 && g == 2) ? 8 : rows_per_pass<F>(1, g);
+constexpr int id_block_rows(int g, bool xf = false) {
+  return (F::kType == 12 && F::kUnitsPerBlock == 4 && g == 2) ? (xf ? 32 : 8) : rows_per_pass<F>(1, g);
 }
 
 // Row window of one team and the unit / slot of one of its lanes.

@@ -148,7 +148,7 @@ static void case_id(const char* name, int64_t M, int64_t K, int E, int T, int g,
   uint8_t* y = alloc16(act_bytes);
   const float* x = xf ? reinterpret_cast<const float*>(y) : nullptr;
   const int units = static_cast<int>(K / F::kQK) * F::kUnitsPerBlock;
-  const int RB = id_block_rows<F>(g);
+  const int RB = id_block_rows<F>(g, xf);
   Shape s = plan_rows(M, units, RB, 256, QMV_TARGET_WAVES_PER_CU, 0);
   const int rb = static_cast<int64_t>(RB) * s.slots <= M ? RB : 1;   // as the launcher
   s.rows = rb;
@@ -377,6 +377,7 @@ int main(int argc, char** argv) {
     case_rows<Q6K>("q6_k", 128256, 4096, 1, 1);
     case_id<Q4K>("q4_k", 14336, 4096, 8, 8, 2);
     case_id<Q4K2>("q4_k2", 14336, 4096, 8, 8, 2);
+    case_id<Q4K2>("q4_k2", 14336, 4096, 8, 8, 2, 0);
     case_mmq<2, 2, 4>(4096, 14336, 64);
     case_mmq<2, 1, 8>(4096, 14336, 16);
     case_mmq<1, 1, 8>(4096, 14336, 16);

@@ -130,6 +130,8 @@ def test_mmvq_glu_f32(O, wtype, M, K, n, op):
 
 ID_F32 = [("q4_k-E4-T3-k2", Q4_K, 4, 200, 512, [[2, 0], [1, 2], [2, 3]]),
           ("q4_k-E8-T8-k2", Q4_K, 8, 300, 2048, "random"),
+          # fewer rows than the fp32 gate/up kernel's 32-row expert blocks
+          ("q4_k-E3-T4-k2-M20", Q4_K, 3, 20, 512, [[2, 0], [1, 2], [0, 1], [2, 1]]),
           ("q4_0-E5-T4-k2", Q4_0, 5, 77, 1024, [[4, 0], [0, 4], [2, 2], [1, 3]]),
           ("q6_k-E4-T2-k2", Q6_K, 4, 50, 768, [[3, 1], [1, 0]])]
 
@@ -169,6 +171,28 @@ def test_mmvq_id_f32(O, name, wtype, E, M, K, ids, fused_glu):
             for k in range(top_k):
                 u, mu = oracle_rows(O, Wu[int(ids[t, k])], wtype, M, K, y[t:t + 1], 1, [(0, M)])
                 assert_close(got[t * top_k + k:t * top_k + k + 1], u, mu, f"id f32 token {t} slot {k}")
+
+
+def test_mmvq_id_glu_f32_moe_workload():
+    """The MoE workload (8 experts, 8 tokens, top-2, Q4_K 14336x4096 gate
+    and up) through the fused fp32 form, in the launch configuration the
+    benchmark times: every output bit-identical to quantize + mmvq_id_glu
+    (whose oracle parity on the same data is tested with the q8_1 entry
+    points)."""
+    wl = synth.BY_NAME["moe_q4_k_8x14336x4096"]
+    announce("mmvq_id_glu_f32 moe workload")
+    d = synth.make(wl, 8)
+    E, M, K, top_k = wl.n_experts, wl.M, wl.K, wl.top_k
+    ids, x = d["ids"].astype(np.int32), d["x"]
+    T = ids.shape[0]
+    stride = (d["W_up"][0].size + 15) // 16 * 16
+    pad = lambda A: np.concatenate(  # noqa: E731
+        [np.pad(A[e].reshape(-1), (0, stride - A[e].size)) for e in range(E)])
+    Wud, Wgd, xd, idsd = dev(pad(d["W_up"])), dev(pad(d["W_gate"])), dev(x), dev(ids)
+    fused, two = _empty(T * top_k, M), _empty(T * top_k, M)
+    B.mmvq_id_glu_f32(Wgd, Wud, stride, E, wl.wtype, M, K, xd, T, x.shape[1], idsd, top_k, B.GLU_SWIGLU, fused)
+    B.mmvq_id_glu(Wgd, Wud, stride, E, wl.wtype, M, K, gpu_quantize(x, K), T, idsd, top_k, B.GLU_SWIGLU, two)
+    _same(fused, two, "id_glu f32 moe workload")
 
 
 WORKLOADS_F32 = [("q4_k_4096x14336", 1), ("q4_k_4096x14336", 2), ("q4_k_4096x14336", 8),
