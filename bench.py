@@ -91,7 +91,7 @@ def kernel_kind(name: str) -> str | None:
     """'fused' / 'gemv' for the n=1 Q4_K plain mat-vec kernels (fp32 or q8_1
     activations), else None."""
     import re
-    m = re.match(r"void qmv::mmvq_rows_kernel<qmv::Q4K, 1, \d+, \d+, 1, (true|false)>", name)
+    m = re.match(r"void qmv::mmvq_rows_kernel<qmv::Q4K, 1, \d+, \d+, 1, (true|false), 1>", name)
     if not m:
         return None
     return "fused" if m.group(1) == "true" else "gemv"
