@@ -170,6 +170,21 @@ __device__ __forceinline__ float h2f(uint32_t bits) {
 
 constexpr int pow2ceil(int v) { int p = 1; while (p < v) p <<= 1; return p; }
 
+// f(Idx<0>{}), ..., f(Idx<N-1>{}): a loop whose index is a compile-time
+// constant in the body, for bodies too large for the loop unroller (a
+// runtime index into a register array puts the array in scratch memory).
+template <int I>
+struct Idx {
+  static constexpr int value = I;
+};
+template <int I, int N, class Fn>
+__host__ __device__ __forceinline__ void static_for(Fn&& f) {
+  if constexpr (I < N) {
+    f(Idx<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
 #ifndef QMV_HOST_MODEL
 // ---------------------------------------------------------------------------
 // Cross-lane exchange

@@ -160,17 +160,21 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
   constexpr bool XE = XF && NC * F::kXWords <= 64;
   typename F::Act act[NC];
   typename F::XRaw xr[XE ? NC : 1];
-#pragma unroll
-  for (int j = 0; j < NC; ++j) {
-    if constexpr (XE) {
-      F::load_x(xr[j], a.x + cols.tok[j] * a.ldx, u);
-    } else if constexpr (XF) {
+  if constexpr (XF && !XE) {
+    // compile-time column index: at 8 columns the body exceeds what the
+    // loop unroller takes, and a runtime index would put act[] in scratch
+    static_for<0, NC>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
       typename F::XRaw t;
       F::load_x(t, a.x + cols.tok[j] * a.ldx, u);
       F::quant_x(act[j], t);
       if (!active) F::zero_act(act[j]);
-    } else {
-      F::issue_act(act[j], a.y + cols.tok[j] * a.ycol_bytes, u);
+    });
+  } else {
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      if constexpr (XE) F::load_x(xr[j], a.x + cols.tok[j] * a.ldx, u);
+      else F::issue_act(act[j], a.y + cols.tok[j] * a.ycol_bytes, u);
     }
   }
   __builtin_amdgcn_sched_barrier(0);

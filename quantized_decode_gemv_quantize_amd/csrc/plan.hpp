@@ -101,14 +101,15 @@ constexpr int launch_max_rows(bool xf, int nc, int g) {
 // and Q6_K, whose one-wave teams at K = 4096 make a grid of many rounds
 // (128256x4096 n = 2: 94.6 -> 85.6 us). The q8_1 forms of the other formats
 // and the gate/up forms measured slower with passes (Q4_K n = 2: 9.6 ->
-// 10.6 us). Two passes hold two passes' weights in registers, which fits
-// without spilling from two columns on (Q6_K: two to six).
+// 10.6 us), and the Q6_K gate/up forms spill with them. Two passes hold two
+// passes' weights in registers, which fits without spilling from two
+// columns on (Q6_K: two to six).
 constexpr int kMaxRowPasses = 4;
 
 template <class F>
 constexpr int launch_max_passes(bool xf, int nc, int g) {
   const bool fits = nc >= 2 && !(F::kType == 14 && nc >= 7);
-  const bool pays = F::kType == 14 || (xf && g == 1);
+  const bool pays = g == 1 && (F::kType == 14 || xf);
   return fits && pays ? kMaxRowPasses : 1;
 }
 
