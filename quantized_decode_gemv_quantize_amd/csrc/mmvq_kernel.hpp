@@ -11,7 +11,10 @@
 //   * A team owns up to R consecutive rows. It issues the weight loads of
 //     all its rows before any arithmetic (branch-free: rows past the end are
 //     clamped and their results dropped), so each wave has R x 32 bytes per
-//     lane in flight and the whole matrix is requested early.
+//     lane in flight and the whole matrix is requested early. Where the
+//     registers cap R, a team may own 2 or 4 times R rows and take them in
+//     double-buffered passes (loads of pass p+1 issued before pass p is
+//     computed), loading its activation slice once.
 //   * Per row the lane decodes its unit once and forms one fp32 partial per
 //     activation column with v_dot4_i32_i8 integer dots; scales are applied
 //     per block after the integer dot [MMVQ §一次 vec_dot 的解剖].
