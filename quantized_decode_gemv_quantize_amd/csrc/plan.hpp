@@ -115,13 +115,15 @@ constexpr int launch_max_passes(bool xf, int nc, int g) {
 
 // Rows per slot an expert block owns (taken in passes when its token count
 // leaves registers for fewer): the register budget at one token, except the
-// whole-chunk Q4_K gate/up kernel, where 8-row blocks measured faster than 4
-// with q8_1 activations (8-expert gate/up MoE: ~100 -> ~92 us; 2 rows: ~138,
-// 16: ~100), and 32-row blocks with fp32 activations, where every block
-// re-quantizes its tokens (131 -> 112 us; 16 rows: 126, 64: 127).
+// whole-chunk Q4_K kernels: with q8_1 activations the gate/up kernel's 8-row
+// blocks measured faster than 4 (8-expert gate/up MoE: ~100 -> ~92 us; 2
+// rows: ~138, 16: ~100); with fp32 activations, where every block
+// re-quantizes its tokens, 32-row blocks (gate/up: 131 -> 112 us, 16 rows:
+// 126, 64: 127; up only: 95 -> 67 us).
 template <class F>
 constexpr int id_block_rows(int g, bool xf = false) {
-  return (F::kType == 12 && F::kUnitsPerBlock == 4 && g == 2) ? (xf ? 32 : 8) : rows_per_pass<F>(1, g);
+  if (F::kType == 12 && F::kUnitsPerBlock == 4) return xf ? 32 : (g == 2 ? 8 : rows_per_pass<F>(1, g));
+  return rows_per_pass<F>(1, g);
 }
 
 // Row window of one team and the unit / slot of one of its lanes.
