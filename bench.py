@@ -12,13 +12,15 @@ Measurement:
   * inputs (weights, activation) are resident in HBM before timing starts;
   * weights rotate over enough copies (>= 3 x the 256 MB last-level cache)
     that every step streams its matrix from HBM, not from cache;
-  * steps are captured in a HIP graph (one graph = one pass over all weight
-    copies) and replayed, so host launch cost does not pace microsecond
-    kernels;
-  * HIP events on the launch stream time the steps and, separately, a graph
-    of back-to-back mat-vec launches alone (the roofline figure);
-  * the CPU oracle (plain C, fp64) runs the same workload on a bounded
-    number of repetitions, rows split over the host's threads, as a
+  * exactly --steps launches are captured in one HIP graph (launch i uses
+    weight copy i mod copies) and replayed once after a graph of --warmup
+    untimed launches, so host launch cost does not pace microsecond kernels;
+  * HIP events on the launch stream time each form: the fused step, the
+    two-launch step, the mat-vec alone, the quantizer alone, and a
+    streaming-read probe (mmvq_read_probe) over the same weight bytes, the
+    read ceiling the kernels are compared with;
+  * the CPU oracle (plain C, fp64) runs the same workload for a bounded
+    time, rows split over every host core and then on one thread, as a
     reported baseline.
 
 Prints one JSON line (rank 0). ``--all`` also prints one line per workload
@@ -49,8 +51,8 @@ TOKENS_DENOM_GB = 3.9        # weight bytes of one decode step of a 7B Q4_K mode
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=4000)
-    p.add_argument("--warmup", type=int, default=400)
+    p.add_argument("--steps", type=int, default=2000)
+    p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--workload", default="q4_k_4096x14336")
     p.add_argument("--n", type=int, default=1, help="activation columns")
     p.add_argument("--step", choices=("fused", "two"), default="fused",
@@ -91,7 +93,7 @@ def kernel_kind(name: str) -> str | None:
     """'fused' / 'gemv' for the n=1 Q4_K plain mat-vec kernels (fp32 or q8_1
     activations), else None."""
     import re
-    m = re.match(r"void qmv::mmvq_rows_kernel<qmv::Q4K, 1, \d+, \d+, 1, (true|false), 1>", name)
+    m = re.match(r"void qmv::mmvq_rows_kernel<qmv::Q4K, 1, \d+, \d+, 1, (true|false), 1(, \d+)?>", name)
     if not m:
         return None
     return "fused" if m.group(1) == "true" else "gemv"
@@ -258,42 +260,53 @@ def capture(torch, stream, fn):
     return g
 
 
-def time_workload(torch, B, wl, n: int, steps: int, warmup: int):
-    """Returns a dict of GPU timings for one workload."""
+def launches_graph(torch, stream, launch, count: int, copies: int):
+    """One HIP graph holding exactly `count` launches; launch i uses weight
+    copy i mod copies."""
+    def body():
+        for i in range(count):
+            launch(i % copies)
+    return capture(torch, stream, body)
+
+
+def timed_replay(torch, stream, g_warm, g_timed):
+    """Untimed warmup graph, then the timed graph bracketed by synchronizes;
+    HIP events on the launch stream. Returns (ms on the events, wall s)."""
+    with torch.cuda.stream(stream):
+        if g_warm is not None:
+            g_warm.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with Timer(torch, stream) as t:
+            g_timed.replay()
+        torch.cuda.synchronize()
+    return t.ms, time.perf_counter() - t0
+
+
+def time_workload(torch, B, wl, n: int, steps: int, warmup: int, probe: bool = True):
+    """GPU timings of one workload: exactly `steps` timed launches of each
+    form after `warmup` untimed ones, weights rotating over the copies.
+    Forms: fused (mmvq_f32), two-launch step (quantize + mmvq), mat-vec alone
+    (mmvq), quantizer alone, and the streaming-read probe over the same
+    weight bytes."""
     data, Ws, x, y, out = gpu_setup(torch, wl, n)
     C = len(Ws)
     s = torch.cuda.Stream()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
     torch.cuda.synchronize()
-
-    def step_pass():
-        for W in Ws:
-            B.mmvq_quantize_q8_1(x, wl.K, n, wl.K, y, s)
-            B.mmvq(W, wl.wtype, wl.M, wl.K, y, n, out, s)
-
-    def gemv_pass():
-        for W in Ws:
-            B.mmvq(W, wl.wtype, wl.M, wl.K, y, n, out, s)
-
-    def quant_pass():
-        for _ in Ws:
-            B.mmvq_quantize_q8_1(x, wl.K, n, wl.K, y, s)
-
-    def fused_pass():
-        for W in Ws:
-            B.mmvq_f32(W, wl.wtype, wl.M, wl.K, x, n, wl.K, out, s)
-
     fused_ok = n <= B.MAX_COLS            # the fused forms take at most 8 columns
-    g_step = capture(torch, s, step_pass)
-    g_gemv = capture(torch, s, gemv_pass)
-    g_quant = capture(torch, s, quant_pass)
-    g_fused = capture(torch, s, fused_pass) if fused_ok else None
-    reps = max(1, math.ceil(steps / C))
-    wreps = max(1, math.ceil(warmup / C))
-    res = {"copies": C, "steps": reps * C, "warmup": wreps * C}
+    forms = {
+        "step": lambda c: (B.mmvq_quantize_q8_1(x, wl.K, n, wl.K, y, s), B.mmvq(Ws[c], wl.wtype, wl.M, wl.K, y, n, out, s)),
+        "gemv": lambda c: B.mmvq(Ws[c], wl.wtype, wl.M, wl.K, y, n, out, s),
+        "quant": lambda c: B.mmvq_quantize_q8_1(x, wl.K, n, wl.K, y, s),
+        "fused": (lambda c: B.mmvq_f32(Ws[c], wl.wtype, wl.M, wl.K, x, n, wl.K, out, s)) if fused_ok else None,
+        "probe": (lambda c: B.mmvq_read_probe(Ws[c], wl.weight_bytes, sink, s)) if probe else None,
+    }
+    res = {"copies": C, "steps": steps, "warmup": warmup}
     # the two step forms must agree before either is timed: bit for bit,
     # except Q4_K at 6..8 columns, where the q8_1 form runs the many-column
     # kernel (another summation order; a loose relative check)
-    if n <= B.MAX_COLS:
+    if fused_ok:
         ref = torch.empty_like(out)
         B.mmvq_quantize_q8_1(x, wl.K, n, wl.K, y, s)
         B.mmvq(Ws[0], wl.wtype, wl.M, wl.K, y, n, ref, s)
@@ -305,23 +318,17 @@ def time_workload(torch, B, wl, n: int, steps: int, warmup: int):
             same = torch.equal(ref.view(torch.int32), out.view(torch.int32))
         if not same:
             raise RuntimeError(f"{wl.name} n={n}: fused and two-launch results differ")
-    with torch.cuda.stream(s):
-        for g, key in ((g_step, "step"), (g_gemv, "gemv"), (g_quant, "quant"), (g_fused, "fused")):
-            if g is None:
-                res[f"{key}_us"] = None
-                continue
-            for _ in range(wreps):
-                g.replay()
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            with Timer(torch, s) as t:
-                for _ in range(reps):
-                    g.replay()
-            torch.cuda.synchronize()
-            wall = time.perf_counter() - t0
-            res[f"{key}_ms_total"] = t.ms
-            res[f"{key}_us"] = t.ms * 1e3 / (reps * C)
-            res[f"{key}_wall_s"] = wall
+    for key, launch in forms.items():
+        if launch is None:
+            res[f"{key}_us"] = None
+            continue
+        g_warm = launches_graph(torch, s, launch, warmup, C) if warmup > 0 else None
+        g_timed = launches_graph(torch, s, launch, steps, C)
+        ms, wall = timed_replay(torch, s, g_warm, g_timed)
+        res[f"{key}_ms_total"] = ms
+        res[f"{key}_us"] = ms * 1e3 / steps
+        res[f"{key}_wall_s"] = wall
+        del g_warm, g_timed
     return res, data, Ws, y, out
 
 
@@ -402,9 +409,20 @@ def time_moe(torch, B, wl, reps: int = 200):
     return res
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, data, n: int, budget_s: float):
-    """The oracle on the host: full mat-vecs (quantize + all rows), rows split
-    over the host threads, repeated until the wall-clock budget is spent."""
+    """The oracle on the host: full mat-vecs (quantize + all rows), repeated
+    until half the wall-clock budget is spent with the rows split over every
+    host core, then for the other half on one thread."""
     import concurrent.futures as cf
 
     import oracle
@@ -412,30 +430,37 @@ def cpu_baseline(wl, data, n: int, budget_s: float):
     L = O.L
     W = np.ascontiguousarray(data["W"]).reshape(-1)
     x = np.ascontiguousarray(data["x"])
-    cores = min(16, os.cpu_count() or 1)
     out = np.zeros((n, wl.M))
-    chunks = np.linspace(0, wl.M, cores + 1).astype(np.int64)
 
-    def rows(i, y):
-        rc = L.orc_mmvq_rows(W.ctypes.data, wl.wtype, wl.M, wl.K, y.ctypes.data, n,
-                             int(chunks[i]), int(chunks[i + 1]), out.ctypes.data, None, None)
+    def rows(r0, r1, y):
+        rc = L.orc_mmvq_rows(W.ctypes.data, wl.wtype, wl.M, wl.K, y.ctypes.data, n, int(r0), int(r1),
+                             out.ctypes.data, None, None)
         assert rc == 0
 
-    reps = 0
-    t0 = time.perf_counter()
-    with cf.ThreadPoolExecutor(max_workers=cores) as ex:
-        while True:
-            y = O.quantize_q8_1(x)
-            list(ex.map(lambda i: rows(i, y), range(cores)))
-            reps += 1
-            if time.perf_counter() - t0 >= budget_s:
-                break
-    dt = time.perf_counter() - t0
+    def run(threads: int, seconds: float):
+        chunks = np.linspace(0, wl.M, threads + 1).astype(np.int64)
+        reps = 0
+        t0 = time.perf_counter()
+        with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+            while True:
+                y = O.quantize_q8_1(x)
+                list(ex.map(lambda i: rows(chunks[i], chunks[i + 1], y), range(threads)))
+                reps += 1
+                if time.perf_counter() - t0 >= seconds:
+                    break
+        return reps, time.perf_counter() - t0
+
+    cores = os.cpu_count() or 1
+    reps, dt = run(cores, budget_s / 2)
+    reps1, dt1 = run(1, budget_s / 2)
     return {"value": round(wl.weight_bytes * reps / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"{reps} full {wl.name} n={n} passes (q8_1 quantize + all {wl.M} rows), "
-                      f"rows split over {cores} threads, {dt:.1f} s wall",
-            "us_per_gemv": round(dt / reps * 1e6, 1)}
+            "sample": f"{reps} full {wl.name} n={n} passes (q8_1 quantize + all {wl.M} rows) with rows split "
+                      f"over {cores} threads in {dt:.1f} s wall, then {reps1} on one thread in {dt1:.1f} s",
+            "us_per_gemv": round(dt / reps * 1e6, 1),
+            "single_thread_gbs": round(wl.weight_bytes * reps1 / dt1 / 1e9, 4),
+            "single_thread_us_per_gemv": round(dt1 / reps1 * 1e6, 1),
+            "cpu_model": cpu_model()}
 
 
 def main():
@@ -527,7 +552,13 @@ def main():
                                 f"mmvq_rows_kernel ({synth.TYPE_NAME[wl.wtype].upper()}, n={n}, "
                                 f"{'fp32' if fused else 'q8_1'} activation)"),
                      "bytes_per_launch": kern_bytes,
-                     "avg_launch_us": round(kern_us, 3)},
+                     "avg_launch_us": round(kern_us, 3),
+                     # the same weight bytes through the streaming-read probe
+                     # (mmvq_read_probe), same copies and step count: the
+                     # read ceiling of one launch of this size on this part
+                     "probe_us": round(res["probe_us"], 3),
+                     "probe_gbs": round(wl.weight_bytes / (res["probe_us"] * 1e-6) / 1e9, 1),
+                     "pct_of_probe": round(100 * res["probe_us"] / kern_us, 2)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -538,12 +569,13 @@ def main():
             w = synth.BY_NAME[name]
             many = (16, 32, 64, 128) if name in ("q4_k_4096x14336", "q4_k_14336x4096") else ()
             for nn in tuple(w.n if name != "q4_k_4096x14336" else (1, 2, 4, 8)) + many:
-                r, *_ = time_workload(torch, B, w, nn, 1000, 100)
+                r, *_ = time_workload(torch, B, w, nn, 500, 50)
                 gb = algorithmic_bytes(w, nn) / (r["gemv_us"] * 1e-6) / 1e9
                 print(json.dumps({"workload": name, "n": nn, "gemv_us": round(r["gemv_us"], 3),
                                   "quantize_us": round(r["quant_us"], 3),
                                   "two_launch_step_us": round(r["step_us"], 3),
                                   "fused_us": None if r["fused_us"] is None else round(r["fused_us"], 3),
+                                  "probe_us": round(r["probe_us"], 3),
                                   "gemv_gbs": round(gb, 1), "frac": round(gb / HBM_PEAK_GBS, 4)}),
                       file=sys.stderr, flush=True)
         print(json.dumps(time_moe(torch, B, synth.BY_NAME["moe_q4_k_8x14336x4096"])), file=sys.stderr,

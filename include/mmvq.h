@@ -71,16 +71,23 @@ enum {
     MMVQ_Q6_K = 14
 };
 
-/* GLU of the fused gate/up variants [MMVQ §融合]. The pages name GEGLU,
- * SWIGLU_OAI and SWIGLU_CLAMP without defining them; the definitions below
- * are this library's (gelu exact; the OAI form as published with the
- * gpt-oss models), with g' = min(gate, limit), u' = clamp(up, -limit, limit). */
+/* GLU of the fused gate/up variants [MMVQ §融合]. The page's epilogue
+ * switch names these ops and calls device functions whose bodies it does
+ * not print; the definitions below are this library's readings:
+ *   GEGLU: gelu in the tanh form published with GELU (Hendrycks and Gimpel,
+ *     2016), gelu(z) = z/2*(1 + tanh(sqrt(2/pi)*(z + 0.044715*z^3)));
+ *   SWIGLU_OAI: the clamped SwiGLU published with the gpt-oss models, with
+ *     that publication's constants alpha = 1.702 and limit = 7 (the page
+ *     calls it with the gate and up values only);
+ *   SWIGLU_CLAMP: silu on the same clamps with the caller's limit (the page
+ *     passes glu_limit to it).
+ * g' = min(gate, limit), u' = clamp(up, -limit, limit). */
 enum {
     MMVQ_GLU_PLAIN = 0,        /* out = gate * up                                  */
     MMVQ_GLU_SWIGLU = 1,       /* out = silu(gate) * up, silu(z) = z/(1+e^-z)      */
-    MMVQ_GLU_GEGLU = 2,        /* out = gelu(gate) * up, gelu(z) = z/2*(1+erf(z/sqrt 2)) */
-    MMVQ_GLU_SWIGLU_OAI = 3,   /* out = g' * sigmoid(alpha*g') * (u' + 1)          */
-    MMVQ_GLU_SWIGLU_CLAMP = 4  /* out = silu(g') * u'                              */
+    MMVQ_GLU_GEGLU = 2,        /* out = gelu(gate) * up, gelu in its tanh form     */
+    MMVQ_GLU_SWIGLU_OAI = 3,   /* out = g' * sigmoid(1.702*g') * (u' + 1), limit 7 */
+    MMVQ_GLU_SWIGLU_CLAMP = 4  /* out = silu(g') * u', limit = glu_limit           */
 };
 
 /* Fused epilogue [MMVQ §融合], applied to each output in the order the
@@ -96,8 +103,7 @@ typedef struct mmvq_epilogue {
     const float *up_scale;
     const float *gate_scale;
     int glu_op;        /* MMVQ_GLU_*, used when a gate matrix is given */
-    float glu_limit;   /* SWIGLU_OAI, SWIGLU_CLAMP                      */
-    float glu_alpha;   /* SWIGLU_OAI (the published value is 1.702)     */
+    float glu_limit;   /* SWIGLU_CLAMP                                  */
 } mmvq_epilogue;
 
 enum {
@@ -161,8 +167,9 @@ int mmvq(const void *W, int type, int64_t M, int64_t K,
          const void *y_q, int64_t n, float *out, void *stream);
 
 /* Fused gate/up: out[j*M + r] = GLU(g, u) with g the mmvq of W_gate and u
- * the mmvq of W_up (same type and shape), per glu_op (limit and alpha 0;
- * mmvq_ex sets them); both weight
+ * the mmvq of W_up (same type and shape), per glu_op: PLAIN, SWIGLU, GEGLU
+ * or SWIGLU_OAI (SWIGLU_CLAMP needs a limit: MMVQ_ERR_TYPE here, use
+ * mmvq_ex); both weight
  * streams are read in one kernel and the epilogue applies the GLU
  * [MMVQ §融合]. Same requirements as mmvq. */
 int mmvq_glu(const void *W_gate, const void *W_up, int type, int64_t M,
@@ -255,6 +262,14 @@ int mmvq_id_ex(const void *W_up, const void *W_gate,
  * [MMVQ §dp4a, §一次 vec_dot 的解剖]. Same requirements as mmvq. */
 int mmvq_block_dots(const void *W, int type, int64_t M, int64_t K,
                     const void *y_q, int64_t n, int32_t *dots, void *stream);
+
+/* MEASUREMENT SUPPORT: reads bytes bytes at src (device, 16-byte aligned,
+ * bytes a positive multiple of 16) with 16-byte coalesced loads and does
+ * nothing else; sink is a device word it may write (4-byte aligned). The
+ * time of this launch is the HBM read ceiling the mat-vec launches are
+ * compared with for the same bytes [MMVQ §性能直觉 (decode is bound by the
+ * weight read)]. Asynchronous on stream; MMVQ_ERR_* codes as above. */
+int mmvq_read_probe(const void *src, int64_t bytes, void *sink, void *stream);
 
 /* Static, human-readable text for a return code. Never NULL. */
 const char *mmvq_strerror(int code);

@@ -65,12 +65,12 @@ def _u8(a) -> np.ndarray:
 
 class _Epilogue(ctypes.Structure):
     _fields_ = [("up_bias", _p), ("gate_bias", _p), ("up_scale", _p), ("gate_scale", _p),
-                ("glu_op", ctypes.c_int), ("limit", ctypes.c_double), ("alpha", ctypes.c_double)]
+                ("glu_op", ctypes.c_int), ("limit", ctypes.c_double)]
 
 
 def _epilogue(epi: dict | None, keep: list):
     """dict(up_bias=, gate_bias=, up_scale=, gate_scale= (arrays or None),
-    glu_op=, limit=, alpha=) -> ctypes struct (arrays kept alive in keep)."""
+    glu_op=, limit=) -> ctypes struct (arrays kept alive in keep)."""
     if epi is None:
         return None
     e = _Epilogue()
@@ -82,7 +82,6 @@ def _epilogue(epi: dict | None, keep: list):
             setattr(e, name, a.ctypes.data)
     e.glu_op = int(epi.get("glu_op", GLU_PLAIN))
     e.limit = float(epi.get("limit", 0.0))
-    e.alpha = float(epi.get("alpha", 0.0))
     return ctypes.byref(e), e
 
 
@@ -103,7 +102,7 @@ def _load(path: str):
     L.orc_mmvq_id_glu.argtypes = [_p, _p, _c_i64, ctypes.c_int, ctypes.c_int, _c_i64,
                                   _c_i64, _p, _c_i64, _p, ctypes.c_int, ctypes.c_int, _p]
     L.orc_glu.argtypes = [ctypes.c_int, ctypes.c_double, ctypes.c_double, ctypes.c_double,
-                          ctypes.c_double, ctypes.POINTER(ctypes.c_double)]
+                          ctypes.POINTER(ctypes.c_double)]
     L.orc_mmvq_ex.argtypes = [_p, _p, ctypes.c_int, _c_i64, _c_i64, _p, _c_i64,
                               ctypes.POINTER(_Epilogue), _p]
     L.orc_mmvq_id_ex.argtypes = [_p, _p, _c_i64, ctypes.c_int, ctypes.c_int, _c_i64, _c_i64,
@@ -178,6 +177,32 @@ class Oracle:
                                    _ptr(out), _ptr(mag), dptr))
         return out, mag, dots
 
+    def mmvq_threaded(self, W, wtype: int, M: int, K: int, y_q: np.ndarray, n: int,
+                      threads: int | None = None):
+        """All rows, split into contiguous row ranges over host threads (the
+        C call releases the interpreter lock). Returns (out [n, M], mag [n, M])."""
+        import concurrent.futures as cf
+        Wb = _u8(W)
+        y = _u8(y_q)
+        out = np.full((n, M), np.nan)
+        mag = np.full((n, M), np.nan)
+        threads = threads or min(16, os.cpu_count() or 1)
+        cuts = np.linspace(0, M, min(threads, M) + 1).astype(np.int64)
+
+        def run(i):
+            _check(self.L.orc_mmvq_rows(_ptr(Wb), wtype, M, K, _ptr(y), n, int(cuts[i]), int(cuts[i + 1]),
+                                       _ptr(out), _ptr(mag), None))
+
+        with cf.ThreadPoolExecutor(max_workers=len(cuts) - 1) as ex:
+            list(ex.map(run, range(len(cuts) - 1)))
+        return out, mag
+
+    def glu_array(self, glu_op: int, g: np.ndarray, u: np.ndarray, limit: float = 0.0) -> np.ndarray:
+        """orc_glu applied elementwise."""
+        gf, uf = np.asarray(g, dtype=np.float64).reshape(-1), np.asarray(u, dtype=np.float64).reshape(-1)
+        return np.array([self.glu(glu_op, float(a), float(b), limit) for a, b in zip(gf, uf)]).reshape(
+            np.shape(g))
+
     def mmvq_glu(self, Wg, Wu, wtype: int, M: int, K: int, y_q: np.ndarray, n: int,
                  glu_op: int = GLU_SWIGLU) -> np.ndarray:
         out = np.zeros((n, M))
@@ -205,9 +230,9 @@ class Oracle:
                                      glu_op, _ptr(out)))
         return out
 
-    def glu(self, glu_op: int, g: float, u: float, limit: float = 0.0, alpha: float = 0.0) -> float:
+    def glu(self, glu_op: int, g: float, u: float, limit: float = 0.0) -> float:
         out = ctypes.c_double()
-        _check(self.L.orc_glu(glu_op, g, u, limit, alpha, ctypes.byref(out)))
+        _check(self.L.orc_glu(glu_op, g, u, limit, ctypes.byref(out)))
         return out.value
 
     def mmvq_ex(self, Wu, Wg, wtype: int, M: int, K: int, y_q: np.ndarray, n: int,

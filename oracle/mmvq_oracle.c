@@ -395,13 +395,64 @@ int orc_mmvq(const uint8_t *W, int type, int64_t M, int64_t K,
 /* ------------------------------------------------------------------------ */
 /* GLU epilogue [MMVQ §融合]                                                 */
 /* ------------------------------------------------------------------------ */
-/* silu is named on the page without a formula; taken as z * sigmoid(z). */
-static double glu_apply(int glu_op, double g, double u) {
-    if (glu_op == ORC_GLU_SWIGLU) return g / (1.0 + exp(-g)) * u;
-    return g * u;
+/* The page's epilogue switch names the GLU ops and the device functions
+ * that apply them, without their bodies. Readings (parity unpinned against
+ * the pages, which fix none of these formulas):
+ *  - SWIGLU: silu(g)*u with silu(z) = z*sigmoid(z), the Swish-1 / SiLU of
+ *    the GLU-variants literature (Shazeer, "GLU Variants Improve
+ *    Transformer", 2020).
+ *  - GEGLU: gelu(g)*u with gelu in the tanh form published with GELU
+ *    (Hendrycks and Gimpel, "Gaussian Error Linear Units", 2016):
+ *    0.5*z*(1 + tanh(sqrt(2/pi)*(z + 0.044715*z^3))). The op list on the
+ *    page has a single GEGLU entry; the operator set it comes from keeps
+ *    the exact erf form as a separate op, so the plain entry is read as the
+ *    tanh form.
+ *  - SWIGLU_OAI: the clamped SwiGLU published with the gpt-oss models,
+ *    g'*sigmoid(alpha*g')*(u' + 1) with g' = min(g, limit),
+ *    u' = clamp(u, -limit, limit) and that publication's constants
+ *    alpha = 1.702, limit = 7. The page calls it with the gate and the up
+ *    value only, so the constants are the op's own, not parameters.
+ *  - SWIGLU_CLAMP: the page passes the caller's glu_limit; taken as the same
+ *    clamps around a plain SwiGLU, silu(g')*u'. No public definition is
+ *    known to this reading beyond the call. */
+#define ORC_OAI_ALPHA 1.702
+#define ORC_OAI_LIMIT 7.0
+
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+static double gelu_tanh(double z) {
+    const double c = sqrt(2.0 / 3.14159265358979323846);
+    return 0.5 * z * (1.0 + tanh(c * (z + 0.044715 * z * z * z)));
 }
 
-static int valid_glu(int glu_op) { return glu_op == ORC_GLU_PLAIN || glu_op == ORC_GLU_SWIGLU; }
+int orc_glu(int glu_op, double g, double u, double limit, double *out) {
+    if (!out) return ORC_ERR_NULL;
+    switch (glu_op) {
+    case ORC_GLU_PLAIN: *out = g * u; break;
+    case ORC_GLU_SWIGLU: *out = silu(g) * u; break;
+    case ORC_GLU_GEGLU: *out = gelu_tanh(g) * u; break;
+    case ORC_GLU_SWIGLU_OAI: {
+        const double gc = g < ORC_OAI_LIMIT ? g : ORC_OAI_LIMIT;
+        const double uc = u < -ORC_OAI_LIMIT ? -ORC_OAI_LIMIT : (u > ORC_OAI_LIMIT ? ORC_OAI_LIMIT : u);
+        *out = gc / (1.0 + exp(-ORC_OAI_ALPHA * gc)) * (uc + 1.0);
+        break;
+    }
+    case ORC_GLU_SWIGLU_CLAMP: {
+        const double gc = g < limit ? g : limit;
+        const double uc = u < -limit ? -limit : (u > limit ? limit : u);
+        *out = silu(gc) * uc;
+        break;
+    }
+    default: return ORC_ERR_TYPE;
+    }
+    return ORC_OK;
+}
+
+/* Ops the plain fused calls take: those with no caller parameter. */
+static int valid_glu(int glu_op) {
+    return glu_op == ORC_GLU_PLAIN || glu_op == ORC_GLU_SWIGLU || glu_op == ORC_GLU_GEGLU ||
+           glu_op == ORC_GLU_SWIGLU_OAI;
+}
 
 int orc_mmvq_glu(const uint8_t *W_gate, const uint8_t *W_up, int type,
                  int64_t M, int64_t K, const uint8_t *y_q, int64_t n,
@@ -418,7 +469,8 @@ int orc_mmvq_glu(const uint8_t *W_gate, const uint8_t *W_up, int type,
             double g, u, mg;
             row_dot(W_gate + r * nb * bb, type, nb, bb, qk, y_q + j * ycol_bytes, &g, &mg, NULL);
             row_dot(W_up + r * nb * bb, type, nb, bb, qk, y_q + j * ycol_bytes, &u, &mg, NULL);
-            out[j * M + r] = glu_apply(glu_op, g, u);
+            rc = orc_glu(glu_op, g, u, 0.0, &out[j * M + r]);
+            if (rc) return rc;
         }
     }
     return ORC_OK;
@@ -427,27 +479,6 @@ int orc_mmvq_glu(const uint8_t *W_gate, const uint8_t *W_up, int type,
 /* ------------------------------------------------------------------------ */
 /* Full fused epilogue [MMVQ §融合]                                           */
 /* ------------------------------------------------------------------------ */
-/* The pages name the GLU variants but print only the silu one. Readings:
- * gelu is the exact z*Phi(z) = z/2*(1 + erf(z/sqrt 2)); the OAI variant is
- * the published clamped form g'*sigmoid(alpha*g')*(u'+1); the clamp variant
- * is silu(g')*u'; g' = min(g, limit), u' = clamp(u, -limit, limit). */
-static double silu(double z) { return z / (1.0 + exp(-z)); }
-
-int orc_glu(int glu_op, double g, double u, double limit, double alpha, double *out) {
-    if (!out) return ORC_ERR_NULL;
-    const double gc = g < limit ? g : limit;
-    const double uc = u < -limit ? -limit : (u > limit ? limit : u);
-    switch (glu_op) {
-    case ORC_GLU_PLAIN: *out = g * u; break;
-    case ORC_GLU_SWIGLU: *out = silu(g) * u; break;
-    case ORC_GLU_GEGLU: *out = 0.5 * g * (1.0 + erf(g / sqrt(2.0))) * u; break;
-    case ORC_GLU_SWIGLU_OAI: *out = gc / (1.0 + exp(-alpha * gc)) * (uc + 1.0); break;
-    case ORC_GLU_SWIGLU_CLAMP: *out = silu(gc) * uc; break;
-    default: return ORC_ERR_TYPE;
-    }
-    return ORC_OK;
-}
-
 /* One output: raw dots of the up (and gate) row, then the epilogue, with
  * the scales and biases of expert e (0 outside the expert-indexed form). */
 static int epilogue_one(const orc_epilogue *epi, int has_gate, int e, int64_t M, int64_t r,
@@ -466,7 +497,7 @@ static int epilogue_one(const orc_epilogue *epi, int has_gate, int e, int64_t M,
     double g = gate;
     if (epi->gate_scale) g *= epi->gate_scale[e];
     if (epi->gate_bias) g += epi->gate_bias[(int64_t)e * M + r];
-    return orc_glu(epi->glu_op, g, u, epi->limit, epi->alpha, out);
+    return orc_glu(epi->glu_op, g, u, epi->limit, out);
 }
 
 int orc_mmvq_ex(const uint8_t *W_up, const uint8_t *W_gate, int type,
@@ -587,7 +618,7 @@ int orc_mmvq_id_ex(const uint8_t *W_up, const uint8_t *W_gate,
                 if (shared_gate) {
                     row_dot(shared_gate + r * nb * bb, type, nb, bb, qk, yt, &g, &mag, NULL);
                     rc = orc_glu(epi ? epi->glu_op : ORC_GLU_PLAIN, g, u, epi ? epi->limit : 0.0,
-                                 epi ? epi->alpha : 0.0, &shared_out[t * M + r]);
+                                 &shared_out[t * M + r]);
                     if (rc) return rc;
                 } else {
                     shared_out[t * M + r] = u;

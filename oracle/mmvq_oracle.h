@@ -49,9 +49,9 @@ extern "C" {
 
 #define ORC_GLU_PLAIN        0 /* out = gate * up (the epilogue's default branch) */
 #define ORC_GLU_SWIGLU       1 /* out = silu(gate) * up                          */
-#define ORC_GLU_GEGLU        2 /* out = gelu(gate) * up, gelu exact (erf form)    */
-#define ORC_GLU_SWIGLU_OAI   3 /* out = g' * sigmoid(alpha*g') * (u' + 1)         */
-#define ORC_GLU_SWIGLU_CLAMP 4 /* out = silu(g') * u'                             */
+#define ORC_GLU_GEGLU        2 /* out = gelu(gate) * up, gelu in its tanh form    */
+#define ORC_GLU_SWIGLU_OAI   3 /* out = g' * sigmoid(1.702*g') * (u' + 1), limit 7 */
+#define ORC_GLU_SWIGLU_CLAMP 4 /* out = silu(g') * u', caller's limit             */
 /* with g' = min(gate, limit), u' = min(max(up, -limit), limit). */
 
 #define ORC_OK          0
@@ -93,8 +93,10 @@ int orc_mmvq(const uint8_t *W, int type, int64_t M, int64_t K,
              const uint8_t *y_q, int64_t n, double *out, double *mag,
              int32_t *dots);
 
-/* out[j*M + r] = act(g) * u with g = W_gate row r . y_j, u = W_up row r . y_j,
- * act = silu (ORC_GLU_SWIGLU) or identity (ORC_GLU_PLAIN). */
+/* out[j*M + r] = orc_glu(glu_op, g, u) with g = W_gate row r . y_j and
+ * u = W_up row r . y_j. Ops that take no caller parameter only (PLAIN,
+ * SWIGLU, GEGLU, SWIGLU_OAI); ORC_ERR_TYPE for SWIGLU_CLAMP, whose limit
+ * only the epilogue form carries. */
 int orc_mmvq_glu(const uint8_t *W_gate, const uint8_t *W_up, int type,
                  int64_t M, int64_t K, const uint8_t *y_q, int64_t n,
                  int glu_op, double *out);
@@ -115,11 +117,10 @@ int orc_mmvq_id_glu(const uint8_t *W_gate, const uint8_t *W_up,
                     int64_t n_tokens, const int32_t *ids, int top_k,
                     int glu_op, double *out);
 
-/* The GLU of one gate value g and one up value u [MMVQ §融合]; limit and
- * alpha are used by the clamped variants only. ORC_ERR_TYPE for an unknown
- * op. */
-int orc_glu(int glu_op, double g, double u, double limit, double alpha,
-            double *out);
+/* The GLU of one gate value g and one up value u [MMVQ §融合]; limit is used
+ * by SWIGLU_CLAMP only (SWIGLU_OAI has its own constants). ORC_ERR_TYPE for
+ * an unknown op. */
+int orc_glu(int glu_op, double g, double u, double limit, double *out);
 
 /* Fused epilogue [MMVQ §融合], applied in the order the pages list it:
  * u = up_dot * up_scale + up_bias[r]; with a gate matrix,
@@ -133,8 +134,7 @@ typedef struct {
     const double *up_scale;
     const double *gate_scale;
     int glu_op;
-    double limit;
-    double alpha;
+    double limit;      /* SWIGLU_CLAMP */
 } orc_epilogue;
 
 /* out[j*M + r] for r < M, j < n. W_gate may be NULL (no gate). */

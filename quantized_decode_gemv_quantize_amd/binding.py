@@ -33,15 +33,15 @@ _p = ctypes.c_void_p
 class Epilogue(ctypes.Structure):
     """``mmvq_epilogue``: device pointers (ints, tensors via ``epilogue()``)."""
     _fields_ = [("up_bias", _p), ("gate_bias", _p), ("up_scale", _p), ("gate_scale", _p),
-                ("glu_op", _int), ("glu_limit", ctypes.c_float), ("glu_alpha", ctypes.c_float)]
+                ("glu_op", _int), ("glu_limit", ctypes.c_float)]
 
 
 def epilogue(up_bias=None, gate_bias=None, up_scale=None, gate_scale=None, glu_op: int = 0,
-             glu_limit: float = 0.0, glu_alpha: float = 0.0) -> Epilogue:
+             glu_limit: float = 0.0) -> Epilogue:
     e = Epilogue()
     e.up_bias, e.gate_bias = _addr(up_bias), _addr(gate_bias)
     e.up_scale, e.gate_scale = _addr(up_scale), _addr(gate_scale)
-    e.glu_op, e.glu_limit, e.glu_alpha = glu_op, glu_limit, glu_alpha
+    e.glu_op, e.glu_limit = glu_op, glu_limit
     return e
 
 
@@ -63,6 +63,7 @@ _SIGS = {
     "mmvq_id_ex": (_int, [_p, _p, _i64, _int, _int, _i64, _i64, _p, _p, _i64, _i64, _p, _int, _EP,
                           _p, _p, _p, _p, _p]),
     "mmvq_block_dots": (_int, [_p, _int, _i64, _i64, _p, _i64, _p, _p]),
+    "mmvq_read_probe": (_int, [_p, _i64, _p, _p]),
     "mmvq_strerror": (ctypes.c_char_p, [_int]),
 }
 
@@ -215,6 +216,10 @@ def mmvq_block_dots(W, wtype: int, M: int, K: int, y_q, n: int, dots, stream=Non
 # ---------------------------------------------------------------------------
 # Tensor-level conveniences (allocate outputs with torch, then call the ABI)
 # ---------------------------------------------------------------------------
+
+def mmvq_read_probe(src, nbytes: int, sink, stream=None) -> None:
+    _check("mmvq_read_probe", lib().mmvq_read_probe(_addr(src), nbytes, _addr(sink), _stream(stream)))
+
 
 def quantize(x, K: int | None = None, stream=None):
     """x: float32 CUDA tensor [n, ldx] -> uint8 tensor [n, (K/32)*36]."""

@@ -20,7 +20,7 @@ ARCH = "gfx950"
 
 SOURCES = ["api.hip", "quantize.hip", "kernels_q4_0.hip", "kernels_q8_0.hip", "kernels_q4_k.hip",
            "kernels_q6_k.hip", "kernels_q4_0_f32.hip", "kernels_q8_0_f32.hip", "kernels_q4_k_f32.hip",
-           "kernels_q6_k_f32.hip", "kernels_mmq.hip"]
+           "kernels_q6_k_f32.hip", "kernels_mmq.hip", "probe.hip"]
 
 # Packed fp32 VALU instructions stay disabled (hipcc forms them from plain
 # float code otherwise); fp32 division is correctly rounded and fp32

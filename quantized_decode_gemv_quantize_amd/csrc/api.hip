@@ -60,6 +60,10 @@ int check_gemv(const void* W, int type, int64_t M, int64_t K, const ActIn& in, i
 
 bool valid_glu(int op) { return op >= MMVQ_GLU_PLAIN && op <= MMVQ_GLU_SWIGLU_CLAMP; }
 
+// The GLU-only calls (no epilogue struct) take the ops without a caller
+// parameter; SWIGLU_CLAMP needs the limit that only mmvq_ex carries.
+int glu_only_op(int op) { return valid_glu(op) && op != MMVQ_GLU_SWIGLU_CLAMP ? MMVQ_OK : MMVQ_ERR_TYPE; }
+
 // Epilogue fields of RowArgs from a caller's (host) mmvq_epilogue.
 int set_epilogue(const mmvq_epilogue* epi, bool gate, RowArgs* a) {
   if (!epi) return MMVQ_OK;
@@ -73,7 +77,6 @@ int set_epilogue(const mmvq_epilogue* epi, bool gate, RowArgs* a) {
   a->gate_scale = gate ? epi->gate_scale : nullptr;
   a->glu_op = epi->glu_op;
   a->glu_limit = epi->glu_limit;
-  a->glu_alpha = epi->glu_alpha;
   return MMVQ_OK;
 }
 
@@ -214,6 +217,7 @@ int mmvq(const void* W, int type, int64_t M, int64_t K, const void* y_q, int64_t
 int mmvq_glu(const void* W_gate, const void* W_up, int type, int64_t M, int64_t K, const void* y_q, int64_t n,
              int glu_op, float* out, void* stream) {
   if (!W_gate) return MMVQ_ERR_NULL;
+  if (glu_only_op(glu_op)) return MMVQ_ERR_TYPE;
   const mmvq_epilogue e = glu_only(glu_op);
   return rows_common(W_up, W_gate, type, M, K, q8(y_q), n, &e, out, stream);
 }
@@ -228,6 +232,7 @@ int mmvq_id_glu(const void* W_gate, const void* W_up, int64_t expert_stride_byte
                 int64_t M, int64_t K, const void* y_q, int64_t n_tokens, const int32_t* ids, int top_k,
                 int glu_op, float* out, void* stream) {
   if (!W_gate) return MMVQ_ERR_NULL;
+  if (glu_only_op(glu_op)) return MMVQ_ERR_TYPE;
   const mmvq_epilogue e = glu_only(glu_op);
   return id_common(W_gate, W_up, expert_stride_bytes, n_experts, type, M, K, q8(y_q), n_tokens, ids, top_k, &e,
                    nullptr, nullptr, nullptr, out, stream);
@@ -242,6 +247,7 @@ int mmvq_f32(const void* W, int type, int64_t M, int64_t K, const float* x, int6
 int mmvq_glu_f32(const void* W_gate, const void* W_up, int type, int64_t M, int64_t K, const float* x, int64_t n,
                  int64_t ldx, int glu_op, float* out, void* stream) {
   if (!x || !W_gate) return MMVQ_ERR_NULL;
+  if (glu_only_op(glu_op)) return MMVQ_ERR_TYPE;
   const mmvq_epilogue e = glu_only(glu_op);
   return rows_common(W_up, W_gate, type, M, K, f32(x, ldx), n, &e, out, stream);
 }
@@ -258,6 +264,7 @@ int mmvq_id_glu_f32(const void* W_gate, const void* W_up, int64_t expert_stride_
                     int64_t M, int64_t K, const float* x, int64_t n_tokens, int64_t ldx, const int32_t* ids,
                     int top_k, int glu_op, float* out, void* stream) {
   if (!x || !W_gate) return MMVQ_ERR_NULL;
+  if (glu_only_op(glu_op)) return MMVQ_ERR_TYPE;
   const mmvq_epilogue e = glu_only(glu_op);
   return id_common(W_gate, W_up, expert_stride_bytes, n_experts, type, M, K, f32(x, ldx), n_tokens, ids, top_k,
                    &e, nullptr, nullptr, nullptr, out, stream);
@@ -289,6 +296,14 @@ int mmvq_block_dots(const void* W, int type, int64_t M, int64_t K, const void* y
   const int rc = check_gemv(W, type, M, K, q8(y_q), n, reinterpret_cast<const float*>(dots), &d, &a);
   if (rc) return rc;
   return d->block_dots(a.W, a.y, dots, M, K, n, static_cast<hipStream_t>(stream));
+}
+
+int mmvq_read_probe(const void* src, int64_t bytes, void* sink, void* stream) {
+  if (!src || !sink) return MMVQ_ERR_NULL;
+  if (bytes < 16 || bytes % 16 != 0 || bytes > (int64_t(1) << 40)) return MMVQ_ERR_SHAPE;
+  if (!aligned(src, 16) || !aligned(sink, 4)) return MMVQ_ERR_ALIGN;
+  return launch_read_probe(static_cast<const uint8_t*>(src), bytes, static_cast<uint32_t*>(sink),
+                           static_cast<hipStream_t>(stream));
 }
 
 const char* mmvq_strerror(int code) {

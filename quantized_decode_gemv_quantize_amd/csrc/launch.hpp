@@ -54,11 +54,24 @@ inline int check_launch() {
   return hipGetLastError() == hipSuccess ? MMVQ_OK : MMVQ_ERR_LAUNCH;
 }
 
-template <class F, bool XF, int NC, int G, int R, int P, int PASSES>
+template <class F, bool XF, int NC, int G, int R, int P, int PASSES, int DEPTH = 0>
 inline int launch_rows_r(const RowArgs& a, const Shape& s, hipStream_t st) {
-  hipLaunchKernelGGL((mmvq_rows_kernel<F, NC, R, P, G, XF, PASSES>), dim3(static_cast<unsigned>(s.blocks)),
+  hipLaunchKernelGGL((mmvq_rows_kernel<F, NC, R, P, G, XF, PASSES, DEPTH>), dim3(static_cast<unsigned>(s.blocks)),
                      dim3(s.teams_per_block * s.team_lanes), 0, st, a);
   return check_launch();
+}
+
+// Single-pass launch, with the pipelined rows of plan_depth for the fp32
+// forms (the q8_1 forms keep their short teams and issue every row first).
+template <class F, bool XF, int NC, int G, int R, int P>
+inline int launch_rows_d(const RowArgs& a, const Shape& s, hipStream_t st) {
+  if constexpr (XF && R >= 8) {
+    if (s.depth == 4) return launch_rows_r<F, XF, NC, G, R, P, 1, 4>(a, s, st);
+    if constexpr (R > 8)
+      if (s.depth == 8) return launch_rows_r<F, XF, NC, G, R, P, 1, 8>(a, s, st);
+  }
+  if (s.depth != 0) return MMVQ_ERR_SHAPE;
+  return launch_rows_r<F, XF, NC, G, R, P, 1>(a, s, st);
 }
 
 // Passes > 1 come only with R = the register budget (plan_rows).
@@ -72,14 +85,17 @@ inline int launch_rows_p(const RowArgs& a, const Shape& s, hipStream_t st) {
       return s.slots == 2 ? launch_rows_r<F, XF, NC, G, R, 2, 4>(a, s, st) : launch_rows_r<F, XF, NC, G, R, 1, 4>(a, s, st);
   }
   if (s.passes != 1) return MMVQ_ERR_SHAPE;
-  return s.slots == 2 ? launch_rows_r<F, XF, NC, G, R, 2, 1>(a, s, st)
-                      : launch_rows_r<F, XF, NC, G, R, 1, 1>(a, s, st);
+  return s.slots == 2 ? launch_rows_d<F, XF, NC, G, R, 2>(a, s, st) : launch_rows_d<F, XF, NC, G, R, 1>(a, s, st);
 }
 
 template <class F, bool XF, int NC, int G>
 inline int launch_rows_nc(RowArgs a, int64_t K, hipStream_t st) {
   constexpr int RMAX = rows_per_pass<F>(NC, G);
-  const Shape s = make_shape<F>(a.M, K, launch_max_rows<F>(XF, NC, G), launch_max_passes<F>(XF, NC, G));
+  Shape s = make_shape<F>(a.M, K, launch_max_rows<F>(XF, NC, G), launch_max_passes<F>(XF, NC, G));
+  if (XF) s.depth = plan_depth(s, device_cus());
+#ifdef QMV_TUNING
+  if (const char* e = getenv("MMVQ_DEPTH")) s.depth = XF ? atoi(e) : 0;
+#endif
   a.units = s.units;
   a.team_lanes = s.team_lanes;
   a.teams_per_block = s.teams_per_block;
@@ -218,6 +234,7 @@ const Dispatch& dispatch_q4_k_f32();
 const Dispatch& dispatch_q6_k_f32();
 
 int launch_quantize_q8_1(const float* x, uint8_t* y, int64_t K, int64_t n, int64_t ldx, hipStream_t st);
+int launch_read_probe(const uint8_t* src, int64_t bytes, uint32_t* sink, hipStream_t st);
 
 struct MmqArgs;
 int launch_mmq_q4k(const MmqArgs& a, hipStream_t st);

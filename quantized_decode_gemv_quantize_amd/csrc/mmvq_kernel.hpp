@@ -72,7 +72,6 @@ struct RowArgs {
   const float* up_scale;
   const float* gate_scale;
   float glu_limit;
-  float glu_alpha;
   // id mode: shared expert in the extra grid slice blockIdx.y == n_experts
   int n_experts;
   const uint8_t* Ws_up;
@@ -80,16 +79,23 @@ struct RowArgs {
   float* shared_out;
 };
 
-// GLU ops of the fused epilogue [MMVQ §融合]: 0 gate*up, 1 silu(gate)*up,
-// 2 gelu(gate)*up (exact erf form), 3 g'*sigmoid(alpha*g')*(u'+1),
-// 4 silu(g')*u', with g' = min(gate, limit), u' = clamp(up, -limit, limit).
-__device__ __forceinline__ float glu(int op, float gate, float up, float limit, float alpha) {
+// GLU ops of the fused epilogue [MMVQ §融合] (the page names them, its
+// switch calls the device functions without their bodies): 0 gate*up,
+// 1 silu(gate)*up, 2 gelu(gate)*up with gelu in its tanh form
+// 0.5*z*(1 + tanh(sqrt(2/pi)*(z + 0.044715*z^3))), 3 the clamped SwiGLU
+// published with the gpt-oss models, g'*sigmoid(1.702*g')*(u'+1) with
+// g' = min(gate, 7), u' = clamp(up, -7, 7) (the page passes it no
+// parameter), 4 silu(g')*u' with the caller's limit in the same clamps.
+__device__ __forceinline__ float glu(int op, float gate, float up, float limit) {
   switch (op) {
     case 1: return gate / (1.0f + __expf(-gate)) * up;
-    case 2: return 0.5f * gate * (1.0f + erff(gate * 0.70710678118654752f)) * up;
+    case 2: {
+      const float t = tanhf(0.7978845608028654f * (gate + 0.044715f * gate * gate * gate));
+      return 0.5f * gate * (1.0f + t) * up;
+    }
     case 3: {
-      const float g = fminf(gate, limit), u = fminf(fmaxf(up, -limit), limit);
-      return g / (1.0f + __expf(-alpha * g)) * (u + 1.0f);
+      const float g = fminf(gate, 7.0f), u = fminf(fmaxf(up, -7.0f), 7.0f);
+      return g / (1.0f + __expf(-1.702f * g)) * (u + 1.0f);
     }
     case 4: {
       const float g = fminf(gate, limit), u = fminf(fmaxf(up, -limit), limit);
@@ -122,7 +128,15 @@ struct RedLds {
 // PASSES: the team owns PASSES * R * P consecutive rows and takes them R * P
 // at a time, loading its activation slice once (the expert-indexed kernel
 // uses this to keep R*P rows of loads in flight whatever the column count).
-template <class F, int NC, int R, int P, int G, bool ID, bool XF, int VMAX, int PASSES = 1>
+// DEPTH (single pass only; 0 = off): software-pipelined rows. Only the first
+// DEPTH rows' loads are issued up front; row i is computed as soon as it has
+// landed and only then are row i + DEPTH's loads issued. Without it a wave
+// issues all R rows' loads first, and under a saturated memory system those
+// issues stall (the queue only takes a load when an older one drains), so
+// the wave sits in its load issues while its first rows have landed and then
+// computes all R rows after its last row arrives; with it the arithmetic
+// runs while the later rows stream.
+template <class F, int NC, int R, int P, int G, bool ID, bool XF, int VMAX, int PASSES = 1, int DEPTH = 0>
 __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
                                           const uint8_t* Wbase, const uint8_t* Wgbase,
                                           RedLds<G, VMAX>& red) {
@@ -191,11 +205,13 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
   typename F::Wt wgb[NB][G == 2 ? R : 1];
   // uniform row pointers; the slot's row is a per-lane 32-bit offset
   const uint32_t slot_off = static_cast<uint32_t>(slot * a.row_bytes);
-  auto issue = [&](typename F::Wt (&w)[R], typename F::Wt (&wg)[G == 2 ? R : 1], int64_t r0) {
-    const uint8_t* rp = Wb + r0 * a.row_bytes;
-    const uint8_t* gp = (G == 2) ? Wgb + r0 * a.row_bytes : nullptr;
+  static_assert(DEPTH == 0 || (PASSES == 1 && DEPTH < R), "pipelined rows: one pass, depth below R");
+  constexpr int FIRST = DEPTH > 0 ? DEPTH : R;      // rows issued up front
+  auto issue = [&](typename F::Wt (&w)[R], typename F::Wt (&wg)[G == 2 ? R : 1], int64_t r0, int i0, int i1) {
+    const uint8_t* rp = Wb + r0 * a.row_bytes + i0 * step;
+    const uint8_t* gp = (G == 2) ? Wgb + r0 * a.row_bytes + i0 * step : nullptr;
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
+    for (int i = i0; i < i1; ++i) {
       F::load_wt(w[i], rp, slot_off, L);
       rp += step;
       if constexpr (G == 2) {
@@ -207,7 +223,7 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  issue(wb[0], wgb[0], row0);
+  issue(wb[0], wgb[0], row0, 0, FIRST);
   // the activation loads were issued before the weight loads, so they
   // retire first: this waits for them only
   if constexpr (XE) {
@@ -230,7 +246,7 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
     row0 += RP;
     skip -= RP;
   }
-  if (pass + 1 < PASSES) issue(wb[(pass + 1) % NB], wgb[(pass + 1) % NB], row0 + RP);
+  if (pass + 1 < PASSES) issue(wb[(pass + 1) % NB], wgb[(pass + 1) % NB], row0 + RP, 0, R);
   typename F::Wt (&w)[R] = wb[pass % NB];
   typename F::Wt (&wg)[G == 2 ? R : 1] = wgb[pass % NB];
   // ---- per row: decode once, one partial per column ----------------------
@@ -258,6 +274,11 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
 #pragma unroll
       for (int j = 0; j < NC; ++j) put(1, j, i, F::col_dot(dec, act[j]));
     }
+    if constexpr (DEPTH > 0) {
+      // row i's arithmetic stays ahead of the next issue
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + DEPTH < R) issue(w, wg, row0, i + DEPTH, i + DEPTH + 1);
+    }
   }
 
   // ---- reduce over the team ----------------------------------------------
@@ -275,7 +296,7 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
       if (gate_scale) gate *= gate_scale[e];
       if (gate_bias) gate += gate_bias[e * a.M + r];
     }
-    const float v = (G == 2) ? glu(a.glu_op, gate, up, a.glu_limit, a.glu_alpha) : up;
+    const float v = (G == 2) ? glu(a.glu_op, gate, up, a.glu_limit) : up;
     if constexpr (ID) {
       // select column j's token and slots with compile-time indices
       uint64_t m = 0;
@@ -332,7 +353,7 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
 
 // Plain / fused kernel: columns 0..NC-1 of y; a team owns PASSES * R * P
 // rows, taken R * P at a time.
-template <class F, int NC, int R, int P, int G, bool XF, int PASSES>
+template <class F, int NC, int R, int P, int G, bool XF, int PASSES, int DEPTH = 0>
 __global__ void __launch_bounds__(kLaunchBound) mmvq_rows_kernel(RowArgs a) {
   Cols cols;
   cols.n = NC;
@@ -340,7 +361,7 @@ __global__ void __launch_bounds__(kLaunchBound) mmvq_rows_kernel(RowArgs a) {
   for (int j = 0; j < kMaxCols; ++j) { cols.tok[j] = j; cols.slots[j] = 0; }
   constexpr int V = pow2ceil(NC * R * P);
   __shared__ RedLds<G, V> red;
-  rows_body<F, NC, R, P, G, false, XF, V, PASSES>(a, cols, a.W, a.Wg, red);
+  rows_body<F, NC, R, P, G, false, XF, V, PASSES, DEPTH>(a, cols, a.W, a.Wg, red);
 }
 
 // Expert-indexed kernel: blockIdx.y = expert. The token list is the same for

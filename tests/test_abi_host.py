@@ -18,7 +18,7 @@ def test_exports_every_declared_symbol(L):
     names = B.declared_symbols()
     assert set(names) == {"mmvq_type_info", "mmvq_quantize_q8_1", "mmvq", "mmvq_glu", "mmvq_id",
                           "mmvq_id_glu", "mmvq_f32", "mmvq_glu_f32", "mmvq_id_f32", "mmvq_id_glu_f32",
-                          "mmvq_ex", "mmvq_id_ex", "mmvq_block_dots", "mmvq_strerror"}
+                          "mmvq_ex", "mmvq_id_ex", "mmvq_block_dots", "mmvq_read_probe", "mmvq_strerror"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -72,6 +72,13 @@ def test_mmvq_argument_checks(L, args, code):
 def test_other_entry_points_argument_checks(L):
     assert L.mmvq_glu(None, P16, B.Q4_K, 1, 256, P16, 1, 1, P16, None) == B.ERR_NULL
     assert L.mmvq_glu(P16, P16, B.Q4_K, 1, 256, P16, 1, 7, P16, None) == B.ERR_TYPE
+    # the clamp op needs a limit, which only the epilogue form carries
+    assert L.mmvq_glu(P16, P16, B.Q4_K, 1, 256, P16, 1, B.GLU_SWIGLU_CLAMP, P16, None) == B.ERR_TYPE
+    assert L.mmvq_glu_f32(P16, P16, B.Q4_K, 1, 256, P16, 1, 256, B.GLU_SWIGLU_CLAMP, P16, None) == B.ERR_TYPE
+    assert L.mmvq_read_probe(None, 64, P16, None) == B.ERR_NULL
+    assert L.mmvq_read_probe(P16, 0, P16, None) == B.ERR_SHAPE
+    assert L.mmvq_read_probe(P16, 24, P16, None) == B.ERR_SHAPE
+    assert L.mmvq_read_probe(P4, 64, P16, None) == B.ERR_ALIGN
     assert L.mmvq_glu(P4, P16, B.Q4_K, 1, 256, P16, 1, 1, P16, None) == B.ERR_ALIGN
     assert L.mmvq_id(P16, 288, 4, B.Q4_K, 2, 256, P16, 1, None, 1, P16, None) == B.ERR_NULL
     assert L.mmvq_id(P16, 144, 4, B.Q4_K, 2, 256, P16, 1, P16, 1, P16, None) == B.ERR_SHAPE

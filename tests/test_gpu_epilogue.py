@@ -64,13 +64,13 @@ def test_mmvq_ex(O, wtype, M, K, n, op, gate, f32):
     x = synth.activations(K, n, rng)
     # biases and scales of the order of the products (|dot| ~ 1..10)
     epi = dict(up_bias=rng.standard_normal(M).astype(np.float32),
-               up_scale=np.float32([rng.uniform(0.5, 1.5)]), glu_op=op, limit=3.0, alpha=1.702)
+               up_scale=np.float32([rng.uniform(0.5, 1.5)]), glu_op=op, limit=3.0)
     if gate:
         epi.update(gate_bias=rng.standard_normal(M).astype(np.float32),
                    gate_scale=np.float32([rng.uniform(0.1, 0.4)]))
     tens = {k: dev(v) for k, v in epi.items() if isinstance(v, np.ndarray)}
     e = B.epilogue(up_bias=tens["up_bias"], up_scale=tens["up_scale"], gate_bias=tens.get("gate_bias"),
-                   gate_scale=tens.get("gate_scale"), glu_op=op, glu_limit=3.0, glu_alpha=1.702)
+                   gate_scale=tens.get("gate_scale"), glu_op=op, glu_limit=3.0)
     out = _nan(n, M)
     Wud, Wgd = dev(Wu), (dev(Wg) if gate else None)
     if f32:
@@ -142,10 +142,10 @@ def test_mmvq_id_ex_shared_expert(O, name, wtype, E, M, K, ids, op, f32):
     epi = dict(up_bias=rng.standard_normal(E * M).astype(np.float32),
                gate_bias=rng.standard_normal(E * M).astype(np.float32),
                up_scale=rng.uniform(0.5, 1.5, E).astype(np.float32),
-               gate_scale=rng.uniform(0.1, 0.4, E).astype(np.float32), glu_op=op, limit=3.0, alpha=1.702)
+               gate_scale=rng.uniform(0.1, 0.4, E).astype(np.float32), glu_op=op, limit=3.0)
     tens = {k: dev(v) for k, v in epi.items() if isinstance(v, np.ndarray)}
     e = B.epilogue(up_bias=tens["up_bias"], gate_bias=tens["gate_bias"], up_scale=tens["up_scale"],
-                   gate_scale=tens["gate_scale"], glu_op=op, glu_limit=3.0, glu_alpha=1.702)
+                   gate_scale=tens["gate_scale"], glu_op=op, glu_limit=3.0)
     out, sh = _nan(T * top_k, M), _nan(T, M)
     act = (None, dev(x), K) if f32 else (gpu_quantize(x), None, 0)
     B.mmvq_id_ex(dev(pad(Wu)), dev(pad(Wg)), stride, E, wtype, M, K, *act, T, dev(ids), top_k, e,
@@ -163,7 +163,7 @@ def test_mmvq_id_ex_shared_expert(O, name, wtype, E, M, K, ids, op, f32):
             _check(got[t * top_k + k:t * top_k + k + 1], ref, tol, f"{name} token {t} slot {k}")
         u, mu, _ = O.mmvq(Su, wtype, M, K, y[t:t + 1], 1)
         g, mg, _ = O.mmvq(Sg, wtype, M, K, y[t:t + 1], 1)
-        ref, tol = epilogue_tolerance(g, u, mg, mu, dict(glu_op=op, limit=3.0, alpha=1.702))
+        ref, tol = epilogue_tolerance(g, u, mg, mu, dict(glu_op=op, limit=3.0))
         _check(got_sh[t:t + 1], ref, tol, f"{name} shared token {t}")
     # the oracle's own id form agrees with the per-slot composition used above
     o_out, o_sh = O.mmvq_id_ex(pad(Wu), pad(Wg), stride, E, wtype, M, K, y, T, ids, top_k, oepi, Su, Sg)

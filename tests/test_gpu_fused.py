@@ -12,8 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_helpers import (TNAME, announce, assert_close, dev, glu_tolerance, gpu_quantize, host, oracle_rows,
-                         sample_rows, special_x)
+from gpu_helpers import TNAME, announce, assert_close, dev, glu_tolerance, gpu_quantize, host, special_x
 from quantized_decode_gemv_quantize_amd import binding as B
 from quantized_decode_gemv_quantize_amd import synth
 
@@ -121,7 +120,7 @@ def test_mmvq_glu_f32(O, wtype, M, K, n, op):
     y = O.quantize_q8_1(x, K)
     g, mg, _ = O.mmvq(Wg, wtype, M, K, y, n)
     u, mu, _ = O.mmvq(Wu, wtype, M, K, y, n)
-    ref = (g / (1.0 + np.exp(-g)) if op == B.GLU_SWIGLU else g) * u
+    ref = O.mmvq_glu(Wg, Wu, wtype, M, K, y, n, op)
     tol = glu_tolerance(g, u, mg, mu, ref, op)
     got = host(fused).astype(np.float64)
     bad = ~(np.abs(got - ref) <= tol)
@@ -162,23 +161,34 @@ def test_mmvq_id_f32(O, name, wtype, E, M, K, ids, fused_glu):
         B.mmvq_id_f32(Wud, stride, E, wtype, M, K, xd, T, ldx, idsd, top_k, fused)
         B.mmvq_id(Wud, stride, E, wtype, M, K, yd, T, idsd, top_k, two)
     _same(fused, two, f"id f32 {name}")
-    # oracle on the plain form (the fused GLU form is pinned to mmvq_id_glu,
-    # whose own oracle parity is tested with the q8_1 entry points)
-    if not fused_glu:
-        y = O.quantize_q8_1(x, K)
-        got = host(fused).astype(np.float64)
-        for t in range(T):
-            for k in range(top_k):
-                u, mu = oracle_rows(O, Wu[int(ids[t, k])], wtype, M, K, y[t:t + 1], 1, [(0, M)])
-                assert_close(got[t * top_k + k:t * top_k + k + 1], u, mu, f"id f32 token {t} slot {k}")
+    _id_against_oracle(O, host(fused), Wu, Wg if fused_glu else None, wtype, M, K, x, ids, f"id f32 {name}")
 
 
-def test_mmvq_id_glu_f32_moe_workload():
+def _id_against_oracle(O, got, Wu, Wg, wtype, M, K, x, ids, what):
+    """Every (token, slot) row of an expert-indexed result against the oracle:
+    the up product alone (Wg None) or SWIGLU of the gate and up products."""
+    y = O.quantize_q8_1(x, K)
+    T, top_k = ids.shape
+    got = np.asarray(got, dtype=np.float64)
+    for t in range(T):
+        for k in range(top_k):
+            e, s = int(ids[t, k]), t * top_k + k
+            u, mu = O.mmvq_threaded(Wu[e], wtype, M, K, y[t:t + 1], 1)
+            if Wg is None:
+                assert_close(got[s:s + 1], u, mu, f"{what} token {t} slot {k}")
+                continue
+            g, mg = O.mmvq_threaded(Wg[e], wtype, M, K, y[t:t + 1], 1)
+            ref = O.glu_array(B.GLU_SWIGLU, g, u)
+            tol = glu_tolerance(g, u, mg, mu, ref, B.GLU_SWIGLU)
+            bad = ~(np.abs(got[s:s + 1] - ref) <= tol)
+            assert not bad.any(), f"{what} token {t} slot {k} expert {e}: first {np.argwhere(bad)[0]}"
+
+
+def test_mmvq_id_glu_f32_moe_workload(O):
     """The MoE workload (8 experts, 8 tokens, top-2, Q4_K 14336x4096 gate
     and up) through the fused fp32 form, in the launch configuration the
-    benchmark times: every output bit-identical to quantize + mmvq_id_glu
-    (whose oracle parity on the same data is tested with the q8_1 entry
-    points)."""
+    benchmark times: every output bit-identical to quantize + mmvq_id_glu,
+    and every row of every slot against the oracle."""
     wl = synth.BY_NAME["moe_q4_k_8x14336x4096"]
     announce("mmvq_id_glu_f32 moe workload")
     d = synth.make(wl, 8)
@@ -193,6 +203,7 @@ def test_mmvq_id_glu_f32_moe_workload():
     B.mmvq_id_glu_f32(Wgd, Wud, stride, E, wl.wtype, M, K, xd, T, x.shape[1], idsd, top_k, B.GLU_SWIGLU, fused)
     B.mmvq_id_glu(Wgd, Wud, stride, E, wl.wtype, M, K, gpu_quantize(x, K), T, idsd, top_k, B.GLU_SWIGLU, two)
     _same(fused, two, "id_glu f32 moe workload")
+    _id_against_oracle(O, host(fused), d["W_up"], d["W_gate"], wl.wtype, M, K, x, ids, "id_glu f32 moe workload")
 
 
 WORKLOADS_F32 = [("q4_k_4096x14336", 1), ("q4_k_4096x14336", 2), ("q4_k_4096x14336", 8),
@@ -204,7 +215,7 @@ WORKLOADS_F32 = [("q4_k_4096x14336", 1), ("q4_k_4096x14336", 2), ("q4_k_4096x143
 def test_mmvq_f32_workload(O, name, n):
     """Workload sizes in the launch configuration the benchmark times: all
     rows bit-identical to the two-step path (Q4_K at 6..8 columns: both
-    forms against the oracle instead), sampled rows against the oracle."""
+    forms against the oracle instead), and every row against the oracle."""
     wl = synth.BY_NAME[name]
     announce(f"mmvq_f32 workload {name} n={n}")
     d = synth.make(wl, n)
@@ -215,17 +226,14 @@ def test_mmvq_f32_workload(O, name, n):
     B.mmvq_f32(Wd, wl.wtype, M, K, xd, n, x.shape[1], fused)
     B.mmvq(Wd, wl.wtype, M, K, gpu_quantize(x, K), n, two)
     y = O.quantize_q8_1(x, K)
-    ranges = sample_rows(M, 256, seed=n)
-    ref, mag = oracle_rows(O, W, wl.wtype, M, K, y, n, ranges)
+    ref, mag = O.mmvq_threaded(W, wl.wtype, M, K, y, n)
     got = host(fused)
-    sel = np.concatenate([np.arange(a, b) for a, b in ranges])
     if _mmq_route(wl.wtype, n):
-        # the two-step form runs the many-column kernel: both against the
-        # oracle on the sampled rows
-        assert_close(host(two)[:, sel], ref[:, sel], mag[:, sel], f"mmvq {name} n={n}")
+        # the two-step form runs the many-column kernel: both against the oracle
+        assert_close(host(two), ref, mag, f"mmvq {name} n={n}")
     else:
         _same(fused, two, f"mmvq_f32 {name} n={n}")
-    assert_close(got[:, sel], ref[:, sel], mag[:, sel], f"mmvq_f32 {name} n={n}")
+    assert_close(got, ref, mag, f"mmvq_f32 {name} n={n}")
 
 
 def test_f32_graph_replay():

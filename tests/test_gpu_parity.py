@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 from gpu_helpers import (TNAME, announce, assert_close, dev, glu_tolerance, gpu_gemv, gpu_quantize, host,
-                         oracle_rows, sample_rows, special_x)
+                         special_x)
 from quantized_decode_gemv_quantize_amd import binding as B
 from quantized_decode_gemv_quantize_amd import synth
 
@@ -113,7 +113,7 @@ def test_gemv_parity(O, wtype, M, K, n):
 
 # ---------------------------------------------------------------------------
 # GEMV at the workload sizes, in the launch configuration the benchmark
-# times; the oracle checks sampled row ranges.
+# times; every row against the oracle (rows split over host threads).
 # ---------------------------------------------------------------------------
 FULL = [("q4_0_256x1024", 1), ("q4_k_4096x4096", 1), ("q4_k_4096x14336", 1),
         ("q4_k_4096x14336", 2), ("q4_k_4096x14336", 4), ("q4_k_4096x14336", 8),
@@ -123,7 +123,7 @@ FULL = [("q4_0_256x1024", 1), ("q4_k_4096x4096", 1), ("q4_k_4096x14336", 1),
 
 
 @pytest.mark.parametrize("name,n", FULL, ids=[f"{a}-n{b}" for a, b in FULL])
-def test_gemv_workload_sampled(O, name, n):
+def test_gemv_workload(O, name, n):
     wl = synth.BY_NAME[name]
     announce(f"mmvq workload {name} n={n}")
     data = synth.make(wl, n)
@@ -132,11 +132,8 @@ def test_gemv_workload_sampled(O, name, n):
     y = O.quantize_q8_1(x)
     assert np.array_equal(host(yd), y)
     got = gpu_gemv(dev(W), wl.wtype, wl.M, wl.K, yd, n)
-    ranges = sample_rows(wl.M, 256, seed=n) if wl.M > 512 else [(0, wl.M)]
-    ref, mag = oracle_rows(O, W, wl.wtype, wl.M, wl.K, y, n, ranges)
-    rows = np.concatenate([np.arange(a, b) for a, b in ranges])
-    assert_close(got[:, rows], ref[:, rows], mag[:, rows], f"{name} n={n}")
-    assert np.isfinite(got).all()
+    ref, mag = O.mmvq_threaded(W, wl.wtype, wl.M, wl.K, y, n)
+    assert_close(got, ref, mag, f"{name} n={n}")
 
 
 # ---------------------------------------------------------------------------
@@ -171,7 +168,7 @@ def test_glu_parity(O, wtype, M, K, n, op):
 # ---------------------------------------------------------------------------
 # Expert-indexed product (plain and fused)
 # ---------------------------------------------------------------------------
-def id_case(O, wtype, E, M, K, ids, fused, op=B.GLU_SWIGLU, rows=None, seed=0, data=None):
+def id_case(O, wtype, E, M, K, ids, fused, op=B.GLU_SWIGLU, seed=0, data=None):
     import torch
     T, top_k = ids.shape
     rng = np.random.default_rng(seed)
@@ -196,22 +193,19 @@ def id_case(O, wtype, E, M, K, ids, fused, op=B.GLU_SWIGLU, rows=None, seed=0, d
     else:
         B.mmvq_id(dev(Wu_buf), stride, E, wtype, M, K, yd, T, idsd, top_k, out)
     got = host(out).astype(np.float64)
-    ranges = rows or [(0, M)]
-    sel = np.concatenate([np.arange(a, b) for a, b in ranges])
     for t in range(T):
         for k in range(top_k):
             e = int(ids[t, k])
             s = t * top_k + k
-            g, mg = oracle_rows(O, Wg[e], wtype, M, K, y[t:t + 1], 1, ranges)
-            u, mu = oracle_rows(O, Wu[e], wtype, M, K, y[t:t + 1], 1, ranges)
+            u, mu = O.mmvq_threaded(Wu[e], wtype, M, K, y[t:t + 1], 1)
             if fused:
-                act = g / (1.0 + np.exp(-g)) if op == B.GLU_SWIGLU else g
-                ref = act * u
+                g, mg = O.mmvq_threaded(Wg[e], wtype, M, K, y[t:t + 1], 1)
+                ref = O.glu_array(op, g, u)
                 tol = glu_tolerance(g, u, mg, mu, ref, op)
-                bad = ~(np.abs(got[s:s + 1, sel] - ref[:, sel]) <= tol[:, sel])
+                bad = ~(np.abs(got[s:s + 1] - ref) <= tol)
                 assert not bad.any(), f"token {t} slot {k} expert {e}: {np.argwhere(bad)[0]}"
             else:
-                assert_close(got[s:s + 1, sel], u[:, sel], mu[:, sel], f"id token {t} slot {k}")
+                assert_close(got[s:s + 1], u, mu, f"id token {t} slot {k}")
 
 
 ID_CASES = [
@@ -235,14 +229,14 @@ def test_id_parity(O, name, wtype, E, M, K, ids, fused):
     id_case(O, wtype, E, M, K, np.asarray(ids), fused, seed=len(name))
 
 
-def test_id_glu_moe_workload_sampled(O):
+def test_id_glu_moe_workload(O):
     """The MoE workload (8 experts, 8 tokens, top-2, 14336x4096 gate and up)
-    in the launch configuration the benchmark times; sampled rows."""
+    in the launch configuration the benchmark times; every row of every slot."""
     wl = synth.BY_NAME["moe_q4_k_8x14336x4096"]
     announce("mmvq_id_glu moe workload")
     d = synth.make(wl, 8)
     id_case(O, wl.wtype, wl.n_experts, wl.M, wl.K, d["ids"], True,
-            rows=sample_rows(wl.M, 128, seed=3), data=(d["W_up"], d["W_gate"], d["x"]))
+            data=(d["W_up"], d["W_gate"], d["x"]))
 
 
 # ---------------------------------------------------------------------------

@@ -48,12 +48,19 @@ MUTATIONS = {
     "q6_k_offset_31": ("isum += (q6_k_code(blk, e) - 32)", "isum += (q6_k_code(blk, e) - 31)"),
     "q6_k_q8_block_map": ("const int64_t yb = qb + s / 2;", "const int64_t yb = qb + s % 8;"),
     "q6_k_scale_unsigned": ("return (int8_t)blk[192 + s];", "return blk[192 + s];"),
-    "glu_sigmoid_only": ("return g / (1.0 + exp(-g)) * u;", "return 1.0 / (1.0 + exp(-g)) * u;"),
+    "silu_sigmoid_only": ("static double silu(double z) { return z / (1.0 + exp(-z)); }",
+                          "static double silu(double z) { return 1.0 / (1.0 + exp(-z)); }"),
+    "glu_plain_for_silu": ("case ORC_GLU_SWIGLU: *out = silu(g) * u; break;",
+                           "case ORC_GLU_SWIGLU: *out = g * u; break;"),
     "id_slot_as_token": ("rc = orc_mmvq(We, type, M, K, y_q + t * (K / 32) * 36, 1,",
                          "rc = orc_mmvq(We, type, M, K, y_q + k * (K / 32) * 36, 1,"),
-    "gelu_erf_unscaled": ("erf(g / sqrt(2.0))", "erf(g)"),
-    "oai_no_plus_one": ("* (uc + 1.0); break;", "* uc; break;"),
-    "oai_alpha_dropped": ("exp(-alpha * gc)", "exp(-gc)"),
+    "gelu_cubic_dropped": ("tanh(c * (z + 0.044715 * z * z * z))", "tanh(c * z)"),
+    "gelu_erf_form": ("return 0.5 * z * (1.0 + tanh(c * (z + 0.044715 * z * z * z)));",
+                      "(void)c; return 0.5 * z * (1.0 + erf(z / sqrt(2.0)));"),
+    "oai_no_plus_one": ("* (uc + 1.0);\n        break;", "* uc;\n        break;"),
+    "oai_alpha_dropped": ("exp(-ORC_OAI_ALPHA * gc)", "exp(-gc)"),
+    "oai_limit_from_caller": ("const double gc = g < ORC_OAI_LIMIT ? g : ORC_OAI_LIMIT;",
+                              "const double gc = g < limit ? g : limit;"),
     "clamp_up_one_sided": ("const double uc = u < -limit ? -limit : (u > limit ? limit : u);",
                            "const double uc = u > limit ? limit : u;"),
     "clamp_gate_both_sides": ("const double gc = g < limit ? g : limit;",
