@@ -255,7 +255,9 @@ int mmvq_id_ex(const void *W_up, const void *W_gate,
                void *stream);
 
 /* TEST SUPPORT: the integer block dots that mmvq forms, through the same
- * device decode routines, written instead of being scaled and summed.
+ * device decode routines (for Q4_K, the lane layout the mat-vec takes at
+ * that K: half chunks up to K = 16384, whole chunks beyond, the layout of
+ * the expert kernels), written instead of being scaled and summed.
  * dots[((j*M + r)*(K/qk) + b)*D + i] with D = 16 for Q4_K (sum(q*qy) of
  * sub-blocks 0..7, then sum(qy) of sub-blocks 0..7), 16 for Q6_K
  * (sum((q-32)*qy) of sub-blocks 0..15), 1 for Q4_0 and Q8_0 (sum(q*qy)).

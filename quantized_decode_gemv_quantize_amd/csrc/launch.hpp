@@ -65,7 +65,7 @@ inline int launch_rows_r(const RowArgs& a, const Shape& s, hipStream_t st) {
 // forms (the q8_1 forms keep their short teams and issue every row first).
 template <class F, bool XF, int NC, int G, int R, int P>
 inline int launch_rows_d(const RowArgs& a, const Shape& s, hipStream_t st) {
-  if constexpr (XF && R >= 8) {
+  if constexpr (XF && R >= 8 && layout_pipelined<F>()) {
     if (s.depth == 4) return launch_rows_r<F, XF, NC, G, R, P, 1, 4>(a, s, st);
     if constexpr (R > 8)
       if (s.depth == 8) return launch_rows_r<F, XF, NC, G, R, P, 1, 8>(a, s, st);
@@ -91,8 +91,12 @@ inline int launch_rows_p(const RowArgs& a, const Shape& s, hipStream_t st) {
 template <class F, bool XF, int NC, int G>
 inline int launch_rows_nc(RowArgs a, int64_t K, hipStream_t st) {
   constexpr int RMAX = rows_per_pass<F>(NC, G);
-  Shape s = make_shape<F>(a.M, K, launch_max_rows<F>(XF, NC, G), launch_max_passes<F>(XF, NC, G));
-  if (XF) s.depth = plan_depth(s, device_cus());
+  int64_t force = 0;
+#ifdef QMV_TUNING
+  if (const char* e = getenv("MMVQ_FORCE_ROWS")) force = atoi(e);
+#endif
+  Shape s = plan_launch(a.M, units_per_row<F>(K), launch_max_rows<F>(XF, NC, G), device_cus(),
+                        launch_max_passes<F>(XF, NC, G), XF, NC, force, layout_pipelined<F>());
 #ifdef QMV_TUNING
   if (const char* e = getenv("MMVQ_DEPTH")) s.depth = XF ? atoi(e) : 0;
 #endif
@@ -220,6 +224,12 @@ Dispatch make_dispatch_q4k() {
   };
   d.id = [](const RowArgs& a, int64_t K, int e, hipStream_t s) { return launch_id<Q4K2, XF, 1>(a, K, e, s); };
   d.id_glu = [](const RowArgs& a, int64_t K, int e, hipStream_t s) { return launch_id<Q4K2, XF, 2>(a, K, e, s); };
+  // the integer dots through the layout the mat-vec takes for this K
+  d.block_dots = [](const uint8_t* W, const uint8_t* y, int32_t* dots, int64_t M, int64_t K, int64_t n,
+                    hipStream_t s) {
+    return K > kQ4KHalfMaxK ? launch_block_dots<Q4K2>(W, y, dots, M, K, n, s)
+                            : launch_block_dots<Q4K>(W, y, dots, M, K, n, s);
+  };
   d.units_per_block = Q4K2::kUnitsPerBlock;
   return d;
 }

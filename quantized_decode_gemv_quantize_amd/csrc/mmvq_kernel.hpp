@@ -156,9 +156,11 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
   const int TL = a.team_lanes;
   // team index and row window are wave-uniform (teams are whole waves):
   // keep them scalar so row addresses are SGPR base + per-lane offset
-  const int team_local = __builtin_amdgcn_readfirstlane(tid / TL);
-  const int lt = tid - team_local * TL;
   const int teams_per_block = a.teams_per_block;
+  // one team per workgroup (every team of 256 lanes or more) needs no
+  // division by the team size before the first loads can be issued
+  const int team_local = teams_per_block == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid / TL);
+  const int lt = tid - team_local * TL;
   const int64_t team = static_cast<int64_t>(blockIdx.x) * teams_per_block + team_local;
   const Window win = team_window(team, lt, R * PASSES, P, a.units, a.M);
   int64_t row0 = win.row0, skip = win.skip;   // of the current pass

@@ -63,17 +63,46 @@ inline Shape plan_rows(int64_t M, int units, int rmax, int64_t cus, int target_w
   return s;
 }
 
-// Pipeline depth of a single-pass launch with R >= 8 rows per slot: about
-// 28 rows' loads in flight per CU across its waves (4096x14336 Q4_K fp32,
-// 7 waves per CU: depth 4 -> 8.43 us against 9.90 with all 16 rows issued
-// first; 14336x4096, 7 waves: 8.45; 4096x4096, 2 waves per CU: depth 8 ->
-// 4.88 us against 5.46). Instantiated depths: 4 and 8.
-inline int plan_depth(const Shape& s, int64_t cus) {
-  if (s.passes != 1 || s.rows < 8) return 0;
+// Pipeline depth of a single-pass launch with R >= 8 rows per slot, for the
+// fp32-activation forms of the lane layouts where it was measured to pay:
+// few waves per CU, each owning many rows (4096x14336 Q4_K, 7 waves per CU:
+// depth 4 -> 8.74 us against 9.90 with all 16 rows issued first; 4096x4096,
+// 2 waves per CU: depth 8). With many waves per CU (the Q6_K LM head: 62)
+// the hardware already overlaps the waves' loads and arithmetic and the
+// shallower queue only costs (84.5 -> 95.5 us), as it did for Q8_0
+// 4096x14336 (14.7 -> 16.2 us). Instantiated depths: 4 and 8.
+inline int plan_depth(const Shape& s, int64_t cus, bool pays = true) {
+  if (!pays || s.passes != 1 || s.rows < 8) return 0;
   const int64_t waves = s.teams * (s.team_lanes / kWave);
   const int64_t per_cu = (waves + cus - 1) / cus;
+  if (per_cu > 8) return 0;
   const int d = per_cu >= 5 ? 4 : 8;
   return d < s.rows ? d : 0;
+}
+
+// Shape of a rows-kernel launch: plan_rows; for the fp32-activation forms of
+// a pipelined layout (layout_pipelined), at one column the most rows per team
+// that still leaves a team per CU (each team quantizes the whole activation;
+// 4096x4096 Q4_K: 4 rows per team 5.42 us, 16 rows at depth 8: 4.82), and
+// the pipelined rows of plan_depth for every single-pass launch.
+inline Shape plan_launch(int64_t M, int units, int rmax, int64_t cus, int max_passes, bool xf, int nc,
+                         int64_t force_rows = 0, bool pipelined = true) {
+  Shape s = plan_rows(M, units, rmax, cus, QMV_TARGET_WAVES_PER_CU, force_rows, max_passes);
+  if (!xf || !pipelined) return s;
+  if (nc == 1 && s.passes == 1 && force_rows == 0) {
+    const int64_t per_cu = M / (cus * s.slots);
+    const Shape t = plan_rows(M, units, rmax, cus, QMV_TARGET_WAVES_PER_CU, per_cu > 0 ? per_cu : 1, 1);
+    if (t.rows > s.rows) s = t;
+  }
+  s.depth = plan_depth(s, cus);
+  return s;
+}
+
+// Lane layouts whose fp32-activation launches take pipelined rows: the
+// half-chunk Q4_K layout (measured); the others keep every row issued first.
+template <class F>
+constexpr bool layout_pipelined() {
+  return F::kType == 12 && F::kUnitsPerBlock == 8;
 }
 
 // Largest rows per slot (register budget) of an instantiation.

@@ -115,11 +115,12 @@ static void case_rows(const char* name, int64_t M, int64_t K, int nc, int g, int
   uint8_t* y = alloc16(act_bytes);
   const float* x = xf ? reinterpret_cast<const float*>(y) : nullptr;
   const int units = static_cast<int>(K / F::kQK) * F::kUnitsPerBlock;
-  const Shape s = plan_rows(M, units, launch_max_rows<F>(xf, nc, g), 256, QMV_TARGET_WAVES_PER_CU, 0,
-                            launch_max_passes<F>(xf, nc, g));
+  const Shape s = plan_launch(M, units, launch_max_rows<F>(xf, nc, g), 256, launch_max_passes<F>(xf, nc, g), xf, nc, 0,
+                              layout_pipelined<F>());
   // the launcher instantiates passes > 1 only at R = the register budget
   bool ok = s.team_lanes <= kLaunchBound && static_cast<int64_t>(s.rows) * s.slots * s.passes <= M &&
-            (s.passes == 1 || ((s.passes == 2 || s.passes == 4) && s.rows == rows_per_pass<F>(nc, g)));
+            (s.passes == 1 || ((s.passes == 2 || s.passes == 4) && s.rows == rows_per_pass<F>(nc, g))) &&
+            (s.depth == 0 || (s.passes == 1 && s.depth < s.rows && (s.depth == 4 || s.depth == 8)));
   int tok[kMaxCols];
   for (int j = 0; j < kMaxCols; ++j) tok[j] = j;
   std::vector<int> stores(M, 0);
@@ -259,12 +260,22 @@ static void case_quantize(int64_t K, int64_t n, int64_t ldx) {
   free(x);
 }
 
+// Arguments: "full" adds the benchmark workloads; "small" runs a reduced
+// case set (the build under the address and undefined-behaviour sanitizers).
 int main(int argc, char** argv) {
   const bool full = argc > 1 && strcmp(argv[1], "full") == 0;
-  const int64_t Ms[] = {1, 2, 3, 5, 7, 8, 9, 15, 16, 17, 31, 33, 64, 100, 129, 300, 1000};
+  const bool small = argc > 1 && strcmp(argv[1], "small") == 0;
+  std::vector<int64_t> Ms = {1, 2, 3, 5, 7, 8, 9, 15, 16, 17, 31, 33, 64, 100, 129, 300, 1000};
+  std::vector<int> nbs = {1, 2, 3, 5, 7, 8, 9, 16, 56};
+  std::vector<int> ncs = {1, 2, 3, 4, 5, 6, 7, 8};
+  if (small) {
+    Ms = {1, 3, 17, 129};
+    nbs = {1, 3, 16, 56};
+    ncs = {1, 2, 8};
+  }
   for (int64_t M : Ms) {
-    for (int nb : {1, 2, 3, 5, 7, 8, 9, 16, 56}) {
-      for (int nc = 1; nc <= 8; ++nc) {
+    for (int nb : nbs) {
+      for (int nc : ncs) {
         for (int g = 1; g <= 2; ++g) {
           for (int xpad : {-1, 3}) {
             if (nb <= 16 || nc <= 2) {
@@ -321,6 +332,10 @@ int main(int argc, char** argv) {
         case_id<Q80>("q8_0", 45, 96, 3, T, g, xpad);
       }
     }
+  }
+  if (small) {
+    printf("host model: %d failing case(s)\n", failures);
+    return failures ? 1 : 0;
   }
   // teams that take their rows in passes (more rows wanted than a pass's
   // register budget), with a ragged last team

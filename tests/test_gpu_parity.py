@@ -56,9 +56,11 @@ def test_quantize_bitexact(O, K, n, ldx):
 # ---------------------------------------------------------------------------
 # Integer block dots: bit-exact
 # ---------------------------------------------------------------------------
+# Q4_K rows longer than 16384 take the whole-chunk lane layout (the one the
+# expert kernels use at every K): K = 16640 and 32768 check its integer dots.
 DOT_CASES = [(Q4_0, 37, 96, 2), (Q4_0, 5, 1024, 1), (Q4_0, 7, 32, 3), (Q4_K, 37, 512, 3),
-             (Q4_K, 3, 4096, 1), (Q6_K, 37, 768, 2), (Q6_K, 9, 256, 1), (Q6_K, 3, 4096, 1),
-             (Q8_0, 37, 96, 2), (Q8_0, 5, 1024, 1), (Q8_0, 7, 32, 3)]
+             (Q4_K, 3, 4096, 1), (Q4_K, 5, 16640, 2), (Q4_K, 3, 32768, 1), (Q6_K, 37, 768, 2),
+             (Q6_K, 9, 256, 1), (Q6_K, 3, 4096, 1), (Q8_0, 37, 96, 2), (Q8_0, 5, 1024, 1), (Q8_0, 7, 32, 3)]
 
 
 @pytest.mark.parametrize("wtype,M,K,n", DOT_CASES,
