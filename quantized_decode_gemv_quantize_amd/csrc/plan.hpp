@@ -80,6 +80,17 @@ inline int plan_depth(const Shape& s, int64_t cus, bool pays = true) {
   return d < s.rows ? d : 0;
 }
 
+// Teams of fewer than 256 lanes share a workgroup; when that would leave
+// compute units without one (4096x4096 Q4_K at 16 rows per team: 256
+// two-wave teams in 128 workgroups), every team takes a workgroup of its own.
+inline Shape spread_teams(Shape s, int64_t cus) {
+  if (s.teams_per_block > 1 && s.blocks < cus) {
+    s.teams_per_block = 1;
+    s.blocks = s.teams;
+  }
+  return s;
+}
+
 // Shape of a rows-kernel launch: plan_rows; for the fp32-activation forms of
 // a pipelined layout (layout_pipelined), at one column the most rows per team
 // that still leaves a team per CU (each team quantizes the whole activation;
@@ -88,14 +99,15 @@ inline int plan_depth(const Shape& s, int64_t cus, bool pays = true) {
 inline Shape plan_launch(int64_t M, int units, int rmax, int64_t cus, int max_passes, bool xf, int nc,
                          int64_t force_rows = 0, bool pipelined = true) {
   Shape s = plan_rows(M, units, rmax, cus, QMV_TARGET_WAVES_PER_CU, force_rows, max_passes);
-  if (!xf || !pipelined) return s;
-  if (nc == 1 && s.passes == 1 && force_rows == 0) {
-    const int64_t per_cu = M / (cus * s.slots);
-    const Shape t = plan_rows(M, units, rmax, cus, QMV_TARGET_WAVES_PER_CU, per_cu > 0 ? per_cu : 1, 1);
-    if (t.rows > s.rows) s = t;
+  if (xf && pipelined) {
+    if (nc == 1 && s.passes == 1 && force_rows == 0) {
+      const int64_t per_cu = M / (cus * s.slots);
+      const Shape t = plan_rows(M, units, rmax, cus, QMV_TARGET_WAVES_PER_CU, per_cu > 0 ? per_cu : 1, 1);
+      if (t.rows > s.rows) s = t;
+    }
+    s.depth = plan_depth(s, cus);
   }
-  s.depth = plan_depth(s, cus);
-  return s;
+  return spread_teams(s, cus);
 }
 
 // Lane layouts whose fp32-activation launches take pipelined rows: the

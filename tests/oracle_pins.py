@@ -7,9 +7,10 @@ when the oracle disagrees with what the pages or the mathematics fix:
   citations inside each fixture);
 * library routines the oracle's hand-written code must reduce to (numpy's
   IEEE binary16 conversion);
-* the pages' own printed bit-level fragments (the Q4_K branch-free scale
-  unpack and the Q6_K ``vil | vih`` code assembly), evaluated on 32-bit words
-  here and compared with the oracle's per-element reading;
+* the bit positions the pages' bit-level fragments fix (the Q4_K
+  branch-free scale unpack and the Q6_K code assembly), restated here as
+  fields of one wide little-endian integer and compared with the oracle's
+  per-byte reading;
 * brute force: fp64 dequantize-then-dot with dequantizers written here from
   the pages' row decoders, against the oracle's integer block dots;
 * special cases that reduce to a plain integer dot, and invariants (column
@@ -83,23 +84,30 @@ def deq_q8_0(row: np.ndarray, K: int) -> np.ndarray:
 
 
 def q4_k_scales_from_fragment(scales: np.ndarray):
-    """The pages' branch-free Q4_K unpack [MMVQ §一次 vec_dot 的解剖]: for a
-    sub-block pair j (0..3), with jm = j & 1, hi = -(j >= 2) and s0, s2, s4
-    read as the 16-bit little-endian words jm, jm+2, jm+4 of the 12 scale
-    bytes, aux0 holds the scales of sub-blocks 2j, 2j+1 and aux1 their
-    mins (one per byte)."""
-    words = [int(scales[2 * w]) | (int(scales[2 * w + 1]) << 8) for w in range(6)]
+    """Scales and mins of the 8 sub-blocks as bit fields of the 12 scale
+    bytes read as one little-endian 96-bit integer V. The positions are
+    worked out from the pages' branch-free unpack [MMVQ §一次 vec_dot 的解剖]
+    (three 16-bit words, a mask selecting the first or second pair of
+    sub-block pairs): sub-blocks 0-3 keep 6-bit fields in the low bits of
+    bytes 0-3 (scales) and 4-7 (mins); sub-blocks 4-7 take their low 4 bits
+    from a nibble of bytes 8-11 (scale: low nibble, min: high nibble) and
+    their top 2 bits from the spare top bits of bytes 0-3 (scale) or 4-7
+    (min). Written as (position, width) pairs, independent of the oracle's
+    byte indexing."""
+    V = int.from_bytes(bytes(np.asarray(scales, dtype=np.uint8)), "little")
+
+    def bits(pos, width):
+        return (V >> pos) & ((1 << width) - 1)
+
     sc, mn = [0] * 8, [0] * 8
-    for j in range(4):
-        jm = j & 1
-        hi = 0xFFFF if j >= 2 else 0
-        s0, s2, s4 = words[jm], words[jm + 2], words[jm + 4]
-        aux0 = ((s0 & 0x3F3F) & ~hi) | ((((s4 >> 0) & 0x0F0F) | ((s0 & 0xC0C0) >> 2)) & hi)
-        aux1 = ((s2 & 0x3F3F) & ~hi) | ((((s4 >> 4) & 0x0F0F) | ((s2 & 0xC0C0) >> 2)) & hi)
-        aux0 &= 0xFFFF
-        aux1 &= 0xFFFF
-        sc[2 * j], sc[2 * j + 1] = aux0 & 0xFF, aux0 >> 8
-        mn[2 * j], mn[2 * j + 1] = aux1 & 0xFF, aux1 >> 8
+    for t in range(8):
+        if t < 4:
+            sc[t] = bits(8 * t, 6)
+            mn[t] = bits(32 + 8 * t, 6)
+        else:
+            k = t - 4
+            sc[t] = bits(64 + 8 * k, 4) | bits(8 * k + 6, 2) << 4
+            mn[t] = bits(64 + 8 * k + 4, 4) | bits(32 + 8 * k + 6, 2) << 4
     return sc, mn
 
 
@@ -121,27 +129,23 @@ def deq_q4_k(row: np.ndarray, K: int) -> np.ndarray:
 
 
 def q6_k_codes_from_fragment(blk: np.ndarray) -> np.ndarray:
-    """Codes of one Q6_K block assembled 4 at a time with the pages' fragment
-    [MMVQ §一次 vec_dot 的解剖]: vil = (vl >> 4i) & 0x0F0F0F0F,
-    vih = ((vh >> 4i) << 4) & 0x30303030, code bytes = vil | vih. vl is a
-    32-bit word of ql, vh the matching word of qh pre-shifted by 0 (first
-    32 bytes of a 64-byte ql half) or 2 (second 32 bytes), and i selects the
-    low (0) or high (1) nibble. Layout reading: ql[128] @0, qh[64] @128."""
-    ql = blk[0:128]
-    qh = blk[128:192]
+    """Codes of one Q6_K block as bit fields of ql (128 bytes) and qh (64
+    bytes), each read as one little-endian integer. The positions are worked
+    out from the pages' code assembly [MMVQ §一次 vec_dot 的解剖]: a 32-bit
+    word of ql gives four low-nibble codes or four high-nibble codes, and the
+    matching word of qh, shifted by 0 or 2 for the first or second 32 bytes
+    of a 64-byte ql half and by 4 more for the high nibbles, gives bits 4-5.
+    So element e = 128h + 32g + l takes its low 4 bits at bit
+    8(64h + 32(g mod 2) + l) + 4(g div 2) of ql and its top 2 bits at bit
+    8(32h + l) + 2g of qh. Layout reading: ql[128] @0, qh[64] @128."""
+    QL = int.from_bytes(bytes(blk[0:128]), "little")
+    QH = int.from_bytes(bytes(blk[128:192]), "little")
     codes = np.zeros(256, dtype=np.int64)
-    for h in range(2):
-        for half in range(2):          # which 32-byte run of this ql half
-            for i in range(2):         # low / high nibble
-                g = half + 2 * i
-                for w in range(8):     # 8 words of 4 bytes = 32 elements
-                    vl = int.from_bytes(bytes(ql[64 * h + 32 * half + 4 * w:][:4]), "little")
-                    vh = int.from_bytes(bytes(qh[32 * h + 4 * w:][:4]), "little") >> (2 * half)
-                    vil = (vl >> (4 * i)) & 0x0F0F0F0F
-                    vih = ((vh >> (4 * i)) << 4) & 0x30303030
-                    word = vil | vih
-                    for k in range(4):
-                        codes[128 * h + 32 * g + 4 * w + k] = (word >> (8 * k)) & 0xFF
+    for e in range(256):
+        h, g, l = e // 128, (e % 128) // 32, e % 32
+        low = (QL >> (8 * (64 * h + 32 * (g % 2) + l) + 4 * (g // 2))) & 15
+        high = (QH >> (8 * (32 * h + l) + 2 * g)) & 3
+        codes[e] = low | high << 4
     return codes
 
 
@@ -398,8 +402,8 @@ def pin_q6_k_e5(O):
 
 
 def pin_q4_k_fragment(O, seed: int = 3):
-    """The oracle's per-sub-block unpack equals the pages' printed
-    branch-free fragment on random scale bytes."""
+    """The oracle's per-sub-block unpack equals the bit positions read from
+    the pages' branch-free fragment, on random scale bytes."""
     rng = np.random.default_rng(seed)
     for _ in range(400):
         s = rng.integers(0, 256, size=12, dtype=np.uint8)
@@ -429,8 +433,8 @@ def pin_q4_k_bijection(O, seed: int = 5):
 
 
 def pin_q6_k_fragment(O, seed: int = 9):
-    """Codes from the oracle's per-element reading equal the codes assembled
-    with the pages' 32-bit fragment."""
+    """Codes from the oracle's per-element reading equal the bit positions
+    read from the pages' 32-bit code assembly."""
     rng = np.random.default_rng(seed)
     for _ in range(20):
         blk = bytearray(rng.integers(0, 256, size=210, dtype=np.uint8).tobytes())
