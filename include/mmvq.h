@@ -153,11 +153,14 @@ int mmvq_quantize_q8_1(const float *x, int64_t K, int64_t n, int64_t ldx,
  * sub-block t, d*sc_t*d8*sum(q*qy) - dmin*m_t*d8*sum(qy). Q6_K: per
  * 16-element sub-block, d*sc*d8*sum((q-32)*qy). Accumulated in fp32.
  * Requires K % qk == 0, M >= 1 and 1 <= n <= MMVQ_MAX_COLS, or for Q4_K
- * 1 <= n <= MMVQ_MAX_COLS_BATCH. For n <= MMVQ_MAX_COLS one row must fit
- * a team of at most 512 lanes: K <= 16384 for Q4_0 and Q8_0 (a block per
- * lane), K <= 32768 for Q4_K (64 weights per lane) and Q6_K (a quarter
- * super-block per lane); longer rows return MMVQ_ERR_SHAPE (the same limits
- * hold for every entry point below except the many-column path).
+ * 1 <= n <= MMVQ_MAX_COLS_BATCH. A lane of the n <= MMVQ_MAX_COLS forms
+ * handles one unit of a row (a block for Q4_0 and Q8_0, half or whole
+ * 64-weight chunks for Q4_K, a quarter super-block for Q6_K); rows of more
+ * than 512 units are walked by the team in chunks of at most 512 lanes
+ * [MMVQ §kernel 的形状: K split across the warps of a block]. Rows of more
+ * than 2^24 units (K > 2^29 for Q4_0 and Q8_0, K > 2^30 for Q4_K and Q6_K)
+ * and M*K > 2^40 return MMVQ_ERR_SHAPE (the same limits hold for every
+ * entry point below except the many-column path).
  * For Q4_K, n >= 6 (without a gate, q8_1 columns) takes the many-column
  * path, where
  * the integer dots of 16 rows x 16 columns x 32 elements come from one int8

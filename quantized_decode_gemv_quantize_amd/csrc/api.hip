@@ -41,7 +41,7 @@ int check_gemv(const void* W, int type, int64_t M, int64_t K, const ActIn& in, i
   *d = dispatch_for(type, f32);
   if (!*d) return MMVQ_ERR_TYPE;
   if (M < 1 || K < 1 || K % (*d)->qk != 0 || n < 1 || n > MMVQ_MAX_COLS) return MMVQ_ERR_SHAPE;
-  if (K / (*d)->qk * (*d)->units_per_block > kLaunchBound) return MMVQ_ERR_SHAPE;
+  if (K / (*d)->qk * (*d)->units_per_block > kMaxUnitsPerRow) return MMVQ_ERR_SHAPE;
   if (M > (int64_t(1) << 40) / K) return MMVQ_ERR_SHAPE;
   if (f32 && (in.ldx < K || in.ldx > (int64_t(1) << 40))) return MMVQ_ERR_SHAPE;
   if (!aligned(W, 16) || !aligned(out, 4)) return MMVQ_ERR_ALIGN;

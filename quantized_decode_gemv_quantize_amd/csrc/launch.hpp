@@ -54,11 +54,25 @@ inline int check_launch() {
   return hipGetLastError() == hipSuccess ? MMVQ_OK : MMVQ_ERR_LAUNCH;
 }
 
-template <class F, bool XF, int NC, int G, int R, int P, int PASSES, int DEPTH = 0>
+template <class F, bool XF, int NC, int G, int R, int P, int PASSES, int DEPTH = 0, bool KLOOP = false>
 inline int launch_rows_r(const RowArgs& a, const Shape& s, hipStream_t st) {
-  hipLaunchKernelGGL((mmvq_rows_kernel<F, NC, R, P, G, XF, PASSES, DEPTH>), dim3(static_cast<unsigned>(s.blocks)),
-                     dim3(s.teams_per_block * s.team_lanes), 0, st, a);
+  hipLaunchKernelGGL((mmvq_rows_kernel<F, NC, R, P, G, XF, PASSES, DEPTH, KLOOP>),
+                     dim3(static_cast<unsigned>(s.blocks)), dim3(s.teams_per_block * s.team_lanes), 0, st, a);
   return check_launch();
+}
+
+// Rows longer than a team: one slot, one pass, at most kChunkRows rows.
+template <class F, bool XF, int NC, int G>
+inline int launch_rows_chunked(const RowArgs& a, const Shape& s, hipStream_t st) {
+  constexpr int RMAX = rows_per_pass<F>(NC, G);
+  if (s.slots != 1 || s.passes != 1 || s.depth != 0 || s.teams_per_block != 1) return MMVQ_ERR_SHAPE;
+  switch (s.rows) {
+    case 1: return launch_rows_r<F, XF, NC, G, 1, 1, 1, 0, true>(a, s, st);
+    case 2: if constexpr (RMAX >= 2) return launch_rows_r<F, XF, NC, G, 2, 1, 1, 0, true>(a, s, st); break;
+    case 4: if constexpr (RMAX >= 4) return launch_rows_r<F, XF, NC, G, 4, 1, 1, 0, true>(a, s, st); break;
+    default: break;
+  }
+  return MMVQ_ERR_SHAPE;
 }
 
 // Single-pass launch, with the pipelined rows of plan_depth for the fp32
@@ -103,6 +117,7 @@ inline int launch_rows_nc(RowArgs a, int64_t K, hipStream_t st) {
   a.units = s.units;
   a.team_lanes = s.team_lanes;
   a.teams_per_block = s.teams_per_block;
+  if (s.chunks > 1) return launch_rows_chunked<F, XF, NC, G>(a, s, st);
   switch (s.rows) {
     case 1: return launch_rows_p<F, XF, NC, G, 1>(a, s, st);
     case 2: if constexpr (RMAX >= 2) return launch_rows_p<F, XF, NC, G, 2>(a, s, st); break;
@@ -129,10 +144,10 @@ inline int launch_rows(const RowArgs& a, int64_t K, int64_t n, hipStream_t st) {
   }
 }
 
-template <class F, bool XF, int G, int RB, int P>
+template <class F, bool XF, int G, int RB, int P, bool KLOOP = false>
 inline int launch_id_r(const RowArgs& a, const Shape& s, int n_experts, hipStream_t st) {
   const unsigned slices = static_cast<unsigned>(n_experts) + (a.Ws_up ? 1u : 0u);   // + shared expert
-  hipLaunchKernelGGL((mmvq_id_kernel<F, RB, P, G, XF>), dim3(static_cast<unsigned>(s.blocks), slices),
+  hipLaunchKernelGGL((mmvq_id_kernel<F, RB, P, G, XF, KLOOP>), dim3(static_cast<unsigned>(s.blocks), slices),
                      dim3(s.teams_per_block * s.team_lanes), 0, st, a);
   return check_launch();
 }
@@ -146,11 +161,16 @@ inline int launch_id(RowArgs a, int64_t K, int n_experts, hipStream_t st) {
   a.units = s.units;
   a.team_lanes = s.team_lanes;
   a.teams_per_block = s.teams_per_block;
-  const bool full = static_cast<int64_t>(RB) * s.slots <= a.M;
+  // rows longer than a team: one row per team, walked in chunks
+  const bool full = s.chunks == 1 && static_cast<int64_t>(RB) * s.slots <= a.M;
   const int rb = full ? RB : 1;
   s.rows = rb;
   s.teams = (a.M + static_cast<int64_t>(rb) * s.slots - 1) / (static_cast<int64_t>(rb) * s.slots);
   s.blocks = (s.teams + s.teams_per_block - 1) / s.teams_per_block;
+  if (s.chunks > 1) {
+    if (s.slots != 1 || s.teams_per_block != 1) return MMVQ_ERR_SHAPE;
+    return launch_id_r<F, XF, G, 1, 1, true>(a, s, n_experts, st);
+  }
   if (full)
     return s.slots == 2 ? launch_id_r<F, XF, G, RB, 2>(a, s, n_experts, st)
                         : launch_id_r<F, XF, G, RB, 1>(a, s, n_experts, st);

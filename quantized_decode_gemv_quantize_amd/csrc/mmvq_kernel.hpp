@@ -136,7 +136,13 @@ struct RedLds {
 // the wave sits in its load issues while its first rows have landed and then
 // computes all R rows after its last row arrives; with it the arithmetic
 // runs while the later rows stream.
-template <class F, int NC, int R, int P, int G, bool ID, bool XF, int VMAX, int PASSES = 1, int DEPTH = 0>
+// KLOOP (one slot, one pass, no pipelining): rows with more units than a
+// team has lanes. The team walks the row in chunks of TL units; in chunk c
+// lane lt handles unit c*TL + lt with that unit's activation slice, and
+// adds its chunks' partials in chunk order before the team reduction (the
+// pages split K over the warps of a block the same way, [MMVQ §kernel 的形状]).
+template <class F, int NC, int R, int P, int G, bool ID, bool XF, int VMAX, int PASSES = 1, int DEPTH = 0,
+          bool KLOOP = false>
 __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
                                           const uint8_t* Wbase, const uint8_t* Wgbase,
                                           RedLds<G, VMAX>& red) {
@@ -165,10 +171,10 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
   const Window win = team_window(team, lt, R * PASSES, P, a.units, a.M);
   int64_t row0 = win.row0, skip = win.skip;   // of the current pass
   const int slot = win.slot;
-  const bool active = win.active;
-  const int u = win.unit;
+  bool active = win.active;        // the lane's unit and its constants
+  int u = win.unit;                // (per chunk with KLOOP)
   const int lane = lane_id();
-  const typename F::Lane L = F::lane(u);
+  typename F::Lane L = F::lane(u);
   const int64_t step = static_cast<int64_t>(P) * a.row_bytes;
 
   // ---- activation slice of every column (zero for idle lanes) -----------
@@ -179,24 +185,42 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
   constexpr bool XE = XF && NC * F::kXWords <= 64;
   typename F::Act act[NC];
   typename F::XRaw xr[XE ? NC : 1];
-  if constexpr (XF && !XE) {
-    // compile-time column index: at 8 columns the body exceeds what the
-    // loop unroller takes, and a runtime index would put act[] in scratch
-    static_for<0, NC>([&](auto jc) {
-      constexpr int j = decltype(jc)::value;
-      typename F::XRaw t;
-      F::load_x(t, a.x + cols.tok[j] * a.ldx, u);
-      F::quant_x(act[j], t);
-      if (!active) F::zero_act(act[j]);
-    });
-  } else {
+  auto load_act = [&]() {
+    if constexpr (XF && !XE) {
+      // compile-time column index: at 8 columns the body exceeds what the
+      // loop unroller takes, and a runtime index would put act[] in scratch
+      static_for<0, NC>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        typename F::XRaw t;
+        F::load_x(t, a.x + cols.tok[j] * a.ldx, u);
+        F::quant_x(act[j], t);
+        if (!active) F::zero_act(act[j]);
+      });
+    } else {
 #pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      if constexpr (XE) F::load_x(xr[j], a.x + cols.tok[j] * a.ldx, u);
-      else F::issue_act(act[j], a.y + cols.tok[j] * a.ycol_bytes, u);
+      for (int j = 0; j < NC; ++j) {
+        if constexpr (XE) F::load_x(xr[j], a.x + cols.tok[j] * a.ldx, u);
+        else F::issue_act(act[j], a.y + cols.tok[j] * a.ycol_bytes, u);
+      }
     }
-  }
-  __builtin_amdgcn_sched_barrier(0);
+  };
+  // the activation loads were issued before the weight loads, so they
+  // retire first: this waits for them only
+  auto finish_act = [&]() {
+    if constexpr (XE) {
+#pragma unroll
+      for (int j = 0; j < NC; ++j) {
+        F::quant_x(act[j], xr[j]);
+        if (!active) F::zero_act(act[j]);
+      }
+    } else if constexpr (!XF) {
+#pragma unroll
+      for (int j = 0; j < NC; ++j) {
+        F::finish_act(act[j]);
+        if (!active) F::zero_act(act[j]);
+      }
+    }
+  };
 
   // ---- issue all weight loads of a pass's rows ---------------------------
   // With several passes the weights are double-buffered: the loads of pass
@@ -225,22 +249,113 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  issue(wb[0], wgb[0], row0, 0, FIRST);
-  // the activation loads were issued before the weight loads, so they
-  // retire first: this waits for them only
-  if constexpr (XE) {
-#pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      F::quant_x(act[j], xr[j]);
-      if (!active) F::zero_act(act[j]);
+
+  // ---- reduce over the team, epilogue, store -----------------------------
+  using RM = ReduceMap<kWave, V>;
+  auto store = [&](int idx, float up, float gate) {
+    const int j = idx / RP, i = idx - j * RP;
+    if (j >= NC || i < skip) return;
+    const int64_t r = row0 + i;
+    const int64_t e = ID ? static_cast<int64_t>(blockIdx.y) : 0;
+    if (up_scale) up *= up_scale[e];
+    if (up_bias) up += up_bias[e * a.M + r];
+    if constexpr (G == 2) {
+      if (gate_scale) gate *= gate_scale[e];
+      if (gate_bias) gate += gate_bias[e * a.M + r];
     }
-  } else if constexpr (!XF) {
+    const float v = (G == 2) ? glu(a.glu_op, gate, up, a.glu_limit) : up;
+    if constexpr (ID) {
+      // select column j's token and slots with compile-time indices
+      uint64_t m = 0;
+      int t = 0;
 #pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      F::finish_act(act[j]);
-      if (!active) F::zero_act(act[j]);
+      for (int jj = 0; jj < NC; ++jj)
+        if (jj == j) { m = cols.slots[jj]; t = cols.tok[jj]; }
+      while (m) {
+        const int k = __builtin_ctzll(m);
+        m &= m - 1;
+        a.out[(static_cast<int64_t>(t) * a.top_k + k) * a.M + r] = v;
+      }
+    } else {
+      a.out[static_cast<int64_t>(j) * a.M + r] = v;
     }
+  };
+  // resync: a previous pass's readers must be done with the LDS first
+  // (uniform: every team of the block runs the same passes)
+  auto reduce_store = [&](float (&part)[G][V], bool resync) {
+    team_reduce<kWave, G, V>(part, lane);
+    if (TL == kWave) {
+      if (RM::representative(lane)) {
+#pragma unroll
+        for (int pos = 0; pos < RM::kPerLane; ++pos) {
+          const int idx = RM::index(lane, pos);
+          store(idx, part[0][pos], G == 2 ? part[G - 1][pos] : 0.0f);
+        }
+      }
+    } else {
+      const int wave = tid / kWave;
+      if (resync) __syncthreads();
+      if (RM::representative(lane)) {
+#pragma unroll
+        for (int pos = 0; pos < RM::kPerLane; ++pos) {
+          const int idx = RM::index(lane, pos);
+#pragma unroll
+          for (int p = 0; p < G; ++p) red.v[p][wave * V + idx] = part[p][pos];
+        }
+      }
+      __syncthreads();
+      const int tw = TL / kWave;
+      const int wave0 = team_local * tw;
+      for (int idx = lt; idx < NC * RP; idx += TL) {
+        float s[G];
+#pragma unroll
+        for (int p = 0; p < G; ++p) {
+          s[p] = 0.0f;
+          for (int k = 0; k < tw; ++k) s[p] += red.v[p][(wave0 + k) * V + idx];
+        }
+        store(idx, s[0], s[G - 1]);
+      }
+    }
+  };
+
+  if constexpr (KLOOP) {
+    static_assert(P == 1 && PASSES == 1 && DEPTH == 0, "chunked rows: one slot, one pass, no pipelining");
+    const int chunks = (a.units + TL - 1) / TL;
+    float part[G][V];
+#pragma unroll
+    for (int p = 0; p < G; ++p)
+#pragma unroll
+      for (int k = 0; k < V; ++k) part[p][k] = 0.0f;
+    typename F::Wt (&w)[R] = wb[0];
+    typename F::Wt (&wg)[G == 2 ? R : 1] = wgb[0];
+    for (int c = 0; c < chunks; ++c) {
+      u = chunk_unit(lt, c, TL, a.units, active);
+      L = F::lane(u);
+      load_act();
+      __builtin_amdgcn_sched_barrier(0);
+      issue(w, wg, row0, 0, R);
+      finish_act();
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        typename F::Dec dec;
+        F::decode(w[i], dec, L);
+#pragma unroll
+        for (int j = 0; j < NC; ++j) part[0][j * R + i] += F::col_dot(dec, act[j]);
+        if constexpr (G == 2) {
+          F::decode(wg[i], dec, L);
+#pragma unroll
+          for (int j = 0; j < NC; ++j) part[1][j * R + i] += F::col_dot(dec, act[j]);
+        }
+      }
+    }
+    reduce_store(part, false);
+    return;
   }
+
+  load_act();
+  __builtin_amdgcn_sched_barrier(0);
+  issue(wb[0], wgb[0], row0, 0, FIRST);
+  finish_act();
 
 #pragma unroll
   for (int pass = 0; pass < PASSES; ++pass) {
@@ -283,79 +398,13 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
     }
   }
 
-  // ---- reduce over the team ----------------------------------------------
-  team_reduce<kWave, G, V>(part, lane);
-  using RM = ReduceMap<kWave, V>;
-
-  auto store = [&](int idx, float up, float gate) {
-    const int j = idx / RP, i = idx - j * RP;
-    if (j >= NC || i < skip) return;
-    const int64_t r = row0 + i;
-    const int64_t e = ID ? static_cast<int64_t>(blockIdx.y) : 0;
-    if (up_scale) up *= up_scale[e];
-    if (up_bias) up += up_bias[e * a.M + r];
-    if constexpr (G == 2) {
-      if (gate_scale) gate *= gate_scale[e];
-      if (gate_bias) gate += gate_bias[e * a.M + r];
-    }
-    const float v = (G == 2) ? glu(a.glu_op, gate, up, a.glu_limit) : up;
-    if constexpr (ID) {
-      // select column j's token and slots with compile-time indices
-      uint64_t m = 0;
-      int t = 0;
-#pragma unroll
-      for (int jj = 0; jj < NC; ++jj)
-        if (jj == j) { m = cols.slots[jj]; t = cols.tok[jj]; }
-      while (m) {
-        const int k = __builtin_ctzll(m);
-        m &= m - 1;
-        a.out[(static_cast<int64_t>(t) * a.top_k + k) * a.M + r] = v;
-      }
-    } else {
-      a.out[static_cast<int64_t>(j) * a.M + r] = v;
-    }
-  };
-
-  if (TL == kWave) {
-    if (RM::representative(lane)) {
-#pragma unroll
-      for (int pos = 0; pos < RM::kPerLane; ++pos) {
-        const int idx = RM::index(lane, pos);
-        store(idx, part[0][pos], G == 2 ? part[G - 1][pos] : 0.0f);
-      }
-    }
-  } else {
-    const int wave = tid / kWave;
-    // the previous pass's readers must be done with the LDS (uniform: every
-    // team of the block runs the same passes)
-    if (PASSES > 1 && pass > 0) __syncthreads();
-    if (RM::representative(lane)) {
-#pragma unroll
-      for (int pos = 0; pos < RM::kPerLane; ++pos) {
-        const int idx = RM::index(lane, pos);
-#pragma unroll
-        for (int p = 0; p < G; ++p) red.v[p][wave * V + idx] = part[p][pos];
-      }
-    }
-    __syncthreads();
-    const int tw = TL / kWave;
-    const int wave0 = team_local * tw;
-    for (int idx = lt; idx < NC * RP; idx += TL) {
-      float s[G];
-#pragma unroll
-      for (int p = 0; p < G; ++p) {
-        s[p] = 0.0f;
-        for (int k = 0; k < tw; ++k) s[p] += red.v[p][(wave0 + k) * V + idx];
-      }
-      store(idx, s[0], s[G - 1]);
-    }
-  }
+  reduce_store(part, PASSES > 1 && pass > 0);
   }   // passes
 }
 
 // Plain / fused kernel: columns 0..NC-1 of y; a team owns PASSES * R * P
-// rows, taken R * P at a time.
-template <class F, int NC, int R, int P, int G, bool XF, int PASSES, int DEPTH = 0>
+// rows, taken R * P at a time (KLOOP: rows longer than the team, in chunks).
+template <class F, int NC, int R, int P, int G, bool XF, int PASSES, int DEPTH = 0, bool KLOOP = false>
 __global__ void __launch_bounds__(kLaunchBound) mmvq_rows_kernel(RowArgs a) {
   Cols cols;
   cols.n = NC;
@@ -363,7 +412,7 @@ __global__ void __launch_bounds__(kLaunchBound) mmvq_rows_kernel(RowArgs a) {
   for (int j = 0; j < kMaxCols; ++j) { cols.tok[j] = j; cols.slots[j] = 0; }
   constexpr int V = pow2ceil(NC * R * P);
   __shared__ RedLds<G, V> red;
-  rows_body<F, NC, R, P, G, false, XF, V, PASSES, DEPTH>(a, cols, a.W, a.Wg, red);
+  rows_body<F, NC, R, P, G, false, XF, V, PASSES, DEPTH, KLOOP>(a, cols, a.W, a.Wg, red);
 }
 
 // Expert-indexed kernel: blockIdx.y = expert. The token list is the same for
@@ -389,8 +438,10 @@ constexpr int id_lds_values() {
   return v;
 }
 
-template <class F, int RB, int P, int G, bool XF>
+// KLOOP: rows longer than the team (RB = 1: one row per pass).
+template <class F, int RB, int P, int G, bool XF, bool KLOOP = false>
 __global__ void __launch_bounds__(kLaunchBound) mmvq_id_kernel(RowArgs a) {
+  static_assert(!KLOOP || (RB == 1 && P == 1), "chunked expert rows: one row, one slot");
   const int e = blockIdx.y;
   const bool shared = e == a.n_experts;
   if (shared) {
@@ -437,7 +488,7 @@ __global__ void __launch_bounds__(kLaunchBound) mmvq_id_kernel(RowArgs a) {
   __shared__ RedLds<G, VMAX> red;
   switch (cols.n) {
 #define QMV_ID_CASE(NC)                                                                          \
-  rows_body<F, NC, id_rows<F, NC, RB, G>(), P, G, true, XF, VMAX, RB / id_rows<F, NC, RB, G>()>( \
+  rows_body<F, NC, id_rows<F, NC, RB, G>(), P, G, true, XF, VMAX, RB / id_rows<F, NC, RB, G>(), 0, KLOOP>( \
       a, cols, We, Wge, red)
     case 1: QMV_ID_CASE(1); break;
     case 2: QMV_ID_CASE(2); break;

@@ -17,6 +17,7 @@ namespace qmv {
 
 struct Shape {
   int units;            // units per row
+  int chunks;           // K-chunks a team walks per row (1: a lane per unit)
   int slots;            // rows a team covers per step (P)
   int team_lanes;       // lanes per team (whole waves)
   int teams_per_block;
@@ -32,8 +33,28 @@ inline int pow2floor(int64_t v) {
   return p;
 }
 
+// Longest row the kernels take, in units (32-bit lane offsets within a row
+// and activation column stay far from overflow: Q6_K rows of 2^24 units
+// are 880 MB).
+constexpr int64_t kMaxUnitsPerRow = int64_t(1) << 24;
+
+// Rows per team of a chunked launch (rows longer than a team: every row
+// loops over its chunks, reloading the activation slice of each).
+constexpr int kChunkRows = 4;
+
+// Unit of lane lt in chunk c of a chunked team of TL lanes; lanes past the
+// row's end re-read its last unit and are inactive.
+__host__ __device__ __forceinline__ int chunk_unit(int lt, int c, int TL, int units, bool& active) {
+  const int u = c * TL + lt;
+  active = u < units;
+  return active ? u : units - 1;
+}
+
 // Team layout and rows per team for an M-row matrix whose rows hold `units`
 // units:
+//  * chunks: rows of more than kLaunchBound units are walked in the fewest
+//    chunks of at most kLaunchBound lanes, the team as wide as one chunk
+//    (whole waves), at most kChunkRows rows per team and one pass;
 //  * slots P = 2 when a row's units fill whole waves only in pairs (e.g.
 //    224 units), else 1 (idle lanes pad the last wave);
 //  * rows per slot and team: a power of two with rows * P <= M, sized for
@@ -46,12 +67,17 @@ inline Shape plan_rows(int64_t M, int units, int rmax, int64_t cus, int target_w
                        int max_passes = 1) {
   Shape s;
   s.units = units;
-  s.slots = (units % kWave != 0 && (2 * units) % kWave == 0 && 2 * units <= kLaunchBound && M >= 2) ? 2 : 1;
-  s.team_lanes = (s.slots * units + kWave - 1) / kWave * kWave;
+  s.chunks = units > kLaunchBound ? (units + kLaunchBound - 1) / kLaunchBound : 1;
+  const int lanes = (units + s.chunks - 1) / s.chunks;     // units per chunk
+  s.slots = (s.chunks == 1 && units % kWave != 0 && (2 * units) % kWave == 0 && 2 * units <= kLaunchBound &&
+             M >= 2) ? 2 : 1;
+  s.team_lanes = (s.slots * lanes + kWave - 1) / kWave * kWave;
   const int tw = s.team_lanes / kWave;
   s.teams_per_block = s.team_lanes >= 256 ? 1 : 256 / s.team_lanes;
   int64_t want = force_rows > 0 ? force_rows : M * tw / (cus * target_waves * s.slots);
   int r = pow2floor(want < 1 ? 1 : want);
+  if (s.chunks > 1) max_passes = 1;
+  if (s.chunks > 1 && rmax > kChunkRows) rmax = kChunkRows;
   if (r > rmax * max_passes) r = rmax * max_passes;
   if (static_cast<int64_t>(r) * s.slots > M) r = pow2floor(M / s.slots);
   s.passes = r > rmax ? r / rmax : 1;

@@ -14,6 +14,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "formats.hpp"
@@ -55,35 +56,48 @@ static bool model_rows(const Shape& s, int R, int P, int G, int64_t M, const uin
   typename F::Wt wt;
   typename F::Act act;
   typename F::Dec dec;
+  std::vector<int> seen(static_cast<size_t>(s.units) * P);   // active lanes per (slot, unit)
   for (int64_t b = 0; b < s.blocks; ++b) {
     for (int tl = 0; tl < s.teams_per_block; ++tl) {
       const int64_t team = b * s.teams_per_block + tl;
+      std::fill(seen.begin(), seen.end(), 0);
       for (int lt = 0; lt < s.team_lanes; ++lt) {
         const Window w = team_window(team, lt, R * passes, P, s.units, M);
-        const typename F::Lane L = F::lane(w.unit);
         const uint32_t slot_off = static_cast<uint32_t>(w.slot * row_bytes);
-        for (int pass = 0; pass < passes; ++pass) {
-          const int64_t row0 = w.row0 + static_cast<int64_t>(pass) * R * P;
-          const uint8_t* rp = W + row0 * row_bytes;
-          const uint8_t* gp = Wg ? Wg + row0 * row_bytes : nullptr;
-          for (int i = 0; i < R; ++i) {
-            F::load_wt(wt, rp, slot_off, L);
-            F::decode(wt, dec, L);
-            rp += P * row_bytes;
-            if (G == 2) {
-              F::load_wt(wt, gp, slot_off, L);
-              gp += P * row_bytes;
+        // chunked rows: the lane's unit in each chunk, as the kernel walks them
+        for (int c = 0; c < s.chunks; ++c) {
+          bool active = w.active;
+          const int unit = s.chunks == 1 ? w.unit : chunk_unit(lt, c, s.team_lanes, s.units, active);
+          if (unit < 0 || unit >= s.units) return false;
+          if (active) seen[static_cast<size_t>(w.slot) * s.units + unit] += 1;
+          const typename F::Lane L = F::lane(unit);
+          for (int pass = 0; pass < passes; ++pass) {
+            const int64_t row0 = w.row0 + static_cast<int64_t>(pass) * R * P;
+            const uint8_t* rp = W + row0 * row_bytes;
+            const uint8_t* gp = Wg ? Wg + row0 * row_bytes : nullptr;
+            for (int i = 0; i < R; ++i) {
+              F::load_wt(wt, rp, slot_off, L);
+              F::decode(wt, dec, L);
+              rp += P * row_bytes;
+              if (G == 2) {
+                F::load_wt(wt, gp, slot_off, L);
+                gp += P * row_bytes;
+              }
             }
           }
-        }
-        for (int j = 0; j < nc; ++j) {
-          if (x) {
-            typename F::XRaw xr;
-            F::load_x(xr, x + tok[j] * ldx, w.unit);
-            F::quant_x(act, xr);
+          for (int j = 0; j < nc; ++j) {
+            if (x) {
+              typename F::XRaw xr;
+              F::load_x(xr, x + tok[j] * ldx, unit);
+              F::quant_x(act, xr);
+            }
+            else F::load_act(act, y + tok[j] * ycol_bytes, unit);
           }
-          else F::load_act(act, y + tok[j] * ycol_bytes, w.unit);
         }
+        // every unit of the row is some lane's in exactly one chunk
+        if (s.chunks > 1 && lt == 0 && (static_cast<int64_t>(s.chunks) * s.team_lanes < s.units ||
+                                        static_cast<int64_t>(s.chunks - 1) * s.team_lanes >= s.units))
+          return false;
         if (lt == 0) {   // the store pattern of the team (one lane's view suffices)
           for (int pass = 0; pass < passes; ++pass) {
             const int64_t row0 = w.row0 + static_cast<int64_t>(pass) * R * P;
@@ -97,6 +111,9 @@ static bool model_rows(const Shape& s, int R, int P, int G, int64_t M, const uin
           }
         }
       }
+      // every unit of every slot's row is one active lane's
+      for (int v : seen)
+        if (v != 1) return false;
     }
   }
   return true;
@@ -120,7 +137,12 @@ static void case_rows(const char* name, int64_t M, int64_t K, int nc, int g, int
   // the launcher instantiates passes > 1 only at R = the register budget
   bool ok = s.team_lanes <= kLaunchBound && static_cast<int64_t>(s.rows) * s.slots * s.passes <= M &&
             (s.passes == 1 || ((s.passes == 2 || s.passes == 4) && s.rows == rows_per_pass<F>(nc, g))) &&
-            (s.depth == 0 || (s.passes == 1 && s.depth < s.rows && (s.depth == 4 || s.depth == 8)));
+            (s.depth == 0 || (s.passes == 1 && s.depth < s.rows && (s.depth == 4 || s.depth == 8))) &&
+            // chunked launches: as launch_rows_chunked instantiates them
+            (s.chunks == 1 || (s.slots == 1 && s.passes == 1 && s.depth == 0 && s.teams_per_block == 1 &&
+                               s.rows <= kChunkRows && s.rows <= rows_per_pass<F>(nc, g) &&
+                               // the chunk count the kernel derives from units and TL
+                               (s.units + s.team_lanes - 1) / s.team_lanes == s.chunks));
   int tok[kMaxCols];
   for (int j = 0; j < kMaxCols; ++j) tok[j] = j;
   std::vector<int> stores(M, 0);
@@ -151,7 +173,7 @@ static void case_id(const char* name, int64_t M, int64_t K, int E, int T, int g,
   const int units = static_cast<int>(K / F::kQK) * F::kUnitsPerBlock;
   const int RB = id_block_rows<F>(g, xf);
   Shape s = plan_rows(M, units, RB, 256, QMV_TARGET_WAVES_PER_CU, 0);
-  const int rb = static_cast<int64_t>(RB) * s.slots <= M ? RB : 1;   // as the launcher
+  const int rb = s.chunks == 1 && static_cast<int64_t>(RB) * s.slots <= M ? RB : 1;   // as the launcher
   s.rows = rb;
   s.teams = (M + static_cast<int64_t>(rb) * s.slots - 1) / (static_cast<int64_t>(rb) * s.slots);
   s.blocks = (s.teams + s.teams_per_block - 1) / s.teams_per_block;
@@ -301,7 +323,7 @@ int main(int argc, char** argv) {
       }
     }
   }
-  // longest rows a team can hold
+  // longest rows a team holds without chunks
   for (int xpad : {-1, 1}) {
     case_rows<Q4K>("q4_k", 129, 16384, 1, 1, xpad);
     case_rows<Q4K2>("q4_k2", 129, 16384, 1, 1, xpad);
@@ -332,6 +354,27 @@ int main(int argc, char** argv) {
         case_id<Q80>("q8_0", 45, 96, 3, T, g, xpad);
       }
     }
+  }
+  // rows longer than a team, walked in chunks (even and ragged last chunks)
+  for (int xpad : {-1, 1}) {
+    for (int nc : {1, 3, 8})
+      for (int g = 1; g <= 2; ++g) {
+        case_rows<Q4K2>("q4_k2", 37, 65536, nc, g, xpad);    // 1024 units: 2 chunks of 512
+        case_rows<Q4K2>("q4_k2", 9, 33024, nc, g, xpad);     // 516 units: 2 chunks, 320-lane team
+        case_rows<Q4K>("q4_k", 9, 16640, nc, g, xpad);       // 520 units
+        case_rows<Q40>("q4_0", 37, 32768, nc, g, xpad);      // 1024 units
+        case_rows<Q40>("q4_0", 5, 16416, nc, g, xpad);       // 513 units
+        case_rows<Q80>("q8_0", 17, 40000, nc, g, xpad);      // 1250 units: 3 chunks
+        case_rows<Q6K>("q6_k", 17, 65792, nc, g, xpad);      // 1028 units: 3 chunks
+        case_rows<Q6K>("q6_k", 3, 33024, nc, g, xpad);       // 516 units
+      }
+    for (int g = 1; g <= 2; ++g)
+      for (int T : {1, 3, 8}) {
+        case_id<Q4K2>("q4_k2", 33, 65536, 3, T, g, xpad);
+        case_id<Q40>("q4_0", 17, 32768, 2, T, g, xpad);
+        case_id<Q6K>("q6_k", 9, 33024, 2, T, g, xpad);
+        case_id<Q80>("q8_0", 5, 16416, 2, T, g, xpad);
+      }
   }
   if (small) {
     printf("host model: %d failing case(s)\n", failures);

@@ -53,14 +53,18 @@ P16, P4 = 1 << 20, (1 << 20) + 4
     ((P16, B.Q4_K, 1, 200, P16, 1, P16), B.ERR_SHAPE),
     ((P16, B.Q4_0, 1, 48, P16, 1, P16), B.ERR_SHAPE),
     ((P16, B.Q8_0, 1, 48, P16, 1, P16), B.ERR_SHAPE),
-    ((P16, B.Q8_0, 1, 32 * 513, P16, 1, P16), B.ERR_SHAPE),
+    # rows of more than 2^24 units (longer rows are walked in chunks)
+    ((P16, B.Q8_0, 1, 32 * ((1 << 24) + 1), P16, 1, P16), B.ERR_SHAPE),
+    ((P16, B.Q4_0, 1, 32 * ((1 << 24) + 1), P16, 1, P16), B.ERR_SHAPE),
     ((P16, B.Q4_K, 0, 256, P16, 1, P16), B.ERR_SHAPE),
     ((P16, B.Q4_K, 1, 256, P16, 0, P16), B.ERR_SHAPE),
     ((P16, B.Q4_K, 1, 256, P16, 257, P16), B.ERR_SHAPE),
     ((P16, B.Q4_0, 1, 256, P16, 9, P16), B.ERR_SHAPE),
     ((P16, B.Q6_K, 1, 256, P16, 9, P16), B.ERR_SHAPE),
-    ((P16, B.Q4_K, 1, 256 * 129, P16, 1, P16), B.ERR_SHAPE),
-    ((P16, B.Q6_K, 1, 256 * 129, P16, 1, P16), B.ERR_SHAPE),
+    ((P16, B.Q4_K, 1, 256 * ((1 << 22) + 1), P16, 1, P16), B.ERR_SHAPE),
+    ((P16, B.Q6_K, 1, 256 * ((1 << 22) + 1), P16, 1, P16), B.ERR_SHAPE),
+    # M * K above 2^40
+    ((P16, B.Q4_K, 1 << 20, 256 * 4097, P16, 1, P16), B.ERR_SHAPE),
     ((P4, B.Q4_K, 1, 256, P16, 1, P16), B.ERR_ALIGN),
     ((P16, B.Q4_K, 1, 256, P4, 1, P16), B.ERR_ALIGN),
     ((P16, B.Q4_K, 1, 256, P16, 1, P16 + 2), B.ERR_ALIGN),
@@ -103,7 +107,8 @@ def test_f32_entry_points_argument_checks(L):
     assert L.mmvq_f32(P16, B.Q8_1, 1, 256, P16, 1, 256, P16, None) == B.ERR_TYPE
     assert L.mmvq_f32(P16, B.Q4_K, 1, 256, P16, 1, 255, P16, None) == B.ERR_SHAPE
     assert L.mmvq_f32(P16, B.Q4_K, 1, 256, P16, 9, 256, P16, None) == B.ERR_SHAPE
-    assert L.mmvq_f32(P16, B.Q4_K, 1, 256 * 129, P16, 1, 256 * 129, P16, None) == B.ERR_SHAPE
+    K = 256 * ((1 << 22) + 1)
+    assert L.mmvq_f32(P16, B.Q4_K, 1, K, P16, 1, K, P16, None) == B.ERR_SHAPE
     assert L.mmvq_f32(P16, B.Q4_K, 1, 256, P16 + 2, 1, 256, P16, None) == B.ERR_ALIGN
     # fp32 x needs only 4-byte alignment (q8_1 columns need 16)
     assert L.mmvq_f32(P4, B.Q4_K, 1, 256, P16, 1, 256, P16, None) == B.ERR_ALIGN

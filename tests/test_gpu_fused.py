@@ -75,7 +75,11 @@ FUSED_CASES = [(Q4_0, 37, 96, 1, 0), (Q4_0, 300, 1024, 3, 5), (Q4_0, 129, 16384,
                (Q8_0, 129, 16384, 8, 1),
                # enough rows that teams take them in 2 or 4 passes (ragged last team)
                (Q4_K, 12301, 4096, 2, 1), (Q4_K, 12301, 4096, 5, 0), (Q4_0, 12301, 4096, 3, 0),
-               (Q8_0, 12301, 4096, 8, 2), (Q6_K, 12301, 4096, 4, 1)]
+               (Q8_0, 12301, 4096, 8, 2), (Q6_K, 12301, 4096, 4, 1),
+               # rows walked in chunks (ragged last chunk for 16416, 33024, 40000)
+               (Q4_K, 37, 65536, 1, 0), (Q4_K, 9, 33024, 8, 3), (Q4_0, 37, 32768, 2, 1),
+               (Q4_0, 5, 16416, 5, 0), (Q8_0, 17, 40000, 3, 2), (Q6_K, 17, 65792, 1, 1),
+               (Q6_K, 3, 33024, 8, 0)]
 
 
 @pytest.mark.parametrize("wtype,M,K,n,pad", FUSED_CASES,
@@ -101,7 +105,8 @@ def test_mmvq_f32(O, wtype, M, K, n, pad):
 
 GLU_F32 = [(Q4_K, 300, 4096, 1, B.GLU_SWIGLU), (Q4_K, 37, 512, 4, B.GLU_PLAIN),
            (Q4_0, 300, 1024, 2, B.GLU_SWIGLU), (Q6_K, 37, 768, 3, B.GLU_SWIGLU),
-           (Q4_K, 129, 14336, 8, B.GLU_SWIGLU)]
+           (Q4_K, 129, 14336, 8, B.GLU_SWIGLU), (Q4_K, 17, 65536, 2, B.GLU_SWIGLU),
+           (Q8_0, 9, 16416, 8, B.GLU_PLAIN)]
 
 
 @pytest.mark.parametrize("wtype,M,K,n,op", GLU_F32,
@@ -132,7 +137,10 @@ ID_F32 = [("q4_k-E4-T3-k2", Q4_K, 4, 200, 512, [[2, 0], [1, 2], [2, 3]]),
           # fewer rows than the fp32 gate/up kernel's 32-row expert blocks
           ("q4_k-E3-T4-k2-M20", Q4_K, 3, 20, 512, [[2, 0], [1, 2], [0, 1], [2, 1]]),
           ("q4_0-E5-T4-k2", Q4_0, 5, 77, 1024, [[4, 0], [0, 4], [2, 2], [1, 3]]),
-          ("q6_k-E4-T2-k2", Q6_K, 4, 50, 768, [[3, 1], [1, 0]])]
+          ("q6_k-E4-T2-k2", Q6_K, 4, 50, 768, [[3, 1], [1, 0]]),
+          # rows walked in chunks
+          ("q4_k-E2-T3-k2-K65536", Q4_K, 2, 17, 65536, [[1, 0], [0, 1], [1, 1]]),
+          ("q8_0-E3-T8-k2-K16416", Q8_0, 3, 9, 16416, "random")]
 
 
 @pytest.mark.parametrize("fused_glu", [False, True])

@@ -58,8 +58,8 @@ def test_quantize_bitexact(O, K, n, ldx):
 # ---------------------------------------------------------------------------
 # Q4_K rows longer than 16384 take the whole-chunk lane layout (the one the
 # expert kernels use at every K): K = 16640 and 32768 check its integer dots.
-DOT_CASES = [(Q4_0, 37, 96, 2), (Q4_0, 5, 1024, 1), (Q4_0, 7, 32, 3), (Q4_K, 37, 512, 3),
-             (Q4_K, 3, 4096, 1), (Q4_K, 5, 16640, 2), (Q4_K, 3, 32768, 1), (Q6_K, 37, 768, 2),
+DOT_CASES = [(Q4_0, 37, 96, 2), (Q4_0, 5, 1024, 1), (Q4_0, 7, 32, 3), (Q4_0, 3, 32768, 1), (Q4_K, 37, 512, 3),
+             (Q4_K, 3, 4096, 1), (Q4_K, 5, 16640, 2), (Q4_K, 3, 32768, 1), (Q4_K, 2, 65536, 1), (Q6_K, 37, 768, 2),
              (Q6_K, 9, 256, 1), (Q6_K, 3, 4096, 1), (Q8_0, 37, 96, 2), (Q8_0, 5, 1024, 1), (Q8_0, 7, 32, 3)]
 
 
@@ -84,11 +84,15 @@ def test_block_dots_bitexact(O, wtype, M, K, n):
 # ---------------------------------------------------------------------------
 # GEMV: all rows, shapes spanning several teams and ragged tails
 # ---------------------------------------------------------------------------
+# Rows of more than 512 units (Q4_0 / Q8_0 K > 16384, Q4_K / Q6_K K > 32768)
+# are walked by the team in chunks; 16416, 33024 and 40000 leave a ragged
+# last chunk.
 SHAPES = {
-    Q4_0: [(1, 32), (37, 96), (300, 1024), (1000, 4096), (129, 16384)],
-    Q8_0: [(1, 32), (37, 96), (300, 1024), (1000, 4096), (129, 16384)],
-    Q4_K: [(1, 256), (37, 512), (300, 2304), (1000, 4096), (129, 14336), (65, 16384), (33, 32768)],
-    Q6_K: [(1, 256), (37, 768), (300, 4096), (129, 32768)],
+    Q4_0: [(1, 32), (37, 96), (300, 1024), (1000, 4096), (129, 16384), (37, 32768), (5, 16416)],
+    Q8_0: [(1, 32), (37, 96), (300, 1024), (1000, 4096), (129, 16384), (17, 40000)],
+    Q4_K: [(1, 256), (37, 512), (300, 2304), (1000, 4096), (129, 14336), (65, 16384), (33, 32768),
+           (37, 65536), (9, 33024)],
+    Q6_K: [(1, 256), (37, 768), (300, 4096), (129, 32768), (17, 65792), (3, 33024)],
 }
 GEMV_CASES = [(t, M, K, n) for t, shapes in SHAPES.items() for (M, K) in shapes
               for n in (1, 2, 3, 5, 8)]
@@ -142,7 +146,9 @@ def test_gemv_workload(O, name, n):
 # Fused gate/up GLU
 # ---------------------------------------------------------------------------
 GLU_CASES = [(t, M, K, n, op) for t, M, K in [(Q4_K, 300, 4096), (Q4_K, 37, 512), (Q4_0, 300, 1024),
-                                               (Q6_K, 100, 4096), (Q4_K, 129, 16384), (Q8_0, 77, 2048)]
+                                               (Q6_K, 100, 4096), (Q4_K, 129, 16384), (Q8_0, 77, 2048),
+                                               # rows walked in chunks
+                                               (Q4_K, 17, 65536), (Q4_0, 9, 16416), (Q6_K, 5, 33024)]
              for n in (1, 2, 8) for op in (B.GLU_SWIGLU, B.GLU_PLAIN)]
 
 
@@ -219,6 +225,10 @@ ID_CASES = [
     ("q4_k-dup-in-token", Q4_K, 4, 100, 512, [[1, 1], [3, 1]]),
     ("q4_0-E5-T4-k2", Q4_0, 5, 77, 1024, [[4, 0], [0, 4], [2, 2], [1, 3]]),
     ("q6_k-E4-T2-k2", Q6_K, 4, 50, 768, [[3, 1], [1, 0]]),
+    # rows walked in chunks
+    ("q4_k-E3-T3-k2-K65536", Q4_K, 3, 33, 65536, [[2, 0], [1, 2], [0, 1]]),
+    ("q4_0-E2-T8-k1-K16416", Q4_0, 2, 17, 16416, [[1], [0], [1], [1], [0], [1], [0], [0]]),
+    ("q6_k-E2-T2-k2-K33024", Q6_K, 2, 9, 33024, [[1, 0], [0, 1]]),
 ]
 
 
@@ -253,7 +263,7 @@ def test_abi_errors_on_device():
     L = B.lib()
     s = torch.cuda.current_stream().cuda_stream
     p, q, o = W.data_ptr(), y.data_ptr(), out.data_ptr()
-    assert L.mmvq(p, Q4_K, 1, 256 * 129, q, 1, o, s) == B.ERR_SHAPE      # row too long for a team
+    assert L.mmvq(p, Q4_K, 1, 256 * ((1 << 22) + 1), q, 1, o, s) == B.ERR_SHAPE   # over 2^24 units
     assert L.mmvq(p + 4, Q4_K, 1, 256, q, 1, o, s) == B.ERR_ALIGN
     assert L.mmvq(p, Q4_K, 1, 256, q + 4, 1, o, s) == B.ERR_ALIGN
     assert L.mmvq(p, Q4_K, 1, 256, q, 0, o, s) == B.ERR_SHAPE
