@@ -18,9 +18,11 @@ LIB = os.path.join(HERE, "libmmvq.so")
 OBJ = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "quantize.hip", "kernels_q4_0.hip", "kernels_q8_0.hip", "kernels_q4_k.hip",
-           "kernels_q6_k.hip", "kernels_q4_0_f32.hip", "kernels_q8_0_f32.hip", "kernels_q4_k_f32.hip",
-           "kernels_q6_k_f32.hip", "kernels_mmq.hip", "probe.hip"]
+# Longest first: the expert-indexed Q4_K kernels sit in units of their own so
+# the fp32 Q4_K unit does not set the build time alone.
+SOURCES = ["kernels_q4_k_f32.hip", "kernels_q4_k_f32_id.hip", "kernels_q4_k.hip", "kernels_q4_k_id.hip",
+           "kernels_q6_k_f32.hip", "kernels_q6_k.hip", "kernels_q4_0_f32.hip", "kernels_q8_0_f32.hip",
+           "kernels_q4_0.hip", "kernels_q8_0.hip", "kernels_mmq.hip", "api.hip", "quantize.hip", "probe.hip"]
 
 # Packed fp32 VALU instructions stay disabled (hipcc forms them from plain
 # float code otherwise); fp32 division is correctly rounded and fp32

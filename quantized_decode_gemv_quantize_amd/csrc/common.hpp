@@ -170,6 +170,11 @@ __device__ __forceinline__ float h2f(uint32_t bits) {
 
 constexpr int pow2ceil(int v) { int p = 1; while (p < v) p <<= 1; return p; }
 
+// Lambdas of the kernel bodies are inlined like the __forceinline__
+// functions around them (a lambda the inliner leaves out of line takes its
+// captured register arrays through scratch memory).
+#define QMV_INLINE __attribute__((always_inline))
+
 // f(Idx<0>{}), ..., f(Idx<N-1>{}): a loop whose index is a compile-time
 // constant in the body, for bodies too large for the loop unroller (a
 // runtime index into a register array puts the array in scratch memory).

@@ -202,15 +202,20 @@ struct Dispatch {
   int qk, block_bytes, units_per_block;
 };
 
-template <class F, bool XF>
+// ID = false leaves the expert-indexed launchers out (set by the caller).
+template <class F, bool XF, bool ID = true>
 Dispatch make_dispatch() {
   Dispatch d;
   d.rows = [](const RowArgs& a, int64_t K, int64_t n, hipStream_t s) { return launch_rows<F, XF, 1>(a, K, n, s); };
   d.rows_glu = [](const RowArgs& a, int64_t K, int64_t n, hipStream_t s) {
     return launch_rows<F, XF, 2>(a, K, n, s);
   };
-  d.id = [](const RowArgs& a, int64_t K, int e, hipStream_t s) { return launch_id<F, XF, 1>(a, K, e, s); };
-  d.id_glu = [](const RowArgs& a, int64_t K, int e, hipStream_t s) { return launch_id<F, XF, 2>(a, K, e, s); };
+  d.id = nullptr;
+  d.id_glu = nullptr;
+  if constexpr (ID) {
+    d.id = [](const RowArgs& a, int64_t K, int e, hipStream_t s) { return launch_id<F, XF, 1>(a, K, e, s); };
+    d.id_glu = [](const RowArgs& a, int64_t K, int e, hipStream_t s) { return launch_id<F, XF, 2>(a, K, e, s); };
+  }
   d.block_dots = launch_block_dots<F>;
   d.qk = F::kQK;
   d.block_bytes = F::kBlockBytes;
@@ -233,17 +238,24 @@ Dispatch make_dispatch() {
 // The row limit is the whole-chunk one.
 constexpr int64_t kQ4KHalfMaxK = static_cast<int64_t>(kLaunchBound) / Q4K::kUnitsPerBlock * Q4K::kQK;
 
+// Expert-indexed Q4_K launchers (whole chunks), each activation type in a
+// translation unit of its own.
+int launch_id_q4k(const RowArgs& a, int64_t K, int n_experts, hipStream_t st);
+int launch_id_glu_q4k(const RowArgs& a, int64_t K, int n_experts, hipStream_t st);
+int launch_id_q4k_f32(const RowArgs& a, int64_t K, int n_experts, hipStream_t st);
+int launch_id_glu_q4k_f32(const RowArgs& a, int64_t K, int n_experts, hipStream_t st);
+
 template <bool XF>
 Dispatch make_dispatch_q4k() {
-  Dispatch d = make_dispatch<Q4K, XF>();
+  Dispatch d = make_dispatch<Q4K, XF, false>();
   d.rows = [](const RowArgs& a, int64_t K, int64_t n, hipStream_t s) {
     return K > kQ4KHalfMaxK ? launch_rows<Q4K2, XF, 1>(a, K, n, s) : launch_rows<Q4K, XF, 1>(a, K, n, s);
   };
   d.rows_glu = [](const RowArgs& a, int64_t K, int64_t n, hipStream_t s) {
     return K > kQ4KHalfMaxK ? launch_rows<Q4K2, XF, 2>(a, K, n, s) : launch_rows<Q4K, XF, 2>(a, K, n, s);
   };
-  d.id = [](const RowArgs& a, int64_t K, int e, hipStream_t s) { return launch_id<Q4K2, XF, 1>(a, K, e, s); };
-  d.id_glu = [](const RowArgs& a, int64_t K, int e, hipStream_t s) { return launch_id<Q4K2, XF, 2>(a, K, e, s); };
+  d.id = XF ? launch_id_q4k_f32 : launch_id_q4k;
+  d.id_glu = XF ? launch_id_glu_q4k_f32 : launch_id_glu_q4k;
   // the integer dots through the layout the mat-vec takes for this K
   d.block_dots = [](const uint8_t* W, const uint8_t* y, int32_t* dots, int64_t M, int64_t K, int64_t n,
                     hipStream_t s) {

@@ -185,11 +185,11 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
   constexpr bool XE = XF && NC * F::kXWords <= 64;
   typename F::Act act[NC];
   typename F::XRaw xr[XE ? NC : 1];
-  auto load_act = [&]() {
+  auto load_act = [&]() QMV_INLINE {
     if constexpr (XF && !XE) {
       // compile-time column index: at 8 columns the body exceeds what the
       // loop unroller takes, and a runtime index would put act[] in scratch
-      static_for<0, NC>([&](auto jc) {
+      static_for<0, NC>([&](auto jc) QMV_INLINE {
         constexpr int j = decltype(jc)::value;
         typename F::XRaw t;
         F::load_x(t, a.x + cols.tok[j] * a.ldx, u);
@@ -206,7 +206,7 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
   };
   // the activation loads were issued before the weight loads, so they
   // retire first: this waits for them only
-  auto finish_act = [&]() {
+  auto finish_act = [&]() QMV_INLINE {
     if constexpr (XE) {
 #pragma unroll
       for (int j = 0; j < NC; ++j) {
@@ -233,7 +233,8 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
   const uint32_t slot_off = static_cast<uint32_t>(slot * a.row_bytes);
   static_assert(DEPTH == 0 || (PASSES == 1 && DEPTH < R), "pipelined rows: one pass, depth below R");
   constexpr int FIRST = DEPTH > 0 ? DEPTH : R;      // rows issued up front
-  auto issue = [&](typename F::Wt (&w)[R], typename F::Wt (&wg)[G == 2 ? R : 1], int64_t r0, int i0, int i1) {
+  auto issue = [&](typename F::Wt (&w)[R], typename F::Wt (&wg)[G == 2 ? R : 1], int64_t r0, int i0,
+                   int i1) QMV_INLINE {
     const uint8_t* rp = Wb + r0 * a.row_bytes + i0 * step;
     const uint8_t* gp = (G == 2) ? Wgb + r0 * a.row_bytes + i0 * step : nullptr;
 #pragma unroll
@@ -252,7 +253,7 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
 
   // ---- reduce over the team, epilogue, store -----------------------------
   using RM = ReduceMap<kWave, V>;
-  auto store = [&](int idx, float up, float gate) {
+  auto store = [&](int idx, float up, float gate) QMV_INLINE {
     const int j = idx / RP, i = idx - j * RP;
     if (j >= NC || i < skip) return;
     const int64_t r = row0 + i;
@@ -282,7 +283,7 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
   };
   // resync: a previous pass's readers must be done with the LDS first
   // (uniform: every team of the block runs the same passes)
-  auto reduce_store = [&](float (&part)[G][V], bool resync) {
+  auto reduce_store = [&](float (&part)[G][V], bool resync) QMV_INLINE {
     team_reduce<kWave, G, V>(part, lane);
     if (TL == kWave) {
       if (RM::representative(lane)) {
@@ -372,7 +373,7 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
   for (int p = 0; p < G; ++p)
 #pragma unroll
     for (int k = 0; k < V; ++k) part[p][k] = 0.0f;
-  auto put = [&](int p, int j, int i, float v) {
+  auto put = [&](int p, int j, int i, float v) QMV_INLINE {
     if constexpr (P == 1) {
       part[p][j * RP + i] = v;
     } else {
@@ -402,6 +403,22 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
   }   // passes
 }
 
+// Columns one rows_body call takes. Where the activation slices of all NC
+// columns and the rows in flight exceed the registers, the kernels take the
+// columns in two halves (measured spills at 256 registers: Q6_K, 24
+// activation words per column, gate/up at 8 columns and in expert blocks
+// from 6; Q6_K expert blocks and chunked fp32 rows at 8; the fp32 Q4_K
+// whole-chunk expert blocks at 8 with a gate or with two row slots).
+template <class F, int G, bool XF, bool ID, bool KLOOP, int P>
+constexpr int max_cols_per_call() {
+  if (F::kType == 14) {
+    if (ID) return G == 2 ? 5 : 7;
+    return (G == 2 || (XF && KLOOP)) ? 7 : kMaxCols;
+  }
+  if (F::kType == 12 && F::kUnitsPerBlock == 4 && ID && XF && (G == 2 || P == 2)) return 7;
+  return kMaxCols;
+}
+
 // Plain / fused kernel: columns 0..NC-1 of y; a team owns PASSES * R * P
 // rows, taken R * P at a time (KLOOP: rows longer than the team, in chunks).
 template <class F, int NC, int R, int P, int G, bool XF, int PASSES, int DEPTH = 0, bool KLOOP = false>
@@ -412,7 +429,21 @@ __global__ void __launch_bounds__(kLaunchBound) mmvq_rows_kernel(RowArgs a) {
   for (int j = 0; j < kMaxCols; ++j) { cols.tok[j] = j; cols.slots[j] = 0; }
   constexpr int V = pow2ceil(NC * R * P);
   __shared__ RedLds<G, V> red;
-  rows_body<F, NC, R, P, G, false, XF, V, PASSES, DEPTH, KLOOP>(a, cols, a.W, a.Wg, red);
+  constexpr int MC = max_cols_per_call<F, G, XF, false, KLOOP, P>();
+  if constexpr (NC <= MC) {
+    rows_body<F, NC, R, P, G, false, XF, V, PASSES, DEPTH, KLOOP>(a, cols, a.W, a.Wg, red);
+  } else {
+    // two halves of the columns; the second re-reads the team's rows (from
+    // cache) with its columns' activations and outputs
+    constexpr int N0 = (NC + 1) / 2;
+    rows_body<F, N0, R, P, G, false, XF, V, PASSES, DEPTH, KLOOP>(a, cols, a.W, a.Wg, red);
+    __syncthreads();       // the first half's LDS readers are done
+    RowArgs a2 = a;
+    if constexpr (XF) a2.x += N0 * a.ldx;
+    else a2.y += N0 * a.ycol_bytes;
+    a2.out += N0 * a.M;
+    rows_body<F, NC - N0, R, P, G, false, XF, V, PASSES, DEPTH, KLOOP>(a2, cols, a2.W, a2.Wg, red);
+  }
 }
 
 // Expert-indexed kernel: blockIdx.y = expert. The token list is the same for
@@ -422,17 +453,16 @@ __global__ void __launch_bounds__(kLaunchBound) mmvq_rows_kernel(RowArgs a) {
 // Rows per pass of an expert block with NC tokens: what the register budget
 // allows for NC columns, at most RB; the team owns RB * P rows and takes them
 // in RB / id_rows passes.
-template <class F, int NC, int RB, int G>
+template <class F, int NC, int RB, int G, bool XF>
 constexpr int id_rows() {
-  return rows_per_pass<F>(NC, G) < RB ? rows_per_pass<F>(NC, G) : RB;
+  return id_rows_n<F>(NC, RB, G, XF);
 }
 
-template <class F, int RB, int P, int G>
+template <class F, int RB, int P, int G, bool XF>
 constexpr int id_lds_values() {
   int v = 1;
   for (int nc = 1; nc <= kMaxCols; ++nc) {
-    const int r = rows_per_pass<F>(nc, G) < RB ? rows_per_pass<F>(nc, G) : RB;
-    const int w = pow2ceil(nc * r * P);
+    const int w = pow2ceil(nc * id_rows_n<F>(nc, RB, G, XF) * P);
     if (w > v) v = w;
   }
   return v;
@@ -484,12 +514,36 @@ __global__ void __launch_bounds__(kLaunchBound) mmvq_id_kernel(RowArgs a) {
   const int64_t eo = shared ? 0 : static_cast<int64_t>(e) * a.expert_stride;
   const uint8_t* We = a.W + eo;
   const uint8_t* Wge = G == 2 ? a.Wg + eo : nullptr;
-  constexpr int VMAX = id_lds_values<F, RB, P, G>();
+  constexpr int VMAX = id_lds_values<F, RB, P, G, XF>();
   __shared__ RedLds<G, VMAX> red;
+  auto run = [&](auto nc, const Cols& c) QMV_INLINE {
+    constexpr int NC = decltype(nc)::value;
+    constexpr int R = id_rows<F, NC, RB, G, XF>();
+    rows_body<F, NC, R, P, G, true, XF, VMAX, RB / R, 0, KLOOP>(a, c, We, Wge, red);
+  };
+  // more tokens than the registers hold at once: two halves, the second
+  // re-reading the block's rows (from cache) for the other tokens
+  constexpr int MC = max_cols_per_call<F, G, XF, true, KLOOP, P>();
+  auto run_split = [&](auto nc) QMV_INLINE {
+    constexpr int NC = decltype(nc)::value;
+    if constexpr (NC <= MC) {
+      run(nc, cols);
+    } else {
+      constexpr int N0 = (NC + 1) / 2;
+      run(Idx<N0>{}, cols);
+      __syncthreads();     // the first half's LDS readers are done
+      Cols c2;
+      c2.n = NC - N0;
+#pragma unroll
+      for (int j = 0; j < kMaxCols; ++j) {
+        c2.tok[j] = j + N0 < kMaxCols ? cols.tok[j + N0 < kMaxCols ? j + N0 : 0] : 0;
+        c2.slots[j] = j + N0 < kMaxCols ? cols.slots[j + N0 < kMaxCols ? j + N0 : 0] : 0;
+      }
+      run(Idx<NC - N0>{}, c2);
+    }
+  };
   switch (cols.n) {
-#define QMV_ID_CASE(NC)                                                                          \
-  rows_body<F, NC, id_rows<F, NC, RB, G>(), P, G, true, XF, VMAX, RB / id_rows<F, NC, RB, G>(), 0, KLOOP>( \
-      a, cols, We, Wge, red)
+#define QMV_ID_CASE(NC) run_split(Idx<NC>{})
     case 1: QMV_ID_CASE(1); break;
     case 2: QMV_ID_CASE(2); break;
     case 3: QMV_ID_CASE(3); break;

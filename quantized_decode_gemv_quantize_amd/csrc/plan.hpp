@@ -208,6 +208,20 @@ constexpr int id_block_rows(int g, bool xf = false) {
   return rows_per_pass<F>(1, g);
 }
 
+// Rows per pass of an expert block with nc tokens: the register budget for
+// nc columns, at most RB. When the block takes its rows in (double-buffered)
+// passes and holds its fp32 activation slice raw across the weight loads,
+// the two passes' weights plus the raw slice are kept within 160 registers
+// (Q4_K whole chunks, one token: 8 rows -> 4, gate/up 4 -> 2; they spilled).
+template <class F>
+constexpr int id_rows_n(int nc, int RB, int G, bool XF) {
+  int r = rows_per_pass<F>(nc, G) < RB ? rows_per_pass<F>(nc, G) : RB;
+  constexpr int wt_words = static_cast<int>(sizeof(typename F::Wt) / 4);
+  if (XF && nc * F::kXWords <= 64 && r < RB)
+    while (r > 1 && 2 * r * G * wt_words + nc * F::kXWords > 160) r /= 2;
+  return r;
+}
+
 // Row window of one team and the unit / slot of one of its lanes.
 // The team owns rows [first, first + RP); the last team's window is moved
 // back to end at row M-1 (M >= RP), and rows of the window below `first`

@@ -185,7 +185,7 @@ static void case_id(const char* name, int64_t M, int64_t K, int E, int T, int g,
     for (int j = 0; j < nt; ++j) tok[j] = (j + e) % T;
     std::vector<int> stores(M, 0);
     // rows per pass for nt tokens, as the kernel picks them
-    const int rn = rows_per_pass<F>(nt, g) < rb ? rows_per_pass<F>(nt, g) : rb;
+    const int rn = id_rows_n<F>(nt, rb, g, xf);
     ok = model_rows<F>(s, rn, s.slots, g, M, W + e * stride, g == 2 ? Wg + e * stride : nullptr, row_bytes,
                        xf ? nullptr : y, ycol, x, ldx, tok, nt, stores, rb / rn);
     for (int64_t q = 0; q < M && ok; ++q) ok = stores[q] == 1;
