@@ -65,7 +65,13 @@ def parse():
     p.add_argument("--moe", action="store_true",
                    help="time only the expert-indexed gate/up workload (one JSON line) and exit")
     p.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
-                   help="write profiles/ summaries from rocprofv3 csv output and exit")
+                   help="write the headline profiles/ summaries from rocprofv3 csv output and exit")
+    p.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                   help="write profiles/<workload>_n<n>_kernel_trace.md for --workload/--n (or --moe) "
+                        "from a rocprofv3 --kernel-trace --stats run of the same arguments, and exit")
+    p.add_argument("--summarize-sq", metavar="SQ_DIR",
+                   help="write profiles/<workload>_n<n>_sq_counters.md for --workload/--n from a "
+                        "rocprofv3 --pmc run of the SQ counters below, and exit")
     return p.parse_args()
 
 
@@ -89,37 +95,163 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def kernel_kind(name: str) -> str | None:
-    """'fused' / 'gemv' for the n=1 Q4_K plain mat-vec kernels (fp32 or q8_1
-    activations), else None."""
-    import re
-    m = re.match(r"void qmv::mmvq_rows_kernel<qmv::Q4K, 1, \d+, \d+, 1, (true|false), 1(, \d+)?>", name)
-    if not m:
-        return None
-    return "fused" if m.group(1) == "true" else "gemv"
+def _targs(name: str) -> list:
+    return name.split("<", 1)[1].split(">", 1)[0].split(", ")
+
+
+def kernel_form(name: str, grid_y: int = 1, n_experts: int = 0) -> str | None:
+    """Which benchmark form a kernel launch belongs to: 'fused' (fp32-activation
+    mat-vec), 'gemv' (q8_1 mat-vec: row or many-column kernel), 'quantize',
+    'probe' (streaming read), 'id' / 'id_fused' (expert-indexed, q8_1 / fp32
+    activations), 'id_shared' (expert-indexed with the shared-expert slice),
+    else None."""
+    if name.startswith("void qmv::mmvq_rows_kernel<"):
+        return "fused" if _targs(name)[5] == "true" else "gemv"      # <F, NC, R, P, G, XF, ...>
+    if name.startswith("void qmv::mmq_q4k_kernel<"):
+        return "gemv"
+    if name.startswith("qmv::quantize_q8_1_kernel"):
+        return "quantize"
+    if name.startswith("qmv::read_probe_kernel"):
+        return "probe"
+    if name.startswith("void qmv::mmvq_id_kernel<"):
+        if n_experts and grid_y == n_experts + 1:
+            return "id_shared"
+        return "id_fused" if _targs(name)[4] == "true" else "id"    # <F, RB, P, G, XF, ...>
+    return None
+
+
 COPY_BYTES = 256 * 2 ** 20     # the --copy-probe copy: reads and writes this many bytes
+
+# SQ counters of one --pmc pass (at most 8 SQ counters per pass)
+SQ_COUNTERS = ["SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_VMEM_RD", "SQ_INSTS_LDS",
+               "SQ_INSTS_MFMA", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES"]
+# Issue ceiling of plain (non-packed) vector instructions: a wave64
+# instruction occupies a 16-lane SIMD for 4 cycles; 256 CUs x 4 SIMDs at
+# 2.4 GHz issue 256 * 4 * 2.4e9 / 4 = 614.4 G wave-instructions per second.
+VALU_ISSUE_PEAK = 256 * 4 * 2.4e9 / 4
+
+
+def _csv_rows(d: str, pat: str) -> list:
+    import csv
+    import glob
+    f = glob.glob(os.path.join(d, "**", pat), recursive=True)
+    if not f:
+        raise FileNotFoundError(f"no {pat} under {d}")
+    return list(csv.DictReader(open(f[0])))
+
+
+def profile_name(workload: str, n: int, moe: bool) -> str:
+    return "moe_q4_k_8x14336x4096" if moe else f"{workload}_n{n}"
+
+
+def summarize_trace(trace_dir: str, workload: str, n: int, moe: bool, steps: int, warmup: int) -> None:
+    """profiles/<workload>_n<n>_kernel_trace.md: the rocprofv3 --stats table
+    and the average duration of each benchmark form, from a kernel-trace run
+    of bench.py with the same arguments."""
+    import statistics
+    stats = _csv_rows(trace_dir, "*kernel_stats.csv")
+    trace = _csv_rows(trace_dir, "*kernel_trace.csv")
+    E = 8 if moe else 0
+    dur = {}
+    for r in trace:
+        k = kernel_form(r["Kernel_Name"], int(r.get("Grid_Size_Y", 1) or 1), E)
+        if k:
+            dur.setdefault(k, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    name = profile_name(workload, n, moe)
+    args = "--moe" if moe else f"--workload {workload} --n {n} --steps {steps} --warmup {warmup}"
+    cmd = (f"cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <out>/trace_{name} -o bench "
+           f"-- python3 <repo>/bench.py --cpu-seconds 0 {args}")
+    forms = {k: {"launches": len(v), "avg_us": round(statistics.mean(v) / 1e3, 3),
+                 "median_us": round(statistics.median(v) / 1e3, 3)} for k, v in sorted(dur.items())}
+    labels = {"fused": "fused quantize + mat-vec (fp32 activation)", "gemv": "mat-vec (q8_1 activation)",
+              "quantize": "q8_1 quantizer", "probe": "streaming-read probe over the same weight bytes",
+              "id": "expert-indexed gate/up (q8_1 activation)",
+              "id_fused": "expert-indexed gate/up (fp32 activation)",
+              "id_shared": "expert-indexed gate/up, scales, bias rows and a shared expert"}
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, f"{name}_kernel_trace.md"), "w") as f:
+        f.write(f"# Kernel trace: {name.replace('_n', ', n=')}\n\n")
+        f.write(f"Command (MI355X, one GPU):\n\n    {cmd}\n\n")
+        f.write("rocprofv3 --stats summary (durations in ns):\n\n")
+        f.write("| kernel | calls | avg ns | min ns | max ns |\n|---|---|---|---|---|\n")
+        for r in stats:
+            f.write(f"| {r['Name'][:100]} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                    f"{r['MinNs']} | {r['MaxNs']} |\n")
+        f.write("\nPer form (from the trace):\n\n")
+        for k, g in forms.items():
+            f.write(f"- {labels.get(k, k)}: {g['launches']} launches, average {g['avg_us']} us, "
+                    f"median {g['median_us']} us\n")
+        f.write("\n```json\n" + json.dumps({"profile": name, "source_sha256_16": kernel_source_hash(),
+                                            "forms": forms}, indent=1) + "\n```\n")
+    print(json.dumps({"profile": name, "forms": forms}))
+
+
+def summarize_sq(sq_dir: str, workload: str, n: int) -> None:
+    """profiles/<workload>_n<n>_sq_counters.md: SQ counters per launch
+    (median over dispatches) of each benchmark form, and the ALU ceiling they
+    imply: VALU wave-instructions / the issue peak."""
+    import statistics
+    from quantized_decode_gemv_quantize_amd import synth
+    wl = synth.BY_NAME[workload]
+    vals = {}
+    for r in _csv_rows(sq_dir, "*counter_collection.csv"):
+        k = kernel_form(r["Kernel_Name"])
+        if k:
+            vals.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    forms = {}
+    for k, cs in sorted(vals.items()):
+        med = {c: statistics.median(v) for c, v in cs.items()}
+        valu = med.get("SQ_INSTS_VALU", 0.0)
+        forms[k] = {"dispatches": len(next(iter(cs.values()))), **{c: round(v) for c, v in med.items()},
+                    "valu_issue_bound_us": round(valu / VALU_ISSUE_PEAK * 1e6, 3),
+                    "valu_per_weight_byte_per_column": round(valu * 64 / (wl.weight_bytes * max(n, 1)), 4)}
+    name = f"{workload}_n{n}"
+    cmd = (f"cd /tmp && timeout -s KILL 120 rocprofv3 --pmc {' '.join(SQ_COUNTERS)} --output-format csv "
+           f"-d <out>/sq_{name} -o bench -- python3 <repo>/bench.py --cpu-seconds 0 --workload {workload} "
+           f"--n {n} --steps 50 --warmup 10")
+    with open(os.path.join(PROFILES, f"{name}_sq_counters.md"), "w") as f:
+        f.write(f"# SQ counters: {workload}, n={n}\n\n")
+        f.write(f"Command (MI355X, one GPU):\n\n    {cmd}\n\n")
+        f.write("Per launch, median over dispatches. `valu_issue_bound_us` = SQ_INSTS_VALU / 614.4e9 "
+                "(256 CUs x 4 SIMDs x 2.4 GHz, one wave64 vector instruction per SIMD every 4 cycles): the "
+                "time the vector instructions alone take with every SIMD issuing every cycle. "
+                "`valu_per_weight_byte_per_column` counts lane-instructions (x64) per weight byte and "
+                "activation column.\n\n")
+        cols = ["dispatches"] + SQ_COUNTERS + ["valu_issue_bound_us", "valu_per_weight_byte_per_column"]
+        f.write("| form | " + " | ".join(cols) + " |\n|" + "---|" * (len(cols) + 1) + "\n")
+        for k, g in forms.items():
+            f.write(f"| {k} | " + " | ".join(str(g.get(c, "")) for c in cols) + " |\n")
+        f.write("\n```json\n" + json.dumps({"workload": workload, "n": n, "source_sha256_16": kernel_source_hash(),
+                                            "forms": forms}, indent=1) + "\n```\n")
+    print(json.dumps({"workload": workload, "n": n, "forms": forms}))
+
+
+def committed_figures(fname: str):
+    """The JSON block of a profiles/ summary, or None when it is absent or
+    the kernel sources changed since it was taken."""
+    path = os.path.join(PROFILES, fname)
+    if not os.path.exists(path):
+        return None
+    try:
+        fig = json.loads(open(path).read().split("```json", 1)[1].split("```", 1)[0])
+    except (IndexError, ValueError):
+        return None
+    return fig if fig.get("source_sha256_16") == kernel_source_hash() else None
 
 
 def summarize(trace_dir: str, fetch_dir: str, write_dir: str) -> None:
     """Write the kernel-trace and HBM-traffic summaries of the default
     workload under profiles/ (text with one JSON block of the figures), for
     the fused kernel and the two-launch form's mat-vec kernel."""
-    import csv
-    import glob
     import statistics
-
-    def rows(d, pat):
-        f = glob.glob(os.path.join(d, "**", pat), recursive=True)
-        return list(csv.DictReader(open(f[0])))
+    rows = _csv_rows
 
     stats = rows(trace_dir, "*kernel_stats.csv")
     trace = rows(trace_dir, "*kernel_trace.csv")
-    dur = {"fused": [], "gemv": [], "quantize": []}
+    dur = {"fused": [], "gemv": [], "quantize": [], "probe": []}
     for r in trace:
-        k = kernel_kind(r["Kernel_Name"])
-        if k is None and r["Kernel_Name"].startswith("qmv::quantize_q8_1_kernel"):
-            k = "quantize"
-        if k:
+        k = kernel_form(r["Kernel_Name"])
+        if k in dur:
             dur[k].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
 
     # calibration: the 256 MiB device copy (reads and writes COPY_BYTES)
@@ -130,23 +262,32 @@ def summarize(trace_dir: str, fetch_dir: str, write_dir: str) -> None:
     fetch_scale = COPY_BYTES / 1024 / fetch_copy
     write_scale = COPY_BYTES / 1024 / write_copy
 
-    def counter(d, kind):
-        vals = [float(r["Counter_Value"]) for r in rows(d, "*counter_collection.csv")
-                if kernel_kind(r["Kernel_Name"]) == kind]
-        return statistics.median(vals), len(vals)
-
     from quantized_decode_gemv_quantize_amd import synth
     wl = synth.BY_NAME["q4_k_4096x14336"]
     figures = {"workload": wl.name, "n": 1, "source_sha256_16": kernel_source_hash(),
                "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4),
                "quantize_avg_us": round(statistics.mean(dur["quantize"]) / 1e3, 3) if dur["quantize"] else None}
-    for kind, alg in (("fused", fused_bytes(wl, 1)), ("gemv", algorithmic_bytes(wl, 1))):
+    kinds = [("fused", fused_bytes(wl, 1)), ("gemv", algorithmic_bytes(wl, 1))]
+
+    def probe_counter(d):
+        return [float(r["Counter_Value"]) for r in rows(d, "*counter_collection.csv")
+                if kernel_form(r["Kernel_Name"]) == "probe"]
+    if probe_counter(fetch_dir) and probe_counter(write_dir):
+        kinds.append(("probe", wl.weight_bytes))
+
+    def counter(d, kind):
+        vals = [float(r["Counter_Value"]) for r in rows(d, "*counter_collection.csv")
+                if kernel_form(r["Kernel_Name"]) == kind]
+        return statistics.median(vals), len(vals)
+
+    for kind, alg in kinds:
         fk, nf = counter(fetch_dir, kind)
         wk, nw = counter(write_dir, kind)
         traffic = fk * 1024 * fetch_scale + wk * 1024 * write_scale
+        d = dur.get(kind) or [0]
         figures[kind] = {
-            "launches": len(dur[kind]), "avg_us": round(statistics.mean(dur[kind]) / 1e3, 3),
-            "median_us": round(statistics.median(dur[kind]) / 1e3, 3),
+            "launches": len(dur.get(kind, [])), "avg_us": round(statistics.mean(d) / 1e3, 3),
+            "median_us": round(statistics.median(d) / 1e3, 3),
             "fetch_kib_per_launch": fk, "write_kib_per_launch": wk, "counter_dispatches": [nf, nw],
             "traffic_bytes_per_launch": int(traffic), "algorithmic_bytes_per_launch": alg,
             "traffic_over_algorithmic": round(traffic / alg, 4)}
@@ -157,7 +298,8 @@ def summarize(trace_dir: str, fetch_dir: str, write_dir: str) -> None:
                  "-- python3 <repo>/bench.py --cpu-seconds 0 --steps 50 --warmup 10 --copy-probe")
     cmd_write = cmd_fetch.replace("FETCH_SIZE", "WRITE_SIZE").replace("pmc_fetch", "pmc_write")
     names = {"fused": "fused quantize + mat-vec (mmvq_f32, fp32 activation)",
-             "gemv": "mat-vec of the two-launch form (mmvq, q8_1 activation)"}
+             "gemv": "mat-vec of the two-launch form (mmvq, q8_1 activation)",
+             "probe": "streaming-read probe over the same weight bytes (mmvq_read_probe)"}
     with open(os.path.join(PROFILES, "mmvq_q4_k_4096x14336_n1_kernel_trace.md"), "w") as f:
         f.write("# Kernel trace: Q4_K mat-vec 4096x14336, n=1 (default bench workload)\n\n")
         f.write(f"Command (MI355X, one GPU):\n\n    {cmd_trace}\n\n")
@@ -167,7 +309,9 @@ def summarize(trace_dir: str, fetch_dir: str, write_dir: str) -> None:
             f.write(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
                     f"{r['MinNs']} | {r['MaxNs']} |\n")
         f.write("\n")
-        for kind in ("fused", "gemv"):
+        for kind in ("fused", "gemv", "probe"):
+            if kind not in figures:
+                continue
             g = figures[kind]
             f.write(f"{names[kind]}: {g['launches']} launches, average {g['avg_us']} us, "
                     f"median {g['median_us']} us.\n")
@@ -179,7 +323,9 @@ def summarize(trace_dir: str, fetch_dir: str, write_dir: str) -> None:
         f.write("Calibration: the same process copies a 256 MiB device buffer (reads and writes 256 MiB);\n"
                 f"FETCH_SIZE reads {fetch_copy:.0f} KiB for it (scale {fetch_scale:.4f}), WRITE_SIZE "
                 f"{write_copy:.0f} KiB (scale {write_scale:.4f}).\n\n")
-        for kind in ("fused", "gemv"):
+        for kind in ("fused", "gemv", "probe"):
+            if kind not in figures:
+                continue
             g = figures[kind]
             f.write(f"{names[kind]}, per launch (median over dispatches): FETCH_SIZE "
                     f"{g['fetch_kib_per_launch']:.1f} KiB, WRITE_SIZE {g['write_kib_per_launch']:.1f} KiB -> "
@@ -194,15 +340,8 @@ def measured_traffic(kind: str):
     """Traffic per launch of the 'fused' or 'gemv' kernel from the committed
     counter summary, or None when the kernel sources changed since the
     counters were taken."""
-    path = os.path.join(PROFILES, "mmvq_q4_k_4096x14336_n1_hbm_traffic.md")
-    if not os.path.exists(path):
-        return None
-    text = open(path).read()
-    try:
-        fig = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
-    except (IndexError, ValueError):
-        return None
-    if fig.get("source_sha256_16") != kernel_source_hash() or kind not in fig:
+    fig = committed_figures("mmvq_q4_k_4096x14336_n1_hbm_traffic.md")
+    if fig is None or kind not in fig:
         return None
     return fig[kind]["traffic_bytes_per_launch"]
 
@@ -468,6 +607,12 @@ def main():
     if args.summarize:
         summarize(*args.summarize)
         return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.workload, args.n, args.moe, args.steps, args.warmup)
+        return
+    if args.summarize_sq:
+        summarize_sq(args.summarize_sq, args.workload, args.n)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               f"(the mat-vec shards by rows across GPUs, see DESIGN.md)", file=sys.stderr)
@@ -561,6 +706,25 @@ def main():
                      "pct_of_probe": round(100 * res["probe_us"] / kern_us, 2)},
         "cpu_baseline": cpu,
     }
+    # ALU ceiling of the dominant kernel from its committed SQ counters (same
+    # sources): where its vector instructions alone need longer than its
+    # bytes at the HBM peak, the kernel is bound by instruction issue and the
+    # roofline is reported against the vector issue peak.
+    sq = committed_figures(f"{wl.name}_n{n}_sq_counters.md")
+    form = "fused" if fused else "gemv"
+    if sq is not None and form in sq.get("forms", {}):
+        valu = sq["forms"][form]["SQ_INSTS_VALU"]
+        issue_us = valu / VALU_ISSUE_PEAK * 1e6
+        hbm_us = kern_bytes / (HBM_PEAK_GBS * 1e9) * 1e6
+        alu = {"valu_wave_insts_per_launch": valu, "valu_issue_bound_us": round(issue_us, 3),
+               "hbm_bound_us": round(hbm_us, 3), "issue_peak_tops": round(VALU_ISSUE_PEAK * 64 / 1e12, 2)}
+        if issue_us > hbm_us:
+            r = line["roofline"]
+            r["hbm"] = {k: r[k] for k in ("achieved", "peak", "unit", "frac")}
+            tops = valu * 64 / (kern_us * 1e-6) / 1e12
+            r.update(bound="alu", achieved=round(tops, 2), peak=alu["issue_peak_tops"], unit="TOP/s",
+                     frac=round(tops / alu["issue_peak_tops"], 4))
+        line["roofline"]["alu"] = alu
     print(json.dumps(line), flush=True)
 
     if args.all:
