@@ -107,7 +107,7 @@ def kernel_form(name: str, grid_y: int = 1, n_experts: int = 0) -> str | None:
     else None."""
     if name.startswith("void qmv::mmvq_rows_kernel<"):
         return "fused" if _targs(name)[5] == "true" else "gemv"      # <F, NC, R, P, G, XF, ...>
-    if name.startswith("void qmv::mmq_q4k_kernel<"):
+    if name.startswith("void qmv::mmq_kernel<"):
         return "gemv"
     if name.startswith("qmv::quantize_q8_1_kernel"):
         return "quantize"
@@ -422,6 +422,12 @@ def timed_replay(torch, stream, g_warm, g_timed):
     return t.ms, time.perf_counter() - t0
 
 
+def mmq_route(B, wl, n: int) -> bool:
+    """True where mmvq with q8_1 columns runs the many-column (matrix-core)
+    kernel: K a multiple of 256 and n >= 9 (Q4_K: n >= 6)."""
+    return wl.K % 256 == 0 and (n >= 9 or (wl.wtype == B.Q4_K and n >= 6))
+
+
 def time_workload(torch, B, wl, n: int, steps: int, warmup: int, probe: bool = True):
     """GPU timings of one workload: exactly `steps` timed launches of each
     form after `warmup` untimed ones, weights rotating over the copies.
@@ -443,15 +449,15 @@ def time_workload(torch, B, wl, n: int, steps: int, warmup: int, probe: bool = T
     }
     res = {"copies": C, "steps": steps, "warmup": warmup}
     # the two step forms must agree before either is timed: bit for bit,
-    # except Q4_K at 6..8 columns, where the q8_1 form runs the many-column
-    # kernel (another summation order; a loose relative check)
+    # except where the q8_1 form runs the many-column kernel (another
+    # summation order; a loose relative check)
     if fused_ok:
         ref = torch.empty_like(out)
         B.mmvq_quantize_q8_1(x, wl.K, n, wl.K, y, s)
         B.mmvq(Ws[0], wl.wtype, wl.M, wl.K, y, n, ref, s)
         B.mmvq_f32(Ws[0], wl.wtype, wl.M, wl.K, x, n, wl.K, out, s)
         torch.cuda.synchronize()
-        if wl.wtype == B.Q4_K and n >= 6:
+        if mmq_route(B, wl, n):
             same = bool(((ref - out).abs() <= 1e-4 * ref.abs().max() + 1e-6).all())
         else:
             same = torch.equal(ref.view(torch.int32), out.view(torch.int32))
@@ -692,8 +698,8 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": (measured_traffic("fused" if fused else "gemv")
                                  if wl.name == "q4_k_4096x14336" and n == 1 else None),
-                     "kernel": (f"mmq_q4k_kernel ({synth.TYPE_NAME[wl.wtype].upper()}, n={n}, int8 matrix cores)"
-                                if wl.wtype == B.Q4_K and n >= 6 and not fused else
+                     "kernel": (f"mmq_kernel ({synth.TYPE_NAME[wl.wtype].upper()}, n={n}, int8 matrix cores)"
+                                if mmq_route(B, wl, n) and not fused else
                                 f"mmvq_rows_kernel ({synth.TYPE_NAME[wl.wtype].upper()}, n={n}, "
                                 f"{'fp32' if fused else 'q8_1'} activation)"),
                      "bytes_per_launch": kern_bytes,
@@ -731,7 +737,8 @@ def main():
         for name in ["q4_0_256x1024", "q4_k_4096x4096", "q4_k_4096x14336", "q4_k_14336x4096",
                      "q6_k_128256x4096", "q8_0_4096x14336"]:
             w = synth.BY_NAME[name]
-            many = (16, 32, 64, 128) if name in ("q4_k_4096x14336", "q4_k_14336x4096") else ()
+            many = ((16, 32, 64, 128) if name in ("q4_k_4096x14336", "q4_k_14336x4096")
+                    else (16, 64) if name in ("q6_k_128256x4096", "q8_0_4096x14336") else ())
             for nn in tuple(w.n if name != "q4_k_4096x14336" else (1, 2, 4, 8)) + many:
                 r, *_ = time_workload(torch, B, w, nn, 500, 50)
                 gb = algorithmic_bytes(w, nn) / (r["gemv_us"] * 1e-6) / 1e9

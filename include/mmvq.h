@@ -121,11 +121,14 @@ enum {
  * forms [MMVQ §分派]. */
 #define MMVQ_MAX_COLS 8
 
-/* Largest number of columns of the many-column path: mmvq and mmvq_ex
- * (q8_1 activations, no gate, Q4_K weights) with 6 <= n <=
- * MMVQ_MAX_COLS_BATCH run on the matrix cores [MMVQ §多个 token 时]; the
- * quantizer takes up to MMVQ_MAX_COLS_BATCH columns too. Other forms and
- * types return MMVQ_ERR_SHAPE for n > MMVQ_MAX_COLS. */
+/* Largest number of columns of the weight-matrix calls without expert ids
+ * (mmvq, mmvq_glu, mmvq_ex and their fp32 forms) and of the quantizer.
+ * mmvq and mmvq_ex with q8_1 activations, no gate and K a multiple of 256
+ * run on the matrix cores from 9 columns (Q4_K from 6) [MMVQ §多个 token 时];
+ * the other forms take more than MMVQ_MAX_COLS columns as groups of at most
+ * MMVQ_MAX_COLS columns through the row kernels (each group reads the
+ * weights again). The expert-indexed calls take at most MMVQ_MAX_COLS
+ * tokens. */
 #define MMVQ_MAX_COLS_BATCH 256
 
 /* Block geometry of a type: elements per block and bytes per block
@@ -152,8 +155,9 @@ int mmvq_quantize_q8_1(const float *x, int64_t K, int64_t n, int64_t ldx,
  * per 32-block. Q4_K: per 32-element
  * sub-block t, d*sc_t*d8*sum(q*qy) - dmin*m_t*d8*sum(qy). Q6_K: per
  * 16-element sub-block, d*sc*d8*sum((q-32)*qy). Accumulated in fp32.
- * Requires K % qk == 0, M >= 1 and 1 <= n <= MMVQ_MAX_COLS, or for Q4_K
- * 1 <= n <= MMVQ_MAX_COLS_BATCH. A lane of the n <= MMVQ_MAX_COLS forms
+ * Requires K % qk == 0, M >= 1 and 1 <= n <= MMVQ_MAX_COLS_BATCH. A lane
+ * of the row kernels (n <= MMVQ_MAX_COLS, and each group of MMVQ_MAX_COLS
+ * columns beyond)
  * handles one unit of a row (a block for Q4_0 and Q8_0, half or whole
  * 64-weight chunks for Q4_K, a quarter super-block for Q6_K); rows of more
  * than 512 units are walked by the team in chunks of at most 512 lanes
@@ -161,11 +165,11 @@ int mmvq_quantize_q8_1(const float *x, int64_t K, int64_t n, int64_t ldx,
  * than 2^24 units (K > 2^29 for Q4_0 and Q8_0, K > 2^30 for Q4_K and Q6_K)
  * and M*K > 2^40 return MMVQ_ERR_SHAPE (the same limits hold for every
  * entry point below except the many-column path).
- * For Q4_K, n >= 6 (without a gate, q8_1 columns) takes the many-column
- * path, where
- * the integer dots of 16 rows x 16 columns x 32 elements come from one int8
- * matrix-core instruction and the same scales are applied per sub-block
- * (no upper bound on K there). */
+ * With K a multiple of 256, n >= 9 (Q4_K: n >= 6) takes the many-column
+ * path, where the integer dots of 16 rows x 16 columns x 32 elements come
+ * from one int8 matrix-core instruction and the same block scales are
+ * applied per 32-element block (Q6_K: per 16-element half); K / 256 up to
+ * 2^24 there. */
 int mmvq(const void *W, int type, int64_t M, int64_t K,
          const void *y_q, int64_t n, float *out, void *stream);
 

@@ -97,13 +97,15 @@ mmvq_epilogue glu_only(int glu_op) {
   return e;
 }
 
-// Many columns (Q4_K from 6 columns, up to MMVQ_MAX_COLS_BATCH): the MFMA
-// kernel, q8_1 activations, no gate; the epilogue's up scale and bias apply.
+// Many columns (up to MMVQ_MAX_COLS_BATCH): the MFMA kernel, q8_1
+// activations, no gate, K a multiple of 256; the epilogue's up scale and
+// bias apply.
 int mmq_common(const void* W, int type, int64_t M, int64_t K, const void* y_q, int64_t n,
                const mmvq_epilogue* epi, float* out, void* stream) {
   if (!W || !y_q || !out) return MMVQ_ERR_NULL;
-  if (type != MMVQ_Q4_K) return dispatch_for(type, false) ? MMVQ_ERR_SHAPE : MMVQ_ERR_TYPE;
-  if (M < 1 || K < 1 || K % 256 != 0 || n > MMVQ_MAX_COLS_BATCH) return MMVQ_ERR_SHAPE;
+  const Dispatch* d = dispatch_for(type, false);
+  if (!d) return MMVQ_ERR_TYPE;
+  if (M < 1 || K < 1 || K % 256 != 0 || n < 1 || n > MMVQ_MAX_COLS_BATCH) return MMVQ_ERR_SHAPE;
   if (M > (int64_t(1) << 40) / K || K / 256 > (int64_t(1) << 24)) return MMVQ_ERR_SHAPE;
   if (!aligned(W, 16) || !aligned(y_q, 16) || !aligned(out, 4)) return MMVQ_ERR_ALIGN;
   RowArgs ra{};
@@ -116,39 +118,57 @@ int mmq_common(const void* W, int type, int64_t M, int64_t K, const void* y_q, i
   a.up_bias = ra.up_bias;
   a.up_scale = ra.up_scale;
   a.M = M;
-  a.row_bytes = K / 256 * 144;
+  a.row_bytes = K / d->qk * d->block_bytes;
   a.ycol_bytes = K / 32 * kQ8Bytes;
   a.n = static_cast<int>(n);
   a.nsb = static_cast<int>(K / 256);
-  return launch_mmq_q4k(a, static_cast<hipStream_t>(stream));
+  return launch_mmq(type, a, static_cast<hipStream_t>(stream));
 }
 
-// Plain or gate/up product with an optional epilogue (W_gate NULL: no gate).
-constexpr int64_t kMmqMinColsQ4K = 6;
+// Columns from which the matrix-core kernel takes a q8_1 product without a
+// gate (K a multiple of 256). Q4_K: from 6 (one 16-column tile: ~14.5 us at
+// 4096x14336 and 14336x4096 for any n <= 16, the row kernels 16.5 / 14.5 us
+// at n = 6 and 24.8 / 17.8 us at n = 8); the other formats past the row
+// kernels' 8 columns.
+int64_t mmq_min_cols(int type) { return type == MMVQ_Q4_K ? 6 : MMVQ_MAX_COLS + 1; }
 
+// Plain or gate/up product with an optional epilogue (W_gate NULL: no gate).
+// More than MMVQ_MAX_COLS columns outside the matrix-core kernel's forms
+// (a gate, fp32 activations, K not a multiple of 256) run as groups of at
+// most MMVQ_MAX_COLS columns through the row kernels, each group reading the
+// weights again; all arguments are checked before the first group is
+// enqueued.
 int rows_common(const void* W_up, const void* W_gate, int type, int64_t M, int64_t K, const ActIn& in, int64_t n,
                 const mmvq_epilogue* epi, float* out, void* stream) {
-  if (n > MMVQ_MAX_COLS && !W_gate && !in.x) return mmq_common(W_up, type, M, K, in.y_q, n, epi, out, stream);
-  // From 6 columns the matrix-core kernel is faster than the row kernels
-  // for Q4_K with q8_1 columns (one 16-column tile: ~14.5 us at 4096x14336
-  // and 14336x4096 for any n <= 16, the row kernels 16.5 / 14.5 us at n = 6
-  // and 24.8 / 17.8 us at n = 8).
-  if (type == MMVQ_Q4_K && n >= kMmqMinColsQ4K && !W_gate && !in.x)
-    return mmq_common(W_up, type, M, K, in.y_q, n, epi, out, stream);
+  const bool mmq_form = !W_gate && !in.x && K % 256 == 0 && dispatch_for(type, false) != nullptr;
+  if (mmq_form && n >= mmq_min_cols(type)) return mmq_common(W_up, type, M, K, in.y_q, n, epi, out, stream);
 #ifdef QMV_TUNING
-  if (getenv("MMVQ_FORCE_MMQ") && !W_gate && !in.x && type == MMVQ_Q4_K)
-    return mmq_common(W_up, type, M, K, in.y_q, n, epi, out, stream);
+  if (getenv("MMVQ_FORCE_MMQ") && mmq_form) return mmq_common(W_up, type, M, K, in.y_q, n, epi, out, stream);
 #endif
+  if (n > MMVQ_MAX_COLS_BATCH) return MMVQ_ERR_SHAPE;
+  const int64_t n0 = n < MMVQ_MAX_COLS ? n : MMVQ_MAX_COLS;
   const Dispatch* d;
   RowArgs a;
-  int rc = check_gemv(W_up, type, M, K, in, n, out, &d, &a);
+  int rc = check_gemv(W_up, type, M, K, in, n0, out, &d, &a);
   if (rc) return rc;
   if (W_gate && !aligned(W_gate, 16)) return MMVQ_ERR_ALIGN;
   rc = set_epilogue(epi, W_gate != nullptr, &a);
   if (rc) return rc;
   a.Wg = static_cast<const uint8_t*>(W_gate);
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  return W_gate ? d->rows_glu(a, K, n, st) : d->rows(a, K, n, st);
+  // column groups: the activation columns and outputs of group g start
+  // g*MMVQ_MAX_COLS columns in (the row kernels need 4-byte aligned q8_1
+  // columns, which every column of a 16-byte aligned y_q is)
+  for (int64_t j0 = 0; j0 < n; j0 += MMVQ_MAX_COLS) {
+    const int64_t nn = n - j0 < MMVQ_MAX_COLS ? n - j0 : MMVQ_MAX_COLS;
+    RowArgs g = a;
+    if (in.x) g.x = a.x + j0 * a.ldx;
+    else g.y = a.y + j0 * a.ycol_bytes;
+    g.out = a.out + j0 * M;
+    rc = W_gate ? d->rows_glu(g, K, nn, st) : d->rows(g, K, nn, st);
+    if (rc) return rc;
+  }
+  return MMVQ_OK;
 }
 
 // Expert-indexed product with an optional epilogue and shared expert.

@@ -8,53 +8,60 @@ namespace qmv {
 
 namespace {
 
-template <int RT, int CT, int NW>
-int launch_tile(const MmqArgs& a, hipStream_t st) {
-  if constexpr (!mmq_fits<RT, CT, NW>()) {
-    return MMVQ_ERR_SHAPE;
-  } else {
-  const int64_t gx = (a.M + 16 * RT - 1) / (16 * RT);
-  const int64_t gy = (a.n + 16 * CT - 1) / (16 * CT);
-  hipLaunchKernelGGL((mmq_q4k_kernel<RT, CT, NW>), dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy)),
-                     dim3(NW * kWave), 0, st, a);
-  return check_launch();
-  }
-}
-
 int64_t groups(const MmqArgs& a, int rt, int ct) {
   return ((a.M + 16 * rt - 1) / (16 * rt)) * ((a.n + 16 * ct - 1) / (16 * ct));
 }
 
-template <int NW>
+template <class F, int RT, int CT, int NW>
+int launch_tile(MmqArgs a, hipStream_t st) {
+  if constexpr (!mmq_fits<F, RT, CT, NW>()) {
+    return MMVQ_ERR_SHAPE;
+  } else {
+    a.gx = static_cast<int>((a.M + 16 * RT - 1) / (16 * RT));
+    a.gy = (a.n + 16 * CT - 1) / (16 * CT);
+    const int64_t grid = static_cast<int64_t>(a.gx) * a.gy;
+    hipLaunchKernelGGL((mmq_kernel<F, RT, CT, NW>), dim3(static_cast<unsigned>(grid)), dim3(NW * kWave), 0, st, a);
+    return check_launch();
+  }
+}
+
+template <class F, int NW>
 int launch_waves(const MmqArgs& a, int rt, int ct, hipStream_t st) {
   switch (rt * 10 + ct) {
-    case 22: return launch_tile<2, 2, NW>(a, st);
-    case 21: return launch_tile<2, 1, NW>(a, st);
-    case 11: return launch_tile<1, 1, NW>(a, st);
+    case 22: return launch_tile<F, 2, 2, NW>(a, st);
+    case 21: return launch_tile<F, 2, 1, NW>(a, st);
+    case 11: return launch_tile<F, 1, 1, NW>(a, st);
     default: return MMVQ_ERR_SHAPE;
   }
 }
 
-}  // namespace
+template <class F>
+constexpr bool fits(int rt, int ct, int nw) {
+  return rt == 2 ? (ct == 2 ? (nw == 8 ? mmq_fits<F, 2, 2, 8>() : mmq_fits<F, 2, 2, 4>())
+                            : (nw == 8 ? mmq_fits<F, 2, 1, 8>() : mmq_fits<F, 2, 1, 4>()))
+                 : (nw == 8 ? mmq_fits<F, 1, 1, 8>() : mmq_fits<F, 1, 1, 4>());
+}
 
 // Tile (row tiles x column tiles of 16 per workgroup): the largest tile that
 // still gives every compute unit a workgroup (larger tiles re-read fewer
-// weights and activations) and has no more column tiles than n needs, else
-// one tile. When the grid is no larger than the chip, eight waves split K
-// instead of four, so each compute unit has more loads in flight.
-int launch_mmq_q4k(const MmqArgs& a, hipStream_t st) {
+// weights and activations), has no more column tiles than n needs and fits
+// the LDS, else one tile. When the grid is no larger than the chip, eight
+// waves split K instead of four, so each compute unit has more loads in
+// flight.
+template <class F>
+int launch_format(const MmqArgs& a, hipStream_t st) {
   static const int kTiles[][2] = {{2, 2}, {2, 1}, {1, 1}};
   const int64_t cus = device_cus();
   const int ct_max = (a.n + 15) / 16;
   int rt = 1, ct = 1;
   for (const auto& t : kTiles) {
-    if (t[1] <= ct_max && groups(a, t[0], t[1]) >= cus) {
+    if (t[1] <= ct_max && groups(a, t[0], t[1]) >= cus && fits<F>(t[0], t[1], 4)) {
       rt = t[0];
       ct = t[1];
       break;
     }
   }
-  int nw = groups(a, rt, ct) <= cus ? 8 : 4;
+  int nw = groups(a, rt, ct) <= cus && fits<F>(rt, ct, 8) ? 8 : 4;
 #ifdef QMV_TUNING
   if (const char* e = getenv("MMVQ_MMQ_TILE")) {
     rt = e[0] - '0';
@@ -63,9 +70,21 @@ int launch_mmq_q4k(const MmqArgs& a, hipStream_t st) {
   if (const char* e = getenv("MMVQ_MMQ_WAVES")) nw = atoi(e);
 #endif
   switch (nw) {
-    case 4: return launch_waves<4>(a, rt, ct, st);
-    case 8: return launch_waves<8>(a, rt, ct, st);
+    case 4: return launch_waves<F, 4>(a, rt, ct, st);
+    case 8: return launch_waves<F, 8>(a, rt, ct, st);
     default: return MMVQ_ERR_SHAPE;
+  }
+}
+
+}  // namespace
+
+int launch_mmq(int type, const MmqArgs& a, hipStream_t st) {
+  switch (type) {
+    case 12: return launch_format<Q4K>(a, st);
+    case 14: return launch_format<Q6K>(a, st);
+    case 2: return launch_format<Q40>(a, st);
+    case 8: return launch_format<Q80>(a, st);
+    default: return MMVQ_ERR_TYPE;
   }
 }
 

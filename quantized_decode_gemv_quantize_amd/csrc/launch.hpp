@@ -279,6 +279,6 @@ int launch_quantize_q8_1(const float* x, uint8_t* y, int64_t K, int64_t n, int64
 int launch_read_probe(const uint8_t* src, int64_t bytes, uint32_t* sink, hipStream_t st);
 
 struct MmqArgs;
-int launch_mmq_q4k(const MmqArgs& a, hipStream_t st);
+int launch_mmq(int type, const MmqArgs& a, hipStream_t st);
 
 }  // namespace qmv

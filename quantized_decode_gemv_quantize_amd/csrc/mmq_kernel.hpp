@@ -1,5 +1,6 @@
-// mmq_kernel.hpp - the many-column path (6 or more activation columns) for
-// Q4_K weights: int8 matrix-core (MFMA) products of 16x16 tiles.
+// mmq_kernel.hpp - the many-column path (more activation columns than the
+// mat-vec kernels take at their best) for Q4_K, Q6_K, Q4_0 and Q8_0 weights:
+// int8 matrix-core (MFMA) products of 16x16 tiles.
 //
 // Citations: [MMVQ §X] = page "llama.cpp 源码完全拆解(十四):mul_mat_vec_q——解码时
 // 一条量化权重如何被 dp4a 逐块点积", section X.
@@ -7,22 +8,26 @@
 // Beyond a handful of columns the per-column integer dots of the mat-vec
 // kernels cost more than the weight stream [MMVQ §多个 token 时, §分派]; here
 // the weights are decoded once into MFMA operands and reused across 16-column
-// tiles, and the integer dots of every (row, column, 32-element sub-block) come
-// from v_mfma_i32_16x16x32_i8: A = 16 rows x 32 codes of one sub-block, B = the
-// matching q8_1 block of 16 columns. The block scales are those of the mat-vec
-// [MMVQ §一次 vec_dot 的解剖], summed in another order:
-//   out[r][c] += d[r] * sum_t sc_t[r]*C_t[r][c] * d8_t[c]
-//              - dmin[r] * sum_t m_t[r] * (d8_t[c]*S_t[c])
-// with C_t the int32 tile of sub-block t and S_t[c] the sum of the q8_1 codes
-// of column c in block t. sc_t*C_t is an exact integer (below 2^22), so each
-// sub-block costs one fp32 multiply-add per output; d is applied once per
-// super-block, and the min term, a contraction over the 8 sub-blocks of an
-// 8-long column of -dmin*m_t by an 8-long row of d8_t*S_t, is two fp32 MFMAs
-// (v_mfma_f32_16x16x4_f32, even and odd t) per tile and super-block.
+// tiles, and the integer dots of every (row, column, 32-element block t) come
+// from v_mfma_i32_16x16x32_i8: A = 16 rows x 32 codes of block t, B = the
+// matching q8_1 block of 16 columns. The block scales are those of the
+// mat-vec [MMVQ §一次 vec_dot 的解剖], summed in another order (C_t the int32
+// tile of block t, S_t[c] the sum of column c's q8_1 codes in block t, d8_t
+// its scale):
+//   Q4_K: out += d * sum_t sc_t*C_t*d8_t - dmin * sum_t m_t*(d8_t*S_t)
+//         (sc_t*C_t exact below 2^22; the min term, a contraction over the 8
+//         sub-blocks, is two fp32 MFMAs per tile and step)
+//   Q4_0: out += sum_t d_t*(d8_t*C_t - 8*s_t)      (codes 0..15; s_t the
+//         q8_1 block's stored fp16 d8*sum(q), as the mat-vec uses it)
+//   Q8_0: out += sum_t d_t*d8_t*C_t                (signed codes)
+//   Q6_K: out += d * sum_t d8_t*(sc_2t*(C_t,lo - 32*S_t,lo) + sc_2t+1*(C_t,hi - 32*S_t,hi))
+//         (codes 0..63; the 16-element sub-blocks 2t and 2t+1 are the two
+//         halves of block t, taken by two MFMAs whose B operand keeps only
+//         its half; each bracket is an exact integer below 2^23)
 //
 // A workgroup owns RT x CT tiles (16 rows x 16 columns each); its NW waves
-// split the K range (super-blocks) and their fp32 partials are summed through
-// LDS in a fixed order. MFMA lane layouts (checked on the device):
+// split the K range (256-weight steps) and their fp32 partials are summed
+// through LDS in a fixed order. MFMA lane layouts (checked on the device):
 //   i8 A: lane l holds row l%16, codes k = 8*(l/16) .. +7
 //   i8 B: lane l holds column l%16, codes k = 8*(l/16) .. +7
 //   f32 A: lane l holds row l%16, k = l/16; f32 B: column l%16, k = l/16
@@ -38,81 +43,110 @@ namespace qmv {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-
 __device__ __forceinline__ long pack2(uint32_t lo, uint32_t hi) {
   return static_cast<long>(static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32));
 }
 
-// LDS of one wave: the staged super-block tiles and the row factors.
-template <int RT, int CT>
-struct MmqWaveLds {
-  uint8_t a[RT][16][144];          // 16 rows' super-blocks
-  uint8_t b[CT][16][288];          // 16 columns' 8 q8_1 blocks
+// LDS accesses of one wave complete in order; the waits make the data
+// written by other lanes of the wave visible to the reads that follow.
+__device__ __forceinline__ void mmq_lds_fence() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);       // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+}
+
+// 8 bytes at a 2-byte aligned LDS address p, misaligned by MIS (0 or 2)
+// bytes from a dword boundary: dword reads re-aligned in registers.
+template <int MIS>
+__device__ __forceinline__ long lds8(const uint8_t* p) {
+  if constexpr (MIS == 0) {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(p);
+    return pack2(w[0], w[1]);
+  } else {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(p - 2);
+    return pack2(__builtin_amdgcn_alignbit(w[1], w[0], 16), __builtin_amdgcn_alignbit(w[2], w[1], 16));
+  }
+}
+
+// Two dwords at a 2-byte aligned LDS address whose misalignment (0 or 2
+// bytes) is known only at run time.
+__device__ __forceinline__ u32x2 lds8_rt(const uint8_t* p, int mis) {
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(p - mis);
+  const uint32_t w0 = w[0], w1 = w[1], w2 = mis ? w[2] : 0u;
+  const uint32_t sh = static_cast<uint32_t>(mis) * 8u;
+  u32x2 r;
+  r.x = __builtin_amdgcn_alignbit(w1, w0, sh);
+  r.y = __builtin_amdgcn_alignbit(w2, w1, sh);
+  return r;
+}
+
+// The q8_1 block t of the lane's column r16 in the B tile of column tile ct:
+// codes 8q..8q+7 (two dword reads: the 36-byte block makes the pair 8-byte
+// aligned only in odd blocks) and the block's scale.
+template <int CT>
+__device__ __forceinline__ long b_operand(const uint8_t (&b)[CT][16][288], int ct, int r16, int q, int t,
+                                          float& d8) {
+  const uint8_t* blk = &b[ct][r16][36 * t];
+  const uint32_t* cw = reinterpret_cast<const uint32_t*>(blk + 4 + 8 * q);
+  d8 = h2f(*reinterpret_cast<const uint16_t*>(blk));
+  return pack2(cw[0], cw[1]);
+}
+
+// Per-row factors of one step, written by the lanes that unpack them and
+// read back in the D layout (rows 4q..4q+3 per lane).
+template <class F, int RT> struct MmqRowLds;
+template <int RT> struct MmqRowLds<Q4K, RT> {
   uint8_t sc[RT][4][16][2];        // sc_t of row, t = 2c + h at [c][row][h]
   float d[RT][16];                 // d of row
+};
+template <int RT> struct MmqRowLds<Q40, RT> { float d[RT][8][16]; };   // d of block t of row
+template <int RT> struct MmqRowLds<Q80, RT> { float d[RT][8][16]; };
+template <int RT> struct MmqRowLds<Q6K, RT> {
+  int8_t sc[RT][16][16];           // scale of sub-block s of row at [s][row]
+  float d[RT][16];
+};
+
+template <class F, int RT, int CT>
+struct MmqWaveLds {
+  uint8_t a[RT][16][MmqGeom<F>::kRowLds];   // the 16 rows' step images
+  uint8_t b[CT][16][288];                    // 16 columns' 8 q8_1 blocks
+  MmqRowLds<F, RT> x;
 };
 
 // LDS bytes of a workgroup (the staging tiles of all waves; the reduction
 // reuses them), and the shapes that fit one compute unit's 160 KB.
-template <int RT, int CT, int NW>
+template <class F, int RT, int CT, int NW>
 constexpr size_t mmq_lds_bytes() {
-  const size_t stage = sizeof(MmqWaveLds<RT, CT>) * NW, red = sizeof(float) * NW * RT * CT * 4 * kWave;
+  const size_t stage = sizeof(MmqWaveLds<F, RT, CT>) * NW, red = sizeof(float) * NW * RT * CT * 4 * kWave;
   return stage > red ? stage : red;
 }
-template <int RT, int CT, int NW>
-constexpr bool mmq_fits() { return mmq_lds_bytes<RT, CT, NW>() <= 160 * 1024; }
+template <class F, int RT, int CT, int NW>
+constexpr bool mmq_fits() { return mmq_lds_bytes<F, RT, CT, NW>() <= 160 * 1024; }
 
-template <int RT, int CT, int NW>
-__global__ void __launch_bounds__(NW * kWave, 8 / NW) mmq_q4k_kernel(MmqArgs a) {
-  const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
-  const int r16 = lane & 15, q = lane >> 4;
-  const int64_t row_base = static_cast<int64_t>(blockIdx.x) * (16 * RT);
-  const int col_base = static_cast<int>(blockIdx.y) * (16 * CT);
-  const int sb0 = mmq_sb_begin(a.nsb, wave, NW), sb1 = mmq_sb_begin(a.nsb, wave + 1, NW);
-  const Q4K::Lane L = Q4K::lane(2 * q);       // scale unpack of chunk q (sub-blocks 2q, 2q+1)
+// Where the lane's rows sit: tile_off = byte offset of the tile's first row
+// from W; row_off(rt) = that of row r16 of row tile rt (clamped to M - 1).
+struct MmqRows {
+  int64_t tile_off, row_base, M, row_bytes;
+  __device__ int64_t row_off(int rt, int r16) const {
+    int64_t r = row_base + 16 * rt + r16;
+    r = r < M ? r : M - 1;
+    return (r - row_base) * row_bytes + tile_off;
+  }
+};
 
-  // the staging tiles of the NW waves; after the K loop the same LDS holds
-  // the partial sums of the reduction
-  constexpr int NV = RT * CT * 4;
-  __shared__ __align__(16) uint8_t smem[mmq_lds_bytes<RT, CT, NW>()];
-  MmqWaveLds<RT, CT>& lds = reinterpret_cast<MmqWaveLds<RT, CT>*>(smem)[wave];
-  float acc[RT][CT][4];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[rt][ct][i] = 0.0f;
+// One step of a format from the wave's LDS, accumulated into acc[rt][ct][i]
+// (row 4q+i of row tile rt, column r16 of column tile ct).
+template <class F> struct MmqStep;
 
-  // staged pieces -> LDS: piece k at byte 16k of the A or B tiles
-  auto store_stage = [&](const MmqStage<RT, CT>& st) {
-    uint8_t* la = &lds.a[0][0][0];
-    uint8_t* lb = &lds.b[0][0][0];
-#pragma unroll
-    for (int j = 0; j < mmq_a_slots<RT>(); ++j) {
-      const int k = lane + kWave * j;
-      if (k < kMmqAPieces * RT) *reinterpret_cast<u32x4*>(la + 16 * k) = st.a[j];
-    }
-#pragma unroll
-    for (int j = 0; j < mmq_b_slots<CT>(); ++j) {
-      const int k = lane + kWave * j;
-      if (k < kMmqBPieces * CT) *reinterpret_cast<u32x4*>(lb + 16 * k) = st.b[j];
-    }
-  };
-
-  // LDS accesses of one wave complete in order; the waits make the data
-  // written by other lanes of the wave visible to the reads that follow
-  auto lds_fence = [&]() {
-    __builtin_amdgcn_s_waitcnt(0xc07f);       // lgkmcnt(0)
-    __builtin_amdgcn_wave_barrier();
-  };
-
-  // one super-block from LDS. Lane (r16, q) unpacks sub-blocks 2q and 2q+1
-  // of row r16: the f32 A operand of the min term (k = q stands for t = 2q in
-  // the even product, t = 2q+1 in the odd one) and the scales, which the D
-  // layout reads back per chunk for rows 4q..4q+3.
-  auto compute = [&]() {
+// Q4_K. Lane (r16, q) unpacks sub-blocks 2q and 2q+1 of row r16: the f32 A
+// operand of the min term (k = q stands for t = 2q in the even product,
+// t = 2q+1 in the odd one) and the scales, which the D layout reads back per
+// chunk for rows 4q..4q+3.
+template <> struct MmqStep<Q4K> {
+  template <int RT, int CT>
+  __device__ static void run(MmqWaveLds<Q4K, RT, CT>& lds, const MmqRows&, int, int lane,
+                             float (&acc)[RT][CT][4]) {
+    const int r16 = lane & 15, q = lane >> 4;
+    const Q4K::Lane L = Q4K::lane(2 * q);       // scale unpack of chunk q (sub-blocks 2q, 2q+1)
     const long ones = 0x0101010101010101l;
     float am[RT][2];
 #pragma unroll
@@ -120,13 +154,13 @@ __global__ void __launch_bounds__(NW * kWave, 8 / NW) mmq_q4k_kernel(MmqArgs a) 
       const u32x4 hdr = *reinterpret_cast<const u32x4*>(&lds.a[rt][r16][0]);
       uint32_t scp, mp;
       Q4K::chunk_scales(hdr, L, scp, mp);
-      *reinterpret_cast<uint16_t*>(&lds.sc[rt][q][r16][0]) = static_cast<uint16_t>(scp & 0xFFFFu);
-      lds.d[rt][r16] = h2f(hdr.x);
+      *reinterpret_cast<uint16_t*>(&lds.x.sc[rt][q][r16][0]) = static_cast<uint16_t>(scp & 0xFFFFu);
+      lds.x.d[rt][r16] = h2f(hdr.x);
       const float dmin = h2f(hdr.x >> 16);
       am[rt][0] = -dmin * static_cast<float>(mp & 0xFFu);
       am[rt][1] = -dmin * static_cast<float>((mp >> 8) & 0xFFu);
     }
-    lds_fence();
+    mmq_lds_fence();
 
     float accd[RT][CT][4], e[CT][2];
 #pragma unroll
@@ -146,7 +180,7 @@ __global__ void __launch_bounds__(NW * kWave, 8 / NW) mmq_q4k_kernel(MmqArgs a) 
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         w[rt] = *reinterpret_cast<const u32x2*>(&lds.a[rt][r16][16 + 32 * c + 8 * q]);
-        scw[rt] = *reinterpret_cast<const u32x2*>(&lds.sc[rt][c][4 * q][0]);
+        scw[rt] = *reinterpret_cast<const u32x2*>(&lds.x.sc[rt][c][4 * q][0]);
       }
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -166,12 +200,7 @@ __global__ void __launch_bounds__(NW * kWave, 8 / NW) mmq_q4k_kernel(MmqArgs a) 
         float d8[CT];
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
-          const uint8_t* blk = &lds.b[ct][r16][36 * t];
-          // codes 8q..8q+7 of the block: two dword reads (the block is
-          // 36 bytes, so the pair is 8-byte aligned only in odd blocks)
-          const uint32_t* cw = reinterpret_cast<const uint32_t*>(blk + 4 + 8 * q);
-          const long B = pack2(cw[0], cw[1]);
-          d8[ct] = h2f(*reinterpret_cast<const uint16_t*>(blk));
+          const long B = b_operand<CT>(lds.b, ct, r16, q, t, d8[ct]);
           const v4i zero = {0, 0, 0, 0};
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) C[rt][ct] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A[rt], B, zero, 0, 0, 0);
@@ -191,7 +220,7 @@ __global__ void __launch_bounds__(NW * kWave, 8 / NW) mmq_q4k_kernel(MmqArgs a) 
     }
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      const float4 dv = *reinterpret_cast<const float4*>(&lds.d[rt][4 * q]);
+      const float4 dv = *reinterpret_cast<const float4*>(&lds.x.d[rt][4 * q]);
       const float dd[4] = {dv.x, dv.y, dv.z, dv.w};
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
@@ -204,25 +233,225 @@ __global__ void __launch_bounds__(NW * kWave, 8 / NW) mmq_q4k_kernel(MmqArgs a) 
         for (int i = 0; i < 4; ++i) acc[rt][ct][i] = v[i];
       }
     }
+  }
+};
+
+// Q4_0 and Q8_0: one fp16 scale per 32-weight block t (block at byte BB*t of
+// the step, codes 2 bytes in). Lane (r16, q) converts the scales of blocks
+// 2q and 2q+1 of row r16 for the D layout. Q4_0: byte j of the codes holds
+// element j (low nibble) and j + 16 (high), so k-slice q reads bytes
+// 8*(q&1) .. +7 and takes nibble q>>1; codes 0..15 with the -8 offset taken
+// from the q8_1 block's s (its fp16 d8*sum(q)), as in the mat-vec. Q8_0:
+// k-slice q reads code bytes 8q .. 8q+7 as they are.
+template <class F, int BB, bool NIBBLES>
+struct MmqStepBlocks {
+  template <int RT, int CT>
+  __device__ static void run(MmqWaveLds<F, RT, CT>& lds, const MmqRows&, int, int lane, float (&acc)[RT][CT][4]) {
+    const int r16 = lane & 15, q = lane >> 4;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int t = 2 * q + h;
+        lds.x.d[rt][t][r16] = h2f(*reinterpret_cast<const uint16_t*>(&lds.a[rt][r16][BB * t]));
+      }
+    mmq_lds_fence();
+    const int nib = 4 * (q >> 1);
+    static_for<0, 8>([&](auto tc) QMV_INLINE {
+      constexpr int t = decltype(tc)::value;
+      // code bytes of this lane in block t: 2-byte aligned, misaligned by a
+      // compile-time 0 or 2 bytes from a dword (BB even; 8*(q&1) and 8q are
+      // multiples of 4)
+      constexpr int kMis = (BB * t + 2) % 4;
+      long A[RT];
+      float dw[RT][4];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const uint8_t* p = &lds.a[rt][r16][BB * t + 2 + (NIBBLES ? 8 * (q & 1) : 8 * q)];
+        const long raw = lds8<kMis>(p);
+        if constexpr (NIBBLES) {
+          const uint32_t lo = static_cast<uint32_t>(raw), hi = static_cast<uint32_t>(static_cast<uint64_t>(raw) >> 32);
+          A[rt] = pack2((lo >> nib) & 0x0F0F0F0Fu, (hi >> nib) & 0x0F0F0F0Fu);
+        } else {
+          A[rt] = raw;
+        }
+        const float4 dv = *reinterpret_cast<const float4*>(&lds.x.d[rt][t][4 * q]);
+        dw[rt][0] = dv.x; dw[rt][1] = dv.y; dw[rt][2] = dv.z; dw[rt][3] = dv.w;
+      }
+      v4i C[RT][CT];
+      float d8[CT], m8s[CT];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const long B = b_operand<CT>(lds.b, ct, r16, q, t, d8[ct]);
+        const v4i zero = {0, 0, 0, 0};
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) C[rt][ct] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A[rt], B, zero, 0, 0, 0);
+        m8s[ct] = 0.0f;
+        if constexpr (NIBBLES) m8s[ct] = -8.0f * h2f(*reinterpret_cast<const uint16_t*>(&lds.b[ct][r16][36 * t + 2]));
+      }
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[rt][ct][i] = fmaf(fmaf(static_cast<float>(C[rt][ct][i]), d8[ct], m8s[ct]), dw[rt][i], acc[rt][ct][i]);
+    });
+  }
+};
+template <> struct MmqStep<Q40> : MmqStepBlocks<Q40, 18, true> {};
+template <> struct MmqStep<Q80> : MmqStepBlocks<Q80, 34, false> {};
+
+// Q6_K super-block at image byte base = 16 - delta of each row (delta per
+// row and step): ql[128] @0, qh[64] @128, int8 sc[16] @192, fp16 d @208.
+// Element e = 128h + 32g + l of block t = 4h + g: low 4 bits in ql[64h +
+// 32(g%2) + l] (nibble g/2), high 2 bits at bit 2g of qh[32h + l]. Lane
+// (r16, q) copies the scales of sub-blocks 4q..4q+3 of row r16 (and q = 0
+// its d) for the D layout.
+template <> struct MmqStep<Q6K> {
+  template <int RT, int CT>
+  __device__ static void run(MmqWaveLds<Q6K, RT, CT>& lds, const MmqRows& rows, int sb, int lane,
+                             float (&acc)[RT][CT][4]) {
+    const int r16 = lane & 15, q = lane >> 4;
+    int base[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      base[rt] = MmqGeom<Q6K>::image_base(rows.row_off(rt, r16), sb);
+      const uint8_t* img = &lds.a[rt][r16][base[rt]];
+      const u32x2 s4 = lds8_rt(img + 192 + 4 * q, base[rt] & 2);   // scales 4q..4q+3 (and 4 more)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) lds.x.sc[rt][4 * q + k][r16] = static_cast<int8_t>((s4.x >> (8 * k)) & 0xFFu);
+      if (q == 0) lds.x.d[rt][r16] = h2f(*reinterpret_cast<const uint16_t*>(img + 208));
+    }
+    mmq_lds_fence();
+    const long ones = 0x0101010101010101l;
+    float accd[RT][CT][4];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) accd[rt][ct][i] = 0.0f;
+#pragma unroll 2
+    for (int t = 0; t < 8; ++t) {
+      const int h = t >> 2, g = t & 3;
+      long A[RT];
+      int sc[RT][2][4];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const uint8_t* img = &lds.a[rt][r16][base[rt]];
+        const int mis = base[rt] & 2;
+        const u32x2 ql = lds8_rt(img + 64 * h + 32 * (g & 1) + 8 * q, mis);
+        const u32x2 qh = lds8_rt(img + 128 + 32 * h + 8 * q, mis);
+        const int ns = 4 * (g >> 1), hs = 2 * g;
+        A[rt] = pack2(((ql.x >> ns) & 0x0F0F0F0Fu) | (((qh.x >> hs) & 0x03030303u) << 4),
+                      ((ql.y >> ns) & 0x0F0F0F0Fu) | (((qh.y >> hs) & 0x03030303u) << 4));
+        const uint32_t s0 = *reinterpret_cast<const uint32_t*>(&lds.x.sc[rt][2 * t][4 * q]);
+        const uint32_t s1 = *reinterpret_cast<const uint32_t*>(&lds.x.sc[rt][2 * t + 1][4 * q]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sc[rt][0][i] = sbfe(s0, 8 * i, 8);
+          sc[rt][1][i] = sbfe(s1, 8 * i, 8);
+        }
+      }
+      // the sub-block halves of block t: k-slices 0, 1 (lanes q < 2) and 2, 3
+      const bool lo_half = q < 2;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        float d8;
+        const long B = b_operand<CT>(lds.b, ct, r16, q, t, d8);
+        const long Blo = lo_half ? B : 0l, Bhi = lo_half ? 0l : B;
+        const v4i zero = {0, 0, 0, 0};
+        const int S32lo = 32 * __builtin_amdgcn_mfma_i32_16x16x32_i8(ones, Blo, zero, 0, 0, 0)[0];
+        const int S32hi = 32 * __builtin_amdgcn_mfma_i32_16x16x32_i8(ones, Bhi, zero, 0, 0, 0)[0];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const v4i Clo = __builtin_amdgcn_mfma_i32_16x16x32_i8(A[rt], Blo, zero, 0, 0, 0);
+          const v4i Chi = __builtin_amdgcn_mfma_i32_16x16x32_i8(A[rt], Bhi, zero, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int v = mul24(sc[rt][0][i], Clo[i] - S32lo) + mul24(sc[rt][1][i], Chi[i] - S32hi);
+            accd[rt][ct][i] = fmaf(static_cast<float>(v), d8, accd[rt][ct][i]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const float4 dv = *reinterpret_cast<const float4*>(&lds.x.d[rt][4 * q]);
+      const float dd[4] = {dv.x, dv.y, dv.z, dv.w};
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[rt][ct][i] = fmaf(dd[i], accd[rt][ct][i], acc[rt][ct][i]);
+    }
+  }
+};
+
+template <class F, int RT, int CT, int NW>
+__global__ void __launch_bounds__(NW * kWave, 8 / NW) mmq_kernel(MmqArgs a) {
+  using Gm = MmqGeom<F>;
+  const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+  const int r16 = lane & 15, q = lane >> 4;
+  int64_t bx;
+  int by;
+  mmq_tile_of(blockIdx.x, a.gx, a.gy, bx, by);
+  const int64_t row_base = bx * (16 * RT);
+  const int col_base = by * (16 * CT);
+  const int sb0 = mmq_sb_begin(a.nsb, wave, NW), sb1 = mmq_sb_begin(a.nsb, wave + 1, NW);
+  const MmqRows rows{row_base * a.row_bytes, row_base, a.M, a.row_bytes};
+
+  // the staging tiles of the NW waves; after the K loop the same LDS holds
+  // the partial sums of the reduction
+  constexpr int NV = RT * CT * 4;
+  __shared__ __align__(16) uint8_t smem[mmq_lds_bytes<F, RT, CT, NW>()];
+  MmqWaveLds<F, RT, CT>& lds = reinterpret_cast<MmqWaveLds<F, RT, CT>*>(smem)[wave];
+  float acc[RT][CT][4];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[rt][ct][i] = 0.0f;
+
+  MmqOffsets<F, RT, CT> off;
+  // staged loads -> LDS: A loads into their rows' images, B piece k at byte
+  // 16k of the B tiles
+  auto store_stage = [&](const MmqStage<F, RT, CT>& st, int sb) QMV_INLINE {
+    uint8_t* la = &lds.a[0][0][0];
+    uint8_t* lb = &lds.b[0][0][0];
+#pragma unroll
+    for (int j = 0; j < mmq_a_slots<F, RT>(); ++j) {
+      if (lane + kWave * j < mmq_a_pieces<F>() * RT) {
+        uint8_t* dst = la + off.arow[j] * Gm::kRowLds + Gm::piece_lds(rows.tile_off + off.a[j], sb, off.apc[j]);
+        if (Gm::piece_short(off.apc[j])) *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(st.a[j].x);
+        else *reinterpret_cast<u32x4*>(dst) = st.a[j];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < mmq_b_slots<CT>(); ++j) {
+      const int k = lane + kWave * j;
+      if (k < kMmqBPieces * CT) *reinterpret_cast<u32x4*>(lb + 16 * k) = st.b[j];
+    }
   };
 
-  // Pipeline: the staging loads of super-block sb+1 are in flight while sb
-  // is computed from LDS. The prefetch is unconditional (past the end it
-  // re-reads the last super-block, from cache) so every path has the same
-  // loads in flight.
+  // Pipeline: the staging loads of step sb+1 are in flight while sb is
+  // computed from LDS. The prefetch is unconditional (past the end it
+  // re-reads the last step, from cache) so every path has the same loads in
+  // flight.
   if (sb0 < sb1) {
-    MmqOffsets<RT, CT> off;
-    mmq_offsets<RT, CT>(a, row_base, col_base, lane, off);
-    MmqStage<RT, CT> st;
-    mmq_stage_load<RT, CT>(a, row_base, col_base, lane, sb0, off, st);
+    mmq_offsets<F, RT, CT>(a, row_base, col_base, lane, off);
+    MmqStage<F, RT, CT> st;
+    mmq_stage_load<F, RT, CT>(a, row_base, col_base, lane, sb0, off, st);
     for (int sb = sb0; sb < sb1; ++sb) {
-      lds_fence();                 // the previous super-block's reads are done
-      store_stage(st);
+      mmq_lds_fence();             // the previous step's reads are done
+      store_stage(st, sb);
       const int next = sb + 1 < sb1 ? sb + 1 : sb;
-      mmq_stage_load<RT, CT>(a, row_base, col_base, lane, next, off, st);
+      mmq_stage_load<F, RT, CT>(a, row_base, col_base, lane, next, off, st);
       __builtin_amdgcn_sched_barrier(0);
-      lds_fence();
-      compute();
+      mmq_lds_fence();
+      MmqStep<F>::template run<RT, CT>(lds, rows, sb, lane, acc);
     }
   }
 

@@ -1,7 +1,7 @@
 // mmq_plan.hpp - addressing of the many-column (MFMA) kernel: argument
-// block, K split, operand pointers and the loads of one super-block. Pure
-// pointer arithmetic and loads, shared by the kernel and the host model of
-// its memory accesses.
+// block, workgroup-to-tile mapping, K split, operand pointers and the loads
+// of one staging step. Pure pointer arithmetic and loads, shared by the
+// kernel and the host model of its memory accesses.
 #pragma once
 
 #include "common.hpp"
@@ -19,53 +19,124 @@ struct MmqArgs {
   int64_t row_bytes;
   int64_t ycol_bytes;
   int n;                     // columns
-  int nsb;                   // super-blocks per row
+  int nsb;                   // staging steps per row (256 weights each)
+  int gx, gy;                // row tiles and column tiles of the grid
 };
 
-// First super-block of wave w's share of the K range when nw waves split it
-// (w = 0..nw).
+// Staging geometry of a weight format: a staging step covers 256 weights of
+// a row (the 8 q8_1 blocks of one step of the activation), kStride bytes of
+// the row, staged with kRowPieces loads per row into a kRowLds-byte row
+// image in LDS. Formats whose steps are 16-byte multiples (Q4_K 144, Q4_0
+// 8 x 18 = 144, Q8_0 8 x 34 = 272 bytes) stage them as 16-byte pieces at
+// 16-byte aligned addresses; step byte y sits at image byte y.
+template <class F> struct MmqGeom;
+template <int STRIDE>
+struct MmqGeomAligned {
+  static constexpr int kStride = STRIDE, kRowPieces = STRIDE / 16, kRowLds = STRIDE;
+  __host__ __device__ static int image_base(int64_t, int) { return 0; }
+  __host__ __device__ static int piece_lds(int64_t, int, int pc) { return 16 * pc; }
+  __host__ __device__ static bool piece_short(int) { return false; }
+  __host__ __device__ static int64_t piece_src(int64_t row_off, int sb, int pc) {
+    return row_off + static_cast<int64_t>(sb) * STRIDE + 16 * pc;
+  }
+};
+template <> struct MmqGeom<Q4K> : MmqGeomAligned<144> {};
+template <> struct MmqGeom<Q40> : MmqGeomAligned<144> {};
+template <> struct MmqGeom<Q80> : MmqGeomAligned<272> {};
+// Q6_K super-blocks (210 bytes) are only 2-byte aligned. As in the row
+// kernels every load stays inside its super-block: 13 sixteen-byte runs at
+// the first dword-aligned byte s' = s + delta (delta = 0 or 2) plus the one
+// 16-bit word the runs miss (the last one when delta = 0, the first one when
+// delta = 2). The image keeps 16 bytes of headroom so the runs land 16-byte
+// aligned: super-block byte y sits at image byte 16 + y - delta.
+template <> struct MmqGeom<Q6K> {
+  static constexpr int kStride = 210, kRowPieces = 14, kRowLds = 240;
+  __host__ __device__ static int delta(int64_t row_off, int sb) {
+    return static_cast<int>((row_off + static_cast<int64_t>(sb) * 210) & 2);
+  }
+  __host__ __device__ static int image_base(int64_t row_off, int sb) { return 16 - delta(row_off, sb); }
+  __host__ __device__ static bool piece_short(int pc) { return pc == 13; }
+  __host__ __device__ static int piece_lds(int64_t row_off, int sb, int pc) {
+    return pc < 13 ? 16 + 16 * pc : (delta(row_off, sb) ? 14 : 224);
+  }
+  __host__ __device__ static int64_t piece_src(int64_t row_off, int sb, int pc) {
+    const int64_t s = row_off + static_cast<int64_t>(sb) * 210;
+    const int d = delta(row_off, sb);
+    return pc < 13 ? s + d + 16 * pc : (d ? s : s + 208);
+  }
+};
+
+// Workgroup w -> tile (bx: row tile, by: column tile). Workgroups go to the
+// 8 XCDs round-robin (w mod 8), and each XCD has its own L2; the mapping
+// gives each XCD a contiguous range of tiles in row-tile-major order, so the
+// column tiles of one row tile run on the same XCD one after another and
+// re-read the row tile's weights from that L2 rather than from HBM. A
+// bijection of [0, gx*gy) for any grid size.
+constexpr int kXcds = 8;
+__host__ __device__ __forceinline__ void mmq_tile_of(int64_t w, int gx, int gy, int64_t& bx, int& by) {
+  const int64_t N = static_cast<int64_t>(gx) * gy;
+  const int64_t x = w % kXcds, j = w / kXcds;
+  const int64_t per = N / kXcds, extra = N % kXcds;
+  const int64_t t = x * per + (x < extra ? x : extra) + j;
+  bx = t / gy;
+  by = static_cast<int>(t - bx * gy);
+}
+
+// First staging step of wave w's share of the K range when nw waves split
+// it (w = 0..nw).
 __host__ __device__ __forceinline__ int mmq_sb_begin(int nsb, int w, int nw) { return (nsb * w) / nw; }
 
-// Staging loads of super-block sb: every load is a 16-byte piece of a
-// contiguous run, so a wave's loads cover whole cache lines. A: the 16 rows'
-// 144-byte super-blocks of each row tile, 144 pieces per tile (row tile
-// k / 144, row (k % 144) / 9); B: the 16 columns' 8 q8_1 blocks of each column
-// tile, a 288-byte run per column, 288 pieces per tile (column tile k / 288,
-// column (k % 288) / 18). Lane L takes pieces L, L + 64, ...; pieces past the
-// end are not loaded. Piece k lands at byte 16k of the wave's A or B tiles in
-// LDS, which the kernel reads the MFMA operands from.
-constexpr int kMmqAPieces = 144, kMmqBPieces = 288;
-template <int RT>
-constexpr int mmq_a_slots() { return (kMmqAPieces * RT + kWave - 1) / kWave; }
+// Staging loads of step sb: every load is a 16-byte piece of a contiguous
+// run (or Q6_K's one 16-bit word per row), so a wave's loads cover whole
+// cache lines. A: kRowPieces loads of each of the 16 rows of each row tile
+// (row tile k / (16*kRowPieces), row (k % (16*kRowPieces)) / kRowPieces);
+// B: the 16 columns' 8 q8_1 blocks of each column tile, a 288-byte run per
+// column, 288 pieces per tile (column tile k / 288, column (k % 288) / 18).
+// Lane L takes loads L, L + 64, ...; loads past the end are not issued.
+// A piece lands in its row's image in LDS (piece_lds), B piece k at byte 16k
+// of the B tiles.
+constexpr int kMmqBPieces = 288;
+template <class F>
+constexpr int mmq_a_pieces() { return 16 * MmqGeom<F>::kRowPieces; }
+template <class F, int RT>
+constexpr int mmq_a_slots() { return (mmq_a_pieces<F>() * RT + kWave - 1) / kWave; }
 template <int CT>
 constexpr int mmq_b_slots() { return (kMmqBPieces * CT + kWave - 1) / kWave; }
 
-template <int RT, int CT>
+template <class F, int RT, int CT>
 struct MmqStage {
-  u32x4 a[mmq_a_slots<RT>()];
+  u32x4 a[mmq_a_slots<F, RT>()];
   u32x4 b[mmq_b_slots<CT>()];
 };
 
-// Piece offsets of a lane, fixed for the whole K range: the byte offset of
-// each piece from the tile's first row (A) or first column (B) at super-block
-// 0. Rows past M - 1 and columns past n - 1 are clamped to the last one
-// (they are read and computed, never stored; each output column depends only
-// on its own). Offsets are 32-bit: a tile spans at most 32 rows or columns.
-template <int RT, int CT>
+// Load slots of a lane, fixed for the whole K range: for A the byte offset
+// of the slot's row from the tile's first row, its row within the tile
+// (0..16*RT-1) and its piece within the row; for B the offset of the piece
+// from the tile's first column. Rows past M - 1 and columns past n - 1 are
+// clamped to the last one (they are read and computed, never stored; each
+// output depends only on its own row and column). Offsets are 32-bit: a
+// tile spans at most 32 rows or columns.
+template <class F, int RT, int CT>
 struct MmqOffsets {
-  uint32_t a[mmq_a_slots<RT>()];
+  uint32_t a[mmq_a_slots<F, RT>()];
+  uint8_t arow[mmq_a_slots<F, RT>()];
+  uint8_t apc[mmq_a_slots<F, RT>()];
   uint32_t b[mmq_b_slots<CT>()];
 };
 
-template <int RT, int CT>
+template <class F, int RT, int CT>
 __host__ __device__ __forceinline__ void mmq_offsets(const MmqArgs& a, int64_t row_base, int col_base, int lane,
-                                                     MmqOffsets<RT, CT>& o) {
+                                                     MmqOffsets<F, RT, CT>& o) {
+  constexpr int RP = MmqGeom<F>::kRowPieces;
 #pragma unroll
-  for (int j = 0; j < mmq_a_slots<RT>(); ++j) {
-    const int k = lane + kWave * j, kk = k % kMmqAPieces;
-    int64_t r = row_base + 16 * (k / kMmqAPieces) + kk / 9;
+  for (int j = 0; j < mmq_a_slots<F, RT>(); ++j) {
+    const int k = lane + kWave * j;
+    const int row = k / RP < 16 * RT ? k / RP : 16 * RT - 1;     // slots past the end: any valid row
+    int64_t r = row_base + row;
     r = r < a.M ? r : a.M - 1;
-    o.a[j] = static_cast<uint32_t>((r - row_base) * a.row_bytes + 16 * (kk % 9));
+    o.a[j] = static_cast<uint32_t>((r - row_base) * a.row_bytes);
+    o.arow[j] = static_cast<uint8_t>(row);
+    o.apc[j] = static_cast<uint8_t>(k % RP);
   }
 #pragma unroll
   for (int j = 0; j < mmq_b_slots<CT>(); ++j) {
@@ -76,17 +147,23 @@ __host__ __device__ __forceinline__ void mmq_offsets(const MmqArgs& a, int64_t r
   }
 }
 
-// The staging loads of super-block sb: a wave-uniform base per operand plus
-// the lane's offsets; pieces past the end (k >= 144*RT or 288*CT) are not
-// loaded.
-template <int RT, int CT>
+// The staging loads of step sb; loads past the end (slot k >= the tile's
+// loads) are not issued.
+template <class F, int RT, int CT>
 __device__ __forceinline__ void mmq_stage_load(const MmqArgs& a, int64_t row_base, int col_base, int lane, int sb,
-                                               const MmqOffsets<RT, CT>& o, MmqStage<RT, CT>& st) {
-  const uint8_t* wb = a.W + (row_base * a.row_bytes + static_cast<int64_t>(sb) * 144);
+                                               const MmqOffsets<F, RT, CT>& o, MmqStage<F, RT, CT>& st) {
+  using Gm = MmqGeom<F>;
+  const int64_t tile_off = row_base * a.row_bytes;
   const uint8_t* yb = a.y + (static_cast<int64_t>(col_base) * a.ycol_bytes + static_cast<int64_t>(sb) * 288);
 #pragma unroll
-  for (int j = 0; j < mmq_a_slots<RT>(); ++j)
-    if (lane + kWave * j < kMmqAPieces * RT) st.a[j] = ld_a16_x4(wb + o.a[j]);
+  for (int j = 0; j < mmq_a_slots<F, RT>(); ++j) {
+    if (lane + kWave * j < mmq_a_pieces<F>() * RT) {
+      const uint8_t* src = a.W + Gm::piece_src(tile_off + o.a[j], sb, o.apc[j]);
+      if (Gm::piece_short(o.apc[j])) st.a[j].x = ld_u16(src);
+      else if constexpr (MmqGeom<F>::kStride % 16 == 0) st.a[j] = ld_a16_x4(src);
+      else st.a[j] = ld_x4(src);
+    }
+  }
 #pragma unroll
   for (int j = 0; j < mmq_b_slots<CT>(); ++j)
     if (lane + kWave * j < kMmqBPieces * CT) st.b[j] = ld_a16_x4(yb + o.b[j]);

@@ -222,46 +222,93 @@ static void case_block_dots(const char* name, int64_t M, int64_t K, int nc) {
   free(y);
 }
 
-// many-column (MFMA) kernel, Q4_K: every load of every lane, wave and
-// super-block; every output stored exactly once.
-template <int RT, int CT, int NW>
-static void case_mmq(int64_t M, int64_t K, int n) {
-  const int64_t row_bytes = K / 256 * 144, ycol = K / 32 * kQ8Bytes;
+// many-column (MFMA) kernel: every load of every lane, wave and step, in
+// the workgroup-to-tile mapping the kernel uses; every output stored exactly
+// once; every A load lands inside its row's LDS image (and the bytes the
+// step's arithmetic reads are covered by loads of that step).
+template <class F, int RT, int CT, int NW>
+static void case_mmq(const char* name, int64_t M, int64_t K, int n) {
+  using Gm = MmqGeom<F>;
+  const int64_t row_bytes = K / F::kQK * F::kBlockBytes, ycol = K / 32 * kQ8Bytes;
   uint8_t* W = alloc16(M * row_bytes);
   uint8_t* y = alloc16(n * ycol);
   begin({{W, W + M * row_bytes}, {y, y + n * ycol}});
   MmqArgs a{};
   a.W = W; a.y = y; a.M = M; a.row_bytes = row_bytes; a.ycol_bytes = ycol; a.n = n;
   a.nsb = static_cast<int>(K / 256);
-  const int64_t gx = (M + 16 * RT - 1) / (16 * RT);
-  const int gy = (n + 16 * CT - 1) / (16 * CT);
+  a.gx = static_cast<int>((M + 16 * RT - 1) / (16 * RT));
+  a.gy = (n + 16 * CT - 1) / (16 * CT);
+  const int64_t groups = static_cast<int64_t>(a.gx) * a.gy;
   std::vector<int> stores(M * n, 0);
+  std::vector<int> tiles(groups, 0);
   bool ok = true;
-  for (int64_t bx = 0; bx < gx; ++bx)
-    for (int by = 0; by < gy; ++by)
-      for (int wave = 0; wave < NW; ++wave)
+  for (int64_t w = 0; w < groups && ok; ++w) {
+    int64_t bx;
+    int by;
+    mmq_tile_of(w, a.gx, a.gy, bx, by);
+    if (bx < 0 || bx >= a.gx || by < 0 || by >= a.gy) { ok = false; break; }
+    tiles[bx * a.gy + by] += 1;
+    const int64_t row_base = bx * 16 * RT;
+    const int col_base = by * 16 * CT;
+    for (int wave = 0; wave < NW; ++wave) {
+      const int sb0 = mmq_sb_begin(a.nsb, wave, NW), sb1 = mmq_sb_begin(a.nsb, wave + 1, NW);
+      for (int sb = sb0; sb < sb1; ++sb) {
+        // bytes of each row image the step's loads write
+        std::vector<std::vector<char>> img(16 * RT, std::vector<char>(Gm::kRowLds, 0));
         for (int lane = 0; lane < 64; ++lane) {
-          const int r16 = lane & 15, q = lane >> 4;
-          const int64_t row_base = bx * 16 * RT;
-          const int col_base = by * 16 * CT;
-          MmqOffsets<RT, CT> off;
-          mmq_offsets<RT, CT>(a, row_base, col_base, lane, off);
-          MmqStage<RT, CT> st;
-          const int sb0 = mmq_sb_begin(a.nsb, wave, NW), sb1 = mmq_sb_begin(a.nsb, wave + 1, NW);
-          if (sb0 < sb1) mmq_stage_load<RT, CT>(a, row_base, col_base, lane, sb0, off, st);
-          for (int sb = sb0; sb < sb1; ++sb)
-            mmq_stage_load<RT, CT>(a, row_base, col_base, lane, sb + 1 < sb1 ? sb + 1 : sb, off, st);
-          for (int v = wave; v < RT * CT * 4; v += NW) {
-            int64_t r;
-            int c;
-            mmq_store_pos<RT, CT>(v, q, r16, row_base, col_base, r, c);
-            if (r < M && c < n) stores[c * M + r] += 1;
+          MmqOffsets<F, RT, CT> off;
+          mmq_offsets<F, RT, CT>(a, row_base, col_base, lane, off);
+          MmqStage<F, RT, CT> st;
+          mmq_stage_load<F, RT, CT>(a, row_base, col_base, lane, sb, off, st);
+          for (int j = 0; j < mmq_a_slots<F, RT>(); ++j) {
+            if (lane + kWave * j >= mmq_a_pieces<F>() * RT) continue;
+            const int64_t ro = row_base * row_bytes + off.a[j];
+            const int at = Gm::piece_lds(ro, sb, off.apc[j]);
+            const int len = Gm::piece_short(off.apc[j]) ? 2 : 16;
+            if (at < 0 || at + len > Gm::kRowLds || off.arow[j] >= 16 * RT) { ok = false; continue; }
+            // the LDS image byte holds the super-block byte the kernel
+            // expects there: source offset - image base = step byte
+            const int64_t src = Gm::piece_src(ro, sb, off.apc[j]);
+            const int64_t step0 = ro + static_cast<int64_t>(sb) * Gm::kStride;
+            if (src - step0 != at - Gm::image_base(ro, sb)) ok = false;
+            for (int b = 0; b < len; ++b) img[off.arow[j]][at + b] += 1;
           }
         }
+        // every byte of every row's step is written exactly once
+        for (int r = 0; r < 16 * RT && ok; ++r) {
+          int64_t rr = row_base + r;
+          rr = rr < M ? rr : M - 1;
+          const int base = Gm::image_base((rr - row_base) * row_bytes + row_base * row_bytes, sb);
+          const int step_bytes = static_cast<int>(K / F::kQK * F::kBlockBytes / a.nsb);
+          for (int b = 0; b < step_bytes && ok; ++b) ok = img[r][base + b] == 1;
+        }
+      }
+      for (int lane = 0; lane < 64; ++lane) {
+        const int r16 = lane & 15, q = lane >> 4;
+        for (int v = wave; v < RT * CT * 4; v += NW) {
+          int64_t r;
+          int c;
+          mmq_store_pos<RT, CT>(v, q, r16, row_base, col_base, r, c);
+          if (r < M && c < n) stores[c * M + r] += 1;
+        }
+      }
+    }
+  }
+  for (int64_t i = 0; i < groups && ok; ++i) ok = tiles[i] == 1;
   for (int64_t i = 0; i < M * n && ok; ++i) ok = stores[i] == 1;
-  report("mmq", ok, "q4_k", M, K, n, 1);
+  report("mmq", ok, name, M, K, n, 1);
   free(W);
   free(y);
+}
+
+template <class F>
+static void case_mmq_all(const char* name, int64_t M, int64_t K, int n) {
+  case_mmq<F, 2, 2, 4>(name, M, K, n);
+  case_mmq<F, 2, 2, 8>(name, M, K, n);
+  case_mmq<F, 2, 1, 4>(name, M, K, n);
+  case_mmq<F, 2, 1, 8>(name, M, K, n);
+  case_mmq<F, 1, 1, 4>(name, M, K, n);
+  case_mmq<F, 1, 1, 8>(name, M, K, n);
 }
 
 // quantizer: 8 lanes per q8_1 block, 4 floats each (clamped to block 0 when
@@ -376,6 +423,13 @@ int main(int argc, char** argv) {
         case_id<Q80>("q8_0", 5, 16416, 2, T, g, xpad);
       }
   }
+  // many-column kernel, a few shapes of every format (the full set below)
+  for (int n : {9, 33}) {
+    case_mmq_all<Q4K>("q4_k", 17, 512, n);
+    case_mmq_all<Q6K>("q6_k", 33, 768, n);
+    case_mmq_all<Q40>("q4_0", 17, 1280, n);
+    case_mmq_all<Q80>("q8_0", 33, 512, n);
+  }
   if (small) {
     printf("host model: %d failing case(s)\n", failures);
     return failures ? 1 : 0;
@@ -397,16 +451,15 @@ int main(int argc, char** argv) {
       }
   for (int64_t M : {1, 15, 16, 17, 33, 100})
     for (int64_t K : {256, 512, 768, 1024, 1280})
-      for (int n : {6, 7, 8, 9, 16, 17, 31, 32, 33, 64, 100}) {
-        case_mmq<2, 2, 4>(M, K, n);
-        case_mmq<2, 2, 8>(M, K, n);
-        case_mmq<2, 1, 4>(M, K, n);
-        case_mmq<2, 1, 8>(M, K, n);
-        case_mmq<1, 1, 4>(M, K, n);
-        case_mmq<1, 1, 8>(M, K, n);
+      for (int n : {6, 9, 16, 17, 33, 100}) {
+        case_mmq_all<Q4K>("q4_k", M, K, n);
+        case_mmq_all<Q6K>("q6_k", M, K, n);
+        case_mmq_all<Q40>("q4_0", M, K, n);
+        case_mmq_all<Q80>("q8_0", M, K, n);
       }
-  case_mmq<2, 2, 4>(300, 4096, 256);
-  case_mmq<1, 1, 8>(300, 4096, 256);
+  case_mmq<Q4K, 2, 2, 4>("q4_k", 300, 4096, 256);
+  case_mmq<Q6K, 1, 1, 8>("q6_k", 300, 4096, 256);
+  case_mmq<Q80, 2, 2, 8>("q8_0", 300, 4096, 256);
   for (int64_t K : {32, 64, 96, 1024, 14336})
     for (int64_t n : {1, 3, 8})
       for (int64_t pad : {0, 1, 3, 64}) case_quantize(K, n, K + pad);
@@ -436,10 +489,12 @@ int main(int argc, char** argv) {
     case_id<Q4K>("q4_k", 14336, 4096, 8, 8, 2);
     case_id<Q4K2>("q4_k2", 14336, 4096, 8, 8, 2);
     case_id<Q4K2>("q4_k2", 14336, 4096, 8, 8, 2, 0);
-    case_mmq<2, 2, 4>(4096, 14336, 64);
-    case_mmq<2, 1, 8>(4096, 14336, 16);
-    case_mmq<1, 1, 8>(4096, 14336, 16);
-    case_mmq<2, 2, 8>(14336, 4096, 32);
+    case_mmq<Q4K, 2, 2, 4>("q4_k", 4096, 14336, 64);
+    case_mmq<Q4K, 2, 1, 8>("q4_k", 4096, 14336, 16);
+    case_mmq<Q4K, 1, 1, 8>("q4_k", 4096, 14336, 16);
+    case_mmq<Q4K, 2, 2, 8>("q4_k", 14336, 4096, 32);
+    case_mmq<Q6K, 2, 2, 4>("q6_k", 4096, 4096, 64);
+    case_mmq<Q6K, 2, 1, 8>("q6_k", 2048, 4096, 16);
     case_id<Q4K>("q4_k", 14336, 4096, 8, 8, 1);
     case_id<Q4K2>("q4_k2", 14336, 4096, 8, 8, 1);
   }

@@ -59,8 +59,9 @@ P16, P4 = 1 << 20, (1 << 20) + 4
     ((P16, B.Q4_K, 0, 256, P16, 1, P16), B.ERR_SHAPE),
     ((P16, B.Q4_K, 1, 256, P16, 0, P16), B.ERR_SHAPE),
     ((P16, B.Q4_K, 1, 256, P16, 257, P16), B.ERR_SHAPE),
-    ((P16, B.Q4_0, 1, 256, P16, 9, P16), B.ERR_SHAPE),
-    ((P16, B.Q6_K, 1, 256, P16, 9, P16), B.ERR_SHAPE),
+    ((P16, B.Q4_0, 1, 256, P16, 257, P16), B.ERR_SHAPE),
+    ((P16, B.Q6_K, 1, 256, P16, 257, P16), B.ERR_SHAPE),
+    ((P16, B.Q4_0, 1, 96, P16, 257, P16), B.ERR_SHAPE),
     ((P16, B.Q4_K, 1, 256 * ((1 << 22) + 1), P16, 1, P16), B.ERR_SHAPE),
     ((P16, B.Q6_K, 1, 256 * ((1 << 22) + 1), P16, 1, P16), B.ERR_SHAPE),
     # M * K above 2^40
@@ -106,7 +107,7 @@ def test_f32_entry_points_argument_checks(L):
     assert L.mmvq_f32(None, B.Q4_K, 1, 256, P16, 1, 256, P16, None) == B.ERR_NULL
     assert L.mmvq_f32(P16, B.Q8_1, 1, 256, P16, 1, 256, P16, None) == B.ERR_TYPE
     assert L.mmvq_f32(P16, B.Q4_K, 1, 256, P16, 1, 255, P16, None) == B.ERR_SHAPE
-    assert L.mmvq_f32(P16, B.Q4_K, 1, 256, P16, 9, 256, P16, None) == B.ERR_SHAPE
+    assert L.mmvq_f32(P16, B.Q4_K, 1, 256, P16, 257, 256, P16, None) == B.ERR_SHAPE
     K = 256 * ((1 << 22) + 1)
     assert L.mmvq_f32(P16, B.Q4_K, 1, K, P16, 1, K, P16, None) == B.ERR_SHAPE
     assert L.mmvq_f32(P16, B.Q4_K, 1, 256, P16 + 2, 1, 256, P16, None) == B.ERR_ALIGN

@@ -287,7 +287,7 @@ def test_f32_errors_on_device():
     p, q, o = W.data_ptr(), x.data_ptr(), out.data_ptr()
     assert L.mmvq_f32(p, Q4_K, 1, 256, q, 1, 255, o, s) == B.ERR_SHAPE
     assert L.mmvq_f32(p, Q4_K, 1, 256, q + 2, 1, 256, o, s) == B.ERR_ALIGN
-    assert L.mmvq_f32(p, Q4_K, 1, 256, q, 9, 256, o, s) == B.ERR_SHAPE
+    assert L.mmvq_f32(p, Q4_K, 1, 256, q, 257, 256, o, s) == B.ERR_SHAPE
     assert L.mmvq_f32(p + 8, Q4_K, 1, 256, q, 1, 256, o, s) == B.ERR_ALIGN
     # x needs only 4-byte alignment: a valid call (zero weights give 0)
     out.fill_(float("nan"))
