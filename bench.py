@@ -69,6 +69,9 @@ def parse():
     p.add_argument("--summarize-trace", metavar="TRACE_DIR",
                    help="write profiles/<workload>_n<n>_kernel_trace.md for --workload/--n (or --moe) "
                         "from a rocprofv3 --kernel-trace --stats run of the same arguments, and exit")
+    p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="write profiles/<workload>_n<n>_hbm_traffic.md for --workload/--n from two "
+                        "rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) with --copy-probe, and exit")
     p.add_argument("--summarize-sq", metavar="SQ_DIR",
                    help="write profiles/<workload>_n<n>_sq_counters.md for --workload/--n from a "
                         "rocprofv3 --pmc run of the SQ counters below, and exit")
@@ -80,15 +83,20 @@ def parse():
 # compile flags.
 HEADLINE_SOURCES = ["common.hpp", "q8.hpp", "formats.hpp", "plan.hpp", "mmvq_kernel.hpp", "launch.hpp",
                     "kernels_q4_k.hip", "kernels_q4_k_f32.hip", os.path.join("..", "..", "include", "mmvq.h")]
+# ... and of every measured kernel, for the per-configuration summaries
+ALL_SOURCES = HEADLINE_SOURCES + ["mmq_plan.hpp", "mmq_kernel.hpp", "kernels_mmq.hip", "kernels_q4_0.hip",
+                                  "kernels_q4_0_f32.hip", "kernels_q8_0.hip", "kernels_q8_0_f32.hip",
+                                  "kernels_q6_k.hip", "kernels_q6_k_f32.hip", "kernels_q4_k_id.hip",
+                                  "kernels_q4_k_f32_id.hip", "quantize.hip", "probe.hip", "api.hip"]
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(names=None) -> str:
     """sha256 over the sources and compile flags of the measured kernels:
     counters taken on one build are reported only while these are unchanged."""
     import hashlib
     from quantized_decode_gemv_quantize_amd import build as qbuild
     h = hashlib.sha256()
-    for name in HEADLINE_SOURCES:
+    for name in names or HEADLINE_SOURCES:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(os.path.basename(name).encode() + b"\0" + f.read())
     h.update(" ".join(qbuild.HIPCC_FLAGS).encode())
@@ -181,9 +189,60 @@ def summarize_trace(trace_dir: str, workload: str, n: int, moe: bool, steps: int
         for k, g in forms.items():
             f.write(f"- {labels.get(k, k)}: {g['launches']} launches, average {g['avg_us']} us, "
                     f"median {g['median_us']} us\n")
-        f.write("\n```json\n" + json.dumps({"profile": name, "source_sha256_16": kernel_source_hash(),
+        f.write("\n```json\n" + json.dumps({"profile": name, "source_sha256_16": kernel_source_hash(ALL_SOURCES),
                                             "forms": forms}, indent=1) + "\n```\n")
     print(json.dumps({"profile": name, "forms": forms}))
+
+
+def summarize_traffic(fetch_dir: str, write_dir: str, workload: str, n: int) -> None:
+    """profiles/<workload>_n<n>_hbm_traffic.md: HBM bytes per launch of each
+    benchmark form (median FETCH_SIZE and WRITE_SIZE over dispatches, scaled
+    by what the counters read for the 256 MiB calibration copy), against the
+    form's algorithmic bytes."""
+    import statistics
+    from quantized_decode_gemv_quantize_amd import synth
+    wl = synth.BY_NAME[workload]
+
+    def big_copy(d):
+        return max(float(r["Counter_Value"]) for r in _csv_rows(d, "*counter_collection.csv")
+                   if r["Kernel_Name"].startswith("__amd_rocclr_copyBuffer"))
+
+    def med(d, kind):
+        v = [float(r["Counter_Value"]) for r in _csv_rows(d, "*counter_collection.csv")
+             if kernel_form(r["Kernel_Name"]) == kind]
+        return (statistics.median(v), len(v)) if v else (None, 0)
+
+    fs, ws = COPY_BYTES / 1024 / big_copy(fetch_dir), COPY_BYTES / 1024 / big_copy(write_dir)
+    alg = {"fused": fused_bytes(wl, n), "gemv": algorithmic_bytes(wl, n), "probe": wl.weight_bytes,
+           "quantize": n * wl.K * 4 + n * (wl.K // 32) * 36}
+    forms = {}
+    for kind, a in alg.items():
+        fk, nf = med(fetch_dir, kind)
+        wk, nw = med(write_dir, kind)
+        if fk is None or wk is None:
+            continue
+        t = fk * 1024 * fs + wk * 1024 * ws
+        forms[kind] = {"fetch_kib_per_launch": fk, "write_kib_per_launch": wk, "dispatches": [nf, nw],
+                       "traffic_bytes_per_launch": int(t), "algorithmic_bytes_per_launch": a,
+                       "traffic_over_algorithmic": round(t / a, 4)}
+    name = f"{workload}_n{n}"
+    cmd = (f"cd /tmp && timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/fetch_{name} "
+           f"-o bench -- python3 <repo>/bench.py --cpu-seconds 0 --workload {workload} --n {n} --steps 50 "
+           f"--warmup 10 --copy-probe")
+    with open(os.path.join(PROFILES, f"{name}_hbm_traffic.md"), "w") as f:
+        f.write(f"# HBM traffic: {workload}, n={n}\n\nCommands (MI355X, one GPU):\n\n    {cmd}\n    "
+                f"{cmd.replace('FETCH_SIZE', 'WRITE_SIZE').replace('fetch_', 'write_')}\n\n")
+        f.write(f"Calibration: a 256 MiB device copy in the same process; FETCH_SIZE scale {fs:.4f}, "
+                f"WRITE_SIZE scale {ws:.4f}.\n\n| form | FETCH KiB | WRITE KiB | traffic MB | algorithmic MB | "
+                f"ratio |\n|---|---|---|---|---|---|\n")
+        for k, g in forms.items():
+            f.write(f"| {k} | {g['fetch_kib_per_launch']:.1f} | {g['write_kib_per_launch']:.1f} | "
+                    f"{g['traffic_bytes_per_launch'] / 1e6:.3f} | {g['algorithmic_bytes_per_launch'] / 1e6:.3f} | "
+                    f"{g['traffic_over_algorithmic']} |\n")
+        f.write("\n```json\n" + json.dumps({"workload": workload, "n": n, "source_sha256_16": kernel_source_hash(ALL_SOURCES),
+                                            "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
+                                            "forms": forms}, indent=1) + "\n```\n")
+    print(json.dumps({"workload": workload, "n": n, "forms": forms}))
 
 
 def summarize_sq(sq_dir: str, workload: str, n: int) -> None:
@@ -221,14 +280,15 @@ def summarize_sq(sq_dir: str, workload: str, n: int) -> None:
         f.write("| form | " + " | ".join(cols) + " |\n|" + "---|" * (len(cols) + 1) + "\n")
         for k, g in forms.items():
             f.write(f"| {k} | " + " | ".join(str(g.get(c, "")) for c in cols) + " |\n")
-        f.write("\n```json\n" + json.dumps({"workload": workload, "n": n, "source_sha256_16": kernel_source_hash(),
+        f.write("\n```json\n" + json.dumps({"workload": workload, "n": n, "source_sha256_16": kernel_source_hash(ALL_SOURCES),
                                             "forms": forms}, indent=1) + "\n```\n")
     print(json.dumps({"workload": workload, "n": n, "forms": forms}))
 
 
-def committed_figures(fname: str):
+def committed_figures(fname: str, names=None):
     """The JSON block of a profiles/ summary, or None when it is absent or
-    the kernel sources changed since it was taken."""
+    the kernel sources changed since it was taken (names: the sources its
+    hash covers; the per-configuration summaries cover every kernel)."""
     path = os.path.join(PROFILES, fname)
     if not os.path.exists(path):
         return None
@@ -236,7 +296,7 @@ def committed_figures(fname: str):
         fig = json.loads(open(path).read().split("```json", 1)[1].split("```", 1)[0])
     except (IndexError, ValueError):
         return None
-    return fig if fig.get("source_sha256_16") == kernel_source_hash() else None
+    return fig if fig.get("source_sha256_16") == kernel_source_hash(names) else None
 
 
 def summarize(trace_dir: str, fetch_dir: str, write_dir: str) -> None:
@@ -619,6 +679,9 @@ def main():
     if args.summarize_sq:
         summarize_sq(args.summarize_sq, args.workload, args.n)
         return
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic, args.workload, args.n)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               f"(the mat-vec shards by rows across GPUs, see DESIGN.md)", file=sys.stderr)
@@ -716,7 +779,7 @@ def main():
     # sources): where its vector instructions alone need longer than its
     # bytes at the HBM peak, the kernel is bound by instruction issue and the
     # roofline is reported against the vector issue peak.
-    sq = committed_figures(f"{wl.name}_n{n}_sq_counters.md")
+    sq = committed_figures(f"{wl.name}_n{n}_sq_counters.md", ALL_SOURCES)
     form = "fused" if fused else "gemv"
     if sq is not None and form in sq.get("forms", {}):
         valu = sq["forms"][form]["SQ_INSTS_VALU"]
