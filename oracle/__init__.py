@@ -23,9 +23,11 @@ SRC = os.path.join(HERE, "mmvq_oracle.c")
 LIB = os.path.join(HERE, "libmmvq_oracle.so")
 
 Q4_0, Q8_0, Q8_1, Q4_K, Q6_K = 2, 8, 9, 12, 14
+Q4_1, Q5_0, Q5_1, Q5_K = 3, 6, 7, 13
 GLU_PLAIN, GLU_SWIGLU, GLU_GEGLU, GLU_SWIGLU_OAI, GLU_SWIGLU_CLAMP = 0, 1, 2, 3, 4
-BLOCK = {Q4_0: (32, 18), Q8_0: (32, 34), Q4_K: (256, 144), Q6_K: (256, 210), Q8_1: (32, 36)}
-DOTS_PER_BLOCK = {Q4_0: 1, Q8_0: 1, Q4_K: 16, Q6_K: 16}
+BLOCK = {Q4_0: (32, 18), Q8_0: (32, 34), Q4_K: (256, 144), Q6_K: (256, 210), Q8_1: (32, 36),
+         Q4_1: (32, 20), Q5_0: (32, 22), Q5_1: (32, 24), Q5_K: (256, 176)}
+DOTS_PER_BLOCK = {Q4_0: 1, Q8_0: 1, Q4_K: 16, Q6_K: 16, Q4_1: 1, Q5_0: 1, Q5_1: 1, Q5_K: 16}
 
 _c_i64 = ctypes.c_int64
 _p = ctypes.c_void_p

@@ -78,8 +78,12 @@ int orc_type_info(int type, int *block_elems, int *block_bytes) {
     int e, b;
     switch (type) {
     case ORC_Q4_0: e = 32;  b = 18;  break;   /* half d + 16 bytes of nibbles      */
+    case ORC_Q4_1: e = 32;  b = 20;  break;   /* half d, half m + 16 bytes          */
+    case ORC_Q5_0: e = 32;  b = 22;  break;   /* half d, 4 bytes of 5th bits, 16    */
+    case ORC_Q5_1: e = 32;  b = 24;  break;   /* half d, half m, 4 + 16 bytes       */
     case ORC_Q8_0: e = 32;  b = 34;  break;   /* half d + 32 int8                   */
     case ORC_Q4_K: e = 256; b = 144; break;   /* half d, half dmin, 12 + 128 bytes  */
+    case ORC_Q5_K: e = 256; b = 176; break;   /* half d, half dmin, 12 + 32 + 128   */
     case ORC_Q6_K: e = 256; b = 210; break;   /* 128 + 64 + 16 + half d             */
     case ORC_Q8_1: e = 32;  b = 36;  break;   /* half d, half s, 32 int8            */
     default: return ORC_ERR_TYPE;
@@ -91,9 +95,9 @@ int orc_type_info(int type, int *block_elems, int *block_bytes) {
 
 int orc_dots_per_block(int type) {
     switch (type) {
-    case ORC_Q4_0: return 1;
+    case ORC_Q4_0: case ORC_Q4_1: case ORC_Q5_0: case ORC_Q5_1: return 1;
     case ORC_Q8_0: return 1;
-    case ORC_Q4_K: return 16;
+    case ORC_Q4_K: case ORC_Q5_K: return 16;
     case ORC_Q6_K: return 16;
     default: return ORC_ERR_TYPE;
     }
@@ -170,6 +174,23 @@ static int q4_0_code(const uint8_t *blk, int e) {
     return e < 16 ? (qs[e] & 0x0F) : (qs[e - 16] >> 4);
 }
 
+/* Q4_1, Q5_0, Q5_1 [MMVQ §权重的排法 (old-style blocks of 32 weights, Q5_1
+ * named among them); GGUF16 §16.1.1 (type ids 3, 6, 7)]. The pages name
+ * these formats without their layouts; the layouts here are readings of the
+ * published GGUF block definitions, field by field:
+ *   Q4_1: fp16 d @0, fp16 m @2, qs[16] @4; weight d*q + m.
+ *   Q5_0: fp16 d @0, qh (4 bytes, little-endian 32-bit word) @2, qs[16] @6;
+ *         weight d*(q - 16).
+ *   Q5_1: fp16 d @0, fp16 m @2, qh @4, qs[16] @8; weight d*q + m.
+ * Low 4 bits of element e as in Q4_0 (the low nibble of qs[e] for e < 16,
+ * the high nibble of qs[e - 16] above); the 5-bit formats take bit e of qh
+ * as bit 4 of the code. */
+static int nib_code(const uint8_t *qs, int e) { return e < 16 ? (qs[e] & 0x0F) : (qs[e - 16] >> 4); }
+static int qh_bit(const uint8_t *qh, int e) { return (qh[e / 8] >> (e % 8)) & 1; }
+static int q4_1_code(const uint8_t *blk, int e) { return nib_code(blk + 4, e); }
+static int q5_0_code(const uint8_t *blk, int e) { return nib_code(blk + 6, e) | (qh_bit(blk + 2, e) << 4); }
+static int q5_1_code(const uint8_t *blk, int e) { return nib_code(blk + 8, e) | (qh_bit(blk + 4, e) << 4); }
+
 /* Q8_0 [LLM §量化格式 (format table: 8-bit, 34 bytes per 32 weights);
  * MMVQ §权重的排法 (old-style blocks: one fp16 scale for 32 codes)]. The
  * pages give the size and the block shape, not the struct. Reading: fp16 d
@@ -233,6 +254,21 @@ static int q6_k_code(const uint8_t *blk, int e) {
 }
 static int q6_k_scale(const uint8_t *blk, int s) { return (int8_t)blk[192 + s]; }
 
+/* Q5_K [MMVQ §激活的量化 (named among the min-term formats); GGUF16
+ * §16.1.1 (type id 13)]. The pages name the format without its layout; the
+ * layout is a reading of the published GGUF block definition: fp16 d @0,
+ * fp16 dmin @2, the 12 packed scale/min bytes of Q4_K @4, qh[32] @16,
+ * qs[128] @48, 176 bytes. Element e of sub-block t = e/32 (l = e%32, chunk
+ * c = t/2): low 4 bits as in Q4_K (low or high nibble of qs[32c + l]), bit 4
+ * = bit t of qh[l]. Weight value d*sc_t*q - dmin*m_t, q in 0..31. */
+static int q5_k_code(const uint8_t *blk, int e) {
+    const uint8_t *qh = blk + 16, *qs = blk + 48;
+    const int t = e / 32, l = e % 32, c = t / 2;
+    const uint8_t byte = qs[32 * c + l];
+    const int low = (t % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
+    return low | (((qh[l] >> t) & 1) << 4);
+}
+
 int orc_dequantize_row(int type, const uint8_t *row, int64_t K, double *w) {
     int qk, bb;
     if (!row || !w) return ORC_ERR_NULL;
@@ -243,6 +279,17 @@ int orc_dequantize_row(int type, const uint8_t *row, int64_t K, double *w) {
         const int i = (int)(e % qk);
         if (type == ORC_Q4_0) {
             w[e] = orc_f16_to_f64(rd16(blk)) * (q4_0_code(blk, i) - 8);
+        } else if (type == ORC_Q4_1) {
+            w[e] = orc_f16_to_f64(rd16(blk)) * q4_1_code(blk, i) + orc_f16_to_f64(rd16(blk + 2));
+        } else if (type == ORC_Q5_0) {
+            w[e] = orc_f16_to_f64(rd16(blk)) * (q5_0_code(blk, i) - 16);
+        } else if (type == ORC_Q5_1) {
+            w[e] = orc_f16_to_f64(rd16(blk)) * q5_1_code(blk, i) + orc_f16_to_f64(rd16(blk + 2));
+        } else if (type == ORC_Q5_K) {
+            int sc, m;
+            orc_q4_k_scale_min(blk + 4, i / 32, &sc, &m);
+            w[e] = orc_f16_to_f64(rd16(blk)) * sc * q5_k_code(blk, i)
+                 - orc_f16_to_f64(rd16(blk + 2)) * m;
         } else if (type == ORC_Q8_0) {
             w[e] = orc_f16_to_f64(rd16(blk)) * q8_0_code(blk, i);
         } else if (type == ORC_Q4_K) {
@@ -281,6 +328,29 @@ static void block_q4_0(const uint8_t *blk, const uint8_t *ycol, int64_t qb,
     if (dots) dots[0] = isum;
 }
 
+/* Q4_1, Q5_1: isum = sum q*qy; contribution d*d8*isum + m*s: the offset
+ * term takes the q8_1 block's stored s (fp16 d8*sum(qy)), as Q4_0 does for
+ * its zero point; the pages give no dot for these formats, and s exists in
+ * q8_1 for exactly this term [MMVQ §激活的量化].
+ * Q5_0: contribution d*(d8*isum - 16*s) (zero point 16 of the 5-bit code,
+ * as Q4_0's 8 of the 4-bit one). */
+static void block_legacy(int type, const uint8_t *blk, const uint8_t *ycol, int64_t qb,
+                         double *acc, double *mag, int32_t *dots) {
+    int isum = 0;
+    for (int e = 0; e < 32; ++e) {
+        const int q = type == ORC_Q4_1 ? q4_1_code(blk, e) : type == ORC_Q5_0 ? q5_0_code(blk, e)
+                                                                            : q5_1_code(blk, e);
+        isum += q * q8_q(ycol, qb, e);
+    }
+    const double d = orc_f16_to_f64(rd16(blk));
+    const double t1 = d * q8_d(ycol, qb) * isum;
+    const double t2 = type == ORC_Q5_0 ? -16.0 * d * q8_s(ycol, qb)
+                                       : orc_f16_to_f64(rd16(blk + 2)) * q8_s(ycol, qb);
+    *acc += t1 + t2;
+    *mag += fabs(t1) + fabs(t2);
+    if (dots) dots[0] = isum;
+}
+
 /* Q8_0: isum = sum q*qy; contribution d_w*d8*isum (symmetric codes: no
  * zero-point or min term). */
 static void block_q8_0(const uint8_t *blk, const uint8_t *ycol, int64_t qb,
@@ -307,6 +377,29 @@ static void block_q4_k(const uint8_t *blk, const uint8_t *ycol, int64_t qb,
         for (int l = 0; l < 32; ++l) {
             const int qy = q8_q(ycol, qb + t, l);
             dot1 += q4_k_code(blk, 32 * t + l) * qy;
+            dot2 += qy;
+        }
+        const double d8 = q8_d(ycol, qb + t);
+        const double t1 = d * sc * d8 * dot1;
+        const double t2 = dmin * m * d8 * dot2;
+        *acc += t1 - t2;
+        *mag += fabs(t1) + fabs(t2);
+        if (dots) { dots[t] = dot1; dots[8 + t] = dot2; }
+    }
+}
+
+/* Q5_K: as Q4_K with the 5-bit codes: per sub-block t, dot1 = sum q*qy,
+ * dot2 = sum qy; contribution d*sc*d8*dot1 - dmin*m*d8*dot2. */
+static void block_q5_k(const uint8_t *blk, const uint8_t *ycol, int64_t qb,
+                       double *acc, double *mag, int32_t *dots) {
+    const double d = orc_f16_to_f64(rd16(blk));
+    const double dmin = orc_f16_to_f64(rd16(blk + 2));
+    for (int t = 0; t < 8; ++t) {
+        int sc, m, dot1 = 0, dot2 = 0;
+        orc_q4_k_scale_min(blk + 4, t, &sc, &m);
+        for (int l = 0; l < 32; ++l) {
+            const int qy = q8_q(ycol, qb + t, l);
+            dot1 += q5_k_code(blk, 32 * t + l) * qy;
             dot2 += qy;
         }
         const double d8 = q8_d(ycol, qb + t);
@@ -349,8 +442,11 @@ static void row_dot(const uint8_t *Wrow, int type, int64_t nb, int bb, int qk,
         const int64_t qb = b * (qk / 32);
         int32_t *dp = dots ? dots + b * nd : NULL;
         if (type == ORC_Q4_0) block_q4_0(blk, ycol, qb, acc, mag, dp);
+        else if (type == ORC_Q4_1 || type == ORC_Q5_0 || type == ORC_Q5_1)
+            block_legacy(type, blk, ycol, qb, acc, mag, dp);
         else if (type == ORC_Q8_0) block_q8_0(blk, ycol, qb, acc, mag, dp);
         else if (type == ORC_Q4_K) block_q4_k(blk, ycol, qb, acc, mag, dp);
+        else if (type == ORC_Q5_K) block_q5_k(blk, ycol, qb, acc, mag, dp);
         else block_q6_k(blk, ycol, qb, acc, mag, dp);
     }
 }

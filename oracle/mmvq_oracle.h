@@ -42,9 +42,13 @@ extern "C" {
 /* Type ids follow the ggml numbering [GGUF16 §16.1.1]. */
 /* (Q8_0 is in the same enumeration, id 8.) */
 #define ORC_Q4_0 2
+#define ORC_Q4_1 3
+#define ORC_Q5_0 6
+#define ORC_Q5_1 7
 #define ORC_Q8_0 8
 #define ORC_Q8_1 9
 #define ORC_Q4_K 12
+#define ORC_Q5_K 13
 #define ORC_Q6_K 14
 
 #define ORC_GLU_PLAIN        0 /* out = gate * up (the epilogue's default branch) */
@@ -64,12 +68,14 @@ extern "C" {
 uint16_t orc_f32_to_f16(float f);   /* round to nearest, ties to even */
 double   orc_f16_to_f64(uint16_t h);
 
-/* Elements and bytes per block: Q4_0 32/18, Q8_0 32/34, Q4_K 256/144,
- * Q6_K 256/210, Q8_1 32/36. */
+/* Elements and bytes per block: Q4_0 32/18, Q4_1 32/20, Q5_0 32/22,
+ * Q5_1 32/24, Q8_0 32/34, Q4_K 256/144, Q5_K 256/176, Q6_K 256/210,
+ * Q8_1 32/36. */
 int orc_type_info(int type, int *block_elems, int *block_bytes);
 
 /* Number of int32 dots the oracle reports per weight block:
- * Q4_0 and Q8_0 1 (the block dot), Q4_K 16 (dot1 of sub-blocks 0..7, then the
+ * Q4_0, Q4_1, Q5_0, Q5_1 and Q8_0 1 (the block dot sum(q*qy) of the unsigned
+ * or signed codes), Q4_K and Q5_K 16 (dot1 of sub-blocks 0..7, then the
  * activation sums dot2 of sub-blocks 0..7), Q6_K 16 (one per sub-block). */
 int orc_dots_per_block(int type);
 

@@ -15,11 +15,22 @@ Block layouts (byte offsets inside one block):
   12 bytes of packed 6-bit scales and mins at 4, 128 bytes of 4-bit codes at 16.
 * Q6_K, 210 bytes / 256 weights: 128 bytes of low code bits at 0, 64 bytes of
   high code bits at 128, 16 int8 sub-block scales at 192, fp16 ``d`` at 208.
+* Q4_1, 20 bytes / 32 weights: fp16 ``d`` at 0, fp16 ``m`` at 2, 16 bytes of
+  4-bit codes at 4.
+* Q5_0, 22 bytes / 32 weights: fp16 ``d`` at 0, 4 bytes of fifth code bits at
+  2, 16 bytes of 4-bit codes at 6.
+* Q5_1, 24 bytes / 32 weights: fp16 ``d`` at 0, fp16 ``m`` at 2, 4 bytes of
+  fifth code bits at 4, 16 bytes of 4-bit codes at 8.
+* Q5_K, 176 bytes / 256 weights: fp16 ``d`` at 0, fp16 ``dmin`` at 2, 12 bytes
+  of packed 6-bit scales and mins at 4, 32 bytes of fifth code bits at 16, 128
+  bytes of 4-bit codes at 48.
 
-Every bit pattern of the packed code bytes and of the 12 Q4_K scale bytes is a
-valid encoding, and uniform random bytes give codes uniform over their range
-(4-bit 0..15, 6-bit 0..63) and 6-bit scales/mins uniform over 0..63, so those
-fields are drawn as raw bytes. The fp16 scales are drawn as fp32 uniforms and
+Every bit pattern of the packed code bytes and of the 12 Q4_K (and Q5_K)
+scale bytes is a valid encoding, and uniform random bytes give codes uniform
+over their range (4-bit 0..15, 5-bit 0..31, 6-bit 0..63) and 6-bit
+scales/mins uniform over 0..63, so those fields are drawn as raw bytes. The
+fp16 offsets ``m`` of Q4_1 / Q5_1 are drawn uniform in -8*d_max..0 (a
+block's values then straddle zero). The fp16 scales are drawn as fp32 uniforms and
 rounded to fp16 by numpy; the Q6_K int8 scales are drawn uniform in -64..63.
 
 Workloads (decode-time layer shapes of a 7B/8B-class model):
@@ -46,11 +57,15 @@ from dataclasses import dataclass
 import numpy as np
 
 Q4_0, Q8_0, Q8_1, Q4_K, Q6_K = 2, 8, 9, 12, 14
-BLOCK = {Q4_0: (32, 18), Q8_0: (32, 34), Q4_K: (256, 144), Q6_K: (256, 210), Q8_1: (32, 36)}
-TYPE_NAME = {Q4_0: "q4_0", Q8_0: "q8_0", Q4_K: "q4_k", Q6_K: "q6_k", Q8_1: "q8_1"}
+Q4_1, Q5_0, Q5_1, Q5_K = 3, 6, 7, 13
+BLOCK = {Q4_0: (32, 18), Q8_0: (32, 34), Q4_K: (256, 144), Q6_K: (256, 210), Q8_1: (32, 36),
+         Q4_1: (32, 20), Q5_0: (32, 22), Q5_1: (32, 24), Q5_K: (256, 176)}
+TYPE_NAME = {Q4_0: "q4_0", Q8_0: "q8_0", Q4_K: "q4_k", Q6_K: "q6_k", Q8_1: "q8_1",
+             Q4_1: "q4_1", Q5_0: "q5_0", Q5_1: "q5_1", Q5_K: "q5_k"}
 
 # fp16 scale ranges per format
-D_RANGE = {Q4_0: (0.001, 0.02), Q8_0: (1e-4, 2e-3), Q4_K: (1e-4, 5e-3), Q6_K: (1e-4, 2e-3)}
+D_RANGE = {Q4_0: (0.001, 0.02), Q8_0: (1e-4, 2e-3), Q4_K: (1e-4, 5e-3), Q6_K: (1e-4, 2e-3),
+           Q4_1: (0.001, 0.02), Q5_0: (5e-4, 1e-2), Q5_1: (5e-4, 1e-2), Q5_K: (1e-4, 5e-3)}
 DMIN_RANGE = (1e-4, 5e-3)
 
 
@@ -130,6 +145,18 @@ def weights(wtype: int, M: int, K: int, rng: np.random.Generator,
         blk[:, 0:192] = rng.integers(0, 256, size=(nb, 192), dtype=np.uint8)
         blk[:, 192:208] = rng.integers(-64, 64, size=(nb, 16), dtype=np.int8).view(np.uint8)
         blk[:, 208:210] = _fp16_bytes(rng, (nb,), lo, hi)
+    elif wtype in (Q4_1, Q5_1):
+        blk[:, 0:2] = _fp16_bytes(rng, (nb,), lo, hi)
+        blk[:, 2:4] = _fp16_bytes(rng, (nb,), -8.0 * hi, 0.0)
+        blk[:, 4:bb] = rng.integers(0, 256, size=(nb, bb - 4), dtype=np.uint8)
+    elif wtype == Q5_0:
+        blk[:, 0:2] = _fp16_bytes(rng, (nb,), lo, hi)
+        blk[:, 2:22] = rng.integers(0, 256, size=(nb, 20), dtype=np.uint8)
+    elif wtype == Q5_K:
+        mlo, mhi = dmin_range or DMIN_RANGE
+        blk[:, 0:2] = _fp16_bytes(rng, (nb,), lo, hi)
+        blk[:, 2:4] = _fp16_bytes(rng, (nb,), mlo, mhi)
+        blk[:, 4:176] = rng.integers(0, 256, size=(nb, 172), dtype=np.uint8)
     else:
         raise ValueError(f"unsupported weight type {wtype}")
     return blk.reshape(M, (K // qk) * bb)

@@ -36,6 +36,7 @@ import os
 import numpy as np
 
 Q4_0, Q8_0, Q8_1, Q4_K, Q6_K = 2, 8, 9, 12, 14
+Q4_1, Q5_0, Q5_1, Q5_K = 3, 6, 7, 13
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
@@ -160,8 +161,66 @@ def deq_q6_k(row: np.ndarray, K: int) -> np.ndarray:
     return np.concatenate(out)
 
 
-DEQ = {Q4_0: deq_q4_0, Q8_0: deq_q8_0, Q4_K: deq_q4_k, Q6_K: deq_q6_k}
-BLOCK = {Q4_0: (32, 18), Q8_0: (32, 34), Q4_K: (256, 144), Q6_K: (256, 210)}
+def _legacy_codes(qs: np.ndarray, qh=None) -> np.ndarray:
+    """32 codes per block row: low nibbles are elements 0..15, high nibbles
+    16..31 (as Q4_0); qh (4 bytes per block) adds bit e of its little-endian
+    word as bit 4 of element e."""
+    qs = qs.astype(np.int64)
+    codes = np.concatenate([qs & 15, qs >> 4], axis=1)
+    if qh is not None:
+        word = (qh[:, 0].astype(np.int64) | (qh[:, 1].astype(np.int64) << 8) | (qh[:, 2].astype(np.int64) << 16)
+                | (qh[:, 3].astype(np.int64) << 24))
+        bits = (word[:, None] >> np.arange(32)[None, :]) & 1
+        codes = codes + 16 * bits
+    return codes
+
+
+def deq_q4_1(row: np.ndarray, K: int) -> np.ndarray:
+    """Reading of the GGUF Q4_1 block (the pages name the format): fp16 d @0,
+    fp16 m @2, qs @4; weight = d*q + m."""
+    blk = row.reshape(K // 32, 20)
+    return (_f16v(blk[:, 0:2])[:, None] * _legacy_codes(blk[:, 4:20]) + _f16v(blk[:, 2:4])[:, None]).reshape(-1)
+
+
+def deq_q5_0(row: np.ndarray, K: int) -> np.ndarray:
+    """Reading of the GGUF Q5_0 block: fp16 d @0, qh @2, qs @6; weight =
+    d*(q - 16)."""
+    blk = row.reshape(K // 32, 22)
+    return (_f16v(blk[:, 0:2])[:, None] * (_legacy_codes(blk[:, 6:22], blk[:, 2:6]) - 16)).reshape(-1)
+
+
+def deq_q5_1(row: np.ndarray, K: int) -> np.ndarray:
+    """Reading of the GGUF Q5_1 block: fp16 d @0, fp16 m @2, qh @4, qs @8;
+    weight = d*q + m."""
+    blk = row.reshape(K // 32, 24)
+    return (_f16v(blk[:, 0:2])[:, None] * _legacy_codes(blk[:, 8:24], blk[:, 4:8])
+            + _f16v(blk[:, 2:4])[:, None]).reshape(-1)
+
+
+def deq_q5_k(row: np.ndarray, K: int) -> np.ndarray:
+    """Reading of the GGUF Q5_K block: fp16 d @0, fp16 dmin @2, the Q4_K scale
+    bytes @4, qh[32] @16, qs[128] @48. Element l of the low (high) nibble run
+    of 64-element chunk c belongs to sub-block t = 2c (2c + 1) and takes bit t
+    of qh[l] as bit 4; weight = d*sc_t*q - dmin*m_t."""
+    out = []
+    for blk in row.reshape(K // 256, 176):
+        d = _f16v(blk[0:2])[0]
+        dmin = _f16v(blk[2:4])[0]
+        sc, mn = q4_k_scales_from_fragment(blk[4:16])
+        qh = blk[16:48].astype(np.int64)
+        qs = blk[48:176].astype(np.int64)
+        for c in range(4):
+            q = qs[32 * c:32 * c + 32]
+            for h, t in ((0, 2 * c), (1, 2 * c + 1)):
+                code = ((q >> (4 * h)) & 15) + 16 * ((qh >> t) & 1)
+                out.append(d * sc[t] * code - dmin * mn[t])
+    return np.concatenate(out)
+
+
+DEQ = {Q4_0: deq_q4_0, Q8_0: deq_q8_0, Q4_K: deq_q4_k, Q6_K: deq_q6_k,
+       Q4_1: deq_q4_1, Q5_0: deq_q5_0, Q5_1: deq_q5_1, Q5_K: deq_q5_k}
+BLOCK = {Q4_0: (32, 18), Q8_0: (32, 34), Q4_K: (256, 144), Q6_K: (256, 210),
+         Q4_1: (32, 20), Q5_0: (32, 22), Q5_1: (32, 24), Q5_K: (256, 176)}
 
 
 def deq_y(col: np.ndarray, K: int) -> np.ndarray:
@@ -223,6 +282,13 @@ def pin_type_info(O):
     assert O.type_info(Q4_K) == (256, 144)
     assert O.type_info(Q6_K) == (256, 210)
     assert O.type_info(Q8_1) == (32, 36)
+    # the formats the pages name without layouts: sizes of the GGUF blocks
+    # (20, 22, 24 bytes per 32 weights; 176 per 256, ~5.5 bits a weight as
+    # the LLM page's Q5_K_M row of ~22 B per 32 weights)
+    assert O.type_info(Q4_1) == (32, 20)
+    assert O.type_info(Q5_0) == (32, 22)
+    assert O.type_info(Q5_1) == (32, 24)
+    assert O.type_info(Q5_K) == (256, 176)
 
 
 def pin_f16_decode(O):
@@ -364,6 +430,40 @@ def pin_q8_0_e6(O):
     assert dots[0][0] == e["isum"] and out == e["out"] and mag == e["mag"], (dots, out, mag)
 
 
+def _pin_legacy_golden(O, fname, wtype):
+    fx = golden(fname)
+    blk = bytes.fromhex(fx["weight_block_hex"])
+    yb = fx["q8_1_block"]
+    y = np.frombuffer(q8_1_block(yb["d_bits"], yb["s_bits"], yb["q"]), dtype=np.uint8)
+    out, mag, dots = _run_block(O, wtype, blk, y, 32)
+    e = fx["expected"]
+    assert dots[0][0] == e["isum"] and out == e["out"] and mag == e["mag"], (fname, dots, out, mag)
+
+
+def pin_q4_1_e7(O):
+    _pin_legacy_golden(O, "q4_1_e7.json", Q4_1)
+
+
+def pin_q5_0_e8(O):
+    _pin_legacy_golden(O, "q5_0_e8.json", Q5_0)
+
+
+def pin_q5_1_e9(O):
+    _pin_legacy_golden(O, "q5_1_e9.json", Q5_1)
+
+
+def pin_q5_k_e10(O):
+    fx = golden("q5_k_e10.json")
+    hdr = bytes.fromhex(fx["weight_block_header_hex"])
+    blk = hdr + bytes([int(fx["qh_byte"], 16)]) * 32 + bytes([int(fx["qs_byte"], 16)]) * 128
+    y = np.frombuffer(b"".join(q8_1_block(b["d_bits"], b["s_bits"], [b["q_all"]] * 32) for b in fx["q8_1_blocks"]),
+                      dtype=np.uint8)
+    out, mag, dots = _run_block(O, Q5_K, blk, y, 256)
+    e = fx["expected"]
+    assert list(dots[0][:8]) == e["dot1"] and list(dots[0][8:]) == e["dot2"], dots
+    assert out == e["out"] and mag == e["mag"], (out, mag)
+
+
 def pin_q4_k_e4(O):
     fx = golden("q4_k_e4.json")
     hdr = bytes.fromhex(fx["weight_block_header_hex"])
@@ -458,7 +558,8 @@ def pin_brute_force(O, seeds=(0, 1, 2)):
     dequantize-then-dot [MMVQ §一次 vec_dot 的解剖; GGUF16 §16.2.2]. K-quants
     agree to fp64 roundoff; Q4_0 uses the fp16 s, so it agrees to within
     8*|d_w|*|s - d8*sum(q)| per block."""
-    for wtype, Ks in [(Q4_0, (32, 64, 256)), (Q8_0, (32, 96)), (Q4_K, (256, 512)), (Q6_K, (256, 512))]:
+    for wtype, Ks in [(Q4_0, (32, 64, 256)), (Q8_0, (32, 96)), (Q4_K, (256, 512)), (Q6_K, (256, 512)),
+                      (Q4_1, (32, 96)), (Q5_0, (32, 96)), (Q5_1, (32, 96)), (Q5_K, (256, 512))]:
         qk, bb = BLOCK[wtype]
         for K in Ks:
             for seed in seeds:
@@ -472,14 +573,18 @@ def pin_brute_force(O, seeds=(0, 1, 2)):
                         w = DEQ[wtype](W[r], K)
                         assert np.array_equal(w, O.dequantize_row(wtype, W[r], K)), (wtype, K, r)
                         ref = float(np.dot(w, yd))
-                        if wtype == Q4_0:
+                        if wtype in (Q4_0, Q4_1, Q5_0, Q5_1):
+                            # the old-style formats take the offset term from
+                            # the fp16 s: off by |offset| * |s - d8*sum(q)|
                             yb = y[j].reshape(-1, 36)
                             d8 = yb[:, 0:2].copy().view(np.float16).astype(np.float64).reshape(-1)
                             s8 = yb[:, 2:4].copy().view(np.float16).astype(np.float64).reshape(-1)
                             sq = yb[:, 4:36].view(np.int8).astype(np.int64).sum(axis=1)
-                            dw = np.abs(W[r].reshape(-1, 18)[:, 0:2].copy().view(np.float16)
-                                        .astype(np.float64).reshape(-1))
-                            tol = float(np.sum(8 * dw * np.abs(s8 - d8 * sq))) * (1 + 1e-9) + 1e-12
+                            wb = W[r].reshape(-1, bb)
+                            dw = np.abs(wb[:, 0:2].copy().view(np.float16).astype(np.float64).reshape(-1))
+                            off = {Q4_0: 8 * dw, Q5_0: 16 * dw}.get(
+                                wtype, np.abs(wb[:, 2:4].copy().view(np.float16).astype(np.float64).reshape(-1)))
+                            tol = float(np.sum(off * np.abs(s8 - d8 * sq))) * (1 + 1e-9) + 1e-12
                         else:
                             tol = 1e-12 * mag[j, r] + 1e-15
                         assert abs(out[j, r] - ref) <= tol, (wtype, K, seed, j, r, out[j, r], ref)
@@ -774,7 +879,7 @@ def pin_error_codes(O):
     assert L.orc_mmvq(None, Q4_K, 1, 256, None, 1, None, None, None) == -1
     buf = np.zeros(4096, dtype=np.uint8)
     p = buf.ctypes.data
-    assert L.orc_mmvq(p, 7, 1, 256, p, 1, p, None, None) == -2
+    assert L.orc_mmvq(p, 5, 1, 256, p, 1, p, None, None) == -2   # id 5: removed from the enumeration
     assert L.orc_mmvq(p, Q4_K, 1, 200, p, 1, p, None, None) == -3
     assert L.orc_mmvq(p, Q4_K, 0, 256, p, 1, p, None, None) == -3
     assert L.orc_quantize_q8_1(p, 33, 1, 33, p) == -3
@@ -782,7 +887,8 @@ def pin_error_codes(O):
 
 
 ALL_PINS = [pin_type_info, pin_f16_decode, pin_f16_encode, pin_q8_1_e1, pin_q8_1_e2,
-            pin_q8_1_properties, pin_q4_0_e3, pin_q4_k_e4, pin_q6_k_e5, pin_q8_0_e6, pin_q4_k_fragment,
+            pin_q8_1_properties, pin_q4_0_e3, pin_q4_k_e4, pin_q6_k_e5, pin_q8_0_e6, pin_q4_1_e7,
+            pin_q5_0_e8, pin_q5_1_e9, pin_q5_k_e10, pin_q4_k_fragment,
             pin_q4_k_bijection, pin_q6_k_fragment, pin_brute_force, pin_int_dot_special,
             pin_columns_independent, pin_glu, pin_id, pin_zero_padding, pin_linearity,
             pin_glu_variants, pin_epilogue, pin_error_codes]

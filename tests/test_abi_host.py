@@ -48,7 +48,7 @@ P16, P4 = 1 << 20, (1 << 20) + 4
     ((None, B.Q4_K, 1, 256, P16, 1, P16), B.ERR_NULL),
     ((P16, B.Q4_K, 1, 256, None, 1, P16), B.ERR_NULL),
     ((P16, B.Q4_K, 1, 256, P16, 1, None), B.ERR_NULL),
-    ((P16, 7, 1, 256, P16, 1, P16), B.ERR_TYPE),
+    ((P16, 5, 1, 256, P16, 1, P16), B.ERR_TYPE),
     ((P16, B.Q8_1, 1, 256, P16, 1, P16), B.ERR_TYPE),
     ((P16, B.Q4_K, 1, 200, P16, 1, P16), B.ERR_SHAPE),
     ((P16, B.Q4_0, 1, 48, P16, 1, P16), B.ERR_SHAPE),

@@ -158,7 +158,7 @@ def test_many_columns_argument_checks():
     assert L.mmvq(p, Q4_K, 1, 256, q, 257, o, s) == B.ERR_SHAPE
     assert L.mmvq(p, B.Q4_0, 1, 256, q, 257, o, s) == B.ERR_SHAPE
     assert L.mmvq(p, B.Q6_K, 1, 96, q, 9, o, s) == B.ERR_SHAPE
-    assert L.mmvq(p, 7, 1, 256, q, 9, o, s) == B.ERR_TYPE
+    assert L.mmvq(p, 5, 1, 256, q, 9, o, s) == B.ERR_TYPE
     assert L.mmvq(p, Q4_K, 1, 200, q, 9, o, s) == B.ERR_SHAPE
     assert L.mmvq(p + 4, Q4_K, 1, 256, q, 9, o, s) == B.ERR_ALIGN
     assert L.mmvq(p + 4, B.Q8_0, 1, 96, q, 9, o, s) == B.ERR_ALIGN     # column groups check first

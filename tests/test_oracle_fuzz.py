@@ -14,6 +14,8 @@ from oracle_pins import BLOCK, DEQ, deq_y
 from quantized_decode_gemv_quantize_amd import synth
 
 Q4_0, Q8_0, Q4_K, Q6_K = oracle.Q4_0, oracle.Q8_0, oracle.Q4_K, oracle.Q6_K
+Q4_1, Q5_0, Q5_1, Q5_K = oracle.Q4_1, oracle.Q5_0, oracle.Q5_1, oracle.Q5_K
+LEGACY = (Q4_0, Q4_1, Q5_0, Q5_1)      # offset term from the q8_1 block's fp16 s
 
 SETTINGS = settings(max_examples=150, deadline=None, suppress_health_check=[HealthCheck.too_slow])
 
@@ -30,7 +32,7 @@ _elem = st.one_of(st.floats(-1e3, 1e3, width=32, allow_nan=False, allow_infinity
 
 @st.composite
 def gemv_case(draw):
-    wtype = draw(st.sampled_from([Q4_0, Q8_0, Q4_K, Q6_K]))
+    wtype = draw(st.sampled_from([Q4_0, Q8_0, Q4_K, Q6_K, Q4_1, Q5_0, Q5_1, Q5_K]))
     qk, _ = BLOCK[wtype]
     nblk = draw(st.integers(1, 3 if qk == 256 else 6))
     K = nblk * qk
@@ -47,7 +49,8 @@ def _rescale(W, wtype, scale):
     1e-3, values stay finite)."""
     qk, bb = BLOCK[wtype]
     W = W.copy().reshape(-1, bb)
-    fields = {Q4_0: [(0, 2)], Q8_0: [(0, 2)], Q4_K: [(0, 2), (2, 4)], Q6_K: [(208, 210)]}[wtype]
+    fields = {Q4_0: [(0, 2)], Q8_0: [(0, 2)], Q4_K: [(0, 2), (2, 4)], Q6_K: [(208, 210)],
+              Q4_1: [(0, 2), (2, 4)], Q5_0: [(0, 2)], Q5_1: [(0, 2), (2, 4)], Q5_K: [(0, 2), (2, 4)]}[wtype]
     for a, b in fields:
         v = W[:, a:b].copy().view(np.float16).astype(np.float64) * scale
         W[:, a:b] = v.astype(np.float16).view(np.uint8)
@@ -68,17 +71,20 @@ def test_oracle_equals_dequantized_dot(O, case):
             w = DEQ[wtype](W[r * row_bytes:(r + 1) * row_bytes], K)
             ref = float(np.dot(w, yd))
             if not np.isfinite(out[j, r]):
-                # a q8_1 s that overflowed fp16 (only Q4_0 reads s)
-                assert wtype == Q4_0
+                # a q8_1 s that overflowed fp16 (only the old-style formats read s)
+                assert wtype in LEGACY
                 continue
-            if wtype == Q4_0:
+            if wtype in LEGACY:
+                bb = BLOCK[wtype][1]
                 yb = y[j].reshape(-1, 36)
                 d8 = yb[:, 0:2].copy().view(np.float16).astype(np.float64).reshape(-1)
                 s8 = yb[:, 2:4].copy().view(np.float16).astype(np.float64).reshape(-1)
                 sq = yb[:, 4:36].view(np.int8).astype(np.int64).sum(axis=1)
-                dw = np.abs(W[r * row_bytes:(r + 1) * row_bytes].reshape(-1, 18)[:, 0:2].copy()
-                            .view(np.float16).astype(np.float64).reshape(-1))
-                tol = float(np.sum(8 * dw * np.abs(s8 - d8 * sq))) * (1 + 1e-9) + 1e-12 * mag[j, r] + 1e-300
+                wb = W[r * row_bytes:(r + 1) * row_bytes].reshape(-1, bb)
+                dw = np.abs(wb[:, 0:2].copy().view(np.float16).astype(np.float64).reshape(-1))
+                off = {Q4_0: 8 * dw, Q5_0: 16 * dw}.get(
+                    wtype, np.abs(wb[:, 2:4].copy().view(np.float16).astype(np.float64).reshape(-1)))
+                tol = float(np.sum(off * np.abs(s8 - d8 * sq))) * (1 + 1e-9) + 1e-12 * mag[j, r] + 1e-300
             else:
                 tol = 1e-12 * mag[j, r] + 1e-300
             assert abs(out[j, r] - ref) <= tol, (wtype, K, j, r, out[j, r], ref)

@@ -48,6 +48,18 @@ MUTATIONS = {
     "q6_k_offset_31": ("isum += (q6_k_code(blk, e) - 32)", "isum += (q6_k_code(blk, e) - 31)"),
     "q6_k_q8_block_map": ("const int64_t yb = qb + s / 2;", "const int64_t yb = qb + s % 8;"),
     "q6_k_scale_unsigned": ("return (int8_t)blk[192 + s];", "return blk[192 + s];"),
+    "legacy_nibbles_swapped": ("static int nib_code(const uint8_t *qs, int e) { return e < 16 ? (qs[e] & 0x0F) : (qs[e - 16] >> 4); }",
+                               "static int nib_code(const uint8_t *qs, int e) { return e < 16 ? (qs[e] >> 4) : (qs[e - 16] & 0x0F); }"),
+    "qh_bit_big_endian": ("return (qh[e / 8] >> (e % 8)) & 1;", "return (qh[3 - e / 8] >> (e % 8)) & 1;"),
+    "q4_1_field_order": ("static int q4_1_code(const uint8_t *blk, int e) { return nib_code(blk + 4, e); }",
+                         "static int q4_1_code(const uint8_t *blk, int e) { return nib_code(blk + 2, e); }"),
+    "q5_1_qh_after_qs": ("static int q5_1_code(const uint8_t *blk, int e) { return nib_code(blk + 8, e) | (qh_bit(blk + 4, e) << 4); }",
+                         "static int q5_1_code(const uint8_t *blk, int e) { return nib_code(blk + 4, e) | (qh_bit(blk + 20, e) << 4); }"),
+    "q5_0_zero_point_8": ("const double t2 = type == ORC_Q5_0 ? -16.0 * d * q8_s(ycol, qb)",
+                          "const double t2 = type == ORC_Q5_0 ? -8.0 * d * q8_s(ycol, qb)"),
+    "legacy_offset_sign": ("*acc += t1 + t2;", "*acc += t1 - t2;"),
+    "q5_k_qh_bit_chunk": ("return low | (((qh[l] >> t) & 1) << 4);", "return low | (((qh[l] >> c) & 1) << 4);"),
+    "q5_k_qs_offset": ("const uint8_t *qh = blk + 16, *qs = blk + 48;", "const uint8_t *qh = blk + 16, *qs = blk + 16;"),
     "silu_sigmoid_only": ("static double silu(double z) { return z / (1.0 + exp(-z)); }",
                           "static double silu(double z) { return 1.0 / (1.0 + exp(-z)); }"),
     "glu_plain_for_silu": ("case ORC_GLU_SWIGLU: *out = silu(g) * u; break;",
