@@ -62,12 +62,30 @@ extern "C" {
 #endif
 
 /* Type ids follow the ggml numbering, whose ids are never reused
- * [GGUF16 §16.1.1]. */
+ * [GGUF16 §16.1.1]. Q4_1, Q5_0, Q5_1 and Q5_K are named on the pages without
+ * their layouts (old-style blocks [MMVQ §权重的排法]; Q5_K among the
+ * min-term formats [MMVQ §激活的量化]); the layouts taken are the published
+ * GGUF block definitions:
+ *   Q4_1 20 B / 32: fp16 d, fp16 m, 16 nibble bytes; weight d*q + m
+ *   Q5_0 22 B / 32: fp16 d, 4 bytes of fifth bits, 16 nibble bytes;
+ *                   weight d*(q - 16)
+ *   Q5_1 24 B / 32: fp16 d, fp16 m, 4 bytes of fifth bits, 16 nibble bytes;
+ *                   weight d*q + m
+ *   Q5_K 176 B / 256: fp16 d, fp16 dmin, the 12 Q4_K scale bytes, 32 bytes
+ *                   of fifth bits, 128 nibble bytes; weight d*sc*q - dmin*m
+ * (nibbles as Q4_0 / Q4_K; bit e of the 32-bit fifth-bit word is bit 4 of
+ * element e; in Q5_K bit t of qh[l] for element l of sub-block t's run).
+ * The old-style formats take their offset term from the q8_1 block's s:
+ * d*d8*sum(q*qy) + m*s, Q5_0 d*(d8*sum(q*qy) - 16*s). */
 enum {
     MMVQ_Q4_0 = 2,
+    MMVQ_Q4_1 = 3,
+    MMVQ_Q5_0 = 6,
+    MMVQ_Q5_1 = 7,
     MMVQ_Q8_0 = 8,
     MMVQ_Q8_1 = 9,
     MMVQ_Q4_K = 12,
+    MMVQ_Q5_K = 13,
     MMVQ_Q6_K = 14
 };
 
@@ -132,7 +150,8 @@ enum {
 #define MMVQ_MAX_COLS_BATCH 256
 
 /* Block geometry of a type: elements per block and bytes per block
- * (Q4_0 32/18, Q8_0 32/34, Q4_K 256/144, Q6_K 256/210, Q8_1 32/36)
+ * (Q4_0 32/18, Q4_1 32/20, Q5_0 32/22, Q5_1 32/24, Q8_0 32/34, Q4_K 256/144,
+ * Q5_K 256/176, Q6_K 256/210, Q8_1 32/36)
  * [MMVQ §一次 vec_dot 的解剖 (format table); GGUF16 §16.1.2, §16.1.3;
  * LLM §量化格式 (Q8_0)].
  * Either output pointer may be NULL. Host-only; touches no device. */

@@ -19,6 +19,7 @@ LIB = os.path.join(HERE, "libmmvq.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "mmvq.h")
 
 Q4_0, Q8_0, Q8_1, Q4_K, Q6_K = 2, 8, 9, 12, 14
+Q4_1, Q5_0, Q5_1, Q5_K = 3, 6, 7, 13
 GLU_PLAIN, GLU_SWIGLU, GLU_GEGLU, GLU_SWIGLU_OAI, GLU_SWIGLU_CLAMP = 0, 1, 2, 3, 4
 MAX_COLS = 8
 BLOCK = {Q4_0: (32, 18), Q8_0: (32, 34), Q4_K: (256, 144), Q6_K: (256, 210), Q8_1: (32, 36)}

@@ -19,6 +19,10 @@ const Dispatch* dispatch_for(int type, bool f32) {
     case MMVQ_Q8_0: return f32 ? &dispatch_q8_0_f32() : &dispatch_q8_0();
     case MMVQ_Q4_K: return f32 ? &dispatch_q4_k_f32() : &dispatch_q4_k();
     case MMVQ_Q6_K: return f32 ? &dispatch_q6_k_f32() : &dispatch_q6_k();
+    case MMVQ_Q4_1: return f32 ? &dispatch_q4_1_f32() : &dispatch_q4_1();
+    case MMVQ_Q5_0: return f32 ? &dispatch_q5_0_f32() : &dispatch_q5_0();
+    case MMVQ_Q5_1: return f32 ? &dispatch_q5_1_f32() : &dispatch_q5_1();
+    case MMVQ_Q5_K: return f32 ? &dispatch_q5_k_f32() : &dispatch_q5_k();
     default: return nullptr;
   }
 }
@@ -97,6 +101,12 @@ mmvq_epilogue glu_only(int glu_op) {
   return e;
 }
 
+// Formats the matrix-core kernel takes (the others run more than
+// MMVQ_MAX_COLS columns as column groups through the row kernels).
+bool mmq_type(int type) {
+  return type == MMVQ_Q4_K || type == MMVQ_Q6_K || type == MMVQ_Q4_0 || type == MMVQ_Q8_0;
+}
+
 // Many columns (up to MMVQ_MAX_COLS_BATCH): the MFMA kernel, q8_1
 // activations, no gate, K a multiple of 256; the epilogue's up scale and
 // bias apply.
@@ -105,6 +115,7 @@ int mmq_common(const void* W, int type, int64_t M, int64_t K, const void* y_q, i
   if (!W || !y_q || !out) return MMVQ_ERR_NULL;
   const Dispatch* d = dispatch_for(type, false);
   if (!d) return MMVQ_ERR_TYPE;
+  if (!mmq_type(type)) return MMVQ_ERR_TYPE;
   if (M < 1 || K < 1 || K % 256 != 0 || n < 1 || n > MMVQ_MAX_COLS_BATCH) return MMVQ_ERR_SHAPE;
   if (M > (int64_t(1) << 40) / K || K / 256 > (int64_t(1) << 24)) return MMVQ_ERR_SHAPE;
   if (!aligned(W, 16) || !aligned(y_q, 16) || !aligned(out, 4)) return MMVQ_ERR_ALIGN;
@@ -140,7 +151,7 @@ int64_t mmq_min_cols(int type) { return type == MMVQ_Q4_K ? 6 : MMVQ_MAX_COLS + 
 // enqueued.
 int rows_common(const void* W_up, const void* W_gate, int type, int64_t M, int64_t K, const ActIn& in, int64_t n,
                 const mmvq_epilogue* epi, float* out, void* stream) {
-  const bool mmq_form = !W_gate && !in.x && K % 256 == 0 && dispatch_for(type, false) != nullptr;
+  const bool mmq_form = !W_gate && !in.x && K % 256 == 0 && mmq_type(type);
   if (mmq_form && n >= mmq_min_cols(type)) return mmq_common(W_up, type, M, K, in.y_q, n, epi, out, stream);
 #ifdef QMV_TUNING
   if (getenv("MMVQ_FORCE_MMQ") && mmq_form) return mmq_common(W_up, type, M, K, in.y_q, n, epi, out, stream);
@@ -211,8 +222,12 @@ int mmvq_type_info(int type, int* block_elems, int* block_bytes) {
   int e, b;
   switch (type) {
     case MMVQ_Q4_0: e = 32; b = 18; break;
+    case MMVQ_Q4_1: e = 32; b = 20; break;
+    case MMVQ_Q5_0: e = 32; b = 22; break;
+    case MMVQ_Q5_1: e = 32; b = 24; break;
     case MMVQ_Q8_0: e = 32; b = 34; break;
     case MMVQ_Q4_K: e = 256; b = 144; break;
+    case MMVQ_Q5_K: e = 256; b = 176; break;
     case MMVQ_Q6_K: e = 256; b = 210; break;
     case MMVQ_Q8_1: e = 32; b = 36; break;
     default: return MMVQ_ERR_TYPE;

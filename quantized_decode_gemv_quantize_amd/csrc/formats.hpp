@@ -855,4 +855,257 @@ struct Q6K {
   }
 };
 
+// ===========================================================================
+// Old-style 32-weight blocks with an offset term: Q4_1, Q5_0, Q5_1
+// [MMVQ §权重的排法 (old-style blocks, Q5_1 named among them), §激活的量化;
+// GGUF16 §16.1.1 (type ids 3, 6, 7)]. The pages name these formats without
+// their layouts; the layouts are the published GGUF block definitions:
+//   Q4_1: fp16 d @0, fp16 m @2, qs[16] @4 (20 bytes); weight d*q + m
+//   Q5_0: fp16 d @0, qh[4] @2, qs[16] @6 (22 bytes); weight d*(q - 16)
+//   Q5_1: fp16 d @0, fp16 m @2, qh[4] @4, qs[16] @8 (24 bytes); weight d*q + m
+// Low 4 bits as in Q4_0 (low nibble of qs[j] = element j, high nibble =
+// element j+16); bit e of the little-endian qh word is bit 4 of element e.
+// Per block: d*d8*sum(q*qy) plus the offset term from the q8_1 block's s
+// (m*s, or -16*d*s for Q5_0), as Q4_0 takes its zero point from s. Unit =
+// one block; the activation side is Q4_0's with s kept unscaled.
+// ===========================================================================
+struct Legacy32Act {
+  static constexpr int kQK = 32, kUnitsPerBlock = 1, kDotsPerBlock = 1;
+
+  struct Act {
+    uint32_t y[8];
+    float d8;
+    float s;
+  };
+
+  __device__ static void issue_act(Act& a, const uint8_t* ycol, int u) {
+    const uint8_t* b = ycol + static_cast<int64_t>(u) * kQ8Bytes;
+    const u32x4 lo = ld_x4(b + 4), hi = ld_x4(b + 20);
+    a.y[0] = lo.x; a.y[1] = lo.y; a.y[2] = lo.z; a.y[3] = lo.w;
+    a.y[4] = hi.x; a.y[5] = hi.y; a.y[6] = hi.z; a.y[7] = hi.w;
+    a.d8 = __uint_as_float(ld_u32(b));     // fp16 d and s, raw
+  }
+
+  __device__ static void finish_act(Act& a) {
+    const uint32_t ds = __float_as_uint(a.d8);
+    a.d8 = h2f(ds);
+    a.s = h2f(ds >> 16);
+  }
+
+  __device__ static void load_act(Act& a, const uint8_t* ycol, int u) {
+    issue_act(a, ycol, u);
+    finish_act(a);
+  }
+
+  struct XRaw {
+    u32x4 r[8];
+  };
+  static constexpr int kXWords = 32;
+
+  __device__ static void load_x(XRaw& x, const float* xcol, int u) {
+    const float* p = xcol + static_cast<int64_t>(u) * 32;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x.r[k] = ld_x4(reinterpret_cast<const uint8_t*>(p + 4 * k));
+  }
+
+  __device__ static void quant_x(Act& a, const XRaw& x) {
+    float m = absmax4(x.r[0]);
+#pragma unroll
+    for (int k = 1; k < 8; ++k) m = fmaxf(m, absmax4(x.r[k]));
+    const float d = q8_scale(m);
+    int sq = 0;
+    q8_quant_block(x.r, d, a.y, sq);
+    a.d8 = q8_d_rounded(d);
+    a.s = h2f(f2h_bits(q8_s(d, sq)));
+  }
+
+  __device__ static void zero_act(Act& a) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) a.y[k] = 0;
+    a.d8 = a.s = 0.0f;
+  }
+
+  struct Lane {
+    uint32_t off;    // block offset from the row start
+  };
+
+  // the 8 code words: lo[k] elements 4k..4k+3, hi[k] elements 16+4k.. (one
+  // byte each), with bit 4 from qh (the 4 qh bits of a word spread to the
+  // bytes' bit 4 by a multiply: bit i of b lands at bit 8i)
+  struct Dec {
+    uint32_t lo[4], hi[4];
+    float d, off;    // off: m, or -16*d
+  };
+
+  __device__ static uint32_t spread4(uint32_t qh, int first) {
+    const uint32_t b = (qh >> first) & 0xFu;
+    return ((b * 0x00204081u) & 0x01010101u) << 4;
+  }
+
+  __device__ static void split(const uint32_t (&qs)[4], uint32_t qh, bool five, Dec& o) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      o.lo[k] = qs[k] & 0x0F0F0F0Fu;
+      o.hi[k] = (qs[k] >> 4) & 0x0F0F0F0Fu;
+      if (five) {
+        o.lo[k] |= spread4(qh, 4 * k);
+        o.hi[k] |= spread4(qh, 16 + 4 * k);
+      }
+    }
+  }
+
+  __device__ static int isum(const Dec& o, const Act& a) {
+    int s = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) s = dot4(o.lo[k], a.y[k], s);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) s = dot4(o.hi[k], a.y[4 + k], s);
+    return s;
+  }
+
+  // d*d8*isum + off*s
+  __device__ static float col_dot(const Dec& o, const Act& a) {
+    return fmaf(o.d * a.d8, static_cast<float>(isum(o, a)), o.off * a.s);
+  }
+
+  __device__ static void int_dots(const Dec& o, const uint8_t* ycol, int u, int* dots) {
+    Act a;
+    load_act(a, ycol, u);
+    dots[0] += isum(o, a);
+  }
+};
+
+// Q4_1: 20-byte blocks, 4-byte aligned (rows of K/32 blocks from a 16-byte
+// aligned base): d | m as one word, the 16 code bytes as one run.
+struct Q41 : Legacy32Act {
+  static constexpr int kType = 3, kBlockBytes = 20;
+  __device__ static Lane lane(int u) { return Lane{static_cast<uint32_t>(u * kBlockBytes)}; }
+  struct Wt {
+    u32x4 qs;
+    uint32_t dm;
+  };
+  __device__ static void load_wt(Wt& w, const uint8_t* row, uint32_t extra, const Lane& l) {
+    const uint32_t off = extra + l.off;
+    w.dm = ld_u32(row + off);
+    w.qs = ld_x4(row + (off + 4));
+  }
+  __device__ static void decode(const Wt& w, Dec& o, const Lane&) {
+    const uint32_t qs[4] = {w.qs.x, w.qs.y, w.qs.z, w.qs.w};
+    split(qs, 0u, false, o);
+    o.d = h2f(w.dm);
+    o.off = h2f(w.dm >> 16);
+  }
+};
+
+// Q5_1: 24-byte blocks, 8-byte aligned: d | m, qh, then the codes.
+struct Q51 : Legacy32Act {
+  static constexpr int kType = 7, kBlockBytes = 24;
+  __device__ static Lane lane(int u) { return Lane{static_cast<uint32_t>(u * kBlockBytes)}; }
+  struct Wt {
+    u32x4 qs;
+    uint32_t dm, qh;
+  };
+  __device__ static void load_wt(Wt& w, const uint8_t* row, uint32_t extra, const Lane& l) {
+    const uint32_t off = extra + l.off;
+    const u32x2 h = ld_x2(row + off);
+    w.dm = h.x;
+    w.qh = h.y;
+    w.qs = ld_x4(row + (off + 8));
+  }
+  __device__ static void decode(const Wt& w, Dec& o, const Lane&) {
+    const uint32_t qs[4] = {w.qs.x, w.qs.y, w.qs.z, w.qs.w};
+    split(qs, w.qh, true, o);
+    o.d = h2f(w.dm);
+    o.off = h2f(w.dm >> 16);
+  }
+};
+
+// Q5_0: 22-byte blocks, only 2-byte aligned. Every read stays inside the
+// block: at an offset = 0 (mod 4) a 16-byte run from the start, the word at
+// 16 and the 16-bit word at 20; at 2 (mod 4) the 16-bit d, a 16-byte run from
+// byte 2 and the word at 18.
+struct Q50 : Legacy32Act {
+  static constexpr int kType = 6, kBlockBytes = 22;
+  __device__ static Lane lane(int u) { return Lane{static_cast<uint32_t>(u * kBlockBytes)}; }
+  struct Wt {
+    u32x4 run;
+    uint32_t w1, w2;
+    bool odd;        // block address = 2 (mod 4)
+  };
+  __device__ static void load_wt(Wt& w, const uint8_t* row, uint32_t extra, const Lane& l) {
+    const uint32_t off = extra + l.off;
+    w.odd = ((static_cast<uint32_t>(reinterpret_cast<uintptr_t>(row)) + off) & 2u) != 0;
+    w.run = ld_x4(row + (off + (w.odd ? 2u : 0u)));
+    w.w1 = ld_u32(row + (off + (w.odd ? 18u : 16u)));
+    w.w2 = ld_u16(row + (off + (w.odd ? 0u : 20u)));
+  }
+  __device__ static void decode(const Wt& w, Dec& o, const Lane&) {
+    // odd: d = w2, bytes 2..17 = run, 18..21 = w1
+    // even: bytes 0..15 = run, 16..19 = w1, 20..21 = w2
+    const uint32_t qh = w.odd ? w.run.x : shr16_pair(w.run.y, w.run.x);
+    uint32_t qs[4];
+    qs[0] = w.odd ? w.run.y : shr16_pair(w.run.z, w.run.y);
+    qs[1] = w.odd ? w.run.z : shr16_pair(w.run.w, w.run.z);
+    qs[2] = w.odd ? w.run.w : shr16_pair(w.w1, w.run.w);
+    qs[3] = w.odd ? w.w1 : shr16_pair(w.w2, w.w1);
+    split(qs, qh, true, o);
+    o.d = h2f(w.odd ? w.w2 : w.run.x);
+    o.off = -16.0f * o.d;
+  }
+};
+
+// ===========================================================================
+// Q5_K [MMVQ §激活的量化 (a min-term format); GGUF16 §16.1.1 (type id 13)].
+// The layout is the published GGUF block definition (the pages do not print
+// it): fp16 d @0, fp16 dmin @2, the 12 packed scale/min bytes of Q4_K @4,
+// qh[32] @16, qs[128] @48; 176 bytes. Element l of the low (high) nibble run
+// of 64-element chunk c is in sub-block t = 2c (2c + 1) and takes bit t of
+// qh[l] as bit 4. Weight d*sc_t*q - dmin*m_t, q in 0..31; the dot is Q4_K's.
+// Unit as Q4_K's half chunks: 16 code bytes of chunk c, half h (elements
+// l = 16h .. 16h+15 of sub-blocks 2c and 2c+1), plus the header and the 16
+// qh bytes of those elements.
+// ===========================================================================
+struct Q5K : Q4K {
+  static constexpr int kType = 13, kBlockBytes = 176;
+  struct Lane : Q4K::Lane {
+    uint32_t qhoff;
+    uint32_t t0;     // sub-block of the low nibbles (2c)
+  };
+  __device__ static Lane lane(int u) {
+    Lane l;
+    const int sb = u >> 3, p = u & 7, c = p >> 1, half = p & 1;
+    l.hoff = static_cast<uint32_t>(sb * kBlockBytes);
+    l.qoff = l.hoff + 48 + 16 * p;
+    l.qhoff = l.hoff + 16 + 16 * half;
+    l.t0 = static_cast<uint32_t>(2 * c);
+    l.lo = c < 2;
+    l.sh = 16u * (c & 1);
+    l.shm = l.lo ? l.sh : l.sh + 4;
+    l.maskA = l.lo ? 0x3F3Fu : 0x0F0Fu;
+    l.maskB = l.lo ? 0u : 0x3030u;
+    return l;
+  }
+  struct Wt {
+    u32x4 qs, hdr, qh;
+  };
+  __device__ static void load_wt(Wt& w, const uint8_t* row, uint32_t extra, const Lane& l) {
+    w.hdr = ld_x4(row + (extra + l.hoff));
+    w.qs = ld_a16_x4(row + (extra + l.qoff));
+    w.qh = ld_a16_x4(row + (extra + l.qhoff));
+  }
+  __device__ static void decode(const Wt& w, Dec& o, const Lane& l) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      o.lo[k] = (w.qs[k] & 0x0F0F0F0Fu) | (((w.qh[k] >> l.t0) & 0x01010101u) << 4);
+      o.hi[k] = ((w.qs[k] >> 4) & 0x0F0F0F0Fu) | (((w.qh[k] >> (l.t0 + 1)) & 0x01010101u) << 4);
+    }
+    o.d = h2f(w.hdr.x);
+    o.dmin = h2f(w.hdr.x >> 16);
+    uint32_t mp;
+    chunk_scales(w.hdr, l, o.scp, mp);
+    o.m0 = static_cast<float>(mp & 0xFFu);
+    o.m1 = static_cast<float>((mp >> 8) & 0xFFu);
+  }
+};
+
 }  // namespace qmv

@@ -1,0 +1,12 @@
+// kernels_q5_1_f32.hip - instantiates the MMVQ kernels for the Q5_1 format with
+// fp32 activations quantized to q8_1 in the kernel prologue.
+#include "launch.hpp"
+
+namespace qmv {
+
+const Dispatch& dispatch_q5_1_f32() {
+  static const Dispatch d = make_dispatch<Q51, true>();
+  return d;
+}
+
+}  // namespace qmv

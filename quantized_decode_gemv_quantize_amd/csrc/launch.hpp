@@ -270,10 +270,18 @@ const Dispatch& dispatch_q4_0();
 const Dispatch& dispatch_q8_0();
 const Dispatch& dispatch_q4_k();
 const Dispatch& dispatch_q6_k();
+const Dispatch& dispatch_q4_1();
+const Dispatch& dispatch_q5_0();
+const Dispatch& dispatch_q5_1();
+const Dispatch& dispatch_q5_k();
 const Dispatch& dispatch_q4_0_f32();
 const Dispatch& dispatch_q8_0_f32();
 const Dispatch& dispatch_q4_k_f32();
 const Dispatch& dispatch_q6_k_f32();
+const Dispatch& dispatch_q4_1_f32();
+const Dispatch& dispatch_q5_0_f32();
+const Dispatch& dispatch_q5_1_f32();
+const Dispatch& dispatch_q5_k_f32();
 
 int launch_quantize_q8_1(const float* x, uint8_t* y, int64_t K, int64_t n, int64_t ldx, hipStream_t st);
 int launch_read_probe(const uint8_t* src, int64_t bytes, uint32_t* sink, hipStream_t st);

@@ -151,6 +151,7 @@ constexpr int rows_per_pass(int nc, int g) {
   else if (F::kType == 12 && F::kUnitsPerBlock == 4)
     r = nc == 1 ? 8 : (nc <= 4 ? 4 : 2);                                      // Q4_K whole chunks: 12 + 20n words
   else if (F::kType == 12) r = nc == 1 ? 16 : (nc <= 4 ? 8 : 4);              // Q4_K: 8 + 12n words
+  else if (F::kType == 13) r = nc == 1 ? 8 : (nc <= 4 ? 4 : 2);               // Q5_K: 12 + 12n words
   else r = nc == 1 ? 16 : (nc <= 4 ? 8 : 4);                                 // Q4_0: 5 + 10n words
   return g == 2 ? (r > 1 ? r / 2 : 1) : r;
 }

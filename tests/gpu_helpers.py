@@ -10,7 +10,8 @@ import numpy as np
 from quantized_decode_gemv_quantize_amd import binding as B
 from quantized_decode_gemv_quantize_amd import synth
 
-TNAME = {B.Q4_0: "q4_0", B.Q8_0: "q8_0", B.Q4_K: "q4_k", B.Q6_K: "q6_k"}
+TNAME = {B.Q4_0: "q4_0", B.Q8_0: "q8_0", B.Q4_K: "q4_k", B.Q6_K: "q6_k",
+         B.Q4_1: "q4_1", B.Q5_0: "q5_0", B.Q5_1: "q5_1", B.Q5_K: "q5_k"}
 
 # |gpu - oracle| <= REL * A + ABS, with A the sum of |block contributions|.
 REL, ABS = 1e-5, 1e-6

@@ -423,6 +423,38 @@ int main(int argc, char** argv) {
         case_id<Q80>("q8_0", 5, 16416, 2, T, g, xpad);
       }
   }
+  // the formats the pages name without layouts: Q4_1, Q5_0 (2-byte aligned
+  // 22-byte blocks), Q5_1, Q5_K
+  for (int64_t M : {1, 3, 17, 129})
+    for (int nb : {1, 3, 16})
+      for (int nc : {1, 2, 8})
+        for (int g = 1; g <= 2; ++g)
+          for (int xpad : {-1, 3}) {
+            case_rows<Q41>("q4_1", M, 32LL * nb * 8, nc, g, xpad);
+            case_rows<Q50>("q5_0", M, 32LL * nb, nc, g, xpad);
+            case_rows<Q50>("q5_0", M, 32LL * nb * 8 + 32, nc, g, xpad);
+            case_rows<Q51>("q5_1", M, 32LL * nb * 8, nc, g, xpad);
+            case_rows<Q5K>("q5_k", M, 256LL * nb, nc, g, xpad);
+          }
+  for (int xpad : {-1, 1})
+    for (int nc : {1, 8}) {
+      case_rows<Q50>("q5_0", 9, 16416, nc, 2, xpad);     // chunked, ragged
+      case_rows<Q41>("q4_1", 5, 32768, nc, 1, xpad);
+      case_rows<Q5K>("q5_k", 7, 16640, nc, 2, xpad);     // 520 units
+      for (int T : {1, 3, 8}) {
+        case_id<Q41>("q4_1", 77, 1024, 3, T, 2, xpad);
+        case_id<Q50>("q5_0", 33, 992, 2, T, 1, xpad);
+        case_id<Q51>("q5_1", 17, 512, 2, T, 2, xpad);
+        case_id<Q5K>("q5_k", 45, 768, 3, T, 2, xpad);
+        case_id<Q5K>("q5_k", 9, 33024, 2, T, 1, xpad);   // chunked expert rows
+      }
+    }
+  for (int64_t M : {1, 7, 33}) {
+    case_block_dots<Q41>("q4_1", M, 96, 2);
+    case_block_dots<Q50>("q5_0", M, 96, 2);
+    case_block_dots<Q51>("q5_1", M, 96, 2);
+    case_block_dots<Q5K>("q5_k", M, 512, 2);
+  }
   // many-column kernel, a few shapes of every format (the full set below)
   for (int n : {9, 33}) {
     case_mmq_all<Q4K>("q4_k", 17, 512, n);

@@ -29,8 +29,12 @@ def test_type_info():
     assert B.mmvq_type_info(B.Q4_K) == (256, 144)
     assert B.mmvq_type_info(B.Q6_K) == (256, 210)
     assert B.mmvq_type_info(B.Q8_1) == (32, 36)
+    assert B.mmvq_type_info(B.Q4_1) == (32, 20)
+    assert B.mmvq_type_info(B.Q5_0) == (32, 22)
+    assert B.mmvq_type_info(B.Q5_1) == (32, 24)
+    assert B.mmvq_type_info(B.Q5_K) == (256, 176)
     with pytest.raises(B.MMVQError) as e:
-        B.mmvq_type_info(3)
+        B.mmvq_type_info(5)
     assert e.value.code == B.ERR_TYPE
     assert B.lib().mmvq_type_info(B.Q4_K, None, None) == 0
 

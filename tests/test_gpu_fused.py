@@ -19,6 +19,7 @@ from quantized_decode_gemv_quantize_amd import synth
 pytestmark = pytest.mark.gpu
 
 Q4_0, Q8_0, Q4_K, Q6_K = B.Q4_0, B.Q8_0, B.Q4_K, B.Q6_K
+Q4_1, Q5_0, Q5_1, Q5_K = B.Q4_1, B.Q5_0, B.Q5_1, B.Q5_K
 
 
 @pytest.fixture(scope="module")
@@ -79,7 +80,11 @@ FUSED_CASES = [(Q4_0, 37, 96, 1, 0), (Q4_0, 300, 1024, 3, 5), (Q4_0, 129, 16384,
                # rows walked in chunks (ragged last chunk for 16416, 33024, 40000)
                (Q4_K, 37, 65536, 1, 0), (Q4_K, 9, 33024, 8, 3), (Q4_0, 37, 32768, 2, 1),
                (Q4_0, 5, 16416, 5, 0), (Q8_0, 17, 40000, 3, 2), (Q6_K, 17, 65792, 1, 1),
-               (Q6_K, 3, 33024, 8, 0)]
+               (Q6_K, 3, 33024, 8, 0),
+               # formats the pages name without layouts
+               (Q4_1, 37, 96, 1, 0), (Q4_1, 300, 1024, 3, 5), (Q5_0, 37, 1056, 2, 1), (Q5_0, 129, 4096, 8, 0),
+               (Q5_1, 300, 1024, 5, 3), (Q5_K, 1000, 4096, 1, 0), (Q5_K, 129, 14336, 8, 7),
+               (Q5_K, 12301, 4096, 2, 1)]
 
 
 @pytest.mark.parametrize("wtype,M,K,n,pad", FUSED_CASES,

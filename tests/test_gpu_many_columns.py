@@ -84,7 +84,9 @@ def test_many_columns_workload(O, name, n):
 
 # Beyond 8 columns the forms the matrix-core kernel does not take run as
 # groups of 8 columns through the row kernels.
-GROUPS = [(Q4_0, 37, 96, 12), (Q8_0, 300, 1056, 17), (Q6_K, 17, 768, 9), (Q4_K, 129, 4096, 20)]
+GROUPS = [(Q4_0, 37, 96, 12), (Q8_0, 300, 1056, 17), (Q6_K, 17, 768, 9), (Q4_K, 129, 4096, 20),
+          # formats without a matrix-core step: every form in column groups
+          (B.Q4_1, 37, 1024, 12), (B.Q5_0, 17, 1056, 9), (B.Q5_1, 33, 512, 20), (B.Q5_K, 65, 2048, 16)]
 
 
 @pytest.mark.parametrize("wtype,M,K,n", GROUPS, ids=[f"{TNAME[c[0]]}-{c[1]}x{c[2]}-n{c[3]}" for c in GROUPS])
@@ -101,7 +103,7 @@ def test_column_groups(O, wtype, M, K, n):
     yd = gpu_quantize(x, K)
     u, mu, _ = O.mmvq(Wu, wtype, M, K, y, n)
     g, mg, _ = O.mmvq(Wg, wtype, M, K, y, n)
-    if K % 256:
+    if K % 256 or wtype in (B.Q4_1, B.Q5_0, B.Q5_1, B.Q5_K):
         out = _nan(n, M)
         B.mmvq(dev(Wu), wtype, M, K, yd, n, out)
         assert_close(host(out), u, mu, "q8_1 column groups")

@@ -21,6 +21,7 @@ from quantized_decode_gemv_quantize_amd import synth
 pytestmark = pytest.mark.gpu
 
 Q4_0, Q8_0, Q4_K, Q6_K = B.Q4_0, B.Q8_0, B.Q4_K, B.Q6_K
+Q4_1, Q5_0, Q5_1, Q5_K = B.Q4_1, B.Q5_0, B.Q5_1, B.Q5_K
 
 
 @pytest.fixture(scope="module")
@@ -60,7 +61,9 @@ def test_quantize_bitexact(O, K, n, ldx):
 # expert kernels use at every K): K = 16640 and 32768 check its integer dots.
 DOT_CASES = [(Q4_0, 37, 96, 2), (Q4_0, 5, 1024, 1), (Q4_0, 7, 32, 3), (Q4_0, 3, 32768, 1), (Q4_K, 37, 512, 3),
              (Q4_K, 3, 4096, 1), (Q4_K, 5, 16640, 2), (Q4_K, 3, 32768, 1), (Q4_K, 2, 65536, 1), (Q6_K, 37, 768, 2),
-             (Q6_K, 9, 256, 1), (Q6_K, 3, 4096, 1), (Q8_0, 37, 96, 2), (Q8_0, 5, 1024, 1), (Q8_0, 7, 32, 3)]
+             (Q6_K, 9, 256, 1), (Q6_K, 3, 4096, 1), (Q8_0, 37, 96, 2), (Q8_0, 5, 1024, 1), (Q8_0, 7, 32, 3),
+             (Q4_1, 37, 96, 2), (Q4_1, 3, 1024, 1), (Q5_0, 37, 96, 2), (Q5_0, 5, 1056, 1), (Q5_1, 37, 96, 2),
+             (Q5_1, 3, 1024, 1), (Q5_K, 37, 512, 2), (Q5_K, 3, 4096, 1)]
 
 
 @pytest.mark.parametrize("wtype,M,K,n", DOT_CASES,
@@ -93,6 +96,11 @@ SHAPES = {
     Q4_K: [(1, 256), (37, 512), (300, 2304), (1000, 4096), (129, 14336), (65, 16384), (33, 32768),
            (37, 65536), (9, 33024)],
     Q6_K: [(1, 256), (37, 768), (300, 4096), (129, 32768), (17, 65792), (3, 33024)],
+    # formats the pages name without layouts (GGUF block definitions)
+    Q4_1: [(1, 32), (37, 96), (300, 1024), (1000, 4096), (9, 32768)],
+    Q5_0: [(1, 32), (37, 96), (300, 1056), (1000, 4096), (9, 16416)],
+    Q5_1: [(1, 32), (37, 96), (300, 1024), (1000, 4096), (5, 32768)],
+    Q5_K: [(1, 256), (37, 512), (300, 2304), (1000, 4096), (129, 14336), (7, 16640)],
 }
 GEMV_CASES = [(t, M, K, n) for t, shapes in SHAPES.items() for (M, K) in shapes
               for n in (1, 2, 3, 5, 8)]
@@ -148,7 +156,9 @@ def test_gemv_workload(O, name, n):
 GLU_CASES = [(t, M, K, n, op) for t, M, K in [(Q4_K, 300, 4096), (Q4_K, 37, 512), (Q4_0, 300, 1024),
                                                (Q6_K, 100, 4096), (Q4_K, 129, 16384), (Q8_0, 77, 2048),
                                                # rows walked in chunks
-                                               (Q4_K, 17, 65536), (Q4_0, 9, 16416), (Q6_K, 5, 33024)]
+                                               (Q4_K, 17, 65536), (Q4_0, 9, 16416), (Q6_K, 5, 33024),
+                                               (Q4_1, 77, 1024), (Q5_0, 77, 1056), (Q5_1, 77, 1024),
+                                               (Q5_K, 100, 4096)]
              for n in (1, 2, 8) for op in (B.GLU_SWIGLU, B.GLU_PLAIN)]
 
 
@@ -229,6 +239,10 @@ ID_CASES = [
     ("q4_k-E3-T3-k2-K65536", Q4_K, 3, 33, 65536, [[2, 0], [1, 2], [0, 1]]),
     ("q4_0-E2-T8-k1-K16416", Q4_0, 2, 17, 16416, [[1], [0], [1], [1], [0], [1], [0], [0]]),
     ("q6_k-E2-T2-k2-K33024", Q6_K, 2, 9, 33024, [[1, 0], [0, 1]]),
+    ("q4_1-E4-T3-k2", Q4_1, 4, 77, 1024, [[2, 0], [1, 2], [2, 3]]),
+    ("q5_0-E3-T4-k2", Q5_0, 3, 45, 1056, [[2, 0], [1, 2], [0, 1], [2, 1]]),
+    ("q5_1-E3-T5-k3", Q5_1, 3, 64, 512, [[0, 1, 2], [2, 1, 0], [1, 0, 2], [0, 2, 1], [2, 0, 1]]),
+    ("q5_k-E8-T8-k2", Q5_K, 8, 129, 2048, "random"),
 ]
 
 
@@ -269,7 +283,7 @@ def test_abi_errors_on_device():
     assert L.mmvq(p, Q4_K, 1, 256, q, 0, o, s) == B.ERR_SHAPE
     assert L.mmvq(p, Q4_K, 1, 256, q, 257, o, s) == B.ERR_SHAPE
     assert L.mmvq(p, Q4_K, 0, 256, q, 1, o, s) == B.ERR_SHAPE
-    assert L.mmvq(p, 3, 1, 256, q, 1, o, s) == B.ERR_TYPE
+    assert L.mmvq(p, 5, 1, 256, q, 1, o, s) == B.ERR_TYPE      # id 5: retired
     assert L.mmvq_glu(p, p, Q4_K, 1, 256, q, 1, 7, o, s) == B.ERR_TYPE
     ids = torch.zeros(16, dtype=torch.int32, device="cuda:0")
     assert L.mmvq_id(p, 144, 4, Q4_K, 2, 256, q, 1, ids.data_ptr(), 1, o, s) == B.ERR_SHAPE  # stride < M*row
