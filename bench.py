@@ -798,7 +798,8 @@ def main():
 
     if args.all:
         for name in ["q4_0_256x1024", "q4_k_4096x4096", "q4_k_4096x14336", "q4_k_14336x4096",
-                     "q6_k_128256x4096", "q8_0_4096x14336"]:
+                     "q6_k_128256x4096", "q8_0_4096x14336", "q4_1_4096x14336", "q5_0_4096x14336",
+                     "q5_1_4096x14336", "q5_k_4096x14336"]:
             w = synth.BY_NAME[name]
             many = ((16, 32, 64, 128) if name in ("q4_k_4096x14336", "q4_k_14336x4096")
                     else (16, 64) if name in ("q6_k_128256x4096", "q8_0_4096x14336") else ())

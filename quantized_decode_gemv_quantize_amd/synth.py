@@ -45,6 +45,10 @@ q4_k_4096x14336        Q4_K    4096   14336  1..8   FFN down (headline)
 q6_k_128256x4096       Q6_K    128256 4096   1      LM head
 moe_q4_k_8x14336x4096  Q4_K    14336  4096   8 tok  8 experts, top-2, gate+up
 q8_0_4096x14336        Q8_0    4096   14336  1      FFN down, 8-bit weights
+q4_1_4096x14336        Q4_1    4096   14336  1      FFN down, other formats:
+q5_0_4096x14336        Q5_0    4096   14336  1      Q4_1, Q5_0, Q5_1, Q5_K
+q5_1_4096x14336        Q5_1    4096   14336  1
+q5_k_4096x14336        Q5_K    4096   14336  1
 =====================  ======  =====  =====  =====  ===========================
 
 Seeds: ``seed = 1000 + workload index``; independent sub-streams are spawned
@@ -102,8 +106,12 @@ WORKLOADS = [
     Workload(3, "q6_k_128256x4096", Q6_K, 128256, 4096, (1,)),
     Workload(4, "moe_q4_k_8x14336x4096", Q4_K, 14336, 4096, (8,), n_experts=8, top_k=2,
              glu=True),
-    # an extra format at the FFN-down shape (not one of the reference configs)
+    # the other formats at the FFN-down shape (not among the reference configs)
     Workload(5, "q8_0_4096x14336", Q8_0, 4096, 14336, (1,)),
+    Workload(6, "q4_1_4096x14336", Q4_1, 4096, 14336, (1,)),
+    Workload(7, "q5_0_4096x14336", Q5_0, 4096, 14336, (1,)),
+    Workload(8, "q5_1_4096x14336", Q5_1, 4096, 14336, (1,)),
+    Workload(9, "q5_k_4096x14336", Q5_K, 4096, 14336, (1,)),
 ]
 # The transposed FFN shape shares workload 2's seed and generator.
 FFN_UP = Workload(2, "q4_k_14336x4096", Q4_K, 14336, 4096, (1, 2, 4, 8))

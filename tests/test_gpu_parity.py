@@ -133,7 +133,8 @@ FULL = [("q4_0_256x1024", 1), ("q4_k_4096x4096", 1), ("q4_k_4096x14336", 1),
         ("q4_k_4096x14336", 2), ("q4_k_4096x14336", 4), ("q4_k_4096x14336", 8),
         ("q4_k_14336x4096", 1), ("q4_k_14336x4096", 2), ("q4_k_14336x4096", 4),
         ("q4_k_14336x4096", 8), ("q6_k_128256x4096", 1), ("q6_k_128256x4096", 2),
-        ("q8_0_4096x14336", 1)]
+        ("q8_0_4096x14336", 1), ("q4_1_4096x14336", 1), ("q5_0_4096x14336", 1), ("q5_1_4096x14336", 1),
+        ("q5_k_4096x14336", 1)]
 
 
 @pytest.mark.parametrize("name,n", FULL, ids=[f"{a}-n{b}" for a, b in FULL])
