@@ -363,12 +363,12 @@ static void block_q8_0(const uint8_t *blk, const uint8_t *ycol, int64_t qb,
     if (dots) dots[0] = isum;
 }
 
-/* Q4_K: per sub-block t, dot1 = sum q*qy, dot2 = sum qy over its 32
- * elements; contribution d*sc*d8*dot1 - dmin*m*d8*dot2, the min term kept
- * apart [MMVQ §一次 vec_dot 的解剖]. Sub-block t pairs with q8_1 block
- * qb + t. */
-static void block_q4_k(const uint8_t *blk, const uint8_t *ycol, int64_t qb,
-                       double *acc, double *mag, int32_t *dots) {
+/* Q4_K (and Q5_K, whose codes come from another code function): per
+ * sub-block t, dot1 = sum q*qy, dot2 = sum qy over its 32 elements;
+ * contribution d*sc*d8*dot1 - dmin*m*d8*dot2, the min term kept apart
+ * [MMVQ §一次 vec_dot 的解剖]. Sub-block t pairs with q8_1 block qb + t. */
+static void block_k_min(const uint8_t *blk, const uint8_t *ycol, int64_t qb, double *acc, double *mag,
+                        int32_t *dots, int (*code)(const uint8_t *, int)) {
     const double d = orc_f16_to_f64(rd16(blk));
     const double dmin = orc_f16_to_f64(rd16(blk + 2));
     for (int t = 0; t < 8; ++t) {
@@ -376,7 +376,7 @@ static void block_q4_k(const uint8_t *blk, const uint8_t *ycol, int64_t qb,
         orc_q4_k_scale_min(blk + 4, t, &sc, &m);
         for (int l = 0; l < 32; ++l) {
             const int qy = q8_q(ycol, qb + t, l);
-            dot1 += q4_k_code(blk, 32 * t + l) * qy;
+            dot1 += code(blk, 32 * t + l) * qy;
             dot2 += qy;
         }
         const double d8 = q8_d(ycol, qb + t);
@@ -388,27 +388,16 @@ static void block_q4_k(const uint8_t *blk, const uint8_t *ycol, int64_t qb,
     }
 }
 
+static void block_q4_k(const uint8_t *blk, const uint8_t *ycol, int64_t qb,
+                       double *acc, double *mag, int32_t *dots) {
+    block_k_min(blk, ycol, qb, acc, mag, dots, q4_k_code);
+}
+
 /* Q5_K: as Q4_K with the 5-bit codes: per sub-block t, dot1 = sum q*qy,
  * dot2 = sum qy; contribution d*sc*d8*dot1 - dmin*m*d8*dot2. */
 static void block_q5_k(const uint8_t *blk, const uint8_t *ycol, int64_t qb,
                        double *acc, double *mag, int32_t *dots) {
-    const double d = orc_f16_to_f64(rd16(blk));
-    const double dmin = orc_f16_to_f64(rd16(blk + 2));
-    for (int t = 0; t < 8; ++t) {
-        int sc, m, dot1 = 0, dot2 = 0;
-        orc_q4_k_scale_min(blk + 4, t, &sc, &m);
-        for (int l = 0; l < 32; ++l) {
-            const int qy = q8_q(ycol, qb + t, l);
-            dot1 += q5_k_code(blk, 32 * t + l) * qy;
-            dot2 += qy;
-        }
-        const double d8 = q8_d(ycol, qb + t);
-        const double t1 = d * sc * d8 * dot1;
-        const double t2 = dmin * m * d8 * dot2;
-        *acc += t1 - t2;
-        *mag += fabs(t1) + fabs(t2);
-        if (dots) { dots[t] = dot1; dots[8 + t] = dot2; }
-    }
+    block_k_min(blk, ycol, qb, acc, mag, dots, q5_k_code);
 }
 
 /* Q6_K: per sub-block s of 16, isum_s = sum (q - 32)*qy; contribution

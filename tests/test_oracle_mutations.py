@@ -21,8 +21,8 @@ MUTATIONS = {
                                "(int)roundf(xb[i] / (float)orc_f16_to_f64(orc_f32_to_f16(d)))"),
     "q8_1_scale_128": ("const float d = amax / 127.0f;", "const float d = amax / 128.0f;"),
     "f16_ties_up": ("return fmod(fl, 2.0) == 0.0 ? fl : fl + 1.0;", "return fl + 1.0;"),
-    "q4_0_nibbles_swapped": ("return e < 16 ? (qs[e] & 0x0F) : (qs[e - 16] >> 4);",
-                             "return e < 16 ? (qs[e] >> 4) : (qs[e - 16] & 0x0F);"),
+    "q4_0_nibbles_swapped": ("const uint8_t *qs = blk + 2;\n    return e < 16 ? (qs[e] & 0x0F) : (qs[e - 16] >> 4);",
+                             "const uint8_t *qs = blk + 2;\n    return e < 16 ? (qs[e] >> 4) : (qs[e - 16] & 0x0F);"),
     "q4_0_zero_point_7": ("const double t2 = 8.0 * dw * q8_s(ycol, qb);",
                           "const double t2 = 7.0 * dw * q8_s(ycol, qb);"),
     "q4_0_no_zero_point": ("const double t2 = 8.0 * dw * q8_s(ycol, qb);",
@@ -36,8 +36,8 @@ MUTATIONS = {
     "q4_k_min_low_bits_from_scale_byte": ("*m = B[t + 4] & 63;", "*m = B[t] & 63;"),
     "q4_k_nibble_parity_swapped": ("return (t % 2 == 0) ? (byte & 0x0F) : (byte >> 4);",
                                    "return (t % 2 == 1) ? (byte & 0x0F) : (byte >> 4);"),
-    "q4_k_chunk_index": ("const uint8_t byte = qs[32 * c + l];",
-                         "const uint8_t byte = qs[32 * (t % 4) + l];"),
+    "q4_k_chunk_index": ("blk + 16;\n    const int t = e / 32, l = e % 32, c = t / 2;\n    const uint8_t byte = qs[32 * c + l];",
+                         "blk + 16;\n    const int t = e / 32, l = e % 32, c = t / 2;\n    const uint8_t byte = qs[32 * (t % 4) + l];"),
     "q4_k_wrong_q8_block": ("const int qy = q8_q(ycol, qb + t, l);",
                             "const int qy = q8_q(ycol, qb + (t ^ 1), l);"),
     "q4_k_field_order": ("const uint8_t *qs = blk + 16;\n    const int t = e / 32",
