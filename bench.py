@@ -87,7 +87,10 @@ HEADLINE_SOURCES = ["common.hpp", "q8.hpp", "formats.hpp", "plan.hpp", "mmvq_ker
 ALL_SOURCES = HEADLINE_SOURCES + ["mmq_plan.hpp", "mmq_kernel.hpp", "kernels_mmq.hip", "kernels_q4_0.hip",
                                   "kernels_q4_0_f32.hip", "kernels_q8_0.hip", "kernels_q8_0_f32.hip",
                                   "kernels_q6_k.hip", "kernels_q6_k_f32.hip", "kernels_q4_k_id.hip",
-                                  "kernels_q4_k_f32_id.hip", "quantize.hip", "probe.hip", "api.hip"]
+                                  "kernels_q4_k_f32_id.hip", "kernels_q4_1.hip", "kernels_q4_1_f32.hip",
+                                  "kernels_q5_0.hip", "kernels_q5_0_f32.hip", "kernels_q5_1.hip",
+                                  "kernels_q5_1_f32.hip", "kernels_q5_k.hip", "kernels_q5_k_f32.hip",
+                                  "quantize.hip", "probe.hip", "api.hip"]
 
 
 def kernel_source_hash(names=None) -> str:
@@ -802,7 +805,7 @@ def main():
                      "q5_1_4096x14336", "q5_k_4096x14336"]:
             w = synth.BY_NAME[name]
             many = ((16, 32, 64, 128) if name in ("q4_k_4096x14336", "q4_k_14336x4096")
-                    else (16, 64) if name in ("q6_k_128256x4096", "q8_0_4096x14336") else ())
+                    else (16, 64) if name in ("q6_k_128256x4096", "q8_0_4096x14336") else (16,))
             for nn in tuple(w.n if name != "q4_k_4096x14336" else (1, 2, 4, 8)) + many:
                 r, *_ = time_workload(torch, B, w, nn, 500, 50)
                 gb = algorithmic_bytes(w, nn) / (r["gemv_us"] * 1e-6) / 1e9

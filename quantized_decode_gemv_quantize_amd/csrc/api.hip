@@ -101,10 +101,12 @@ mmvq_epilogue glu_only(int glu_op) {
   return e;
 }
 
-// Formats the matrix-core kernel takes (the others run more than
-// MMVQ_MAX_COLS columns as column groups through the row kernels).
+// Formats the matrix-core kernel takes: all of them (the forms it does not
+// take run more than MMVQ_MAX_COLS columns as column groups through the row
+// kernels).
 bool mmq_type(int type) {
-  return type == MMVQ_Q4_K || type == MMVQ_Q6_K || type == MMVQ_Q4_0 || type == MMVQ_Q8_0;
+  return type == MMVQ_Q4_K || type == MMVQ_Q6_K || type == MMVQ_Q4_0 || type == MMVQ_Q8_0 || type == MMVQ_Q4_1 ||
+         type == MMVQ_Q5_0 || type == MMVQ_Q5_1 || type == MMVQ_Q5_K;
 }
 
 // Many columns (up to MMVQ_MAX_COLS_BATCH): the MFMA kernel, q8_1

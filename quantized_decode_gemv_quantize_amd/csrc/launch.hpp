@@ -110,7 +110,7 @@ inline int launch_rows_nc(RowArgs a, int64_t K, hipStream_t st) {
   if (const char* e = getenv("MMVQ_FORCE_ROWS")) force = atoi(e);
 #endif
   Shape s = plan_launch(a.M, units_per_row<F>(K), launch_max_rows<F>(XF, NC, G), device_cus(),
-                        launch_max_passes<F>(XF, NC, G), XF, NC, force, layout_pipelined<F>());
+                        launch_max_passes<F>(XF, NC, G), XF, NC, force, layout_depth_cap<F>());
 #ifdef QMV_TUNING
   if (const char* e = getenv("MMVQ_DEPTH")) s.depth = XF ? atoi(e) : 0;
 #endif

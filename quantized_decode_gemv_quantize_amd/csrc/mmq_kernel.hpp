@@ -1,6 +1,6 @@
 // mmq_kernel.hpp - the many-column path (more activation columns than the
-// mat-vec kernels take at their best) for Q4_K, Q6_K, Q4_0 and Q8_0 weights:
-// int8 matrix-core (MFMA) products of 16x16 tiles.
+// mat-vec kernels take at their best) for every weight format: int8
+// matrix-core (MFMA) products of 16x16 tiles.
 //
 // Citations: [MMVQ §X] = page "llama.cpp 源码完全拆解(十四):mul_mat_vec_q——解码时
 // 一条量化权重如何被 dp4a 逐块点积", section X.
@@ -17,8 +17,13 @@
 //   Q4_K: out += d * sum_t sc_t*C_t*d8_t - dmin * sum_t m_t*(d8_t*S_t)
 //         (sc_t*C_t exact below 2^22; the min term, a contraction over the 8
 //         sub-blocks, is two fp32 MFMAs per tile and step)
+//   Q5_K: as Q4_K with codes 0..31 (bit 4 from qh)
 //   Q4_0: out += sum_t d_t*(d8_t*C_t - 8*s_t)      (codes 0..15; s_t the
 //         q8_1 block's stored fp16 d8*sum(q), as the mat-vec uses it)
+//   Q5_0: out += sum_t d_t*(d8_t*C_t - 16*s_t)     (codes 0..31)
+//   Q4_1, Q5_1: out += sum_t d_t*d8_t*C_t + sum_t m_t*s_t (codes 0..15 /
+//         0..31; the min term a contraction over the 8 blocks, two fp32
+//         MFMAs per tile and step)
 //   Q8_0: out += sum_t d_t*d8_t*C_t                (signed codes)
 //   Q6_K: out += d * sum_t d8_t*(sc_2t*(C_t,lo - 32*S_t,lo) + sc_2t+1*(C_t,hi - 32*S_t,hi))
 //         (codes 0..63; the 16-element sub-blocks 2t and 2t+1 are the two
@@ -98,7 +103,11 @@ template <int RT> struct MmqRowLds<Q4K, RT> {
   uint8_t sc[RT][4][16][2];        // sc_t of row, t = 2c + h at [c][row][h]
   float d[RT][16];                 // d of row
 };
+template <int RT> struct MmqRowLds<Q5K, RT> : MmqRowLds<Q4K, RT> {};
 template <int RT> struct MmqRowLds<Q40, RT> { float d[RT][8][16]; };   // d of block t of row
+template <int RT> struct MmqRowLds<Q41, RT> { float d[RT][8][16]; };
+template <int RT> struct MmqRowLds<Q50, RT> { float d[RT][8][16]; };
+template <int RT> struct MmqRowLds<Q51, RT> { float d[RT][8][16]; };
 template <int RT> struct MmqRowLds<Q80, RT> { float d[RT][8][16]; };
 template <int RT> struct MmqRowLds<Q6K, RT> {
   int8_t sc[RT][16][16];           // scale of sub-block s of row at [s][row]
@@ -137,13 +146,16 @@ struct MmqRows {
 // (row 4q+i of row tile rt, column r16 of column tile ct).
 template <class F> struct MmqStep;
 
-// Q4_K. Lane (r16, q) unpacks sub-blocks 2q and 2q+1 of row r16: the f32 A
-// operand of the min term (k = q stands for t = 2q in the even product,
-// t = 2q+1 in the odd one) and the scales, which the D layout reads back per
-// chunk for rows 4q..4q+3.
-template <> struct MmqStep<Q4K> {
+// Q4_K and Q5_K (header of Q4_K at step byte 0, the codes of chunk c at
+// QS + 32c; Q5_K: qh[32] at byte 16, bit t of qh[l] the fifth bit of element
+// l of sub-block t). Lane (r16, q) unpacks sub-blocks 2q and 2q+1 of row
+// r16: the f32 A operand of the min term (k = q stands for t = 2q in the
+// even product, t = 2q+1 in the odd one) and the scales, which the D layout
+// reads back per chunk for rows 4q..4q+3.
+template <class F, int QS, bool HB>
+struct MmqStepK {
   template <int RT, int CT>
-  __device__ static void run(MmqWaveLds<Q4K, RT, CT>& lds, const MmqRows&, int, int lane,
+  __device__ static void run(MmqWaveLds<F, RT, CT>& lds, const MmqRows&, int, int lane,
                              float (&acc)[RT][CT][4]) {
     const int r16 = lane & 15, q = lane >> 4;
     const Q4K::Lane L = Q4K::lane(2 * q);       // scale unpack of chunk q (sub-blocks 2q, 2q+1)
@@ -171,6 +183,13 @@ template <> struct MmqStep<Q4K> {
         for (int i = 0; i < 4; ++i) accd[rt][ct][i] = 0.0f;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) e[ct][0] = e[ct][1] = 0.0f;
+    // fifth bits of elements 8q..8q+7 (the same bytes for every chunk)
+    u32x2 qh[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      qh[rt].x = qh[rt].y = 0u;
+      if constexpr (HB) qh[rt] = *reinterpret_cast<const u32x2*>(&lds.a[rt][r16][16 + 8 * q]);
+    }
     // sub-blocks 2c and 2c+1 share the code bytes of chunk c (low and high
     // nibbles); the chunk loop is kept rolled so only one chunk's operands
     // are live
@@ -179,7 +198,7 @@ template <> struct MmqStep<Q4K> {
       u32x2 w[RT], scw[RT];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        w[rt] = *reinterpret_cast<const u32x2*>(&lds.a[rt][r16][16 + 32 * c + 8 * q]);
+        w[rt] = *reinterpret_cast<const u32x2*>(&lds.a[rt][r16][QS + 32 * c + 8 * q]);
         scw[rt] = *reinterpret_cast<const u32x2*>(&lds.x.sc[rt][c][4 * q][0]);
       }
 #pragma unroll
@@ -189,7 +208,12 @@ template <> struct MmqStep<Q4K> {
         int sc[RT][4];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-          A[rt] = pack2((w[rt].x >> (4 * h)) & 0x0F0F0F0Fu, (w[rt].y >> (4 * h)) & 0x0F0F0F0Fu);
+          uint32_t lo = (w[rt].x >> (4 * h)) & 0x0F0F0F0Fu, hi = (w[rt].y >> (4 * h)) & 0x0F0F0F0Fu;
+          if constexpr (HB) {
+            lo |= ((qh[rt].x >> t) & 0x01010101u) << 4;
+            hi |= ((qh[rt].y >> t) & 0x01010101u) << 4;
+          }
+          A[rt] = pack2(lo, hi);
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             sc[rt][i] = static_cast<int>(((i < 2 ? scw[rt].x : scw[rt].y) >> (8 * (2 * (i & 1) + h))) & 0xFFu);
@@ -236,42 +260,68 @@ template <> struct MmqStep<Q4K> {
   }
 };
 
-// Q4_0 and Q8_0: one fp16 scale per 32-weight block t (block at byte BB*t of
-// the step, codes 2 bytes in). Lane (r16, q) converts the scales of blocks
-// 2q and 2q+1 of row r16 for the D layout. Q4_0: byte j of the codes holds
-// element j (low nibble) and j + 16 (high), so k-slice q reads bytes
-// 8*(q&1) .. +7 and takes nibble q>>1; codes 0..15 with the -8 offset taken
-// from the q8_1 block's s (its fp16 d8*sum(q)), as in the mat-vec. Q8_0:
-// k-slice q reads code bytes 8q .. 8q+7 as they are.
-template <class F, int BB, bool NIBBLES>
+template <> struct MmqStep<Q4K> : MmqStepK<Q4K, 16, false> {};
+template <> struct MmqStep<Q5K> : MmqStepK<Q5K, 48, true> {};
+
+// The 32-weight block formats: one fp16 scale d per block t (block at byte
+// BB*t of the step, its codes CO bytes in). Lane (r16, q) converts the
+// scales of blocks 2q and 2q+1 of row r16 for the D layout. Nibble formats:
+// byte j of the codes holds element j (low nibble) and j + 16 (high), so
+// k-slice q reads bytes 8*(q&1) .. +7 and takes nibble q>>1; with QH >= 0
+// the 32-bit word at block byte QH holds the fifth bit of element e at bit
+// e, so k-slice q (elements 8q .. 8q+7) takes byte q of it. ZP: the zero
+// point as a multiple of the q8_1 block's stored s (its fp16 d8*sum(q)), as
+// in the mat-vec: Q4_0 -8, Q5_0 -16. MIN: Q4_1 / Q5_1, the fp16 min m at
+// block byte 2 times s, summed over the 8 blocks of the step by two fp32
+// MFMAs per tile (lane (r16, q) supplies m of blocks 2q + h of row r16 and s
+// of blocks 2q + h of column r16). Q8_0: k-slice q reads code bytes
+// 8q .. 8q+7 as they are.
+template <class F, int BB, int CO, bool NIBBLES, int QH, int ZP, bool MIN>
 struct MmqStepBlocks {
   template <int RT, int CT>
   __device__ static void run(MmqWaveLds<F, RT, CT>& lds, const MmqRows&, int, int lane, float (&acc)[RT][CT][4]) {
     const int r16 = lane & 15, q = lane >> 4;
+    float am[RT][2], e[CT][2];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int t = 2 * q + h;
         lds.x.d[rt][t][r16] = h2f(*reinterpret_cast<const uint16_t*>(&lds.a[rt][r16][BB * t]));
+        am[rt][h] = MIN ? h2f(*reinterpret_cast<const uint16_t*>(&lds.a[rt][r16][BB * t + 2])) : 0.0f;
       }
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        e[ct][h] = MIN ? h2f(*reinterpret_cast<const uint16_t*>(&lds.b[ct][r16][36 * (2 * q + h) + 2])) : 0.0f;
     mmq_lds_fence();
     const int nib = 4 * (q >> 1);
     static_for<0, 8>([&](auto tc) QMV_INLINE {
       constexpr int t = decltype(tc)::value;
       // code bytes of this lane in block t: 2-byte aligned, misaligned by a
-      // compile-time 0 or 2 bytes from a dword (BB even; 8*(q&1) and 8q are
-      // multiples of 4)
-      constexpr int kMis = (BB * t + 2) % 4;
+      // compile-time 0 or 2 bytes from a dword (BB and CO even; 8*(q&1) and
+      // 8q are multiples of 4)
+      constexpr int kMis = (BB * t + CO) % 4;
       long A[RT];
       float dw[RT][4];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        const uint8_t* p = &lds.a[rt][r16][BB * t + 2 + (NIBBLES ? 8 * (q & 1) : 8 * q)];
+        const uint8_t* p = &lds.a[rt][r16][BB * t + CO + (NIBBLES ? 8 * (q & 1) : 8 * q)];
         const long raw = lds8<kMis>(p);
         if constexpr (NIBBLES) {
-          const uint32_t lo = static_cast<uint32_t>(raw), hi = static_cast<uint32_t>(static_cast<uint64_t>(raw) >> 32);
-          A[rt] = pack2((lo >> nib) & 0x0F0F0F0Fu, (hi >> nib) & 0x0F0F0F0Fu);
+          uint32_t lo = static_cast<uint32_t>(raw), hi = static_cast<uint32_t>(static_cast<uint64_t>(raw) >> 32);
+          lo = (lo >> nib) & 0x0F0F0F0Fu;
+          hi = (hi >> nib) & 0x0F0F0F0Fu;
+          if constexpr (QH >= 0) {
+            // bit i of the byte goes to bit 4 of byte i (4 bits per word:
+            // the multiply places bit i at bit 8i, the partial products do
+            // not overlap)
+            const uint32_t b = lds.a[rt][r16][BB * t + QH + q];
+            lo |= (((b & 0xFu) * 0x00204081u) & 0x01010101u) << 4;
+            hi |= (((b >> 4) * 0x00204081u) & 0x01010101u) << 4;
+          }
+          A[rt] = pack2(lo, hi);
         } else {
           A[rt] = raw;
         }
@@ -279,15 +329,16 @@ struct MmqStepBlocks {
         dw[rt][0] = dv.x; dw[rt][1] = dv.y; dw[rt][2] = dv.z; dw[rt][3] = dv.w;
       }
       v4i C[RT][CT];
-      float d8[CT], m8s[CT];
+      float d8[CT], zs[CT];
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
         const long B = b_operand<CT>(lds.b, ct, r16, q, t, d8[ct]);
         const v4i zero = {0, 0, 0, 0};
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) C[rt][ct] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A[rt], B, zero, 0, 0, 0);
-        m8s[ct] = 0.0f;
-        if constexpr (NIBBLES) m8s[ct] = -8.0f * h2f(*reinterpret_cast<const uint16_t*>(&lds.b[ct][r16][36 * t + 2]));
+        zs[ct] = 0.0f;
+        if constexpr (ZP != 0)
+          zs[ct] = static_cast<float>(ZP) * h2f(*reinterpret_cast<const uint16_t*>(&lds.b[ct][r16][36 * t + 2]));
       }
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
@@ -295,12 +346,30 @@ struct MmqStepBlocks {
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            acc[rt][ct][i] = fmaf(fmaf(static_cast<float>(C[rt][ct][i]), d8[ct], m8s[ct]), dw[rt][i], acc[rt][ct][i]);
+            acc[rt][ct][i] = fmaf(fmaf(static_cast<float>(C[rt][ct][i]), d8[ct], zs[ct]), dw[rt][i], acc[rt][ct][i]);
     });
+    if constexpr (MIN) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          v4f v;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = acc[rt][ct][i];
+          v = __builtin_amdgcn_mfma_f32_16x16x4f32(am[rt][0], e[ct][0], v, 0, 0, 0);
+          v = __builtin_amdgcn_mfma_f32_16x16x4f32(am[rt][1], e[ct][1], v, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[rt][ct][i] = v[i];
+        }
+    }
   }
 };
-template <> struct MmqStep<Q40> : MmqStepBlocks<Q40, 18, true> {};
-template <> struct MmqStep<Q80> : MmqStepBlocks<Q80, 34, false> {};
+//                                                   BB  CO  NIB    QH  ZP   MIN
+template <> struct MmqStep<Q40> : MmqStepBlocks<Q40, 18, 2, true, -1, -8, false> {};
+template <> struct MmqStep<Q41> : MmqStepBlocks<Q41, 20, 4, true, -1, 0, true> {};
+template <> struct MmqStep<Q50> : MmqStepBlocks<Q50, 22, 6, true, 2, -16, false> {};
+template <> struct MmqStep<Q51> : MmqStepBlocks<Q51, 24, 8, true, 4, 0, true> {};
+template <> struct MmqStep<Q80> : MmqStepBlocks<Q80, 34, 2, false, -1, 0, false> {};
 
 // Q6_K super-block at image byte base = 16 - delta of each row (delta per
 // row and step): ql[128] @0, qh[64] @128, int8 sc[16] @192, fp16 d @208.
@@ -439,7 +508,8 @@ __global__ void __launch_bounds__(NW * kWave, 8 / NW) mmq_kernel(MmqArgs a) {
   // Pipeline: the staging loads of step sb+1 are in flight while sb is
   // computed from LDS. The prefetch is unconditional (past the end it
   // re-reads the last step, from cache) so every path has the same loads in
-  // flight.
+  // flight. (Two steps in flight, in a second register buffer, measured
+  // slower at 16 columns: 16.3 -> 17.3 us at 4096x14336.)
   if (sb0 < sb1) {
     mmq_offsets<F, RT, CT>(a, row_base, col_base, lane, off);
     MmqStage<F, RT, CT> st;

@@ -26,8 +26,9 @@ struct MmqArgs {
 // Staging geometry of a weight format: a staging step covers 256 weights of
 // a row (the 8 q8_1 blocks of one step of the activation), kStride bytes of
 // the row, staged with kRowPieces loads per row into a kRowLds-byte row
-// image in LDS. Formats whose steps are 16-byte multiples (Q4_K 144, Q4_0
-// 8 x 18 = 144, Q8_0 8 x 34 = 272 bytes) stage them as 16-byte pieces at
+// image in LDS. Formats whose steps are 16-byte multiples (Q4_K 144, Q5_K
+// 176, Q4_0 8 x 18 = 144, Q4_1 8 x 20 = 160, Q5_0 8 x 22 = 176, Q5_1
+// 8 x 24 = 192, Q8_0 8 x 34 = 272 bytes) stage them as 16-byte pieces at
 // 16-byte aligned addresses; step byte y sits at image byte y.
 template <class F> struct MmqGeom;
 template <int STRIDE>
@@ -43,6 +44,10 @@ struct MmqGeomAligned {
 template <> struct MmqGeom<Q4K> : MmqGeomAligned<144> {};
 template <> struct MmqGeom<Q40> : MmqGeomAligned<144> {};
 template <> struct MmqGeom<Q80> : MmqGeomAligned<272> {};
+template <> struct MmqGeom<Q41> : MmqGeomAligned<160> {};
+template <> struct MmqGeom<Q50> : MmqGeomAligned<176> {};
+template <> struct MmqGeom<Q51> : MmqGeomAligned<192> {};
+template <> struct MmqGeom<Q5K> : MmqGeomAligned<176> {};
 // Q6_K super-blocks (210 bytes) are only 2-byte aligned. As in the row
 // kernels every load stays inside its super-block: 13 sixteen-byte runs at
 // the first dword-aligned byte s' = s + delta (delta = 0 or 2) plus the one

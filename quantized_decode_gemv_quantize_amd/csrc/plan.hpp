@@ -96,12 +96,14 @@ inline Shape plan_rows(int64_t M, int units, int rmax, int64_t cus, int target_w
 // 2 waves per CU: depth 8). With many waves per CU (the Q6_K LM head: 62)
 // the hardware already overlaps the waves' loads and arithmetic and the
 // shallower queue only costs (84.5 -> 95.5 us), as it did for Q8_0
-// 4096x14336 (14.7 -> 16.2 us). Instantiated depths: 4 and 8.
-inline int plan_depth(const Shape& s, int64_t cus, bool pays = true) {
-  if (!pays || s.passes != 1 || s.rows < 8) return 0;
+// 4096x14336 (14.7 -> 16.2 us). max_per_cu: the most waves per CU at which
+// the layout pipelines (layout_depth_cap; 0: never). Instantiated depths: 4
+// and 8.
+inline int plan_depth(const Shape& s, int64_t cus, int max_per_cu) {
+  if (max_per_cu <= 0 || s.passes != 1 || s.rows < 8) return 0;
   const int64_t waves = s.teams * (s.team_lanes / kWave);
   const int64_t per_cu = (waves + cus - 1) / cus;
-  if (per_cu > 8) return 0;
+  if (per_cu > max_per_cu) return 0;
   const int d = per_cu >= 5 ? 4 : 8;
   return d < s.rows ? d : 0;
 }
@@ -118,30 +120,38 @@ inline Shape spread_teams(Shape s, int64_t cus) {
 }
 
 // Shape of a rows-kernel launch: plan_rows; for the fp32-activation forms of
-// a pipelined layout (layout_pipelined), at one column the most rows per team
-// that still leaves a team per CU (each team quantizes the whole activation;
-// 4096x4096 Q4_K: 4 rows per team 5.42 us, 16 rows at depth 8: 4.82), and
-// the pipelined rows of plan_depth for every single-pass launch.
+// a pipelined layout (depth_cap = layout_depth_cap > 0), at one column the
+// most rows per team that still leaves a team per CU (each team quantizes
+// the whole activation; 4096x4096 Q4_K: 4 rows per team 5.42 us, 16 rows at
+// depth 8: 4.82), and the pipelined rows of plan_depth for every
+// single-pass launch.
 inline Shape plan_launch(int64_t M, int units, int rmax, int64_t cus, int max_passes, bool xf, int nc,
-                         int64_t force_rows = 0, bool pipelined = true) {
+                         int64_t force_rows, int depth_cap) {
   Shape s = plan_rows(M, units, rmax, cus, QMV_TARGET_WAVES_PER_CU, force_rows, max_passes);
-  if (xf && pipelined) {
+  if (xf && depth_cap > 0) {
     if (nc == 1 && s.passes == 1 && force_rows == 0) {
       const int64_t per_cu = M / (cus * s.slots);
       const Shape t = plan_rows(M, units, rmax, cus, QMV_TARGET_WAVES_PER_CU, per_cu > 0 ? per_cu : 1, 1);
       if (t.rows > s.rows) s = t;
     }
-    s.depth = plan_depth(s, cus);
+    s.depth = plan_depth(s, cus, depth_cap);
   }
   return spread_teams(s, cus);
 }
 
-// Lane layouts whose fp32-activation launches take pipelined rows: the
-// half-chunk Q4_K layout (measured); the others keep every row issued first.
+// Lane layouts whose fp32-activation launches take pipelined rows, where
+// measured faster, and up to how many waves per CU: the half-chunk Q4_K
+// layout (8, above), Q4_1, Q5_1 and Q5_K (16; at 4096x14336, one column:
+// Q4_1 9.82 -> 9.62 us at 7 waves per CU, Q5_1 12.08 -> 10.68 at 7, Q5_K
+// 13.82 -> 11.92 at 14). The others keep every row issued first (Q5_0
+// measured slower pipelined: 13.4 -> 16.0 us; Q8_0 and Q6_K see plan_depth).
 template <class F>
-constexpr bool layout_pipelined() {
-  return F::kType == 12 && F::kUnitsPerBlock == 8;
+constexpr int layout_depth_cap() {
+  if (F::kType == 12 && F::kUnitsPerBlock == 8) return 8;
+  return (F::kType == 3 || F::kType == 7 || F::kType == 13) ? 16 : 0;
 }
+template <class F>
+constexpr bool layout_pipelined() { return layout_depth_cap<F>() > 0; }
 
 // Largest rows per slot (register budget) of an instantiation.
 template <class F>
@@ -157,15 +167,18 @@ constexpr int rows_per_pass(int nc, int g) {
 }
 
 // Most rows per slot a mat-vec launch uses: the register budget, except the
-// plain half-chunk Q4_K and the Q8_0 mat-vec at one q8_1 column, where teams
-// of at most 4 rows measured faster (more, shorter teams: Q4_K 4096x14336
-// 8.65 -> 8.05 us, 14336x4096 8.58 -> 7.75 us; Q8_0 4096x14336 13.25 ->
-// 12.83 us); their fused fp32 forms keep larger teams, which re-read the
-// fp32 activation fewer times. The result does not depend on the rows per
-// team: every output's team sum runs the same reduction tree.
+// plain half-chunk Q4_K, Q8_0, Q4_1, Q5_0, Q5_1 and Q5_K mat-vecs at one
+// q8_1 column, where teams of at most 4 rows measured faster (more, shorter
+// teams: Q4_K 4096x14336 8.65 -> 8.05 us, 14336x4096 8.58 -> 7.75 us; Q8_0
+// 4096x14336 13.25 -> 12.83 us; at 4096x14336 Q4_1 8.40 -> 8.13, Q5_0
+// 10.19 -> 9.27, Q5_1 10.38 -> 9.68, Q5_K 10.60 -> 9.70 us); their fused
+// fp32 forms keep larger teams, which re-read the fp32 activation fewer
+// times. The result does not depend on the rows per team: every output's
+// team sum runs the same reduction tree.
 template <class F>
 constexpr bool launch_short_teams(bool xf, int nc, int g) {
-  const bool short_teams = (F::kType == 12 && F::kUnitsPerBlock == 8) || F::kType == 8;
+  const bool short_teams = (F::kType == 12 && F::kUnitsPerBlock == 8) || F::kType == 8 || F::kType == 3 ||
+                           F::kType == 6 || F::kType == 7 || F::kType == 13;
   return short_teams && !xf && nc == 1 && g == 1 && rows_per_pass<F>(nc, g) > 4;
 }
 

@@ -133,7 +133,7 @@ static void case_rows(const char* name, int64_t M, int64_t K, int nc, int g, int
   const float* x = xf ? reinterpret_cast<const float*>(y) : nullptr;
   const int units = static_cast<int>(K / F::kQK) * F::kUnitsPerBlock;
   const Shape s = plan_launch(M, units, launch_max_rows<F>(xf, nc, g), 256, launch_max_passes<F>(xf, nc, g), xf, nc, 0,
-                              layout_pipelined<F>());
+                              layout_depth_cap<F>());
   // the launcher instantiates passes > 1 only at R = the register budget
   bool ok = s.team_lanes <= kLaunchBound && static_cast<int64_t>(s.rows) * s.slots * s.passes <= M &&
             (s.passes == 1 || ((s.passes == 2 || s.passes == 4) && s.rows == rows_per_pass<F>(nc, g))) &&
@@ -461,6 +461,10 @@ int main(int argc, char** argv) {
     case_mmq_all<Q6K>("q6_k", 33, 768, n);
     case_mmq_all<Q40>("q4_0", 17, 1280, n);
     case_mmq_all<Q80>("q8_0", 33, 512, n);
+    case_mmq_all<Q41>("q4_1", 17, 768, n);
+    case_mmq_all<Q50>("q5_0", 33, 512, n);
+    case_mmq_all<Q51>("q5_1", 17, 1280, n);
+    case_mmq_all<Q5K>("q5_k", 33, 768, n);
   }
   if (small) {
     printf("host model: %d failing case(s)\n", failures);
@@ -488,6 +492,10 @@ int main(int argc, char** argv) {
         case_mmq_all<Q6K>("q6_k", M, K, n);
         case_mmq_all<Q40>("q4_0", M, K, n);
         case_mmq_all<Q80>("q8_0", M, K, n);
+        case_mmq_all<Q41>("q4_1", M, K, n);
+        case_mmq_all<Q50>("q5_0", M, K, n);
+        case_mmq_all<Q51>("q5_1", M, K, n);
+        case_mmq_all<Q5K>("q5_k", M, K, n);
       }
   case_mmq<Q4K, 2, 2, 4>("q4_k", 300, 4096, 256);
   case_mmq<Q6K, 1, 1, 8>("q6_k", 300, 4096, 256);
@@ -527,6 +535,10 @@ int main(int argc, char** argv) {
     case_mmq<Q4K, 2, 2, 8>("q4_k", 14336, 4096, 32);
     case_mmq<Q6K, 2, 2, 4>("q6_k", 4096, 4096, 64);
     case_mmq<Q6K, 2, 1, 8>("q6_k", 2048, 4096, 16);
+    case_mmq<Q41, 2, 1, 8>("q4_1", 4096, 14336, 16);
+    case_mmq<Q50, 2, 1, 8>("q5_0", 4096, 14336, 16);
+    case_mmq<Q51, 2, 2, 4>("q5_1", 4096, 14336, 32);
+    case_mmq<Q5K, 2, 1, 8>("q5_k", 4096, 14336, 16);
     case_id<Q4K>("q4_k", 14336, 4096, 8, 8, 1);
     case_id<Q4K2>("q4_k2", 14336, 4096, 8, 8, 1);
   }

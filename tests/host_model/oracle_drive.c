@@ -102,8 +102,8 @@ static void one_shape(int type, int64_t M, int64_t K, int64_t n) {
 }
 
 int main(void) {
-    const int types[4] = {ORC_Q4_0, ORC_Q8_0, ORC_Q4_K, ORC_Q6_K};
-    for (int t = 0; t < 4; ++t) {
+    const int types[8] = {ORC_Q4_0, ORC_Q8_0, ORC_Q4_K, ORC_Q6_K, ORC_Q4_1, ORC_Q5_0, ORC_Q5_1, ORC_Q5_K};
+    for (int t = 0; t < 8; ++t) {
         int qk, bb;
         orc_type_info(types[t], &qk, &bb);
         const int64_t Ks[3] = {qk, 2 * qk, 4 * qk > 256 ? 4 * qk : 256};
@@ -119,7 +119,7 @@ int main(void) {
     /* error paths */
     double d;
     CHECK(orc_mmvq(NULL, ORC_Q4_K, 1, 256, y, 1, &d, NULL, NULL), ORC_ERR_NULL);
-    CHECK(orc_mmvq(y, 7, 1, 256, y, 1, &d, NULL, NULL), ORC_ERR_TYPE);
+    CHECK(orc_mmvq(y, 5, 1, 256, y, 1, &d, NULL, NULL), ORC_ERR_TYPE);
     CHECK(orc_mmvq(y, ORC_Q4_K, 1, 200, y, 1, &d, NULL, NULL), ORC_ERR_SHAPE);
     CHECK(orc_quantize_q8_1(x, 33, 1, 33, y), ORC_ERR_SHAPE);
     CHECK(orc_glu(9, 1.0, 1.0, 0.0, &d), ORC_ERR_TYPE);

@@ -84,7 +84,10 @@ FUSED_CASES = [(Q4_0, 37, 96, 1, 0), (Q4_0, 300, 1024, 3, 5), (Q4_0, 129, 16384,
                # formats the pages name without layouts
                (Q4_1, 37, 96, 1, 0), (Q4_1, 300, 1024, 3, 5), (Q5_0, 37, 1056, 2, 1), (Q5_0, 129, 4096, 8, 0),
                (Q5_1, 300, 1024, 5, 3), (Q5_K, 1000, 4096, 1, 0), (Q5_K, 129, 14336, 8, 7),
-               (Q5_K, 12301, 4096, 2, 1)]
+               (Q5_K, 12301, 4096, 2, 1),
+               # pipelined rows (few waves per CU, 8 or 16 rows per team)
+               (Q4_1, 4096, 4096, 1, 0), (Q5_1, 4096, 4096, 1, 2), (Q5_K, 4096, 4096, 1, 1),
+               (Q5_K, 2048, 14336, 1, 0)]
 
 
 @pytest.mark.parametrize("wtype,M,K,n,pad", FUSED_CASES,
@@ -221,7 +224,8 @@ def test_mmvq_id_glu_f32_moe_workload(O):
 
 WORKLOADS_F32 = [("q4_k_4096x14336", 1), ("q4_k_4096x14336", 2), ("q4_k_4096x14336", 8),
                  ("q4_k_14336x4096", 4), ("q6_k_128256x4096", 1), ("q6_k_128256x4096", 2),
-                 ("q4_0_256x1024", 1), ("q8_0_4096x14336", 1)]
+                 ("q4_0_256x1024", 1), ("q8_0_4096x14336", 1), ("q4_1_4096x14336", 1),
+                 ("q5_0_4096x14336", 1), ("q5_1_4096x14336", 1), ("q5_k_4096x14336", 1)]
 
 
 @pytest.mark.parametrize("name,n", WORKLOADS_F32, ids=[f"{a}-n{b}" for a, b in WORKLOADS_F32])

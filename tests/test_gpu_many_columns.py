@@ -1,6 +1,6 @@
 """GPU parity of the many-column path (more than the row kernels' columns,
-int8 matrix cores; Q4_K, Q6_K, Q4_0 and Q8_0 with q8_1 activations and no
-gate) through the C ABI: against the oracle within the stated tolerance for
+int8 matrix cores; every weight format with q8_1 activations and no gate)
+through the C ABI: against the oracle within the stated tolerance for
 every row and column, at shapes with ragged row and column tiles, at the
 FFN-down and LM-head workloads, with the epilogue's scale and bias; the
 forms beyond 8 columns that run as column groups through the row kernels
@@ -46,7 +46,7 @@ def _nan(rows, M):
 SHAPES = [(1, 256, 9), (37, 512, 16), (300, 2304, 17), (1000, 4096, 33), (129, 14336, 64),
           (65, 16384, 100), (33, 768, 256), (17, 1280, 31),
           (9000, 256, 32), (9000, 512, 16), (8192, 256, 9), (5000, 256, 16)]
-CASES = [(t, M, K, n) for t in (Q4_K, Q6_K, Q4_0, Q8_0) for (M, K, n) in SHAPES]
+CASES = [(t, M, K, n) for t in (Q4_K, Q6_K, Q4_0, Q8_0, B.Q4_1, B.Q5_0, B.Q5_1, B.Q5_K) for (M, K, n) in SHAPES]
 CASES += [(Q4_K, 300, 2304, 6), (Q4_K, 129, 14336, 7), (Q4_K, 1000, 4096, 8)]
 
 
@@ -65,7 +65,9 @@ def test_many_columns_parity(O, wtype, M, K, n):
     assert_close(host(out), ref, mag, f"many columns {TNAME[wtype]} {M}x{K} n={n}")
 
 
-@pytest.mark.parametrize("name,n", [("q4_k_4096x14336", 64), ("q6_k_128256x4096", 16), ("q8_0_4096x14336", 32)])
+@pytest.mark.parametrize("name,n", [("q4_k_4096x14336", 64), ("q6_k_128256x4096", 16), ("q8_0_4096x14336", 32),
+                                    ("q4_1_4096x14336", 16), ("q5_0_4096x14336", 9), ("q5_1_4096x14336", 32),
+                                    ("q5_k_4096x14336", 16)])
 def test_many_columns_workload(O, name, n):
     """The FFN-down and LM-head shapes with many columns, the launches the
     benchmark times; every row and column against the oracle."""
@@ -85,8 +87,7 @@ def test_many_columns_workload(O, name, n):
 # Beyond 8 columns the forms the matrix-core kernel does not take run as
 # groups of 8 columns through the row kernels.
 GROUPS = [(Q4_0, 37, 96, 12), (Q8_0, 300, 1056, 17), (Q6_K, 17, 768, 9), (Q4_K, 129, 4096, 20),
-          # formats without a matrix-core step: every form in column groups
-          (B.Q4_1, 37, 1024, 12), (B.Q5_0, 17, 1056, 9), (B.Q5_1, 33, 512, 20), (B.Q5_K, 65, 2048, 16)]
+          (B.Q4_1, 37, 1056, 12), (B.Q5_0, 17, 1056, 9), (B.Q5_1, 33, 512, 20), (B.Q5_K, 65, 2048, 16)]
 
 
 @pytest.mark.parametrize("wtype,M,K,n", GROUPS, ids=[f"{TNAME[c[0]]}-{c[1]}x{c[2]}-n{c[3]}" for c in GROUPS])
@@ -103,7 +104,7 @@ def test_column_groups(O, wtype, M, K, n):
     yd = gpu_quantize(x, K)
     u, mu, _ = O.mmvq(Wu, wtype, M, K, y, n)
     g, mg, _ = O.mmvq(Wg, wtype, M, K, y, n)
-    if K % 256 or wtype in (B.Q4_1, B.Q5_0, B.Q5_1, B.Q5_K):
+    if K % 256:
         out = _nan(n, M)
         B.mmvq(dev(Wu), wtype, M, K, yd, n, out)
         assert_close(host(out), u, mu, "q8_1 column groups")
