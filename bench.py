@@ -487,16 +487,17 @@ def timed_replay(torch, stream, g_warm, g_timed):
 
 def mmq_route(B, wl, n: int) -> bool:
     """True where mmvq with q8_1 columns runs the many-column (matrix-core)
-    kernel: K a multiple of 256 and n >= 9 (Q4_K: n >= 6)."""
-    return wl.K % 256 == 0 and (n >= 9 or (wl.wtype == B.Q4_K and n >= 6))
+    kernel: K a multiple of 256 and n at least the library's crossover."""
+    return wl.K % 256 == 0 and n >= B.mmvq_many_columns_min(wl.wtype, False)
 
 
-def time_workload(torch, B, wl, n: int, steps: int, warmup: int, probe: bool = True):
+def time_workload(torch, B, wl, n: int, steps: int, warmup: int, probe: bool = True, glu: bool = False):
     """GPU timings of one workload: exactly `steps` timed launches of each
     form after `warmup` untimed ones, weights rotating over the copies.
     Forms: fused (mmvq_f32), two-launch step (quantize + mmvq), mat-vec alone
-    (mmvq), quantizer alone, and the streaming-read probe over the same
-    weight bytes."""
+    (mmvq), quantizer alone, the gate/up form (mmvq_glu, SwiGLU, the next
+    weight copy as the gate matrix: twice the weight bytes) and the
+    streaming-read probe over the same weight bytes."""
     data, Ws, x, y, out = gpu_setup(torch, wl, n)
     C = len(Ws)
     s = torch.cuda.Stream()
@@ -506,6 +507,8 @@ def time_workload(torch, B, wl, n: int, steps: int, warmup: int, probe: bool = T
     forms = {
         "step": lambda c: (B.mmvq_quantize_q8_1(x, wl.K, n, wl.K, y, s), B.mmvq(Ws[c], wl.wtype, wl.M, wl.K, y, n, out, s)),
         "gemv": lambda c: B.mmvq(Ws[c], wl.wtype, wl.M, wl.K, y, n, out, s),
+        "glu": (lambda c: B.mmvq_glu(Ws[(c + 1) % C], Ws[c], wl.wtype, wl.M, wl.K, y, n, B.GLU_SWIGLU, out, s))
+        if glu else None,
         "quant": lambda c: B.mmvq_quantize_q8_1(x, wl.K, n, wl.K, y, s),
         "fused": (lambda c: B.mmvq_f32(Ws[c], wl.wtype, wl.M, wl.K, x, n, wl.K, out, s)) if fused_ok else None,
         "probe": (lambda c: B.mmvq_read_probe(Ws[c], wl.weight_bytes, sink, s)) if probe else None,
@@ -807,9 +810,10 @@ def main():
             many = ((16, 32, 64, 128) if name in ("q4_k_4096x14336", "q4_k_14336x4096")
                     else (16, 64) if name in ("q6_k_128256x4096", "q8_0_4096x14336") else (16,))
             for nn in tuple(w.n if name != "q4_k_4096x14336" else (1, 2, 4, 8)) + many:
-                r, *_ = time_workload(torch, B, w, nn, 500, 50)
+                r, *_ = time_workload(torch, B, w, nn, 500, 50, glu=name == "q4_k_14336x4096")
                 gb = algorithmic_bytes(w, nn) / (r["gemv_us"] * 1e-6) / 1e9
                 print(json.dumps({"workload": name, "n": nn, "gemv_us": round(r["gemv_us"], 3),
+                                  "glu_us": None if r["glu_us"] is None else round(r["glu_us"], 3),
                                   "quantize_us": round(r["quant_us"], 3),
                                   "two_launch_step_us": round(r["step_us"], 3),
                                   "fused_us": None if r["fused_us"] is None else round(r["fused_us"], 3),

@@ -141,13 +141,25 @@ enum {
 
 /* Largest number of columns of the weight-matrix calls without expert ids
  * (mmvq, mmvq_glu, mmvq_ex and their fp32 forms) and of the quantizer.
- * mmvq and mmvq_ex with q8_1 activations, no gate and K a multiple of 256
- * run on the matrix cores from 9 columns (Q4_K from 6) [MMVQ §多个 token 时];
- * the other forms take more than MMVQ_MAX_COLS columns as groups of at most
- * MMVQ_MAX_COLS columns through the row kernels (each group reads the
- * weights again). The expert-indexed calls take at most MMVQ_MAX_COLS
- * tokens. */
+ * mmvq, mmvq_glu and mmvq_ex with q8_1 activations and K a multiple of 256
+ * run on the matrix cores from mmvq_many_columns_min columns
+ * [MMVQ §多个 token 时]; the fp32 forms and K not a multiple of 256 take
+ * more than MMVQ_MAX_COLS columns as groups of at most MMVQ_MAX_COLS
+ * columns through the row kernels (each group reads the weights again).
+ * The expert-indexed calls take at most MMVQ_MAX_COLS tokens. */
 #define MMVQ_MAX_COLS_BATCH 256
+
+/* Fewest columns from which mmvq / mmvq_ex (gated = 0) or mmvq_glu /
+ * mmvq_ex with a gate matrix (gated != 0), with q8_1 activations and K a
+ * multiple of 256, run on the many-column (matrix-core) kernel instead of
+ * the row kernels, written to *n_min: the measured crossover of the two on
+ * MI355X (without a gate Q5_K 5, Q4_K 6, Q6_K 7, Q4_0 / Q5_0 / Q8_0 8,
+ * Q4_1 / Q5_1 9; with one Q5_K 5, Q4_K 7, the others 9). Below it and in
+ * the fp32 forms the row kernels run, so there the fp32 form of a call is
+ * bit-identical to quantize + its q8_1 form; at or above it the two agree
+ * within the accumulation-order tolerance. Host-only; touches no device.
+ * Errors: MMVQ_ERR_NULL (n_min NULL), MMVQ_ERR_TYPE (weight type). */
+int mmvq_many_columns_min(int type, int gated, int *n_min);
 
 /* Block geometry of a type: elements per block and bytes per block
  * (Q4_0 32/18, Q4_1 32/20, Q5_0 32/22, Q5_1 32/24, Q8_0 32/34, Q4_K 256/144,

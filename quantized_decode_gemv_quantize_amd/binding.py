@@ -50,6 +50,7 @@ _EP = ctypes.POINTER(Epilogue)
 
 _SIGS = {
     "mmvq_type_info": (_int, [_int, ctypes.POINTER(_int), ctypes.POINTER(_int)]),
+    "mmvq_many_columns_min": (_int, [_int, _int, ctypes.POINTER(_int)]),
     "mmvq_quantize_q8_1": (_int, [_p, _i64, _i64, _i64, _p, _p]),
     "mmvq": (_int, [_p, _int, _i64, _i64, _p, _i64, _p, _p]),
     "mmvq_glu": (_int, [_p, _p, _int, _i64, _i64, _p, _i64, _int, _p, _p]),
@@ -130,6 +131,12 @@ def mmvq_type_info(wtype: int) -> tuple[int, int]:
     e, b = _int(), _int()
     _check("mmvq_type_info", lib().mmvq_type_info(wtype, ctypes.byref(e), ctypes.byref(b)))
     return e.value, b.value
+
+
+def mmvq_many_columns_min(wtype: int, gated: bool) -> int:
+    n = _int()
+    _check("mmvq_many_columns_min", lib().mmvq_many_columns_min(wtype, int(bool(gated)), ctypes.byref(n)))
+    return n.value
 
 
 def mmvq_quantize_q8_1(x, K: int, n: int, ldx: int, y_q, stream=None) -> None:

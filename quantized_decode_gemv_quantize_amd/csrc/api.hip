@@ -110,9 +110,9 @@ bool mmq_type(int type) {
 }
 
 // Many columns (up to MMVQ_MAX_COLS_BATCH): the MFMA kernel, q8_1
-// activations, no gate, K a multiple of 256; the epilogue's up scale and
-// bias apply.
-int mmq_common(const void* W, int type, int64_t M, int64_t K, const void* y_q, int64_t n,
+// activations, K a multiple of 256, with or without a gate (W_gate NULL);
+// the whole epilogue applies.
+int mmq_common(const void* W, const void* W_gate, int type, int64_t M, int64_t K, const void* y_q, int64_t n,
                const mmvq_epilogue* epi, float* out, void* stream) {
   if (!W || !y_q || !out) return MMVQ_ERR_NULL;
   const Dispatch* d = dispatch_for(type, false);
@@ -121,15 +121,21 @@ int mmq_common(const void* W, int type, int64_t M, int64_t K, const void* y_q, i
   if (M < 1 || K < 1 || K % 256 != 0 || n < 1 || n > MMVQ_MAX_COLS_BATCH) return MMVQ_ERR_SHAPE;
   if (M > (int64_t(1) << 40) / K || K / 256 > (int64_t(1) << 24)) return MMVQ_ERR_SHAPE;
   if (!aligned(W, 16) || !aligned(y_q, 16) || !aligned(out, 4)) return MMVQ_ERR_ALIGN;
+  if (W_gate && !aligned(W_gate, 16)) return MMVQ_ERR_ALIGN;
   RowArgs ra{};
-  int rc = set_epilogue(epi, false, &ra);
+  int rc = set_epilogue(epi, W_gate != nullptr, &ra);
   if (rc) return rc;
   MmqArgs a{};
   a.W = static_cast<const uint8_t*>(W);
+  a.Wg = static_cast<const uint8_t*>(W_gate);
   a.y = static_cast<const uint8_t*>(y_q);
   a.out = out;
   a.up_bias = ra.up_bias;
   a.up_scale = ra.up_scale;
+  a.gate_bias = ra.gate_bias;
+  a.gate_scale = ra.gate_scale;
+  a.glu_op = ra.glu_op;
+  a.glu_limit = ra.glu_limit;
   a.M = M;
   a.row_bytes = K / d->qk * d->block_bytes;
   a.ycol_bytes = K / 32 * kQ8Bytes;
@@ -138,25 +144,42 @@ int mmq_common(const void* W, int type, int64_t M, int64_t K, const void* y_q, i
   return launch_mmq(type, a, static_cast<hipStream_t>(stream));
 }
 
-// Columns from which the matrix-core kernel takes a q8_1 product without a
-// gate (K a multiple of 256). Q4_K: from 6 (one 16-column tile: ~14.5 us at
-// 4096x14336 and 14336x4096 for any n <= 16, the row kernels 16.5 / 14.5 us
-// at n = 6 and 24.8 / 17.8 us at n = 8); the other formats past the row
-// kernels' 8 columns.
-int64_t mmq_min_cols(int type) { return type == MMVQ_Q4_K ? 6 : MMVQ_MAX_COLS + 1; }
+// Columns from which the matrix-core kernel takes a q8_1 product (K a
+// multiple of 256): where it measured faster than the row kernels at
+// 4096x14336 and 14336x4096 (us, row kernels / matrix cores). Without a
+// gate: Q5_K from 5 (24.6 / 16.3 and 19.6 / 16.5 at n = 5), Q4_K from 6
+// (one 16-column tile: ~14.5 us for any n <= 16), Q6_K from 7 (57.7 / 31.5
+// and 42.8 / 29.0 at n = 7), Q4_0, Q5_0 and Q8_0 from 8 (22.0 / 18.4 and
+// 19.1 / 19.5 for Q8_0 at n = 8), Q4_1 and Q5_1 never below 9. Gate/up at
+// 14336x4096: Q5_K from 5 (33.4 / 29.5), Q4_K from 7 (28.5 / 25.4; 24.8 /
+// 25.3 at 6), the others from 9 (Q6_K 75.3 / 75.7 at 8). 0: not a type.
+int mmq_min_cols(int type, bool gate) {
+  switch (type) {
+    case MMVQ_Q5_K: return 5;
+    case MMVQ_Q4_K: return gate ? 7 : 6;
+    case MMVQ_Q6_K: return gate ? MMVQ_MAX_COLS + 1 : 7;
+    case MMVQ_Q4_0:
+    case MMVQ_Q5_0:
+    case MMVQ_Q8_0: return gate ? MMVQ_MAX_COLS + 1 : 8;
+    case MMVQ_Q4_1:
+    case MMVQ_Q5_1: return MMVQ_MAX_COLS + 1;
+    default: return 0;
+  }
+}
 
 // Plain or gate/up product with an optional epilogue (W_gate NULL: no gate).
 // More than MMVQ_MAX_COLS columns outside the matrix-core kernel's forms
-// (a gate, fp32 activations, K not a multiple of 256) run as groups of at
-// most MMVQ_MAX_COLS columns through the row kernels, each group reading the
+// (fp32 activations, K not a multiple of 256) run as groups of at most
+// MMVQ_MAX_COLS columns through the row kernels, each group reading the
 // weights again; all arguments are checked before the first group is
 // enqueued.
 int rows_common(const void* W_up, const void* W_gate, int type, int64_t M, int64_t K, const ActIn& in, int64_t n,
                 const mmvq_epilogue* epi, float* out, void* stream) {
-  const bool mmq_form = !W_gate && !in.x && K % 256 == 0 && mmq_type(type);
-  if (mmq_form && n >= mmq_min_cols(type)) return mmq_common(W_up, type, M, K, in.y_q, n, epi, out, stream);
+  const bool mmq_form = !in.x && K % 256 == 0 && mmq_type(type);
+  if (mmq_form && mmq_min_cols(type, W_gate != nullptr) > 0 && n >= mmq_min_cols(type, W_gate != nullptr))
+    return mmq_common(W_up, W_gate, type, M, K, in.y_q, n, epi, out, stream);
 #ifdef QMV_TUNING
-  if (getenv("MMVQ_FORCE_MMQ") && mmq_form) return mmq_common(W_up, type, M, K, in.y_q, n, epi, out, stream);
+  if (getenv("MMVQ_FORCE_MMQ") && mmq_form) return mmq_common(W_up, W_gate, type, M, K, in.y_q, n, epi, out, stream);
 #endif
   if (n > MMVQ_MAX_COLS_BATCH) return MMVQ_ERR_SHAPE;
   const int64_t n0 = n < MMVQ_MAX_COLS ? n : MMVQ_MAX_COLS;
@@ -219,6 +242,14 @@ int id_common(const void* W_gate, const void* W_up, int64_t expert_stride_bytes,
 }  // namespace
 
 extern "C" {
+
+int mmvq_many_columns_min(int type, int gated, int* n_min) {
+  if (!n_min) return MMVQ_ERR_NULL;
+  const int m = mmq_min_cols(type, gated != 0);
+  if (m == 0) return MMVQ_ERR_TYPE;
+  *n_min = m;
+  return MMVQ_OK;
+}
 
 int mmvq_type_info(int type, int* block_elems, int* block_bytes) {
   int e, b;

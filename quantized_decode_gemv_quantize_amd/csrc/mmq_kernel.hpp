@@ -42,6 +42,7 @@
 #include "common.hpp"
 #include "formats.hpp"
 #include "mmq_plan.hpp"
+#include "mmvq_kernel.hpp"     // glu(), the epilogue shared with the row kernels
 
 namespace qmv {
 
@@ -114,22 +115,30 @@ template <int RT> struct MmqRowLds<Q6K, RT> {
   float d[RT][16];
 };
 
-template <class F, int RT, int CT>
-struct MmqWaveLds {
+// One matrix's part of a wave's staging: the step images of its RT x 16
+// rows and their per-row factors.
+template <class F, int RT>
+struct alignas(16) MmqImage {
   uint8_t a[RT][16][MmqGeom<F>::kRowLds];   // the 16 rows' step images
-  uint8_t b[CT][16][288];                    // 16 columns' 8 q8_1 blocks
   MmqRowLds<F, RT> x;
+};
+template <int CT> using MmqBTiles = uint8_t[CT][16][288];   // 16 columns' 8 q8_1 blocks per tile
+
+template <class F, int RT, int CT, int G>
+struct MmqWaveLds {
+  MmqImage<F, RT> m[G];                      // [0] up (or plain), [1] gate
+  MmqBTiles<CT> b;
 };
 
 // LDS bytes of a workgroup (the staging tiles of all waves; the reduction
 // reuses them), and the shapes that fit one compute unit's 160 KB.
-template <class F, int RT, int CT, int NW>
+template <class F, int RT, int CT, int NW, int G>
 constexpr size_t mmq_lds_bytes() {
-  const size_t stage = sizeof(MmqWaveLds<F, RT, CT>) * NW, red = sizeof(float) * NW * RT * CT * 4 * kWave;
+  const size_t stage = sizeof(MmqWaveLds<F, RT, CT, G>) * NW, red = sizeof(float) * NW * G * RT * CT * 4 * kWave;
   return stage > red ? stage : red;
 }
-template <class F, int RT, int CT, int NW>
-constexpr bool mmq_fits() { return mmq_lds_bytes<F, RT, CT, NW>() <= 160 * 1024; }
+template <class F, int RT, int CT, int NW, int G>
+constexpr bool mmq_fits() { return mmq_lds_bytes<F, RT, CT, NW, G>() <= 160 * 1024; }
 
 // Where the lane's rows sit: tile_off = byte offset of the tile's first row
 // from W; row_off(rt) = that of row r16 of row tile rt (clamped to M - 1).
@@ -155,7 +164,7 @@ template <class F> struct MmqStep;
 template <class F, int QS, bool HB>
 struct MmqStepK {
   template <int RT, int CT>
-  __device__ static void run(MmqWaveLds<F, RT, CT>& lds, const MmqRows&, int, int lane,
+  __device__ static void run(MmqImage<F, RT>& img, const MmqBTiles<CT>& b, const MmqRows&, int, int lane,
                              float (&acc)[RT][CT][4]) {
     const int r16 = lane & 15, q = lane >> 4;
     const Q4K::Lane L = Q4K::lane(2 * q);       // scale unpack of chunk q (sub-blocks 2q, 2q+1)
@@ -163,11 +172,11 @@ struct MmqStepK {
     float am[RT][2];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      const u32x4 hdr = *reinterpret_cast<const u32x4*>(&lds.a[rt][r16][0]);
+      const u32x4 hdr = *reinterpret_cast<const u32x4*>(&img.a[rt][r16][0]);
       uint32_t scp, mp;
       Q4K::chunk_scales(hdr, L, scp, mp);
-      *reinterpret_cast<uint16_t*>(&lds.x.sc[rt][q][r16][0]) = static_cast<uint16_t>(scp & 0xFFFFu);
-      lds.x.d[rt][r16] = h2f(hdr.x);
+      *reinterpret_cast<uint16_t*>(&img.x.sc[rt][q][r16][0]) = static_cast<uint16_t>(scp & 0xFFFFu);
+      img.x.d[rt][r16] = h2f(hdr.x);
       const float dmin = h2f(hdr.x >> 16);
       am[rt][0] = -dmin * static_cast<float>(mp & 0xFFu);
       am[rt][1] = -dmin * static_cast<float>((mp >> 8) & 0xFFu);
@@ -188,7 +197,7 @@ struct MmqStepK {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       qh[rt].x = qh[rt].y = 0u;
-      if constexpr (HB) qh[rt] = *reinterpret_cast<const u32x2*>(&lds.a[rt][r16][16 + 8 * q]);
+      if constexpr (HB) qh[rt] = *reinterpret_cast<const u32x2*>(&img.a[rt][r16][16 + 8 * q]);
     }
     // sub-blocks 2c and 2c+1 share the code bytes of chunk c (low and high
     // nibbles); the chunk loop is kept rolled so only one chunk's operands
@@ -198,8 +207,8 @@ struct MmqStepK {
       u32x2 w[RT], scw[RT];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        w[rt] = *reinterpret_cast<const u32x2*>(&lds.a[rt][r16][QS + 32 * c + 8 * q]);
-        scw[rt] = *reinterpret_cast<const u32x2*>(&lds.x.sc[rt][c][4 * q][0]);
+        w[rt] = *reinterpret_cast<const u32x2*>(&img.a[rt][r16][QS + 32 * c + 8 * q]);
+        scw[rt] = *reinterpret_cast<const u32x2*>(&img.x.sc[rt][c][4 * q][0]);
       }
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -224,7 +233,7 @@ struct MmqStepK {
         float d8[CT];
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
-          const long B = b_operand<CT>(lds.b, ct, r16, q, t, d8[ct]);
+          const long B = b_operand<CT>(b, ct, r16, q, t, d8[ct]);
           const v4i zero = {0, 0, 0, 0};
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) C[rt][ct] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A[rt], B, zero, 0, 0, 0);
@@ -244,7 +253,7 @@ struct MmqStepK {
     }
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      const float4 dv = *reinterpret_cast<const float4*>(&lds.x.d[rt][4 * q]);
+      const float4 dv = *reinterpret_cast<const float4*>(&img.x.d[rt][4 * q]);
       const float dd[4] = {dv.x, dv.y, dv.z, dv.w};
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
@@ -279,7 +288,7 @@ template <> struct MmqStep<Q5K> : MmqStepK<Q5K, 48, true> {};
 template <class F, int BB, int CO, bool NIBBLES, int QH, int ZP, bool MIN>
 struct MmqStepBlocks {
   template <int RT, int CT>
-  __device__ static void run(MmqWaveLds<F, RT, CT>& lds, const MmqRows&, int, int lane, float (&acc)[RT][CT][4]) {
+  __device__ static void run(MmqImage<F, RT>& img, const MmqBTiles<CT>& b, const MmqRows&, int, int lane, float (&acc)[RT][CT][4]) {
     const int r16 = lane & 15, q = lane >> 4;
     float am[RT][2], e[CT][2];
 #pragma unroll
@@ -287,14 +296,14 @@ struct MmqStepBlocks {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int t = 2 * q + h;
-        lds.x.d[rt][t][r16] = h2f(*reinterpret_cast<const uint16_t*>(&lds.a[rt][r16][BB * t]));
-        am[rt][h] = MIN ? h2f(*reinterpret_cast<const uint16_t*>(&lds.a[rt][r16][BB * t + 2])) : 0.0f;
+        img.x.d[rt][t][r16] = h2f(*reinterpret_cast<const uint16_t*>(&img.a[rt][r16][BB * t]));
+        am[rt][h] = MIN ? h2f(*reinterpret_cast<const uint16_t*>(&img.a[rt][r16][BB * t + 2])) : 0.0f;
       }
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        e[ct][h] = MIN ? h2f(*reinterpret_cast<const uint16_t*>(&lds.b[ct][r16][36 * (2 * q + h) + 2])) : 0.0f;
+        e[ct][h] = MIN ? h2f(*reinterpret_cast<const uint16_t*>(&b[ct][r16][36 * (2 * q + h) + 2])) : 0.0f;
     mmq_lds_fence();
     const int nib = 4 * (q >> 1);
     static_for<0, 8>([&](auto tc) QMV_INLINE {
@@ -307,7 +316,7 @@ struct MmqStepBlocks {
       float dw[RT][4];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        const uint8_t* p = &lds.a[rt][r16][BB * t + CO + (NIBBLES ? 8 * (q & 1) : 8 * q)];
+        const uint8_t* p = &img.a[rt][r16][BB * t + CO + (NIBBLES ? 8 * (q & 1) : 8 * q)];
         const long raw = lds8<kMis>(p);
         if constexpr (NIBBLES) {
           uint32_t lo = static_cast<uint32_t>(raw), hi = static_cast<uint32_t>(static_cast<uint64_t>(raw) >> 32);
@@ -317,28 +326,28 @@ struct MmqStepBlocks {
             // bit i of the byte goes to bit 4 of byte i (4 bits per word:
             // the multiply places bit i at bit 8i, the partial products do
             // not overlap)
-            const uint32_t b = lds.a[rt][r16][BB * t + QH + q];
-            lo |= (((b & 0xFu) * 0x00204081u) & 0x01010101u) << 4;
-            hi |= (((b >> 4) * 0x00204081u) & 0x01010101u) << 4;
+            const uint32_t hb = img.a[rt][r16][BB * t + QH + q];
+            lo |= (((hb & 0xFu) * 0x00204081u) & 0x01010101u) << 4;
+            hi |= (((hb >> 4) * 0x00204081u) & 0x01010101u) << 4;
           }
           A[rt] = pack2(lo, hi);
         } else {
           A[rt] = raw;
         }
-        const float4 dv = *reinterpret_cast<const float4*>(&lds.x.d[rt][t][4 * q]);
+        const float4 dv = *reinterpret_cast<const float4*>(&img.x.d[rt][t][4 * q]);
         dw[rt][0] = dv.x; dw[rt][1] = dv.y; dw[rt][2] = dv.z; dw[rt][3] = dv.w;
       }
       v4i C[RT][CT];
       float d8[CT], zs[CT];
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
-        const long B = b_operand<CT>(lds.b, ct, r16, q, t, d8[ct]);
+        const long B = b_operand<CT>(b, ct, r16, q, t, d8[ct]);
         const v4i zero = {0, 0, 0, 0};
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) C[rt][ct] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A[rt], B, zero, 0, 0, 0);
         zs[ct] = 0.0f;
         if constexpr (ZP != 0)
-          zs[ct] = static_cast<float>(ZP) * h2f(*reinterpret_cast<const uint16_t*>(&lds.b[ct][r16][36 * t + 2]));
+          zs[ct] = static_cast<float>(ZP) * h2f(*reinterpret_cast<const uint16_t*>(&b[ct][r16][36 * t + 2]));
       }
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
@@ -379,18 +388,18 @@ template <> struct MmqStep<Q80> : MmqStepBlocks<Q80, 34, 2, false, -1, 0, false>
 // its d) for the D layout.
 template <> struct MmqStep<Q6K> {
   template <int RT, int CT>
-  __device__ static void run(MmqWaveLds<Q6K, RT, CT>& lds, const MmqRows& rows, int sb, int lane,
+  __device__ static void run(MmqImage<Q6K, RT>& im, const MmqBTiles<CT>& b, const MmqRows& rows, int sb, int lane,
                              float (&acc)[RT][CT][4]) {
     const int r16 = lane & 15, q = lane >> 4;
     int base[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       base[rt] = MmqGeom<Q6K>::image_base(rows.row_off(rt, r16), sb);
-      const uint8_t* img = &lds.a[rt][r16][base[rt]];
+      const uint8_t* img = &im.a[rt][r16][base[rt]];
       const u32x2 s4 = lds8_rt(img + 192 + 4 * q, base[rt] & 2);   // scales 4q..4q+3 (and 4 more)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) lds.x.sc[rt][4 * q + k][r16] = static_cast<int8_t>((s4.x >> (8 * k)) & 0xFFu);
-      if (q == 0) lds.x.d[rt][r16] = h2f(*reinterpret_cast<const uint16_t*>(img + 208));
+      for (int k = 0; k < 4; ++k) im.x.sc[rt][4 * q + k][r16] = static_cast<int8_t>((s4.x >> (8 * k)) & 0xFFu);
+      if (q == 0) im.x.d[rt][r16] = h2f(*reinterpret_cast<const uint16_t*>(img + 208));
     }
     mmq_lds_fence();
     const long ones = 0x0101010101010101l;
@@ -408,15 +417,15 @@ template <> struct MmqStep<Q6K> {
       int sc[RT][2][4];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        const uint8_t* img = &lds.a[rt][r16][base[rt]];
+        const uint8_t* img = &im.a[rt][r16][base[rt]];
         const int mis = base[rt] & 2;
         const u32x2 ql = lds8_rt(img + 64 * h + 32 * (g & 1) + 8 * q, mis);
         const u32x2 qh = lds8_rt(img + 128 + 32 * h + 8 * q, mis);
         const int ns = 4 * (g >> 1), hs = 2 * g;
         A[rt] = pack2(((ql.x >> ns) & 0x0F0F0F0Fu) | (((qh.x >> hs) & 0x03030303u) << 4),
                       ((ql.y >> ns) & 0x0F0F0F0Fu) | (((qh.y >> hs) & 0x03030303u) << 4));
-        const uint32_t s0 = *reinterpret_cast<const uint32_t*>(&lds.x.sc[rt][2 * t][4 * q]);
-        const uint32_t s1 = *reinterpret_cast<const uint32_t*>(&lds.x.sc[rt][2 * t + 1][4 * q]);
+        const uint32_t s0 = *reinterpret_cast<const uint32_t*>(&im.x.sc[rt][2 * t][4 * q]);
+        const uint32_t s1 = *reinterpret_cast<const uint32_t*>(&im.x.sc[rt][2 * t + 1][4 * q]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           sc[rt][0][i] = sbfe(s0, 8 * i, 8);
@@ -428,7 +437,7 @@ template <> struct MmqStep<Q6K> {
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
         float d8;
-        const long B = b_operand<CT>(lds.b, ct, r16, q, t, d8);
+        const long B = b_operand<CT>(b, ct, r16, q, t, d8);
         const long Blo = lo_half ? B : 0l, Bhi = lo_half ? 0l : B;
         const v4i zero = {0, 0, 0, 0};
         const int S32lo = 32 * __builtin_amdgcn_mfma_i32_16x16x32_i8(ones, Blo, zero, 0, 0, 0)[0];
@@ -447,7 +456,7 @@ template <> struct MmqStep<Q6K> {
     }
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      const float4 dv = *reinterpret_cast<const float4*>(&lds.x.d[rt][4 * q]);
+      const float4 dv = *reinterpret_cast<const float4*>(&im.x.d[rt][4 * q]);
       const float dd[4] = {dv.x, dv.y, dv.z, dv.w};
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
@@ -457,7 +466,11 @@ template <> struct MmqStep<Q6K> {
   }
 };
 
-template <class F, int RT, int CT, int NW>
+// G = 2: the gate/up form. The up (W) and gate (Wg) rows of a tile are
+// staged side by side and each runs the format's step against the same B
+// tiles; the epilogue sums both over the waves and applies the scales,
+// biases and GLU of the row kernels' epilogue.
+template <class F, int RT, int CT, int NW, int G>
 __global__ void __launch_bounds__(NW * kWave, 8 / NW) mmq_kernel(MmqArgs a) {
   using Gm = MmqGeom<F>;
   const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
@@ -474,28 +487,33 @@ __global__ void __launch_bounds__(NW * kWave, 8 / NW) mmq_kernel(MmqArgs a) {
   // the staging tiles of the NW waves; after the K loop the same LDS holds
   // the partial sums of the reduction
   constexpr int NV = RT * CT * 4;
-  __shared__ __align__(16) uint8_t smem[mmq_lds_bytes<F, RT, CT, NW>()];
-  MmqWaveLds<F, RT, CT>& lds = reinterpret_cast<MmqWaveLds<F, RT, CT>*>(smem)[wave];
-  float acc[RT][CT][4];
+  __shared__ __align__(16) uint8_t smem[mmq_lds_bytes<F, RT, CT, NW, G>()];
+  MmqWaveLds<F, RT, CT, G>& lds = reinterpret_cast<MmqWaveLds<F, RT, CT, G>*>(smem)[wave];
+  float acc[G][RT][CT][4];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
+  for (int g = 0; g < G; ++g)
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[rt][ct][i] = 0.0f;
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[g][rt][ct][i] = 0.0f;
 
   MmqOffsets<F, RT, CT> off;
   // staged loads -> LDS: A loads into their rows' images, B piece k at byte
   // 16k of the B tiles
-  auto store_stage = [&](const MmqStage<F, RT, CT>& st, int sb) QMV_INLINE {
-    uint8_t* la = &lds.a[0][0][0];
+  auto store_stage = [&](const MmqStage<F, RT, CT, G>& st, int sb) QMV_INLINE {
     uint8_t* lb = &lds.b[0][0][0];
 #pragma unroll
-    for (int j = 0; j < mmq_a_slots<F, RT>(); ++j) {
-      if (lane + kWave * j < mmq_a_pieces<F>() * RT) {
-        uint8_t* dst = la + off.arow[j] * Gm::kRowLds + Gm::piece_lds(rows.tile_off + off.a[j], sb, off.apc[j]);
-        if (Gm::piece_short(off.apc[j])) *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(st.a[j].x);
-        else *reinterpret_cast<u32x4*>(dst) = st.a[j];
+    for (int g = 0; g < G; ++g) {
+      uint8_t* la = &lds.m[g].a[0][0][0];
+#pragma unroll
+      for (int j = 0; j < mmq_a_slots<F, RT>(); ++j) {
+        if (lane + kWave * j < mmq_a_pieces<F>() * RT) {
+          uint8_t* dst = la + off.arow[j] * Gm::kRowLds + Gm::piece_lds(rows.tile_off + off.a[j], sb, off.apc[j]);
+          if (Gm::piece_short(off.apc[j])) *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(st.a[g][j].x);
+          else *reinterpret_cast<u32x4*>(dst) = st.a[g][j];
+        }
       }
     }
 #pragma unroll
@@ -512,40 +530,54 @@ __global__ void __launch_bounds__(NW * kWave, 8 / NW) mmq_kernel(MmqArgs a) {
   // slower at 16 columns: 16.3 -> 17.3 us at 4096x14336.)
   if (sb0 < sb1) {
     mmq_offsets<F, RT, CT>(a, row_base, col_base, lane, off);
-    MmqStage<F, RT, CT> st;
-    mmq_stage_load<F, RT, CT>(a, row_base, col_base, lane, sb0, off, st);
+    MmqStage<F, RT, CT, G> st;
+    mmq_stage_load<F, RT, CT, G>(a, row_base, col_base, lane, sb0, off, st);
     for (int sb = sb0; sb < sb1; ++sb) {
       mmq_lds_fence();             // the previous step's reads are done
       store_stage(st, sb);
       const int next = sb + 1 < sb1 ? sb + 1 : sb;
-      mmq_stage_load<F, RT, CT>(a, row_base, col_base, lane, next, off, st);
+      mmq_stage_load<F, RT, CT, G>(a, row_base, col_base, lane, next, off, st);
       __builtin_amdgcn_sched_barrier(0);
       mmq_lds_fence();
-      MmqStep<F>::template run<RT, CT>(lds, rows, sb, lane, acc);
+#pragma unroll
+      for (int g = 0; g < G; ++g) MmqStep<F>::template run<RT, CT>(lds.m[g], lds.b, rows, sb, lane, acc[g]);
     }
   }
 
-  // ---- sum the waves' partials (in wave order) and store
+  // ---- sum the waves' partials (in wave order), epilogue, store
   __syncthreads();                 // every wave is done with its staging tiles
-  float(*red)[NV][kWave] = reinterpret_cast<float(*)[NV][kWave]>(smem);
+  float(*red)[G][NV][kWave] = reinterpret_cast<float(*)[G][NV][kWave]>(smem);
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
+  for (int g = 0; g < G; ++g)
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red[wave][(rt * CT + ct) * 4 + i][lane] = acc[rt][ct][i];
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wave][g][(rt * CT + ct) * 4 + i][lane] = acc[g][rt][ct][i];
   __syncthreads();
   for (int v = wave; v < NV; v += NW) {
-    float s = red[0][v][lane];
+    float s[G];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) s += red[w][v][lane];
+    for (int g = 0; g < G; ++g) {
+      s[g] = red[0][g][v][lane];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) s[g] += red[w][g][v][lane];
+    }
     int64_t r;
     int c;
     mmq_store_pos<RT, CT>(v, q, r16, row_base, col_base, r, c);
     if (r < a.M && c < a.n) {
-      float o = s;
-      if (a.up_scale) o *= a.up_scale[0];
-      if (a.up_bias) o += a.up_bias[r];
+      float up = s[0];
+      if (a.up_scale) up *= a.up_scale[0];
+      if (a.up_bias) up += a.up_bias[r];
+      float o = up;
+      if constexpr (G == 2) {
+        float gate = s[G - 1];
+        if (a.gate_scale) gate *= a.gate_scale[0];
+        if (a.gate_bias) gate += a.gate_bias[r];
+        o = glu(a.glu_op, gate, up, a.glu_limit);
+      }
       a.out[static_cast<int64_t>(c) * a.M + r] = o;
     }
   }

@@ -10,11 +10,19 @@
 namespace qmv {
 
 struct MmqArgs {
-  const uint8_t* W;
+  const uint8_t* W;          // up (or plain) weights
+  const uint8_t* Wg;         // gate weights (gate/up form), same layout; NULL without a gate
   const uint8_t* y;          // q8_1 columns
   float* out;                // out[c*M + r]
-  const float* up_bias;      // epilogue without a gate: out*up_scale[0] + up_bias[r]
+  // epilogue: up = up*up_scale[0] + up_bias[r], the same for the gate, then
+  // glu(glu_op, gate, up, glu_limit) in the gate/up form; NULL pointers are
+  // skipped
+  const float* up_bias;
   const float* up_scale;
+  const float* gate_bias;
+  const float* gate_scale;
+  int glu_op;
+  float glu_limit;
   int64_t M;
   int64_t row_bytes;
   int64_t ycol_bytes;
@@ -108,9 +116,9 @@ constexpr int mmq_a_slots() { return (mmq_a_pieces<F>() * RT + kWave - 1) / kWav
 template <int CT>
 constexpr int mmq_b_slots() { return (kMmqBPieces * CT + kWave - 1) / kWave; }
 
-template <class F, int RT, int CT>
+template <class F, int RT, int CT, int G>
 struct MmqStage {
-  u32x4 a[mmq_a_slots<F, RT>()];
+  u32x4 a[G][mmq_a_slots<F, RT>()];   // [0] up (or plain) rows, [1] gate rows
   u32x4 b[mmq_b_slots<CT>()];
 };
 
@@ -153,20 +161,25 @@ __host__ __device__ __forceinline__ void mmq_offsets(const MmqArgs& a, int64_t r
 }
 
 // The staging loads of step sb; loads past the end (slot k >= the tile's
-// loads) are not issued.
-template <class F, int RT, int CT>
+// loads) are not issued. The gate rows (G = 2) sit at the same offsets of
+// Wg as the up rows of W.
+template <class F, int RT, int CT, int G>
 __device__ __forceinline__ void mmq_stage_load(const MmqArgs& a, int64_t row_base, int col_base, int lane, int sb,
-                                               const MmqOffsets<F, RT, CT>& o, MmqStage<F, RT, CT>& st) {
+                                               const MmqOffsets<F, RT, CT>& o, MmqStage<F, RT, CT, G>& st) {
   using Gm = MmqGeom<F>;
   const int64_t tile_off = row_base * a.row_bytes;
   const uint8_t* yb = a.y + (static_cast<int64_t>(col_base) * a.ycol_bytes + static_cast<int64_t>(sb) * 288);
 #pragma unroll
-  for (int j = 0; j < mmq_a_slots<F, RT>(); ++j) {
-    if (lane + kWave * j < mmq_a_pieces<F>() * RT) {
-      const uint8_t* src = a.W + Gm::piece_src(tile_off + o.a[j], sb, o.apc[j]);
-      if (Gm::piece_short(o.apc[j])) st.a[j].x = ld_u16(src);
-      else if constexpr (MmqGeom<F>::kStride % 16 == 0) st.a[j] = ld_a16_x4(src);
-      else st.a[j] = ld_x4(src);
+  for (int g = 0; g < G; ++g) {
+    const uint8_t* W = g == 0 ? a.W : a.Wg;
+#pragma unroll
+    for (int j = 0; j < mmq_a_slots<F, RT>(); ++j) {
+      if (lane + kWave * j < mmq_a_pieces<F>() * RT) {
+        const uint8_t* src = W + Gm::piece_src(tile_off + o.a[j], sb, o.apc[j]);
+        if (Gm::piece_short(o.apc[j])) st.a[g][j].x = ld_u16(src);
+        else if constexpr (MmqGeom<F>::kStride % 16 == 0) st.a[g][j] = ld_a16_x4(src);
+        else st.a[g][j] = ld_x4(src);
+      }
     }
   }
 #pragma unroll

@@ -225,16 +225,19 @@ static void case_block_dots(const char* name, int64_t M, int64_t K, int nc) {
 // many-column (MFMA) kernel: every load of every lane, wave and step, in
 // the workgroup-to-tile mapping the kernel uses; every output stored exactly
 // once; every A load lands inside its row's LDS image (and the bytes the
-// step's arithmetic reads are covered by loads of that step).
-template <class F, int RT, int CT, int NW>
+// step's arithmetic reads are covered by loads of that step). G = 2: the
+// gate/up form, whose gate loads must stay inside the gate matrix.
+template <class F, int RT, int CT, int NW, int G = 1>
 static void case_mmq(const char* name, int64_t M, int64_t K, int n) {
   using Gm = MmqGeom<F>;
   const int64_t row_bytes = K / F::kQK * F::kBlockBytes, ycol = K / 32 * kQ8Bytes;
   uint8_t* W = alloc16(M * row_bytes);
+  uint8_t* Wg = G == 2 ? alloc16(M * row_bytes) : nullptr;
   uint8_t* y = alloc16(n * ycol);
-  begin({{W, W + M * row_bytes}, {y, y + n * ycol}});
+  if (G == 2) begin({{W, W + M * row_bytes}, {Wg, Wg + M * row_bytes}, {y, y + n * ycol}});
+  else begin({{W, W + M * row_bytes}, {y, y + n * ycol}});
   MmqArgs a{};
-  a.W = W; a.y = y; a.M = M; a.row_bytes = row_bytes; a.ycol_bytes = ycol; a.n = n;
+  a.W = W; a.Wg = Wg; a.y = y; a.M = M; a.row_bytes = row_bytes; a.ycol_bytes = ycol; a.n = n;
   a.nsb = static_cast<int>(K / 256);
   a.gx = static_cast<int>((M + 16 * RT - 1) / (16 * RT));
   a.gy = (n + 16 * CT - 1) / (16 * CT);
@@ -258,8 +261,8 @@ static void case_mmq(const char* name, int64_t M, int64_t K, int n) {
         for (int lane = 0; lane < 64; ++lane) {
           MmqOffsets<F, RT, CT> off;
           mmq_offsets<F, RT, CT>(a, row_base, col_base, lane, off);
-          MmqStage<F, RT, CT> st;
-          mmq_stage_load<F, RT, CT>(a, row_base, col_base, lane, sb, off, st);
+          MmqStage<F, RT, CT, G> st;
+          mmq_stage_load<F, RT, CT, G>(a, row_base, col_base, lane, sb, off, st);
           for (int j = 0; j < mmq_a_slots<F, RT>(); ++j) {
             if (lane + kWave * j >= mmq_a_pieces<F>() * RT) continue;
             const int64_t ro = row_base * row_bytes + off.a[j];
@@ -296,8 +299,9 @@ static void case_mmq(const char* name, int64_t M, int64_t K, int n) {
   }
   for (int64_t i = 0; i < groups && ok; ++i) ok = tiles[i] == 1;
   for (int64_t i = 0; i < M * n && ok; ++i) ok = stores[i] == 1;
-  report("mmq", ok, name, M, K, n, 1);
+  report(G == 2 ? "mmq_glu" : "mmq", ok, name, M, K, n, 1);
   free(W);
+  free(Wg);
   free(y);
 }
 
@@ -309,6 +313,9 @@ static void case_mmq_all(const char* name, int64_t M, int64_t K, int n) {
   case_mmq<F, 2, 1, 8>(name, M, K, n);
   case_mmq<F, 1, 1, 4>(name, M, K, n);
   case_mmq<F, 1, 1, 8>(name, M, K, n);
+  case_mmq<F, 2, 2, 4, 2>(name, M, K, n);
+  case_mmq<F, 2, 1, 8, 2>(name, M, K, n);
+  case_mmq<F, 1, 1, 8, 2>(name, M, K, n);
 }
 
 // quantizer: 8 lanes per q8_1 block, 4 floats each (clamped to block 0 when
@@ -539,6 +546,8 @@ int main(int argc, char** argv) {
     case_mmq<Q50, 2, 1, 8>("q5_0", 4096, 14336, 16);
     case_mmq<Q51, 2, 2, 4>("q5_1", 4096, 14336, 32);
     case_mmq<Q5K, 2, 1, 8>("q5_k", 4096, 14336, 16);
+    case_mmq<Q4K, 2, 1, 8, 2>("q4_k", 14336, 4096, 16);
+    case_mmq<Q4K, 2, 2, 4, 2>("q4_k", 14336, 4096, 64);
     case_id<Q4K>("q4_k", 14336, 4096, 8, 8, 1);
     case_id<Q4K2>("q4_k2", 14336, 4096, 8, 8, 1);
   }

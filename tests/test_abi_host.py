@@ -18,7 +18,8 @@ def test_exports_every_declared_symbol(L):
     names = B.declared_symbols()
     assert set(names) == {"mmvq_type_info", "mmvq_quantize_q8_1", "mmvq", "mmvq_glu", "mmvq_id",
                           "mmvq_id_glu", "mmvq_f32", "mmvq_glu_f32", "mmvq_id_f32", "mmvq_id_glu_f32",
-                          "mmvq_ex", "mmvq_id_ex", "mmvq_block_dots", "mmvq_read_probe", "mmvq_strerror"}
+                          "mmvq_ex", "mmvq_id_ex", "mmvq_block_dots", "mmvq_read_probe", "mmvq_strerror",
+                          "mmvq_many_columns_min"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -37,6 +38,20 @@ def test_type_info():
         B.mmvq_type_info(5)
     assert e.value.code == B.ERR_TYPE
     assert B.lib().mmvq_type_info(B.Q4_K, None, None) == 0
+
+
+def test_many_columns_min(L):
+    """The documented crossover table, and its errors."""
+    plain = {B.Q5_K: 5, B.Q4_K: 6, B.Q6_K: 7, B.Q4_0: 8, B.Q5_0: 8, B.Q8_0: 8, B.Q4_1: 9, B.Q5_1: 9}
+    gated = {B.Q5_K: 5, B.Q4_K: 7, B.Q6_K: 9, B.Q4_0: 9, B.Q5_0: 9, B.Q8_0: 9, B.Q4_1: 9, B.Q5_1: 9}
+    for t in plain:
+        assert B.mmvq_many_columns_min(t, False) == plain[t]
+        assert B.mmvq_many_columns_min(t, True) == gated[t]
+    for t in (5, B.Q8_1, -1):
+        with pytest.raises(B.MMVQError) as e:
+            B.mmvq_many_columns_min(t, False)
+        assert e.value.code == B.ERR_TYPE
+    assert L.mmvq_many_columns_min(B.Q4_K, 0, None) == B.ERR_NULL
 
 
 def test_strerror(L):

@@ -1,6 +1,7 @@
 """GPU parity of the full fused epilogue (mmvq_ex, mmvq_id_ex): per-matrix
 or per-expert scales, bias rows, every GLU op, the MoE shared expert, with
-q8_1 or fp32 activations, against the oracle (orc_mmvq_ex, orc_mmvq_id_ex)
+q8_1 or fp32 activations, at one to 40 columns (the many-column kernel's
+gate/up form beyond 8), against the oracle (orc_mmvq_ex, orc_mmvq_id_ex)
 within the propagated tolerance; the reduced forms (no epilogue; GLU only)
 equal mmvq / mmvq_glu bit for bit."""
 import numpy as np
@@ -51,6 +52,14 @@ CASES = [(t, M, K, n, op, gate, f32)
          for gate in (True,)
          for f32 in (False, True)]
 CASES += [(t, 129, 4096, n, 0, False, f32) for t in (Q4_K, Q6_K) for n in (1, 8) for f32 in (False, True)]
+# more than 8 columns: the gate/up form of the many-column kernel (q8_1),
+# column groups through the row kernels (fp32)
+CASES += [(t, M, K, n, op, True, False)
+          for (t, M, K) in [(Q4_K, 300, 2048), (Q4_0, 77, 1024), (Q6_K, 65, 768), (Q8_0, 45, 512),
+                            (B.Q4_1, 33, 512), (B.Q5_0, 40, 768), (B.Q5_1, 17, 1024), (B.Q5_K, 100, 1536)]
+          for n in (9, 40)
+          for op in OPS]
+CASES += [(Q4_K, 300, 2048, 17, B.GLU_SWIGLU, True, True), (Q6_K, 65, 768, 12, B.GLU_GEGLU, True, True)]
 
 
 @pytest.mark.parametrize("wtype,M,K,n,op,gate,f32", CASES,

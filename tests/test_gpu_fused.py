@@ -40,19 +40,11 @@ def _empty(rows, M):
     return torch.full((rows, M), float("nan"), dtype=torch.float32, device="cuda:0")
 
 
-def _mmq_route(wtype, n):
-    """Q4_K q8_1 mat-vec with 6..8 columns runs the many-column kernel (the
-    fused form keeps the row kernel): the two agree within the tolerance."""
-    return wtype == Q4_K and 6 <= n <= B.MAX_COLS
-
-
-def _close(a, b, mag, what):
-    """Within the oracle tolerance of each other (both are within it of the
-    oracle): |a - b| <= 2 * (REL * A + ABS)."""
-    from gpu_helpers import ABS, REL
-    d = np.abs(host(a).astype(np.float64) - host(b).astype(np.float64))
-    bad = ~(d <= 2 * (REL * mag + ABS))
-    assert not bad.any(), f"{what}: fused and two-step differ beyond the tolerance at {np.argwhere(bad)[0]}"
+def _mmq_route(wtype, K, n, gated=False):
+    """The q8_1 form runs the many-column kernel from the library's crossover
+    (K a multiple of 256) while the fused form keeps the row kernel up to
+    8 columns: there the two agree within the tolerance, not bit for bit."""
+    return K % 256 == 0 and B.mmvq_many_columns_min(wtype, gated) <= n <= B.MAX_COLS
 
 
 def _same(a, b, what):
@@ -104,8 +96,9 @@ def test_mmvq_f32(O, wtype, M, K, n, pad):
     B.mmvq(Wd, wtype, M, K, yd, n, two)
     y = O.quantize_q8_1(x, K)
     ref, mag, _ = O.mmvq(W, wtype, M, K, y, n)
-    if _mmq_route(wtype, n):
-        _close(fused, two, mag, f"mmvq_f32 {TNAME[wtype]} {M}x{K} n={n}")
+    if _mmq_route(wtype, K, n):
+        # the q8_1 form on the many-column kernel: both forms against the oracle
+        assert_close(host(two), ref, mag, f"mmvq {TNAME[wtype]} {M}x{K} n={n}")
     else:
         _same(fused, two, f"mmvq_f32 {TNAME[wtype]} {M}x{K} n={n}")
     assert_close(host(fused), ref, mag, f"mmvq_f32 {TNAME[wtype]} {M}x{K} n={n}")
@@ -129,15 +122,19 @@ def test_mmvq_glu_f32(O, wtype, M, K, n, op):
     fused, two = _empty(n, M), _empty(n, M)
     B.mmvq_glu_f32(Wgd, Wud, wtype, M, K, xd, n, ldx, op, fused)
     B.mmvq_glu(Wgd, Wud, wtype, M, K, gpu_quantize(x, K), n, op, two)
-    _same(fused, two, f"mmvq_glu_f32 {TNAME[wtype]} {M}x{K} n={n}")
+    routed = _mmq_route(wtype, K, n, gated=True)
+    if not routed:
+        _same(fused, two, f"mmvq_glu_f32 {TNAME[wtype]} {M}x{K} n={n}")
     y = O.quantize_q8_1(x, K)
     g, mg, _ = O.mmvq(Wg, wtype, M, K, y, n)
     u, mu, _ = O.mmvq(Wu, wtype, M, K, y, n)
     ref = O.mmvq_glu(Wg, Wu, wtype, M, K, y, n, op)
     tol = glu_tolerance(g, u, mg, mu, ref, op)
-    got = host(fused).astype(np.float64)
-    bad = ~(np.abs(got - ref) <= tol)
-    assert not bad.any(), f"first bad at {np.argwhere(bad)[0]}"
+    # the q8_1 form on the many-column kernel: both forms against the oracle
+    for out in ([fused, two] if routed else [fused]):
+        got = host(out).astype(np.float64)
+        bad = ~(np.abs(got - ref) <= tol)
+        assert not bad.any(), f"first bad at {np.argwhere(bad)[0]}"
 
 
 ID_F32 = [("q4_k-E4-T3-k2", Q4_K, 4, 200, 512, [[2, 0], [1, 2], [2, 3]]),
@@ -245,7 +242,7 @@ def test_mmvq_f32_workload(O, name, n):
     y = O.quantize_q8_1(x, K)
     ref, mag = O.mmvq_threaded(W, wl.wtype, M, K, y, n)
     got = host(fused)
-    if _mmq_route(wl.wtype, n):
+    if _mmq_route(wl.wtype, wl.K, n):
         # the two-step form runs the many-column kernel: both against the oracle
         assert_close(host(two), ref, mag, f"mmvq {name} n={n}")
     else:

@@ -1,6 +1,6 @@
 """GPU parity of the many-column path (more than the row kernels' columns,
-int8 matrix cores; every weight format with q8_1 activations and no gate)
-through the C ABI: against the oracle within the stated tolerance for
+int8 matrix cores; every weight format with q8_1 activations, with or
+without a gate) through the C ABI: against the oracle within the stated tolerance for
 every row and column, at shapes with ragged row and column tiles, at the
 FFN-down and LM-head workloads, with the epilogue's scale and bias; the
 forms beyond 8 columns that run as column groups through the row kernels
@@ -84,16 +84,41 @@ def test_many_columns_workload(O, name, n):
     assert_close(host(out), ref, mag, f"many columns workload {name} n={n}")
 
 
-# Beyond 8 columns the forms the matrix-core kernel does not take run as
-# groups of 8 columns through the row kernels.
+@pytest.mark.parametrize("wtype", [Q4_K, Q6_K, B.Q5_K])
+def test_many_columns_glu_workload(O, wtype):
+    """The gate/up form at the FFN-up shape (14336x4096), 16 columns: every
+    output against the oracle's gate/up product within the propagated
+    tolerance."""
+    M, K, n = 14336, 4096, 16
+    announce(f"mmvq_glu many columns {TNAME[wtype]} M={M} K={K} n={n}")
+    rng = np.random.default_rng(99 + wtype)
+    Wu = synth.weights(wtype, M, K, rng)
+    Wg = synth.weights(wtype, M, K, rng)
+    x = synth.activations(K, n, rng)
+    y = O.quantize_q8_1(x)
+    out = _nan(n, M)
+    B.mmvq_glu(dev(Wg), dev(Wu), wtype, M, K, gpu_quantize(x), n, B.GLU_SWIGLU, out)
+    u, mu = O.mmvq_threaded(Wu, wtype, M, K, y, n)
+    g, mg = O.mmvq_threaded(Wg, wtype, M, K, y, n)
+    ref = O.mmvq_glu(Wg, Wu, wtype, M, K, y, n, B.GLU_SWIGLU)
+    tol = glu_tolerance(g, u, mg, mu, ref, B.GLU_SWIGLU)
+    got = host(out).astype(np.float64)
+    bad = ~(np.abs(got - ref) <= tol)
+    assert not bad.any(), f"first bad at {np.argwhere(bad)[0]}"
+
+
+# Beyond 8 columns the forms the matrix-core kernel does not take (fp32
+# activations, K not a multiple of 256) run as groups of 8 columns through
+# the row kernels; the gate/up form with q8_1 columns takes the matrix-core
+# kernel when K is a multiple of 256.
 GROUPS = [(Q4_0, 37, 96, 12), (Q8_0, 300, 1056, 17), (Q6_K, 17, 768, 9), (Q4_K, 129, 4096, 20),
           (B.Q4_1, 37, 1056, 12), (B.Q5_0, 17, 1056, 9), (B.Q5_1, 33, 512, 20), (B.Q5_K, 65, 2048, 16)]
 
 
 @pytest.mark.parametrize("wtype,M,K,n", GROUPS, ids=[f"{TNAME[c[0]]}-{c[1]}x{c[2]}-n{c[3]}" for c in GROUPS])
 def test_column_groups(O, wtype, M, K, n):
-    """q8_1 (K not a multiple of 256 for Q4_0 / Q8_0), fp32 and gate/up forms
-    with more than 8 columns, against the oracle."""
+    """q8_1 (K not a multiple of 256 for Q4_0 / Q8_0 / Q4_1 / Q5_0), fp32 and
+    gate/up forms with more than 8 columns, against the oracle."""
     announce(f"column groups {TNAME[wtype]} M={M} K={K} n={n}")
     rng = np.random.default_rng(M * 3 + K + n)
     Wu = synth.weights(wtype, M, K, rng)
