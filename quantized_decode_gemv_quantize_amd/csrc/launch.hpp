@@ -75,10 +75,31 @@ inline int launch_rows_chunked(const RowArgs& a, const Shape& s, hipStream_t st)
   return MMVQ_ERR_SHAPE;
 }
 
+template <class F, int R, int DEPTH, bool XF>
+inline int launch_rows1(const RowArgs& a, const Shape& s, hipStream_t st) {
+  hipLaunchKernelGGL((mmvq_rows1_kernel<F, R, DEPTH, XF>), dim3(static_cast<unsigned>(s.blocks)),
+                     dim3(s.team_lanes), 0, st, a);
+  return check_launch();
+}
+
 // Single-pass launch, with the pipelined rows of plan_depth for the fp32
-// forms (the q8_1 forms keep their short teams and issue every row first).
+// forms (the q8_1 forms keep their short teams and issue every row first);
+// one column, no gate, one slot and one team per workgroup take the lean
+// kernel of that case (the pipelined fp32 forms, and the q8_1 forms of the
+// layouts with short teams).
 template <class F, bool XF, int NC, int G, int R, int P>
 inline int launch_rows_d(const RowArgs& a, const Shape& s, hipStream_t st) {
+  if constexpr (NC == 1 && G == 1 && P == 1) {
+    if (s.teams_per_block == 1) {
+      if constexpr (XF && R >= 8 && layout_pipelined<F>()) {
+        if (s.depth == 4) return launch_rows1<F, R, 4, true>(a, s, st);
+        if constexpr (R > 8)
+          if (s.depth == 8) return launch_rows1<F, R, 8, true>(a, s, st);
+      }
+      if constexpr (!XF && R == 4 && launch_short_teams<F>(false, 1, 1))
+        if (s.depth == 0) return launch_rows1<F, R, 0, false>(a, s, st);
+    }
+  }
   if constexpr (XF && R >= 8 && layout_pipelined<F>()) {
     if (s.depth == 4) return launch_rows_r<F, XF, NC, G, R, P, 1, 4>(a, s, st);
     if constexpr (R > 8)

@@ -403,6 +403,85 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
   }   // passes
 }
 
+// The single-column mat-vec with one team of whole waves per workgroup and
+// one row slot (a single decode token: the fused step with pipelined rows,
+// XF, or the q8_1 form with every row issued first, DEPTH = 0): the same
+// loads, arithmetic and reduction order as rows_body for that case (so the
+// outputs equal rows_body's, and the fused form's quantize + the q8_1
+// form's, bit for bit), with the general kernel's per-team bookkeeping left
+// out: the team is the workgroup, the row window a clamp of blockIdx.x * R,
+// the weight rows 32-bit offsets from the team's first row (one team's rows
+// span less than 4 GB: at most 512 units of a row), the epilogue the up
+// scale and bias. At 4096x14336 Q4_K the fused form measured 8.42-8.45 us
+// against rows_body's 8.67-8.72 (experiment harness, same launch shape).
+template <class F, int R, int DEPTH, bool XF>
+__global__ void __launch_bounds__(kLaunchBound) mmvq_rows1_kernel(RowArgs a) {
+  static_assert(DEPTH >= 0 && DEPTH < R, "pipelined rows below R");
+  constexpr int FIRST = DEPTH > 0 ? DEPTH : R;      // rows issued up front
+  __shared__ float red[kMaxWavesPerBlock * R];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = lane_id();
+  const int units = a.units;
+  const bool active = tid < units;
+  const int u = active ? tid : units - 1;
+  int64_t row0 = static_cast<int64_t>(blockIdx.x) * R;
+  int skip = 0;
+  if (row0 + R > a.M) {
+    skip = static_cast<int>(row0 + R - a.M);
+    row0 = a.M - R;
+  }
+  // activation loads first, then the first rows' weight loads; what needs
+  // the activation (its quantization) waits only for it
+  typename F::XRaw xr[1];                 // fp32 values (XF)
+  typename F::Act act;
+  if constexpr (XF) F::load_x(xr[0], a.x, u);
+  else F::issue_act(act, a.y, u);
+  __builtin_amdgcn_sched_barrier(0);
+  const typename F::Lane L = F::lane(u);
+  typename F::Wt w[R];
+  const uint8_t* base = a.W + row0 * a.row_bytes;
+  const uint32_t rb = static_cast<uint32_t>(a.row_bytes);
+#pragma unroll
+  for (int r = 0; r < FIRST; ++r) {
+    F::load_wt(w[r], base, static_cast<uint32_t>(r) * rb, L);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (XF) F::quant_x(act, xr[0]);
+  else F::finish_act(act);
+  if (!active) F::zero_act(act);
+  float pt[1][R];
+  static_for<0, R>([&](auto rc) QMV_INLINE {
+    constexpr int r = decltype(rc)::value;
+    typename F::Dec dec;
+    F::decode(w[r], dec, L);
+    pt[0][r] = F::col_dot(dec, act);
+    // row r's arithmetic stays ahead of the next issue
+    if constexpr (DEPTH > 0) __builtin_amdgcn_sched_barrier(0);
+    if constexpr (DEPTH > 0 && r + DEPTH < R) {
+      F::load_wt(w[r + DEPTH], base, static_cast<uint32_t>(r + DEPTH) * rb, L);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  });
+  // the team reduction of rows_body: within each wave, then the waves'
+  // partials summed in wave order
+  team_reduce<kWave, 1, R>(pt, lane);
+  using RM = ReduceMap<kWave, R>;
+  if (RM::representative(lane)) {
+#pragma unroll
+    for (int pos = 0; pos < RM::kPerLane; ++pos) red[wave * R + RM::index(lane, pos)] = pt[0][pos];
+  }
+  __syncthreads();
+  if (tid < R && tid >= skip) {
+    const int tw = static_cast<int>(blockDim.x) / kWave;
+    float v = 0.0f;
+    for (int k = 0; k < tw; ++k) v += red[k * R + tid];
+    if (a.up_scale) v *= a.up_scale[0];
+    if (a.up_bias) v += a.up_bias[row0 + tid];
+    a.out[row0 + tid] = v;
+  }
+}
+
 // Columns one rows_body call takes. Where the activation slices of all NC
 // columns and the rows in flight exceed the registers, the kernels take the
 // columns in two halves (measured spills at 256 registers: Q6_K, 24
