@@ -125,13 +125,14 @@ inline int launch_rows_p(const RowArgs& a, const Shape& s, hipStream_t st) {
 
 template <class F, bool XF, int NC, int G>
 inline int launch_rows_nc(RowArgs a, int64_t K, hipStream_t st) {
-  constexpr int RMAX = rows_per_pass<F>(NC, G);
+  constexpr int RMAX = launch_max_rows<F>(XF, NC, G);
   int64_t force = 0;
 #ifdef QMV_TUNING
   if (const char* e = getenv("MMVQ_FORCE_ROWS")) force = atoi(e);
 #endif
   Shape s = plan_launch(a.M, units_per_row<F>(K), launch_max_rows<F>(XF, NC, G), device_cus(),
-                        launch_max_passes<F>(XF, NC, G), XF, NC, force, layout_depth_cap<F>());
+                        launch_max_passes<F>(XF, NC, G), XF, NC, force, layout_depth_cap<F>(),
+                        rows_per_pass<F>(NC, G));
 #ifdef QMV_TUNING
   if (const char* e = getenv("MMVQ_DEPTH")) s.depth = XF ? atoi(e) : 0;
 #endif

@@ -125,8 +125,11 @@ inline Shape spread_teams(Shape s, int64_t cus) {
 // the whole activation; 4096x4096 Q4_K: 4 rows per team 5.42 us, 16 rows at
 // depth 8: 4.82), and the pipelined rows of plan_depth for every
 // single-pass launch.
+// rmax_flat (0: rmax): the most rows a team issues all at once, when rmax
+// counts on pipelined rows (only DEPTH + 1 rows' weights live): a launch
+// left without pipelining is planned again within it.
 inline Shape plan_launch(int64_t M, int units, int rmax, int64_t cus, int max_passes, bool xf, int nc,
-                         int64_t force_rows, int depth_cap) {
+                         int64_t force_rows, int depth_cap, int rmax_flat = 0) {
   Shape s = plan_rows(M, units, rmax, cus, QMV_TARGET_WAVES_PER_CU, force_rows, max_passes);
   if (xf && depth_cap > 0) {
     if (nc == 1 && s.passes == 1 && force_rows == 0) {
@@ -136,6 +139,8 @@ inline Shape plan_launch(int64_t M, int units, int rmax, int64_t cus, int max_pa
     }
     s.depth = plan_depth(s, cus, depth_cap);
   }
+  if (s.depth == 0 && rmax_flat > 0 && s.rows > rmax_flat)
+    s = plan_rows(M, units, rmax_flat, cus, QMV_TARGET_WAVES_PER_CU, force_rows, max_passes);
   return spread_teams(s, cus);
 }
 
@@ -182,9 +187,14 @@ constexpr bool launch_short_teams(bool xf, int nc, int g) {
   return short_teams && !xf && nc == 1 && g == 1 && rows_per_pass<F>(nc, g) > 4;
 }
 
+// ... and the single-column fp32 Q5_K form, whose 16-row teams (pipelined:
+// only DEPTH + 1 rows' weights live; 4096x14336 11.4-11.8 -> 10.5-10.6 us
+// against 8-row teams) re-quantize the activation half as often.
 template <class F>
 constexpr int launch_max_rows(bool xf, int nc, int g) {
-  return launch_short_teams<F>(xf, nc, g) ? 4 : rows_per_pass<F>(nc, g);
+  if (launch_short_teams<F>(xf, nc, g)) return 4;
+  if (F::kType == 13 && xf && nc == 1 && g == 1) return 16;
+  return rows_per_pass<F>(nc, g);
 }
 
 // Passes per team a mat-vec launch may use (rows kernels take a pass count of

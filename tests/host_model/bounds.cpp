@@ -133,7 +133,7 @@ static void case_rows(const char* name, int64_t M, int64_t K, int nc, int g, int
   const float* x = xf ? reinterpret_cast<const float*>(y) : nullptr;
   const int units = static_cast<int>(K / F::kQK) * F::kUnitsPerBlock;
   const Shape s = plan_launch(M, units, launch_max_rows<F>(xf, nc, g), 256, launch_max_passes<F>(xf, nc, g), xf, nc, 0,
-                              layout_depth_cap<F>());
+                              layout_depth_cap<F>(), rows_per_pass<F>(nc, g));
   // the launcher instantiates passes > 1 only at R = the register budget
   bool ok = s.team_lanes <= kLaunchBound && static_cast<int64_t>(s.rows) * s.slots * s.passes <= M &&
             (s.passes == 1 || ((s.passes == 2 || s.passes == 4) && s.rows == rows_per_pass<F>(nc, g))) &&

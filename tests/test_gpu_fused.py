@@ -79,7 +79,9 @@ FUSED_CASES = [(Q4_0, 37, 96, 1, 0), (Q4_0, 300, 1024, 3, 5), (Q4_0, 129, 16384,
                (Q5_K, 12301, 4096, 2, 1),
                # pipelined rows (few waves per CU, 8 or 16 rows per team)
                (Q4_1, 4096, 4096, 1, 0), (Q5_1, 4096, 4096, 1, 2), (Q5_K, 4096, 4096, 1, 1),
-               (Q5_K, 2048, 14336, 1, 0)]
+               (Q5_K, 2048, 14336, 1, 0),
+               # the one-column single-team-per-workgroup kernel, ragged last team
+               (Q4_K, 4099, 14336, 1, 3), (Q4_1, 4100, 8192, 1, 0), (Q5_1, 2055, 16384, 1, 1)]
 
 
 @pytest.mark.parametrize("wtype,M,K,n,pad", FUSED_CASES,

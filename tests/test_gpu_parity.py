@@ -107,7 +107,10 @@ GEMV_CASES = [(t, M, K, n) for t, shapes in SHAPES.items() for (M, K) in shapes
 GEMV_CASES += [(Q4_K, 1000, 4096, 4), (Q4_K, 1000, 4096, 6), (Q4_K, 1000, 4096, 7),
                (Q4_0, 300, 1024, 4), (Q6_K, 300, 4096, 4), (Q6_K, 300, 4096, 7),
                # enough rows that Q6_K teams take them in 2 or 4 passes
-               (Q6_K, 12301, 4096, 2), (Q6_K, 12301, 4096, 5)]
+               (Q6_K, 12301, 4096, 2), (Q6_K, 12301, 4096, 5),
+               # one-column single-team-per-workgroup kernel (4-row teams), a
+               # ragged last team
+               (Q4_K, 4099, 14336, 1), (Q4_1, 2050, 8192, 1), (Q5_K, 1031, 16384, 1), (Q8_0, 777, 8192, 1)]
 
 
 @pytest.mark.parametrize("wtype,M,K,n", GEMV_CASES,
