@@ -75,11 +75,20 @@ inline int launch_rows_chunked(const RowArgs& a, const Shape& s, hipStream_t st)
   return MMVQ_ERR_SHAPE;
 }
 
+// one team per workgroup, or teams of one or two waves several per
+// workgroup; other team widths: not launched here (MMVQ_ERR_SHAPE)
 template <class F, int R, int DEPTH, bool XF>
 inline int launch_rows1(const RowArgs& a, const Shape& s, hipStream_t st) {
-  hipLaunchKernelGGL((mmvq_rows1_kernel<F, R, DEPTH, XF>), dim3(static_cast<unsigned>(s.blocks)),
-                     dim3(s.team_lanes), 0, st, a);
+  const dim3 grid(static_cast<unsigned>(s.blocks)), block(static_cast<unsigned>(s.teams_per_block * s.team_lanes));
+  if (s.teams_per_block == 1) hipLaunchKernelGGL((mmvq_rows1_kernel<F, R, DEPTH, XF, 0>), grid, block, 0, st, a);
+  else if (s.team_lanes == kWave) hipLaunchKernelGGL((mmvq_rows1_kernel<F, R, DEPTH, XF, 1>), grid, block, 0, st, a);
+  else if (s.team_lanes == 2 * kWave) hipLaunchKernelGGL((mmvq_rows1_kernel<F, R, DEPTH, XF, 2>), grid, block, 0, st, a);
+  else return MMVQ_ERR_SHAPE;
   return check_launch();
+}
+
+inline bool rows1_team_ok(const Shape& s) {
+  return s.teams_per_block == 1 || s.team_lanes == kWave || s.team_lanes == 2 * kWave;
 }
 
 // Single-pass launch, with the pipelined rows of plan_depth for the fp32
@@ -90,7 +99,7 @@ inline int launch_rows1(const RowArgs& a, const Shape& s, hipStream_t st) {
 template <class F, bool XF, int NC, int G, int R, int P>
 inline int launch_rows_d(const RowArgs& a, const Shape& s, hipStream_t st) {
   if constexpr (NC == 1 && G == 1 && P == 1) {
-    if (s.teams_per_block == 1) {
+    if (rows1_team_ok(s)) {
       if constexpr (XF && R >= 8 && layout_pipelined<F>()) {
         if (s.depth == 4) return launch_rows1<F, R, 4, true>(a, s, st);
         if constexpr (R > 8)

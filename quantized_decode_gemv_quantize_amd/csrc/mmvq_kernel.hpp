@@ -414,7 +414,10 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, const Cols& cols,
 // span less than 4 GB: at most 512 units of a row), the epilogue the up
 // scale and bias. At 4096x14336 Q4_K the fused form measured 8.42-8.45 us
 // against rows_body's 8.67-8.72 (experiment harness, same launch shape).
-template <class F, int R, int DEPTH, bool XF>
+// TW = 0: one team per workgroup; TW > 0: teams of TW waves, as many per
+// workgroup as it holds (the team index a compile-time division of the
+// wave index).
+template <class F, int R, int DEPTH, bool XF, int TW>
 __global__ void __launch_bounds__(kLaunchBound) mmvq_rows1_kernel(RowArgs a) {
   static_assert(DEPTH >= 0 && DEPTH < R, "pipelined rows below R");
   constexpr int FIRST = DEPTH > 0 ? DEPTH : R;      // rows issued up front
@@ -422,13 +425,20 @@ __global__ void __launch_bounds__(kLaunchBound) mmvq_rows1_kernel(RowArgs a) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = lane_id();
+  const int team_local = TW > 0 ? wave / TW : 0;
+  const int tw = TW > 0 ? TW : static_cast<int>(blockDim.x) / kWave;     // waves of the team
+  const int lt = tid - team_local * TW * kWave;
+  const int64_t team = TW > 0 ? static_cast<int64_t>(blockIdx.x) * (blockDim.x / (TW * kWave)) + team_local
+                              : static_cast<int64_t>(blockIdx.x);
   const int units = a.units;
-  const bool active = tid < units;
-  const int u = active ? tid : units - 1;
-  int64_t row0 = static_cast<int64_t>(blockIdx.x) * R;
-  int skip = 0;
+  const bool active = lt < units;
+  const int u = active ? lt : units - 1;
+  // teams past the last row (the last workgroup's) clamp to it and store
+  // nothing
+  int64_t row0 = team * R;
+  int64_t skip = 0;
   if (row0 + R > a.M) {
-    skip = static_cast<int>(row0 + R - a.M);
+    skip = row0 + R - a.M;
     row0 = a.M - R;
   }
   // activation loads first, then the first rows' weight loads; what needs
@@ -472,13 +482,13 @@ __global__ void __launch_bounds__(kLaunchBound) mmvq_rows1_kernel(RowArgs a) {
     for (int pos = 0; pos < RM::kPerLane; ++pos) red[wave * R + RM::index(lane, pos)] = pt[0][pos];
   }
   __syncthreads();
-  if (tid < R && tid >= skip) {
-    const int tw = static_cast<int>(blockDim.x) / kWave;
+  if (lt < R && lt >= skip) {
+    const int wave0 = team_local * tw;
     float v = 0.0f;
-    for (int k = 0; k < tw; ++k) v += red[k * R + tid];
+    for (int k = 0; k < tw; ++k) v += red[(wave0 + k) * R + lt];
     if (a.up_scale) v *= a.up_scale[0];
-    if (a.up_bias) v += a.up_bias[row0 + tid];
-    a.out[row0 + tid] = v;
+    if (a.up_bias) v += a.up_bias[row0 + lt];
+    a.out[row0 + lt] = v;
   }
 }
 
