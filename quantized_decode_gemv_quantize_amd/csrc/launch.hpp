@@ -93,9 +93,8 @@ inline bool rows1_team_ok(const Shape& s) {
 
 // Single-pass launch, with the pipelined rows of plan_depth for the fp32
 // forms (the q8_1 forms keep their short teams and issue every row first);
-// one column, no gate, one slot and one team per workgroup take the lean
-// kernel of that case (the pipelined fp32 forms, and the q8_1 forms of the
-// layouts with short teams).
+// one column, no gate and one slot, in teams of one workgroup or of one or
+// two waves, take the lean kernel of that case.
 template <class F, bool XF, int NC, int G, int R, int P>
 inline int launch_rows_d(const RowArgs& a, const Shape& s, hipStream_t st) {
   if constexpr (NC == 1 && G == 1 && P == 1) {
@@ -105,8 +104,10 @@ inline int launch_rows_d(const RowArgs& a, const Shape& s, hipStream_t st) {
         if constexpr (R > 8)
           if (s.depth == 8) return launch_rows1<F, R, 8, true>(a, s, st);
       }
-      if constexpr (!XF && R == 4 && launch_short_teams<F>(false, 1, 1))
-        if (s.depth == 0) return launch_rows1<F, R, 0, false>(a, s, st);
+      // (not Q6_K: its one-wave LM-head teams measured slower there, 73.5 ->
+      // 75.2 us at 128256x4096)
+      if constexpr (R >= 2 && F::kType != 14)
+        if (s.depth == 0) return launch_rows1<F, R, 0, XF>(a, s, st);
     }
   }
   if constexpr (XF && R >= 8 && layout_pipelined<F>()) {
