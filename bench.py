@@ -118,6 +118,8 @@ def kernel_form(name: str, grid_y: int = 1, n_experts: int = 0) -> str | None:
     else None."""
     if name.startswith("void qmv::mmvq_rows_kernel<"):
         return "fused" if _targs(name)[5] == "true" else "gemv"      # <F, NC, R, P, G, XF, ...>
+    if name.startswith("void qmv::mmvq_rows1_kernel<"):
+        return "fused" if _targs(name)[3] == "true" else "gemv"      # <F, R, DEPTH, XF, TW>
     if name.startswith("void qmv::mmq_kernel<"):
         return "gemv"
     if name.startswith("qmv::quantize_q8_1_kernel"):
@@ -769,7 +771,8 @@ def main():
                                  if wl.name == "q4_k_4096x14336" and n == 1 else None),
                      "kernel": (f"mmq_kernel ({synth.TYPE_NAME[wl.wtype].upper()}, n={n}, int8 matrix cores)"
                                 if mmq_route(B, wl, n) and not fused else
-                                f"mmvq_rows_kernel ({synth.TYPE_NAME[wl.wtype].upper()}, n={n}, "
+                                f"{'mmvq_rows1_kernel' if n == 1 and wl.wtype != B.Q6_K and wl.M >= 4096 else 'mmvq_rows_kernel'} "
+                                f"({synth.TYPE_NAME[wl.wtype].upper()}, n={n}, "
                                 f"{'fp32' if fused else 'q8_1'} activation)"),
                      "bytes_per_launch": kern_bytes,
                      "avg_launch_us": round(kern_us, 3),
