@@ -366,24 +366,30 @@ static void block_q8_0(const uint8_t *blk, const uint8_t *ycol, int64_t qb,
 /* Q4_K (and Q5_K, whose codes come from another code function): per
  * sub-block t, dot1 = sum q*qy, dot2 = sum qy over its 32 elements;
  * contribution d*sc*d8*dot1 - dmin*m*d8*dot2, the min term kept apart
- * [MMVQ §一次 vec_dot 的解剖]. Sub-block t pairs with q8_1 block qb + t. */
+ * [MMVQ §一次 vec_dot 的解剖]. Sub-block t pairs with q8_1 block qb + t.
+ * The magnitude (the tolerance's error scale) sums both terms over each
+ * 16-element half of the sub-block: an evaluation may scale and sum the
+ * halves' partial dots in fp32 before they meet, and where the halves
+ * cancel, those partials exceed the sub-block's terms. */
 static void block_k_min(const uint8_t *blk, const uint8_t *ycol, int64_t qb, double *acc, double *mag,
                         int32_t *dots, int (*code)(const uint8_t *, int)) {
     const double d = orc_f16_to_f64(rd16(blk));
     const double dmin = orc_f16_to_f64(rd16(blk + 2));
     for (int t = 0; t < 8; ++t) {
-        int sc, m, dot1 = 0, dot2 = 0;
+        int sc, m, dot1 = 0, dot2 = 0, half1[2] = {0, 0}, half2[2] = {0, 0};
         orc_q4_k_scale_min(blk + 4, t, &sc, &m);
         for (int l = 0; l < 32; ++l) {
             const int qy = q8_q(ycol, qb + t, l);
             dot1 += code(blk, 32 * t + l) * qy;
             dot2 += qy;
+            half1[l / 16] += code(blk, 32 * t + l) * qy;
+            half2[l / 16] += qy;
         }
         const double d8 = q8_d(ycol, qb + t);
         const double t1 = d * sc * d8 * dot1;
         const double t2 = dmin * m * d8 * dot2;
         *acc += t1 - t2;
-        *mag += fabs(t1) + fabs(t2);
+        for (int h = 0; h < 2; ++h) *mag += fabs(d * sc * d8 * half1[h]) + fabs(dmin * m * d8 * half2[h]);
         if (dots) { dots[t] = dot1; dots[8 + t] = dot2; }
     }
 }
