@@ -84,7 +84,8 @@ def parse():
 HEADLINE_SOURCES = ["common.hpp", "q8.hpp", "formats.hpp", "plan.hpp", "mmvq_kernel.hpp", "launch.hpp",
                     "kernels_q4_k.hip", "kernels_q4_k_f32.hip", os.path.join("..", "..", "include", "mmvq.h")]
 # ... and of every measured kernel, for the per-configuration summaries
-ALL_SOURCES = HEADLINE_SOURCES + ["mmq_plan.hpp", "mmq_kernel.hpp", "kernels_mmq.hip", "kernels_q4_0.hip",
+ALL_SOURCES = HEADLINE_SOURCES + ["mmq_plan.hpp", "mmq_kernel.hpp", "mmq_launch.hpp", "kernels_mmq.hip",
+                                  "kernels_mmq_f32.hip", "kernels_q4_0.hip",
                                   "kernels_q4_0_f32.hip", "kernels_q8_0.hip", "kernels_q8_0_f32.hip",
                                   "kernels_q6_k.hip", "kernels_q6_k_f32.hip", "kernels_q4_k_id.hip",
                                   "kernels_q4_k_f32_id.hip", "kernels_q4_1.hip", "kernels_q4_1_f32.hip",
@@ -121,7 +122,7 @@ def kernel_form(name: str, grid_y: int = 1, n_experts: int = 0) -> str | None:
     if name.startswith("void qmv::mmvq_rows1_kernel<"):
         return "fused" if _targs(name)[3] == "true" else "gemv"      # <F, R, DEPTH, XF, TW>
     if name.startswith("void qmv::mmq_kernel<"):
-        return "gemv"
+        return "fused" if _targs(name)[5] == "true" else "gemv"      # <F, RT, CT, NW, G, XF>
     if name.startswith("qmv::quantize_q8_1_kernel"):
         return "quantize"
     if name.startswith("qmv::read_probe_kernel"):
@@ -487,10 +488,13 @@ def timed_replay(torch, stream, g_warm, g_timed):
     return t.ms, time.perf_counter() - t0
 
 
-def mmq_route(B, wl, n: int) -> bool:
-    """True where mmvq with q8_1 columns runs the many-column (matrix-core)
-    kernel: K a multiple of 256 and n at least the library's crossover."""
-    return wl.K % 256 == 0 and n >= B.mmvq_many_columns_min(wl.wtype, False)
+def mmq_route(B, wl, n: int, fp32: bool = False) -> bool:
+    """True where mmvq (q8_1 columns) or mmvq_f32 (fp32 columns) runs the
+    many-column (matrix-core) kernel: K a multiple of 256 and n at least the
+    library's crossover (fp32 columns: more than the row kernels' 8)."""
+    if wl.K % 256:
+        return False
+    return n > B.MAX_COLS if fp32 else n >= B.mmvq_many_columns_min(wl.wtype, False)
 
 
 def time_workload(torch, B, wl, n: int, steps: int, warmup: int, probe: bool = True, glu: bool = False):
@@ -498,39 +502,40 @@ def time_workload(torch, B, wl, n: int, steps: int, warmup: int, probe: bool = T
     form after `warmup` untimed ones, weights rotating over the copies.
     Forms: fused (mmvq_f32), two-launch step (quantize + mmvq), mat-vec alone
     (mmvq), quantizer alone, the gate/up form (mmvq_glu, SwiGLU, the next
-    weight copy as the gate matrix: twice the weight bytes) and the
-    streaming-read probe over the same weight bytes."""
+    weight copy as the gate matrix: twice the weight bytes) and its fused
+    form (mmvq_glu_f32), and the streaming-read probe over the same weight
+    bytes."""
     data, Ws, x, y, out = gpu_setup(torch, wl, n)
     C = len(Ws)
     s = torch.cuda.Stream()
     sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
     torch.cuda.synchronize()
-    fused_ok = n <= B.MAX_COLS            # the fused forms take at most 8 columns
     forms = {
         "step": lambda c: (B.mmvq_quantize_q8_1(x, wl.K, n, wl.K, y, s), B.mmvq(Ws[c], wl.wtype, wl.M, wl.K, y, n, out, s)),
         "gemv": lambda c: B.mmvq(Ws[c], wl.wtype, wl.M, wl.K, y, n, out, s),
         "glu": (lambda c: B.mmvq_glu(Ws[(c + 1) % C], Ws[c], wl.wtype, wl.M, wl.K, y, n, B.GLU_SWIGLU, out, s))
         if glu else None,
+        "glu_f32": (lambda c: B.mmvq_glu_f32(Ws[(c + 1) % C], Ws[c], wl.wtype, wl.M, wl.K, x, n, wl.K,
+                                             B.GLU_SWIGLU, out, s)) if glu else None,
         "quant": lambda c: B.mmvq_quantize_q8_1(x, wl.K, n, wl.K, y, s),
-        "fused": (lambda c: B.mmvq_f32(Ws[c], wl.wtype, wl.M, wl.K, x, n, wl.K, out, s)) if fused_ok else None,
+        "fused": lambda c: B.mmvq_f32(Ws[c], wl.wtype, wl.M, wl.K, x, n, wl.K, out, s),
         "probe": (lambda c: B.mmvq_read_probe(Ws[c], wl.weight_bytes, sink, s)) if probe else None,
     }
     res = {"copies": C, "steps": steps, "warmup": warmup}
     # the two step forms must agree before either is timed: bit for bit,
-    # except where the q8_1 form runs the many-column kernel (another
+    # except where only the q8_1 form runs the many-column kernel (another
     # summation order; a loose relative check)
-    if fused_ok:
-        ref = torch.empty_like(out)
-        B.mmvq_quantize_q8_1(x, wl.K, n, wl.K, y, s)
-        B.mmvq(Ws[0], wl.wtype, wl.M, wl.K, y, n, ref, s)
-        B.mmvq_f32(Ws[0], wl.wtype, wl.M, wl.K, x, n, wl.K, out, s)
-        torch.cuda.synchronize()
-        if mmq_route(B, wl, n):
-            same = bool(((ref - out).abs() <= 1e-4 * ref.abs().max() + 1e-6).all())
-        else:
-            same = torch.equal(ref.view(torch.int32), out.view(torch.int32))
-        if not same:
-            raise RuntimeError(f"{wl.name} n={n}: fused and two-launch results differ")
+    ref = torch.empty_like(out)
+    B.mmvq_quantize_q8_1(x, wl.K, n, wl.K, y, s)
+    B.mmvq(Ws[0], wl.wtype, wl.M, wl.K, y, n, ref, s)
+    B.mmvq_f32(Ws[0], wl.wtype, wl.M, wl.K, x, n, wl.K, out, s)
+    torch.cuda.synchronize()
+    if mmq_route(B, wl, n) != mmq_route(B, wl, n, fp32=True):
+        same = bool(((ref - out).abs() <= 1e-4 * ref.abs().max() + 1e-6).all())
+    else:
+        same = torch.equal(ref.view(torch.int32), out.view(torch.int32))
+    if not same:
+        raise RuntimeError(f"{wl.name} n={n}: fused and two-launch results differ")
     for key, launch in forms.items():
         if launch is None:
             res[f"{key}_us"] = None
@@ -769,8 +774,9 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": (measured_traffic("fused" if fused else "gemv")
                                  if wl.name == "q4_k_4096x14336" and n == 1 else None),
-                     "kernel": (f"mmq_kernel ({synth.TYPE_NAME[wl.wtype].upper()}, n={n}, int8 matrix cores)"
-                                if mmq_route(B, wl, n) and not fused else
+                     "kernel": (f"mmq_kernel ({synth.TYPE_NAME[wl.wtype].upper()}, n={n}, int8 matrix cores, "
+                                f"{'fp32' if fused else 'q8_1'} columns)"
+                                if mmq_route(B, wl, n, fp32=fused) else
                                 f"{'mmvq_rows1_kernel' if n == 1 and wl.wtype != B.Q6_K and wl.M >= 4096 else 'mmvq_rows_kernel'} "
                                 f"({synth.TYPE_NAME[wl.wtype].upper()}, n={n}, "
                                 f"{'fp32' if fused else 'q8_1'} activation)"),
@@ -817,6 +823,7 @@ def main():
                 gb = algorithmic_bytes(w, nn) / (r["gemv_us"] * 1e-6) / 1e9
                 print(json.dumps({"workload": name, "n": nn, "gemv_us": round(r["gemv_us"], 3),
                                   "glu_us": None if r["glu_us"] is None else round(r["glu_us"], 3),
+                                  "glu_f32_us": None if r["glu_f32_us"] is None else round(r["glu_f32_us"], 3),
                                   "quantize_us": round(r["quant_us"], 3),
                                   "two_launch_step_us": round(r["step_us"], 3),
                                   "fused_us": None if r["fused_us"] is None else round(r["fused_us"], 3),

@@ -141,12 +141,13 @@ enum {
 
 /* Largest number of columns of the weight-matrix calls without expert ids
  * (mmvq, mmvq_glu, mmvq_ex and their fp32 forms) and of the quantizer.
- * mmvq, mmvq_glu and mmvq_ex with q8_1 activations and K a multiple of 256
- * run on the matrix cores from mmvq_many_columns_min columns
- * [MMVQ §多个 token 时]; the fp32 forms and K not a multiple of 256 take
- * more than MMVQ_MAX_COLS columns as groups of at most MMVQ_MAX_COLS
- * columns through the row kernels (each group reads the weights again).
- * The expert-indexed calls take at most MMVQ_MAX_COLS tokens. */
+ * With K a multiple of 256 these calls run on the matrix cores
+ * [MMVQ §多个 token 时]: with q8_1 activations from mmvq_many_columns_min
+ * columns, with fp32 activations beyond MMVQ_MAX_COLS columns. With K not a
+ * multiple of 256 they take more than MMVQ_MAX_COLS columns as groups of at
+ * most MMVQ_MAX_COLS columns through the row kernels (each group reads the
+ * weights again). The expert-indexed calls take at most MMVQ_MAX_COLS
+ * tokens. */
 #define MMVQ_MAX_COLS_BATCH 256
 
 /* Fewest columns from which mmvq / mmvq_ex (gated = 0) or mmvq_glu /
@@ -154,11 +155,14 @@ enum {
  * multiple of 256, run on the many-column (matrix-core) kernel instead of
  * the row kernels, written to *n_min: the measured crossover of the two on
  * MI355X (without a gate Q5_K 5, Q4_K 6, Q6_K 7, Q4_0 / Q5_0 / Q8_0 8,
- * Q4_1 / Q5_1 9; with one Q5_K 5, Q4_K 7, the others 9). Below it and in
- * the fp32 forms the row kernels run, so there the fp32 form of a call is
- * bit-identical to quantize + its q8_1 form; at or above it the two agree
- * within the accumulation-order tolerance. Host-only; touches no device.
- * Errors: MMVQ_ERR_NULL (n_min NULL), MMVQ_ERR_TYPE (weight type). */
+ * Q4_1 / Q5_1 9; with one Q5_K 5, Q4_K 7, the others 9). The fp32 forms
+ * take that kernel beyond MMVQ_MAX_COLS columns (it quantizes its columns
+ * in every row-tile workgroup, which costs more than the row kernels'
+ * prologue up to there). The two kernels order their sums differently: from
+ * n_min to MMVQ_MAX_COLS columns the fp32 form of a call agrees with
+ * quantize + its q8_1 form within the accumulation-order tolerance, at
+ * every other n bit for bit. Host-only; touches no device. Errors:
+ * MMVQ_ERR_NULL (n_min NULL), MMVQ_ERR_TYPE (weight type). */
 int mmvq_many_columns_min(int type, int gated, int *n_min);
 
 /* Block geometry of a type: elements per block and bytes per block
@@ -196,11 +200,11 @@ int mmvq_quantize_q8_1(const float *x, int64_t K, int64_t n, int64_t ldx,
  * than 2^24 units (K > 2^29 for Q4_0 and Q8_0, K > 2^30 for Q4_K and Q6_K)
  * and M*K > 2^40 return MMVQ_ERR_SHAPE (the same limits hold for every
  * entry point below except the many-column path).
- * With K a multiple of 256, n >= 9 (Q4_K: n >= 6) takes the many-column
- * path, where the integer dots of 16 rows x 16 columns x 32 elements come
- * from one int8 matrix-core instruction and the same block scales are
- * applied per 32-element block (Q6_K: per 16-element half); K / 256 up to
- * 2^24 there. */
+ * With K a multiple of 256, n >= mmvq_many_columns_min takes the
+ * many-column path, where the integer dots of 16 rows x 16 columns x 32
+ * elements come from one int8 matrix-core instruction and the same block
+ * scales are applied per 32-element block (Q6_K: per 16-element half);
+ * K / 256 up to 2^24 there. */
 int mmvq(const void *W, int type, int64_t M, int64_t K,
          const void *y_q, int64_t n, float *out, void *stream);
 
@@ -237,16 +241,18 @@ int mmvq_id_glu(const void *W_gate, const void *W_up,
 
 /* Fused quantize + product, fp32 activations [MMVQ §激活的量化, §融合].
  * The four calls below equal mmvq_quantize_q8_1 followed by mmvq, mmvq_glu,
- * mmvq_id and mmvq_id_glu respectively, bit for bit (one exception: Q4_K
- * mmvq with 6 <= n <= 8 runs the many-column kernel on q8_1 columns, whose
- * sums are ordered differently; mmvq_f32 then agrees with it within the
- * tolerance, its q8_1 codes and scales still identical): each kernel quantizes
+ * mmvq_id and mmvq_id_glu respectively, bit for bit (except from
+ * mmvq_many_columns_min to MMVQ_MAX_COLS columns, where the q8_1 form runs
+ * the many-column kernel and the two agree within the accumulation-order
+ * tolerance, the q8_1 codes and scales still identical): each kernel quantizes
  * the slice of x that its lanes multiply, with the quantizer's arithmetic,
- * in registers, so the q8_1 columns are never written to memory and one
- * launch replaces two. Column j of x starts at x + j*ldx (ldx >= K floats;
- * the first K values are used; x 4-byte aligned). Each workgroup re-reads
- * x (K*n*4 bytes) from cache; there is no y_q. Same requirements and error
- * codes as the q8_1 forms, plus MMVQ_ERR_SHAPE for ldx < K. */
+ * in registers (the row kernels in their prologue; the many-column kernel
+ * each 32-value block it stages, before the block goes to LDS), so the
+ * q8_1 columns are never written to memory and one launch replaces two.
+ * Column j of x starts at x + j*ldx (ldx >= K floats; the first K values
+ * are used; x 4-byte aligned). Each workgroup re-reads its slice of x
+ * from cache and quantizes it again; there is no y_q. Same requirements
+ * and error codes as the q8_1 forms, plus MMVQ_ERR_SHAPE for ldx < K. */
 int mmvq_f32(const void *W, int type, int64_t M, int64_t K, const float *x,
              int64_t n, int64_t ldx, float *out, void *stream);
 

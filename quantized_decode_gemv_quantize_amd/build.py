@@ -24,7 +24,8 @@ SOURCES = ["kernels_q4_k_f32.hip", "kernels_q4_k_f32_id.hip", "kernels_q4_k.hip"
            "kernels_q6_k_f32.hip", "kernels_q6_k.hip", "kernels_q4_0_f32.hip", "kernels_q8_0_f32.hip",
            "kernels_q4_0.hip", "kernels_q8_0.hip", "kernels_q5_k_f32.hip", "kernels_q5_k.hip",
            "kernels_q4_1_f32.hip", "kernels_q5_0_f32.hip", "kernels_q5_1_f32.hip", "kernels_q4_1.hip",
-           "kernels_q5_0.hip", "kernels_q5_1.hip", "kernels_mmq.hip", "api.hip", "quantize.hip", "probe.hip"]
+           "kernels_q5_0.hip", "kernels_q5_1.hip", "kernels_mmq.hip", "kernels_mmq_f32.hip", "api.hip", "quantize.hip",
+           "probe.hip"]
 
 # Packed fp32 VALU instructions stay disabled (hipcc forms them from plain
 # float code otherwise); fp32 division is correctly rounded and fp32
@@ -45,6 +46,7 @@ HIPCC_FLAGS = [
 # accumulation registers each value would first be copied out).
 SOURCE_FLAGS = {
     "kernels_mmq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "kernels_mmq_f32.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

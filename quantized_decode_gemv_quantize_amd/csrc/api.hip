@@ -109,18 +109,22 @@ bool mmq_type(int type) {
          type == MMVQ_Q5_0 || type == MMVQ_Q5_1 || type == MMVQ_Q5_K;
 }
 
-// Many columns (up to MMVQ_MAX_COLS_BATCH): the MFMA kernel, q8_1
-// activations, K a multiple of 256, with or without a gate (W_gate NULL);
-// the whole epilogue applies.
-int mmq_common(const void* W, const void* W_gate, int type, int64_t M, int64_t K, const void* y_q, int64_t n,
+// Many columns (up to MMVQ_MAX_COLS_BATCH): the MFMA kernel, q8_1 or fp32
+// activations (the fp32 form quantizes its staged blocks in the kernel, to
+// the same codes), K a multiple of 256, with or without a gate (W_gate
+// NULL); the whole epilogue applies.
+int mmq_common(const void* W, const void* W_gate, int type, int64_t M, int64_t K, const ActIn& in, int64_t n,
                const mmvq_epilogue* epi, float* out, void* stream) {
-  if (!W || !y_q || !out) return MMVQ_ERR_NULL;
+  const bool f32 = in.x != nullptr;
+  if (!W || !(f32 || in.y_q) || !out) return MMVQ_ERR_NULL;
   const Dispatch* d = dispatch_for(type, false);
   if (!d) return MMVQ_ERR_TYPE;
   if (!mmq_type(type)) return MMVQ_ERR_TYPE;
   if (M < 1 || K < 1 || K % 256 != 0 || n < 1 || n > MMVQ_MAX_COLS_BATCH) return MMVQ_ERR_SHAPE;
   if (M > (int64_t(1) << 40) / K || K / 256 > (int64_t(1) << 24)) return MMVQ_ERR_SHAPE;
-  if (!aligned(W, 16) || !aligned(y_q, 16) || !aligned(out, 4)) return MMVQ_ERR_ALIGN;
+  if (f32 && (in.ldx < K || in.ldx > (int64_t(1) << 40))) return MMVQ_ERR_SHAPE;
+  if (!aligned(W, 16) || !aligned(out, 4)) return MMVQ_ERR_ALIGN;
+  if (f32 ? !aligned(in.x, 4) : !aligned(in.y_q, 16)) return MMVQ_ERR_ALIGN;
   if (W_gate && !aligned(W_gate, 16)) return MMVQ_ERR_ALIGN;
   RowArgs ra{};
   int rc = set_epilogue(epi, W_gate != nullptr, &ra);
@@ -128,7 +132,9 @@ int mmq_common(const void* W, const void* W_gate, int type, int64_t M, int64_t K
   MmqArgs a{};
   a.W = static_cast<const uint8_t*>(W);
   a.Wg = static_cast<const uint8_t*>(W_gate);
-  a.y = static_cast<const uint8_t*>(y_q);
+  a.y = static_cast<const uint8_t*>(in.y_q);
+  a.x = in.x;
+  a.ldx = in.ldx;
   a.out = out;
   a.up_bias = ra.up_bias;
   a.up_scale = ra.up_scale;
@@ -141,7 +147,8 @@ int mmq_common(const void* W, const void* W_gate, int type, int64_t M, int64_t K
   a.ycol_bytes = K / 32 * kQ8Bytes;
   a.n = static_cast<int>(n);
   a.nsb = static_cast<int>(K / 256);
-  return launch_mmq(type, a, static_cast<hipStream_t>(stream));
+  return f32 ? launch_mmq_f32(type, a, static_cast<hipStream_t>(stream))
+             : launch_mmq(type, a, static_cast<hipStream_t>(stream));
 }
 
 // Columns from which the matrix-core kernel takes a q8_1 product (K a
@@ -169,17 +176,21 @@ int mmq_min_cols(int type, bool gate) {
 
 // Plain or gate/up product with an optional epilogue (W_gate NULL: no gate).
 // More than MMVQ_MAX_COLS columns outside the matrix-core kernel's forms
-// (fp32 activations, K not a multiple of 256) run as groups of at most
+// (K not a multiple of 256) run as groups of at most
 // MMVQ_MAX_COLS columns through the row kernels, each group reading the
 // weights again; all arguments are checked before the first group is
 // enqueued.
 int rows_common(const void* W_up, const void* W_gate, int type, int64_t M, int64_t K, const ActIn& in, int64_t n,
                 const mmvq_epilogue* epi, float* out, void* stream) {
-  const bool mmq_form = !in.x && K % 256 == 0 && mmq_type(type);
-  if (mmq_form && mmq_min_cols(type, W_gate != nullptr) > 0 && n >= mmq_min_cols(type, W_gate != nullptr))
-    return mmq_common(W_up, W_gate, type, M, K, in.y_q, n, epi, out, stream);
+  // fp32 columns take the matrix-core kernel only beyond MMVQ_MAX_COLS: it
+  // quantizes its columns again in every row-tile workgroup, which up to
+  // MMVQ_MAX_COLS columns costs more than the row kernels' prologue
+  // (4096x14336 Q4_K, 8 columns: 36.6 us against 28.3)
+  const bool mmq_form = K % 256 == 0 && mmq_type(type);
+  const int mmq_from = in.x ? MMVQ_MAX_COLS + 1 : mmq_min_cols(type, W_gate != nullptr);
+  if (mmq_form && n >= mmq_from) return mmq_common(W_up, W_gate, type, M, K, in, n, epi, out, stream);
 #ifdef QMV_TUNING
-  if (getenv("MMVQ_FORCE_MMQ") && mmq_form) return mmq_common(W_up, W_gate, type, M, K, in.y_q, n, epi, out, stream);
+  if (getenv("MMVQ_FORCE_MMQ") && mmq_form) return mmq_common(W_up, W_gate, type, M, K, in, n, epi, out, stream);
 #endif
   if (n > MMVQ_MAX_COLS_BATCH) return MMVQ_ERR_SHAPE;
   const int64_t n0 = n < MMVQ_MAX_COLS ? n : MMVQ_MAX_COLS;

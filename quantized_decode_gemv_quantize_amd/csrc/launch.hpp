@@ -320,5 +320,6 @@ int launch_read_probe(const uint8_t* src, int64_t bytes, uint32_t* sink, hipStre
 
 struct MmqArgs;
 int launch_mmq(int type, const MmqArgs& a, hipStream_t st);
+int launch_mmq_f32(int type, const MmqArgs& a, hipStream_t st);   // a.x: fp32 columns
 
 }  // namespace qmv

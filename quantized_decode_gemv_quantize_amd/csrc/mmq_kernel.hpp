@@ -466,11 +466,30 @@ template <> struct MmqStep<Q6K> {
   }
 };
 
+// Largest magnitude of the 32 fp32 values of a staged block: each v_max3
+// takes two magnitudes (the values are finite, so the NaN quieting that a
+// plain fmaxf adds per operand is not needed); equal to the quantizer's
+// amax, since a maximum is exact in any order.
+__device__ __forceinline__ float block_amax(const u32x4 (&v)[8]) {
+  float m0 = 0.0f, m1 = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    asm("v_max3_f32 %0, |%1|, |%2|, %0" : "+v"(m0) : "v"(v[k].x), "v"(v[k].y));
+    asm("v_max3_f32 %0, |%1|, |%2|, %0" : "+v"(m1) : "v"(v[k].z), "v"(v[k].w));
+  }
+  return fmaxf(m0, m1);
+}
+
 // G = 2: the gate/up form. The up (W) and gate (Wg) rows of a tile are
 // staged side by side and each runs the format's step against the same B
 // tiles; the epilogue sums both over the waves and applies the scales,
 // biases and GLU of the row kernels' epilogue.
-template <class F, int RT, int CT, int NW, int G>
+//
+// XF: the columns arrive as fp32 (the fused form). Each lane quantizes the
+// q8_1 blocks it staged, with the stand-alone quantizer's arithmetic (same
+// amax, scale, codes and fp16 {d, s}), and writes them into the B tiles, so
+// the tiles and the result are those of the q8_1 form bit for bit.
+template <class F, int RT, int CT, int NW, int G, bool XF>
 __global__ void __launch_bounds__(NW * kWave, 8 / NW) mmq_kernel(MmqArgs a) {
   using Gm = MmqGeom<F>;
   const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
@@ -501,9 +520,9 @@ __global__ void __launch_bounds__(NW * kWave, 8 / NW) mmq_kernel(MmqArgs a) {
 
   MmqOffsets<F, RT, CT> off;
   // staged loads -> LDS: A loads into their rows' images, B piece k at byte
-  // 16k of the B tiles
-  auto store_stage = [&](const MmqStage<F, RT, CT, G>& st, int sb) QMV_INLINE {
-    uint8_t* lb = &lds.b[0][0][0];
+  // 16k of the B tiles (fp32 columns: each staged block quantized into its
+  // 36 bytes at column * 288 + block * 36)
+  auto store_a = [&](const MmqStage<F, RT, CT, G, XF>& st, int sb) QMV_INLINE {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       uint8_t* la = &lds.m[g].a[0][0][0];
@@ -516,10 +535,32 @@ __global__ void __launch_bounds__(NW * kWave, 8 / NW) mmq_kernel(MmqArgs a) {
         }
       }
     }
+  };
+  // (fp32 columns: each slot's registers take the next step's values as
+  // soon as the slot is quantized)
+  auto store_b = [&](MmqStage<F, RT, CT, G, XF>& st, int next) QMV_INLINE {
+    uint8_t* lb = &lds.b[0][0][0];
+    if constexpr (XF) {
 #pragma unroll
-    for (int j = 0; j < mmq_b_slots<CT>(); ++j) {
-      const int k = lane + kWave * j;
-      if (k < kMmqBPieces * CT) *reinterpret_cast<u32x4*>(lb + 16 * k) = st.b[j];
+      for (int j = 0; j < mmq_x_slots<CT>(); ++j) {
+        int col, blk, c;
+        mmq_x_pair(lane, j, 0, a.n, col, blk, c);
+        const float d = q8_scale(block_amax(st.x[j]));
+        uint32_t codes[8];
+        int sq = 0;
+        q8_quant_block<8>(st.x[j], d, codes, sq);
+        mmq_stage_load_x<F, RT, CT, G>(a, col_base, lane, next, j, st);
+        uint32_t* dst = reinterpret_cast<uint32_t*>(lb + col * 288 + blk * 36);
+        dst[0] = f2h_bits(d) | (f2h_bits(q8_s(d, sq)) << 16);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) dst[1 + k] = codes[k];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < mmq_b_slots<CT>(); ++j) {
+        const int k = lane + kWave * j;
+        if (k < kMmqBPieces * CT) *reinterpret_cast<u32x4*>(lb + 16 * k) = st.b[j];
+      }
     }
   };
 
@@ -527,16 +568,25 @@ __global__ void __launch_bounds__(NW * kWave, 8 / NW) mmq_kernel(MmqArgs a) {
   // computed from LDS. The prefetch is unconditional (past the end it
   // re-reads the last step, from cache) so every path has the same loads in
   // flight. (Two steps in flight, in a second register buffer, measured
-  // slower at 16 columns: 16.3 -> 17.3 us at 4096x14336.)
+  // slower at 16 columns: 16.3 -> 17.3 us at 4096x14336.) The fp32 form
+  // issues the next weights before it quantizes the staged columns, and the
+  // next values of each column slot once that slot is quantized.
   if (sb0 < sb1) {
     mmq_offsets<F, RT, CT>(a, row_base, col_base, lane, off);
-    MmqStage<F, RT, CT, G> st;
-    mmq_stage_load<F, RT, CT, G>(a, row_base, col_base, lane, sb0, off, st);
+    MmqStage<F, RT, CT, G, XF> st;
+    mmq_stage_load<F, RT, CT, G, XF>(a, row_base, col_base, lane, sb0, off, st);
     for (int sb = sb0; sb < sb1; ++sb) {
       mmq_lds_fence();             // the previous step's reads are done
-      store_stage(st, sb);
       const int next = sb + 1 < sb1 ? sb + 1 : sb;
-      mmq_stage_load<F, RT, CT, G>(a, row_base, col_base, lane, next, off, st);
+      store_a(st, sb);
+      if constexpr (XF) {
+        mmq_stage_load_a<F, RT, CT, G, XF>(a, row_base, lane, next, off, st);
+        __builtin_amdgcn_sched_barrier(0);
+        store_b(st, next);
+      } else {
+        store_b(st, next);
+        mmq_stage_load<F, RT, CT, G, XF>(a, row_base, col_base, lane, next, off, st);
+      }
       __builtin_amdgcn_sched_barrier(0);
       mmq_lds_fence();
 #pragma unroll

@@ -13,6 +13,8 @@ struct MmqArgs {
   const uint8_t* W;          // up (or plain) weights
   const uint8_t* Wg;         // gate weights (gate/up form), same layout; NULL without a gate
   const uint8_t* y;          // q8_1 columns
+  const float* x;            // fp32 columns instead (the fused form), column stride ldx; NULL: y
+  int64_t ldx;
   float* out;                // out[c*M + r]
   // epilogue: up = up*up_scale[0] + up_bias[r], the same for the gate, then
   // glu(glu_op, gate, up, glu_limit) in the gate/up form; NULL pointers are
@@ -116,11 +118,29 @@ constexpr int mmq_a_slots() { return (mmq_a_pieces<F>() * RT + kWave - 1) / kWav
 template <int CT>
 constexpr int mmq_b_slots() { return (kMmqBPieces * CT + kWave - 1) / kWave; }
 
-template <class F, int RT, int CT, int G>
-struct MmqStage {
+// The fused form (fp32 columns) stages the step's activations raw: each of
+// the 16*CT*8 (column, block) pairs of the step is one lane's 32 values
+// (pair k = lane + 64*j: column tile k / 128, column (k % 128) / 8, block
+// k % 8), quantized by that lane before they go to LDS.
+template <int CT>
+constexpr int mmq_x_slots() { return 16 * 8 * CT / kWave; }
+template <int CT, bool XF> struct MmqBStage { u32x4 b[mmq_b_slots<CT>()]; };
+template <int CT> struct MmqBStage<CT, true> { u32x4 x[mmq_x_slots<CT>()][8]; };
+
+template <class F, int RT, int CT, int G, bool XF = false>
+struct MmqStage : MmqBStage<CT, XF> {
   u32x4 a[G][mmq_a_slots<F, RT>()];   // [0] up (or plain) rows, [1] gate rows
-  u32x4 b[mmq_b_slots<CT>()];
 };
+
+// Column and block of fused-form pair slot j of a lane (column within the
+// workgroup's CT tiles; clamped to n - 1 like the q8_1 columns).
+__host__ __device__ __forceinline__ void mmq_x_pair(int lane, int j, int col_base, int n, int& col, int& blk,
+                                                    int& c) {
+  const int k = lane + kWave * j;
+  col = 16 * (k / 128) + (k % 128) / 8;
+  blk = k % 8;
+  c = col_base + col < n ? col_base + col : n - 1;
+}
 
 // Load slots of a lane, fixed for the whole K range: for A the byte offset
 // of the slot's row from the tile's first row, its row within the tile
@@ -162,13 +182,13 @@ __host__ __device__ __forceinline__ void mmq_offsets(const MmqArgs& a, int64_t r
 
 // The staging loads of step sb; loads past the end (slot k >= the tile's
 // loads) are not issued. The gate rows (G = 2) sit at the same offsets of
-// Wg as the up rows of W.
-template <class F, int RT, int CT, int G>
-__device__ __forceinline__ void mmq_stage_load(const MmqArgs& a, int64_t row_base, int col_base, int lane, int sb,
-                                               const MmqOffsets<F, RT, CT>& o, MmqStage<F, RT, CT, G>& st) {
+// Wg as the up rows of W. Weights (A) and activations (B) separately, so the
+// fp32 form can have the next weights in flight while it quantizes.
+template <class F, int RT, int CT, int G, bool XF>
+__device__ __forceinline__ void mmq_stage_load_a(const MmqArgs& a, int64_t row_base, int lane, int sb,
+                                                 const MmqOffsets<F, RT, CT>& o, MmqStage<F, RT, CT, G, XF>& st) {
   using Gm = MmqGeom<F>;
   const int64_t tile_off = row_base * a.row_bytes;
-  const uint8_t* yb = a.y + (static_cast<int64_t>(col_base) * a.ycol_bytes + static_cast<int64_t>(sb) * 288);
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const uint8_t* W = g == 0 ? a.W : a.Wg;
@@ -182,9 +202,38 @@ __device__ __forceinline__ void mmq_stage_load(const MmqArgs& a, int64_t row_bas
       }
     }
   }
+}
+
+// fp32 columns: the 32 values of pair slot j of a lane at step sb
+template <class F, int RT, int CT, int G>
+__device__ __forceinline__ void mmq_stage_load_x(const MmqArgs& a, int col_base, int lane, int sb, int j,
+                                                 MmqStage<F, RT, CT, G, true>& st) {
+  int col, blk, c;
+  mmq_x_pair(lane, j, col_base, a.n, col, blk, c);
+  const float* p = a.x + (static_cast<int64_t>(c) * a.ldx + static_cast<int64_t>(sb) * 256 + 32 * blk);
 #pragma unroll
-  for (int j = 0; j < mmq_b_slots<CT>(); ++j)
-    if (lane + kWave * j < kMmqBPieces * CT) st.b[j] = ld_a16_x4(yb + o.b[j]);
+  for (int k = 0; k < 8; ++k) st.x[j][k] = ld_x4(reinterpret_cast<const uint8_t*>(p + 4 * k));
+}
+
+template <class F, int RT, int CT, int G, bool XF>
+__device__ __forceinline__ void mmq_stage_load_b(const MmqArgs& a, int col_base, int lane, int sb,
+                                                 const MmqOffsets<F, RT, CT>& o, MmqStage<F, RT, CT, G, XF>& st) {
+  if constexpr (XF) {
+#pragma unroll
+    for (int j = 0; j < mmq_x_slots<CT>(); ++j) mmq_stage_load_x<F, RT, CT, G>(a, col_base, lane, sb, j, st);
+  } else {
+    const uint8_t* yb = a.y + (static_cast<int64_t>(col_base) * a.ycol_bytes + static_cast<int64_t>(sb) * 288);
+#pragma unroll
+    for (int j = 0; j < mmq_b_slots<CT>(); ++j)
+      if (lane + kWave * j < kMmqBPieces * CT) st.b[j] = ld_a16_x4(yb + o.b[j]);
+  }
+}
+
+template <class F, int RT, int CT, int G, bool XF = false>
+__device__ __forceinline__ void mmq_stage_load(const MmqArgs& a, int64_t row_base, int col_base, int lane, int sb,
+                                               const MmqOffsets<F, RT, CT>& o, MmqStage<F, RT, CT, G, XF>& st) {
+  mmq_stage_load_a<F, RT, CT, G, XF>(a, row_base, lane, sb, o, st);
+  mmq_stage_load_b<F, RT, CT, G, XF>(a, col_base, lane, sb, o, st);
 }
 
 // Output of partial value v (0 .. RT*CT*4-1) of a lane with k-slice q and

@@ -58,17 +58,19 @@ __device__ __forceinline__ uint32_t pack_low_bytes(uint32_t w0, uint32_t w1, uin
 
 // Codes of the 4*W values of one q8_1 block that the lane holds (word k of
 // `out` packs the codes of v[k]), their sum added to `sum`; equal to
-// q8_quant4 on every word, at about a third of the arithmetic:
-//   r = 1/d correctly rounded, once per block; q1 = x*r. With u = 2^-24,
-//   |q1 - RN(x/d)| <= 3.001*u*|q1| (one rounding in r, one in the product,
-//   one in RN(x/d)), and |q1| <= 127.0001 since |x| <= amax and
-//   d = RN(amax/127). So when q1 is farther than 2^-15 (> 3.001*u*128) from
-//   every half-integer, no half-integer lies between q1 and RN(x/d) or on
-//   either, and both round to the same integer: then rounding q1 to nearest
-//   (adding and removing 1.5*2^23, whose ulp is 1) gives the code, whose
+// q8_quant4 on every word, at about a quarter of the arithmetic:
+//   r = 1/d correctly rounded, once per block; p = x*r (exact product).
+//   With u = 2^-24, |p - x/d| <= u*|x/d| (the rounding of r) and
+//   |RN(x/d) - x/d| <= u*|x/d|, where |x/d| <= 127.0000076 since |x| <= amax
+//   and d = RN(amax/127): so |p - RN(x/d)| <= 254.00002*u < 2^-16 - 2^-25.
+//   One fma rounds p to an integer (adding 1.5*2^23, whose ulp is 1: ties to
+//   even), the bias comes off exactly, and a second fma gives p minus that
+//   integer with an error of at most 2^-25. When that residue is below
+//   1/2 - 2^-16, RN(x/d) lies strictly inside the same unit interval around
+//   the integer, which is then round(RN(x/d)) (no tie can occur), and its
 //   two's complement low byte is the low byte of the biased sum. Otherwise
-//   (rare), or when d is 0 or subnormal (r out of range), the block is redone
-//   with exact quotients.
+//   (about 2^-15 of the values), or when d is 0 or subnormal (r out of
+//   range), the block is redone with exact quotients.
 template <int W>
 __device__ __forceinline__ void q8_quant_block(const u32x4 (&v)[W], float d, uint32_t (&out)[W], int& sum) {
   constexpr float kBias = 0x1.8p23f;
@@ -81,10 +83,10 @@ __device__ __forceinline__ void q8_quant_block(const u32x4 (&v)[W], float d, uin
     uint32_t m[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float q = __uint_as_float(v[k][e]) * r;
-      const float biased = q + kBias;
-      const float rq = biased - kBias;                 // q rounded to nearest, exact
-      near = near || fabsf(q - rq) >= 0.5f - 0x1p-15f;
+      const float x = __uint_as_float(v[k][e]);
+      const float biased = fmaf(x, r, kBias);          // x*r rounded to an integer, biased
+      const float rq = biased - kBias;                 // that integer, exact
+      near = near || fabsf(fmaf(x, r, -rq)) >= 0.5f - 0x1p-16f;
       m[e] = __float_as_uint(biased);
     }
     out[k] = pack_low_bytes(m[0], m[1], m[2], m[3]);

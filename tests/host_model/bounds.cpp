@@ -226,18 +226,26 @@ static void case_block_dots(const char* name, int64_t M, int64_t K, int nc) {
 // the workgroup-to-tile mapping the kernel uses; every output stored exactly
 // once; every A load lands inside its row's LDS image (and the bytes the
 // step's arithmetic reads are covered by loads of that step). G = 2: the
-// gate/up form, whose gate loads must stay inside the gate matrix.
-template <class F, int RT, int CT, int NW, int G = 1>
+// gate/up form, whose gate loads must stay inside the gate matrix. XF: fp32
+// columns (column stride K + 3), whose staged blocks must stay inside x and
+// whose quantized blocks must write every byte of the B tiles exactly once.
+template <class F, int RT, int CT, int NW, int G = 1, bool XF = false>
 static void case_mmq(const char* name, int64_t M, int64_t K, int n) {
   using Gm = MmqGeom<F>;
   const int64_t row_bytes = K / F::kQK * F::kBlockBytes, ycol = K / 32 * kQ8Bytes;
+  const int64_t ldx = K + 3, xfloats = (n - 1) * ldx + K;
   uint8_t* W = alloc16(M * row_bytes);
   uint8_t* Wg = G == 2 ? alloc16(M * row_bytes) : nullptr;
-  uint8_t* y = alloc16(n * ycol);
-  if (G == 2) begin({{W, W + M * row_bytes}, {Wg, Wg + M * row_bytes}, {y, y + n * ycol}});
-  else begin({{W, W + M * row_bytes}, {y, y + n * ycol}});
+  uint8_t* y = XF ? nullptr : alloc16(n * ycol);
+  uint8_t* x = XF ? alloc16(xfloats * 4) : nullptr;
+  uint8_t* act = XF ? x : y;
+  const int64_t act_bytes = XF ? xfloats * 4 : n * ycol;
+  if (G == 2) begin({{W, W + M * row_bytes}, {Wg, Wg + M * row_bytes}, {act, act + act_bytes}});
+  else begin({{W, W + M * row_bytes}, {act, act + act_bytes}});
   MmqArgs a{};
   a.W = W; a.Wg = Wg; a.y = y; a.M = M; a.row_bytes = row_bytes; a.ycol_bytes = ycol; a.n = n;
+  a.x = reinterpret_cast<const float*>(x);
+  a.ldx = ldx;
   a.nsb = static_cast<int>(K / 256);
   a.gx = static_cast<int>((M + 16 * RT - 1) / (16 * RT));
   a.gy = (n + 16 * CT - 1) / (16 * CT);
@@ -258,11 +266,24 @@ static void case_mmq(const char* name, int64_t M, int64_t K, int n) {
       for (int sb = sb0; sb < sb1; ++sb) {
         // bytes of each row image the step's loads write
         std::vector<std::vector<char>> img(16 * RT, std::vector<char>(Gm::kRowLds, 0));
+        std::vector<char> btile(kMmqBPieces * 16 * CT, 0);
         for (int lane = 0; lane < 64; ++lane) {
           MmqOffsets<F, RT, CT> off;
           mmq_offsets<F, RT, CT>(a, row_base, col_base, lane, off);
-          MmqStage<F, RT, CT, G> st;
-          mmq_stage_load<F, RT, CT, G>(a, row_base, col_base, lane, sb, off, st);
+          MmqStage<F, RT, CT, G, XF> st;
+          mmq_stage_load<F, RT, CT, G, XF>(a, row_base, col_base, lane, sb, off, st);
+          if constexpr (XF) {
+            for (int j = 0; j < mmq_x_slots<CT>(); ++j) {
+              int col, blk, c;
+              mmq_x_pair(lane, j, 0, n, col, blk, c);
+              const int at = col * 288 + blk * 36;
+              if (col < 0 || col >= 16 * CT || at + 36 > kMmqBPieces * 16 * CT) {
+                ok = false;
+                continue;
+              }
+              for (int b = 0; b < 36; ++b) btile[at + b] += 1;
+            }
+          }
           for (int j = 0; j < mmq_a_slots<F, RT>(); ++j) {
             if (lane + kWave * j >= mmq_a_pieces<F>() * RT) continue;
             const int64_t ro = row_base * row_bytes + off.a[j];
@@ -277,7 +298,9 @@ static void case_mmq(const char* name, int64_t M, int64_t K, int n) {
             for (int b = 0; b < len; ++b) img[off.arow[j]][at + b] += 1;
           }
         }
-        // every byte of every row's step is written exactly once
+        // every byte of every row's step (and, fp32 columns, of the B
+        // tiles) is written exactly once
+        for (size_t b = 0; XF && b < btile.size() && ok; ++b) ok = btile[b] == 1;
         for (int r = 0; r < 16 * RT && ok; ++r) {
           int64_t rr = row_base + r;
           rr = rr < M ? rr : M - 1;
@@ -299,10 +322,11 @@ static void case_mmq(const char* name, int64_t M, int64_t K, int n) {
   }
   for (int64_t i = 0; i < groups && ok; ++i) ok = tiles[i] == 1;
   for (int64_t i = 0; i < M * n && ok; ++i) ok = stores[i] == 1;
-  report(G == 2 ? "mmq_glu" : "mmq", ok, name, M, K, n, 1);
+  report(XF ? (G == 2 ? "mmq_glu_f32" : "mmq_f32") : (G == 2 ? "mmq_glu" : "mmq"), ok, name, M, K, n, 1);
   free(W);
   free(Wg);
   free(y);
+  free(x);
 }
 
 template <class F>
@@ -316,6 +340,10 @@ static void case_mmq_all(const char* name, int64_t M, int64_t K, int n) {
   case_mmq<F, 2, 2, 4, 2>(name, M, K, n);
   case_mmq<F, 2, 1, 8, 2>(name, M, K, n);
   case_mmq<F, 1, 1, 8, 2>(name, M, K, n);
+  case_mmq<F, 2, 1, 4, 1, true>(name, M, K, n);
+  case_mmq<F, 1, 1, 8, 1, true>(name, M, K, n);
+  case_mmq<F, 2, 1, 8, 2, true>(name, M, K, n);
+  case_mmq<F, 1, 1, 4, 2, true>(name, M, K, n);
 }
 
 // quantizer: 8 lanes per q8_1 block, 4 floats each (clamped to block 0 when
@@ -548,6 +576,10 @@ int main(int argc, char** argv) {
     case_mmq<Q5K, 2, 1, 8>("q5_k", 4096, 14336, 16);
     case_mmq<Q4K, 2, 1, 8, 2>("q4_k", 14336, 4096, 16);
     case_mmq<Q4K, 2, 2, 4, 2>("q4_k", 14336, 4096, 64);
+    case_mmq<Q4K, 2, 1, 8, 1, true>("q4_k", 4096, 14336, 16);
+    case_mmq<Q4K, 2, 1, 4, 1, true>("q4_k", 4096, 14336, 64);
+    case_mmq<Q4K, 2, 1, 8, 2, true>("q4_k", 14336, 4096, 16);
+    case_mmq<Q6K, 2, 1, 4, 1, true>("q6_k", 4096, 4096, 37);
     case_id<Q4K>("q4_k", 14336, 4096, 8, 8, 1);
     case_id<Q4K2>("q4_k2", 14336, 4096, 8, 8, 1);
   }

@@ -2,11 +2,16 @@
 mmvq_glu_f32, mmvq_id_f32, mmvq_id_glu_f32).
 
 Each must equal, bit for bit, the q8_1 quantizer followed by the matching
-q8_1 entry point on the same inputs (the kernel quantizes in its prologue
-with the quantizer's arithmetic), and be within the oracle tolerance of the
-oracle's quantize-then-multiply. Activations include the quantizer's edge
-cases (zero, tie, subnormal, large and constant blocks) and column strides
-that are not multiples of 4 floats.
+q8_1 entry point on the same inputs (the row kernels quantize in their
+prologue, the many-column kernel in its staging, both with the quantizer's
+arithmetic; where the q8_1 form already runs the many-column kernel at 8 or
+fewer columns and the fp32 form the row kernels, both against the oracle
+instead), and be within the oracle tolerance of the oracle's
+quantize-then-multiply. Activations include the quantizer's edge cases
+(zero, tie, subnormal, large and constant blocks) and column strides that
+are not multiples of 4 floats; column counts span the row kernels (1..8),
+the many-column kernel (from the library's crossover up to 256) and the
+column groups of the forms it does not take.
 """
 import numpy as np
 import pytest
@@ -41,9 +46,10 @@ def _empty(rows, M):
 
 
 def _mmq_route(wtype, K, n, gated=False):
-    """The q8_1 form runs the many-column kernel from the library's crossover
-    (K a multiple of 256) while the fused form keeps the row kernel up to
-    8 columns: there the two agree within the tolerance, not bit for bit."""
+    """Where the q8_1 form runs the many-column kernel (K a multiple of 256,
+    from the library's crossover) while the fp32 form keeps the row kernels
+    (up to 8 columns): there the two sum in different orders and agree
+    within the tolerance, not bit for bit."""
     return K % 256 == 0 and B.mmvq_many_columns_min(wtype, gated) <= n <= B.MAX_COLS
 
 
@@ -81,7 +87,15 @@ FUSED_CASES = [(Q4_0, 37, 96, 1, 0), (Q4_0, 300, 1024, 3, 5), (Q4_0, 129, 16384,
                (Q4_1, 4096, 4096, 1, 0), (Q5_1, 4096, 4096, 1, 2), (Q5_K, 4096, 4096, 1, 1),
                (Q5_K, 2048, 14336, 1, 0),
                # the one-column single-team-per-workgroup kernel, ragged last team
-               (Q4_K, 4099, 14336, 1, 3), (Q4_1, 4100, 8192, 1, 0), (Q5_1, 2055, 16384, 1, 1)]
+               (Q4_K, 4099, 14336, 1, 3), (Q4_1, 4100, 8192, 1, 0), (Q5_1, 2055, 16384, 1, 1),
+               # many columns: the matrix-core kernel quantizing its staged blocks
+               # (ragged row and column tiles, up to the 256-column maximum), and
+               # column groups through the row kernels where K is not a multiple of 256
+               (Q4_K, 300, 4096, 16, 3), (Q4_K, 129, 14336, 33, 1), (Q4_K, 37, 512, 256, 2),
+               (Q4_K, 1000, 2048, 6, 0), (Q6_K, 37, 768, 9, 2), (Q6_K, 300, 2304, 40, 0),
+               (Q4_0, 300, 1024, 40, 5), (Q8_0, 65, 2048, 17, 0), (Q4_1, 33, 1280, 24, 1),
+               (Q5_0, 70, 768, 9, 0), (Q5_1, 17, 1280, 64, 2), (Q5_K, 129, 4096, 16, 1),
+               (Q5_K, 9000, 512, 5, 3), (Q4_0, 37, 96, 20, 1), (Q8_0, 33, 1056, 12, 2)]
 
 
 @pytest.mark.parametrize("wtype,M,K,n,pad", FUSED_CASES,
@@ -99,7 +113,6 @@ def test_mmvq_f32(O, wtype, M, K, n, pad):
     y = O.quantize_q8_1(x, K)
     ref, mag, _ = O.mmvq(W, wtype, M, K, y, n)
     if _mmq_route(wtype, K, n):
-        # the q8_1 form on the many-column kernel: both forms against the oracle
         assert_close(host(two), ref, mag, f"mmvq {TNAME[wtype]} {M}x{K} n={n}")
     else:
         _same(fused, two, f"mmvq_f32 {TNAME[wtype]} {M}x{K} n={n}")
@@ -109,7 +122,11 @@ def test_mmvq_f32(O, wtype, M, K, n, pad):
 GLU_F32 = [(Q4_K, 300, 4096, 1, B.GLU_SWIGLU), (Q4_K, 37, 512, 4, B.GLU_PLAIN),
            (Q4_0, 300, 1024, 2, B.GLU_SWIGLU), (Q6_K, 37, 768, 3, B.GLU_SWIGLU),
            (Q4_K, 129, 14336, 8, B.GLU_SWIGLU), (Q4_K, 17, 65536, 2, B.GLU_SWIGLU),
-           (Q8_0, 9, 16416, 8, B.GLU_PLAIN)]
+           (Q8_0, 9, 16416, 8, B.GLU_PLAIN),
+           # many columns (matrix-core kernel, and column groups for K % 256 != 0)
+           (Q4_K, 300, 4096, 16, B.GLU_SWIGLU), (Q4_K, 129, 2048, 7, B.GLU_GEGLU),
+           (Q5_K, 129, 2048, 9, B.GLU_GEGLU), (Q6_K, 37, 768, 33, B.GLU_SWIGLU),
+           (Q8_0, 65, 1024, 12, B.GLU_PLAIN), (Q4_0, 17, 1056, 11, B.GLU_SWIGLU)]
 
 
 @pytest.mark.parametrize("wtype,M,K,n,op", GLU_F32,
@@ -132,7 +149,6 @@ def test_mmvq_glu_f32(O, wtype, M, K, n, op):
     u, mu, _ = O.mmvq(Wu, wtype, M, K, y, n)
     ref = O.mmvq_glu(Wg, Wu, wtype, M, K, y, n, op)
     tol = glu_tolerance(g, u, mg, mu, ref, op)
-    # the q8_1 form on the many-column kernel: both forms against the oracle
     for out in ([fused, two] if routed else [fused]):
         got = host(out).astype(np.float64)
         bad = ~(np.abs(got - ref) <= tol)
@@ -224,7 +240,8 @@ def test_mmvq_id_glu_f32_moe_workload(O):
 WORKLOADS_F32 = [("q4_k_4096x14336", 1), ("q4_k_4096x14336", 2), ("q4_k_4096x14336", 8),
                  ("q4_k_14336x4096", 4), ("q6_k_128256x4096", 1), ("q6_k_128256x4096", 2),
                  ("q4_0_256x1024", 1), ("q8_0_4096x14336", 1), ("q4_1_4096x14336", 1),
-                 ("q5_0_4096x14336", 1), ("q5_1_4096x14336", 1), ("q5_k_4096x14336", 1)]
+                 ("q5_0_4096x14336", 1), ("q5_1_4096x14336", 1), ("q5_k_4096x14336", 1),
+                 ("q4_k_4096x14336", 16), ("q5_k_4096x14336", 16), ("q8_0_4096x14336", 32)]
 
 
 @pytest.mark.parametrize("name,n", WORKLOADS_F32, ids=[f"{a}-n{b}" for a, b in WORKLOADS_F32])
@@ -245,11 +262,36 @@ def test_mmvq_f32_workload(O, name, n):
     ref, mag = O.mmvq_threaded(W, wl.wtype, M, K, y, n)
     got = host(fused)
     if _mmq_route(wl.wtype, wl.K, n):
-        # the two-step form runs the many-column kernel: both against the oracle
         assert_close(host(two), ref, mag, f"mmvq {name} n={n}")
     else:
         _same(fused, two, f"mmvq_f32 {name} n={n}")
     assert_close(got, ref, mag, f"mmvq_f32 {name} n={n}")
+
+
+@pytest.mark.parametrize("wtype", [Q4_K, Q5_K])
+def test_mmvq_glu_f32_many_columns_workload(O, wtype):
+    """The gate/up form at the FFN-up shape (14336x4096) with 16 fp32
+    columns, the launch the benchmark times: bit-identical to the quantizer
+    followed by the q8_1 gate/up call, and every output against the
+    oracle's gate/up product within the propagated tolerance."""
+    M, K, n = 14336, 4096, 16
+    announce(f"mmvq_glu_f32 many columns workload {TNAME[wtype]} M={M} K={K} n={n}")
+    rng = np.random.default_rng(515 + wtype)
+    Wu, Wg = synth.weights(wtype, M, K, rng), synth.weights(wtype, M, K, rng)
+    x = synth.activations(K, n, rng)
+    Wgd, Wud, xd = dev(Wg), dev(Wu), dev(x)
+    fused, two = _empty(n, M), _empty(n, M)
+    B.mmvq_glu_f32(Wgd, Wud, wtype, M, K, xd, n, K, B.GLU_SWIGLU, fused)
+    B.mmvq_glu(Wgd, Wud, wtype, M, K, gpu_quantize(x, K), n, B.GLU_SWIGLU, two)
+    _same(fused, two, f"mmvq_glu_f32 workload {TNAME[wtype]}")
+    y = O.quantize_q8_1(x, K)
+    u, mu = O.mmvq_threaded(Wu, wtype, M, K, y, n)
+    g, mg = O.mmvq_threaded(Wg, wtype, M, K, y, n)
+    ref = O.mmvq_glu(Wg, Wu, wtype, M, K, y, n, B.GLU_SWIGLU)
+    tol = glu_tolerance(g, u, mg, mu, ref, B.GLU_SWIGLU)
+    got = host(fused).astype(np.float64)
+    bad = ~(np.abs(got - ref) <= tol)
+    assert not bad.any(), f"first bad at {np.argwhere(bad)[0]}"
 
 
 def test_f32_graph_replay():

@@ -3,9 +3,9 @@ int8 matrix cores; every weight format with q8_1 activations, with or
 without a gate) through the C ABI: against the oracle within the stated tolerance for
 every row and column, at shapes with ragged row and column tiles, at the
 FFN-down and LM-head workloads, with the epilogue's scale and bias; the
-forms beyond 8 columns that run as column groups through the row kernels
-(a gate, fp32 activations, K not a multiple of 256); and the argument checks
-of the path."""
+fp32-activation and gate/up forms beyond 8 columns, and the forms that run
+as column groups through the row kernels (K not a multiple of 256); and the
+argument checks of the path."""
 import numpy as np
 import pytest
 
@@ -107,10 +107,10 @@ def test_many_columns_glu_workload(O, wtype):
     assert not bad.any(), f"first bad at {np.argwhere(bad)[0]}"
 
 
-# Beyond 8 columns the forms the matrix-core kernel does not take (fp32
-# activations, K not a multiple of 256) run as groups of 8 columns through
-# the row kernels; the gate/up form with q8_1 columns takes the matrix-core
-# kernel when K is a multiple of 256.
+# Beyond 8 columns the forms the matrix-core kernel does not take (K not a
+# multiple of 256) run as groups of 8 columns through the row kernels; the
+# fp32 and gate/up forms take the matrix-core kernel when K is a multiple of
+# 256.
 GROUPS = [(Q4_0, 37, 96, 12), (Q8_0, 300, 1056, 17), (Q6_K, 17, 768, 9), (Q4_K, 129, 4096, 20),
           (B.Q4_1, 37, 1056, 12), (B.Q5_0, 17, 1056, 9), (B.Q5_1, 33, 512, 20), (B.Q5_K, 65, 2048, 16)]
 
@@ -192,4 +192,9 @@ def test_many_columns_argument_checks():
     assert L.mmvq(p + 4, B.Q8_0, 1, 96, q, 9, o, s) == B.ERR_ALIGN     # column groups check first
     assert L.mmvq_glu(p, p, Q4_K, 1, 256, q, 257, 1, o, s) == B.ERR_SHAPE
     assert L.mmvq_f32(p, Q4_K, 1, 256, o, 257, 256, o, s) == B.ERR_SHAPE
+    # the fp32 form on the matrix-core kernel checks its column stride and alignment
+    assert L.mmvq_f32(p, Q4_K, 1, 256, o, 9, 255, o, s) == B.ERR_SHAPE
+    assert L.mmvq_f32(p, Q4_K, 1, 256, o + 2, 9, 256, o, s) == B.ERR_ALIGN
+    assert L.mmvq_f32(p + 4, Q4_K, 1, 256, o, 9, 256, o, s) == B.ERR_ALIGN
+    assert L.mmvq_glu_f32(p, p + 4, Q4_K, 1, 256, o, 9, 256, 1, o, s) == B.ERR_ALIGN
     torch.cuda.synchronize()
