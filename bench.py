@@ -491,10 +491,10 @@ def timed_replay(torch, stream, g_warm, g_timed):
 def mmq_route(B, wl, n: int, fp32: bool = False) -> bool:
     """True where mmvq (q8_1 columns) or mmvq_f32 (fp32 columns) runs the
     many-column (matrix-core) kernel: K a multiple of 256 and n at least the
-    library's crossover (fp32 columns: more than the row kernels' 8)."""
+    library's crossover for that form."""
     if wl.K % 256:
         return False
-    return n > B.MAX_COLS if fp32 else n >= B.mmvq_many_columns_min(wl.wtype, False)
+    return n >= B.mmvq_many_columns_min(wl.wtype, False, fp32=fp32)
 
 
 def time_workload(torch, B, wl, n: int, steps: int, warmup: int, probe: bool = True, glu: bool = False):

@@ -141,9 +141,8 @@ enum {
 
 /* Largest number of columns of the weight-matrix calls without expert ids
  * (mmvq, mmvq_glu, mmvq_ex and their fp32 forms) and of the quantizer.
- * With K a multiple of 256 these calls run on the matrix cores
- * [MMVQ §多个 token 时]: with q8_1 activations from mmvq_many_columns_min
- * columns, with fp32 activations beyond MMVQ_MAX_COLS columns. With K not a
+ * With K a multiple of 256 these calls run on the matrix cores from
+ * mmvq_many_columns_min columns [MMVQ §多个 token 时]; with K not a
  * multiple of 256 they take more than MMVQ_MAX_COLS columns as groups of at
  * most MMVQ_MAX_COLS columns through the row kernels (each group reads the
  * weights again). The expert-indexed calls take at most MMVQ_MAX_COLS
@@ -151,19 +150,20 @@ enum {
 #define MMVQ_MAX_COLS_BATCH 256
 
 /* Fewest columns from which mmvq / mmvq_ex (gated = 0) or mmvq_glu /
- * mmvq_ex with a gate matrix (gated != 0), with q8_1 activations and K a
- * multiple of 256, run on the many-column (matrix-core) kernel instead of
- * the row kernels, written to *n_min: the measured crossover of the two on
- * MI355X (without a gate Q5_K 5, Q4_K 6, Q6_K 7, Q4_0 / Q5_0 / Q8_0 8,
- * Q4_1 / Q5_1 9; with one Q5_K 5, Q4_K 7, the others 9). The fp32 forms
- * take that kernel beyond MMVQ_MAX_COLS columns (it quantizes its columns
- * in every row-tile workgroup, which costs more than the row kernels'
- * prologue up to there). The two kernels order their sums differently: from
- * n_min to MMVQ_MAX_COLS columns the fp32 form of a call agrees with
- * quantize + its q8_1 form within the accumulation-order tolerance, at
- * every other n bit for bit. Host-only; touches no device. Errors:
- * MMVQ_ERR_NULL (n_min NULL), MMVQ_ERR_TYPE (weight type). */
-int mmvq_many_columns_min(int type, int gated, int *n_min);
+ * mmvq_ex with a gate matrix (gated != 0), with K a multiple of 256 and
+ * q8_1 activations (fp32 = 0) or fp32 activations (fp32 != 0: mmvq_f32,
+ * mmvq_glu_f32, mmvq_ex with x), run on the many-column (matrix-core)
+ * kernel instead of the row kernels, written to *n_min: the measured
+ * crossover of the two on MI355X. q8_1 activations: without a gate Q5_K 5,
+ * Q4_K 6, Q6_K 7, Q4_0 / Q5_0 / Q8_0 8, Q4_1 / Q5_1 9; with one Q5_K 5,
+ * Q4_K 7, the others 9. fp32 activations (the kernel quantizes its columns
+ * in every row-tile workgroup): without a gate Q6_K 6, Q5_K 8, the others
+ * 9; with one Q4_0 / Q5_0 / Q5_K 4, the others 5. The two kernels order
+ * their sums differently: where a call's fp32 and q8_1 forms run different
+ * kernels, they agree within the accumulation-order tolerance, elsewhere
+ * bit for bit. Host-only; touches no device. Errors: MMVQ_ERR_NULL (n_min
+ * NULL), MMVQ_ERR_TYPE (weight type). */
+int mmvq_many_columns_min(int type, int gated, int fp32, int *n_min);
 
 /* Block geometry of a type: elements per block and bytes per block
  * (Q4_0 32/18, Q4_1 32/20, Q5_0 32/22, Q5_1 32/24, Q8_0 32/34, Q4_K 256/144,
@@ -241,9 +241,9 @@ int mmvq_id_glu(const void *W_gate, const void *W_up,
 
 /* Fused quantize + product, fp32 activations [MMVQ §激活的量化, §融合].
  * The four calls below equal mmvq_quantize_q8_1 followed by mmvq, mmvq_glu,
- * mmvq_id and mmvq_id_glu respectively, bit for bit (except from
- * mmvq_many_columns_min to MMVQ_MAX_COLS columns, where the q8_1 form runs
- * the many-column kernel and the two agree within the accumulation-order
+ * mmvq_id and mmvq_id_glu respectively, bit for bit (except at column
+ * counts where only one of the two forms runs the many-column kernel, see
+ * mmvq_many_columns_min: there the two agree within the accumulation-order
  * tolerance, the q8_1 codes and scales still identical): each kernel quantizes
  * the slice of x that its lanes multiply, with the quantizer's arithmetic,
  * in registers (the row kernels in their prologue; the many-column kernel

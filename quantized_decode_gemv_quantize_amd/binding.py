@@ -50,7 +50,7 @@ _EP = ctypes.POINTER(Epilogue)
 
 _SIGS = {
     "mmvq_type_info": (_int, [_int, ctypes.POINTER(_int), ctypes.POINTER(_int)]),
-    "mmvq_many_columns_min": (_int, [_int, _int, ctypes.POINTER(_int)]),
+    "mmvq_many_columns_min": (_int, [_int, _int, _int, ctypes.POINTER(_int)]),
     "mmvq_quantize_q8_1": (_int, [_p, _i64, _i64, _i64, _p, _p]),
     "mmvq": (_int, [_p, _int, _i64, _i64, _p, _i64, _p, _p]),
     "mmvq_glu": (_int, [_p, _p, _int, _i64, _i64, _p, _i64, _int, _p, _p]),
@@ -133,9 +133,10 @@ def mmvq_type_info(wtype: int) -> tuple[int, int]:
     return e.value, b.value
 
 
-def mmvq_many_columns_min(wtype: int, gated: bool) -> int:
+def mmvq_many_columns_min(wtype: int, gated: bool, fp32: bool = False) -> int:
     n = _int()
-    _check("mmvq_many_columns_min", lib().mmvq_many_columns_min(wtype, int(bool(gated)), ctypes.byref(n)))
+    _check("mmvq_many_columns_min",
+           lib().mmvq_many_columns_min(wtype, int(bool(gated)), int(bool(fp32)), ctypes.byref(n)))
     return n.value
 
 

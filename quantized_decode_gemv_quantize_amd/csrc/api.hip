@@ -174,6 +174,29 @@ int mmq_min_cols(int type, bool gate) {
   }
 }
 
+// The same for fp32 activations, where the matrix-core kernel quantizes its
+// columns again in every row-tile workgroup (about 35 us at these shapes
+// for any n <= 16) and the row kernels quantize in their prologue: measured
+// at 4096x14336 without a gate and 14336x4096 with one (us, row kernels /
+// matrix cores). Without a gate Q6_K from 6 (45.2 / 42.6; 159 / 43 at 7),
+// Q5_K from 8 (36.6 / 36.3), the others never below 9 (Q4_K 25.3 / 38.2 at
+// 8). With a gate, where the row kernels hold the raw columns of two weight
+// streams: Q4_0, Q5_0 and Q5_K from 4 (Q5_K 50.6 / 39.4), the others from 5
+// (Q4_K 50.1 / 35.0; 33.3 / 35.6 at 4). 0: not a type.
+int mmq_min_cols_f32(int type, bool gate) {
+  switch (type) {
+    case MMVQ_Q4_0:
+    case MMVQ_Q5_0: return gate ? 4 : MMVQ_MAX_COLS + 1;
+    case MMVQ_Q5_K: return gate ? 4 : 8;
+    case MMVQ_Q6_K: return gate ? 5 : 6;
+    case MMVQ_Q4_K:
+    case MMVQ_Q8_0:
+    case MMVQ_Q4_1:
+    case MMVQ_Q5_1: return gate ? 5 : MMVQ_MAX_COLS + 1;
+    default: return 0;
+  }
+}
+
 // Plain or gate/up product with an optional epilogue (W_gate NULL: no gate).
 // More than MMVQ_MAX_COLS columns outside the matrix-core kernel's forms
 // (K not a multiple of 256) run as groups of at most
@@ -182,12 +205,8 @@ int mmq_min_cols(int type, bool gate) {
 // enqueued.
 int rows_common(const void* W_up, const void* W_gate, int type, int64_t M, int64_t K, const ActIn& in, int64_t n,
                 const mmvq_epilogue* epi, float* out, void* stream) {
-  // fp32 columns take the matrix-core kernel only beyond MMVQ_MAX_COLS: it
-  // quantizes its columns again in every row-tile workgroup, which up to
-  // MMVQ_MAX_COLS columns costs more than the row kernels' prologue
-  // (4096x14336 Q4_K, 8 columns: 36.6 us against 28.3)
   const bool mmq_form = K % 256 == 0 && mmq_type(type);
-  const int mmq_from = in.x ? MMVQ_MAX_COLS + 1 : mmq_min_cols(type, W_gate != nullptr);
+  const int mmq_from = in.x ? mmq_min_cols_f32(type, W_gate != nullptr) : mmq_min_cols(type, W_gate != nullptr);
   if (mmq_form && n >= mmq_from) return mmq_common(W_up, W_gate, type, M, K, in, n, epi, out, stream);
 #ifdef QMV_TUNING
   if (getenv("MMVQ_FORCE_MMQ") && mmq_form) return mmq_common(W_up, W_gate, type, M, K, in, n, epi, out, stream);
@@ -254,9 +273,9 @@ int id_common(const void* W_gate, const void* W_up, int64_t expert_stride_bytes,
 
 extern "C" {
 
-int mmvq_many_columns_min(int type, int gated, int* n_min) {
+int mmvq_many_columns_min(int type, int gated, int fp32, int* n_min) {
   if (!n_min) return MMVQ_ERR_NULL;
-  const int m = mmq_min_cols(type, gated != 0);
+  const int m = fp32 ? mmq_min_cols_f32(type, gated != 0) : mmq_min_cols(type, gated != 0);
   if (m == 0) return MMVQ_ERR_TYPE;
   *n_min = m;
   return MMVQ_OK;

@@ -44,14 +44,20 @@ def test_many_columns_min(L):
     """The documented crossover table, and its errors."""
     plain = {B.Q5_K: 5, B.Q4_K: 6, B.Q6_K: 7, B.Q4_0: 8, B.Q5_0: 8, B.Q8_0: 8, B.Q4_1: 9, B.Q5_1: 9}
     gated = {B.Q5_K: 5, B.Q4_K: 7, B.Q6_K: 9, B.Q4_0: 9, B.Q5_0: 9, B.Q8_0: 9, B.Q4_1: 9, B.Q5_1: 9}
+    plain_f32 = {B.Q5_K: 8, B.Q4_K: 9, B.Q6_K: 6, B.Q4_0: 9, B.Q5_0: 9, B.Q8_0: 9, B.Q4_1: 9, B.Q5_1: 9}
+    gated_f32 = {B.Q5_K: 4, B.Q4_K: 5, B.Q6_K: 5, B.Q4_0: 4, B.Q5_0: 4, B.Q8_0: 5, B.Q4_1: 5, B.Q5_1: 5}
     for t in plain:
         assert B.mmvq_many_columns_min(t, False) == plain[t]
         assert B.mmvq_many_columns_min(t, True) == gated[t]
+        assert B.mmvq_many_columns_min(t, False, fp32=True) == plain_f32[t]
+        assert B.mmvq_many_columns_min(t, True, fp32=True) == gated_f32[t]
     for t in (5, B.Q8_1, -1):
-        with pytest.raises(B.MMVQError) as e:
-            B.mmvq_many_columns_min(t, False)
-        assert e.value.code == B.ERR_TYPE
-    assert L.mmvq_many_columns_min(B.Q4_K, 0, None) == B.ERR_NULL
+        for f in (False, True):
+            with pytest.raises(B.MMVQError) as e:
+                B.mmvq_many_columns_min(t, False, fp32=f)
+            assert e.value.code == B.ERR_TYPE
+    assert L.mmvq_many_columns_min(B.Q4_K, 0, 0, None) == B.ERR_NULL
+    assert L.mmvq_many_columns_min(B.Q4_K, 1, 1, None) == B.ERR_NULL
 
 
 def test_strerror(L):

@@ -4,10 +4,9 @@ mmvq_glu_f32, mmvq_id_f32, mmvq_id_glu_f32).
 Each must equal, bit for bit, the q8_1 quantizer followed by the matching
 q8_1 entry point on the same inputs (the row kernels quantize in their
 prologue, the many-column kernel in its staging, both with the quantizer's
-arithmetic; where the q8_1 form already runs the many-column kernel at 8 or
-fewer columns and the fp32 form the row kernels, both against the oracle
-instead), and be within the oracle tolerance of the oracle's
-quantize-then-multiply. Activations include the quantizer's edge cases
+arithmetic; where only one of the two forms runs the many-column kernel,
+both against the oracle instead), and be within the oracle tolerance of the
+oracle's quantize-then-multiply. Activations include the quantizer's edge cases
 (zero, tie, subnormal, large and constant blocks) and column strides that
 are not multiples of 4 floats; column counts span the row kernels (1..8),
 the many-column kernel (from the library's crossover up to 256) and the
@@ -46,11 +45,13 @@ def _empty(rows, M):
 
 
 def _mmq_route(wtype, K, n, gated=False):
-    """Where the q8_1 form runs the many-column kernel (K a multiple of 256,
-    from the library's crossover) while the fp32 form keeps the row kernels
-    (up to 8 columns): there the two sum in different orders and agree
-    within the tolerance, not bit for bit."""
-    return K % 256 == 0 and B.mmvq_many_columns_min(wtype, gated) <= n <= B.MAX_COLS
+    """Where exactly one of the q8_1 and fp32 forms runs the many-column
+    kernel (K a multiple of 256, each form from its own crossover): there
+    the two sum in different orders and agree within the tolerance, not bit
+    for bit."""
+    if K % 256:
+        return False
+    return (n >= B.mmvq_many_columns_min(wtype, gated)) != (n >= B.mmvq_many_columns_min(wtype, gated, fp32=True))
 
 
 def _same(a, b, what):
@@ -95,7 +96,8 @@ FUSED_CASES = [(Q4_0, 37, 96, 1, 0), (Q4_0, 300, 1024, 3, 5), (Q4_0, 129, 16384,
                (Q4_K, 1000, 2048, 6, 0), (Q6_K, 37, 768, 9, 2), (Q6_K, 300, 2304, 40, 0),
                (Q4_0, 300, 1024, 40, 5), (Q8_0, 65, 2048, 17, 0), (Q4_1, 33, 1280, 24, 1),
                (Q5_0, 70, 768, 9, 0), (Q5_1, 17, 1280, 64, 2), (Q5_K, 129, 4096, 16, 1),
-               (Q5_K, 9000, 512, 5, 3), (Q4_0, 37, 96, 20, 1), (Q8_0, 33, 1056, 12, 2)]
+               (Q5_K, 9000, 512, 5, 3), (Q4_0, 37, 96, 20, 1), (Q8_0, 33, 1056, 12, 2),
+               (Q6_K, 300, 2048, 6, 1), (Q6_K, 129, 4096, 8, 0), (Q5_K, 300, 2048, 8, 2)]
 
 
 @pytest.mark.parametrize("wtype,M,K,n,pad", FUSED_CASES,
@@ -126,7 +128,12 @@ GLU_F32 = [(Q4_K, 300, 4096, 1, B.GLU_SWIGLU), (Q4_K, 37, 512, 4, B.GLU_PLAIN),
            # many columns (matrix-core kernel, and column groups for K % 256 != 0)
            (Q4_K, 300, 4096, 16, B.GLU_SWIGLU), (Q4_K, 129, 2048, 7, B.GLU_GEGLU),
            (Q5_K, 129, 2048, 9, B.GLU_GEGLU), (Q6_K, 37, 768, 33, B.GLU_SWIGLU),
-           (Q8_0, 65, 1024, 12, B.GLU_PLAIN), (Q4_0, 17, 1056, 11, B.GLU_SWIGLU)]
+           (Q8_0, 65, 1024, 12, B.GLU_PLAIN), (Q4_0, 17, 1056, 11, B.GLU_SWIGLU),
+           # the gate/up fp32 form on the many-column kernel from 4 or 5 columns
+           (Q4_0, 300, 1024, 4, B.GLU_SWIGLU), (B.Q5_0, 129, 2048, 6, B.GLU_GEGLU),
+           (Q5_K, 65, 1024, 4, B.GLU_SWIGLU), (Q4_K, 300, 2048, 5, B.GLU_SWIGLU),
+           (Q6_K, 37, 768, 5, B.GLU_PLAIN), (Q8_0, 129, 1024, 8, B.GLU_SWIGLU),
+           (B.Q4_1, 65, 512, 7, B.GLU_SWIGLU), (B.Q5_1, 33, 1280, 6, B.GLU_GEGLU)]
 
 
 @pytest.mark.parametrize("wtype,M,K,n,op", GLU_F32,
@@ -247,8 +254,9 @@ WORKLOADS_F32 = [("q4_k_4096x14336", 1), ("q4_k_4096x14336", 2), ("q4_k_4096x143
 @pytest.mark.parametrize("name,n", WORKLOADS_F32, ids=[f"{a}-n{b}" for a, b in WORKLOADS_F32])
 def test_mmvq_f32_workload(O, name, n):
     """Workload sizes in the launch configuration the benchmark times: all
-    rows bit-identical to the two-step path (Q4_K at 6..8 columns: both
-    forms against the oracle instead), and every row against the oracle."""
+    rows bit-identical to the two-step path (where only one of the two
+    forms runs the many-column kernel: both against the oracle instead),
+    and every row against the oracle."""
     wl = synth.BY_NAME[name]
     announce(f"mmvq_f32 workload {name} n={n}")
     d = synth.make(wl, n)
