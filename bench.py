@@ -697,7 +697,8 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              f"(the mat-vec shards by rows across GPUs, see DESIGN.md)", file=sys.stderr)
+              f"(across GPUs the mat-vec would shard by rows, each GPU running this kernel on its share)",
+              file=sys.stderr)
         sys.exit(2)
     import torch
 
