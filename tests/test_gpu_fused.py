@@ -302,28 +302,41 @@ def test_mmvq_glu_f32_many_columns_workload(O, wtype):
     assert not bad.any(), f"first bad at {np.argwhere(bad)[0]}"
 
 
-def test_f32_graph_replay():
+# (n, gated): the row kernel, the many-column kernel on fp32 columns, and
+# its gate/up form (both forms on the many-column kernel at these n)
+GRAPH_CASES = [(2, False), (16, False), (8, True)]
+
+
+@pytest.mark.parametrize("n,gated", GRAPH_CASES, ids=[f"n{c[0]}-{'glu' if c[1] else 'plain'}" for c in GRAPH_CASES])
+def test_f32_graph_replay(n, gated):
     """One fused launch captured in a HIP graph on a side stream, replayed
     with new activations copied in between (eager work and synchronization
     between replays): every replay equals the eager two-step result."""
     import torch
-    announce("mmvq_f32 graph replay")
-    rng = np.random.default_rng(78)
+    announce(f"mmvq_f32 graph replay n={n} gated={gated}")
+    rng = np.random.default_rng(78 + n)
     M, K = 1000, 4096
     W = dev(synth.weights(Q4_K, M, K, rng))
-    xs = [dev(synth.activations(K, 2, rng)) for _ in range(3)]
+    Wg = dev(synth.weights(Q4_K, M, K, rng))
+    xs = [dev(synth.activations(K, n, rng)) for _ in range(3)]
     eager = []
     for xv in xs:
-        o = _empty(2, M)
-        B.mmvq(W, Q4_K, M, K, B.quantize(xv), 2, o)
+        o = _empty(n, M)
+        if gated:
+            B.mmvq_glu(Wg, W, Q4_K, M, K, B.quantize(xv), n, B.GLU_SWIGLU, o)
+        else:
+            B.mmvq(W, Q4_K, M, K, B.quantize(xv), n, o)
         eager.append(o)
     torch.cuda.synchronize()
     x_in = xs[0].clone()
-    out = _empty(2, M)
+    out = _empty(n, M)
     side = torch.cuda.Stream()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=side):
-        B.mmvq_f32(W, Q4_K, M, K, x_in, 2, K, out, side)
+        if gated:
+            B.mmvq_glu_f32(Wg, W, Q4_K, M, K, x_in, n, K, B.GLU_SWIGLU, out, side)
+        else:
+            B.mmvq_f32(W, Q4_K, M, K, x_in, n, K, out, side)
     for rep in range(6):
         x_in.copy_(xs[rep % 3])
         torch.cuda.synchronize()
