@@ -4,8 +4,9 @@ Default workload: Q4_K weights, M = 4096 rows x K = 14336, n = 1 activation
 column (the FFN down-projection shape of a 7B/8B-class model), fp32 output.
 One step is one pass of the hot path over one activation: quantize the fp32
 activation to q8_1, then the quantized mat-vec against a weight matrix. The
-step runs as one fused launch (mmvq_f32: the kernel quantizes its slice of
-the activation in its prologue) unless ``--step two`` asks for the two
+step runs as one fused launch (mmvq_f32: the row kernel quantizes its slice
+of the activation in its prologue, the many-column kernel each block it
+stages) unless ``--step two`` asks for the two
 launches (mmvq_quantize_q8_1, then mmvq); both forms are timed and reported.
 
 Measurement:
