@@ -479,6 +479,26 @@ def pin_q4_k_e4(O):
     assert out == e["out"] and mag == e["mag"], (out, mag)
 
 
+def pin_k_min_magnitude_halves(O):
+    """The tolerance's error scale for Q4_K and Q5_K sums both terms over each
+    16-element half of a sub-block (an fp32 evaluation may scale the halves'
+    partial dots before they meet). Hand-worked block: d = 1, dmin = 0,
+    sc = 1 and m = 0 for all 8 sub-blocks (scale bytes 01 01 01 01 00 00 00 00
+    01 01 01 01 by the 6-bit packing: sub-blocks 0-3 take the low 6 bits of
+    bytes 0-3 and 4-7, sub-blocks 4-7 the nibbles of bytes 8-11), every code
+    1 (qs bytes 0x11; Q5_K: qh bytes 0, so the fifth bits are 0), and q8_1
+    blocks with d8 = 1, qy = +1 on elements 0-15 and -1 on 16-31. Each half
+    dot is +16 or -16 and each sub-block's dot 0: the result is 0, the
+    magnitude 8 sub-blocks x 2 halves x 16 = 256 (it would be 0 over whole
+    sub-blocks)."""
+    hdr = h2b("0x3C00") + h2b("0x0000") + bytes([1, 1, 1, 1, 0, 0, 0, 0, 1, 1, 1, 1])
+    y = np.frombuffer(q8_1_block("0x3C00", "0x0000", [1] * 16 + [-1] * 16) * 8, dtype=np.uint8)
+    for wtype, blk in ((Q4_K, hdr + bytes([0x11]) * 128), (Q5_K, hdr + bytes(32) + bytes([0x11]) * 128)):
+        out, mag, dots = _run_block(O, wtype, blk, y, 256)
+        assert list(dots[0][:8]) == [0] * 8 and list(dots[0][8:]) == [0] * 8, dots
+        assert out == 0.0 and mag == 256.0, (wtype, out, mag)
+
+
 def pin_q6_k_e5(O):
     fx = golden("q6_k_e5.json")
     ql = bytearray(bytes.fromhex(fx["ql_hex_default"]) * 128)
@@ -891,4 +911,4 @@ ALL_PINS = [pin_type_info, pin_f16_decode, pin_f16_encode, pin_q8_1_e1, pin_q8_1
             pin_q5_0_e8, pin_q5_1_e9, pin_q5_k_e10, pin_q4_k_fragment,
             pin_q4_k_bijection, pin_q6_k_fragment, pin_brute_force, pin_int_dot_special,
             pin_columns_independent, pin_glu, pin_id, pin_zero_padding, pin_linearity,
-            pin_glu_variants, pin_epilogue, pin_error_codes]
+            pin_glu_variants, pin_epilogue, pin_error_codes, pin_k_min_magnitude_halves]

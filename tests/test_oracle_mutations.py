@@ -27,6 +27,9 @@ MUTATIONS = {
                           "const double t2 = 7.0 * dw * q8_s(ycol, qb);"),
     "q4_0_no_zero_point": ("const double t2 = 8.0 * dw * q8_s(ycol, qb);",
                            "const double t2 = 0.0 * dw * q8_s(ycol, qb);"),
+    "k_min_magnitude_whole_sub_blocks": (
+        "for (int h = 0; h < 2; ++h) *mag += fabs(d * sc * d8 * half1[h]) + fabs(dmin * m * d8 * half2[h]);",
+        "*mag += fabs(t1) + fabs(t2);"),
     "q4_k_min_sign": ("const double t2 = dmin * m * d8 * dot2;\n        *acc += t1 - t2;",
                       "const double t2 = dmin * m * d8 * dot2;\n        *acc += t1 + t2;"),
     "q4_k_d_dmin_swapped": ("const double dmin = orc_f16_to_f64(rd16(blk + 2));",
